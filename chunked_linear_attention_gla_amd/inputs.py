@@ -1,0 +1,130 @@
+"""Seeded synthetic workloads for the bounded-decay chunked GLA forward pass.
+
+This module only draws random numbers and lays them out.  It holds none of the
+method's arithmetic (no gate, no decay, no cumulative sums), so both the GPU
+path and the CPU oracle may consume what it produces.
+
+Workload recipe, shared by every named workload:
+  q ~ N(0, 1) / sqrt(dk)                  (drawn in fp32, then stored)
+  k ~ N(0, 1), L2-normalised per token    (normalised in fp32, then stored)
+  v ~ N(0, 1)
+  x ~ N(x_mean, x_std), one fp32 scalar per (batch, head, token)
+  S0 ~ N(0, s0_std) fp32 when s0_std > 0, else absent (zero initial state)
+q, k, v are stored in bf16 (round-to-nearest-even, torch's cast) or fp32; x, S0
+always fp32.  N(m, s) means mean m and standard deviation s.  Draws happen in the
+order q, k, v, x, S0 from one torch generator seeded with the workload's seed on
+the target device, so a workload is reproducible per device.
+
+The model-scale context lengths these sizes follow are the staged windows 8K,
+64K, 256K and 1M of [LCT §2] ("Engineering Long-Context Training for
+Trillion-Parameter MoE Models: Three Key Breakthroughs", §2).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, Optional
+
+import torch
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    H: int
+    T: int
+    dk: int
+    dv: int
+    qkv_dtype: str          # "bf16" or "f32"
+    x_mean: float
+    x_std: float
+    s0_std: float           # 0 -> no initial state
+    gate: str               # "bounded" (g = -5 sigmoid(x)) or "neg_softplus"
+    seed: int
+    note: str = ""
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "fp32_small": Workload("fp32_small", 1, 2, 256, 64, 64, "f32", 0.0, 1.0, 0.0,
+                           "bounded", 1000, "fp32 path, correctness size"),
+    "bf16_8k": Workload("bf16_8k", 4, 16, 8192, 128, 128, "bf16", 0.0, 1.0, 0.1,
+                        "bounded", 1001, "bf16 q/k/v, fp32 x/S0/o/S_T"),
+    "bf16_64k_strong": Workload("bf16_64k_strong", 1, 32, 65536, 128, 128, "bf16", 4.0, 1.0, 0.0,
+                                "bounded", 1002,
+                                "strong decay: g sits near the -5 bound, tile sums near -80"),
+    "bf16_64k_strong_softplus": Workload("bf16_64k_strong_softplus", 1, 32, 65536, 128, 128, "bf16",
+                                         -4.0, 1.0, 0.0, "neg_softplus", 1002,
+                                         "ablation: g = -softplus(-x) in the same strong-decay regime"),
+    "bf16_256k": Workload("bf16_256k", 1, 16, 262144, 128, 128, "bf16", 0.0, 2.0, 0.0,
+                          "bounded", 1003, "long sequence; chained continuation of 65536 tokens"),
+    "bf16_1m": Workload("bf16_1m", 1, 8, 1048576, 128, 128, "bf16", 0.0, 1.0, 0.0,
+                        "bounded", 1004, "million-token head group"),
+}
+
+# The 64K strong-decay workload is the one throughput is quoted on.
+HEADLINE = "bf16_64k_strong"
+
+
+def _dtype(name: str) -> torch.dtype:
+    if name == "bf16":
+        return torch.bfloat16
+    if name == "f32":
+        return torch.float32
+    raise ValueError(name)
+
+
+def make_inputs(w: Workload, device="cpu", *, T: Optional[int] = None, H: Optional[int] = None,
+                B: Optional[int] = None, seed: Optional[int] = None,
+                x_const: Optional[float] = None) -> Dict[str, Optional[torch.Tensor]]:
+    """Draw one seeded batch of workload ``w`` on ``device``.
+
+    T, H, B, seed override the workload's values (smaller samples of the same
+    recipe).  x_const replaces the gate pre-activation by a constant (for example
+    -inf gives decay exactly 1 under the bounded gate).
+    Returns dict(q, k, v, x, S0) with q/k [B,H,T,dk], v [B,H,T,dv], x [B,H,T],
+    S0 [B,H,dk,dv] or None.
+    """
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    seed = w.seed if seed is None else seed
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    st = _dtype(w.qkv_dtype)
+    f32 = dict(device=dev, dtype=torch.float32, generator=gen)
+
+    q = torch.randn(B, H, T, w.dk, **f32)
+    q.mul_(1.0 / math.sqrt(w.dk))
+    q = q.to(st)
+    k = torch.randn(B, H, T, w.dk, **f32)
+    k.div_(torch.linalg.vector_norm(k, dim=-1, keepdim=True).clamp_min(1e-30))
+    k = k.to(st)
+    v = torch.randn(B, H, T, w.dv, **f32).to(st)
+    x = torch.randn(B, H, T, **f32)
+    x.mul_(w.x_std).add_(w.x_mean)
+    if x_const is not None:
+        x.fill_(x_const)
+    S0 = None
+    if w.s0_std > 0:
+        S0 = torch.randn(B, H, w.dk, w.dv, **f32).mul_(w.s0_std)
+    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), x=x.contiguous(), S0=S0)
+
+
+def to_numpy_bits(t: torch.Tensor):
+    """Host numpy view of a tensor for the oracle: bf16 -> uint16 bit patterns,
+    fp32 -> float32 (values unchanged)."""
+    t = t.detach().to("cpu").contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view("uint16")
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError(t.dtype)

@@ -1,0 +1,198 @@
+/*
+ * gla_oracle.c -- fp64 CPU oracle for the gated linear attention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU product path
+ * never links, loads or calls it, and it shares no source with that path.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [LCT] "Engineering Long-Context Training for Trillion-Parameter MoE Models:
+ *          Three Key Breakthroughs"
+ *   [STM] "Scaling Trillion-Parameter MoE and Long-Context LLMs: Architecture
+ *          and Engineering in Practice"
+ *   [ESU] "Engineering Stability in Ultra-Long Context and Trillion-Parameter
+ *          Sparse Models"
+ *
+ * What it computes.  [LCT §3.1] and [ESU §2.1] describe linear attention whose
+ * state is carried from token to token and multiplied by a per-position decay;
+ * the cumulative product of those decays is the factor Gamma.  The pages never
+ * write the recurrence out; the plainest reading, which this file implements
+ * literally, one token at a time, is
+ *
+ *     S_{-1} = S0                       (dk x dv; zero when S0 is absent)
+ *     S_t    = a_t * S_{t-1} + k_t v_t^T
+ *     o_t    = S_t^T q_t                (token t sees its own key/value)
+ *     S_T    = S_{T-1}
+ *
+ * with a_t = exp(g_t) and the log-decay g_t taken from the gate of [LCT §3.2]:
+ *     bounded gate:        g = -5 * sigmoid(x)        range (-5, 0)
+ *     negative softplus:   g = -softplus(-x) = log(sigmoid(x))  range (-inf, 0)
+ * (the second is the unbounded conventional form kept for the ablation; its
+ * sign follows the strong-decay reading, so that x ~ N(-4,1) decays strongly).
+ *
+ * There is no chunking, blocking, tiling or reordering here: the chunked
+ * method of [LCT §3.1] reaches the same result up to rounding order.
+ *
+ * Inputs are read after their storage rounding: q, k, v are bf16 bit patterns
+ * (qkv_is_bf16 = 1) or fp32 values; x is fp32; S0 is given in double (an fp32
+ * initial state widens exactly; a double one lets states be chained without
+ * rounding).  Every value is widened to double before any arithmetic, and all
+ * arithmetic is double.
+ *
+ * Layouts (row-major, contiguous; BH = batch * heads, heads independent):
+ *   q, k [BH][T][dk]   v [BH][T][dv]   x [BH][T]   S0 [BH][dk][dv] or NULL
+ *   o    [BH][T][dv]   S_T [BH][dk][dv]             (outputs, double)
+ * Work is split over (head, block of `col_block` value columns) with OpenMP:
+ * the columns of S evolve independently, so the split does not change any
+ * arithmetic, only which thread performs it.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Planted-mistake builds: the test suite compiles this file with
+ * -DGLA_ORACLE_MUTANT=n to check that its pins catch each mistake.  The normal
+ * build defines nothing and takes none of these branches. */
+#ifndef GLA_ORACLE_MUTANT
+#define GLA_ORACLE_MUTANT 0
+#endif
+
+enum { ORACLE_GATE_BOUNDED_SIGMOID = 0, ORACLE_GATE_NEG_SOFTPLUS = 1 };
+
+static double widen(const void* p, int is_bf16, size_t idx) {
+  if (is_bf16) {
+    /* a bf16 value is the upper half of the fp32 with the same bits */
+    uint32_t u = (uint32_t)((const uint16_t*)p)[idx] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+  }
+  return (double)((const float*)p)[idx];
+}
+
+/* sigmoid(x) = 1 / (1 + e^-x), evaluated so that no intermediate overflows */
+static double sigmoid(double x) {
+  if (x >= 0.0) return 1.0 / (1.0 + exp(-x));
+  double e = exp(x);
+  return e / (1.0 + e);
+}
+
+/* softplus(z) = log(1 + e^z) = max(z, 0) + log1p(e^-|z|) */
+static double softplus(double z) {
+  return (z > 0.0 ? z : 0.0) + log1p(exp(-fabs(z)));
+}
+
+/* log-decay g(x) [LCT §3.2]: bounded g = g_min * sigmoid(x) with g_min = -5,
+ * or the conventional unbounded negative softplus. */
+double gla_oracle_gate(double x, int gate) {
+#if GLA_ORACLE_MUTANT == 4
+  x = -x; /* planted: gate argument sign flipped */
+#endif
+  if (gate == ORACLE_GATE_NEG_SOFTPLUS) return -softplus(-x);
+  return -5.0 * sigmoid(x);
+}
+
+/* Returns 0 on success, 1 on a bad argument. */
+int gla_oracle_forward(const void* q, const void* k, const void* v, int qkv_is_bf16,
+                       const float* x, const double* S0, double* o, double* S_T,
+                       long long BH, long long T, int dk, int dv, int gate,
+                       int col_block, int nthreads) {
+  if (!q || !k || !v || !x || !o || !S_T) return 1;
+  if (BH < 0 || T < 0 || dk <= 0 || dv <= 0) return 1;
+  if (gate != ORACLE_GATE_BOUNDED_SIGMOID && gate != ORACLE_GATE_NEG_SOFTPLUS) return 1;
+  if (col_block <= 0 || col_block > dv) col_block = dv;
+  const long long ncb = (dv + col_block - 1) / col_block;
+  const long long tasks = BH * ncb;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long long task = 0; task < tasks; ++task) {
+    const long long bh = task / ncb;
+    const int n0 = (int)(task % ncb) * col_block;
+    const int nc = (n0 + col_block <= dv) ? col_block : dv - n0;
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)nc);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* vt = (double*)malloc(sizeof(double) * (size_t)nc);
+
+    for (int d = 0; d < dk; ++d)
+      for (int n = 0; n < nc; ++n)
+        S[(size_t)d * nc + n] = S0 ? S0[((size_t)bh * dk + d) * dv + n0 + n] : 0.0;
+
+    for (long long t = 0; t < T; ++t) {
+      const size_t row = (size_t)bh * (size_t)T + (size_t)t;
+#if GLA_ORACLE_MUTANT == 5
+      /* planted: decay index shifted by one token (a_0 = 1, a_t from x[t-1]) */
+      const double a = t == 0 ? 1.0 : exp(gla_oracle_gate((double)x[row - 1], gate));
+#elif GLA_ORACLE_MUTANT == 6
+      /* planted: the initial state is not decayed at the first token */
+      const double a = t == 0 ? 1.0 : exp(gla_oracle_gate((double)x[row], gate));
+#else
+      const double a = exp(gla_oracle_gate((double)x[row], gate));
+#endif
+      for (int d = 0; d < dk; ++d) {
+#if GLA_ORACLE_MUTANT == 3
+        /* planted: query and key roles swapped */
+        qt[d] = widen(k, qkv_is_bf16, row * (size_t)dk + d);
+        kt[d] = widen(q, qkv_is_bf16, row * (size_t)dk + d);
+#else
+        kt[d] = widen(k, qkv_is_bf16, row * (size_t)dk + d);
+        qt[d] = widen(q, qkv_is_bf16, row * (size_t)dk + d);
+#endif
+      }
+      for (int n = 0; n < nc; ++n) vt[n] = widen(v, qkv_is_bf16, row * (size_t)dv + n0 + n);
+
+#if GLA_ORACLE_MUTANT == 1
+      /* planted: output read before this token's update (drops token t) */
+      for (int n = 0; n < nc; ++n) {
+        double acc = 0.0;
+        for (int d = 0; d < dk; ++d) acc += S[(size_t)d * nc + n] * qt[d];
+        o[row * (size_t)dv + n0 + n] = acc;
+      }
+#endif
+      /* S_t = a_t S_{t-1} + k_t v_t^T */
+      for (int d = 0; d < dk; ++d)
+        for (int n = 0; n < nc; ++n) {
+#if GLA_ORACLE_MUTANT == 2
+          /* planted: decay also applied to the new outer product */
+          S[(size_t)d * nc + n] = a * (S[(size_t)d * nc + n] + kt[d] * vt[n]);
+#else
+          S[(size_t)d * nc + n] = a * S[(size_t)d * nc + n] + kt[d] * vt[n];
+#endif
+        }
+#if GLA_ORACLE_MUTANT != 1
+      /* o_t = S_t^T q_t */
+      for (int n = 0; n < nc; ++n) {
+        double acc = 0.0;
+        for (int d = 0; d < dk; ++d) acc += S[(size_t)d * nc + n] * qt[d];
+        o[row * (size_t)dv + n0 + n] = acc;
+      }
+#endif
+    }
+    for (int d = 0; d < dk; ++d)
+      for (int n = 0; n < nc; ++n)
+        S_T[((size_t)bh * dk + d) * dv + n0 + n] = S[(size_t)d * nc + n];
+    free(S);
+    free(kt);
+    free(qt);
+    free(vt);
+  }
+  return 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
+int gla_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
