@@ -1,0 +1,250 @@
+"""ctypes binding of libgla.so (the C ABI in include/gla.h).
+
+Argument marshalling only: shapes and dtypes are checked so that the sizes handed
+to the library describe the tensors, outputs and workspace are allocated with
+torch on the inputs' device, and the call goes to torch's current stream on that
+device.  Every step of the computation runs in the library's HIP kernels; there is
+no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgla.so")
+
+GLA_BF16, GLA_F32 = 0, 1
+GATES = {"bounded": 0, "bounded_sigmoid": 0, "neg_softplus": 1, "softplus": 1}
+PATHS = {"unified": 0, "diag_branch": 1, "diag": 1}
+STATUS = {
+    0: "GLA_OK", 1: "GLA_ERR_NULL", 2: "GLA_ERR_SHAPE", 3: "GLA_ERR_DTYPE", 4: "GLA_ERR_ALIAS",
+    5: "GLA_ERR_WORKSPACE", 6: "GLA_ERR_HIP", 7: "GLA_ERR_PLAN", 8: "GLA_ERR_ALIGN", 9: "GLA_ERR_ARG",
+    10: "GLA_ERR_UNSUPPORTED",
+}
+CHUNK = 64
+MAX_SEGMENTS = 16
+
+
+class GLAError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed: {STATUS.get(code, code)}")
+
+
+class Plan(NamedTuple):
+    segments: int
+    dv_split: int
+
+
+class _CPlan(ctypes.Structure):
+    _fields_ = [("segments", ctypes.c_int), ("dv_split", ctypes.c_int)]
+
+
+_lib = None
+
+_vp, _i, _ll, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong, ctypes.c_size_t
+_pplan = ctypes.POINTER(_CPlan)
+_psz = ctypes.POINTER(ctypes.c_size_t)
+_SIGS = {
+    "gla_status_string": (ctypes.c_char_p, [_i]),
+    "gla_abi_version": (_i, []),
+    "gla_plan_default": (_i, [_i, _i, _ll, _i, _i, _i, _i, _pplan]),
+    "gla_plan_check": (_i, [_i, _i, _ll, _i, _i, _i, _i, _pplan]),
+    "gla_segment_workspace_size": (_i, [_i, _i, _ll, _i, _i, _pplan, _psz]),
+    "gla_workspace_size": (_i, [_i, _i, _ll, _i, _i, _i, _i, _pplan, _psz]),
+    "gla_gate_cumsum": (_i, [_vp, _vp, _i, _i, _ll, _i, _vp]),
+    "gla_segment_states": (_i, [_vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _pplan, _vp, _sz, _vp]),
+    "gla_chunk_output": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan,
+                              _vp, _sz, _vp]),
+    "gla_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i,
+                           _vp, _psz, _vp]),
+    "gla_chunk_fwd_plan": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i,
+                                _pplan, _vp, _psz, _vp]),
+}
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgla.so (raises when it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m chunked_linear_attention_gla_amd._build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, code: int) -> None:
+    if code != 0:
+        raise GLAError(fn, code)
+
+
+def _cplan(plan: Optional[Plan]):
+    return None if plan is None else ctypes.byref(_CPlan(int(plan.segments), int(plan.dv_split)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GLA_BF16
+    if t.dtype == torch.float32:
+        return GLA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _gate(gate) -> int:
+    return GATES[gate] if isinstance(gate, str) else int(gate)
+
+
+def _path(path) -> int:
+    return PATHS[path] if isinstance(path, str) else int(path)
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _check_qkv(q, k, v, x=None, S0=None):
+    _need(q.dim() == 4 and k.shape == q.shape, "q and k must be [B, H, T, dk] of one shape")
+    B, H, T, dk = q.shape
+    _need(v.dim() == 4 and tuple(v.shape[:3]) == (B, H, T), "v must be [B, H, T, dv]")
+    dv = v.shape[3]
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _need(t.is_cuda and t.is_contiguous(), f"{name} must be a contiguous GPU tensor")
+        _need(t.device == q.device, "all tensors must be on one device")
+    if x is not None:
+        _need(tuple(x.shape) == (B, H, T) and x.dtype == torch.float32 and x.is_cuda and x.is_contiguous()
+              and x.device == q.device, "x must be a contiguous fp32 [B, H, T] tensor on q's device")
+    if S0 is not None:
+        _need(tuple(S0.shape) == (B, H, dk, dv) and S0.dtype == torch.float32 and S0.is_cuda
+              and S0.is_contiguous() and S0.device == q.device,
+              "S0 must be a contiguous fp32 [B, H, dk, dv] tensor on q's device")
+    return B, H, T, dk, dv
+
+
+# ------------------------------------------------------------------------------------ queries
+
+def abi_version() -> int:
+    return int(load().gla_abi_version())
+
+
+def status_string(code: int) -> str:
+    return load().gla_status_string(code).decode()
+
+
+def plan_default(B: int, H: int, T: int, dk: int, dv: int, dtype=GLA_BF16, path="unified") -> Plan:
+    cp = _CPlan()
+    _check("gla_plan_default", load().gla_plan_default(B, H, T, dk, dv, dtype, _path(path), ctypes.byref(cp)))
+    return Plan(cp.segments, cp.dv_split)
+
+
+def plan_check(B: int, H: int, T: int, dk: int, dv: int, plan: Plan, dtype=GLA_BF16, path="unified") -> int:
+    """Status code of gla_plan_check (0 = valid)."""
+    return int(load().gla_plan_check(B, H, T, dk, dv, dtype, _path(path), _cplan(plan)))
+
+
+def workspace_size(B: int, H: int, T: int, dk: int, dv: int, dtype=GLA_BF16, path="unified",
+                   plan: Optional[Plan] = None) -> int:
+    n = ctypes.c_size_t(0)
+    _check("gla_workspace_size", load().gla_workspace_size(B, H, T, dk, dv, dtype, _path(path), _cplan(plan),
+                                                           ctypes.byref(n)))
+    return int(n.value)
+
+
+def segment_workspace_size(B: int, H: int, T: int, dk: int, dv: int, plan: Plan) -> int:
+    n = ctypes.c_size_t(0)
+    _check("gla_segment_workspace_size",
+           load().gla_segment_workspace_size(B, H, T, dk, dv, _cplan(plan), ctypes.byref(n)))
+    return int(n.value)
+
+
+# ------------------------------------------------------------------------------------ calls
+
+def gate_cumsum(x: torch.Tensor, gate="bounded", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunk-local cumulative log-decay b (fp32, same shape as x = [B, H, T])."""
+    _need(x.dim() == 3 and x.dtype == torch.float32 and x.is_cuda and x.is_contiguous(),
+          "x must be a contiguous fp32 [B, H, T] GPU tensor")
+    B, H, T = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out.shape == x.shape and out.dtype == torch.float32 and out.is_contiguous() and out.device == x.device,
+          "out must match x")
+    _check("gla_gate_cumsum", load().gla_gate_cumsum(_ptr(x), _ptr(out), B, H, T, _gate(gate), _stream(x.device)))
+    return out
+
+
+def segment_states(k: torch.Tensor, v: torch.Tensor, b: torch.Tensor, plan: Plan, seg_ws: torch.Tensor) -> None:
+    """Segment pre-pass into seg_ws (uint8 tensor of segment_workspace_size bytes)."""
+    B, H, T, dk, dv = _check_qkv(k, k, v)
+    _need(tuple(b.shape) == (B, H, T) and b.dtype == torch.float32 and b.is_contiguous(), "b must be fp32 [B,H,T]")
+    _check("gla_segment_states", load().gla_segment_states(
+        _ptr(k), _ptr(v), _ptr(b), B, H, T, dk, dv, _dtype_code(k), _cplan(plan), _ptr(seg_ws),
+        seg_ws.numel() * seg_ws.element_size(), _stream(k.device)))
+
+
+def chunk_output(q, k, v, b, S0, plan: Plan, seg_ws: Optional[torch.Tensor], o: torch.Tensor,
+                 S_T: torch.Tensor, path="unified") -> None:
+    """Fused output pass (o and S_T written in place)."""
+    B, H, T, dk, dv = _check_qkv(q, k, v, None, S0)
+    _need(tuple(b.shape) == (B, H, T) and b.dtype == torch.float32 and b.is_contiguous(), "b must be fp32 [B,H,T]")
+    _need(tuple(o.shape) == (B, H, T, dv) and o.dtype == torch.float32 and o.is_contiguous(), "o must be fp32 [B,H,T,dv]")
+    _need(tuple(S_T.shape) == (B, H, dk, dv) and S_T.dtype == torch.float32 and S_T.is_contiguous(),
+          "S_T must be fp32 [B,H,dk,dv]")
+    nbytes = 0 if seg_ws is None else seg_ws.numel() * seg_ws.element_size()
+    _check("gla_chunk_output", load().gla_chunk_output(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, _dtype_code(q),
+        _path(path), _cplan(plan), _ptr(seg_ws), nbytes, _stream(q.device)))
+
+
+def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor,
+              S0: Optional[torch.Tensor] = None, gate="bounded", path="unified", plan: Optional[Plan] = None,
+              o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+              workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Chunked gated-linear-attention forward: returns (o [B,H,T,dv] fp32, S_T [B,H,dk,dv] fp32).
+
+    q, k: [B, H, T, dk] and v: [B, H, T, dv], all bfloat16 or all float32; x: [B, H, T] fp32 gate
+    pre-activation; S0: [B, H, dk, dv] fp32 or None.  gate: "bounded" (g = -5 sigmoid(x)) or
+    "neg_softplus"; path: "unified" or "diag_branch"; plan: None for the device default.
+    """
+    B, H, T, dk, dv = _check_qkv(q, k, v, x, S0)
+    dev = q.device
+    lib = load()
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty(B, H, T, dv, device=dev, dtype=torch.float32)
+    if S_T is None:
+        S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+    _need(tuple(o.shape) == (B, H, T, dv) and o.dtype == torch.float32 and o.is_contiguous() and o.device == dev,
+          "o must be fp32 [B, H, T, dv] on q's device")
+    _need(tuple(S_T.shape) == (B, H, dk, dv) and S_T.dtype == torch.float32 and S_T.is_contiguous()
+          and S_T.device == dev, "S_T must be fp32 [B, H, dk, dv] on q's device")
+    need = ctypes.c_size_t(0)
+    cplan = _cplan(plan)
+    _check("gla_chunk_fwd_plan", lib.gla_chunk_fwd_plan(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, dt, _gate(gate),
+        _path(path), cplan, None, ctypes.byref(need), _stream(dev)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check("gla_chunk_fwd_plan", lib.gla_chunk_fwd_plan(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, dt, _gate(gate),
+        _path(path), cplan, _ptr(workspace), ctypes.byref(have), _stream(dev)))
+    return o, S_T

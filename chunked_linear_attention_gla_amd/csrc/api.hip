@@ -1,0 +1,337 @@
+// api.hip -- the C ABI declared in include/gla.h: argument validation, launch
+// plans, workspace carving and launch sequencing.  No allocation, no host
+// synchronisation; every launch goes to the caller's stream.
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "gla.h"
+#include "gla_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+bool valid_dtype(int d) { return d == GLA_BF16 || d == GLA_F32; }
+bool valid_gate(int g) { return g == GLA_GATE_BOUNDED_SIGMOID || g == GLA_GATE_NEG_SOFTPLUS; }
+bool valid_path(int p) { return p == GLA_PATH_UNIFIED || p == GLA_PATH_DIAG_BRANCH; }
+size_t elem_size(gla_dtype_t d) { return d == GLA_BF16 ? 2 : 4; }
+
+long long n_chunks(long long T) { return (T + GLA_CHUNK - 1) / GLA_CHUNK; }
+
+gla_status_t check_sizes(int B, int H, long long T, int dk, int dv) {
+  if (B < 1 || H < 1 || T < 0) return GLA_ERR_SHAPE;
+  if (dk != 64 && dk != 128) return GLA_ERR_SHAPE;
+  if (dv != 64 && dv != 128) return GLA_ERR_SHAPE;
+  const long long BH = (long long)B * H;
+  if (BH > (1LL << 24)) return GLA_ERR_SHAPE;
+  if (n_chunks(T) > (1LL << 30)) return GLA_ERR_SHAPE;
+  return GLA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+struct Range {
+  const void* p;
+  size_t n;
+};
+
+bool overlap(Range a, Range b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.n && b0 < a0 + a.n;
+}
+
+gla_status_t plan_check_impl(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype, gla_path_t path,
+                             const gla_plan_t* plan) {
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_path(path)) return GLA_ERR_ARG;
+  if (!plan) return GLA_ERR_NULL;
+  const long long nc = n_chunks(T);
+  if (plan->segments < 1 || plan->segments > GLA_MAX_SEGMENTS) return GLA_ERR_PLAN;
+  if (plan->segments > std::max(1LL, nc)) return GLA_ERR_PLAN;
+  const int s = plan->dv_split;
+  if (s != 1 && s != 2 && s != 4 && s != 8) return GLA_ERR_PLAN;
+  if (dv % s) return GLA_ERR_PLAN;
+  const int slice = dv / s;
+  if (slice != 16 && slice != 32 && slice != 64 && slice != 128) return GLA_ERR_PLAN;
+  if (!gla::chunk_config_built(dtype == GLA_BF16 ? 0 : 1, dk, slice, path == GLA_PATH_DIAG_BRANCH)) {
+    // a valid plan shape that this build has no kernel for
+    if (dtype == GLA_F32 && path == GLA_PATH_DIAG_BRANCH && dk != 64) return GLA_ERR_UNSUPPORTED;
+    return GLA_ERR_PLAN;
+  }
+  return GLA_OK;
+}
+
+size_t seg_bytes(long long BH, int dk, int dv, int segments) {
+  if (segments <= 1) return 0;
+  return align_up((size_t)BH * (size_t)(segments - 1) * (size_t)dk * (size_t)dv * 4) +
+         align_up((size_t)BH * (size_t)segments * 4);
+}
+
+// Default plan.  Value slices share q/k through L2, segments cost a second read of
+// k and v for all but the last segment, so: as few segments as fill the device,
+// value slices of 64 columns (32 for dv = 64).
+gla_status_t default_plan_for(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype, gla_path_t path,
+                              int cus, gla_plan_t* plan) {
+  const long long BH = (long long)B * H;
+  const long long nc = n_chunks(T);
+  int split = dv == 128 ? 2 : 2;  // 64-column slices for dv = 128, 32 for dv = 64
+  if (dtype == GLA_F32) split = dv / 64;  // fp32 kernels are built for slices <= 64
+  const long long target = 2LL * cus;     // workgroups wanted in flight
+  long long units = BH * split;
+  int segs = 1;
+  while (segs < GLA_MAX_SEGMENTS && units * segs < target && nc / (2LL * segs) >= 8) segs *= 2;
+  if (segs > std::max(1LL, nc)) segs = (int)std::max(1LL, nc);
+  plan->segments = segs;
+  plan->dv_split = split;
+  return plan_check_impl(B, H, T, dk, dv, dtype, path, plan);
+}
+
+gla_status_t device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return GLA_ERR_HIP;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return GLA_ERR_HIP;
+  if (*cus <= 0) return GLA_ERR_HIP;
+  return GLA_OK;
+}
+
+gla::ChunkParams make_params(const void* q, const void* k, const void* v, const float* b, const float* S0,
+                             float* o, float* S_T, int B, int H, long long T, int dk, int dv,
+                             const gla_plan_t& plan, const void* seg_ws) {
+  gla::ChunkParams p;
+  const long long BH = (long long)B * H;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.b = b;
+  p.S0 = S0;
+  p.o = o;
+  p.ST = S_T;
+  p.T = T;
+  p.dk = dk;
+  p.dv = dv;
+  p.BH = (int)BH;
+  p.nchunks = (int)n_chunks(T);
+  p.segments = plan.segments;
+  p.nslices = plan.dv_split;
+  p.seg_state = nullptr;
+  p.seg_decay = nullptr;
+  if (plan.segments > 1 && seg_ws) {
+    char* base = (char*)seg_ws;
+    p.seg_state = (float*)base;
+    p.seg_decay = (float*)(base + align_up((size_t)BH * (plan.segments - 1) * dk * dv * 4));
+  }
+  p.grid = 0;
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gla_status_string(gla_status_t s) {
+  switch (s) {
+    case GLA_OK: return "GLA_OK";
+    case GLA_ERR_NULL: return "GLA_ERR_NULL: a required pointer is NULL";
+    case GLA_ERR_SHAPE: return "GLA_ERR_SHAPE: B, H, T, dk or dv out of the supported range";
+    case GLA_ERR_DTYPE: return "GLA_ERR_DTYPE: unknown dtype";
+    case GLA_ERR_ALIAS: return "GLA_ERR_ALIAS: an output overlaps an input or another output";
+    case GLA_ERR_WORKSPACE: return "GLA_ERR_WORKSPACE: workspace missing or too small";
+    case GLA_ERR_HIP: return "GLA_ERR_HIP: HIP runtime call or kernel launch failed";
+    case GLA_ERR_PLAN: return "GLA_ERR_PLAN: plan invalid for these sizes";
+    case GLA_ERR_ALIGN: return "GLA_ERR_ALIGN: pointer alignment violated";
+    case GLA_ERR_ARG: return "GLA_ERR_ARG: unknown gate or path";
+    case GLA_ERR_UNSUPPORTED: return "GLA_ERR_UNSUPPORTED: combination not built";
+  }
+  return "unknown gla_status_t";
+}
+
+int gla_abi_version(void) { return GLA_ABI_VERSION; }
+
+gla_status_t gla_plan_check(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype, gla_path_t path,
+                            const gla_plan_t* plan) {
+  return plan_check_impl(B, H, T, dk, dv, dtype, path, plan);
+}
+
+gla_status_t gla_plan_default(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype, gla_path_t path,
+                              gla_plan_t* plan) {
+  if (!plan) return GLA_ERR_NULL;
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_path(path)) return GLA_ERR_ARG;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  return default_plan_for(B, H, T, dk, dv, dtype, path, cus, plan);
+}
+
+gla_status_t gla_segment_workspace_size(int B, int H, long long T, int dk, int dv, const gla_plan_t* plan,
+                                        size_t* bytes) {
+  if (!plan || !bytes) return GLA_ERR_NULL;
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (plan->segments < 1 || plan->segments > GLA_MAX_SEGMENTS) return GLA_ERR_PLAN;
+  *bytes = seg_bytes((long long)B * H, dk, dv, plan->segments);
+  return GLA_OK;
+}
+
+gla_status_t gla_workspace_size(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype, gla_path_t path,
+                                const gla_plan_t* plan, size_t* bytes) {
+  if (!bytes) return GLA_ERR_NULL;
+  gla_plan_t pl;
+  gla_status_t st;
+  if (plan) {
+    st = plan_check_impl(B, H, T, dk, dv, dtype, path, plan);
+    if (st != GLA_OK) return st;
+    pl = *plan;
+  } else {
+    st = gla_plan_default(B, H, T, dk, dv, dtype, path, &pl);
+    if (st != GLA_OK) return st;
+  }
+  const long long BH = (long long)B * H;
+  *bytes = align_up((size_t)BH * (size_t)T * 4) + seg_bytes(BH, dk, dv, pl.segments);
+  return GLA_OK;
+}
+
+gla_status_t gla_gate_cumsum(const float* x, float* b, int B, int H, long long T, gla_gate_t gate,
+                             void* stream) {
+  if (B < 1 || H < 1 || T < 0) return GLA_ERR_SHAPE;
+  if (!valid_gate(gate)) return GLA_ERR_ARG;
+  const long long BH = (long long)B * H;
+  if (T == 0) return GLA_OK;
+  if (!x || !b) return GLA_ERR_NULL;
+  if (!aligned(x, 4) || !aligned(b, 4)) return GLA_ERR_ALIGN;
+  const size_t n = (size_t)BH * (size_t)T * 4;
+  if (overlap({x, n}, {b, n})) return GLA_ERR_ALIAS;
+  hipError_t e = gla::launch_gate_cumsum(x, b, BH, T, gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid
+                                                                                     : gla::kGateNegSoftplus,
+                                         (hipStream_t)stream);
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+gla_status_t gla_segment_states(const void* k, const void* v, const float* b, int B, int H, long long T, int dk,
+                                int dv, gla_dtype_t dtype, const gla_plan_t* plan, void* seg_ws,
+                                size_t seg_ws_bytes, void* stream) {
+  gla_status_t st = plan_check_impl(B, H, T, dk, dv, dtype, GLA_PATH_UNIFIED, plan);
+  if (st != GLA_OK) return st;
+  if (plan->segments <= 1 || T == 0) return GLA_OK;
+  if (!k || !v || !b) return GLA_ERR_NULL;
+  const long long BH = (long long)B * H;
+  const size_t need = seg_bytes(BH, dk, dv, plan->segments);
+  if (!seg_ws || seg_ws_bytes < need) return GLA_ERR_WORKSPACE;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(b, 4) || !aligned(seg_ws, kAlign)) return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dtype);
+  const Range ws{seg_ws, need};
+  if (overlap(ws, {k, (size_t)BH * T * dk * es}) || overlap(ws, {v, (size_t)BH * T * dv * es}) ||
+      overlap(ws, {b, (size_t)BH * T * 4}))
+    return GLA_ERR_ALIAS;
+  gla::ChunkParams p = make_params(nullptr, k, v, b, nullptr, nullptr, nullptr, B, H, T, dk, dv, *plan, seg_ws);
+  p.grid = (int)(BH * plan->dv_split * (plan->segments - 1));
+  hipError_t e = gla::launch_segment_states(p, dtype == GLA_BF16 ? 0 : 1, (hipStream_t)stream);
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+gla_status_t gla_chunk_output(const void* q, const void* k, const void* v, const float* b, const float* S0,
+                              float* o, float* S_T, int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                              gla_path_t path, const gla_plan_t* plan, const void* seg_ws, size_t seg_ws_bytes,
+                              void* stream) {
+  gla_status_t st = plan_check_impl(B, H, T, dk, dv, dtype, path, plan);
+  if (st != GLA_OK) return st;
+  if (!S_T) return GLA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !b || !o)) return GLA_ERR_NULL;
+  const long long BH = (long long)B * H;
+  const size_t es = elem_size(dtype);
+  const size_t need = seg_bytes(BH, dk, dv, plan->segments);
+  if (plan->segments > 1 && (!seg_ws || seg_ws_bytes < need)) return GLA_ERR_WORKSPACE;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(S_T, 16) ||
+      !aligned(S0, 16) || !aligned(b, 4))
+    return GLA_ERR_ALIGN;
+  const Range rq{q, (size_t)BH * T * dk * es}, rk{k, (size_t)BH * T * dk * es}, rv{v, (size_t)BH * T * dv * es};
+  const Range rb{b, (size_t)BH * T * 4}, rs0{S0, (size_t)BH * dk * dv * 4};
+  const Range ro{o, (size_t)BH * T * dv * 4}, rst{S_T, (size_t)BH * dk * dv * 4};
+  const Range rws{plan->segments > 1 ? seg_ws : nullptr, need};
+  for (const Range& in : {rq, rk, rv, rb, rs0, rws})
+    if (overlap(ro, in) || overlap(rst, in)) return GLA_ERR_ALIAS;
+  if (overlap(ro, rst)) return GLA_ERR_ALIAS;
+  gla::ChunkParams p = make_params(q, k, v, b, S0, o, S_T, B, H, T, dk, dv, *plan, seg_ws);
+  p.grid = (int)(BH * plan->dv_split * plan->segments);
+  hipError_t e = gla::launch_chunk_output(p, dtype == GLA_BF16 ? 0 : 1, path == GLA_PATH_DIAG_BRANCH,
+                                          (hipStream_t)stream);
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, const float* x, const float* S0,
+                                float* o, float* S_T, int B, int H, long long T, int dk, int dv,
+                                gla_dtype_t dtype, gla_gate_t gate, gla_path_t path, const gla_plan_t* plan,
+                                void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!workspace_bytes) return GLA_ERR_NULL;
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_gate(gate) || !valid_path(path)) return GLA_ERR_ARG;
+  gla_plan_t pl;
+  if (plan) {
+    st = plan_check_impl(B, H, T, dk, dv, dtype, path, plan);
+    if (st != GLA_OK) return st;
+    pl = *plan;
+  } else {
+    st = gla_plan_default(B, H, T, dk, dv, dtype, path, &pl);
+    if (st != GLA_OK) return st;
+  }
+  const long long BH = (long long)B * H;
+  const size_t b_bytes = align_up((size_t)BH * (size_t)T * 4);
+  const size_t s_bytes = seg_bytes(BH, dk, dv, pl.segments);
+  if (!workspace) {
+    *workspace_bytes = b_bytes + s_bytes;
+    return GLA_OK;
+  }
+  if (*workspace_bytes < b_bytes + s_bytes) return GLA_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return GLA_ERR_ALIGN;
+  if (!S_T) return GLA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !x || !o)) return GLA_ERR_NULL;
+  if (!aligned(x, 4)) return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dtype);
+  const Range rws{workspace, b_bytes + s_bytes};
+  const Range ins[] = {{q, (size_t)BH * T * dk * es}, {k, (size_t)BH * T * dk * es}, {v, (size_t)BH * T * dv * es},
+                       {x, (size_t)BH * T * 4},       {S0, (size_t)BH * dk * dv * 4}, {o, (size_t)BH * T * dv * 4},
+                       {S_T, (size_t)BH * dk * dv * 4}};
+  for (const Range& r : ins)
+    if (overlap(rws, r)) return GLA_ERR_ALIAS;
+  if (overlap(ins[5], ins[3]) || overlap(ins[6], ins[3])) return GLA_ERR_ALIAS;  // o, S_T vs x
+  float* bbuf = (float*)workspace;
+  void* seg = (char*)workspace + b_bytes;
+  // Validate the output pass fully before enqueueing anything.
+  {
+    const Range rq = ins[0], rk = ins[1], rv = ins[2], rs0 = ins[4], ro = ins[5], rst = ins[6];
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(S_T, 16) ||
+        !aligned(S0, 16))
+      return GLA_ERR_ALIGN;
+    for (const Range& in : {rq, rk, rv, rs0})
+      if (overlap(ro, in) || overlap(rst, in)) return GLA_ERR_ALIAS;
+    if (overlap(ro, rst)) return GLA_ERR_ALIAS;
+  }
+  st = gla_gate_cumsum(x, bbuf, B, H, T, gate, stream);
+  if (st != GLA_OK) return st;
+  if (pl.segments > 1) {
+    st = gla_segment_states(k, v, bbuf, B, H, T, dk, dv, dtype, &pl, seg, s_bytes, stream);
+    if (st != GLA_OK) return st;
+  }
+  return gla_chunk_output(q, k, v, bbuf, S0, o, S_T, B, H, T, dk, dv, dtype, path, &pl, seg, s_bytes, stream);
+}
+
+gla_status_t gla_chunk_fwd(const void* q, const void* k, const void* v, const float* x, const float* S0, float* o,
+                           float* S_T, int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                           gla_gate_t gate, gla_path_t path, void* workspace, size_t* workspace_bytes,
+                           void* stream) {
+  return gla_chunk_fwd_plan(q, k, v, x, S0, o, S_T, B, H, T, dk, dv, dtype, gate, path, nullptr, workspace,
+                            workspace_bytes, stream);
+}
+
+}  // extern "C"

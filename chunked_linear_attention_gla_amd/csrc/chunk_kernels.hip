@@ -1,0 +1,566 @@
+// chunk_kernels.hip -- chunked gated-linear-attention forward on gfx950 matrix cores.
+//
+// Sources (web pages; cited by title and section):
+//   [LCT] "Engineering Long-Context Training for Trillion-Parameter MoE Models:
+//          Three Key Breakthroughs"
+//   [ESU] "Engineering Stability in Ultra-Long Context and Trillion-Parameter
+//          Sparse Models"
+//
+// Chunked form of S_t = a_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t [LCT §3.1],
+// [ESU §2.1]: the sequence is cut into 64-token chunks, each made of four
+// 16-token tiles u = 0..3.  With b_j the chunk-local cumulative log-decay,
+// r_u = b_{16u-1} (r_0 = 0) and gamma = b_63, for query j and key i of one chunk:
+//   weight of k_i v_i^T in o_j  (i <= j)  = e^{b_j - b_i}
+//                                        = e^{b_j - r_u(j)} e^{r_u(j) - r_u(i)} e^{r_u(i) - b_i}
+//   weight of S_{c-1} in o_j              = e^{b_j}    = e^{r_u(j)} e^{b_j - r_u(j)}
+//   weight of k_i v_i^T in S_c            = e^{gamma - b_i}
+// so, with Qh_j = q_j e^{b_j - r_u(j)} ("q * Gamma") and Kh_i = k_i e^{r_u(i) - b_i}
+// ("k / Gamma"):
+//   A_ji = (Qh_j . Kh_i) e^{r_u(j) - r_u(i)}  for i <= j, 0 above the diagonal
+//   o_j  = e^{r_u(j)} (Qh_j^T S_{c-1}) + sum_i A_ji v_i
+//   S_c  = e^gamma S_{c-1} + sum_i (k_i e^{gamma - b_i}) v_i^T
+// Because g >= -5, the tile-relative factors lie in [e^-80, 1] and [1, e^80],
+// inside the fp32/bf16 exponent range [LCT §3.2], [ESU §2.2], so every causal
+// 16x16 tile of A, diagonal or not, comes out of the same matrix-core product
+// with no separate diagonal branch [LCT §3.3].  The remaining scalars
+// e^{r_u(j) - r_u(i)}, e^{r_u(j)} and e^gamma are all <= 1.
+//
+// The conventional design kept for the ablation (DIAG = true) computes only the
+// off-diagonal tiles on matrix cores, with factors referenced to the end of the
+// key tile, E_u = b_{16u+15} (Kh_i = k_i e^{E_u(i) - b_i} <= 1 and a tile scalar
+// e^{r_u(j) - E_u(i)} <= 1), and the diagonal tiles by explicit position pairs,
+// A_ji = e^{b_j - b_i} (q_j . k_i), on the vector ALUs [LCT §3.1], [ESU §2.1].
+//
+// Work decomposition: one workgroup per (head, slice of DVS value columns,
+// segment of consecutive chunks).  A workgroup streams its chunks in order,
+// holding its slice of the state in fp32 MFMA accumulators; wave w owns value
+// columns [w*CPW, (w+1)*CPW) of the slice for o and S.  Segments after the first
+// start from the state assembled from the pre-pass (segment_state_kernel).
+#include "gla_device.h"
+#include "gla_internal.h"
+
+namespace gla {
+
+template <typename T, int DK, int DVS>
+struct Cfg {
+  static constexpr int NW = DVS >= 64 ? 4 : DVS / 16;  // waves per workgroup
+  static constexpr int NB = DVS / (16 * NW);           // 16-column blocks per wave
+  static constexpr int CPW = 16 * NB;                  // value columns per wave
+  static constexpr int NT = 64 * NW;                   // threads per workgroup
+  static constexpr int PAD = Elem<T>::kPad;
+  static constexpr int QLD = DK + PAD;   // row stride of Qh, Kh (and raw q, k)
+  static constexpr int TLD = 64 + PAD;   // row stride of the token-contiguous tiles
+  static constexpr int QU = 8 * DK / NT;   // 8-element q (and k) units per thread per chunk
+  static constexpr int VU = 8 * DVS / NT;  // 8-element v units per thread per chunk
+  static constexpr int DB = DK / 16;       // 16-row blocks of the key dimension
+  static constexpr int KS = DK / 32;       // K-steps over the key dimension
+  static_assert(QU >= 1 && 8 * DK == QU * NT, "q staging must divide evenly");
+  static_assert(VU >= 1 && 8 * DVS == VU * NT, "v staging must divide evenly");
+};
+
+template <typename T, int DK, int DVS, bool DIAG>
+struct OutSmem {
+  using C = Cfg<T, DK, DVS>;
+  T qh[64 * C::QLD];    // Qh[j][d]                 row-major
+  T kh[64 * C::QLD];    // Kh[i][d]                 row-major
+  T kpt[DK * C::TLD];   // (k_i e^{gamma-b_i})[d][i] token-contiguous
+  T vt[DVS * C::TLD];   // v[n][i]                  token-contiguous
+  T a[64 * C::TLD];     // A[j][i]                  row-major
+  T qr[DIAG ? 64 * C::QLD : 1];  // raw q, diagonal-branch path only
+  T kr[DIAG ? 64 * C::QLD : 1];  // raw k, diagonal-branch path only
+  float sb[2][64];      // b of the current and the next chunk
+};
+
+template <typename T, int DK, int DVS>
+struct SegSmem {
+  using C = Cfg<T, DK, DVS>;
+  T kpt[DK * C::TLD];
+  T vt[DVS * C::TLD];
+  float sb[2][64];
+};
+
+// Causal 16x16 tiles of a 64x64 chunk: (query tile jb, key tile ib), ib <= jb.
+__device__ __constant__ const int kTriJ[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__device__ __constant__ const int kTriI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+__device__ __constant__ const int kOffJ[6] = {1, 2, 2, 3, 3, 3};
+__device__ __constant__ const int kOffI[6] = {0, 0, 1, 0, 1, 2};
+
+// Per-thread registers holding one chunk of q, k, v on its way to LDS.
+template <typename T, int DK, int DVS, bool LOAD_Q>
+struct Staged {
+  using E = Elem<T>;
+  using C = Cfg<T, DK, DVS>;
+  typename E::Vec8 q[LOAD_Q ? C::QU : 1];
+  typename E::Vec8 k[C::QU];
+  typename E::Vec8 v[C::VU];
+
+  __device__ __forceinline__ void load(const T* qg, const T* kg, const T* vg, long long t0, long long len,
+                                       int dv, int col0, int tid) {
+    const bool full = t0 + kChunk <= len;
+#pragma unroll
+    for (int m = 0; m < C::QU; ++m) {
+      const int u = tid + m * C::NT;
+      const int row = u / (DK / 8), c8 = u % (DK / 8);
+      const long long off = (t0 + row) * DK + c8 * 8;
+      const bool ok = full || (t0 + row < len);
+      if (LOAD_Q) q[m] = ok ? E::load8(qg + off) : E::zero8();
+      k[m] = ok ? E::load8(kg + off) : E::zero8();
+    }
+#pragma unroll
+    for (int m = 0; m < C::VU; ++m) {
+      const int u = tid + m * C::NT;
+      const int row = u / (DVS / 8), c8 = u % (DVS / 8);
+      const bool ok = full || (t0 + row < len);
+      v[m] = ok ? E::load8(vg + (t0 + row) * dv + col0 + c8 * 8) : E::zero8();
+    }
+  }
+};
+
+// b of token t0 + j of a chunk; past the end of the sequence the cumulative sum
+// stays at its last value (absent tokens have g = 0).
+__device__ __forceinline__ float load_b(const float* bg, long long t0, int j, long long T) {
+  long long t = t0 + j;
+  if (t >= T) t = T - 1;
+  return bg[t];
+}
+
+// Writes k e^{gamma - b} (token-contiguous) and v (token-contiguous) into LDS.
+template <typename T, int DK, int DVS, bool LOAD_Q>
+__device__ __forceinline__ void stage_state_operands(T* kpt, T* vt, const Staged<T, DK, DVS, LOAD_Q>& st,
+                                                     const float* sbc, int tid) {
+  using E = Elem<T>;
+  using C = Cfg<T, DK, DVS>;
+  const float gam = sbc[63];
+#pragma unroll
+  for (int m = 0; m < C::QU; ++m) {
+    const int u = tid + m * C::NT;
+    const int row = u / (DK / 8), c8 = u % (DK / 8);
+    const float f = exp_e(gam - sbc[row]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kpt[(c8 * 8 + e) * C::TLD + row] = E::cvt(E::get(st.k[m], e) * f);
+  }
+#pragma unroll
+  for (int m = 0; m < C::VU; ++m) {
+    const int u = tid + m * C::NT;
+    const int row = u / (DVS / 8), c8 = u % (DVS / 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt[(c8 * 8 + e) * C::TLD + row] = E::cvt(E::get(st.v[m], e));
+  }
+}
+
+// S[nb][db] += sum_i kpt[d][i] v[n][i] over the chunk's 64 tokens (two K-steps).
+// fp32 state slice of one wave: S[d = 16 db + 4 g + e][n = 16 nb + r16], e = 0..3
+template <typename T, int DK, int DVS>
+struct StateAcc {
+  floatx4 s[Cfg<T, DK, DVS>::NB][Cfg<T, DK, DVS>::DB];
+};
+
+// v[n][i] operand fragments of one wave for the chunk's two token K-steps
+template <typename T, int DK, int DVS>
+struct VFrags {
+  typename Elem<T>::Frag f[Cfg<T, DK, DVS>::NB][2];
+};
+
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void state_update(StateAcc<T, DK, DVS>& S, const VFrags<T, DK, DVS>& Vf,
+                                             const T* kpt, float decay, int r16, int g) {
+  using E = Elem<T>;
+  using C = Cfg<T, DK, DVS>;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) S.s[nb][db] *= decay;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const typename E::Frag ka = E::load_frag(kpt + (db * 16 + r16) * C::TLD, ks * 32 + 4 * g);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) E::mfma(S.s[nb][db], ka, Vf.f[nb][ks]);
+    }
+  }
+}
+
+// ============================================================================
+// Segment pre-pass: local final state of every segment but the last.
+// ============================================================================
+template <typename T, int DK, int DVS>
+__global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(ChunkParams p) {
+  using E = Elem<T>;
+  using C = Cfg<T, DK, DVS>;
+  __shared__ SegSmem<T, DK, DVS> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nseg = p.segments - 1;
+  const int L = xcd_linear_index(blockIdx.x, p.grid);
+  const int slice = L % p.nslices;
+  const int rest = L / p.nslices;
+  const int seg = rest % nseg;
+  const int bh = rest / nseg;
+  const int col0 = slice * DVS;
+  const int wcol = col0 + wave * C::CPW;
+  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
+
+  const T* kg = static_cast<const T*>(p.k) + (long long)bh * p.T * DK;
+  const T* vg = static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv;
+  const float* bg = p.b + (long long)bh * p.T;
+
+  StateAcc<T, DK, DVS> S;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) S.s[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float gsum = 0.0f;  // total log-decay of the segment (thread 0)
+
+  Staged<T, DK, DVS, false> st;
+  float rb = 0.0f;
+  if (c_begin < c_end) {
+    if (tid < 64) sm.sb[0][tid] = load_b(bg, (long long)c_begin * kChunk, tid, p.T);
+    st.load(nullptr, kg, vg, (long long)c_begin * kChunk, p.T, p.dv, col0, tid);
+    if (tid < 64 && c_begin + 1 < c_end) rb = load_b(bg, (long long)(c_begin + 1) * kChunk, tid, p.T);
+    __syncthreads();
+  }
+  for (int c = c_begin; c < c_end; ++c) {
+    const int buf = (c - c_begin) & 1;
+    const float* sbc = sm.sb[buf];
+    stage_state_operands<T, DK, DVS, false>(sm.kpt, sm.vt, st, sbc, tid);
+    if (tid < 64) sm.sb[buf ^ 1][tid] = rb;
+    if (tid == 0) gsum += sbc[63];
+    if (c + 1 < c_end) st.load(nullptr, kg, vg, (long long)(c + 1) * kChunk, p.T, p.dv, col0, tid);
+    if (tid < 64 && c + 2 < c_end) rb = load_b(bg, (long long)(c + 2) * kChunk, tid, p.T);
+    __syncthreads();
+    VFrags<T, DK, DVS> Vf;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+        Vf.f[nb][ks] = E::load_frag(sm.vt + (wave * C::CPW + nb * 16 + r16) * C::TLD, ks * 32 + 4 * g);
+    state_update<T, DK, DVS>(S, Vf, sm.kpt, exp_e(sbc[63]), r16, g);
+    __syncthreads();
+  }
+
+  float* H = p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = db * 16 + 4 * g + e;
+        const int n = wcol + nb * 16 + r16;
+        H[(long long)d * p.dv + n] = S.s[nb][db][e];
+      }
+  if (slice == 0 && tid == 0) p.seg_decay[(long long)bh * p.segments + seg] = gsum;
+}
+
+// ============================================================================
+// Fused output pass.
+// ============================================================================
+template <typename T, int DK, int DVS, bool DIAG>
+__global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(ChunkParams p) {
+  using E = Elem<T>;
+  using C = Cfg<T, DK, DVS>;
+  __shared__ OutSmem<T, DK, DVS, DIAG> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int L = xcd_linear_index(blockIdx.x, p.grid);
+  const int slice = L % p.nslices;
+  const int rest = L / p.nslices;
+  const int seg = rest % p.segments;
+  const int bh = rest / p.segments;
+  const int col0 = slice * DVS;
+  const int wcol = col0 + wave * C::CPW;
+  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
+
+  const T* qg = static_cast<const T*>(p.q) + (long long)bh * p.T * DK;
+  const T* kg = static_cast<const T*>(p.k) + (long long)bh * p.T * DK;
+  const T* vg = static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv;
+  const float* bg = p.b + (long long)bh * p.T;
+  float* og = p.o + (long long)bh * p.T * p.dv;
+
+  // ---- initial state of this segment:  S0, folded with the earlier segments'
+  //      local states:  S <- e^{Gamma_p} S + H_p  for p < seg.
+  StateAcc<T, DK, DVS> S;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = db * 16 + 4 * g + e;
+        const int n = wcol + nb * 16 + r16;
+        S.s[nb][db][e] = p.S0 ? p.S0[((long long)bh * DK + d) * p.dv + n] : 0.0f;
+      }
+  for (int ps = 0; ps < seg; ++ps) {
+    const float f = exp_e(p.seg_decay[(long long)bh * p.segments + ps]);
+    const float* H = p.seg_state + ((long long)bh * (p.segments - 1) + ps) * DK * p.dv;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = db * 16 + 4 * g + e;
+          const int n = wcol + nb * 16 + r16;
+          S.s[nb][db][e] = f * S.s[nb][db][e] + H[(long long)d * p.dv + n];
+        }
+  }
+
+  // The two key tiles that a 32-wide K-step reads above the diagonal, (jb 0, ib 1)
+  // and (jb 2, ib 3), are never written by the loop: zero them once.
+  for (int e = tid; e < 2 * 256; e += C::NT) {
+    const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+    sm.a[(blk * 32 + rr) * C::TLD + blk * 32 + 16 + cc] = E::cvt(0.0f);
+  }
+
+  Staged<T, DK, DVS, true> st;
+  float rb = 0.0f;
+  if (c_begin < c_end) {
+    if (tid < 64) sm.sb[0][tid] = load_b(bg, (long long)c_begin * kChunk, tid, p.T);
+    st.load(qg, kg, vg, (long long)c_begin * kChunk, p.T, p.dv, col0, tid);
+    if (tid < 64 && c_begin + 1 < c_end) rb = load_b(bg, (long long)(c_begin + 1) * kChunk, tid, p.T);
+  }
+  __syncthreads();
+
+  for (int c = c_begin; c < c_end; ++c) {
+    const int buf = (c - c_begin) & 1;
+    const float* sbc = sm.sb[buf];
+    const long long t0 = (long long)c * kChunk;
+
+    // ---- (1) chunk c: registers -> LDS with the tile-relative decay factors
+#pragma unroll
+    for (int m = 0; m < C::QU; ++m) {
+      const int u = tid + m * C::NT;
+      const int row = u / (DK / 8), c8 = u % (DK / 8);
+      const int tile = row >> 4;
+      const float brow = sbc[row];
+      const float rj = tile ? sbc[tile * 16 - 1] : 0.0f;
+      E::store8_scaled(sm.qh + row * C::QLD + c8 * 8, st.q[m], exp_e(brow - rj));
+      const float kref = DIAG ? sbc[tile * 16 + 15] : rj;
+      E::store8_scaled(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(kref - brow));
+      if (DIAG) {
+        E::store8_raw(sm.qr + row * C::QLD + c8 * 8, st.q[m]);
+        E::store8_raw(sm.kr + row * C::QLD + c8 * 8, st.k[m]);
+      }
+    }
+    stage_state_operands<T, DK, DVS, true>(sm.kpt, sm.vt, st, sbc, tid);
+    if (tid < 64) sm.sb[buf ^ 1][tid] = rb;
+
+    // ---- (2) prefetch chunk c + 1 (and b of chunk c + 2) while c is computed
+    if (c + 1 < c_end) st.load(qg, kg, vg, t0 + kChunk, p.T, p.dv, col0, tid);
+    if (tid < 64 && c + 2 < c_end) rb = load_b(bg, t0 + 2 * kChunk, tid, p.T);
+    __syncthreads();
+
+    // ---- (3) attention matrix A of the chunk (bf16 / fp32 in LDS)
+    {
+      constexpr int NBLK = DIAG ? 6 : 10;
+      for (int bi = wave; bi < NBLK; bi += C::NW) {
+        const int jb = DIAG ? kOffJ[bi] : kTriJ[bi];
+        const int ib = DIAG ? kOffI[bi] : kTriI[bi];
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          const typename E::Frag ka = E::load_frag(sm.kh + (ib * 16 + r16) * C::QLD, ks * 32 + 4 * g);
+          const typename E::Frag qb = E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g);
+          E::mfma(acc, ka, qb);
+        }
+        // acc[e] = (Qh_j . Kh_i), j = 16 jb + r16, i = 16 ib + 4 g + e
+        const float rj = jb ? sbc[jb * 16 - 1] : 0.0f;
+        const float ri = DIAG ? sbc[ib * 16 + 15] : (ib ? sbc[ib * 16 - 1] : 0.0f);
+        const float f = (jb == ib) ? 1.0f : exp_e(rj - ri);
+        float vals[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool keep = (jb != ib) || (4 * g + e <= r16);
+          vals[e] = keep ? acc[e] * f : 0.0f;
+        }
+        E::store4(sm.a + (jb * 16 + r16) * C::TLD + ib * 16 + 4 * g, vals[0], vals[1], vals[2], vals[3]);
+      }
+      if (DIAG) {
+        // diagonal tiles by explicit position pairs: A_ji = e^{b_j - b_i} (q_j . k_i), i <= j
+        for (int e = tid; e < 4 * 256; e += C::NT) {
+          const int u = e >> 8, j = (e >> 4) & 15, i = e & 15;
+          float val = 0.0f;
+          if (i <= j) {
+            const T* qrow = sm.qr + (u * 16 + j) * C::QLD;
+            const T* krow = sm.kr + (u * 16 + i) * C::QLD;
+            float dot = 0.0f;
+#pragma unroll 8
+            for (int d = 0; d < DK; ++d) dot += E::to_f32(qrow[d]) * E::to_f32(krow[d]);
+            val = dot * exp_e(sbc[u * 16 + j] - sbc[u * 16 + i]);
+          }
+          sm.a[(u * 16 + j) * C::TLD + u * 16 + i] = E::cvt(val);
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- (4) o = e^{r_u(j)} Qh S_{c-1} + A V  for this wave's columns; then S_c
+    {
+      typename E::Frag Sf[C::NB][C::KS];
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) Sf[nb][ks] = E::from_acc(S.s[nb][2 * ks], S.s[nb][2 * ks + 1]);
+      VFrags<T, DK, DVS> Vf;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          Vf.f[nb][ks] = E::load_frag(sm.vt + (wave * C::CPW + nb * 16 + r16) * C::TLD, ks * 32 + 4 * g);
+
+      floatx4 O[4][C::NB];
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      // inter-chunk: O^T[n][j] = sum_d S[d][n] Qh[j][d]
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const typename E::Frag qb = E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], Sf[nb][ks], qb);
+        }
+      }
+#pragma unroll
+      for (int jb = 1; jb < 4; ++jb) {
+        const float f = exp_e(sbc[jb * 16 - 1]);
+#pragma unroll
+        for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] *= f;
+      }
+      // intra-chunk: O^T[n][j] += sum_i v[n][i] A[j][i], keys up to the end of tile jb
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+        for (int ks = 0; ks <= jb / 2; ++ks) {
+          const typename E::Frag ab = E::load_frag(sm.a + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], Vf.f[nb][ks], ab);
+        }
+      }
+      // lane holds o[t0 + 16 jb + r16][wcol + 16 nb + 4 g + 0..3]
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        const long long t = t0 + jb * 16 + r16;
+        if (t < p.T) {
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb) {
+            float* dst = og + t * p.dv + wcol + nb * 16 + 4 * g;
+            __builtin_nontemporal_store(O[jb][nb], reinterpret_cast<floatx4*>(dst));
+          }
+        }
+      }
+      state_update<T, DK, DVS>(S, Vf, sm.kpt, exp_e(sbc[63]), r16, g);
+    }
+    __syncthreads();
+  }
+
+  if (seg == p.segments - 1) {
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = db * 16 + 4 * g + e;
+          const int n = wcol + nb * 16 + r16;
+          p.ST[((long long)bh * DK + d) * p.dv + n] = S.s[nb][db][e];
+        }
+  }
+}
+
+// ============================================================================
+// Host dispatch.
+// ============================================================================
+namespace {
+
+template <typename T, int DK, int DVS>
+hipError_t seg_launch(const ChunkParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((segment_state_kernel<T, DK, DVS>), dim3(p.grid), dim3(Cfg<T, DK, DVS>::NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int DK, int DVS, bool DIAG>
+hipError_t out_launch(const ChunkParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((chunk_output_kernel<T, DK, DVS, DIAG>), dim3(p.grid), dim3(Cfg<T, DK, DVS>::NT), 0, s,
+                     p);
+  return hipGetLastError();
+}
+
+// Built (dtype, dk, slice) combinations.  fp32 keeps slices <= 64 columns (LDS and
+// registers); the fp32 diagonal-branch path needs dk = 64 (raw q, k in LDS).
+template <typename F>
+hipError_t dispatch(int dtype, int dk, int slice, bool diag, F&& f) {
+#define GLA_CASE(TT, DKV, DVSV)                                                   \
+  if (dk == DKV && slice == DVSV) {                                                \
+    return diag ? f.template operator()<TT, DKV, DVSV, true>()                     \
+                : f.template operator()<TT, DKV, DVSV, false>();                   \
+  }
+  if (dtype == 0) {
+    GLA_CASE(bf16, 128, 128) GLA_CASE(bf16, 128, 64) GLA_CASE(bf16, 128, 32) GLA_CASE(bf16, 128, 16)
+    GLA_CASE(bf16, 64, 64) GLA_CASE(bf16, 64, 32) GLA_CASE(bf16, 64, 16)
+  } else {
+    if (!diag || dk == 64) {
+      GLA_CASE(float, 128, 64) GLA_CASE(float, 128, 32) GLA_CASE(float, 128, 16)
+      GLA_CASE(float, 64, 64) GLA_CASE(float, 64, 32) GLA_CASE(float, 64, 16)
+    }
+  }
+#undef GLA_CASE
+  return hipErrorInvalidValue;
+}
+
+struct OutFn {
+  const ChunkParams& p;
+  hipStream_t s;
+  template <typename T, int DK, int DVS, bool DIAG>
+  hipError_t operator()() const {
+    if constexpr (DIAG && sizeof(T) == 4 && DK == 128) {
+      return hipErrorInvalidValue;
+    } else {
+      return out_launch<T, DK, DVS, DIAG>(p, s);
+    }
+  }
+};
+
+struct SegFn {
+  const ChunkParams& p;
+  hipStream_t s;
+  template <typename T, int DK, int DVS, bool DIAG>
+  hipError_t operator()() const {
+    if constexpr (DIAG) {
+      return hipErrorInvalidValue;  // the pre-pass has no diagonal tiles
+    } else {
+      return seg_launch<T, DK, DVS>(p, s);
+    }
+  }
+};
+
+struct ProbeFn {
+  template <typename T, int DK, int DVS, bool DIAG>
+  hipError_t operator()() const {
+    if constexpr (DIAG && sizeof(T) == 4 && DK == 128) return hipErrorInvalidValue;
+    return hipSuccess;
+  }
+};
+
+}  // namespace
+
+bool chunk_config_built(int dtype, int dk, int slice, bool diag) {
+  return dispatch(dtype, dk, slice, diag, ProbeFn{}) == hipSuccess;
+}
+
+hipError_t launch_segment_states(const ChunkParams& p, int dtype, hipStream_t stream) {
+  if (p.segments <= 1 || p.grid == 0) return hipSuccess;
+  return dispatch(dtype, p.dk, p.dv / p.nslices, false, SegFn{p, stream});
+}
+
+hipError_t launch_chunk_output(const ChunkParams& p, int dtype, bool diag, hipStream_t stream) {
+  if (p.grid == 0) return hipSuccess;
+  return dispatch(dtype, p.dk, p.dv / p.nslices, diag, OutFn{p, stream});
+}
+
+}  // namespace gla

@@ -1,0 +1,97 @@
+// gate_cumsum.hip -- log-decay gate and chunk-local cumulative log-decay.
+//
+// Sources: "Engineering Long-Context Training for Trillion-Parameter MoE Models:
+// Three Key Breakthroughs" (§3.1 the per-position cumulative decay Gamma; §3.2 the
+// gate g = g_min * sigmoid(x) with g_min = -5, replacing g = -softplus(.)).
+//
+// b[t] = sum_{i in chunk(t), i <= t} g(x[i]) is log Gamma restarted at each 64-token
+// chunk.  The chunk kernels read every decay factor they need from b: the
+// tile-start prefix r_u = b[16u - 1], the chunk total gamma = b[63] and
+// differences of entries.  One 64-lane wavefront owns one chunk, lane j owning
+// token j, and forms the inclusive scan with DPP row shifts inside each 16-lane
+// row followed by the three row totals read across lanes.
+#include "gla_device.h"
+#include "gla_internal.h"
+
+namespace gla {
+
+// g = -5 * sigmoid(x), sigmoid evaluated without overflow for either sign of x.
+__device__ __forceinline__ float gate_bounded_sigmoid(float x) {
+  float s;
+  if (x >= 0.0f) {
+    s = 1.0f / (1.0f + exp_e(-x));
+  } else {
+    const float e = exp_e(x);
+    s = e / (1.0f + e);
+  }
+  return -5.0f * s;
+}
+
+// g = -softplus(-x) = -(max(-x, 0) + log1p(e^-|x|)) = log sigmoid(x)
+__device__ __forceinline__ float gate_neg_softplus(float x) {
+  const float z = -x;
+  return -(fmaxf(z, 0.0f) + log1pf(exp_e(-fabsf(z))));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  // row-local lane shift; lanes whose source falls outside the 16-lane row read 0
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
+
+// inclusive prefix sum over the 64 lanes of the wavefront
+__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
+  v += dpp_or_zero<0x111>(v);  // row_shr:1
+  v += dpp_or_zero<0x112>(v);  // row_shr:2
+  v += dpp_or_zero<0x114>(v);  // row_shr:4
+  v += dpp_or_zero<0x118>(v);  // row_shr:8
+  const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+  const int row = lane >> 4;
+  float off = 0.0f;
+  if (row >= 1) off = t0;
+  if (row >= 2) off = off + t1;
+  if (row >= 3) off = off + t2;
+  return v + off;
+}
+
+template <int GATE>
+__global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restrict__ x,
+                                                          float* __restrict__ b, long long T,
+                                                          long long chunks_per_head,
+                                                          long long total_chunks) {
+  const int lane = threadIdx.x & 63;
+  const long long chunk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (chunk >= total_chunks) return;  // uniform across the wavefront
+  const long long bh = chunk / chunks_per_head;
+  const long long t = (chunk - bh * chunks_per_head) * kChunk + lane;
+  const bool valid = t < T;
+  const long long idx = bh * T + t;
+  float g = 0.0f;
+  if (valid) {
+    const float xv = x[idx];
+    g = (GATE == kGateBoundedSigmoid) ? gate_bounded_sigmoid(xv) : gate_neg_softplus(xv);
+  }
+  const float s = wave_inclusive_scan(g, lane);
+  if (valid) b[idx] = s;
+}
+
+hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long T, int gate,
+                              hipStream_t stream) {
+  const long long cph = (T + kChunk - 1) / kChunk;
+  const long long total = BH * cph;
+  if (total == 0) return hipSuccess;
+  const long long blocks = (total + 3) / 4;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  if (gate == kGateBoundedSigmoid)
+    hipLaunchKernelGGL(gate_cumsum_kernel<kGateBoundedSigmoid>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, x, b, T, cph, total);
+  else
+    hipLaunchKernelGGL(gate_cumsum_kernel<kGateNegSoftplus>, dim3((unsigned)blocks), dim3(256), 0,
+                       stream, x, b, T, cph, total);
+  return hipGetLastError();
+}
+
+}  // namespace gla

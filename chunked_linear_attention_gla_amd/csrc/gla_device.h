@@ -1,0 +1,159 @@
+// gla_device.h -- device-side building blocks for the gfx950 (CDNA4) GLA kernels.
+//
+// MFMA fragment convention used by every kernel in this library.
+// A 16x16 output tile is produced by v_mfma_f32_16x16x32_bf16 (bf16 operands)
+// or by eight v_mfma_f32_16x16x4_f32 (fp32 operands).  Lane l = 16*g + r
+// (g = l / 16 in 0..3, r = l % 16) holds, for a K-step of 32 starting at k0,
+// eight operand elements e = 0..7 at the logical contraction indices
+//     kappa(g, e) = k0 + 16*(e / 4) + 4*g + (e % 4),
+// for row/column r of its operand.  kappa is a permutation of k0..k0+31, so any
+// such assignment computes the same sum as long as both operands use it.  This
+// one is chosen because the accumulator of a 16x16 tile holds rows 4g..4g+3 of
+// column r in lane l: two vertically adjacent accumulator tiles are therefore
+// already a K-step fragment, and the state S (an accumulator) feeds the q.S
+// product and the attention matrix feeds A.V without any shuffle.
+//   bf16: the 8 elements are the hardware K positions 8g..8g+7 of one 16x16x32.
+//   fp32: element e is the (lane-group g) K position of the e-th 16x16x4.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gla {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 64;  // tokens per chunk
+constexpr int kTile = 16;   // tokens per tile (the bounded-decay safe length)
+
+// e^x as 2^(x log2 e) on the hardware exp2 (v_exp_f32).  e^-inf = 0, e^+inf = inf.
+__device__ __forceinline__ float exp_e(float x) {
+  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// ---------------------------------------------------------------- element traits
+
+template <typename T> struct Elem;
+
+template <> struct Elem<bf16> {
+  // 8 consecutive elements as loaded from global memory (16 bytes)
+  struct Vec8 { uint4 u; };
+  struct Frag { bf16x8 v; };
+  static constexpr int kPad = 8;  // LDS row padding in elements (16 bytes)
+
+  __device__ static __forceinline__ Vec8 zero8() { Vec8 r; r.u = make_uint4(0, 0, 0, 0); return r; }
+  __device__ static __forceinline__ Vec8 load8(const bf16* p) {
+    Vec8 r; r.u = *reinterpret_cast<const uint4*>(p); return r;
+  }
+  __device__ static __forceinline__ float get(const Vec8& v, int e) {
+    const uint32_t w = (e < 2) ? v.u.x : (e < 4) ? v.u.y : (e < 6) ? v.u.z : v.u.w;
+    return bf16_bits_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+  __device__ static __forceinline__ bf16 cvt(float f) { return static_cast<bf16>(f); }
+  // store 8 scaled elements as one 16-byte LDS write
+  __device__ static __forceinline__ void store8_scaled(bf16* dst, const Vec8& v, float s) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = cvt(get(v, e) * s);
+    *reinterpret_cast<bf16x8*>(dst) = o;
+  }
+  __device__ static __forceinline__ void store8_raw(bf16* dst, const Vec8& v) {
+    *reinterpret_cast<uint4*>(dst) = v.u;
+  }
+  // two 4-element (8-byte) LDS reads at cols c and c + 16 of one row
+  __device__ static __forceinline__ Frag load_frag(const bf16* row, int c) {
+    const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + c);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + c + 16);
+    Frag f;
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+  }
+  __device__ static __forceinline__ Frag from_acc(const floatx4& a, const floatx4& b) {
+    Frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { f.v[e] = cvt(a[e]); f.v[4 + e] = cvt(b[e]); }
+    return f;
+  }
+  __device__ static __forceinline__ void store4(bf16* dst, float a, float b, float c, float d) {
+    bf16x4 o;
+    o[0] = cvt(a); o[1] = cvt(b); o[2] = cvt(c); o[3] = cvt(d);
+    *reinterpret_cast<bf16x4*>(dst) = o;
+  }
+  __device__ static __forceinline__ void mfma(floatx4& acc, const Frag& a, const Frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+};
+
+template <> struct Elem<float> {
+  struct Vec8 { float4 a, b; };
+  struct Frag { floatx4 lo, hi; };
+  static constexpr int kPad = 4;  // 16 bytes
+
+  __device__ static __forceinline__ Vec8 zero8() {
+    Vec8 r; r.a = make_float4(0, 0, 0, 0); r.b = r.a; return r;
+  }
+  __device__ static __forceinline__ Vec8 load8(const float* p) {
+    Vec8 r;
+    r.a = *reinterpret_cast<const float4*>(p);
+    r.b = *reinterpret_cast<const float4*>(p + 4);
+    return r;
+  }
+  __device__ static __forceinline__ float get(const Vec8& v, int e) {
+    switch (e) {
+      case 0: return v.a.x; case 1: return v.a.y; case 2: return v.a.z; case 3: return v.a.w;
+      case 4: return v.b.x; case 5: return v.b.y; case 6: return v.b.z; default: return v.b.w;
+    }
+  }
+  __device__ static __forceinline__ float cvt(float f) { return f; }
+  __device__ static __forceinline__ void store8_scaled(float* dst, const Vec8& v, float s) {
+    float4 a = v.a, b = v.b;
+    a.x *= s; a.y *= s; a.z *= s; a.w *= s;
+    b.x *= s; b.y *= s; b.z *= s; b.w *= s;
+    *reinterpret_cast<float4*>(dst) = a;
+    *reinterpret_cast<float4*>(dst + 4) = b;
+  }
+  __device__ static __forceinline__ void store8_raw(float* dst, const Vec8& v) {
+    *reinterpret_cast<float4*>(dst) = v.a;
+    *reinterpret_cast<float4*>(dst + 4) = v.b;
+  }
+  __device__ static __forceinline__ Frag load_frag(const float* row, int c) {
+    Frag f;
+    f.lo = *reinterpret_cast<const floatx4*>(row + c);
+    f.hi = *reinterpret_cast<const floatx4*>(row + c + 16);
+    return f;
+  }
+  __device__ static __forceinline__ Frag from_acc(const floatx4& a, const floatx4& b) {
+    Frag f; f.lo = a; f.hi = b; return f;
+  }
+  __device__ static __forceinline__ void store4(float* dst, float a, float b, float c, float d) {
+    floatx4 o = {a, b, c, d};
+    *reinterpret_cast<floatx4*>(dst) = o;
+  }
+  __device__ static __forceinline__ void mfma(floatx4& acc, const Frag& a, const Frag& b) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo[s], b.lo[s], acc, 0, 0, 0);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[s], b.hi[s], acc, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f32(float x) { return x; }
+};
+
+// Workgroup index -> linear work index, so that consecutive work indices land on
+// the same XCD.  The dispatcher hands workgroups to the 8 XCDs round-robin
+// (workgroup w runs on XCD w % 8); grouping consecutive work items on one XCD
+// lets value-column slices of the same head share q and k through that XCD's L2.
+__device__ __forceinline__ int xcd_linear_index(int w, int G) {
+  const int x = w & 7, y = w >> 3;
+  const int base = G >> 3, rem = G & 7;
+  return x * base + (x < rem ? x : rem) + y;
+}
+
+}  // namespace gla

@@ -1,0 +1,190 @@
+/*
+ * gla.h -- C ABI of the MI355X (gfx950) chunked gated-linear-attention forward pass.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [LCT] "Engineering Long-Context Training for Trillion-Parameter MoE Models:
+ *          Three Key Breakthroughs"
+ *   [STM] "Scaling Trillion-Parameter MoE and Long-Context LLMs: Architecture
+ *          and Engineering in Practice"
+ *   [ESU] "Engineering Stability in Ultra-Long Context and Trillion-Parameter
+ *          Sparse Models"
+ *
+ * Operation.  Linear attention with a scalar per-(batch, head, token) decay,
+ * computed chunk by chunk: matrix products inside each chunk and a state
+ * carried from chunk to chunk [LCT §3.1], [ESU §2.1].  For each head,
+ *     S_{-1} = S0,   S_t = a_t S_{t-1} + k_t v_t^T,   o_t = S_t^T q_t,
+ *     S_T = S_{T-1},  a_t = exp(g_t),
+ * where the log-decay is g = -5 * sigmoid(x), the bounded "scaled sigmoid" of
+ * [LCT §3.2] / [STM §II] / [ESU §2.2], or, for the ablation only, the
+ * conventional unbounded negative softplus, g = -softplus(-x) = log sigmoid(x).
+ * o_t includes token t itself; the initial state is decayed by a_0.  q is used
+ * as given (no internal scale).
+ *
+ * The product path (GLA_GATE_BOUNDED_SIGMOID + GLA_PATH_UNIFIED) relies on the
+ * bound: inside every 16-token tile the reciprocal cumulative decay stays below
+ * e^80, so all causal tiles of a chunk, diagonal ones included, go through the
+ * same dense matrix-core product [LCT §3.2, §3.3], [ESU §2.2].
+ * GLA_PATH_DIAG_BRANCH is the conventional design of [LCT §3.1] / [ESU §2.1]:
+ * diagonal tiles take an explicit element-wise position-pair path.  It exists
+ * so the difference can be measured.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are device memory owned by the caller, row-major and
+ *     contiguous:
+ *       q, k [B][H][T][dk]      v [B][H][T][dv]     (dtype: bf16 or fp32)
+ *       x, b [B][H][T]          fp32
+ *       S0, S_T [B][H][dk][dv]  fp32                (S0 may be NULL: zero state)
+ *       o [B][H][T][dv]         fp32
+ *     q, k, v, o, S0, S_T must be 16-byte aligned; x and b 4-byte aligned.
+ *   - The library allocates nothing and keeps no per-call state.  Work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the default stream) and the
+ *     host is never synchronised: outputs are valid once the stream reaches
+ *     that point.  Calls on different streams are safe when their output and
+ *     workspace buffers are disjoint.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     rejected call enqueues nothing and writes nothing.  A HIP launch error
+ *     is reported as GLA_ERR_HIP.  No C++ exception crosses this boundary.
+ *   - T may be any value >= 0.  Sequences are processed in chunks of
+ *     GLA_CHUNK tokens; a final partial chunk is handled in place (tokens past
+ *     T are treated as absent).  T = 0 writes S_T = S0 (or zeros) and no o.
+ *   - Supported sizes: dk in {64, 128}, dv in {64, 128}, B >= 1, H >= 1.
+ *     The fp32 diagonal-branch path additionally needs dk == 64.
+ */
+#ifndef GLA_H_
+#define GLA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GLA_ABI_VERSION 1
+#define GLA_CHUNK 64          /* tokens per chunk */
+#define GLA_TILE 16           /* tokens per tile inside a chunk [LCT §3.2] */
+#define GLA_MAX_SEGMENTS 16   /* upper bound on gla_plan_t.segments */
+
+typedef enum {
+  GLA_OK = 0,
+  GLA_ERR_NULL = 1,        /* a required pointer is NULL */
+  GLA_ERR_SHAPE = 2,       /* B, H, T, dk or dv out of the supported range */
+  GLA_ERR_DTYPE = 3,       /* unknown dtype */
+  GLA_ERR_ALIAS = 4,       /* an output overlaps an input or another output */
+  GLA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  GLA_ERR_HIP = 6,         /* a HIP runtime call or kernel launch failed */
+  GLA_ERR_PLAN = 7,        /* plan fields invalid for these sizes */
+  GLA_ERR_ALIGN = 8,       /* a pointer violates the alignment rule */
+  GLA_ERR_ARG = 9,         /* unknown gate or path enum value */
+  GLA_ERR_UNSUPPORTED = 10 /* valid enums, but this combination is not built */
+} gla_status_t;
+
+typedef enum { GLA_BF16 = 0, GLA_F32 = 1 } gla_dtype_t;   /* storage of q, k, v */
+
+/* Log-decay g(x) [LCT §3.2]. */
+typedef enum {
+  GLA_GATE_BOUNDED_SIGMOID = 0, /* g = -5 * sigmoid(x), range (-5, 0) (the product) */
+  GLA_GATE_NEG_SOFTPLUS = 1     /* g = -softplus(-x) = log sigmoid(x), range (-inf, 0) */
+} gla_gate_t;
+
+/* How the causal tiles of a chunk are computed. */
+typedef enum {
+  GLA_PATH_UNIFIED = 0,     /* every causal 16x16 tile on MFMA: q*Gamma, k/Gamma (product) */
+  GLA_PATH_DIAG_BRANCH = 1  /* off-diagonal tiles on MFMA, diagonal tiles element-wise (ablation) */
+} gla_path_t;
+
+/* Launch plan.  Each head's value columns are cut into dv_split slices and its
+ * sequence into `segments` contiguous runs of chunks (segment p owns chunks
+ * [p*nc/segments, (p+1)*nc/segments), nc = ceil(T/64)); every (head, slice,
+ * segment) is one workgroup.  segments > 1 adds a pre-pass that computes each
+ * segment's local final state (gla_segment_states).  Results do not depend on
+ * the plan beyond floating-point summation order. */
+typedef struct {
+  int segments;  /* 1 .. GLA_MAX_SEGMENTS, and at most the number of chunks (>= 1 when T = 0) */
+  int dv_split;  /* 1, 2, 4 or 8 with dv / dv_split in {16, 32, 64, 128} */
+} gla_plan_t;
+
+/* Human-readable name of a status code (static storage). */
+const char* gla_status_string(gla_status_t status);
+
+/* GLA_ABI_VERSION of the built library. */
+int gla_abi_version(void);
+
+/* Default plan for the current HIP device (queries its compute-unit count).
+ * Returns GLA_ERR_HIP when no device is usable. */
+gla_status_t gla_plan_default(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                              gla_path_t path, gla_plan_t* plan);
+
+/* Validates a plan for these sizes without touching the device. */
+gla_status_t gla_plan_check(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                            gla_path_t path, const gla_plan_t* plan);
+
+/* Bytes of segment workspace that gla_segment_states writes and
+ * gla_chunk_output reads for `plan` (0 when plan->segments == 1).  Host only. */
+gla_status_t gla_segment_workspace_size(int B, int H, long long T, int dk, int dv,
+                                        const gla_plan_t* plan, size_t* bytes);
+
+/* Bytes of workspace gla_chunk_fwd needs: the chunk-local cumulative log-decay
+ * b (B*H*T fp32) plus the segment workspace of `plan`.  plan == NULL means the
+ * default plan of the current device (a HIP query).  Host only, enqueues nothing. */
+gla_status_t gla_workspace_size(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                                gla_path_t path, const gla_plan_t* plan, size_t* bytes);
+
+/* Gate and chunk-local cumulative log-decay [LCT §3.1, §3.2].
+ *   b[t] = sum over the tokens i of t's 64-token chunk with i <= t of g(x[i]),
+ * i.e. log Gamma restarted at every chunk boundary, computed by one 64-lane
+ * wavefront scan per chunk.  x and b: [B][H][T] fp32 (b may not overlap x).
+ * Non-finite x follows the gate's limits: x = +inf gives g = -5 (bounded) or
+ * 0 (softplus); x = -inf gives g = 0 (bounded) or -inf (softplus); NaN gives NaN. */
+gla_status_t gla_gate_cumsum(const float* x, float* b, int B, int H, long long T,
+                             gla_gate_t gate, void* stream);
+
+/* Segment pre-pass (only meaningful when plan->segments > 1).  For every head
+ * and every segment p but the last, runs the state recurrence over the
+ * segment's chunks from a zero state and stores its final state H_p and its
+ * total log-decay Gamma_p into `seg_ws` (gla_segment_workspace_size bytes).
+ * Uses k, v and b (from gla_gate_cumsum).  Does nothing when segments == 1. */
+gla_status_t gla_segment_states(const void* k, const void* v, const float* b,
+                                int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                                const gla_plan_t* plan, void* seg_ws, size_t seg_ws_bytes,
+                                void* stream);
+
+/* Fused chunk output pass: for every chunk, the intra-chunk causal product
+ * (q*Gamma)(k/Gamma)^T V, the inter-chunk term (q*Gamma) S, and the decayed
+ * state update, o written once, S_T written by the last segment [LCT §3.1-§3.3].
+ * b from gla_gate_cumsum; seg_ws from gla_segment_states with the same plan
+ * (ignored when plan->segments == 1).  S0 may be NULL.  o and S_T must not
+ * overlap any input; S_T must not overlap S0. */
+gla_status_t gla_chunk_output(const void* q, const void* k, const void* v, const float* b,
+                              const float* S0, float* o, float* S_T,
+                              int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                              gla_path_t path, const gla_plan_t* plan,
+                              const void* seg_ws, size_t seg_ws_bytes, void* stream);
+
+/* The whole forward pass: gla_gate_cumsum, gla_segment_states (when the plan
+ * has several segments) and gla_chunk_output, enqueued in that order on
+ * `stream` with the default plan of the current device.
+ *   workspace == NULL: *workspace_bytes receives the required size; nothing is
+ *                      enqueued (this queries the device for the plan).
+ *   otherwise:         *workspace_bytes is the caller's workspace size; a
+ *                      smaller value than required returns GLA_ERR_WORKSPACE.
+ * The workspace is device memory, 256-byte aligned, owned by the caller, and
+ * must not overlap any argument. */
+gla_status_t gla_chunk_fwd(const void* q, const void* k, const void* v, const float* x,
+                           const float* S0, float* o, float* S_T,
+                           int B, int H, long long T, int dk, int dv,
+                           gla_dtype_t dtype, gla_gate_t gate, gla_path_t path,
+                           void* workspace, size_t* workspace_bytes, void* stream);
+
+/* gla_chunk_fwd with an explicit plan (NULL = default plan). */
+gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, const float* x,
+                                const float* S0, float* o, float* S_T,
+                                int B, int H, long long T, int dk, int dv,
+                                gla_dtype_t dtype, gla_gate_t gate, gla_path_t path,
+                                const gla_plan_t* plan,
+                                void* workspace, size_t* workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GLA_H_ */

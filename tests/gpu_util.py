@@ -1,0 +1,48 @@
+"""Helpers shared by the GPU parity tests: run the HIP path and the CPU oracle on the
+same seeded inputs and compare them."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from chunked_linear_attention_gla_amd import inputs as gin
+
+# Tolerances of the comparison, max |gpu - ref| / max |ref| over each whole tensor:
+# 2e-2 for bf16 operands and 1e-4 for the fp32 path, on o and on the final state.
+TOL = {"bf16": 2e-2, "f32": 1e-4}
+
+
+def device():
+    if not torch.cuda.is_available():
+        import pytest
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def oracle_heads(inp, heads=None, gate="bounded", T=None, S0=None):
+    """fp64 oracle on flat head indices `heads` (default all) and the first T tokens."""
+    q, k, v, x = inp["q"], inp["k"], inp["v"], inp["x"]
+    B, H, Tfull, dk = q.shape
+    dv = v.shape[-1]
+    T = Tfull if T is None else T
+    idx = list(range(B * H)) if heads is None else list(heads)
+    sel = lambda t: t.reshape(B * H, *t.shape[2:])[idx]
+    s0 = inp["S0"] if S0 is None else S0
+    s0n = None if s0 is None else sel(s0).detach().cpu().numpy().astype(np.float64)
+    o, ST = oracle.forward(gin.to_numpy_bits(sel(q)[:, :T]), gin.to_numpy_bits(sel(k)[:, :T]),
+                           gin.to_numpy_bits(sel(v)[:, :T]), gin.to_numpy_bits(sel(x)[:, :T]),
+                           s0n, gate=gate)
+    return o, ST
+
+
+def gpu_heads(t, heads, T=None):
+    B, H = t.shape[:2]
+    flat = t.reshape(B * H, *t.shape[2:])[list(heads)]
+    if T is not None:
+        flat = flat[:, :T]
+    return flat.detach().cpu().double().numpy()
+
+
+def rel(got, ref):
+    return oracle.max_rel_err(got, ref)

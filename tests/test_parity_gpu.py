@@ -1,0 +1,183 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle on the
+same seeded inputs.  Bar: max |gpu - ref| / max |ref| <= 2e-2 with bf16 operands,
+<= 1e-4 on the fp32 path, separately for o and the final state S_T."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import chunked_linear_attention_gla_amd as gla
+from chunked_linear_attention_gla_amd import inputs as gin
+from gpu_util import TOL, device, gpu_heads, oracle_heads, rel
+
+pytestmark = pytest.mark.gpu
+
+SMALL = gin.WORKLOADS["bf16_8k"]
+
+
+def small(T, H=3, B=1, dk=128, dv=128, qkv="bf16", x_mean=0.0, x_std=1.0, s0=0.1, seed=7, x_const=None,
+          gate="bounded"):
+    w = SMALL.with_(B=B, H=H, T=T, dk=dk, dv=dv, qkv_dtype=qkv, x_mean=x_mean, x_std=x_std, s0_std=s0,
+                    seed=seed, gate=gate)
+    return w, gin.make_inputs(w, device(), x_const=x_const)
+
+
+def check(inp, w, plan=None, path="unified", gate="bounded", tol=None):
+    o, ST = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], gate=gate, path=path, plan=plan)
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle_heads(inp, gate=gate)
+    B, H, T, dv = o.shape
+    got_o = o.reshape(B * H, T, dv).cpu().double().numpy()
+    got_s = ST.reshape(B * H, *ST.shape[2:]).cpu().double().numpy()
+    tol = TOL[w.qkv_dtype] if tol is None else tol
+    eo, es = rel(got_o, o_ref), rel(got_s, S_ref)
+    assert np.isfinite(got_o).all() and np.isfinite(got_s).all()
+    assert eo <= tol and es <= tol, (eo, es)
+    return eo, es
+
+
+# ------------------------------------------------------------------------------ gate + cumsum
+
+@pytest.mark.parametrize("gate", ["bounded", "neg_softplus"])
+@pytest.mark.parametrize("T", [1, 64, 100, 1000])
+def test_gate_cumsum_matches_fp64(gate, T):
+    dev = device()
+    g = torch.Generator(device=dev).manual_seed(3)
+    x = torch.randn(2, 3, T, device=dev, generator=g) * 3.0
+    x[0, 0, 0] = float("inf")
+    x[1, 2, -1] = float("-inf") if gate == "bounded" else 50.0
+    b = gla.gate_cumsum(x, gate=gate)
+    torch.cuda.synchronize()
+    xn = x.cpu().numpy()
+    ref = oracle.chunk_local_cumsum(np.pad(oracle.gate(xn, gate), [(0, 0), (0, 0), (0, (-T) % 64)]))[..., :T]
+    got = b.cpu().double().numpy()
+    assert np.all(np.abs(got - ref) <= 1e-6 * np.abs(ref) + 1e-6)
+
+
+def test_bounded_gate_tile_sums_above_minus_80():
+    dev = device()
+    g = torch.Generator(device=dev).manual_seed(4)
+    x = torch.randn(1, 4, 4096, device=dev, generator=g) + 4.0  # strong decay
+    b = gla.gate_cumsum(x).cpu().double().numpy().reshape(4, -1, 4, 16)
+    prev = np.concatenate([np.zeros_like(b[..., :1, -1:]), b[..., :-1, -1:]], axis=-2)
+    tile_sums = b[..., -1:] - prev  # chunk-local: each tile's own sum
+    assert np.all(tile_sums > -80.0)
+
+
+# ------------------------------------------------------------------------------ forward parity
+
+@pytest.mark.parametrize("T", [64, 200, 640, 1000])
+def test_bf16_default_plan(T):
+    w, inp = small(T)
+    check(inp, w)
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 64), (64, 128), (128, 64)])
+def test_bf16_other_head_dims(dk, dv):
+    w, inp = small(300, dk=dk, dv=dv)
+    check(inp, w)
+
+
+@pytest.mark.parametrize("plan", [(1, 1), (1, 2), (1, 4), (1, 8), (2, 1), (3, 2), (4, 4), (7, 8), (16, 2)])
+def test_bf16_every_plan(plan):
+    w, inp = small(16 * 64 + 17, H=2)
+    check(inp, w, plan=gla.Plan(*plan))
+
+
+def test_fp32_path_small_workload():
+    w = gin.WORKLOADS["fp32_small"]
+    inp = gin.make_inputs(w, device())
+    check(inp, w)
+
+
+@pytest.mark.parametrize("plan", [(1, 1), (2, 2), (4, 4)])
+@pytest.mark.parametrize("dk", [64, 128])
+def test_fp32_path_plans(plan, dk):
+    w, inp = small(64 * 7 + 9, H=2, dk=dk, dv=64, qkv="f32")
+    check(inp, w, plan=gla.Plan(*plan))
+
+
+@pytest.mark.parametrize("regime", ["weak", "unit", "strong"])
+def test_decay_regimes(regime):
+    # weak decay (a ~ 0.99) and unit decay (a = 1) make the carried state dominate o,
+    # so a broken inter-chunk path or segment hand-over cannot hide under the tolerance
+    kw = dict(weak=dict(x_mean=-6.0), unit=dict(x_const=float("-inf")), strong=dict(x_mean=4.0))[regime]
+    w, inp = small(2048 + 64 * 3, H=4, **kw)
+    check(inp, w)
+    check(inp, w, plan=gla.Plan(8, 2))
+
+
+def test_zero_initial_state():
+    w, inp = small(500, s0=0.0)
+    assert inp["S0"] is None
+    check(inp, w)
+
+
+def test_empty_sequence_returns_initial_state():
+    w, inp = small(0)
+    o, ST = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"])
+    torch.cuda.synchronize()
+    assert o.shape[2] == 0
+    assert torch.equal(ST, inp["S0"])
+    w, inp = small(0, s0=0.0)
+    o, ST = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], None)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(ST).item() == 0
+
+
+@pytest.mark.parametrize("T", [1, 15, 63, 65])
+def test_short_and_ragged(T):
+    w, inp = small(T, H=2)
+    check(inp, w)
+
+
+def test_many_heads_batch():
+    w, inp = small(256, B=5, H=7)
+    check(inp, w)
+
+
+def test_chaining_matches_single_call():
+    w, inp = small(64 * 20, H=2, x_mean=-5.0)
+    o, ST = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"])
+    T1 = 64 * 7
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    o1, S1 = gla.chunk_fwd(*(sl(inp[n], 0, T1) for n in "qkvx"), inp["S0"])
+    o2, S2 = gla.chunk_fwd(*(sl(inp[n], T1, None) for n in "qkvx"), S1)
+    torch.cuda.synchronize()
+    assert rel(torch.cat([o1, o2], 2).cpu().numpy(), o.cpu().numpy()) <= 1e-5
+    assert rel(S2.cpu().numpy(), ST.cpu().numpy()) <= 1e-5
+
+
+def test_repeat_calls_are_bitwise_identical():
+    w, inp = small(64 * 33, H=4)
+    plan = gla.Plan(4, 4)
+    o1, S1 = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], plan=plan)
+    o2, S2 = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], plan=plan)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+# ------------------------------------------------------------------------------ ablation path
+
+@pytest.mark.parametrize("gate,x_mean", [("neg_softplus", -4.0), ("neg_softplus", 0.0), ("bounded", 4.0)])
+def test_diag_branch_matches_oracle(gate, x_mean):
+    w, inp = small(64 * 9 + 5, H=3, x_mean=x_mean, gate=gate)
+    check(inp, w, path="diag_branch", gate=gate)
+    check(inp, w, path="diag_branch", gate=gate, plan=gla.Plan(3, 4))
+
+
+def test_diag_branch_fp32():
+    w, inp = small(64 * 4 + 3, H=2, dk=64, dv=64, qkv="f32", x_mean=-4.0, gate="neg_softplus")
+    check(inp, w, path="diag_branch", gate="neg_softplus")
+
+
+def test_forced_overflow_breaks_only_the_unified_factorisation():
+    """x = -6 under the softplus gate gives g ~ -6.0025, a tile sum near -96, and a
+    reciprocal e^96 beyond fp32: the unified factorisation overflows, the
+    diagonal-branch path (all factors <= 1) still matches the oracle."""
+    w, inp = small(256, H=2, x_const=-6.0, gate="neg_softplus")
+    o_u, S_u = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], gate="neg_softplus",
+                             path="unified")
+    torch.cuda.synchronize()
+    assert not torch.isfinite(o_u).all()
+    check(inp, w, path="diag_branch", gate="neg_softplus")
