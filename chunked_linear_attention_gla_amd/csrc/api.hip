@@ -28,7 +28,8 @@ gla_status_t check_sizes(int B, int H, long long T, int dk, int dv) {
   if (dv != 64 && dv != 128) return GLA_ERR_SHAPE;
   const long long BH = (long long)B * H;
   if (BH > (1LL << 24)) return GLA_ERR_SHAPE;
-  if (n_chunks(T) > (1LL << 30)) return GLA_ERR_SHAPE;
+  // one head's q, k, v or o must fit a 32-bit buffer descriptor
+  if ((unsigned long long)T * (unsigned long long)std::max(dk, dv) * 4ULL > 0xFFFF0000ULL) return GLA_ERR_SHAPE;
   return GLA_OK;
 }
 
@@ -74,19 +75,25 @@ size_t seg_bytes(long long BH, int dk, int dv, int segments) {
          align_up((size_t)BH * (size_t)segments * 4);
 }
 
-// Default plan.  Value slices share q/k through L2, segments cost a second read of
-// k and v for all but the last segment, so: as few segments as fill the device,
-// value slices of 64 columns (32 for dv = 64).
+// Default plan.  Measured on MI355X (256 CUs): one workgroup per CU, each owning a
+// full-width value slice, is fastest; segments are added until the grid covers the
+// CUs (a segment costs one extra read of k and v, a narrower value slice costs a
+// re-read of q and k and a repeated q.k^T).  The fp32 kernels are built for
+// slices of at most 64 columns.
 gla_status_t default_plan_for(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype, gla_path_t path,
                               int cus, gla_plan_t* plan) {
   const long long BH = (long long)B * H;
   const long long nc = n_chunks(T);
-  int split = dv == 128 ? 2 : 2;  // 64-column slices for dv = 128, 32 for dv = 64
-  if (dtype == GLA_F32) split = dv / 64;  // fp32 kernels are built for slices <= 64
-  const long long target = 2LL * cus;     // workgroups wanted in flight
+  int split = 1;
+  if (dtype == GLA_F32) split = dv / 64;
   long long units = BH * split;
+  // too few heads to fill the device even with segments: narrow the value slices
+  while (units * GLA_MAX_SEGMENTS < cus && dv / (split * 2) >= 32 && dtype == GLA_BF16) {
+    split *= 2;
+    units *= 2;
+  }
   int segs = 1;
-  while (segs < GLA_MAX_SEGMENTS && units * segs < target && nc / (2LL * segs) >= 8) segs *= 2;
+  while (segs < GLA_MAX_SEGMENTS && units * segs < cus && nc / (2LL * segs) >= 4) segs *= 2;
   if (segs > std::max(1LL, nc)) segs = (int)std::max(1LL, nc);
   plan->segments = segs;
   plan->dv_split = split;

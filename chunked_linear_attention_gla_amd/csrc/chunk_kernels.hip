@@ -61,31 +61,41 @@ struct Cfg {
 template <typename T, int DK, int DVS, bool DIAG>
 struct OutSmem {
   using C = Cfg<T, DK, DVS>;
-  T qh[64 * C::QLD];    // Qh[j][d]                 row-major
-  T kh[64 * C::QLD];    // Kh[i][d]                 row-major
-  T kpt[DK * C::TLD];   // (k_i e^{gamma-b_i})[d][i] token-contiguous
-  T vt[DVS * C::TLD];   // v[n][i]                  token-contiguous
-  T a[64 * C::TLD];     // A[j][i]                  row-major
-  T qr[DIAG ? 64 * C::QLD : 1];  // raw q, diagonal-branch path only
-  T kr[DIAG ? 64 * C::QLD : 1];  // raw k, diagonal-branch path only
-  float sb[2][64];      // b of the current and the next chunk
+  T qh[64 * C::QLD];                 // Qh[j][d]  row-major
+  T kh[64 * C::QLD];                 // Kh[i][d]  row-major
+  T kp[TokTile<T, DK>::SIZE];        // k_i e^{gamma - b_i}, token-major tile
+  T vv[TokTile<T, DVS>::SIZE];       // v, token-major tile
+  T a[64 * C::TLD];                  // A[j][i]   row-major
+  T qr[DIAG ? 64 * C::QLD : 1];      // raw q, diagonal-branch path only
+  T kr[DIAG ? 64 * C::QLD : 1];      // raw k, diagonal-branch path only
+  float sb[2][64];                   // b of the current and the next chunk
 };
 
 template <typename T, int DK, int DVS>
 struct SegSmem {
-  using C = Cfg<T, DK, DVS>;
-  T kpt[DK * C::TLD];
-  T vt[DVS * C::TLD];
+  T kp[TokTile<T, DK>::SIZE];
+  T vv[TokTile<T, DVS>::SIZE];
   float sb[2][64];
 };
 
-// Causal 16x16 tiles of a 64x64 chunk: (query tile jb, key tile ib), ib <= jb.
-__device__ __constant__ const int kTriJ[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__device__ __constant__ const int kTriI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-__device__ __constant__ const int kOffJ[6] = {1, 2, 2, 3, 3, 3};
-__device__ __constant__ const int kOffI[6] = {0, 0, 1, 0, 1, 2};
+// Causal 16x16 tiles of a 64x64 chunk, (query tile jb, key tile ib) with ib <= jb,
+// numbered row by row: 0 -> (0,0), 1 -> (1,0), 2 -> (1,1), 3 -> (2,0), ...  The
+// strictly-below-diagonal tiles are numbered the same way without the diagonal.
+// Evaluated at compile time inside unrolled loops (no table in memory).
+__host__ __device__ constexpr int tri_j(int t) { return t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0; }
+__host__ __device__ constexpr int tri_i(int t) { return t - tri_j(t) * (tri_j(t) + 1) / 2; }
+__host__ __device__ constexpr int off_j(int t) { return t >= 3 ? 3 : t >= 1 ? 2 : 1; }
+__host__ __device__ constexpr int off_i(int t) { return t - (off_j(t) - 1) * off_j(t) / 2; }
+static_assert(tri_j(9) == 3 && tri_i(9) == 3 && tri_j(4) == 2 && tri_i(4) == 1, "tile numbering");
+static_assert(off_j(5) == 3 && off_i(5) == 2 && off_j(2) == 2 && off_i(2) == 1, "tile numbering");
 
-// Per-thread registers holding one chunk of q, k, v on its way to LDS.
+// Per-head buffer descriptors of the streamed tensors.
+struct HeadBuffers {
+  rsrc_t q, k, v, b, o;
+};
+
+// Per-thread registers holding one chunk of q, k, v on its way to LDS.  Rows past
+// the end of the sequence read as zeros (buffer range check).
 template <typename T, int DK, int DVS, bool LOAD_Q>
 struct Staged {
   using E = Elem<T>;
@@ -94,61 +104,52 @@ struct Staged {
   typename E::Vec8 k[C::QU];
   typename E::Vec8 v[C::VU];
 
-  __device__ __forceinline__ void load(const T* qg, const T* kg, const T* vg, long long t0, long long len,
-                                       int dv, int col0, int tid) {
-    const bool full = t0 + kChunk <= len;
+  __device__ __forceinline__ void load(const HeadBuffers& hb, uint32_t t0, int dv, int col0, int tid) {
 #pragma unroll
     for (int m = 0; m < C::QU; ++m) {
       const int u = tid + m * C::NT;
       const int row = u / (DK / 8), c8 = u % (DK / 8);
-      const long long off = (t0 + row) * DK + c8 * 8;
-      const bool ok = full || (t0 + row < len);
-      if (LOAD_Q) q[m] = ok ? E::load8(qg + off) : E::zero8();
-      k[m] = ok ? E::load8(kg + off) : E::zero8();
+      const uint32_t off = ((t0 + row) * DK + c8 * 8) * (uint32_t)sizeof(T);
+      if (LOAD_Q) q[m] = E::load8(hb.q, off);
+      k[m] = E::load8(hb.k, off);
     }
 #pragma unroll
     for (int m = 0; m < C::VU; ++m) {
       const int u = tid + m * C::NT;
       const int row = u / (DVS / 8), c8 = u % (DVS / 8);
-      const bool ok = full || (t0 + row < len);
-      v[m] = ok ? E::load8(vg + (t0 + row) * dv + col0 + c8 * 8) : E::zero8();
+      v[m] = E::load8(hb.v, ((t0 + row) * dv + col0 + c8 * 8) * (uint32_t)sizeof(T));
     }
   }
 };
 
 // b of token t0 + j of a chunk; past the end of the sequence the cumulative sum
 // stays at its last value (absent tokens have g = 0).
-__device__ __forceinline__ float load_b(const float* bg, long long t0, int j, long long T) {
-  long long t = t0 + j;
+__device__ __forceinline__ float load_b(rsrc_t b, uint32_t t0, int j, uint32_t T) {
+  uint32_t t = t0 + j;
   if (t >= T) t = T - 1;
-  return bg[t];
+  return buf_load4(b, t * 4u);
 }
 
-// Writes k e^{gamma - b} (token-contiguous) and v (token-contiguous) into LDS.
+// Writes k e^{gamma - b} and v into their token-major LDS tiles.
 template <typename T, int DK, int DVS, bool LOAD_Q>
-__device__ __forceinline__ void stage_state_operands(T* kpt, T* vt, const Staged<T, DK, DVS, LOAD_Q>& st,
+__device__ __forceinline__ void stage_state_operands(T* kp, T* vv, const Staged<T, DK, DVS, LOAD_Q>& st,
                                                      const float* sbc, int tid) {
-  using E = Elem<T>;
   using C = Cfg<T, DK, DVS>;
   const float gam = sbc[63];
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT;
     const int row = u / (DK / 8), c8 = u % (DK / 8);
-    const float f = exp_e(gam - sbc[row]);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) kpt[(c8 * 8 + e) * C::TLD + row] = E::cvt(E::get(st.k[m], e) * f);
+    TokTile<T, DK>::store8(kp, row, c8 * 8, st.k[m], exp_e(gam - sbc[row]));
   }
 #pragma unroll
   for (int m = 0; m < C::VU; ++m) {
     const int u = tid + m * C::NT;
     const int row = u / (DVS / 8), c8 = u % (DVS / 8);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) vt[(c8 * 8 + e) * C::TLD + row] = E::cvt(E::get(st.v[m], e));
+    TokTile<T, DVS>::store8_raw(vv, row, c8 * 8, st.v[m]);
   }
 }
 
-// S[nb][db] += sum_i kpt[d][i] v[n][i] over the chunk's 64 tokens (two K-steps).
 // fp32 state slice of one wave: S[d = 16 db + 4 g + e][n = 16 nb + r16], e = 0..3
 template <typename T, int DK, int DVS>
 struct StateAcc {
@@ -163,7 +164,7 @@ struct VFrags {
 
 template <typename T, int DK, int DVS>
 __device__ __forceinline__ void state_update(StateAcc<T, DK, DVS>& S, const VFrags<T, DK, DVS>& Vf,
-                                             const T* kpt, float decay, int r16, int g) {
+                                             const T* kp, float decay, int lane) {
   using E = Elem<T>;
   using C = Cfg<T, DK, DVS>;
 #pragma unroll
@@ -174,11 +175,21 @@ __device__ __forceinline__ void state_update(StateAcc<T, DK, DVS>& S, const VFra
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
-      const typename E::Frag ka = E::load_frag(kpt + (db * 16 + r16) * C::TLD, ks * 32 + 4 * g);
+      const typename E::Frag ka = TokTile<T, DK>::load(kp, ks * 32, db * 16, lane);
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) E::mfma(S.s[nb][db], ka, Vf.f[nb][ks]);
     }
   }
+}
+
+// v fragments of one wave's columns for both token K-steps of the chunk
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void load_v_frags(VFrags<T, DK, DVS>& Vf, const T* vv, int wave, int lane) {
+  using C = Cfg<T, DK, DVS>;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) Vf.f[nb][ks] = TokTile<T, DVS>::load(vv, ks * 32, wave * C::CPW + nb * 16, lane);
 }
 
 // ============================================================================
@@ -186,10 +197,10 @@ __device__ __forceinline__ void state_update(StateAcc<T, DK, DVS>& S, const VFra
 // ============================================================================
 template <typename T, int DK, int DVS>
 __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(ChunkParams p) {
-  using E = Elem<T>;
   using C = Cfg<T, DK, DVS>;
   __shared__ SegSmem<T, DK, DVS> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int nseg = p.segments - 1;
   const int L = xcd_linear_index(blockIdx.x, p.grid);
@@ -202,9 +213,11 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
   const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
   const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
 
-  const T* kg = static_cast<const T*>(p.k) + (long long)bh * p.T * DK;
-  const T* vg = static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv;
-  const float* bg = p.b + (long long)bh * p.T;
+  const uint32_t Tn = (uint32_t)p.T;
+  HeadBuffers hb;
+  hb.k = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
+  hb.v = make_rsrc(static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * (uint32_t)sizeof(T));
+  hb.b = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
 
   StateAcc<T, DK, DVS> S;
 #pragma unroll
@@ -216,27 +229,26 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
   Staged<T, DK, DVS, false> st;
   float rb = 0.0f;
   if (c_begin < c_end) {
-    if (tid < 64) sm.sb[0][tid] = load_b(bg, (long long)c_begin * kChunk, tid, p.T);
-    st.load(nullptr, kg, vg, (long long)c_begin * kChunk, p.T, p.dv, col0, tid);
-    if (tid < 64 && c_begin + 1 < c_end) rb = load_b(bg, (long long)(c_begin + 1) * kChunk, tid, p.T);
+    const float b0 = load_b(hb.b, (uint32_t)c_begin * kChunk, lane, Tn);
+    if (tid < 64) sm.sb[0][tid] = b0;
+    st.load(hb, (uint32_t)c_begin * kChunk, p.dv, col0, tid);
+    rb = load_b(hb.b, (uint32_t)min(c_begin + 1, c_end - 1) * kChunk, lane, Tn);
     __syncthreads();
   }
   for (int c = c_begin; c < c_end; ++c) {
     const int buf = (c - c_begin) & 1;
     const float* sbc = sm.sb[buf];
-    stage_state_operands<T, DK, DVS, false>(sm.kpt, sm.vt, st, sbc, tid);
+    stage_state_operands<T, DK, DVS, false>(sm.kp, sm.vv, st, sbc, tid);
     if (tid < 64) sm.sb[buf ^ 1][tid] = rb;
     if (tid == 0) gsum += sbc[63];
-    if (c + 1 < c_end) st.load(nullptr, kg, vg, (long long)(c + 1) * kChunk, p.T, p.dv, col0, tid);
-    if (tid < 64 && c + 2 < c_end) rb = load_b(bg, (long long)(c + 2) * kChunk, tid, p.T);
+    // prefetch the next chunk (the last iteration re-reads its own chunk so that
+    // every iteration issues the same loads)
+    rb = load_b(hb.b, (uint32_t)min(c + 2, c_end - 1) * kChunk, lane, Tn);
+    st.load(hb, (uint32_t)min(c + 1, c_end - 1) * kChunk, p.dv, col0, tid);
     __syncthreads();
     VFrags<T, DK, DVS> Vf;
-#pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-        Vf.f[nb][ks] = E::load_frag(sm.vt + (wave * C::CPW + nb * 16 + r16) * C::TLD, ks * 32 + 4 * g);
-    state_update<T, DK, DVS>(S, Vf, sm.kpt, exp_e(sbc[63]), r16, g);
+    load_v_frags<T, DK, DVS>(Vf, sm.vv, wave, lane);
+    state_update<T, DK, DVS>(S, Vf, sm.kp, exp_e(sbc[63]), lane);
     __syncthreads();
   }
 
@@ -262,7 +274,8 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
   using E = Elem<T>;
   using C = Cfg<T, DK, DVS>;
   __shared__ OutSmem<T, DK, DVS, DIAG> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int L = xcd_linear_index(blockIdx.x, p.grid);
   const int slice = L % p.nslices;
@@ -274,11 +287,13 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
   const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
   const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
 
-  const T* qg = static_cast<const T*>(p.q) + (long long)bh * p.T * DK;
-  const T* kg = static_cast<const T*>(p.k) + (long long)bh * p.T * DK;
-  const T* vg = static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv;
-  const float* bg = p.b + (long long)bh * p.T;
-  float* og = p.o + (long long)bh * p.T * p.dv;
+  const uint32_t Tn = (uint32_t)p.T;
+  HeadBuffers hb;
+  hb.q = make_rsrc(static_cast<const T*>(p.q) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
+  hb.k = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
+  hb.v = make_rsrc(static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * (uint32_t)sizeof(T));
+  hb.b = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+  hb.o = make_rsrc(p.o + (long long)bh * p.T * p.dv, Tn * p.dv * 4u);
 
   // ---- initial state of this segment:  S0, folded with the earlier segments'
   //      local states:  S <- e^{Gamma_p} S + H_p  for p < seg.
@@ -318,16 +333,37 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
   Staged<T, DK, DVS, true> st;
   float rb = 0.0f;
   if (c_begin < c_end) {
-    if (tid < 64) sm.sb[0][tid] = load_b(bg, (long long)c_begin * kChunk, tid, p.T);
-    st.load(qg, kg, vg, (long long)c_begin * kChunk, p.T, p.dv, col0, tid);
-    if (tid < 64 && c_begin + 1 < c_end) rb = load_b(bg, (long long)(c_begin + 1) * kChunk, tid, p.T);
+    const float b0 = load_b(hb.b, (uint32_t)c_begin * kChunk, lane, Tn);
+    if (tid < 64) sm.sb[0][tid] = b0;
+    rb = load_b(hb.b, (uint32_t)min(c_begin + 1, c_end - 1) * kChunk, lane, Tn);
+    st.load(hb, (uint32_t)c_begin * kChunk, p.dv, col0, tid);
   }
   __syncthreads();
+
+  // o of the previous chunk, kept in registers and stored at the start of the next
+  // iteration, ahead of that iteration's prefetch: the stores then have a whole
+  // iteration to complete before the loads behind them are waited on.  The first
+  // iteration stores to an offset past the descriptor, which the hardware drops.
+  floatx4 O[4][C::NB];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  uint32_t o_row0 = 0xFFFFFFFFu;  // first row of the chunk held in O (none yet)
+  auto store_o = [&]() {
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const uint32_t t = o_row0 + jb * 16 + r16;
+      const uint32_t off = (o_row0 == 0xFFFFFFFFu) ? kDroppedOffset : (t * p.dv + wcol + 4 * g) * 4u;
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) buf_store16<kAuxStream>(hb.o, off + nb * 64u, O[jb][nb]);
+    }
+  };
 
   for (int c = c_begin; c < c_end; ++c) {
     const int buf = (c - c_begin) & 1;
     const float* sbc = sm.sb[buf];
-    const long long t0 = (long long)c * kChunk;
+    const uint32_t t0 = (uint32_t)c * kChunk;
 
     // ---- (1) chunk c: registers -> LDS with the tile-relative decay factors
 #pragma unroll
@@ -345,20 +381,25 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
         E::store8_raw(sm.kr + row * C::QLD + c8 * 8, st.k[m]);
       }
     }
-    stage_state_operands<T, DK, DVS, true>(sm.kpt, sm.vt, st, sbc, tid);
+    stage_state_operands<T, DK, DVS, true>(sm.kp, sm.vv, st, sbc, tid);
     if (tid < 64) sm.sb[buf ^ 1][tid] = rb;
 
-    // ---- (2) prefetch chunk c + 1 (and b of chunk c + 2) while c is computed
-    if (c + 1 < c_end) st.load(qg, kg, vg, t0 + kChunk, p.T, p.dv, col0, tid);
-    if (tid < 64 && c + 2 < c_end) rb = load_b(bg, t0 + 2 * kChunk, tid, p.T);
+    // ---- (2) o of chunk c - 1; then prefetch chunk c + 1 (and b of chunk c + 2) while
+    //      c is computed.  The last iteration re-reads its own chunk so every iteration
+    //      issues the same loads.
+    store_o();
+    rb = load_b(hb.b, (uint32_t)min(c + 2, c_end - 1) * kChunk, lane, Tn);
+    st.load(hb, (uint32_t)min(c + 1, c_end - 1) * kChunk, p.dv, col0, tid);
     __syncthreads();
 
     // ---- (3) attention matrix A of the chunk (bf16 / fp32 in LDS)
     {
       constexpr int NBLK = DIAG ? 6 : 10;
-      for (int bi = wave; bi < NBLK; bi += C::NW) {
-        const int jb = DIAG ? kOffJ[bi] : kTriJ[bi];
-        const int ib = DIAG ? kOffI[bi] : kTriI[bi];
+#pragma unroll
+      for (int bi = 0; bi < NBLK; ++bi) {
+        if (bi % C::NW != wave) continue;  // wave-uniform
+        const int jb = DIAG ? off_j(bi) : tri_j(bi);
+        const int ib = DIAG ? off_i(bi) : tri_i(bi);
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
@@ -405,17 +446,13 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) Sf[nb][ks] = E::from_acc(S.s[nb][2 * ks], S.s[nb][2 * ks + 1]);
       VFrags<T, DK, DVS> Vf;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          Vf.f[nb][ks] = E::load_frag(sm.vt + (wave * C::CPW + nb * 16 + r16) * C::TLD, ks * 32 + 4 * g);
+      load_v_frags<T, DK, DVS>(Vf, sm.vv, wave, lane);
 
-      floatx4 O[4][C::NB];
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      o_row0 = t0;
       // inter-chunk: O^T[n][j] = sum_d S[d][n] Qh[j][d]
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -442,22 +479,14 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
           for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], Vf.f[nb][ks], ab);
         }
       }
-      // lane holds o[t0 + 16 jb + r16][wcol + 16 nb + 4 g + 0..3]
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const long long t = t0 + jb * 16 + r16;
-        if (t < p.T) {
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) {
-            float* dst = og + t * p.dv + wcol + nb * 16 + 4 * g;
-            __builtin_nontemporal_store(O[jb][nb], reinterpret_cast<floatx4*>(dst));
-          }
-        }
-      }
-      state_update<T, DK, DVS>(S, Vf, sm.kpt, exp_e(sbc[63]), r16, g);
+      // lane holds o[t0 + 16 jb + r16][wcol + 16 nb + 4 g + 0..3]; stored next
+      // iteration.  Rows past the end of the sequence fall outside the descriptor.
+      state_update<T, DK, DVS>(S, Vf, sm.kp, exp_e(sbc[63]), lane);
     }
     __syncthreads();
   }
+
+  if (c_begin < c_end) store_o();  // the last chunk's o
 
   if (seg == p.segments - 1) {
 #pragma unroll

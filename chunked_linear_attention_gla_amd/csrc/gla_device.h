@@ -38,6 +38,45 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
 
+// ---------------------------------------------------------------- buffer access
+//
+// Streaming tensors are read and written through raw buffer instructions with a
+// per-head resource descriptor whose size is the head's extent in bytes.  The
+// hardware range check returns zeros for loads past the end and drops stores
+// past the end, so the ragged last chunk needs no branches: every wave issues
+// the same memory instructions every chunk and the compiler can wait on exact
+// counts instead of draining all outstanding loads and stores.
+// Descriptor word 3 for gfx9-family raw buffers: DATA_FORMAT (bits 15..18) = 4,
+// 32-bit elements; no swizzle, no stride.
+constexpr int kBufferWord3 = 0x00020000;
+// cache-policy operand of the buffer builtins: bit 1 marks a streaming
+// (non-temporal) access
+constexpr int kAuxStream = 2;
+// Largest extent of one head's tensor (bytes) that a descriptor may describe, and
+// an offset beyond it that leaves room for a few 16-byte accesses without
+// wrapping: a store there is always out of range and dropped.
+constexpr uint32_t kMaxHeadBytes = 0xFFFF0000u;
+constexpr uint32_t kDroppedOffset = 0xFFFFF000u;
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferWord3);
+}
+template <int AUX = 0>
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ float buf_load4(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
+}
+template <int AUX = 0>
+__device__ __forceinline__ void buf_store16(rsrc_t r, uint32_t off, const floatx4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, AUX);
+}
+
 // ---------------------------------------------------------------- element traits
 
 template <typename T> struct Elem;
@@ -49,8 +88,8 @@ template <> struct Elem<bf16> {
   static constexpr int kPad = 8;  // LDS row padding in elements (16 bytes)
 
   __device__ static __forceinline__ Vec8 zero8() { Vec8 r; r.u = make_uint4(0, 0, 0, 0); return r; }
-  __device__ static __forceinline__ Vec8 load8(const bf16* p) {
-    Vec8 r; r.u = *reinterpret_cast<const uint4*>(p); return r;
+  __device__ static __forceinline__ Vec8 load8(rsrc_t r, uint32_t byte_off) {
+    Vec8 v; v.u = buf_load16(r, byte_off); return v;
   }
   __device__ static __forceinline__ float get(const Vec8& v, int e) {
     const uint32_t w = (e < 2) ? v.u.x : (e < 4) ? v.u.y : (e < 6) ? v.u.z : v.u.w;
@@ -100,11 +139,14 @@ template <> struct Elem<float> {
   __device__ static __forceinline__ Vec8 zero8() {
     Vec8 r; r.a = make_float4(0, 0, 0, 0); r.b = r.a; return r;
   }
-  __device__ static __forceinline__ Vec8 load8(const float* p) {
-    Vec8 r;
-    r.a = *reinterpret_cast<const float4*>(p);
-    r.b = *reinterpret_cast<const float4*>(p + 4);
-    return r;
+  __device__ static __forceinline__ Vec8 load8(rsrc_t r, uint32_t byte_off) {
+    Vec8 v;
+    const uint4 a = buf_load16(r, byte_off), b = buf_load16(r, byte_off + 16);
+    v.a = make_float4(__builtin_bit_cast(float, a.x), __builtin_bit_cast(float, a.y),
+                      __builtin_bit_cast(float, a.z), __builtin_bit_cast(float, a.w));
+    v.b = make_float4(__builtin_bit_cast(float, b.x), __builtin_bit_cast(float, b.y),
+                      __builtin_bit_cast(float, b.z), __builtin_bit_cast(float, b.w));
+    return v;
   }
   __device__ static __forceinline__ float get(const Vec8& v, int e) {
     switch (e) {
@@ -144,6 +186,64 @@ template <> struct Elem<float> {
     for (int s = 0; s < 4; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.hi[s], b.hi[s], acc, 0, 0, 0);
   }
   __device__ static __forceinline__ float to_f32(float x) { return x; }
+};
+
+// ---------------------------------------------------------------- token-major tiles
+//
+// Tiles whose token index is the MFMA contraction index: k e^{gamma-b} and v in the
+// state update, v in A.V.  An operand fragment needs, in lane (g, r16), eight
+// tokens (kappa order) of one feature column c0 + r16.
+//
+// bf16: the tile is stored row-major [64 tokens][NCOL] and the fragment is read
+// with the gfx950 LDS transpose read ds_read_b64_tr_b16.  Within each group of
+// 16 lanes that instruction hands destination lane 4a + b, as its element e,
+// element b of the 8 bytes addressed by source lane a + 4e.  Source lane s of
+// lane group g therefore points at row k0 + 4g + s/4, columns c0 + 4(s%4)..+3,
+// and every lane receives tokens k0 + 4g + 0..3 of its own column c0 + r16: the
+// first half of the fragment; rows 16 further give the second half.
+// fp32: there is no 32-bit transpose read, so the tile is stored transposed
+// [NCOL][64 tokens] and read with ordinary fragment loads.
+template <typename T, int NCOL> struct TokTile;
+
+template <int NCOL> struct TokTile<bf16, NCOL> {
+  static constexpr int LD = NCOL + 8;    // row stride (elements) of [token][col]
+  static constexpr int SIZE = 64 * LD;
+  using E = Elem<bf16>;
+  __device__ static __forceinline__ void store8(bf16* t, int row, int col, const E::Vec8& v, float s) {
+    E::store8_scaled(t + row * LD + col, v, s);
+  }
+  __device__ static __forceinline__ void store8_raw(bf16* t, int row, int col, const E::Vec8& v) {
+    E::store8_raw(t + row * LD + col, v);
+  }
+  __device__ static __forceinline__ E::Frag load(const bf16* t, int k0, int c0, int lane) {
+    typedef short shortx4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+    const int s = lane & 15, g = lane >> 4;
+    const bf16* p0 = t + (k0 + 4 * g + (s >> 2)) * LD + c0 + 4 * (s & 3);
+    const bf16* p1 = p0 + 16 * LD;
+    const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0));
+    const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p1));
+    E::Frag f;
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return f;
+  }
+};
+
+template <int NCOL> struct TokTile<float, NCOL> {
+  static constexpr int LD = 64 + 4;      // row stride (elements) of [col][token]
+  static constexpr int SIZE = NCOL * LD;
+  using E = Elem<float>;
+  __device__ static __forceinline__ void store8(float* t, int row, int col, const E::Vec8& v, float s) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = E::get(v, e) * s;
+  }
+  __device__ static __forceinline__ void store8_raw(float* t, int row, int col, const E::Vec8& v) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = E::get(v, e);
+  }
+  __device__ static __forceinline__ E::Frag load(const float* t, int k0, int c0, int lane) {
+    return E::load_frag(t + (c0 + (lane & 15)) * LD, k0 + 4 * (lane >> 4));
+  }
 };
 
 // Workgroup index -> linear work index, so that consecutive work indices land on

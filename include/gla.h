@@ -47,7 +47,9 @@
  *   - T may be any value >= 0.  Sequences are processed in chunks of
  *     GLA_CHUNK tokens; a final partial chunk is handled in place (tokens past
  *     T are treated as absent).  T = 0 writes S_T = S0 (or zeros) and no o.
- *   - Supported sizes: dk in {64, 128}, dv in {64, 128}, B >= 1, H >= 1.
+ *   - Supported sizes: dk in {64, 128}, dv in {64, 128}, B >= 1, H >= 1, and
+ *     T * max(dk, dv) * 4 <= 0xFFFF0000 (one head's tensors are addressed
+ *     through 32-bit buffer descriptors): T < 8M tokens at d = 128.
  *     The fp32 diagonal-branch path additionally needs dk == 64.
  */
 #ifndef GLA_H_
