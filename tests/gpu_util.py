@@ -46,3 +46,12 @@ def gpu_heads(t, heads, T=None):
 
 def rel(got, ref):
     return oracle.max_rel_err(got, ref)
+
+
+def gpu_rel(got: torch.Tensor, ref: torch.Tensor) -> float:
+    """max |got - ref| / max |ref| computed on the device, one head slice at a time."""
+    g = got.reshape(-1, *got.shape[-2:])
+    r = ref.reshape(-1, *ref.shape[-2:])
+    scale = max(r[i].abs().max().item() for i in range(r.shape[0]))
+    diff = max((g[i] - r[i]).abs().max().item() for i in range(g.shape[0]))
+    return diff / scale if scale else diff
