@@ -26,7 +26,7 @@ STATUS = {
     10: "GLA_ERR_UNSUPPORTED",
 }
 CHUNK = 64
-MAX_SEGMENTS = 16
+MAX_SEGMENTS = 64
 
 
 class GLAError(RuntimeError):

@@ -43,13 +43,14 @@ namespace gla {
 
 template <typename T, int DK, int DVS>
 struct Cfg {
-  static constexpr int NW = DVS >= 64 ? 4 : DVS / 16;  // waves per workgroup
-  static constexpr int NB = DVS / (16 * NW);           // 16-column blocks per wave
+  static constexpr int NB = DVS >= 32 ? 2 : 1;         // 16-column blocks per wave
   static constexpr int CPW = 16 * NB;                  // value columns per wave
+  static constexpr int NW = DVS / CPW;                 // waves per workgroup
   static constexpr int NT = 64 * NW;                   // threads per workgroup
+
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int QLD = DK + PAD;   // row stride of Qh, Kh (and raw q, k)
-  static constexpr int TLD = 64 + PAD;   // row stride of the token-contiguous tiles
+  static constexpr int TLD = 64 + PAD;   // row stride of the attention matrix A
   static constexpr int QU = 8 * DK / NT;   // 8-element q (and k) units per thread per chunk
   static constexpr int VU = 8 * DVS / NT;  // 8-element v units per thread per chunk
   static constexpr int DB = DK / 16;       // 16-row blocks of the key dimension
@@ -68,14 +69,13 @@ struct OutSmem {
   T a[64 * C::TLD];                  // A[j][i]   row-major
   T qr[DIAG ? 64 * C::QLD : 1];      // raw q, diagonal-branch path only
   T kr[DIAG ? 64 * C::QLD : 1];      // raw k, diagonal-branch path only
-  float sb[2][64];                   // b of the current and the next chunk
+  float sb[DIAG ? 64 : 1];           // b of the chunk, diagonal-branch path only
 };
 
 template <typename T, int DK, int DVS>
 struct SegSmem {
   T kp[TokTile<T, DK>::SIZE];
   T vv[TokTile<T, DVS>::SIZE];
-  float sb[2][64];
 };
 
 // Causal 16x16 tiles of a 64x64 chunk, (query tile jb, key tile ib) with ib <= jb,
@@ -94,8 +94,28 @@ struct HeadBuffers {
   rsrc_t q, k, v, b, o;
 };
 
-// Per-thread registers holding one chunk of q, k, v on its way to LDS.  Rows past
-// the end of the sequence read as zeros (buffer range check).
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Cumulative log-decay of one chunk: lane j of every wave holds b_j; the tile
+// boundaries are read out once per chunk as wave-uniform scalars.
+struct ChunkDecay {
+  float b;               // b_j for this lane's token j
+  float r1, r2, r3, gam; // b_15, b_31, b_47, b_63
+  __device__ __forceinline__ explicit ChunkDecay(float bl)
+      : b(bl), r1(lane_value(bl, 15)), r2(lane_value(bl, 31)), r3(lane_value(bl, 47)), gam(lane_value(bl, 63)) {}
+  // r_u = b_{16u-1}, the cumulative decay before tile u (r_0 = 0)
+  __device__ __forceinline__ float r(int u) const { return u == 0 ? 0.0f : u == 1 ? r1 : u == 2 ? r2 : r3; }
+  // E_u = b_{16u+15}, the cumulative decay at the end of tile u
+  __device__ __forceinline__ float end(int u) const { return u == 0 ? r1 : u == 1 ? r2 : u == 2 ? r3 : gam; }
+  // b of another token of the chunk
+  __device__ __forceinline__ float at(int j) const { return __shfl(b, j); }
+};
+
+// Per-thread registers holding one chunk of q, k, v (and b) on its way to LDS.
+// Rows past the end of the sequence read as zeros (buffer range check); b past
+// the end repeats its last value (absent tokens have g = 0).
 template <typename T, int DK, int DVS, bool LOAD_Q>
 struct Staged {
   using E = Elem<T>;
@@ -103,8 +123,12 @@ struct Staged {
   typename E::Vec8 q[LOAD_Q ? C::QU : 1];
   typename E::Vec8 k[C::QU];
   typename E::Vec8 v[C::VU];
+  float b;
 
-  __device__ __forceinline__ void load(const HeadBuffers& hb, uint32_t t0, int dv, int col0, int tid) {
+  __device__ __forceinline__ void load(const HeadBuffers& hb, uint32_t t0, uint32_t len, int dv, int col0,
+                                       int tid) {
+    const uint32_t tb = t0 + (tid & 63);
+    b = buf_load4(hb.b, (tb < len ? tb : len - 1) * 4u);
 #pragma unroll
     for (int m = 0; m < C::QU; ++m) {
       const int u = tid + m * C::NT;
@@ -122,25 +146,26 @@ struct Staged {
   }
 };
 
-// b of token t0 + j of a chunk; past the end of the sequence the cumulative sum
-// stays at its last value (absent tokens have g = 0).
-__device__ __forceinline__ float load_b(rsrc_t b, uint32_t t0, int j, uint32_t T) {
-  uint32_t t = t0 + j;
-  if (t >= T) t = T - 1;
-  return buf_load4(b, t * 4u);
-}
+// b of the rows this thread stages (one shuffle each, issued together)
+template <typename T, int DK, int DVS>
+struct RowB {
+  float v[Cfg<T, DK, DVS>::QU];
+  __device__ __forceinline__ RowB(const ChunkDecay& cd, int tid) {
+#pragma unroll
+    for (int m = 0; m < Cfg<T, DK, DVS>::QU; ++m) v[m] = cd.at((tid + m * Cfg<T, DK, DVS>::NT) / (DK / 8));
+  }
+};
 
 // Writes k e^{gamma - b} and v into their token-major LDS tiles.
 template <typename T, int DK, int DVS, bool LOAD_Q>
 __device__ __forceinline__ void stage_state_operands(T* kp, T* vv, const Staged<T, DK, DVS, LOAD_Q>& st,
-                                                     const float* sbc, int tid) {
+                                                     const ChunkDecay& cd, const RowB<T, DK, DVS>& brow, int tid) {
   using C = Cfg<T, DK, DVS>;
-  const float gam = sbc[63];
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT;
     const int row = u / (DK / 8), c8 = u % (DK / 8);
-    TokTile<T, DK>::store8(kp, row, c8 * 8, st.k[m], exp_e(gam - sbc[row]));
+    TokTile<T, DK>::store8(kp, row, c8 * 8, st.k[m], exp_e(cd.gam - brow.v[m]));
   }
 #pragma unroll
   for (int m = 0; m < C::VU; ++m) {
@@ -224,31 +249,22 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
   for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) S.s[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float gsum = 0.0f;  // total log-decay of the segment (thread 0)
+  float gsum = 0.0f;  // total log-decay of the segment
 
   Staged<T, DK, DVS, false> st;
-  float rb = 0.0f;
-  if (c_begin < c_end) {
-    const float b0 = load_b(hb.b, (uint32_t)c_begin * kChunk, lane, Tn);
-    if (tid < 64) sm.sb[0][tid] = b0;
-    st.load(hb, (uint32_t)c_begin * kChunk, p.dv, col0, tid);
-    rb = load_b(hb.b, (uint32_t)min(c_begin + 1, c_end - 1) * kChunk, lane, Tn);
-    __syncthreads();
-  }
+  if (c_begin < c_end) st.load(hb, (uint32_t)c_begin * kChunk, Tn, p.dv, col0, tid);
   for (int c = c_begin; c < c_end; ++c) {
-    const int buf = (c - c_begin) & 1;
-    const float* sbc = sm.sb[buf];
-    stage_state_operands<T, DK, DVS, false>(sm.kp, sm.vv, st, sbc, tid);
-    if (tid < 64) sm.sb[buf ^ 1][tid] = rb;
-    if (tid == 0) gsum += sbc[63];
+    const ChunkDecay cd(st.b);
+    const RowB<T, DK, DVS> brow(cd, tid);
+    stage_state_operands<T, DK, DVS, false>(sm.kp, sm.vv, st, cd, brow, tid);
+    gsum += cd.gam;
     // prefetch the next chunk (the last iteration re-reads its own chunk so that
     // every iteration issues the same loads)
-    rb = load_b(hb.b, (uint32_t)min(c + 2, c_end - 1) * kChunk, lane, Tn);
-    st.load(hb, (uint32_t)min(c + 1, c_end - 1) * kChunk, p.dv, col0, tid);
+    st.load(hb, (uint32_t)min(c + 1, c_end - 1) * kChunk, Tn, p.dv, col0, tid);
     __syncthreads();
     VFrags<T, DK, DVS> Vf;
     load_v_frags<T, DK, DVS>(Vf, sm.vv, wave, lane);
-    state_update<T, DK, DVS>(S, Vf, sm.kp, exp_e(sbc[63]), lane);
+    state_update<T, DK, DVS>(S, Vf, sm.kp, exp_e(cd.gam), lane);
     __syncthreads();
   }
 
@@ -269,8 +285,17 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
 // ============================================================================
 // Fused output pass.
 // ============================================================================
+// Register budget of the output kernel: two waves per SIMD where it then still fits
+// without spilling (the bf16 unified kernels with 4 waves of 32 columns, and dk = 64
+// with 2); this also keeps the MFMA accumulators in VGPRs instead of AGPR copies.
 template <typename T, int DK, int DVS, bool DIAG>
-__global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(ChunkParams p) {
+constexpr int out_waves_per_simd() {
+  return (sizeof(T) == 2 && !DIAG && (DVS == 128 || (DK == 64 && DVS == 64))) ? 2 : 1;
+}
+
+template <typename T, int DK, int DVS, bool DIAG>
+__global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT))
+__attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chunk_output_kernel(ChunkParams p) {
   using E = Elem<T>;
   using C = Cfg<T, DK, DVS>;
   __shared__ OutSmem<T, DK, DVS, DIAG> sm;
@@ -331,65 +356,61 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
   }
 
   Staged<T, DK, DVS, true> st;
-  float rb = 0.0f;
-  if (c_begin < c_end) {
-    const float b0 = load_b(hb.b, (uint32_t)c_begin * kChunk, lane, Tn);
-    if (tid < 64) sm.sb[0][tid] = b0;
-    rb = load_b(hb.b, (uint32_t)min(c_begin + 1, c_end - 1) * kChunk, lane, Tn);
-    st.load(hb, (uint32_t)c_begin * kChunk, p.dv, col0, tid);
-  }
+  if (c_begin < c_end) st.load(hb, (uint32_t)c_begin * kChunk, Tn, p.dv, col0, tid);
   __syncthreads();
 
-  // o of the previous chunk, kept in registers and stored at the start of the next
-  // iteration, ahead of that iteration's prefetch: the stores then have a whole
-  // iteration to complete before the loads behind them are waited on.  The first
-  // iteration stores to an offset past the descriptor, which the hardware drops.
-  floatx4 O[4][C::NB];
+  // o of a chunk is stored at the end of its iteration, after that iteration's
+  // prefetch loads; lane (g, r16) holds row r16 of tile jb at columns 16 nb + 4g.
+  // Rows past the end of the sequence fall outside the descriptor and are dropped.
+  auto store_o = [&](const floatx4 (&O)[4][C::NB], uint32_t row0, bool none) {
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
+    for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-  uint32_t o_row0 = 0xFFFFFFFFu;  // first row of the chunk held in O (none yet)
-  auto store_o = [&]() {
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      const uint32_t t = o_row0 + jb * 16 + r16;
-      const uint32_t off = (o_row0 == 0xFFFFFFFFu) ? kDroppedOffset : (t * p.dv + wcol + 4 * g) * 4u;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) buf_store16<kAuxStream>(hb.o, off + nb * 64u, O[jb][nb]);
-    }
+      for (int nb = 0; nb < C::NB; ++nb) {
+        const uint32_t off = none ? kDroppedOffset : ((row0 + jb * 16 + r16) * p.dv + wcol + nb * 16 + 4 * g) * 4u;
+        buf_store16<kAuxStream>(hb.o, off, O[jb][nb]);
+      }
   };
+  // Issuing the same number of (dropped) stores after the first loads gives both
+  // entries into the loop the same outstanding memory operations, so the wait for
+  // the prefetched data never waits for the stores behind it.
+  {
+    floatx4 Oz[4][C::NB];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) Oz[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    store_o(Oz, 0, true);
+  }
 
   for (int c = c_begin; c < c_end; ++c) {
-    const int buf = (c - c_begin) & 1;
-    const float* sbc = sm.sb[buf];
     const uint32_t t0 = (uint32_t)c * kChunk;
+    const ChunkDecay cd(st.b);
 
     // ---- (1) chunk c: registers -> LDS with the tile-relative decay factors
+    {
+      const RowB<T, DK, DVS> brow(cd, tid);
 #pragma unroll
-    for (int m = 0; m < C::QU; ++m) {
-      const int u = tid + m * C::NT;
-      const int row = u / (DK / 8), c8 = u % (DK / 8);
-      const int tile = row >> 4;
-      const float brow = sbc[row];
-      const float rj = tile ? sbc[tile * 16 - 1] : 0.0f;
-      E::store8_scaled(sm.qh + row * C::QLD + c8 * 8, st.q[m], exp_e(brow - rj));
-      const float kref = DIAG ? sbc[tile * 16 + 15] : rj;
-      E::store8_scaled(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(kref - brow));
-      if (DIAG) {
-        E::store8_raw(sm.qr + row * C::QLD + c8 * 8, st.q[m]);
-        E::store8_raw(sm.kr + row * C::QLD + c8 * 8, st.k[m]);
+      for (int m = 0; m < C::QU; ++m) {
+        const int u = tid + m * C::NT;
+        const int row = u / (DK / 8), c8 = u % (DK / 8);
+        const int tile = row >> 4;
+        const float rj = cd.r(tile);
+        E::store8_scaled(sm.qh + row * C::QLD + c8 * 8, st.q[m], exp_e(brow.v[m] - rj));
+        const float kref = DIAG ? cd.end(tile) : rj;
+        E::store8_scaled(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(kref - brow.v[m]));
+        if (DIAG) {
+          E::store8_raw(sm.qr + row * C::QLD + c8 * 8, st.q[m]);
+          E::store8_raw(sm.kr + row * C::QLD + c8 * 8, st.k[m]);
+        }
       }
+      stage_state_operands<T, DK, DVS, true>(sm.kp, sm.vv, st, cd, brow, tid);
+      if (DIAG && tid < 64) sm.sb[tid] = cd.b;
     }
-    stage_state_operands<T, DK, DVS, true>(sm.kp, sm.vv, st, sbc, tid);
-    if (tid < 64) sm.sb[buf ^ 1][tid] = rb;
 
-    // ---- (2) o of chunk c - 1; then prefetch chunk c + 1 (and b of chunk c + 2) while
-    //      c is computed.  The last iteration re-reads its own chunk so every iteration
-    //      issues the same loads.
-    store_o();
-    rb = load_b(hb.b, (uint32_t)min(c + 2, c_end - 1) * kChunk, lane, Tn);
-    st.load(hb, (uint32_t)min(c + 1, c_end - 1) * kChunk, p.dv, col0, tid);
+    // ---- (2) prefetch chunk c + 1 while c is computed.  The last iteration re-reads
+    //      its own chunk so every iteration issues the same loads.
+    st.load(hb, (uint32_t)min(c + 1, c_end - 1) * kChunk, Tn, p.dv, col0, tid);
     __syncthreads();
 
     // ---- (3) attention matrix A of the chunk (bf16 / fp32 in LDS)
@@ -408,9 +429,8 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
           E::mfma(acc, ka, qb);
         }
         // acc[e] = (Qh_j . Kh_i), j = 16 jb + r16, i = 16 ib + 4 g + e
-        const float rj = jb ? sbc[jb * 16 - 1] : 0.0f;
-        const float ri = DIAG ? sbc[ib * 16 + 15] : (ib ? sbc[ib * 16 - 1] : 0.0f);
-        const float f = (jb == ib) ? 1.0f : exp_e(rj - ri);
+        const float ri = DIAG ? cd.end(ib) : cd.r(ib);
+        const float f = (jb == ib) ? 1.0f : exp_e(cd.r(jb) - ri);
         float vals[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -430,7 +450,7 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
             float dot = 0.0f;
 #pragma unroll 8
             for (int d = 0; d < DK; ++d) dot += E::to_f32(qrow[d]) * E::to_f32(krow[d]);
-            val = dot * exp_e(sbc[u * 16 + j] - sbc[u * 16 + i]);
+            val = dot * exp_e(sm.sb[u * 16 + j] - sm.sb[u * 16 + i]);
           }
           sm.a[(u * 16 + j) * C::TLD + u * 16 + i] = E::cvt(val);
         }
@@ -448,11 +468,11 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
       VFrags<T, DK, DVS> Vf;
       load_v_frags<T, DK, DVS>(Vf, sm.vv, wave, lane);
 
+      floatx4 O[4][C::NB];
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-      o_row0 = t0;
       // inter-chunk: O^T[n][j] = sum_d S[d][n] Qh[j][d]
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) {
@@ -465,7 +485,7 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
       }
 #pragma unroll
       for (int jb = 1; jb < 4; ++jb) {
-        const float f = exp_e(sbc[jb * 16 - 1]);
+        const float f = exp_e(cd.r(jb));
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] *= f;
       }
@@ -479,14 +499,12 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) chunk_output_kernel(Chu
           for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], Vf.f[nb][ks], ab);
         }
       }
-      // lane holds o[t0 + 16 jb + r16][wcol + 16 nb + 4 g + 0..3]; stored next
-      // iteration.  Rows past the end of the sequence fall outside the descriptor.
-      state_update<T, DK, DVS>(S, Vf, sm.kp, exp_e(sbc[63]), lane);
+      state_update<T, DK, DVS>(S, Vf, sm.kp, exp_e(cd.gam), lane);
+      // lane holds o[t0 + 16 jb + r16][wcol + 16 nb + 4 g + 0..3]
+      store_o(O, t0, false);
     }
     __syncthreads();
   }
-
-  if (c_begin < c_end) store_o();  // the last chunk's o
 
   if (seg == p.segments - 1) {
 #pragma unroll

@@ -64,7 +64,7 @@ extern "C" {
 #define GLA_ABI_VERSION 1
 #define GLA_CHUNK 64          /* tokens per chunk */
 #define GLA_TILE 16           /* tokens per tile inside a chunk [LCT §3.2] */
-#define GLA_MAX_SEGMENTS 16   /* upper bound on gla_plan_t.segments */
+#define GLA_MAX_SEGMENTS 64   /* upper bound on gla_plan_t.segments */
 
 typedef enum {
   GLA_OK = 0,

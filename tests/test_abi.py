@@ -84,7 +84,7 @@ def test_workspace_query_with_explicit_plan(lib):
     (dict(B=0), SHAPE), (dict(H=-1), SHAPE), (dict(T=-5), SHAPE),
     (dict(dk=32), SHAPE), (dict(dk=96), SHAPE), (dict(dv=256), SHAPE), (dict(dv=48), SHAPE),
     (dict(dtype=7), DTYPE), (dict(gate=3), ARG), (dict(path=5), ARG),
-    (dict(plan=(0, 1)), PLAN), (dict(plan=(17, 1)), PLAN), (dict(plan=(5, 1)), PLAN),  # 4 chunks < 5 segs
+    (dict(plan=(0, 1)), PLAN), (dict(plan=(65, 1)), PLAN), (dict(plan=(5, 1)), PLAN),  # 4 chunks < 5 segs
     (dict(plan=(1, 3)), PLAN), (dict(plan=(1, 16)), PLAN), (dict(plan=(1, 8)), PLAN),  # 64/8 = 8 cols
 ])
 def test_bad_sizes_and_enums(lib, kw, code):
