@@ -1,0 +1,156 @@
+// chunk_common.h -- pieces shared by the chunk kernels: launch shape of the
+// compute waves, causal tile numbering, chunk decay scalars and the MFMA state
+// update.
+#pragma once
+
+#include "gla_device.h"
+#include "gla_internal.h"
+
+namespace gla {
+
+template <typename T, int DK, int DVS>
+struct Cfg {
+  static constexpr int NB = DVS >= 32 ? 2 : 1;         // 16-column blocks per wave
+  static constexpr int CPW = 16 * NB;                  // value columns per wave
+  static constexpr int NW = DVS / CPW;                 // waves per workgroup
+  static constexpr int NT = 64 * NW;                   // threads per workgroup
+
+  static constexpr int PAD = Elem<T>::kPad;
+  static constexpr int QLD = DK + PAD;   // row stride of Qh, Kh (and raw q, k)
+  static constexpr int TLD = 64 + PAD;   // row stride of the attention matrix A
+  static constexpr int QU = 8 * DK / NT;   // 8-element q (and k) units per thread per chunk
+  static constexpr int VU = 8 * DVS / NT;  // 8-element v units per thread per chunk
+  static constexpr int DB = DK / 16;       // 16-row blocks of the key dimension
+  static constexpr int KS = DK / 32;       // K-steps over the key dimension
+  static_assert(QU >= 1 && 8 * DK == QU * NT, "q staging must divide evenly");
+  static_assert(VU >= 1 && 8 * DVS == VU * NT, "v staging must divide evenly");
+};
+
+// Causal 16x16 tiles of a 64x64 chunk, (query tile jb, key tile ib) with ib <= jb,
+// numbered row by row: 0 -> (0,0), 1 -> (1,0), 2 -> (1,1), 3 -> (2,0), ...  The
+// strictly-below-diagonal tiles are numbered the same way without the diagonal.
+// Evaluated at compile time inside unrolled loops (no table in memory).
+__host__ __device__ constexpr int tri_j(int t) { return t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0; }
+__host__ __device__ constexpr int tri_i(int t) { return t - tri_j(t) * (tri_j(t) + 1) / 2; }
+__host__ __device__ constexpr int off_j(int t) { return t >= 3 ? 3 : t >= 1 ? 2 : 1; }
+__host__ __device__ constexpr int off_i(int t) { return t - (off_j(t) - 1) * off_j(t) / 2; }
+static_assert(tri_j(9) == 3 && tri_i(9) == 3 && tri_j(4) == 2 && tri_i(4) == 1, "tile numbering");
+static_assert(off_j(5) == 3 && off_i(5) == 2 && off_j(2) == 2 && off_i(2) == 1, "tile numbering");
+
+// Per-head buffer descriptors of the streamed tensors.
+struct HeadBuffers {
+  rsrc_t q, k, v, b, o;
+};
+
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Cumulative log-decay of one chunk: lane j of every wave holds b_j; the tile
+// boundaries are read out once per chunk as wave-uniform scalars.
+struct ChunkDecay {
+  float b;               // b_j for this lane's token j
+  float r1, r2, r3, gam; // b_15, b_31, b_47, b_63
+  __device__ __forceinline__ explicit ChunkDecay(float bl)
+      : b(bl), r1(lane_value(bl, 15)), r2(lane_value(bl, 31)), r3(lane_value(bl, 47)), gam(lane_value(bl, 63)) {}
+  // r_u = b_{16u-1}, the cumulative decay before tile u (r_0 = 0)
+  __device__ __forceinline__ float r(int u) const { return u == 0 ? 0.0f : u == 1 ? r1 : u == 2 ? r2 : r3; }
+  // E_u = b_{16u+15}, the cumulative decay at the end of tile u
+  __device__ __forceinline__ float end(int u) const { return u == 0 ? r1 : u == 1 ? r2 : u == 2 ? r3 : gam; }
+  // b of another token of the chunk
+  __device__ __forceinline__ float at(int j) const { return __shfl(b, j); }
+};
+
+// fp32 state slice of one wave: S[d = 16 db + 4 g + e][n = 16 nb + r16], e = 0..3
+template <typename T, int DK, int DVS>
+struct StateAcc {
+  floatx4 s[Cfg<T, DK, DVS>::NB][Cfg<T, DK, DVS>::DB];
+};
+
+// v[n][i] operand fragments of one wave for the chunk's two token K-steps
+template <typename T, int DK, int DVS>
+struct VFrags {
+  typename Elem<T>::Frag f[Cfg<T, DK, DVS>::NB][2];
+};
+
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void state_update(StateAcc<T, DK, DVS>& S, const VFrags<T, DK, DVS>& Vf,
+                                             const T* kp, float decay, int lane) {
+  using E = Elem<T>;
+  using C = Cfg<T, DK, DVS>;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) S.s[nb][db] *= decay;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      const typename E::Frag ka = TokTile<T, DK>::load(kp, ks * 32, db * 16, lane);
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb) E::mfma(S.s[nb][db], ka, Vf.f[nb][ks]);
+    }
+  }
+}
+
+// v fragments of one wave's columns for both token K-steps of the chunk
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void load_v_frags(VFrags<T, DK, DVS>& Vf, const T* vv, int wave, int lane) {
+  using C = Cfg<T, DK, DVS>;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) Vf.f[nb][ks] = TokTile<T, DVS>::load(vv, ks * 32, wave * C::CPW + nb * 16, lane);
+}
+
+// Initial state of a segment: S0 (or zero), folded with the local final states of
+// the earlier segments of the same head, S <- e^{Gamma_p} S + H_p for p < seg.
+// The wave's slice of S: d = 16 db + 4 g + e, n = wcol + 16 nb + r16.
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void load_initial_state(StateAcc<T, DK, DVS>& S, const ChunkParams& p, int bh, int seg,
+                                                   int wcol, int g, int r16) {
+  using C = Cfg<T, DK, DVS>;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = db * 16 + 4 * g + e;
+        const int n = wcol + nb * 16 + r16;
+        S.s[nb][db][e] = p.S0 ? p.S0[((long long)bh * DK + d) * p.dv + n] : 0.0f;
+      }
+  for (int ps = 0; ps < seg; ++ps) {
+    const float f = exp_e(p.seg_decay[(long long)bh * p.segments + ps]);
+    const float* H = p.seg_state + ((long long)bh * (p.segments - 1) + ps) * DK * p.dv;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int d = db * 16 + 4 * g + e;
+          const int n = wcol + nb * 16 + r16;
+          S.s[nb][db][e] = f * S.s[nb][db][e] + H[(long long)d * p.dv + n];
+        }
+  }
+}
+
+// Writes the wave's slice of a state to dst [dk][dv] (one head).
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void store_state(const StateAcc<T, DK, DVS>& S, float* dst, int dv, int wcol, int g,
+                                            int r16) {
+  using C = Cfg<T, DK, DVS>;
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = db * 16 + 4 * g + e;
+        const int n = wcol + nb * 16 + r16;
+        dst[(long long)d * dv + n] = S.s[nb][db][e];
+      }
+}
+
+}  // namespace gla
