@@ -464,12 +464,14 @@ bool chunk_config_built(int dtype, int dk, int slice, bool diag) {
 
 hipError_t launch_segment_states(const ChunkParams& p, int dtype, hipStream_t stream) {
   if (p.segments <= 1 || p.grid == 0) return hipSuccess;
+  if (ws_kernels_supported(dtype, p.dk, p.dv / p.nslices))
+    return launch_segment_states_ws(p, p.dk, p.dv / p.nslices, stream);
   return dispatch(dtype, p.dk, p.dv / p.nslices, false, SegFn{p, stream});
 }
 
 hipError_t launch_chunk_output(const ChunkParams& p, int dtype, bool diag, hipStream_t stream) {
   if (p.grid == 0) return hipSuccess;
-  if (chunk_output_ws_supported(dtype, p.dk, p.dv / p.nslices))
+  if (ws_kernels_supported(dtype, p.dk, p.dv / p.nslices))
     return launch_chunk_output_ws(p, p.dk, p.dv / p.nslices, diag, stream);
   return dispatch(dtype, p.dk, p.dv / p.nslices, diag, OutFn{p, stream});
 }

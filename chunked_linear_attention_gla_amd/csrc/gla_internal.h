@@ -35,9 +35,11 @@ hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long 
 bool chunk_config_built(int dtype, int dk, int slice, bool diag);
 hipError_t launch_segment_states(const ChunkParams& p, int dtype, hipStream_t stream);
 hipError_t launch_chunk_output(const ChunkParams& p, int dtype, bool diag, hipStream_t stream);
-// The wave-specialised output pass (output_ws.hip) covers bf16, dk in {64, 128},
-// slices of 32, 64 or 128 columns; launch_chunk_output routes those to it.
-bool chunk_output_ws_supported(int dtype, int dk, int slice);
+// The wave-specialised kernels (ws_kernels.hip) cover bf16, dk in {64, 128},
+// slices of 32, 64 or 128 columns; launch_chunk_output and launch_segment_states
+// route those to them.
+bool ws_kernels_supported(int dtype, int dk, int slice);
 hipError_t launch_chunk_output_ws(const ChunkParams& p, int dk, int slice, bool diag, hipStream_t stream);
+hipError_t launch_segment_states_ws(const ChunkParams& p, int dk, int slice, hipStream_t stream);
 
 }  // namespace gla

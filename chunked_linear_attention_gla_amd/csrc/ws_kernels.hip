@@ -1,5 +1,6 @@
-// output_ws.hip -- wave-specialised output pass of the chunked GLA forward (bf16
-// operands, fp32 accumulation) for gfx950.
+// ws_kernels.hip -- wave-specialised kernels of the chunked GLA forward (bf16
+// operands, fp32 accumulation) for gfx950: the output pass and the segment
+// pre-pass.
 //
 // Sources (web pages; cited by title and section):
 //   [LCT] "Engineering Long-Context Training for Trillion-Parameter MoE Models:
@@ -79,13 +80,13 @@ struct WsSmem {
 // piece; the swizzle puts them in different banks.
 __device__ __forceinline__ int raw_piece(int p, int r) { return p ^ ((r >> 2) & 3); }
 
-// Registers of one staging thread holding a chunk of q, k, v (and b) between
-// its loads and its LDS writes.  Rows past the end read as zeros (buffer range
-// check); b past the end repeats the last value (absent tokens have g = 0).
-template <int DK, int DVS>
+// Registers of one staging thread holding a chunk of q (LOAD_Q), k, v and b
+// between its loads and its LDS writes.  Rows past the end read as zeros (buffer
+// range check); b past the end repeats the last value (absent tokens have g = 0).
+template <int DK, int DVS, bool LOAD_Q = true>
 struct WsStaged {
   static constexpr int QU = 8 * DK / 256, VU = 8 * DVS / 256;
-  uint4 q[QU], k[QU], v[VU];
+  uint4 q[LOAD_Q ? QU : 1], k[QU], v[VU];
   float b;
 
   __device__ __forceinline__ void load(const HeadBuffers& hb, uint32_t t0, uint32_t len, int dv, int col0, int st) {
@@ -96,7 +97,7 @@ struct WsStaged {
       const int u = st + m * 256;
       const int row = u / (DK / 8), c8 = u % (DK / 8);
       const uint32_t off = ((t0 + row) * DK + c8 * 8) * 2u;
-      q[m] = buf_load16(hb.q, off);
+      if (LOAD_Q) q[m] = buf_load16(hb.q, off);
       k[m] = buf_load16(hb.k, off);
     }
 #pragma unroll
@@ -389,19 +390,144 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
   }
 }
 
+// ============================================================================
+// Segment pre-pass: local final state (from a zero state) and total log-decay of
+// every segment but the last, for the output pass to fold into its initial state.
+// Same split as the output pass: staging waves load chunk c+2 and write
+// k e^{gamma - b} and v of chunk c+1 into the second buffer set while the compute
+// waves apply chunk c to their state slice; one barrier per chunk.
+// ============================================================================
+template <int DK, int DVS>
+struct WsSegSmem {
+  using W = WsCfg<DK, DVS, false>;
+  bf16 kp[2][64 * W::LD];   // k_i e^{gamma - b_i}, [i][d]
+  bf16 vv[2][64 * W::VLD];  // v[i][n]
+  float gam[2];             // gamma of the chunk in each buffer set
+};
+
+template <int DK, int DVS>
+__global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_kernel(ChunkParams p) {
+  using W = WsCfg<DK, DVS, false>;
+  using C = typename W::C;
+  using E = Elem<bf16>;
+  __shared__ WsSegSmem<DK, DVS> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool compute = wave < W::NCW;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nseg = p.segments - 1;
+  const int L = xcd_linear_index(blockIdx.x, p.grid);
+  const int slice = L % p.nslices;
+  const int rest = L / p.nslices;
+  const int seg = rest % nseg;
+  const int bh = rest / nseg;
+  const int col0 = slice * DVS;
+  const int cw = compute ? wave : 0;
+  const int sw = compute ? 0 : wave - W::NCW;
+  const int st = compute ? 0 : tid - 64 * W::NCW;
+  const int wcol = col0 + cw * C::CPW;
+  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
+
+  if (compute) {
+    StateAcc<bf16, DK, DVS> S;
+#pragma unroll
+    for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) S.s[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
+    float gsum = 0.0f;  // total log-decay of the segment
+    __syncthreads();
+    for (int c = c_begin; c < c_end; ++c) {
+      const int slot = (c - c_begin) & 1;
+      const float gam = sm.gam[slot];
+      gsum += gam;
+      VFrags<bf16, DK, DVS> Vf;
+      load_v_frags<bf16, DK, DVS>(Vf, sm.vv[slot], cw, lane);
+      state_update<bf16, DK, DVS>(S, Vf, sm.kp[slot], exp_e(gam), lane);
+      __syncthreads();
+    }
+    store_state<bf16, DK, DVS>(S, p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv, p.dv, wcol, g, r16);
+    if (slice == 0 && tid == 0) p.seg_decay[(long long)bh * p.segments + seg] = gsum;
+  } else {
+    const uint32_t Tn = (uint32_t)p.T;
+    HeadBuffers hb;
+    hb.k = make_rsrc(static_cast<const bf16*>(p.k) + (long long)bh * p.T * DK, Tn * DK * 2u);
+    hb.v = make_rsrc(static_cast<const bf16*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * 2u);
+    hb.b = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+    const auto stage = [&](const WsStaged<DK, DVS, false>& stg, int ns) {
+      const ChunkDecay cd(stg.b);
+      float brow[W::QU];
+#pragma unroll
+      for (int m = 0; m < W::QU; ++m) brow[m] = cd.at((st + m * 256) / (DK / 8));
+#pragma unroll
+      for (int m = 0; m < W::QU; ++m) {
+        const int u = st + m * 256;
+        const int row = u / (DK / 8), c8 = u % (DK / 8);
+        E::Vec8 kv;
+        kv.u = stg.k[m];
+        E::store8_scaled(sm.kp[ns] + row * W::LD + c8 * 8, kv, exp_e(cd.gam - brow[m]));
+      }
+#pragma unroll
+      for (int m = 0; m < W::VU; ++m) {
+        const int u = st + m * 256;
+        const int row = u / (DVS / 8), c8 = u % (DVS / 8);
+        *reinterpret_cast<uint4*>(sm.vv[ns] + row * W::VLD + c8 * 8) = stg.v[m];
+      }
+      if (sw == 0 && lane == 0) sm.gam[ns] = cd.gam;
+    };
+    const auto chunk_t0 = [&](int c) { return (uint32_t)min(c, c_end - 1) * kChunk; };
+    // register set s0: chunks at even offsets from c_begin, s1: odd offsets
+    WsStaged<DK, DVS, false> s0, s1;
+    if (c_begin < c_end) {
+      s0.load(hb, chunk_t0(c_begin), Tn, p.dv, col0, st);
+      stage(s0, 0);
+      s1.load(hb, chunk_t0(c_begin + 1), Tn, p.dv, col0, st);
+      s0.load(hb, chunk_t0(c_begin + 2), Tn, p.dv, col0, st);
+    }
+    __syncthreads();
+    int c = c_begin;
+    for (; c + 1 < c_end; c += 2) {
+      stage(s1, 1);
+      s1.load(hb, chunk_t0(c + 3), Tn, p.dv, col0, st);
+      __syncthreads();
+      stage(s0, 0);
+      s0.load(hb, chunk_t0(c + 4), Tn, p.dv, col0, st);
+      __syncthreads();
+    }
+    if (c < c_end) __syncthreads();
+    // no loads left in flight when the wave ends
+    __builtin_amdgcn_s_waitcnt(0);
+  }
+}
+
+template <int DK, int DVS>
+hipError_t ws_seg_launch(const ChunkParams& p, hipStream_t s) {
+  hipLaunchKernelGGL((segment_state_ws_kernel<DK, DVS>), dim3(p.grid), dim3(WsCfg<DK, DVS, false>::NT), 0, s, p);
+  return hipGetLastError();
+}
+
 template <int DK, int DVS, bool DIAG>
 hipError_t ws_launch(const ChunkParams& p, hipStream_t s) {
   hipLaunchKernelGGL((chunk_output_ws_kernel<DK, DVS, DIAG>), dim3(p.grid), dim3(WsCfg<DK, DVS, DIAG>::NT), 0, s, p);
   return hipGetLastError();
 }
 
-bool chunk_output_ws_supported(int dtype, int dk, int slice) {
+bool ws_kernels_supported(int dtype, int dk, int slice) {
   return dtype == 0 && (dk == 64 || dk == 128) && (slice == 32 || slice == 64 || slice == 128);
 }
 
 hipError_t launch_chunk_output_ws(const ChunkParams& p, int dk, int slice, bool diag, hipStream_t stream) {
 #define GLA_WS_CASE(DKV, DVSV)                                                                   \
   if (dk == DKV && slice == DVSV) return diag ? ws_launch<DKV, DVSV, true>(p, stream) : ws_launch<DKV, DVSV, false>(p, stream);
+  GLA_WS_CASE(128, 128) GLA_WS_CASE(128, 64) GLA_WS_CASE(128, 32)
+  GLA_WS_CASE(64, 128) GLA_WS_CASE(64, 64) GLA_WS_CASE(64, 32)
+#undef GLA_WS_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_segment_states_ws(const ChunkParams& p, int dk, int slice, hipStream_t stream) {
+#define GLA_WS_CASE(DKV, DVSV) \
+  if (dk == DKV && slice == DVSV) return ws_seg_launch<DKV, DVSV>(p, stream);
   GLA_WS_CASE(128, 128) GLA_WS_CASE(128, 64) GLA_WS_CASE(128, 32)
   GLA_WS_CASE(64, 128) GLA_WS_CASE(64, 64) GLA_WS_CASE(64, 32)
 #undef GLA_WS_CASE
