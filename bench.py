@@ -9,8 +9,11 @@ output kernel, enqueued through the C ABI on the current stream.
 Prints one JSON line.  `value` is tokens/s (batch * sequence tokens, all heads) of
 the whole step; `roofline` is the fused output kernel (the dominant kernel): its
 algorithmic HBM bytes per launch over its average launch time, measured with HIP
-events on the stream it runs on, against the 8 TB/s HBM3E peak; `cpu_baseline` is
-the fp64 CPU oracle timed on a bounded sample of the same workload on this host.
+events on the stream it runs on, against the 8 TB/s HBM3E peak; `ablation` times the
+diagonal-branch variant (negative-softplus gate, diagonal tiles by position pairs)
+on its own strong-decay inputs beside the unified path on the same inputs;
+`cpu_baseline` is the fp64 CPU oracle timed on a bounded sample of the same workload
+on this host.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload bf16_64k_strong]
 """
@@ -31,7 +34,10 @@ METRIC = "tokens/s and MFMA TFLOP/s (% bf16 peak), chunked GLA fwd at T=64K, d=1
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 KERNEL_SOURCES = ["chunked_linear_attention_gla_amd/csrc/chunk_kernels.hip",
+                  "chunked_linear_attention_gla_amd/csrc/ws_kernels.hip",
+                  "chunked_linear_attention_gla_amd/csrc/chunk_common.h",
                   "chunked_linear_attention_gla_amd/csrc/gla_device.h"]
+ABLATION_WORKLOAD = "bf16_64k_strong_softplus"
 
 
 def kernel_source_sha() -> str:
@@ -65,6 +71,7 @@ def parse():
     ap.add_argument("--plan", default=None, help="segments,dv_split (default: the library's plan)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ablation", action="store_true", help="skip the diagonal-branch comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration) and exit")
     return ap.parse_args()
@@ -108,10 +115,18 @@ def cpu_baseline(w, target_s: float):
                       f"fp64 sequential recurrence, OpenMP over heads x 16-column blocks; {dt:.1f} s"}
 
 
-def load_traffic(workload: str, plan, path: str):
+def output_kernel_name(dtype_bytes: int, dk: int, slice_cols: int) -> str:
+    # the library runs the wave-specialised output pass for bf16 with dk in {64, 128}
+    # and slices of 32, 64 or 128 value columns, the plain one otherwise
+    if dtype_bytes == 2 and dk in (64, 128) and slice_cols in (32, 64, 128):
+        return "chunk_output_ws_kernel"
+    return "chunk_output_kernel"
+
+
+def load_traffic(kernel: str, workload: str, plan, path: str):
     """HBM traffic of the output kernel from committed rocprofv3 counter runs, only if
     they were taken on the kernel source and plan in use now."""
-    fn = os.path.join(ROOT, "profiles", f"chunk_output_kernel_{workload}_traffic.json")
+    fn = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
     if not os.path.exists(fn):
         return None
     with open(fn) as f:
@@ -120,6 +135,61 @@ def load_traffic(workload: str, plan, path: str):
             or rec.get("path", "unified") != path:
         return None
     return rec.get("bytes_per_launch")
+
+
+class StepTimer:
+    """One workload, one path: inputs, outputs and workspace on the device, and a step
+    that enqueues the gate + cumsum kernel, the segment pre-pass and the output pass,
+    with optional HIP events between them on the current stream."""
+
+    def __init__(self, gla, gin, torch, w, path, plan=None):
+        dev = torch.device("cuda:0")
+        self.gla, self.torch, self.w, self.path = gla, torch, w, path
+        inp = gin.make_inputs(w, dev)
+        self.q, self.k, self.v, self.x, self.S0 = inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"]
+        B, H, T, dk = self.q.shape
+        dv = self.v.shape[-1]
+        self.shape = (B, H, T, dk, dv)
+        dt_code = gla.GLA_BF16 if self.q.dtype == torch.bfloat16 else gla.GLA_F32
+        self.plan = plan or gla.plan_default(B, H, T, dk, dv, dt_code, path)
+        self.o = torch.empty(B, H, T, dv, device=dev, dtype=torch.float32)
+        self.ST = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+        self.b = torch.empty(B, H, T, device=dev, dtype=torch.float32)
+        seg_bytes = gla.segment_workspace_size(B, H, T, dk, dv, self.plan)
+        self.seg = torch.empty(max(seg_bytes, 256), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self, evs=None):
+        gla, plan = self.gla, self.plan
+        if evs is not None:
+            evs[0].record()
+        gla.gate_cumsum(self.x, gate=self.w.gate, out=self.b)
+        if evs is not None:
+            evs[1].record()
+        if plan.segments > 1:
+            gla.segment_states(self.k, self.v, self.b, plan, self.seg)
+        if evs is not None:
+            evs[2].record()
+        gla.chunk_output(self.q, self.k, self.v, self.b, self.S0, plan, self.seg if plan.segments > 1 else None,
+                         self.o, self.ST, path=self.path)
+        if evs is not None:
+            evs[3].record()
+
+    def run(self, steps, warmup):
+        """Returns (ms per step from the host clock, [gate, pre-pass, output] ms from events)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            self.step(events[i])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        stage = [sum(e[j].elapsed_time(e[j + 1]) for e in events) / steps for j in range(3)]
+        return elapsed * 1e3 / steps, stage
 
 
 def main():
@@ -138,66 +208,24 @@ def main():
 
     w = gin.WORKLOADS[args.workload]
     path = args.path or "unified"
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    inp = gin.make_inputs(w, dev)
-    q, k, v, x, S0 = inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"]
-    B, H, T, dk = q.shape
-    dv = v.shape[-1]
-    dt_code = gla.GLA_BF16 if q.dtype == torch.bfloat16 else gla.GLA_F32
-    if args.plan:
-        plan = gla.Plan(*(int(s) for s in args.plan.split(",")))
-    else:
-        plan = gla.plan_default(B, H, T, dk, dv, dt_code, path)
-    o = torch.empty(B, H, T, dv, device=dev, dtype=torch.float32)
-    ST = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
-    b = torch.empty(B, H, T, device=dev, dtype=torch.float32)
-    seg_bytes = gla.segment_workspace_size(B, H, T, dk, dv, plan)
-    seg = torch.empty(max(seg_bytes, 256), dtype=torch.uint8, device=dev)
-    torch.cuda.synchronize()
+    torch.cuda.set_device(torch.device("cuda:0"))
+    plan = gla.Plan(*(int(s) for s in args.plan.split(","))) if args.plan else None
+    timer = StepTimer(gla, gin, torch, w, path, plan)
+    plan = timer.plan
+    ms_step, (ms_gate, ms_seg, ms_out) = timer.run(args.steps, args.warmup)
+    B, H, T, dk, dv = timer.shape
+    es = timer.q.element_size()
+    S0 = timer.S0
+    del timer
 
-    n_ev = 4
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record()
-        gla.gate_cumsum(x, gate=w.gate, out=b)
-        if evs is not None:
-            evs[1].record()
-        if plan.segments > 1:
-            gla.segment_states(k, v, b, plan, seg)
-        if evs is not None:
-            evs[2].record()
-        gla.chunk_output(q, k, v, b, S0, plan, seg if plan.segments > 1 else None, o, ST, path=path)
-        if evs is not None:
-            evs[3].record()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    if torch.distributed.is_available() and torch.distributed.is_initialized():
-        torch.distributed.barrier()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    if torch.distributed.is_available() and torch.distributed.is_initialized():
-        torch.distributed.barrier()
-
-    stage_ms = [[e[j].elapsed_time(e[j + 1]) for e in events] for j in range(n_ev - 1)]
-    avg = lambda xs: sum(xs) / len(xs)
-    ms_gate, ms_seg, ms_out = (avg(s) for s in stage_ms)
-    ms_step = elapsed * 1e3 / args.steps
     tokens = B * T
     value = tokens / (ms_step / 1e3)
-    es = q.element_size()
     bh = B * H
     bytes_out = bh * T * algorithmic_bytes_per_token_head(dk, dv, es) + bh * dk * dv * 4 * (2 if S0 is not None else 1)
     flops = bh * T * algorithmic_flops_per_token_head(dk, dv)
     achieved = bytes_out / (ms_out / 1e3) / 1e9
-    traffic = load_traffic(w.name, plan, path)
+    kname = output_kernel_name(es, dk, dv // plan.dv_split)
+    traffic = load_traffic(kname, w.name, plan, path)
     tflops = flops / (ms_step / 1e3) / 1e12
 
     result = {
@@ -221,7 +249,7 @@ def main():
         "stage_ms": {"gate_cumsum": round(ms_gate, 4), "segment_states": round(ms_seg, 4),
                      "chunk_output": round(ms_out, 4)},
         "roofline": {
-            "kernel": "chunk_output_kernel",
+            "kernel": kname,
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -232,6 +260,22 @@ def main():
             "avg_launch_ms": round(ms_out, 4),
         },
     }
+    if w.name == gin.HEADLINE and path == "unified" and not args.plan and not args.no_ablation:
+        # the pages' comparison: conventional gate + diagonal branch against the unified
+        # path, both on the ablation's own inputs (same shapes, strong decay)
+        wa = gin.WORKLOADS[ABLATION_WORKLOAD]
+        steps_a = min(args.steps, 20)
+        abl = {"workload": wa.name, "gate": wa.gate, "x": f"N({wa.x_mean},{wa.x_std})", "steps": steps_a}
+        for p_ in ("diag_branch", "unified"):
+            t = StepTimer(gla, gin, torch, wa, p_)
+            ms_a, st_a = t.run(steps_a, min(args.warmup, 5))
+            abl[p_] = {"ms_per_step": round(ms_a, 4), "chunk_output_ms": round(st_a[2], 4),
+                       "tokens_per_s": round(wa.B * wa.T / (ms_a / 1e3), 1)}
+            del t
+        abl["unified_speedup_step"] = round(abl["diag_branch"]["ms_per_step"] / abl["unified"]["ms_per_step"], 3)
+        abl["unified_speedup_output_kernel"] = round(
+            abl["diag_branch"]["chunk_output_ms"] / abl["unified"]["chunk_output_ms"], 3)
+        result["ablation"] = abl
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
