@@ -166,6 +166,18 @@ def test_diag_branch_matches_oracle(gate, x_mean):
     check(inp, w, path="diag_branch", gate=gate, plan=gla.Plan(3, 4))
 
 
+@pytest.mark.parametrize("dk,dv,plan,path", [
+    (64, 64, (2, 2), "unified"), (64, 128, (3, 4), "diag_branch"), (128, 128, (5, 1), "diag_branch"),
+    (64, 64, (1, 1), "diag_branch"), (128, 64, (2, 2), "diag_branch"), (128, 128, (17, 1), "unified")])
+def test_wave_specialised_shapes(dk, dv, plan, path):
+    """Head dims, slice widths (32, 64, 128 columns: 1, 2 or 4 compute waves) and
+    segment lengths (odd, even, single chunk) of the wave-specialised kernels, both
+    paths; 17 chunks of 64 plus a ragged tail."""
+    gate = "neg_softplus" if path == "diag_branch" else "bounded"
+    w, inp = small(17 * 64 + 9, H=2, dk=dk, dv=dv, x_mean=-2.0 if path == "diag_branch" else 0.0, gate=gate)
+    check(inp, w, plan=gla.Plan(*plan), path=path, gate=gate)
+
+
 def test_diag_branch_fp32():
     w, inp = small(64 * 4 + 3, H=2, dk=64, dv=64, qkv="f32", x_mean=-4.0, gate="neg_softplus")
     check(inp, w, path="diag_branch", gate="neg_softplus")
