@@ -13,13 +13,16 @@ Sources (web pages; cited by title and section):
   [ESU] "Engineering Stability in Ultra-Long Context and Trillion-Parameter
          Sparse Models"
 
-Three independent formulations live here:
+Three independent formulations of the forward pass live here, and the backward
+pass of the recurrence:
 
 * :func:`forward` -- the sequential recurrence, one token at a time, in C (fp64,
   OpenMP over heads and value-column blocks).  This is the oracle proper.
 * :func:`closed_form` -- the quadratic form, numpy fp64, with every decay weight
   formed as an explicit product of per-token decays (no cumulative sums, no
   exponent differences).  Used to pin :func:`forward` on tiny inputs.
+* :func:`backward` -- the reverse-mode chain rule of the same recurrence, one token
+  at a time, in C (fp64): dq, dk, dv, dx and dS0 from dO and dS_T.
 * :func:`gate` / :func:`chunk_local_cumsum` -- the log-decay of [LCT §3.2] and the
   chunk-local inclusive cumulative sum of it, the per-position cumulative decay
   Gamma of [LCT §3.1] in log form, restarted at each chunk.
@@ -84,6 +87,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_longlong, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int]
+    lib.gla_oracle_backward.restype = ctypes.c_int
+    lib.gla_oracle_backward.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_longlong, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
     lib.gla_oracle_gate.restype = ctypes.c_double
     lib.gla_oracle_gate.argtypes = [ctypes.c_double, ctypes.c_int]
     lib.gla_oracle_max_threads.restype = ctypes.c_int
@@ -141,6 +150,52 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, x: np.ndarray,
     if rc != 0:
         raise ValueError(f"gla_oracle_forward rejected its arguments (rc={rc})")
     return o, ST
+
+
+def backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, x: np.ndarray, dO: np.ndarray,
+             S0: Optional[np.ndarray] = None, dST: Optional[np.ndarray] = None, gate="bounded",
+             nthreads: int = 0, lib_path: str = LIB_PATH):
+    """Reverse-mode gradients of the recurrence (fp64, one token at a time, in C).
+
+    Inputs as for :func:`forward`, plus dO = dL/do [..., T, dv] and dST = dL/dS_T
+    [..., dk, dv] (None: zero), any float dtype (widened to float64).
+    Returns (dq, dk [..., T, dk], dv [..., T, dv], dx [..., T], dS0 [..., dk, dv]),
+    all float64, with L the scalar whose partials dO and dST are.
+    """
+    kind = _qkv_kind(q)
+    if _qkv_kind(k) != kind or _qkv_kind(v) != kind:
+        raise TypeError("q, k, v must share a storage kind")
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or x.shape != lead + (T,) \
+            or dO.shape != lead + (T, dv):
+        raise ValueError("shape mismatch")
+    BH = int(np.prod(lead)) if lead else 1
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    dO = np.ascontiguousarray(dO, dtype=np.float64)
+    if S0 is not None:
+        S0 = np.ascontiguousarray(S0, dtype=np.float64)
+    if dST is not None:
+        dST = np.ascontiguousarray(dST, dtype=np.float64)
+    for a in (S0, dST):
+        if a is not None and a.shape != lead + (dk, dv):
+            raise ValueError("state shape mismatch")
+    dq = np.empty(lead + (T, dk))
+    dk_ = np.empty(lead + (T, dk))
+    dv_ = np.empty(lead + (T, dv))
+    dx = np.empty(lead + (T,))
+    dS0 = np.empty(lead + (dk, dv))
+    lib = load(lib_path)
+    rc = lib.gla_oracle_backward(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, kind, x.ctypes.data,
+        None if S0 is None else S0.ctypes.data, dO.ctypes.data, None if dST is None else dST.ctypes.data,
+        dq.ctypes.data, dk_.ctypes.data, dv_.ctypes.data, dx.ctypes.data, dS0.ctypes.data,
+        BH, T, dk, dv, gate_id(gate), nthreads)
+    if rc != 0:
+        raise ValueError(f"gla_oracle_backward failed (rc={rc})")
+    return dq, dk_, dv_, dx, dS0
 
 
 # --------------------------------------------------------------------------- numpy parts

@@ -39,6 +39,9 @@
  * rounding).  Every value is widened to double before any arithmetic, and all
  * arithmetic is double.
  *
+ * The backward pass (gla_oracle_backward) is the reverse-mode chain rule of the
+ * same recurrence, also one token at a time; see its comment.
+ *
  * Layouts (row-major, contiguous; BH = batch * heads, heads independent):
  *   q, k [BH][T][dk]   v [BH][T][dv]   x [BH][T]   S0 [BH][dk][dv] or NULL
  *   o    [BH][T][dv]   S_T [BH][dk][dv]             (outputs, double)
@@ -186,6 +189,140 @@ int gla_oracle_forward(const void* q, const void* k, const void* v, int qkv_is_b
     free(vt);
   }
   return 0;
+}
+
+/* d g / d x of the gate: bounded -5 sigmoid(x) (1 - sigmoid(x)); negative
+ * softplus -softplus(-x) has derivative sigmoid(-x). */
+static double gate_slope(double x, int gate) {
+  if (gate == ORACLE_GATE_NEG_SOFTPLUS) return sigmoid(-x);
+  const double s = sigmoid(x);
+  return -5.0 * s * (1.0 - s);
+}
+
+/* Backward pass of the recurrence, by the reverse-mode chain rule one token at a
+ * time.  Given dO = dL/do [BH][T][dv] and dS_T = dL/dS_T [BH][dk][dv] (NULL: zero),
+ * with D_t = dL/dS_t through o_t and every later state,
+ *
+ *     D_{T-1} = q_{T-1} dO_{T-1}^T + dS_T
+ *     D_t     = q_t dO_t^T + a_{t+1} D_{t+1}
+ *     dq_t = S_t dO_t        dk_t = D_t v_t        dv_t = D_t^T k_t
+ *     dL/da_t = <D_t, S_{t-1}>  (Frobenius),  dx_t = dL/da_t * a_t * g'(x_t)
+ *     dS0 = a_0 D_0
+ *
+ * S_t is needed in reverse order; it is recomputed forward inside blocks of 64
+ * tokens from checkpoints of S taken on a first forward sweep (the recurrence is
+ * never run backwards).  Outputs are double: dq, dk [BH][T][dk], dv [BH][T][dv],
+ * dx [BH][T], dS0 [BH][dk][dv].  Heads run in parallel (OpenMP).
+ * Returns 0 on success, 1 on a bad argument, 2 when memory runs out. */
+int gla_oracle_backward(const void* q, const void* k, const void* v, int qkv_is_bf16,
+                        const float* x, const double* S0, const double* dO, const double* dST,
+                        double* dq, double* dk, double* dv, double* dx, double* dS0,
+                        long long BH, long long T, int dkd, int dvd, int gate, int nthreads) {
+  if (!q || !k || !v || !x || !dO || !dq || !dk || !dv || !dx || !dS0) return 1;
+  if (BH < 0 || T < 0 || dkd <= 0 || dvd <= 0) return 1;
+  if (gate != ORACLE_GATE_BOUNDED_SIGMOID && gate != ORACLE_GATE_NEG_SOFTPLUS) return 1;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+  const long long B = 64;  /* tokens per recompute block */
+  const long long nblk = (T + B - 1) / B;
+  const size_t SZ = (size_t)dkd * (size_t)dvd;
+  int failed = 0;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long long bh = 0; bh < BH; ++bh) {
+    double* ck = (double*)malloc(sizeof(double) * SZ * (size_t)(nblk > 0 ? nblk : 1)); /* S before each block */
+    double* Sb = (double*)malloc(sizeof(double) * SZ * (size_t)B);                    /* S_t inside a block */
+    double* S = (double*)malloc(sizeof(double) * SZ);
+    double* D = (double*)malloc(sizeof(double) * SZ);
+    double* a = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+    if (!ck || !Sb || !S || !D || !a) {
+#pragma omp atomic write
+      failed = 1;
+      free(ck); free(Sb); free(S); free(D); free(a);
+      continue;
+    }
+    const size_t r0 = (size_t)bh * (size_t)T;
+    for (long long t = 0; t < T; ++t) a[t] = exp(gla_oracle_gate((double)x[r0 + t], gate));
+#define KQ(arr, t, d) widen(arr, qkv_is_bf16, (r0 + (size_t)(t)) * (size_t)dkd + (size_t)(d))
+#define VV(t, n) widen(v, qkv_is_bf16, (r0 + (size_t)(t)) * (size_t)dvd + (size_t)(n))
+    /* forward sweep: checkpoints of S_{64c-1} */
+    for (size_t i = 0; i < SZ; ++i) S[i] = S0 ? S0[(size_t)bh * SZ + i] : 0.0;
+    for (long long t = 0; t < T; ++t) {
+      if (t % B == 0) memcpy(ck + (size_t)(t / B) * SZ, S, sizeof(double) * SZ);
+      for (int d = 0; d < dkd; ++d) {
+        const double kd = KQ(k, t, d);
+        for (int n = 0; n < dvd; ++n) S[(size_t)d * dvd + n] = a[t] * S[(size_t)d * dvd + n] + kd * VV(t, n);
+      }
+    }
+    /* backward sweep */
+    for (size_t i = 0; i < SZ; ++i) D[i] = dST ? dST[(size_t)bh * SZ + i] : 0.0;
+    for (long long c = nblk - 1; c >= 0; --c) {
+      const long long t0 = c * B, t1 = (t0 + B < T) ? t0 + B : T;
+      /* S_t for t in [t0, t1) */
+      memcpy(S, ck + (size_t)c * SZ, sizeof(double) * SZ);
+      for (long long t = t0; t < t1; ++t) {
+        double* St = Sb + (size_t)(t - t0) * SZ;
+        for (int d = 0; d < dkd; ++d) {
+          const double kd = KQ(k, t, d);
+          for (int n = 0; n < dvd; ++n) {
+            S[(size_t)d * dvd + n] = a[t] * S[(size_t)d * dvd + n] + kd * VV(t, n);
+            St[(size_t)d * dvd + n] = S[(size_t)d * dvd + n];
+          }
+        }
+      }
+      for (long long t = t1 - 1; t >= t0; --t) {
+        const double* St = Sb + (size_t)(t - t0) * SZ;
+        const double* Sp = (t > t0) ? Sb + (size_t)(t - t0 - 1) * SZ : ck + (size_t)c * SZ;
+        const double* g = dO + (r0 + (size_t)t) * (size_t)dvd;
+        /* D_t = q_t dO_t^T + (carried a_{t+1} D_{t+1}) */
+        for (int d = 0; d < dkd; ++d) {
+          const double qd = KQ(q, t, d);
+          for (int n = 0; n < dvd; ++n) D[(size_t)d * dvd + n] += qd * g[n];
+        }
+        for (int d = 0; d < dkd; ++d) {
+          double accq = 0.0, acck = 0.0;
+          for (int n = 0; n < dvd; ++n) {
+#if GLA_ORACLE_MUTANT == 9
+            accq += Sp[(size_t)d * dvd + n] * g[n];  /* planted: dq from S_{t-1} */
+#else
+            accq += St[(size_t)d * dvd + n] * g[n];
+#endif
+            acck += D[(size_t)d * dvd + n] * VV(t, n);
+          }
+          dq[(r0 + (size_t)t) * (size_t)dkd + d] = accq;
+          dk[(r0 + (size_t)t) * (size_t)dkd + d] = acck;
+        }
+        for (int n = 0; n < dvd; ++n) {
+          double acc = 0.0;
+          for (int d = 0; d < dkd; ++d)
+#if GLA_ORACLE_MUTANT == 10
+            acc += D[(size_t)d * dvd + n] * KQ(q, t, d);  /* planted: dv from q instead of k */
+#else
+            acc += D[(size_t)d * dvd + n] * KQ(k, t, d);
+#endif
+          dv[(r0 + (size_t)t) * (size_t)dvd + n] = acc;
+        }
+        double da = 0.0;
+        for (size_t i = 0; i < SZ; ++i) da += D[i] * Sp[i];
+#if GLA_ORACLE_MUTANT == 8
+        dx[r0 + (size_t)t] = da * gate_slope((double)x[r0 + t], gate);  /* planted: a_t factor dropped */
+#else
+        dx[r0 + (size_t)t] = da * a[t] * gate_slope((double)x[r0 + t], gate);
+#endif
+#if GLA_ORACLE_MUTANT != 7
+        for (size_t i = 0; i < SZ; ++i) D[i] *= a[t];  /* carry a_t D_t to t-1 */
+#endif
+      }
+    }
+#undef KQ
+#undef VV
+    memcpy(dS0 + (size_t)bh * SZ, D, sizeof(double) * SZ);  /* a_0 D_0 (dS_T when T = 0) */
+    free(ck); free(Sb); free(S); free(D); free(a);
+  }
+  return failed ? 2 : 0;
 }
 
 /* Number of OpenMP threads a parallel region would use (1 without OpenMP). */
