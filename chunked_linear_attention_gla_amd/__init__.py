@@ -1,4 +1,4 @@
-"""Chunked gated linear attention with bounded decay, forward pass, for MI355X (gfx950).
+"""Chunked gated linear attention with bounded decay, forward and backward passes, for MI355X (gfx950).
 
 The computation lives in hand-written HIP kernels behind the C ABI of
 ``include/gla.h`` (``libgla.so``, built in-tree by ``_build.py``); this package
@@ -6,6 +6,6 @@ is the thin Python binding over it plus the seeded workload generators.
 """
 from ._lib import (  # noqa: F401
     CHUNK, GATES, GLA_BF16, GLA_F32, MAX_SEGMENTS, PATHS, GLAError, LIB_PATH, Plan, abi_version,
-    chunk_fwd, chunk_output, gate_cumsum, load, plan_check, plan_default, segment_states,
+    chunk_bwd, chunk_fwd, chunk_output, gate_cumsum, load, plan_check, plan_default, segment_states,
     segment_workspace_size, status_string, workspace_size,
 )

@@ -64,6 +64,8 @@ _SIGS = {
                            _vp, _psz, _vp]),
     "gla_chunk_fwd_plan": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i,
                                 _pplan, _vp, _psz, _vp]),
+    "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
+                           _i, _i, _i, _vp, _psz, _vp]),
 }
 
 
@@ -248,3 +250,37 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor
         _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, dt, _gate(gate),
         _path(path), cplan, _ptr(workspace), ctypes.byref(have), _stream(dev)))
     return o, S_T
+
+
+def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor, dO: torch.Tensor,
+              S0: Optional[torch.Tensor] = None, dS_T: Optional[torch.Tensor] = None, gate="bounded",
+              path="unified", workspace: Optional[torch.Tensor] = None):
+    """Backward of :func:`chunk_fwd`: returns (dq, dk [B,H,T,dk], dv [B,H,T,dv], dx [B,H,T],
+    dS0 [B,H,dk,dv]), all fp32, for a loss L with dL/do = dO and dL/dS_T = dS_T.
+
+    dO: [B, H, T, dv] in q's dtype (the operand precision); dS_T: fp32 [B, H, dk, dv] or None.
+    """
+    B, H, T, dk, dv = _check_qkv(q, k, v, x, S0)
+    dev = q.device
+    _need(tuple(dO.shape) == (B, H, T, dv) and dO.dtype == q.dtype and dO.is_cuda and dO.is_contiguous()
+          and dO.device == dev, "dO must be a contiguous [B, H, T, dv] tensor of q's dtype on q's device")
+    if dS_T is not None:
+        _need(tuple(dS_T.shape) == (B, H, dk, dv) and dS_T.dtype == torch.float32 and dS_T.is_contiguous()
+              and dS_T.device == dev, "dS_T must be a contiguous fp32 [B, H, dk, dv] tensor on q's device")
+    lib = load()
+    dt = _dtype_code(q)
+    f32 = dict(device=dev, dtype=torch.float32)
+    dq = torch.empty(B, H, T, dk, **f32)
+    dk_ = torch.empty(B, H, T, dk, **f32)
+    dv_ = torch.empty(B, H, T, dv, **f32)
+    dx = torch.empty(B, H, T, **f32)
+    dS0 = torch.empty(B, H, dk, dv, **f32)
+    args = lambda ws: (_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk_),
+                       _ptr(dv_), _ptr(dx), _ptr(dS0), B, H, T, dk, dv, dt, _gate(gate), _path(path), ws)
+    need = ctypes.c_size_t(0)
+    _check("gla_chunk_bwd", lib.gla_chunk_bwd(*args(None), ctypes.byref(need), _stream(dev)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check("gla_chunk_bwd", lib.gla_chunk_bwd(*args(_ptr(workspace)), ctypes.byref(have), _stream(dev)))
+    return dq, dk_, dv_, dx, dS0

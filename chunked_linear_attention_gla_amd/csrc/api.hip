@@ -135,6 +135,11 @@ gla::ChunkParams make_params(const void* q, const void* k, const void* v, const 
     p.seg_decay = (float*)(base + align_up((size_t)BH * (plan.segments - 1) * dk * dv * 4));
   }
   p.grid = 0;
+  p.reverse = 0;
+  p.pad = 0;
+  p.Tl = T;
+  p.s0_transposed = 0;
+  p.state_out = nullptr;
   return p;
 }
 
@@ -219,7 +224,7 @@ gla_status_t gla_gate_cumsum(const float* x, float* b, int B, int H, long long T
   if (overlap({x, n}, {b, n})) return GLA_ERR_ALIAS;
   hipError_t e = gla::launch_gate_cumsum(x, b, BH, T, gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid
                                                                                      : gla::kGateNegSoftplus,
-                                         (hipStream_t)stream);
+                                         false, (hipStream_t)stream);
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
@@ -331,6 +336,118 @@ gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, con
     if (st != GLA_OK) return st;
   }
   return gla_chunk_output(q, k, v, bbuf, S0, o, S_T, B, H, T, dk, dv, dtype, path, &pl, seg, s_bytes, stream);
+}
+
+gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const float* x, const float* S0,
+                           const void* dO, const float* dS_T, float* dq, float* dk, float* dv, float* dx, float* dS0,
+                           int B, int H, long long T, int dk_, int dv_, gla_dtype_t dtype, gla_gate_t gate,
+                           gla_path_t path, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!workspace_bytes) return GLA_ERR_NULL;
+  gla_status_t st = check_sizes(B, H, T, dk_, dv_);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_gate(gate) || !valid_path(path)) return GLA_ERR_ARG;
+  // plans of the three passes: dq and dk run with state dims (dv, dk), dv with (dk, dv)
+  gla_plan_t pa, pc;
+  if (T > 0) {
+    st = gla_plan_default(B, H, T, dv_, dk_, dtype, path, &pa);
+    if (st != GLA_OK) return st;
+    st = gla_plan_default(B, H, T, dk_, dv_, dtype, path, &pc);
+    if (st != GLA_OK) return st;
+  } else {
+    pa.segments = pc.segments = 1;
+    pa.dv_split = pc.dv_split = 1;
+  }
+  // the dq and dk passes store their state before / after every chunk for dx; their
+  // kernels do that for value slices of at least 32 columns
+  if (T > 0 && (dk_ / pa.dv_split < 32)) return GLA_ERR_UNSUPPORTED;
+  const long long BH = (long long)B * H;
+  const long long nc = n_chunks(T);
+  const size_t es = elem_size(dtype);
+  const size_t tok = align_up((size_t)BH * (size_t)T * 4);
+  const size_t tokr = align_up((size_t)BH * (size_t)nc * GLA_CHUNK * 4);
+  const size_t chs = align_up((size_t)BH * (size_t)nc * (size_t)dk_ * (size_t)dv_ * es);
+  const size_t stt = align_up((size_t)BH * (size_t)dk_ * (size_t)dv_ * 4);
+  const size_t segb = std::max(seg_bytes(BH, dv_, dk_, pa.segments), seg_bytes(BH, dk_, dv_, pc.segments));
+  // b | b' (reversed, padded to whole chunks) | per-chunk states of the dq and dk passes |
+  // final states of the three passes (the dv pass's is D_0) | segment states
+  const size_t need = tok + tokr + 2 * chs + 3 * stt + segb;
+  if (!workspace) {
+    *workspace_bytes = need;
+    return GLA_OK;
+  }
+  if (*workspace_bytes < need) return GLA_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return GLA_ERR_ALIGN;
+  if (!dS0) return GLA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !x || !dO || !dq || !dk || !dv || !dx)) return GLA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dO, 16) || !aligned(S0, 16) ||
+      !aligned(dS_T, 16) || !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(dS0, 16) ||
+      !aligned(x, 4) || !aligned(dx, 4))
+    return GLA_ERR_ALIGN;
+  const size_t nk = (size_t)BH * T * dk_, nv = (size_t)BH * T * dv_, ns = (size_t)BH * dk_ * dv_;
+  const Range ins[] = {{q, nk * es}, {k, nk * es}, {v, nv * es}, {x, (size_t)BH * T * 4},
+                       {S0, ns * 4}, {dO, nv * es}, {dS_T, ns * 4}};
+  const Range outs[] = {{dq, nk * 4}, {dk, nk * 4}, {dv, nv * 4}, {dx, (size_t)BH * T * 4}, {dS0, ns * 4},
+                        {workspace, need}};
+  for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); ++i) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return GLA_ERR_ALIAS;
+    for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); ++j)
+      if (overlap(outs[i], outs[j])) return GLA_ERR_ALIAS;
+  }
+  char* w = (char*)workspace;
+  float* b = (float*)w;
+  float* br = (float*)(w + tok);
+  void* Sfw = w + tok + tokr;
+  void* Sbw = w + tok + tokr + chs;
+  float* STt = (float*)(w + tok + tokr + 2 * chs);
+  float* Sdk = (float*)(w + tok + tokr + 2 * chs + stt);
+  float* D0 = (float*)(w + tok + tokr + 2 * chs + 2 * stt);
+  void* seg = w + tok + tokr + 2 * chs + 3 * stt;
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = dtype == GLA_BF16 ? 0 : 1;
+  const int g = gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus;
+  const bool diag = path == GLA_PATH_DIAG_BRANCH;
+  const int pad = (int)(nc * GLA_CHUNK - T);
+  hipError_t e = hipSuccess;
+  if (T > 0) {
+    e = gla::launch_gate_cumsum(x, b, BH, T, g, false, s);
+    if (e == hipSuccess) e = gla::launch_gate_cumsum(x, br, BH, T, g, true, s);
+    // one forward-shaped pass: segment pre-pass (when segmented) and output pass.  A
+    // reversed pass reads its rows back to front behind `pad` zero rows, so that its
+    // chunks are the forward chunks in reverse order.
+    const auto pass = [&](const void* pq, const void* pk, const void* pv, const float* pb, const float* ps0,
+                          int s0t, int rev, float* po, float* pst, void* chunk_states, int sdk, int sdv,
+                          const gla_plan_t& pl) {
+      gla::ChunkParams p = make_params(pq, pk, pv, pb, ps0, po, pst, B, H, T, sdk, sdv, pl, seg);
+      p.reverse = rev;
+      p.s0_transposed = s0t;
+      if (rev) {
+        p.pad = pad;
+        p.Tl = T + pad;
+      }
+      hipError_t r = hipSuccess;
+      if (pl.segments > 1) {
+        p.grid = (int)(BH * pl.dv_split * (pl.segments - 1));
+        r = gla::launch_segment_states(p, dt, s);
+      }
+      if (r == hipSuccess) {
+        p.state_out = chunk_states;
+        p.grid = (int)(BH * pl.dv_split * pl.segments);
+        r = gla::launch_chunk_output(p, dt, diag, s);
+      }
+      return r;
+    };
+    // dq = forward(dO, v, k) from S0^T; stores S^T before every chunk
+    if (e == hipSuccess) e = pass(dO, v, k, b, S0, 1, 0, dq, STt, Sfw, dv_, dk_, pa);
+    // dk = reversed forward(v, dO, q) from dS_T^T; stores D^T after every chunk
+    if (e == hipSuccess) e = pass(v, dO, q, br, dS_T, 1, 1, dk, Sdk, Sbw, dv_, dk_, pa);
+    // dv = reversed forward(k, q, dO) from dS_T; its final state is D_0
+    if (e == hipSuccess) e = pass(k, q, dO, br, dS_T, 0, 1, dv, D0, nullptr, dk_, dv_, pc);
+    if (e == hipSuccess) e = gla::launch_grad_dx(q, k, v, dO, b, x, Sfw, Sbw, dx, BH, T, dk_, dv_, dt, g, s);
+  }
+  if (e == hipSuccess) e = gla::launch_grad_ds0(D0, b, dS_T, dS0, BH, T, dk_, dv_, s);
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
 gla_status_t gla_chunk_fwd(const void* q, const void* k, const void* v, const float* x, const float* S0, float* o,

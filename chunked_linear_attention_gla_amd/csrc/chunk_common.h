@@ -103,8 +103,9 @@ __device__ __forceinline__ void load_v_frags(VFrags<T, DK, DVS>& Vf, const T* vv
     for (int ks = 0; ks < 2; ++ks) Vf.f[nb][ks] = TokTile<T, DVS>::load(vv, ks * 32, wave * C::CPW + nb * 16, lane);
 }
 
-// Initial state of a segment: S0 (or zero), folded with the local final states of
-// the earlier segments of the same head, S <- e^{Gamma_p} S + H_p for p < seg.
+// Initial state of a segment: S0 (or zero; stored [dv][dk] when s0_transposed),
+// folded with the local final states of the earlier segments of the same head,
+// S <- e^{Gamma_p} S + H_p for p < seg.
 // The wave's slice of S: d = 16 db + 4 g + e, n = wcol + 16 nb + r16.
 template <typename T, int DK, int DVS>
 __device__ __forceinline__ void load_initial_state(StateAcc<T, DK, DVS>& S, const ChunkParams& p, int bh, int seg,
@@ -118,7 +119,10 @@ __device__ __forceinline__ void load_initial_state(StateAcc<T, DK, DVS>& S, cons
       for (int e = 0; e < 4; ++e) {
         const int d = db * 16 + 4 * g + e;
         const int n = wcol + nb * 16 + r16;
-        S.s[nb][db][e] = p.S0 ? p.S0[((long long)bh * DK + d) * p.dv + n] : 0.0f;
+        const long long i0 = (long long)bh * DK * p.dv;
+        S.s[nb][db][e] = !p.S0 ? 0.0f
+                         : p.s0_transposed ? p.S0[i0 + (long long)n * DK + d]
+                                           : p.S0[i0 + (long long)d * p.dv + n];
       }
   for (int ps = 0; ps < seg; ++ps) {
     const float f = exp_e(p.seg_decay[(long long)bh * p.segments + ps]);
@@ -134,6 +138,36 @@ __device__ __forceinline__ void load_initial_state(StateAcc<T, DK, DVS>& S, cons
           S.s[nb][db][e] = f * S.s[nb][db][e] + H[(long long)d * p.dv + n];
         }
   }
+}
+
+// Per-chunk state storage (for the backward pass): the state before each chunk,
+// in the operand dtype, in MFMA-fragment order
+//     [bh][chunk][g32 = value column / 32][nb][db][lane][e]
+// so that each lane writes (and a kernel with the same fragment layout later reads)
+// its own 4 consecutive elements: S[16 db + 4 g + e][32 g32 + 16 nb + r16].
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void store_chunk_state(const StateAcc<T, DK, DVS>& S, const ChunkParams& p, int bh,
+                                                  int c, int wcol, int lane) {
+  using C = Cfg<T, DK, DVS>;
+  static_assert(C::NB == 2, "chunk states are stored in groups of 32 value columns");
+  const int cc = p.reverse ? p.nchunks - 1 - c : c;
+  T* base = static_cast<T*>(p.state_out) +
+            ((((long long)bh * p.nchunks + cc) * (p.dv / 32) + wcol / 32) * 2) * (long long)C::DB * 256;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) {
+      T* dst = base + ((nb * C::DB + db) * 64 + lane) * 4;
+      if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+        bf16x4v w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = static_cast<__bf16>(S.s[nb][db][e]);
+        *reinterpret_cast<bf16x4v*>(dst) = w;
+      } else {
+        *reinterpret_cast<floatx4*>(dst) = S.s[nb][db];
+      }
+    }
 }
 
 // Writes the wave's slice of a state to dst [dk][dv] (one head).

@@ -71,15 +71,17 @@ struct Staged {
   typename E::Vec8 v[C::VU];
   float b;
 
-  __device__ __forceinline__ void load(const HeadBuffers& hb, uint32_t t0, uint32_t len, int dv, int col0,
+  // chunk starting at logical token t0 (rows in logical order; see row_offset)
+  __device__ __forceinline__ void load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0, int col0,
                                        int tid) {
+    const uint32_t len = (uint32_t)p.Tl;  // b is in logical order
     const uint32_t tb = t0 + (tid & 63);
     b = buf_load4(hb.b, (tb < len ? tb : len - 1) * 4u);
 #pragma unroll
     for (int m = 0; m < C::QU; ++m) {
       const int u = tid + m * C::NT;
       const int row = u / (DK / 8), c8 = u % (DK / 8);
-      const uint32_t off = ((t0 + row) * DK + c8 * 8) * (uint32_t)sizeof(T);
+      const uint32_t off = row_offset(p, t0 + row, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T);
       if (LOAD_Q) q[m] = E::load8(hb.q, off);
       k[m] = E::load8(hb.k, off);
     }
@@ -87,7 +89,8 @@ struct Staged {
     for (int m = 0; m < C::VU; ++m) {
       const int u = tid + m * C::NT;
       const int row = u / (DVS / 8), c8 = u % (DVS / 8);
-      v[m] = E::load8(hb.v, ((t0 + row) * dv + col0 + c8 * 8) * (uint32_t)sizeof(T));
+      v[m] = E::load8(hb.v, row_offset(p, t0 + row, (uint32_t)p.dv * (uint32_t)sizeof(T)) +
+                                (col0 + c8 * 8) * (uint32_t)sizeof(T));
     }
   }
 };
@@ -146,7 +149,7 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
   HeadBuffers hb;
   hb.k = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
   hb.v = make_rsrc(static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * (uint32_t)sizeof(T));
-  hb.b = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+  hb.b = make_rsrc(p.b + (long long)bh * p.Tl, (uint32_t)p.Tl * 4u);
 
   StateAcc<T, DK, DVS> S;
 #pragma unroll
@@ -156,7 +159,7 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
   float gsum = 0.0f;  // total log-decay of the segment
 
   Staged<T, DK, DVS, false> st;
-  if (c_begin < c_end) st.load(hb, (uint32_t)c_begin * kChunk, Tn, p.dv, col0, tid);
+  if (c_begin < c_end) st.load(hb, p, (uint32_t)c_begin * kChunk, col0, tid);
   for (int c = c_begin; c < c_end; ++c) {
     const ChunkDecay cd(st.b);
     const RowB<T, DK, DVS> brow(cd, tid);
@@ -164,7 +167,7 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
     gsum += cd.gam;
     // prefetch the next chunk (the last iteration re-reads its own chunk so that
     // every iteration issues the same loads)
-    st.load(hb, (uint32_t)min(c + 1, c_end - 1) * kChunk, Tn, p.dv, col0, tid);
+    st.load(hb, p, (uint32_t)min(c + 1, c_end - 1) * kChunk, col0, tid);
     __syncthreads();
     VFrags<T, DK, DVS> Vf;
     load_v_frags<T, DK, DVS>(Vf, sm.vv, wave, lane);
@@ -211,7 +214,7 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
   hb.q = make_rsrc(static_cast<const T*>(p.q) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
   hb.k = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
   hb.v = make_rsrc(static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * (uint32_t)sizeof(T));
-  hb.b = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+  hb.b = make_rsrc(p.b + (long long)bh * p.Tl, (uint32_t)p.Tl * 4u);
   hb.o = make_rsrc(p.o + (long long)bh * p.T * p.dv, Tn * p.dv * 4u);
 
   // ---- initial state of this segment
@@ -226,12 +229,12 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
   }
 
   Staged<T, DK, DVS, true> st;
-  if (c_begin < c_end) st.load(hb, (uint32_t)c_begin * kChunk, Tn, p.dv, col0, tid);
+  if (c_begin < c_end) st.load(hb, p, (uint32_t)c_begin * kChunk, col0, tid);
   __syncthreads();
 
   // o of a chunk is stored at the end of its iteration, after that iteration's
   // prefetch loads; lane (g, r16) holds row r16 of tile jb at columns 16 nb + 4g.
-  // Rows past the end of the sequence fall outside the descriptor and are dropped.
+  // Rows outside the head get an out-of-range offset and are dropped.
   auto store_o = [&](const floatx4 (&O)[4][C::NB], uint32_t row0, bool none) {
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb)
@@ -240,7 +243,8 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
         // dropped stores get distinct addresses: identical ones would be merged
         // into one, and the loop's wait counts assume all of them are issued
         const uint32_t off = none ? kDroppedOffset + 16u * (jb * C::NB + nb)
-                                  : ((row0 + jb * 16 + r16) * p.dv + wcol + nb * 16 + 4 * g) * 4u;
+                                  : row_offset(p, row0 + jb * 16 + r16, (uint32_t)p.dv * 4u) +
+                                        (wcol + nb * 16 + 4 * g) * 4u;
         buf_store16<kAuxStream>(hb.o, off, O[jb][nb]);
       }
   };
@@ -258,6 +262,9 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
 
   for (int c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)c * kChunk;
+    if constexpr (C::NB == 2) {
+      if (p.state_out) store_chunk_state<T, DK, DVS>(S, p, bh, c, wcol, lane);
+    }
     const ChunkDecay cd(st.b);
 
     // ---- (1) chunk c: registers -> LDS with the tile-relative decay factors
@@ -283,7 +290,7 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
 
     // ---- (2) prefetch chunk c + 1 while c is computed.  The last iteration re-reads
     //      its own chunk so every iteration issues the same loads.
-    st.load(hb, (uint32_t)min(c + 1, c_end - 1) * kChunk, Tn, p.dv, col0, tid);
+    st.load(hb, p, (uint32_t)min(c + 1, c_end - 1) * kChunk, col0, tid);
     __syncthreads();
 
     // ---- (3) attention matrix A of the chunk (bf16 / fp32 in LDS)

@@ -57,7 +57,7 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
   return v + off;
 }
 
-template <int GATE>
+template <int GATE, bool REV>
 __global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restrict__ x,
                                                           float* __restrict__ b, long long T,
                                                           long long chunks_per_head,
@@ -67,30 +67,40 @@ __global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restric
   if (chunk >= total_chunks) return;  // uniform across the wavefront
   const long long bh = chunk / chunks_per_head;
   const long long t = (chunk - bh * chunks_per_head) * kChunk + lane;
-  const bool valid = t < T;
-  const long long idx = bh * T + t;
+  // REV: the reversed sequence has pad absent tokens first, then original tokens
+  // T-1 .. 0; logical token t > pad takes the gate of original token T + pad - t
+  // (the token after it in original order), t <= pad none (g = 0)
+  const long long pad = REV ? (kChunk - T % kChunk) % kChunk : 0;
+  const long long Tl = T + pad;
+  const bool valid = t < Tl;
   float g = 0.0f;
-  if (valid) {
-    const float xv = x[idx];
+  if (valid && (!REV || t > pad)) {
+    const float xv = x[bh * T + (REV ? T + pad - t : t)];
     g = (GATE == kGateBoundedSigmoid) ? gate_bounded_sigmoid(xv) : gate_neg_softplus(xv);
   }
   const float s = wave_inclusive_scan(g, lane);
-  if (valid) b[idx] = s;
+  if (valid) b[bh * Tl + t] = s;
 }
 
 hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long T, int gate,
-                              hipStream_t stream) {
+                              bool reversed_shift, hipStream_t stream) {
   const long long cph = (T + kChunk - 1) / kChunk;
   const long long total = BH * cph;
   if (total == 0) return hipSuccess;
   const long long blocks = (total + 3) / 4;
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  if (gate == kGateBoundedSigmoid)
-    hipLaunchKernelGGL(gate_cumsum_kernel<kGateBoundedSigmoid>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, x, b, T, cph, total);
-  else
-    hipLaunchKernelGGL(gate_cumsum_kernel<kGateNegSoftplus>, dim3((unsigned)blocks), dim3(256), 0,
-                       stream, x, b, T, cph, total);
+  const dim3 grid((unsigned)blocks), block(256);
+  if (gate == kGateBoundedSigmoid) {
+    if (reversed_shift)
+      hipLaunchKernelGGL((gate_cumsum_kernel<kGateBoundedSigmoid, true>), grid, block, 0, stream, x, b, T, cph, total);
+    else
+      hipLaunchKernelGGL((gate_cumsum_kernel<kGateBoundedSigmoid, false>), grid, block, 0, stream, x, b, T, cph, total);
+  } else {
+    if (reversed_shift)
+      hipLaunchKernelGGL((gate_cumsum_kernel<kGateNegSoftplus, true>), grid, block, 0, stream, x, b, T, cph, total);
+    else
+      hipLaunchKernelGGL((gate_cumsum_kernel<kGateNegSoftplus, false>), grid, block, 0, stream, x, b, T, cph, total);
+  }
   return hipGetLastError();
 }
 

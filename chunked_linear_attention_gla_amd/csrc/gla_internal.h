@@ -26,10 +26,36 @@ struct ChunkParams {
                           // [p * nchunks / segments, (p + 1) * nchunks / segments)
   int nslices;            // value-column slices per head
   int grid;               // workgroups in this launch
+  int reverse;            // 1: logical token t is stored at row T-1+pad-t of q, k, v and o
+                          //    (b and the states are in logical order)
+  int pad;                // reversed passes: absent logical tokens before the first real
+                          //    one, so that logical chunks line up with the stored chunks
+  long long Tl;           // logical length, T + pad: per-head length and stride of b
+  int s0_transposed;      // 1: S0 is stored [dv][dk] (the transpose of the state)
+  void* state_out;        // optional: the state before every chunk, in the operand dtype,
+                          //    in MFMA-fragment order (see store_chunk_state); a reversed
+                          //    pass stores logical chunk c at chunk nchunks-1-c
 };
 
+// Byte offset of logical token t's row in a per-head tensor with rows of
+// row_bytes bytes.  Rows outside the head (t >= T, or t < 0 once reversed) get an
+// offset beyond every descriptor's range that cannot wrap round to a valid one
+// when an instruction offset is added: loads there return zeros, stores are
+// dropped.
+// (Accepted sizes keep T * row_bytes below 2^32 - 2^16, so 32-bit arithmetic is exact.)
+__host__ __device__ inline unsigned row_offset(const ChunkParams& p, unsigned t, unsigned row_bytes) {
+  const int T = (int)p.T;
+  const int r = p.reverse ? T - 1 + p.pad - (int)t : (int)t;
+  return (r >= 0 && r < T) ? (unsigned)r * row_bytes : 0xFFFFF000u;
+}
+
+// b = chunk-local cumsum of g(x), [BH][T].  reversed_shift: the gate of the time-reversed
+// sequence, shifted by one token and preceded by pad = (-T mod 64) absent tokens,
+// [BH][T + pad]: g'(tau) = g(x[T + pad - tau]) for tau > pad, 0 for tau <= pad -- the
+// decays a_{t+1} that the state gradient crosses when run backwards, with chunks
+// that line up with the forward chunks.
 hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long T, int gate,
-                              hipStream_t stream);
+                              bool reversed_shift, hipStream_t stream);
 
 // dtype: 0 = bf16, 1 = fp32.  slice = dv / nslices.  diag: element-wise diagonal tiles.
 bool chunk_config_built(int dtype, int dk, int slice, bool diag);
@@ -41,5 +67,16 @@ hipError_t launch_chunk_output(const ChunkParams& p, int dtype, bool diag, hipSt
 bool ws_kernels_supported(int dtype, int dk, int slice);
 hipError_t launch_chunk_output_ws(const ChunkParams& p, int dk, int slice, bool diag, hipStream_t stream);
 hipError_t launch_segment_states_ws(const ChunkParams& p, int dk, int slice, hipStream_t stream);
+
+// Backward-pass kernels (bwd_kernels.hip).
+//   dx from the pairs that span each token (see bwd_kernels.hip); Sfw and Sbw are the
+//   per-chunk states stored by the dq pass (S^T before each chunk) and by the dk pass
+//   (D^T after each chunk, before the next chunk's decay);
+hipError_t launch_grad_dx(const void* q, const void* k, const void* v, const void* dO, const float* b,
+                          const float* x, const void* Sfw, const void* Sbw, float* dx, long long BH, long long T,
+                          int dk_, int dv_, int dtype, int gate, hipStream_t stream);
+//   dS0 = e^{b[0]} D0 (dS_T, or zero, when T = 0).
+hipError_t launch_grad_ds0(const float* D0, const float* b, const float* dST, float* dS0, long long BH,
+                           long long T, int dk_, int dv_, hipStream_t stream);
 
 }  // namespace gla

@@ -89,14 +89,16 @@ struct WsStaged {
   uint4 q[LOAD_Q ? QU : 1], k[QU], v[VU];
   float b;
 
-  __device__ __forceinline__ void load(const HeadBuffers& hb, uint32_t t0, uint32_t len, int dv, int col0, int st) {
+  // chunk starting at logical token t0 (rows in logical order; see row_offset)
+  __device__ __forceinline__ void load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0, int col0, int st) {
+    const uint32_t len = (uint32_t)p.Tl;  // b is in logical order
     const uint32_t tb = t0 + (st & 63);
     b = buf_load4(hb.b, (tb < len ? tb : len - 1) * 4u);
 #pragma unroll
     for (int m = 0; m < QU; ++m) {
       const int u = st + m * 256;
       const int row = u / (DK / 8), c8 = u % (DK / 8);
-      const uint32_t off = ((t0 + row) * DK + c8 * 8) * 2u;
+      const uint32_t off = row_offset(p, t0 + row, DK * 2u) + c8 * 16u;
       if (LOAD_Q) q[m] = buf_load16(hb.q, off);
       k[m] = buf_load16(hb.k, off);
     }
@@ -104,7 +106,7 @@ struct WsStaged {
     for (int m = 0; m < VU; ++m) {
       const int u = st + m * 256;
       const int row = u / (DVS / 8), c8 = u % (DVS / 8);
-      v[m] = buf_load16(hb.v, ((t0 + row) * dv + col0 + c8 * 8) * 2u);
+      v[m] = buf_load16(hb.v, row_offset(p, t0 + row, (uint32_t)p.dv * 2u) + (col0 + c8 * 8) * 2u);
     }
   }
 };
@@ -223,7 +225,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
   hb.q = make_rsrc(static_cast<const bf16*>(p.q) + (long long)bh * p.T * DK, Tn * DK * 2u);
   hb.k = make_rsrc(static_cast<const bf16*>(p.k) + (long long)bh * p.T * DK, Tn * DK * 2u);
   hb.v = make_rsrc(static_cast<const bf16*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * 2u);
-  hb.b = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+  hb.b = make_rsrc(p.b + (long long)bh * p.Tl, (uint32_t)p.Tl * 4u);
   hb.o = make_rsrc(p.o + (long long)bh * p.T * p.dv, Tn * p.dv * 4u);
 
   // The two key tiles that a 32-wide K-step of A.V reads above the diagonal,
@@ -244,6 +246,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
     for (int c = c_begin; c < c_end; ++c) {
       const int slot = (c - c_begin) & 1;
       const uint32_t t0 = (uint32_t)c * kChunk;
+      if (p.state_out) store_chunk_state<bf16, DK, DVS>(S, p, bh, c, wcol, lane);
 
       // ---- part 1: off-diagonal tiles of A(c)
       const ChunkDecay cd(sm.sb[lane]);
@@ -297,13 +300,14 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         }
       }
       state_update<bf16, DK, DVS>(S, Vf, sm.kp[slot], exp_e(cd.gam), lane);
-      // lane holds o[t0 + 16 jb + r16][wcol + 16 nb + 4 g + 0..3]; rows past the
-      // end fall outside the descriptor and are dropped
+      // lane holds o[t0 + 16 jb + r16][wcol + 16 nb + 4 g + 0..3]; rows outside the
+      // head get an out-of-range offset and are dropped
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb)
-          buf_store16<0>(hb.o, ((t0 + jb * 16 + r16) * p.dv + wcol + nb * 16 + 4 * g) * 4u, O[jb][nb]);
+          buf_store16<0>(hb.o, row_offset(p, t0 + jb * 16 + r16, (uint32_t)p.dv * 4u) + (wcol + nb * 16 + 4 * g) * 4u,
+                         O[jb][nb]);
       __syncthreads();
     }
     if (seg == p.segments - 1) store_state<bf16, DK, DVS>(S, p.ST + (long long)bh * DK * p.dv, p.dv, wcol, g, r16);
@@ -357,10 +361,10 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
     // issued right after into the freed set, two chunks ahead of their use.
     WsStaged<DK, DVS> s0, s1;
     if (c_begin < c_end) {
-      s0.load(hb, chunk_t0(c_begin), Tn, p.dv, col0, st);
+      s0.load(hb, p, chunk_t0(c_begin), col0, st);
       stage(s0, 0);
-      s1.load(hb, chunk_t0(c_begin + 1), Tn, p.dv, col0, st);
-      s0.load(hb, chunk_t0(c_begin + 2), Tn, p.dv, col0, st);
+      s1.load(hb, p, chunk_t0(c_begin + 1), col0, st);
+      s0.load(hb, p, chunk_t0(c_begin + 2), col0, st);
     }
     __syncthreads();
     // Chunks are taken in pairs so that each set is named statically; staging and
@@ -372,12 +376,12 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
       diagonal(c);
       __syncthreads();
       stage(s1, 1);
-      s1.load(hb, chunk_t0(c + 3), Tn, p.dv, col0, st);
+      s1.load(hb, p, chunk_t0(c + 3), col0, st);
       __syncthreads();
       diagonal(c + 1);
       __syncthreads();
       stage(s0, 0);
-      s0.load(hb, chunk_t0(c + 4), Tn, p.dv, col0, st);
+      s0.load(hb, p, chunk_t0(c + 4), col0, st);
       __syncthreads();
     }
     if (c < c_end) {  // odd number of chunks: the last one has nothing to stage after it
@@ -453,7 +457,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
     HeadBuffers hb;
     hb.k = make_rsrc(static_cast<const bf16*>(p.k) + (long long)bh * p.T * DK, Tn * DK * 2u);
     hb.v = make_rsrc(static_cast<const bf16*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * 2u);
-    hb.b = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+    hb.b = make_rsrc(p.b + (long long)bh * p.Tl, (uint32_t)p.Tl * 4u);
     const auto stage = [&](const WsStaged<DK, DVS, false>& stg, int ns) {
       const ChunkDecay cd(stg.b);
       float brow[W::QU];
@@ -479,19 +483,19 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
     // register set s0: chunks at even offsets from c_begin, s1: odd offsets
     WsStaged<DK, DVS, false> s0, s1;
     if (c_begin < c_end) {
-      s0.load(hb, chunk_t0(c_begin), Tn, p.dv, col0, st);
+      s0.load(hb, p, chunk_t0(c_begin), col0, st);
       stage(s0, 0);
-      s1.load(hb, chunk_t0(c_begin + 1), Tn, p.dv, col0, st);
-      s0.load(hb, chunk_t0(c_begin + 2), Tn, p.dv, col0, st);
+      s1.load(hb, p, chunk_t0(c_begin + 1), col0, st);
+      s0.load(hb, p, chunk_t0(c_begin + 2), col0, st);
     }
     __syncthreads();
     int c = c_begin;
     for (; c + 1 < c_end; c += 2) {
       stage(s1, 1);
-      s1.load(hb, chunk_t0(c + 3), Tn, p.dv, col0, st);
+      s1.load(hb, p, chunk_t0(c + 3), col0, st);
       __syncthreads();
       stage(s0, 0);
-      s0.load(hb, chunk_t0(c + 4), Tn, p.dv, col0, st);
+      s0.load(hb, p, chunk_t0(c + 4), col0, st);
       __syncthreads();
     }
     if (c < c_end) __syncthreads();

@@ -185,6 +185,38 @@ gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, con
                                 const gla_plan_t* plan,
                                 void* workspace, size_t* workspace_bytes, void* stream);
 
+/* Backward pass of gla_chunk_fwd: the gradients of a scalar loss L given
+ * dO = dL/do and dS_T = dL/dS_T, for the same recurrence
+ * S_t = a_t S_{t-1} + k_t v_t^T, o_t = S_t^T q_t, a_t = e^{g(x_t)} [LCT §3.1, §3.2].
+ *   q, k, v, x, S0, B..path: as passed to gla_chunk_fwd (S0 may be NULL: zero).
+ *   dO   [B][H][T][dv] in `dtype` (the operand precision of q, k, v).
+ *   dS_T [B][H][dk][dv] fp32, or NULL (zero).
+ *   dq, dk [B][H][T][dk], dv [B][H][T][dv], dx [B][H][T], dS0 [B][H][dk][dv]: fp32
+ *   outputs (dS0 is written even when S0 is NULL), device memory, none
+ *   overlapping another argument or the workspace.
+ * Method: dq is the forward pass with (q, k, v, S0) replaced by (dO, v, k, S0^T);
+ * dk and dv are forward passes in reversed time over (v, dO, q, dS_T^T) and
+ * (k, q, dO, dS_T), whose decays are those of the next token (the state gradient
+ * D_t = q_t dO_t^T + a_{t+1} D_{t+1} is a forward recurrence run backwards); its
+ * final state gives dS0 = a_0 D_0.  dL/dg_t is the sum over the (key token s,
+ * output token j) pairs whose decay path spans t (s < t <= j, with j = "after the
+ * end" for the final state), taken per chunk: pairs inside the chunk from q.k and
+ * dO.v on the matrix cores, pairs that enter or leave the chunk from the states
+ * before and after it (stored by the dq and dk passes), and pairs that cross it
+ * whole; dx = g'(x) dL/dg.  Each pass uses the device's default plan; the dq and
+ * dk passes need value slices of at least 32 columns (GLA_ERR_UNSUPPORTED
+ * otherwise, which the default plans never give).
+ * workspace == NULL: *workspace_bytes receives the size and nothing is enqueued;
+ * otherwise the workspace (256-byte aligned device memory) must be at least that
+ * size.  Errors as gla_chunk_fwd; everything is validated before anything is
+ * enqueued on `stream`. */
+gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const float* x,
+                           const float* S0, const void* dO, const float* dS_T,
+                           float* dq, float* dk, float* dv, float* dx, float* dS0,
+                           int B, int H, long long T, int dk_dim, int dv_dim,
+                           gla_dtype_t dtype, gla_gate_t gate, gla_path_t path,
+                           void* workspace, size_t* workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

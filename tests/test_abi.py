@@ -174,3 +174,36 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 64)
     with pytest.raises(ValueError):
         gla.chunk_fwd(q, q, q, x)
+
+
+# ------------------------------------------------------------------------------ backward
+
+def bwd(lib, B=1, H=2, T=0, dk=64, dv=64, dtype=BF16, gate=BOUNDED, path=UNIFIED, ws=None, wsz=0,
+        q=0x1000, k=0x100000, v=0x200000, x=0x300000, S0=None, dO=0x400000, dST=None,
+        dq=0x500000, dk_=0x600000, dv_=0x700000, dx=0x800000, dS0=0x900000, nbytes=True):
+    n = ctypes.c_size_t(wsz)
+    return lib.gla_chunk_bwd(q, k, v, x, S0, dO, dST, dq, dk_, dv_, dx, dS0, B, H, T, dk, dv, dtype, gate, path,
+                             ws, ctypes.byref(n) if nbytes else None, None), n.value
+
+
+def test_backward_validates_before_any_device_call(lib):
+    assert bwd(lib, nbytes=False)[0] == NULL
+    assert bwd(lib, dk=96)[0] == SHAPE
+    assert bwd(lib, B=0)[0] == SHAPE
+    assert bwd(lib, T=-1)[0] == SHAPE
+    assert bwd(lib, dtype=7)[0] == DTYPE
+    assert bwd(lib, gate=5)[0] == ARG
+    assert bwd(lib, path=9)[0] == ARG
+
+
+def test_backward_workspace_query_for_an_empty_sequence(lib):
+    # T = 0 needs no plan (no device query): b, b', s and chunk arrays are empty,
+    # the three state buffers remain
+    rc, need = bwd(lib, B=2, H=3, T=0, dk=64, dv=128)
+    assert rc == OK
+    assert need == 3 * ((2 * 3 * 64 * 128 * 4 + 255) // 256 * 256)
+    # with a workspace of that size, a missing dS0 is rejected before launching
+    rc, _ = bwd(lib, B=2, H=3, T=0, dk=64, dv=128, ws=0x10000000, wsz=need, dS0=None)
+    assert rc == NULL
+    rc, _ = bwd(lib, B=2, H=3, T=0, dk=64, dv=128, ws=0x10000000, wsz=need - 1)
+    assert rc == WORKSPACE

@@ -7,7 +7,7 @@
 * a ≡ 1 (x = -inf under the bounded gate): the gradients of causal linear
   attention o = tril(QK^T)V + Q S0, S_T = S0 + K^T V, written with numpy matmuls;
 * the log-decay gradient identity dL/dg_t = sum_{t' >= t} (q_t'.dq_t' - k_t'.dk_t')
-  + <dS_T, S_T>, which the GPU backward uses, checked on the oracle's outputs;
+  + <dS_T, S_T>, checked on the oracle's outputs (it ties dx to dq and dk);
 * planted mistakes in the backward must make the autodiff pin fail.
 
 The recurrence (the plainest reading of the chunked linear attention with a
