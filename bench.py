@@ -61,6 +61,18 @@ def algorithmic_flops_per_token_head(dk: int, dv: int) -> int:
     return 4 * dk * dv + 2 * 40 * (dk + dv)
 
 
+def backward_bytes_per_token_head(dk: int, dv: int, es: int) -> int:
+    # reads q, k (dk each), v and dO (dv each) in storage precision and x; writes dq, dk
+    # (dk fp32 each), dv (dv fp32) and dx
+    return (2 * dk + 2 * dv) * es + 4 + 4 * (2 * dk + dv) + 4
+
+
+def backward_flops_per_token_head(dk: int, dv: int) -> int:
+    # three forward-shaped passes (dq, dk, dv) and, for dx, q.k and dO.v on the causal
+    # tiles plus S dO and D v against the states before and after each chunk
+    return 3 * algorithmic_flops_per_token_head(dk, dv) + 2 * 40 * (dk + dv) + 4 * dk * dv
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -72,6 +84,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true", help="skip the diagonal-branch comparison")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--backward-only", action="store_true", help="time only the backward pass (profiling)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration) and exit")
     return ap.parse_args()
@@ -113,6 +127,38 @@ def cpu_baseline(w, target_s: float):
     return {"value": w.B * T / dt, "unit": "tokens/s", "cores": lib_threads, "kind": "oracle",
             "sample": f"all {w.B * w.H} heads of {w.name}, first {T} of {w.T} tokens (seed {w.seed}); "
                       f"fp64 sequential recurrence, OpenMP over heads x 16-column blocks; {dt:.1f} s"}
+
+
+def cpu_baseline_backward(w, target_s: float):
+    """Time the fp64 backward oracle on a bounded sample of the workload, like cpu_baseline."""
+    import numpy as np
+    import torch
+    import oracle
+    from chunked_linear_attention_gla_amd import inputs as gin
+    lib_threads = oracle.max_threads()
+
+    def run(T):
+        inp = gin.make_inputs(w, "cuda:0", T=T)
+        flat = lambda t: t.reshape(w.B * w.H, *t.shape[2:])
+        args = [gin.to_numpy_bits(flat(inp[n])) for n in ("q", "k", "v", "x")]
+        s0 = None if inp["S0"] is None else flat(inp["S0"]).cpu().numpy().astype(np.float64)
+        gen = torch.Generator(device="cuda:0").manual_seed(w.seed + 500)
+        dO = torch.randn(w.B * w.H, T, w.dv, device="cuda:0", generator=gen).to(inp["q"].dtype)
+        dST = torch.randn(w.B * w.H, w.dk, w.dv, device="cuda:0", generator=gen) * 0.1
+        dO64 = dO.double().cpu().numpy()
+        dST64 = dST.double().cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.backward(*args, dO64, s0, dST64, gate=w.gate)
+        return time.perf_counter() - t0
+
+    T0 = 128
+    dt0 = run(T0)
+    T = int(min(w.T, max(T0, target_s / max(dt0, 1e-6) * T0)))
+    T = max(64, T // 64 * 64)
+    dt = run(T)
+    return {"value": w.B * T / dt, "unit": "tokens/s", "cores": lib_threads, "kind": "oracle",
+            "sample": f"backward, all {w.B * w.H} heads of {w.name}, first {T} of {w.T} tokens (seed {w.seed}); "
+                      f"fp64 recurrence with 64-token checkpoints, OpenMP over heads; {dt:.1f} s"}
 
 
 def output_kernel_name(dtype_bytes: int, dk: int, slice_cols: int) -> str:
@@ -192,6 +238,73 @@ class StepTimer:
         return elapsed * 1e3 / steps, stage
 
 
+class BackwardTimer:
+    """The backward pass (gla_chunk_bwd) of one workload with a given dO and dS_T, outputs
+    and workspace preallocated, timed with HIP events on the current stream around each
+    call."""
+
+    def __init__(self, gla, gin, torch, w, path):
+        dev = torch.device("cuda:0")
+        self.gla, self.torch, self.w, self.path = gla, torch, w, path
+        inp = gin.make_inputs(w, dev)
+        self.q, self.k, self.v, self.x, self.S0 = inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"]
+        B, H, T, dk = self.q.shape
+        dv = self.v.shape[-1]
+        self.shape = (B, H, T, dk, dv)
+        gen = torch.Generator(device=dev).manual_seed(w.seed + 500)
+        self.dO = torch.randn(B, H, T, dv, device=dev, generator=gen).to(self.q.dtype)
+        self.dST = torch.randn(B, H, dk, dv, device=dev, generator=gen) * 0.1
+        f32 = dict(device=dev, dtype=torch.float32)
+        self.out = (torch.empty(B, H, T, dk, **f32), torch.empty(B, H, T, dk, **f32),
+                    torch.empty(B, H, T, dv, **f32), torch.empty(B, H, T, **f32), torch.empty(B, H, dk, dv, **f32))
+        dt_code = gla.GLA_BF16 if self.q.dtype == torch.bfloat16 else gla.GLA_F32
+        need = gla.backward_workspace_size(B, H, T, dk, dv, dt_code, w.gate, path)
+        self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def step(self):
+        self.gla.chunk_bwd(self.q, self.k, self.v, self.x, self.dO, self.S0, self.dST, gate=self.w.gate,
+                           path=self.path, workspace=self.ws, out=self.out)
+
+    def run(self, steps, warmup):
+        """Returns (ms per call from the host clock, ms per call from events)."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        t0 = time.perf_counter()
+        ev[0].record()
+        for i in range(steps):
+            self.step()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        return elapsed * 1e3 / steps, ev[0].elapsed_time(ev[steps]) / steps
+
+
+def backward_result(gla, gin, torch, w, path, steps, warmup):
+    t = BackwardTimer(gla, gin, torch, w, path)
+    ms_host, ms_ev = t.run(steps, warmup)
+    B, H, T, dk, dv = t.shape
+    es = t.q.element_size()
+    del t
+    bh = B * H
+    nbytes = bh * T * backward_bytes_per_token_head(dk, dv, es) + bh * dk * dv * 4 * 3
+    flops = bh * T * backward_flops_per_token_head(dk, dv)
+    achieved = nbytes / (ms_ev / 1e3) / 1e9
+    return {
+        "what": "gla_chunk_bwd: dq, dk, dv, dx, dS0 from dO and dS_T (all kernels of the call)",
+        "steps": steps,
+        "ms_per_call": round(ms_host, 4),
+        "ms_per_call_events": round(ms_ev, 4),
+        "tokens_per_s": round(B * T / (ms_ev / 1e3), 1),
+        "tflops": round(flops / (ms_ev / 1e3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -210,6 +323,10 @@ def main():
     path = args.path or "unified"
     torch.cuda.set_device(torch.device("cuda:0"))
     plan = gla.Plan(*(int(s) for s in args.plan.split(","))) if args.plan else None
+    if args.backward_only:
+        print(json.dumps({"workload": w.name, "backward": backward_result(gla, gin, torch, w, path, args.steps,
+                                                                         args.warmup)}), flush=True)
+        return
     timer = StepTimer(gla, gin, torch, w, path, plan)
     plan = timer.plan
     ms_step, (ms_gate, ms_seg, ms_out) = timer.run(args.steps, args.warmup)
@@ -276,6 +393,10 @@ def main():
         abl["unified_speedup_output_kernel"] = round(
             abl["diag_branch"]["chunk_output_ms"] / abl["unified"]["chunk_output_ms"], 3)
         result["ablation"] = abl
+    if not args.no_backward and not args.plan:
+        result["backward"] = backward_result(gla, gin, torch, w, path, min(args.steps, 20), min(args.warmup, 5))
+        if not args.no_cpu_baseline:
+            result["backward"]["cpu_baseline"] = cpu_baseline_backward(w, args.cpu_seconds / 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -6,6 +6,7 @@ is the thin Python binding over it plus the seeded workload generators.
 """
 from ._lib import (  # noqa: F401
     CHUNK, GATES, GLA_BF16, GLA_F32, MAX_SEGMENTS, PATHS, GLAError, LIB_PATH, Plan, abi_version,
+    backward_workspace_size,
     chunk_bwd, chunk_fwd, chunk_output, gate_cumsum, load, plan_check, plan_default, segment_states,
     segment_workspace_size, status_string, workspace_size,
 )

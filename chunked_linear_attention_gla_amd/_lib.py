@@ -171,6 +171,16 @@ def workspace_size(B: int, H: int, T: int, dk: int, dv: int, dtype=GLA_BF16, pat
     return int(n.value)
 
 
+def backward_workspace_size(B: int, H: int, T: int, dk: int, dv: int, dtype=GLA_BF16, gate="bounded",
+                            path="unified") -> int:
+    """Workspace bytes gla_chunk_bwd needs for these sizes (default plans of this device)."""
+    n = ctypes.c_size_t(0)
+    _check("gla_chunk_bwd", load().gla_chunk_bwd(None, None, None, None, None, None, None, None, None, None, None,
+                                                 None, B, H, T, dk, dv, dtype, _gate(gate), _path(path), None,
+                                                 ctypes.byref(n), None))
+    return int(n.value)
+
+
 def segment_workspace_size(B: int, H: int, T: int, dk: int, dv: int, plan: Plan) -> int:
     n = ctypes.c_size_t(0)
     _check("gla_segment_workspace_size",
@@ -254,11 +264,12 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor
 
 def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor, dO: torch.Tensor,
               S0: Optional[torch.Tensor] = None, dS_T: Optional[torch.Tensor] = None, gate="bounded",
-              path="unified", workspace: Optional[torch.Tensor] = None):
+              path="unified", workspace: Optional[torch.Tensor] = None, out=None):
     """Backward of :func:`chunk_fwd`: returns (dq, dk [B,H,T,dk], dv [B,H,T,dv], dx [B,H,T],
     dS0 [B,H,dk,dv]), all fp32, for a loss L with dL/do = dO and dL/dS_T = dS_T.
 
     dO: [B, H, T, dv] in q's dtype (the operand precision); dS_T: fp32 [B, H, dk, dv] or None.
+    out: optional tuple of five preallocated output tensors of those shapes.
     """
     B, H, T, dk, dv = _check_qkv(q, k, v, x, S0)
     dev = q.device
@@ -270,11 +281,14 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor
     lib = load()
     dt = _dtype_code(q)
     f32 = dict(device=dev, dtype=torch.float32)
-    dq = torch.empty(B, H, T, dk, **f32)
-    dk_ = torch.empty(B, H, T, dk, **f32)
-    dv_ = torch.empty(B, H, T, dv, **f32)
-    dx = torch.empty(B, H, T, **f32)
-    dS0 = torch.empty(B, H, dk, dv, **f32)
+    shapes = ((B, H, T, dk), (B, H, T, dk), (B, H, T, dv), (B, H, T), (B, H, dk, dv))
+    if out is None:
+        out = tuple(torch.empty(*sh, **f32) for sh in shapes)
+    else:
+        _need(len(out) == 5 and all(tuple(t.shape) == sh and t.dtype == torch.float32 and t.is_contiguous()
+                                    and t.device == dev for t, sh in zip(out, shapes)),
+              "out must be five contiguous fp32 tensors (dq, dk, dv, dx, dS0) on q's device")
+    dq, dk_, dv_, dx, dS0 = out
     args = lambda ws: (_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk_),
                        _ptr(dv_), _ptr(dx), _ptr(dS0), B, H, T, dk, dv, dt, _gate(gate), _path(path), ws)
     need = ctypes.c_size_t(0)
