@@ -13,7 +13,7 @@ Sources (web pages; cited by title and section):
   [ESU] "Engineering Stability in Ultra-Long Context and Trillion-Parameter
          Sparse Models"
 
-Three independent formulations of the forward pass live here, and the backward
+Independent formulations of the forward pass live here, and the backward
 pass of the recurrence:
 
 * :func:`forward` -- the sequential recurrence, one token at a time, in C (fp64,
@@ -21,6 +21,8 @@ pass of the recurrence:
 * :func:`closed_form` -- the quadratic form, numpy fp64, with every decay weight
   formed as an explicit product of per-token decays (no cumulative sums, no
   exponent differences).  Used to pin :func:`forward` on tiny inputs.
+* :func:`forward_pc` / :func:`closed_form_pc` -- the same two formulations for a
+  decay with one value per key channel (the state's row d decays by a_t[d]).
 * :func:`backward` -- the reverse-mode chain rule of the same recurrence, one token
   at a time, in C (fp64): dq, dk, dv, dx and dS0 from dO and dS_T.
 * :func:`gate` / :func:`chunk_local_cumsum` -- the log-decay of [LCT §3.2] and the
@@ -87,6 +89,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
         ctypes.c_longlong, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int]
+    lib.gla_oracle_forward_pc.restype = ctypes.c_int
+    lib.gla_oracle_forward_pc.argtypes = lib.gla_oracle_forward.argtypes
     lib.gla_oracle_backward.restype = ctypes.c_int
     lib.gla_oracle_backward.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -149,6 +153,42 @@ def forward(q: np.ndarray, k: np.ndarray, v: np.ndarray, x: np.ndarray,
         o.ctypes.data, ST.ctypes.data, BH, T, dk, dv, gate_id(gate), col_block, nthreads)
     if rc != 0:
         raise ValueError(f"gla_oracle_forward rejected its arguments (rc={rc})")
+    return o, ST
+
+
+def forward_pc(q: np.ndarray, k: np.ndarray, v: np.ndarray, x: np.ndarray,
+               S0: Optional[np.ndarray] = None, gate="bounded", nthreads: int = 0,
+               col_block: int = 16, lib_path: str = LIB_PATH):
+    """Per-channel-decay recurrence (fp64, one token at a time, in C):
+
+        S_t[d, :] = a_t[d] S_{t-1}[d, :] + k_t[d] v_t,  a_t[d] = exp(g(x_t[d])),  o_t = S_t^T q_t
+
+    q, k [..., T, dk], v [..., T, dv] as for :func:`forward`; x [..., T, dk] fp32.
+    Returns (o [..., T, dv], S_T [..., dk, dv]) in float64.
+    """
+    kind = _qkv_kind(q)
+    if _qkv_kind(k) != kind or _qkv_kind(v) != kind:
+        raise TypeError("q, k, v must share a storage kind")
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or x.shape != q.shape:
+        raise ValueError("shape mismatch")
+    BH = int(np.prod(lead)) if lead else 1
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if S0 is not None:
+        S0 = np.ascontiguousarray(S0, dtype=np.float64)
+        if S0.shape != lead + (dk, dv):
+            raise ValueError("S0 shape mismatch")
+    o = np.empty(lead + (T, dv))
+    ST = np.empty(lead + (dk, dv))
+    rc = load(lib_path).gla_oracle_forward_pc(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, kind, x.ctypes.data,
+        None if S0 is None else S0.ctypes.data, o.ctypes.data, ST.ctypes.data,
+        BH, T, dk, dv, gate_id(gate), col_block, nthreads)
+    if rc != 0:
+        raise ValueError(f"gla_oracle_forward_pc rejected its arguments (rc={rc})")
     return o, ST
 
 
@@ -301,6 +341,44 @@ def closed_form(q, k, v, x, S0=None, gate="bounded") -> Tuple[np.ndarray, np.nda
 
 
 gate_fn = gate
+
+
+def closed_form_pc(q, k, v, x, S0=None, gate="bounded") -> Tuple[np.ndarray, np.ndarray]:
+    """Quadratic closed form of the per-channel recurrence, fp64 (tiny inputs only):
+
+        o_t[n] = sum_d q_t[d] (D_t[d] S0[d, n] + sum_{s <= t} W_d[t, s] k_s[d] v_s[n])
+        S_T    = diag(D_{T-1}) S0 + sum_s diag(W[T-1, s]) k_s v_s^T
+
+    with W_d, D_d the explicit decay products of :func:`decay_weights` for channel d.
+    """
+    q = _widen(np.asarray(q))
+    k = _widen(np.asarray(k))
+    v = _widen(np.asarray(v))
+    x = np.asarray(x, dtype=np.float64)
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    qf, kf, vf, xf = (q.reshape(BH, T, dk), k.reshape(BH, T, dk), v.reshape(BH, T, dv),
+                      x.reshape(BH, T, dk))
+    S0f = None if S0 is None else np.asarray(S0, dtype=np.float64).reshape(BH, dk, dv)
+    o = np.zeros((BH, T, dv))
+    ST = np.zeros((BH, dk, dv))
+    for h in range(BH):
+        if T == 0:
+            ST[h] = 0.0 if S0f is None else S0f[h]
+            continue
+        W = np.empty((dk, T, T))
+        D = np.empty((dk, T))
+        for d in range(dk):
+            W[d], D[d] = decay_weights(np.exp(gate_fn(xf[h, :, d], gate)))
+        scores = np.einsum("td,dts,sd->ts", qf[h], W, kf[h])   # sum_d q_t[d] W_d[t,s] k_s[d]
+        o[h] = scores @ vf[h]
+        ST[h] = (W[:, T - 1, :] * kf[h].T) @ vf[h]             # [d, n] = sum_s W_d[T-1,s] k_s[d] v_s[n]
+        if S0f is not None:
+            o[h] += (qf[h] * D.T) @ S0f[h]
+            ST[h] += D[:, T - 1][:, None] * S0f[h]
+    return o.reshape(lead + (T, dv)), ST.reshape(lead + (dk, dv))
 
 
 def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:

@@ -191,6 +191,95 @@ int gla_oracle_forward(const void* q, const void* k, const void* v, int qkv_is_b
   return 0;
 }
 
+/* Per-channel decay.  [LCT §3.1] speaks of a per-position cumulative decay
+ * without saying whether it is one scalar per position or one value per key
+ * channel; the second reading, in which each row d of the state has its own
+ * decay, is the gated-linear-attention form the scalar one specialises:
+ *
+ *     S_t[d][n] = a_t[d] * S_{t-1}[d][n] + k_t[d] v_t[n],   a_t[d] = exp(g(x_t[d]))
+ *     o_t       = S_t^T q_t
+ *
+ * with x of layout [BH][T][dk] and the same gates.  When every channel has the
+ * same x it is exactly the scalar recurrence above.  One token at a time, same
+ * threading as gla_oracle_forward. */
+int gla_oracle_forward_pc(const void* q, const void* k, const void* v, int qkv_is_bf16,
+                          const float* x, const double* S0, double* o, double* S_T,
+                          long long BH, long long T, int dk, int dv, int gate,
+                          int col_block, int nthreads) {
+  if (!q || !k || !v || !x || !o || !S_T) return 1;
+  if (BH < 0 || T < 0 || dk <= 0 || dv <= 0) return 1;
+  if (gate != ORACLE_GATE_BOUNDED_SIGMOID && gate != ORACLE_GATE_NEG_SOFTPLUS) return 1;
+  if (col_block <= 0 || col_block > dv) col_block = dv;
+  const long long ncb = (dv + col_block - 1) / col_block;
+  const long long tasks = BH * ncb;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long long task = 0; task < tasks; ++task) {
+    const long long bh = task / ncb;
+    const int n0 = (int)(task % ncb) * col_block;
+    const int nc = (n0 + col_block <= dv) ? col_block : dv - n0;
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)nc);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* at = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* vt = (double*)malloc(sizeof(double) * (size_t)nc);
+
+    for (int d = 0; d < dk; ++d)
+      for (int n = 0; n < nc; ++n)
+        S[(size_t)d * nc + n] = S0 ? S0[((size_t)bh * dk + d) * dv + n0 + n] : 0.0;
+
+    for (long long t = 0; t < T; ++t) {
+      const size_t row = (size_t)bh * (size_t)T + (size_t)t;
+      for (int d = 0; d < dk; ++d) {
+        kt[d] = widen(k, qkv_is_bf16, row * (size_t)dk + d);
+        qt[d] = widen(q, qkv_is_bf16, row * (size_t)dk + d);
+#if GLA_ORACLE_MUTANT == 12
+        /* planted: every channel takes channel 0's decay */
+        at[d] = exp(gla_oracle_gate((double)x[row * (size_t)dk], gate));
+#elif GLA_ORACLE_MUTANT == 13
+        /* planted: decay index shifted by one token */
+        at[d] = t == 0 ? 1.0 : exp(gla_oracle_gate((double)x[(row - 1) * (size_t)dk + d], gate));
+#else
+        at[d] = exp(gla_oracle_gate((double)x[row * (size_t)dk + d], gate));
+#endif
+      }
+      for (int n = 0; n < nc; ++n) vt[n] = widen(v, qkv_is_bf16, row * (size_t)dv + n0 + n);
+
+      /* S_t = diag(a_t) S_{t-1} + k_t v_t^T */
+      for (int d = 0; d < dk; ++d)
+        for (int n = 0; n < nc; ++n) {
+#if GLA_ORACLE_MUTANT == 11
+          /* planted: decay taken by value column instead of key row */
+          const double a = at[(n0 + n) % dk];
+#else
+          const double a = at[d];
+#endif
+          S[(size_t)d * nc + n] = a * S[(size_t)d * nc + n] + kt[d] * vt[n];
+        }
+      /* o_t = S_t^T q_t */
+      for (int n = 0; n < nc; ++n) {
+        double acc = 0.0;
+        for (int d = 0; d < dk; ++d) acc += S[(size_t)d * nc + n] * qt[d];
+        o[row * (size_t)dv + n0 + n] = acc;
+      }
+    }
+    for (int d = 0; d < dk; ++d)
+      for (int n = 0; n < nc; ++n)
+        S_T[((size_t)bh * dk + d) * dv + n0 + n] = S[(size_t)d * nc + n];
+    free(S);
+    free(kt);
+    free(qt);
+    free(at);
+    free(vt);
+  }
+  return 0;
+}
+
 /* d g / d x of the gate: bounded -5 sigmoid(x) (1 - sigmoid(x)); negative
  * softplus -softplus(-x) has derivative sigmoid(-x). */
 static double gate_slope(double x, int gate) {
