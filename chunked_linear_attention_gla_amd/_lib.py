@@ -64,6 +64,10 @@ _SIGS = {
                            _vp, _psz, _vp]),
     "gla_chunk_fwd_plan": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i,
                                 _pplan, _vp, _psz, _vp]),
+    "gla_plan_default_pc": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
+    "gla_plan_check_pc": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
+    "gla_chunk_fwd_pc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan,
+                              _vp, _psz, _vp]),
     "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
                            _i, _i, _i, _vp, _psz, _vp]),
 }
@@ -259,6 +263,52 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor
     _check("gla_chunk_fwd_plan", lib.gla_chunk_fwd_plan(
         _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, dt, _gate(gate),
         _path(path), cplan, _ptr(workspace), ctypes.byref(have), _stream(dev)))
+    return o, S_T
+
+
+def plan_default_pc(B: int, H: int, T: int, dk: int, dv: int, dtype=GLA_BF16) -> Plan:
+    cp = _CPlan()
+    _check("gla_plan_default_pc", load().gla_plan_default_pc(B, H, T, dk, dv, dtype, ctypes.byref(cp)))
+    return Plan(cp.segments, cp.dv_split)
+
+
+def plan_check_pc(B: int, H: int, T: int, dk: int, dv: int, plan: Plan, dtype=GLA_BF16) -> int:
+    """Status code of gla_plan_check_pc (0 = valid)."""
+    return int(load().gla_plan_check_pc(B, H, T, dk, dv, dtype, _cplan(plan)))
+
+
+def chunk_fwd_pc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor,
+                 S0: Optional[torch.Tensor] = None, gate="bounded", plan: Optional[Plan] = None,
+                 o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Per-channel-decay forward: returns (o [B,H,T,dv] fp32, S_T [B,H,dk,dv] fp32).
+
+    As :func:`chunk_fwd`, except x: [B, H, T, dk] fp32, one gate pre-activation per key
+    channel (row d of the state decays by exp(g(x[..., t, d]))).
+    """
+    B, H, T, dk, dv = _check_qkv(q, k, v, None, S0)
+    dev = q.device
+    _need(tuple(x.shape) == (B, H, T, dk) and x.dtype == torch.float32 and x.is_cuda and x.is_contiguous()
+          and x.device == dev, "x must be a contiguous fp32 [B, H, T, dk] tensor on q's device")
+    lib = load()
+    dt = _dtype_code(q)
+    if o is None:
+        o = torch.empty(B, H, T, dv, device=dev, dtype=torch.float32)
+    if S_T is None:
+        S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+    _need(tuple(o.shape) == (B, H, T, dv) and o.dtype == torch.float32 and o.is_contiguous() and o.device == dev,
+          "o must be fp32 [B, H, T, dv] on q's device")
+    _need(tuple(S_T.shape) == (B, H, dk, dv) and S_T.dtype == torch.float32 and S_T.is_contiguous()
+          and S_T.device == dev, "S_T must be fp32 [B, H, dk, dv] on q's device")
+    cplan = _cplan(plan)
+    args = lambda ws: (_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, dt,
+                       _gate(gate), cplan, ws)
+    need = ctypes.c_size_t(0)
+    _check("gla_chunk_fwd_pc", lib.gla_chunk_fwd_pc(*args(None), ctypes.byref(need), _stream(dev)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check("gla_chunk_fwd_pc", lib.gla_chunk_fwd_pc(*args(_ptr(workspace)), ctypes.byref(have), _stream(dev)))
     return o, S_T
 
 

@@ -450,6 +450,127 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
+gla_status_t gla_plan_check_pc(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                               const gla_plan_t* plan) {
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!plan) return GLA_ERR_NULL;
+  const long long nc = n_chunks(T);
+  if (plan->segments < 1 || plan->segments > GLA_MAX_SEGMENTS) return GLA_ERR_PLAN;
+  if (plan->segments > std::max(1LL, nc)) return GLA_ERR_PLAN;
+  const int s = plan->dv_split;
+  if (s != 1 && s != 2) return GLA_ERR_PLAN;
+  if (dv % s) return GLA_ERR_PLAN;
+  if (!gla::pc_config_built(dtype == GLA_BF16 ? 0 : 1, dk, dv / s))
+    return (dtype == GLA_F32 && dk != 64) ? GLA_ERR_UNSUPPORTED : GLA_ERR_PLAN;
+  return GLA_OK;
+}
+
+gla_status_t gla_plan_default_pc(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype, gla_plan_t* plan) {
+  if (!plan) return GLA_ERR_NULL;
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  // whole value rows per workgroup (fp32: 64-column slices), then segments until
+  // the grid covers the compute units
+  const long long BH = (long long)B * H;
+  const long long nc = n_chunks(T);
+  const int split = (dtype == GLA_F32) ? dv / 64 : 1;
+  const long long units = BH * split;
+  int segs = 1;
+  while (segs < GLA_MAX_SEGMENTS && units * segs < cus && nc / (2LL * segs) >= 4) segs *= 2;
+  if (segs > std::max(1LL, nc)) segs = (int)std::max(1LL, nc);
+  plan->segments = segs;
+  plan->dv_split = split;
+  return gla_plan_check_pc(B, H, T, dk, dv, dtype, plan);
+}
+
+gla_status_t gla_chunk_fwd_pc(const void* q, const void* k, const void* v, const float* x, const float* S0,
+                              float* o, float* S_T, int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                              gla_gate_t gate, const gla_plan_t* plan, void* workspace, size_t* workspace_bytes,
+                              void* stream) {
+  if (!workspace_bytes) return GLA_ERR_NULL;
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_gate(gate)) return GLA_ERR_ARG;
+  gla_plan_t pl;
+  if (plan) {
+    st = gla_plan_check_pc(B, H, T, dk, dv, dtype, plan);
+    if (st != GLA_OK) return st;
+    pl = *plan;
+  } else {
+    st = gla_plan_default_pc(B, H, T, dk, dv, dtype, &pl);
+    if (st != GLA_OK) return st;
+  }
+  const long long BH = (long long)B * H;
+  const size_t hs = pl.segments > 1 ? align_up((size_t)BH * (pl.segments - 1) * dk * dv * 4) : 0;
+  const size_t gs = pl.segments > 1 ? align_up((size_t)BH * pl.segments * dk * 4) : 0;
+  if (!workspace) {
+    *workspace_bytes = std::max<size_t>(hs + gs, kAlign);
+    return GLA_OK;
+  }
+  if (*workspace_bytes < hs + gs) return GLA_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return GLA_ERR_ALIGN;
+  if (!S_T) return GLA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !x || !o)) return GLA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(x, 16) || !aligned(o, 16) ||
+      !aligned(S_T, 16) || !aligned(S0, 16))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dtype);
+  const Range ins[] = {{q, (size_t)BH * T * dk * es}, {k, (size_t)BH * T * dk * es}, {v, (size_t)BH * T * dv * es},
+                       {x, (size_t)BH * T * dk * 4},  {S0, (size_t)BH * dk * dv * 4}};
+  const Range outs[] = {{o, (size_t)BH * T * dv * 4}, {S_T, (size_t)BH * dk * dv * 4},
+                        {pl.segments > 1 ? workspace : nullptr, hs + gs}};
+  for (size_t i = 0; i < 3; ++i) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return GLA_ERR_ALIAS;
+    for (size_t j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return GLA_ERR_ALIAS;
+  }
+  gla::PcParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.x = x;
+  p.S0 = S0;
+  p.o = o;
+  p.ST = S_T;
+  p.seg_state = pl.segments > 1 ? (float*)workspace : nullptr;
+  p.seg_decay = pl.segments > 1 ? (float*)((char*)workspace + hs) : nullptr;
+  p.T = T;
+  p.dk = dk;
+  p.dv = dv;
+  p.BH = (int)BH;
+  p.nchunks = (int)n_chunks(T);
+  p.segments = pl.segments;
+  p.nslices = pl.dv_split;
+  p.gate = gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus;
+  const int dt = dtype == GLA_BF16 ? 0 : 1;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (T == 0) {
+    // nothing decays: S_T = S0 (or zero), one workgroup per head writes it
+    p.segments = 1;
+    p.nchunks = 0;
+    p.grid = (int)(BH * pl.dv_split);
+    return gla::launch_pc_chunk_output(p, dt, s) == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+  }
+  if (pl.segments > 1) {
+    p.grid = (int)(BH * pl.dv_split * (pl.segments - 1));
+    e = gla::launch_pc_segment_states(p, dt, s);
+  }
+  if (e == hipSuccess) {
+    p.grid = (int)(BH * pl.dv_split * pl.segments);
+    e = gla::launch_pc_chunk_output(p, dt, s);
+  }
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
 gla_status_t gla_chunk_fwd(const void* q, const void* k, const void* v, const float* x, const float* S0, float* o,
                            float* S_T, int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
                            gla_gate_t gate, gla_path_t path, void* workspace, size_t* workspace_bytes,

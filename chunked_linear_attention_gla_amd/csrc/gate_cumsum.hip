@@ -15,24 +15,6 @@
 
 namespace gla {
 
-// g = -5 * sigmoid(x), sigmoid evaluated without overflow for either sign of x.
-__device__ __forceinline__ float gate_bounded_sigmoid(float x) {
-  float s;
-  if (x >= 0.0f) {
-    s = 1.0f / (1.0f + exp_e(-x));
-  } else {
-    const float e = exp_e(x);
-    s = e / (1.0f + e);
-  }
-  return -5.0f * s;
-}
-
-// g = -softplus(-x) = -(max(-x, 0) + log1p(e^-|x|)) = log sigmoid(x)
-__device__ __forceinline__ float gate_neg_softplus(float x) {
-  const float z = -x;
-  return -(fmaxf(z, 0.0f) + log1pf(exp_e(-fabsf(z))));
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_or_zero(float v) {
   // row-local lane shift; lanes whose source falls outside the 16-lane row read 0

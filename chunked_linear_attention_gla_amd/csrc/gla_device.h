@@ -34,6 +34,26 @@ __device__ __forceinline__ float exp_e(float x) {
   return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
 }
 
+// Log-decay gates ("Engineering Long-Context Training for Trillion-Parameter MoE
+// Models: Three Key Breakthroughs", §3.2).
+// g = -5 * sigmoid(x), sigmoid evaluated without overflow for either sign of x.
+__device__ __forceinline__ float gate_bounded_sigmoid(float x) {
+  float s;
+  if (x >= 0.0f) {
+    s = 1.0f / (1.0f + exp_e(-x));
+  } else {
+    const float e = exp_e(x);
+    s = e / (1.0f + e);
+  }
+  return -5.0f * s;
+}
+
+// g = -softplus(-x) = -(max(-x, 0) + log1p(e^-|x|)) = log sigmoid(x)
+__device__ __forceinline__ float gate_neg_softplus(float x) {
+  const float z = -x;
+  return -(fmaxf(z, 0.0f) + log1pf(exp_e(-fabsf(z))));
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
@@ -106,6 +126,13 @@ template <> struct Elem<bf16> {
   __device__ static __forceinline__ void store8_raw(bf16* dst, const Vec8& v) {
     *reinterpret_cast<uint4*>(dst) = v.u;
   }
+  // store 8 elements, each with its own scale
+  __device__ static __forceinline__ void store8_vscaled(bf16* dst, const Vec8& v, const float (&s)[8]) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = cvt(get(v, e) * s[e]);
+    *reinterpret_cast<bf16x8*>(dst) = o;
+  }
   // two 4-element (8-byte) LDS reads at cols c and c + 16 of one row
   __device__ static __forceinline__ Frag load_frag(const bf16* row, int c) {
     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + c);
@@ -166,6 +193,10 @@ template <> struct Elem<float> {
     *reinterpret_cast<float4*>(dst) = v.a;
     *reinterpret_cast<float4*>(dst + 4) = v.b;
   }
+  __device__ static __forceinline__ void store8_vscaled(float* dst, const Vec8& v, const float (&s)[8]) {
+    *reinterpret_cast<float4*>(dst) = make_float4(v.a.x * s[0], v.a.y * s[1], v.a.z * s[2], v.a.w * s[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(v.b.x * s[4], v.b.y * s[5], v.b.z * s[6], v.b.w * s[7]);
+  }
   __device__ static __forceinline__ Frag load_frag(const float* row, int c) {
     Frag f;
     f.lo = *reinterpret_cast<const floatx4*>(row + c);
@@ -215,6 +246,9 @@ template <int NCOL> struct TokTile<bf16, NCOL> {
   __device__ static __forceinline__ void store8_raw(bf16* t, int row, int col, const E::Vec8& v) {
     E::store8_raw(t + row * LD + col, v);
   }
+  __device__ static __forceinline__ void store8_v(bf16* t, int row, int col, const E::Vec8& v, const float (&s)[8]) {
+    E::store8_vscaled(t + row * LD + col, v, s);
+  }
   __device__ static __forceinline__ E::Frag load(const bf16* t, int k0, int c0, int lane) {
     typedef short shortx4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
@@ -240,6 +274,10 @@ template <int NCOL> struct TokTile<float, NCOL> {
   __device__ static __forceinline__ void store8_raw(float* t, int row, int col, const E::Vec8& v) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = E::get(v, e);
+  }
+  __device__ static __forceinline__ void store8_v(float* t, int row, int col, const E::Vec8& v, const float (&s)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = E::get(v, e) * s[e];
   }
   __device__ static __forceinline__ E::Frag load(const float* t, int k0, int c0, int lane) {
     return E::load_frag(t + (c0 + (lane & 15)) * LD, k0 + 4 * (lane >> 4));

@@ -68,6 +68,32 @@ bool ws_kernels_supported(int dtype, int dk, int slice);
 hipError_t launch_chunk_output_ws(const ChunkParams& p, int dk, int slice, bool diag, hipStream_t stream);
 hipError_t launch_segment_states_ws(const ChunkParams& p, int dk, int slice, hipStream_t stream);
 
+// Per-channel decay (pc_kernels.hip): x [BH][T][dk]; the gate and the chunk-local
+// cumulative sum are computed inside the kernels.
+struct PcParams {
+  const void* q;          // [BH][T][dk]
+  const void* k;          // [BH][T][dk]
+  const void* v;          // [BH][T][dv]
+  const float* x;         // [BH][T][dk] gate pre-activation, one per key channel
+  const float* S0;        // [BH][dk][dv] or nullptr
+  float* o;               // [BH][T][dv]
+  float* ST;              // [BH][dk][dv]
+  float* seg_state;       // [BH][segments-1][dk][dv]  local final states
+  float* seg_decay;       // [BH][segments][dk]        per-channel log-decay of each segment
+  long long T;
+  int dk, dv;
+  int BH;
+  int nchunks;
+  int segments;
+  int nslices;
+  int grid;
+  int gate;               // GateKind
+};
+// Built (dtype, dk, slice) combinations: bf16 with dk, slice in {64, 128}; fp32 with 64, 64.
+bool pc_config_built(int dtype, int dk, int slice);
+hipError_t launch_pc_segment_states(const PcParams& p, int dtype, hipStream_t stream);
+hipError_t launch_pc_chunk_output(const PcParams& p, int dtype, hipStream_t stream);
+
 // Backward-pass kernels (bwd_kernels.hip).
 //   dx from the pairs that span each token (see bwd_kernels.hip); Sfw and Sbw are the
 //   per-chunk states stored by the dq pass (S^T before each chunk) and by the dk pass

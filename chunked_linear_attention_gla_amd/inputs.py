@@ -8,7 +8,8 @@ Workload recipe, shared by every named workload:
   q ~ N(0, 1) / sqrt(dk)                  (drawn in fp32, then stored)
   k ~ N(0, 1), L2-normalised per token    (normalised in fp32, then stored)
   v ~ N(0, 1)
-  x ~ N(x_mean, x_std), one fp32 scalar per (batch, head, token)
+  x ~ N(x_mean, x_std), one fp32 scalar per (batch, head, token), or per
+      (batch, head, token, key channel) for the per-channel-decay workloads
   S0 ~ N(0, s0_std) fp32 when s0_std > 0, else absent (zero initial state)
 q, k, v are stored in bf16 (round-to-nearest-even, torch's cast) or fp32; x, S0
 always fp32.  N(m, s) means mean m and standard deviation s.  Draws happen in the
@@ -43,6 +44,7 @@ class Workload:
     gate: str               # "bounded" (g = -5 sigmoid(x)) or "neg_softplus"
     seed: int
     note: str = ""
+    per_channel: bool = False  # x has one value per key channel: [B, H, T, dk]
 
     @property
     def tokens(self) -> int:
@@ -67,6 +69,9 @@ WORKLOADS: Dict[str, Workload] = {
                           "bounded", 1003, "long sequence; chained continuation of 65536 tokens"),
     "bf16_1m": Workload("bf16_1m", 1, 8, 1048576, 128, 128, "bf16", 0.0, 1.0, 0.0,
                         "bounded", 1004, "million-token head group"),
+    "bf16_64k_pc": Workload("bf16_64k_pc", 1, 32, 65536, 128, 128, "bf16", 4.0, 1.0, 0.0, "bounded", 1005,
+                            "per-channel decay: x per (token, key channel), same shapes and regime",
+                            per_channel=True),
 }
 
 # The 64K strong-decay workload is the one throughput is quoted on.
@@ -89,8 +94,8 @@ def make_inputs(w: Workload, device="cpu", *, T: Optional[int] = None, H: Option
     T, H, B, seed override the workload's values (smaller samples of the same
     recipe).  x_const replaces the gate pre-activation by a constant (for example
     -inf gives decay exactly 1 under the bounded gate).
-    Returns dict(q, k, v, x, S0) with q/k [B,H,T,dk], v [B,H,T,dv], x [B,H,T],
-    S0 [B,H,dk,dv] or None.
+    Returns dict(q, k, v, x, S0) with q/k [B,H,T,dk], v [B,H,T,dv], x [B,H,T]
+    ([B,H,T,dk] for a per-channel workload), S0 [B,H,dk,dv] or None.
     """
     B = w.B if B is None else B
     H = w.H if H is None else H
@@ -109,7 +114,7 @@ def make_inputs(w: Workload, device="cpu", *, T: Optional[int] = None, H: Option
     k.div_(torch.linalg.vector_norm(k, dim=-1, keepdim=True).clamp_min(1e-30))
     k = k.to(st)
     v = torch.randn(B, H, T, w.dv, **f32).to(st)
-    x = torch.randn(B, H, T, **f32)
+    x = torch.randn(B, H, T, *((w.dk,) if w.per_channel else ()), **f32)
     x.mul_(w.x_std).add_(w.x_mean)
     if x_const is not None:
         x.fill_(x_const)

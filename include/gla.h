@@ -217,6 +217,35 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
                            gla_dtype_t dtype, gla_gate_t gate, gla_path_t path,
                            void* workspace, size_t* workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Per-channel decay.  The same chunked method with one decay per key channel
+ * (the per-position decay of [LCT §3.1] read as a vector over the key
+ * dimension):
+ *     S_t[d][n] = a_t[d] S_{t-1}[d][n] + k_t[d] v_t[n],  a_t[d] = e^{g(x_t[d])},
+ *     o_t = S_t^T q_t.
+ * The decay cannot be factored out of the sum over d, so every causal 16x16
+ * tile, diagonal or not, is one matrix product of q e^{b - r_u} with k
+ * e^{r_u - b} referenced to the query tile's start; the bounded gate keeps the
+ * reciprocal factor of a 16-token tile below e^80 [LCT §3.2-§3.3].  The gate and
+ * the chunk-local cumulative sum run inside the kernels (no b buffer).
+ *   x [B][H][T][dk] fp32 (one gate pre-activation per key channel, 16-byte
+ *   aligned); other arguments as for gla_chunk_fwd (S0 may be NULL).
+ * Built: bf16 with dk in {64, 128} and value slices of 64 or 128 columns
+ * (dv_split 1 or 2); fp32 with dk = 64 and 64-column slices.  Other valid
+ * shapes return GLA_ERR_PLAN or GLA_ERR_UNSUPPORTED.  The workspace holds the
+ * segment states when the plan has several segments; workspace == NULL returns
+ * its size (at least 256) in *workspace_bytes and enqueues nothing.  Errors and
+ * validation as gla_chunk_fwd. */
+gla_status_t gla_plan_default_pc(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                                 gla_plan_t* plan);
+gla_status_t gla_plan_check_pc(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                               const gla_plan_t* plan);
+gla_status_t gla_chunk_fwd_pc(const void* q, const void* k, const void* v, const float* x,
+                              const float* S0, float* o, float* S_T,
+                              int B, int H, long long T, int dk, int dv,
+                              gla_dtype_t dtype, gla_gate_t gate, const gla_plan_t* plan,
+                              void* workspace, size_t* workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
