@@ -86,6 +86,8 @@ def parse():
     ap.add_argument("--no-ablation", action="store_true", help="skip the diagonal-branch comparison")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--backward-only", action="store_true", help="time only the backward pass (profiling)")
+    ap.add_argument("--no-per-channel", action="store_true", help="skip the per-channel-decay measurement")
+    ap.add_argument("--per-channel-only", action="store_true", help="time only the per-channel forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration) and exit")
     return ap.parse_args()
@@ -102,7 +104,7 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
 
 
-def cpu_baseline(w, target_s: float):
+def cpu_baseline(w, target_s: float, per_channel: bool = False):
     """Time the fp64 oracle on a bounded sample of the workload (all heads, a prefix of
     the sequence sized to take about target_s seconds on this host)."""
     import numpy as np
@@ -116,7 +118,7 @@ def cpu_baseline(w, target_s: float):
         args = [gin.to_numpy_bits(flat(inp[n])) for n in ("q", "k", "v", "x")]
         s0 = None if inp["S0"] is None else flat(inp["S0"]).cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
-        oracle.forward(*args, s0, gate=w.gate)
+        (oracle.forward_pc if per_channel else oracle.forward)(*args, s0, gate=w.gate)
         return time.perf_counter() - t0
 
     T0 = 256
@@ -126,7 +128,8 @@ def cpu_baseline(w, target_s: float):
     dt = run(T)
     return {"value": w.B * T / dt, "unit": "tokens/s", "cores": lib_threads, "kind": "oracle",
             "sample": f"all {w.B * w.H} heads of {w.name}, first {T} of {w.T} tokens (seed {w.seed}); "
-                      f"fp64 sequential recurrence, OpenMP over heads x 16-column blocks; {dt:.1f} s"}
+                      f"fp64 sequential {'per-channel ' if per_channel else ''}recurrence, OpenMP over heads x "
+                      f"16-column blocks; {dt:.1f} s"}
 
 
 def cpu_baseline_backward(w, target_s: float):
@@ -283,6 +286,59 @@ class BackwardTimer:
         return elapsed * 1e3 / steps, ev[0].elapsed_time(ev[steps]) / steps
 
 
+def time_calls(torch, fn, steps, warmup):
+    """(ms per call from the host clock, ms per call from HIP events on the current stream)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    t0 = time.perf_counter()
+    ev[0].record()
+    for _ in range(steps):
+        fn()
+    ev[1].record()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps, ev[0].elapsed_time(ev[1]) / steps
+
+
+def per_channel_bytes_per_token_head(dk: int, dv: int, es: int) -> int:
+    # q, k, v in storage precision, x (one fp32 per key channel) and o (fp32)
+    return (2 * dk + dv) * es + 4 * dk + 4 * dv
+
+
+def per_channel_result(gla, gin, torch, steps, warmup, cpu_seconds):
+    """The per-channel-decay forward (gla_chunk_fwd_pc: segment pre-pass + output pass)
+    on its own 64K workload, timed per call."""
+    w = gin.WORKLOADS["bf16_64k_pc"]
+    dev = torch.device("cuda:0")
+    inp = gin.make_inputs(w, dev)
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    o = torch.empty(B, H, T, dv, device=dev)
+    ST = torch.empty(B, H, dk, dv, device=dev)
+    plan = gla.plan_default_pc(B, H, T, dk, dv)
+    ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    fn = lambda: gla.chunk_fwd_pc(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], gate=w.gate, plan=plan,
+                                  o=o, S_T=ST, workspace=ws)
+    ms_host, ms_ev = time_calls(torch, fn, steps, warmup)
+    es = inp["q"].element_size()
+    del inp, o, ws
+    nbytes = B * H * T * per_channel_bytes_per_token_head(dk, dv, es) + B * H * dk * dv * 4
+    achieved = nbytes / (ms_ev / 1e3) / 1e9
+    res = {
+        "what": "gla_chunk_fwd_pc: per-channel decay forward, all kernels of the call",
+        "workload": w.name, "x": f"N({w.x_mean},{w.x_std}) per (token, key channel)",
+        "plan": {"segments": plan.segments, "dv_split": plan.dv_split}, "steps": steps,
+        "ms_per_call": round(ms_host, 4), "ms_per_call_events": round(ms_ev, 4),
+        "tokens_per_s": round(B * T / (ms_ev / 1e3), 1),
+        "tflops": round(B * H * T * algorithmic_flops_per_token_head(dk, dv) / (ms_ev / 1e3) / 1e12, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes},
+    }
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(w, cpu_seconds, per_channel=True)
+    return res
+
+
 def backward_result(gla, gin, torch, w, path, steps, warmup):
     t = BackwardTimer(gla, gin, torch, w, path)
     ms_host, ms_ev = t.run(steps, warmup)
@@ -323,6 +379,10 @@ def main():
     path = args.path or "unified"
     torch.cuda.set_device(torch.device("cuda:0"))
     plan = gla.Plan(*(int(s) for s in args.plan.split(","))) if args.plan else None
+    if args.per_channel_only:
+        print(json.dumps({"per_channel": per_channel_result(gla, gin, torch, args.steps, args.warmup, 0.0)}),
+              flush=True)
+        return
     if args.backward_only:
         print(json.dumps({"workload": w.name, "backward": backward_result(gla, gin, torch, w, path, args.steps,
                                                                          args.warmup)}), flush=True)
@@ -397,6 +457,9 @@ def main():
         result["backward"] = backward_result(gla, gin, torch, w, path, min(args.steps, 20), min(args.warmup, 5))
         if not args.no_cpu_baseline:
             result["backward"]["cpu_baseline"] = cpu_baseline_backward(w, args.cpu_seconds / 2)
+    if not args.no_per_channel and not args.plan and w.name == gin.HEADLINE:
+        result["per_channel"] = per_channel_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5),
+                                                   0.0 if args.no_cpu_baseline else args.cpu_seconds / 2)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
