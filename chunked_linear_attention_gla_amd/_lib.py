@@ -68,6 +68,9 @@ _SIGS = {
     "gla_plan_check_pc": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
     "gla_chunk_fwd_pc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan,
                               _vp, _psz, _vp]),
+    "gla_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
+    "gla_chunk_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _ll, _i, _i, _i, _i, _i,
+                                  _vp, _psz, _vp]),
     "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
                            _i, _i, _i, _vp, _psz, _vp]),
 }
@@ -309,6 +312,81 @@ def chunk_fwd_pc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Ten
         workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=dev)
     have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     _check("gla_chunk_fwd_pc", lib.gla_chunk_fwd_pc(*args(_ptr(workspace)), ctypes.byref(have), _stream(dev)))
+    return o, S_T
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor, S: torch.Tensor,
+                gate="bounded", o: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent step per head: S <- diag(a) S + k v^T (in place), returns o = S^T q.
+
+    q, k: [B, H, dk], v: [B, H, dv] (bfloat16 or float32); x: fp32 [B, H] (one decay per head)
+    or [B, H, dk] (one per key channel); S: fp32 [B, H, dk, dv], updated in place.
+    """
+    _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3 and v.shape[:2] == q.shape[:2],
+          "q, k must be [B, H, dk] and v [B, H, dv]")
+    B, H, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    for t in (q, k, v, x, S):
+        _need(t.is_cuda and t.is_contiguous() and t.device == dev, "tensors must be contiguous on q's device")
+    per_channel = x.dim() == 3
+    _need(x.dtype == torch.float32 and tuple(x.shape) in ((B, H), (B, H, dk)), "x must be fp32 [B, H] or [B, H, dk]")
+    _need(S.dtype == torch.float32 and tuple(S.shape) == (B, H, dk, dv), "S must be fp32 [B, H, dk, dv]")
+    if o is None:
+        o = torch.empty(B, H, dv, device=dev, dtype=torch.float32)
+    _need(tuple(o.shape) == (B, H, dv) and o.dtype == torch.float32 and o.is_contiguous() and o.device == dev,
+          "o must be fp32 [B, H, dv] on q's device")
+    _check("gla_decode_step", load().gla_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S), _ptr(o), B, H, dk,
+                                                     dv, _dtype_code(q), _gate(gate), int(per_channel),
+                                                     _stream(dev)))
+    return o
+
+
+def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor, cu_seqlens: torch.Tensor,
+                     max_seqlen: int, S0: Optional[torch.Tensor] = None, gate="bounded", path="unified",
+                     o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Forward over packed sequences: returns (o [H, T, dv] fp32, S_T [N, H, dk, dv] fp32).
+
+    q, k: [H, T, dk], v: [H, T, dv], x: fp32 [H, T] -- every head holds the N sequences back
+    to back; cu_seqlens: int64 [N + 1] offsets on the device (sequence n is rows
+    cu_seqlens[n]:cu_seqlens[n+1]); max_seqlen: the longest sequence (host int);
+    S0: fp32 [N, H, dk, dv] or None.  Rows covered by no sequence are left unwritten in o.
+    """
+    _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3 and v.shape[:2] == q.shape[:2],
+          "q, k must be [H, T, dk] and v [H, T, dv]")
+    H, T, dk = q.shape
+    dv = v.shape[2]
+    dev = q.device
+    _need(q.dtype == k.dtype == v.dtype, "q, k, v must share a dtype")
+    for t in (q, k, v, x, cu_seqlens):
+        _need(t.is_cuda and t.is_contiguous() and t.device == dev, "tensors must be contiguous on q's device")
+    _need(x.dtype == torch.float32 and tuple(x.shape) == (H, T), "x must be fp32 [H, T]")
+    _need(cu_seqlens.dtype == torch.int64 and cu_seqlens.dim() == 1 and cu_seqlens.numel() >= 2,
+          "cu_seqlens must be int64 [N + 1]")
+    N = cu_seqlens.numel() - 1
+    if S0 is not None:
+        _need(tuple(S0.shape) == (N, H, dk, dv) and S0.dtype == torch.float32 and S0.is_contiguous()
+              and S0.device == dev, "S0 must be fp32 [N, H, dk, dv] on q's device")
+    if o is None:
+        o = torch.zeros(H, T, dv, device=dev, dtype=torch.float32)
+    if S_T is None:
+        S_T = torch.empty(N, H, dk, dv, device=dev, dtype=torch.float32)
+    _need(tuple(o.shape) == (H, T, dv) and o.dtype == torch.float32 and o.is_contiguous() and o.device == dev,
+          "o must be fp32 [H, T, dv] on q's device")
+    _need(tuple(S_T.shape) == (N, H, dk, dv) and S_T.dtype == torch.float32 and S_T.is_contiguous()
+          and S_T.device == dev, "S_T must be fp32 [N, H, dk, dv] on q's device")
+    lib = load()
+    args = lambda ws: (_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(cu_seqlens), N, H,
+                       T, int(max_seqlen), dk, dv, _dtype_code(q), _gate(gate), _path(path), ws)
+    need = ctypes.c_size_t(0)
+    _check("gla_chunk_fwd_varlen", lib.gla_chunk_fwd_varlen(*args(None), ctypes.byref(need), _stream(dev)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check("gla_chunk_fwd_varlen", lib.gla_chunk_fwd_varlen(*args(_ptr(workspace)), ctypes.byref(have),
+                                                            _stream(dev)))
     return o, S_T
 
 

@@ -140,6 +140,8 @@ gla::ChunkParams make_params(const void* q, const void* k, const void* v, const 
   p.Tl = T;
   p.s0_transposed = 0;
   p.state_out = nullptr;
+  p.cu_seqlens = nullptr;
+  p.H = H;
   return p;
 }
 
@@ -447,6 +449,99 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
     if (e == hipSuccess) e = gla::launch_grad_dx(q, k, v, dO, b, x, Sfw, Sbw, dx, BH, T, dk_, dv_, dt, g, s);
   }
   if (e == hipSuccess) e = gla::launch_grad_ds0(D0, b, dS_T, dS0, BH, T, dk_, dv_, s);
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* x, const float* S0,
+                                  float* o, float* S_T, const long long* cu_seqlens, int N, int H, long long T,
+                                  long long max_seqlen, int dk, int dv, gla_dtype_t dtype, gla_gate_t gate,
+                                  gla_path_t path, void* workspace, size_t* workspace_bytes, void* stream) {
+  if (!workspace_bytes) return GLA_ERR_NULL;
+  if (N < 1) return GLA_ERR_SHAPE;
+  gla_status_t st = check_sizes(N, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (max_seqlen < 0 || max_seqlen > T) return GLA_ERR_SHAPE;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_gate(gate) || !valid_path(path)) return GLA_ERR_ARG;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  // the plan is sized by the longest sequence; every sequence is cut into the same
+  // number of segments
+  gla_plan_t pl;
+  st = default_plan_for(N, H, max_seqlen, dk, dv, dtype, path, cus, &pl);
+  if (st != GLA_OK) return st;
+  const long long NH = (long long)N * H;
+  const size_t b_bytes = align_up((size_t)H * (size_t)T * 4);
+  const size_t s_bytes = seg_bytes(NH, dk, dv, pl.segments);
+  if (!workspace) {
+    *workspace_bytes = std::max(b_bytes + s_bytes, kAlign);
+    return GLA_OK;
+  }
+  if (*workspace_bytes < b_bytes + s_bytes) return GLA_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return GLA_ERR_ALIGN;
+  if (!S_T || !cu_seqlens) return GLA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !x || !o)) return GLA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(S_T, 16) ||
+      !aligned(S0, 16) || !aligned(x, 4) || !aligned(cu_seqlens, 8))
+    return GLA_ERR_ALIGN;
+  const size_t es = elem_size(dtype);
+  const Range ins[] = {{q, (size_t)H * T * dk * es},      {k, (size_t)H * T * dk * es},
+                       {v, (size_t)H * T * dv * es},      {x, (size_t)H * T * 4},
+                       {S0, (size_t)NH * dk * dv * 4},    {cu_seqlens, (size_t)(N + 1) * 8}};
+  const Range outs[] = {{o, (size_t)H * T * dv * 4}, {S_T, (size_t)NH * dk * dv * 4}, {workspace, b_bytes + s_bytes}};
+  for (size_t i = 0; i < 3; ++i) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return GLA_ERR_ALIAS;
+    for (size_t j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return GLA_ERR_ALIAS;
+  }
+  float* bbuf = (float*)workspace;
+  void* seg = (char*)workspace + b_bytes;
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = dtype == GLA_BF16 ? 0 : 1;
+  const long long max_chunks = n_chunks(max_seqlen);
+  hipError_t e = gla::launch_gate_cumsum_varlen(
+      x, bbuf, cu_seqlens, N, H, T, max_chunks,
+      gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus, s);
+  gla::ChunkParams p = make_params(q, k, v, bbuf, S0, o, S_T, N, H, T, dk, dv, pl, seg);
+  p.cu_seqlens = cu_seqlens;
+  p.nchunks = (int)max_chunks;
+  if (e == hipSuccess && pl.segments > 1) {
+    p.grid = (int)(NH * pl.dv_split * (pl.segments - 1));
+    e = gla::launch_segment_states(p, dt, s);
+  }
+  if (e == hipSuccess) {
+    p.grid = (int)(NH * pl.dv_split * pl.segments);
+    e = gla::launch_chunk_output(p, dt, path == GLA_PATH_DIAG_BRANCH, s);
+  }
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
+gla_status_t gla_decode_step(const void* q, const void* k, const void* v, const float* x, float* S, float* o,
+                             int B, int H, int dk, int dv, gla_dtype_t dtype, gla_gate_t gate, int per_channel,
+                             void* stream) {
+  gla_status_t st = check_sizes(B, H, 1, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_gate(gate) || (per_channel != 0 && per_channel != 1)) return GLA_ERR_ARG;
+  if (!q || !k || !v || !x || !S || !o) return GLA_ERR_NULL;
+  if (!aligned(S, 16) || !aligned(o, 16) || !aligned(q, 4) || !aligned(k, 4) || !aligned(v, 4) || !aligned(x, 4))
+    return GLA_ERR_ALIGN;
+  const long long BH = (long long)B * H;
+  const size_t es = elem_size(dtype);
+  const Range ins[] = {{q, (size_t)BH * dk * es},
+                       {k, (size_t)BH * dk * es},
+                       {v, (size_t)BH * dv * es},
+                       {x, (size_t)BH * (per_channel ? dk : 1) * 4}};
+  const Range rs{S, (size_t)BH * dk * dv * 4}, ro{o, (size_t)BH * dv * 4};
+  for (const Range& in : ins)
+    if (overlap(rs, in) || overlap(ro, in)) return GLA_ERR_ALIAS;
+  if (overlap(rs, ro)) return GLA_ERR_ALIAS;
+  hipError_t e = gla::launch_decode_step(q, k, v, x, S, o, BH, dk, dv, dtype == GLA_BF16 ? 0 : 1,
+                                         gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid
+                                                                          : gla::kGateNegSoftplus,
+                                         per_channel != 0, (hipStream_t)stream);
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 

@@ -37,10 +37,62 @@ __host__ __device__ constexpr int off_i(int t) { return t - (off_j(t) - 1) * off
 static_assert(tri_j(9) == 3 && tri_i(9) == 3 && tri_j(4) == 2 && tri_i(4) == 1, "tile numbering");
 static_assert(off_j(5) == 3 && off_i(5) == 2 && off_j(2) == 2 && off_i(2) == 1, "tile numbering");
 
-// Per-head buffer descriptors of the streamed tensors.
+// Rows of one work unit (a head of the dense layout, or one sequence of one head
+// when sequences are packed) in the streamed tensors.
+struct HeadSpan {
+  long long row0;   // first row in q, k, v, o
+  long long brow0;  // first entry in b
+  uint32_t T;       // rows of the unit
+  uint32_t Tl;      // entries of b (T + pad for a reversed pass)
+  int nchunks;
+};
+
+// Packed sequences: the offsets are clamped into [0, total] and the length to the
+// chunk count the launch was sized for, so inconsistent offsets give wrong values,
+// never an access outside the tensors.
+__device__ __forceinline__ HeadSpan head_span(const ChunkParams& p, int bh) {
+  HeadSpan s;
+  if (!p.cu_seqlens) {
+    s.row0 = (long long)bh * p.T;
+    s.brow0 = (long long)bh * p.Tl;
+    s.T = (uint32_t)p.T;
+    s.Tl = (uint32_t)p.Tl;
+    s.nchunks = p.nchunks;
+    return s;
+  }
+  const int n = bh / p.H, h = bh - n * p.H;
+  long long a = p.cu_seqlens[n], e = p.cu_seqlens[n + 1];
+  a = a < 0 ? 0 : (a > p.T ? p.T : a);
+  e = e < a ? a : (e > p.T ? p.T : e);
+  if (e - a > (long long)p.nchunks * kChunk) e = a + (long long)p.nchunks * kChunk;
+  s.row0 = (long long)h * p.T + a;
+  s.brow0 = s.row0;
+  s.T = (uint32_t)(e - a);
+  s.Tl = s.T;
+  s.nchunks = (int)((e - a + kChunk - 1) / kChunk);
+  return s;
+}
+
+// Per-unit buffer descriptors of the streamed tensors (sized to the unit's rows) and
+// the unit's row counts.
 struct HeadBuffers {
   rsrc_t q, k, v, b, o;
+  uint32_t T, Tl;
 };
+
+template <typename T, int DK>
+__device__ __forceinline__ HeadBuffers head_buffers(const ChunkParams& p, const HeadSpan& s) {
+  HeadBuffers hb;
+  const uint32_t es = (uint32_t)sizeof(T);
+  hb.q = p.q ? make_rsrc(static_cast<const T*>(p.q) + s.row0 * DK, s.T * DK * es) : make_rsrc(nullptr, 0u);
+  hb.k = make_rsrc(static_cast<const T*>(p.k) + s.row0 * DK, s.T * DK * es);
+  hb.v = make_rsrc(static_cast<const T*>(p.v) + s.row0 * p.dv, s.T * (uint32_t)p.dv * es);
+  hb.b = make_rsrc(p.b + s.brow0, s.Tl * 4u);
+  hb.o = p.o ? make_rsrc(p.o + s.row0 * p.dv, s.T * (uint32_t)p.dv * 4u) : make_rsrc(nullptr, 0u);
+  hb.T = s.T;
+  hb.Tl = s.Tl;
+  return hb;
+}
 
 __device__ __forceinline__ float lane_value(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));

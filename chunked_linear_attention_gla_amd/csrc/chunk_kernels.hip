@@ -74,14 +74,14 @@ struct Staged {
   // chunk starting at logical token t0 (rows in logical order; see row_offset)
   __device__ __forceinline__ void load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0, int col0,
                                        int tid) {
-    const uint32_t len = (uint32_t)p.Tl;  // b is in logical order
+    const uint32_t len = hb.Tl;  // b is in logical order
     const uint32_t tb = t0 + (tid & 63);
     b = buf_load4(hb.b, (tb < len ? tb : len - 1) * 4u);
 #pragma unroll
     for (int m = 0; m < C::QU; ++m) {
       const int u = tid + m * C::NT;
       const int row = u / (DK / 8), c8 = u % (DK / 8);
-      const uint32_t off = row_offset(p, t0 + row, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T);
+      const uint32_t off = row_offset(p, hb.T, t0 + row, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T);
       if (LOAD_Q) q[m] = E::load8(hb.q, off);
       k[m] = E::load8(hb.k, off);
     }
@@ -89,7 +89,7 @@ struct Staged {
     for (int m = 0; m < C::VU; ++m) {
       const int u = tid + m * C::NT;
       const int row = u / (DVS / 8), c8 = u % (DVS / 8);
-      v[m] = E::load8(hb.v, row_offset(p, t0 + row, (uint32_t)p.dv * (uint32_t)sizeof(T)) +
+      v[m] = E::load8(hb.v, row_offset(p, hb.T, t0 + row, (uint32_t)p.dv * (uint32_t)sizeof(T)) +
                                 (col0 + c8 * 8) * (uint32_t)sizeof(T));
     }
   }
@@ -142,14 +142,10 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
   const int bh = rest / nseg;
   const int col0 = slice * DVS;
   const int wcol = col0 + wave * C::CPW;
-  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
-  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
-
-  const uint32_t Tn = (uint32_t)p.T;
-  HeadBuffers hb;
-  hb.k = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
-  hb.v = make_rsrc(static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * (uint32_t)sizeof(T));
-  hb.b = make_rsrc(p.b + (long long)bh * p.Tl, (uint32_t)p.Tl * 4u);
+  const HeadSpan span = head_span(p, bh);
+  const int c_begin = (int)((long long)seg * span.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * span.nchunks / p.segments);
+  const HeadBuffers hb = head_buffers<T, DK>(p, span);
 
   StateAcc<T, DK, DVS> S;
 #pragma unroll
@@ -206,16 +202,10 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
   const int bh = rest / p.segments;
   const int col0 = slice * DVS;
   const int wcol = col0 + wave * C::CPW;
-  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
-  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
-
-  const uint32_t Tn = (uint32_t)p.T;
-  HeadBuffers hb;
-  hb.q = make_rsrc(static_cast<const T*>(p.q) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
-  hb.k = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
-  hb.v = make_rsrc(static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * (uint32_t)sizeof(T));
-  hb.b = make_rsrc(p.b + (long long)bh * p.Tl, (uint32_t)p.Tl * 4u);
-  hb.o = make_rsrc(p.o + (long long)bh * p.T * p.dv, Tn * p.dv * 4u);
+  const HeadSpan span = head_span(p, bh);
+  const int c_begin = (int)((long long)seg * span.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * span.nchunks / p.segments);
+  const HeadBuffers hb = head_buffers<T, DK>(p, span);
 
   // ---- initial state of this segment
   StateAcc<T, DK, DVS> S;
@@ -243,7 +233,7 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
         // dropped stores get distinct addresses: identical ones would be merged
         // into one, and the loop's wait counts assume all of them are issued
         const uint32_t off = none ? kDroppedOffset + 16u * (jb * C::NB + nb)
-                                  : row_offset(p, row0 + jb * 16 + r16, (uint32_t)p.dv * 4u) +
+                                  : row_offset(p, hb.T, row0 + jb * 16 + r16, (uint32_t)p.dv * 4u) +
                                         (wcol + nb * 16 + 4 * g) * 4u;
         buf_store16<kAuxStream>(hb.o, off, O[jb][nb]);
       }
@@ -466,6 +456,7 @@ struct ProbeFn {
 }  // namespace
 
 bool chunk_config_built(int dtype, int dk, int slice, bool diag) {
+  if (ws_kernels_supported(dtype, dk, slice)) return true;
   return dispatch(dtype, dk, slice, diag, ProbeFn{}) == hipSuccess;
 }
 

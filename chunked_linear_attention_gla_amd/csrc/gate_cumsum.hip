@@ -64,6 +64,52 @@ __global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restric
   if (valid) b[bh * Tl + t] = s;
 }
 
+// Packed sequences: wavefront `chunk` of unit bh = n * H + h covers tokens
+// [cu[n] + 64 c, ...) of head h, so chunks restart at every sequence start.  Offsets
+// are clamped into [0, T] and lengths to max_chunks chunks (inconsistent offsets give
+// wrong values, never an access outside x or b).
+template <int GATE>
+__global__ void __launch_bounds__(256) gate_cumsum_varlen_kernel(const float* __restrict__ x,
+                                                                 float* __restrict__ b,
+                                                                 const long long* __restrict__ cu,
+                                                                 int H, long long T, long long max_chunks,
+                                                                 long long total_chunks) {
+  const int lane = threadIdx.x & 63;
+  const long long chunk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (chunk >= total_chunks) return;  // uniform across the wavefront
+  const long long bh = chunk / max_chunks;
+  const long long c = chunk - bh * max_chunks;
+  const long long n = bh / H, h = bh - n * H;
+  long long a = cu[n], e = cu[n + 1];
+  a = a < 0 ? 0 : (a > T ? T : a);
+  e = e < a ? a : (e > T ? T : e);
+  if (e - a > max_chunks * kChunk) e = a + max_chunks * kChunk;
+  const long long t = c * kChunk + lane;
+  if (c * kChunk >= e - a) return;  // uniform: the sequence has fewer chunks
+  const bool valid = t < e - a;
+  const long long row = h * T + a + t;
+  float g = 0.0f;
+  if (valid) g = (GATE == kGateBoundedSigmoid) ? gate_bounded_sigmoid(x[row]) : gate_neg_softplus(x[row]);
+  const float s = wave_inclusive_scan(g, lane);
+  if (valid) b[row] = s;
+}
+
+hipError_t launch_gate_cumsum_varlen(const float* x, float* b, const long long* cu_seqlens, int N, int H,
+                                     long long T, long long max_chunks, int gate, hipStream_t stream) {
+  const long long total = (long long)N * H * max_chunks;
+  if (total == 0) return hipSuccess;
+  const long long blocks = (total + 3) / 4;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (gate == kGateBoundedSigmoid)
+    hipLaunchKernelGGL((gate_cumsum_varlen_kernel<kGateBoundedSigmoid>), grid, block, 0, stream, x, b, cu_seqlens,
+                       H, T, max_chunks, total);
+  else
+    hipLaunchKernelGGL((gate_cumsum_varlen_kernel<kGateNegSoftplus>), grid, block, 0, stream, x, b, cu_seqlens, H,
+                       T, max_chunks, total);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long T, int gate,
                               bool reversed_shift, hipStream_t stream) {
   const long long cph = (T + kChunk - 1) / kChunk;

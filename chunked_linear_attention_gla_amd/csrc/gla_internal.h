@@ -35,18 +35,23 @@ struct ChunkParams {
   void* state_out;        // optional: the state before every chunk, in the operand dtype,
                           //    in MFMA-fragment order (see store_chunk_state); a reversed
                           //    pass stores logical chunk c at chunk nchunks-1-c
+  const long long* cu_seqlens;  // packed sequences: N+1 token offsets (device memory) into the
+                          //    rows of every head; nullptr for the dense [BH][T] layout.  With
+                          //    it, q, k, v, o, b are [H][T][.] (T = total tokens), the work
+                          //    unit bh = n * H + h is sequence n of head h, and nchunks is
+                          //    the largest sequence's chunk count
+  int H;                  // heads (packed sequences only)
 };
 
-// Byte offset of logical token t's row in a per-head tensor with rows of
-// row_bytes bytes.  Rows outside the head (t >= T, or t < 0 once reversed) get an
+// Byte offset of logical token t's row in a per-unit tensor of T rows with rows of
+// row_bytes bytes.  Rows outside the unit (t >= T, or t < 0 once reversed) get an
 // offset beyond every descriptor's range that cannot wrap round to a valid one
 // when an instruction offset is added: loads there return zeros, stores are
 // dropped.
 // (Accepted sizes keep T * row_bytes below 2^32 - 2^16, so 32-bit arithmetic is exact.)
-__host__ __device__ inline unsigned row_offset(const ChunkParams& p, unsigned t, unsigned row_bytes) {
-  const int T = (int)p.T;
-  const int r = p.reverse ? T - 1 + p.pad - (int)t : (int)t;
-  return (r >= 0 && r < T) ? (unsigned)r * row_bytes : 0xFFFFF000u;
+__host__ __device__ inline unsigned row_offset(const ChunkParams& p, unsigned T, unsigned t, unsigned row_bytes) {
+  const int r = p.reverse ? (int)T - 1 + p.pad - (int)t : (int)t;
+  return (r >= 0 && r < (int)T) ? (unsigned)r * row_bytes : 0xFFFFF000u;
 }
 
 // b = chunk-local cumsum of g(x), [BH][T].  reversed_shift: the gate of the time-reversed
@@ -56,6 +61,11 @@ __host__ __device__ inline unsigned row_offset(const ChunkParams& p, unsigned t,
 // that line up with the forward chunks.
 hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long T, int gate,
                               bool reversed_shift, hipStream_t stream);
+// Packed sequences: x and b are [H][T] (T = total tokens), sequence n of every head
+// covers rows [cu_seqlens[n], cu_seqlens[n+1]) and restarts its chunks there; at most
+// max_chunks chunks per sequence.
+hipError_t launch_gate_cumsum_varlen(const float* x, float* b, const long long* cu_seqlens, int N, int H,
+                                     long long T, long long max_chunks, int gate, hipStream_t stream);
 
 // dtype: 0 = bf16, 1 = fp32.  slice = dv / nslices.  diag: element-wise diagonal tiles.
 bool chunk_config_built(int dtype, int dk, int slice, bool diag);
@@ -93,6 +103,13 @@ struct PcParams {
 bool pc_config_built(int dtype, int dk, int slice);
 hipError_t launch_pc_segment_states(const PcParams& p, int dtype, hipStream_t stream);
 hipError_t launch_pc_chunk_output(const PcParams& p, int dtype, hipStream_t stream);
+
+// One recurrent step per head (decode.hip): S <- diag(a) S + k v^T in place, o = S^T q.
+// q, k [BH][dk], v [BH][dv] in the operand dtype; x [BH] or, per_channel, [BH][dk];
+// S [BH][dk][dv] and o [BH][dv] fp32.  dk, dv <= 128, dv a multiple of 4.
+hipError_t launch_decode_step(const void* q, const void* k, const void* v, const float* x, float* S, float* o,
+                              long long BH, int dk, int dv, int dtype, int gate, bool per_channel,
+                              hipStream_t stream);
 
 // Backward-pass kernels (bwd_kernels.hip).
 //   dx from the pairs that span each token (see bwd_kernels.hip); Sfw and Sbw are the

@@ -91,14 +91,14 @@ struct WsStaged {
 
   // chunk starting at logical token t0 (rows in logical order; see row_offset)
   __device__ __forceinline__ void load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0, int col0, int st) {
-    const uint32_t len = (uint32_t)p.Tl;  // b is in logical order
+    const uint32_t len = hb.Tl;  // b is in logical order
     const uint32_t tb = t0 + (st & 63);
     b = buf_load4(hb.b, (tb < len ? tb : len - 1) * 4u);
 #pragma unroll
     for (int m = 0; m < QU; ++m) {
       const int u = st + m * 256;
       const int row = u / (DK / 8), c8 = u % (DK / 8);
-      const uint32_t off = row_offset(p, t0 + row, DK * 2u) + c8 * 16u;
+      const uint32_t off = row_offset(p, hb.T, t0 + row, DK * 2u) + c8 * 16u;
       if (LOAD_Q) q[m] = buf_load16(hb.q, off);
       k[m] = buf_load16(hb.k, off);
     }
@@ -106,7 +106,7 @@ struct WsStaged {
     for (int m = 0; m < VU; ++m) {
       const int u = st + m * 256;
       const int row = u / (DVS / 8), c8 = u % (DVS / 8);
-      v[m] = buf_load16(hb.v, row_offset(p, t0 + row, (uint32_t)p.dv * 2u) + (col0 + c8 * 8) * 2u);
+      v[m] = buf_load16(hb.v, row_offset(p, hb.T, t0 + row, (uint32_t)p.dv * 2u) + (col0 + c8 * 8) * 2u);
     }
   }
 };
@@ -217,16 +217,10 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
   const int sw = compute ? 0 : wave - W::NCW;    // staging-wave index
   const int st = compute ? 0 : tid - 64 * W::NCW;
   const int wcol = col0 + cw * C::CPW;
-  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
-  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
-
-  const uint32_t Tn = (uint32_t)p.T;
-  HeadBuffers hb;
-  hb.q = make_rsrc(static_cast<const bf16*>(p.q) + (long long)bh * p.T * DK, Tn * DK * 2u);
-  hb.k = make_rsrc(static_cast<const bf16*>(p.k) + (long long)bh * p.T * DK, Tn * DK * 2u);
-  hb.v = make_rsrc(static_cast<const bf16*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * 2u);
-  hb.b = make_rsrc(p.b + (long long)bh * p.Tl, (uint32_t)p.Tl * 4u);
-  hb.o = make_rsrc(p.o + (long long)bh * p.T * p.dv, Tn * p.dv * 4u);
+  const HeadSpan span = head_span(p, bh);
+  const int c_begin = (int)((long long)seg * span.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * span.nchunks / p.segments);
+  const HeadBuffers hb = head_buffers<bf16, DK>(p, span);
 
   // The two key tiles that a 32-wide K-step of A.V reads above the diagonal,
   // (jb 0, ib 1) and (jb 2, ib 3), are never written by the loop: zero them once.
@@ -306,7 +300,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb)
-          buf_store16<0>(hb.o, row_offset(p, t0 + jb * 16 + r16, (uint32_t)p.dv * 4u) + (wcol + nb * 16 + 4 * g) * 4u,
+          buf_store16<0>(hb.o, row_offset(p, hb.T, t0 + jb * 16 + r16, (uint32_t)p.dv * 4u) + (wcol + nb * 16 + 4 * g) * 4u,
                          O[jb][nb]);
       __syncthreads();
     }
@@ -430,8 +424,9 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
   const int sw = compute ? 0 : wave - W::NCW;
   const int st = compute ? 0 : tid - 64 * W::NCW;
   const int wcol = col0 + cw * C::CPW;
-  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
-  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
+  const HeadSpan span = head_span(p, bh);
+  const int c_begin = (int)((long long)seg * span.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * span.nchunks / p.segments);
 
   if (compute) {
     StateAcc<bf16, DK, DVS> S;
@@ -453,11 +448,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
     store_state<bf16, DK, DVS>(S, p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv, p.dv, wcol, g, r16);
     if (slice == 0 && tid == 0) p.seg_decay[(long long)bh * p.segments + seg] = gsum;
   } else {
-    const uint32_t Tn = (uint32_t)p.T;
-    HeadBuffers hb;
-    hb.k = make_rsrc(static_cast<const bf16*>(p.k) + (long long)bh * p.T * DK, Tn * DK * 2u);
-    hb.v = make_rsrc(static_cast<const bf16*>(p.v) + (long long)bh * p.T * p.dv, Tn * p.dv * 2u);
-    hb.b = make_rsrc(p.b + (long long)bh * p.Tl, (uint32_t)p.Tl * 4u);
+    const HeadBuffers hb = head_buffers<bf16, DK>(p, span);
     const auto stage = [&](const WsStaged<DK, DVS, false>& stg, int ns) {
       const ChunkDecay cd(stg.b);
       float brow[W::QU];

@@ -69,6 +69,10 @@ WORKLOADS: Dict[str, Workload] = {
                           "bounded", 1003, "long sequence; chained continuation of 65536 tokens"),
     "bf16_1m": Workload("bf16_1m", 1, 8, 1048576, 128, 128, "bf16", 0.0, 1.0, 0.0,
                         "bounded", 1004, "million-token head group"),
+    "bf16_decode": Workload("bf16_decode", 64, 32, 1, 128, 128, "bf16", 0.0, 1.0, 0.0, "bounded", 1006,
+                            "serving step: 64 sequences x 32 heads, one token each, fp32 state carried"),
+    "bf16_varlen_256k": Workload("bf16_varlen_256k", 1, 16, 262144, 128, 128, "bf16", 0.0, 1.0, 0.0, "bounded",
+                                 1007, "64 packed sequences, log-uniform length mix, 256K tokens in total"),
     "bf16_64k_pc": Workload("bf16_64k_pc", 1, 32, 65536, 128, 128, "bf16", 4.0, 1.0, 0.0, "bounded", 1005,
                             "per-channel decay: x per (token, key channel), same shapes and regime",
                             per_channel=True),
@@ -122,6 +126,48 @@ def make_inputs(w: Workload, device="cpu", *, T: Optional[int] = None, H: Option
     if w.s0_std > 0:
         S0 = torch.randn(B, H, w.dk, w.dv, **f32).mul_(w.s0_std)
     return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), x=x.contiguous(), S0=S0)
+
+
+def varlen_lengths(n: int, total: int, seed: int, min_len: int = 1) -> list:
+    """n sequence lengths summing to `total`, log-uniformly mixed (a packed batch of
+    short and long documents), each at least min_len."""
+    g = torch.Generator().manual_seed(seed)
+    w = torch.exp(torch.rand(n, generator=g, dtype=torch.float64) * math.log(64.0))
+    raw = (w / w.sum() * (total - n * min_len)).floor().long() + min_len
+    raw[0] += total - int(raw.sum())
+    return [int(r) for r in raw]
+
+
+def make_varlen_inputs(w: Workload, lengths, device="cpu", seed: Optional[int] = None):
+    """Packed sequences of the given lengths with workload w's recipe and head count:
+    q, k [H, T, dk], v [H, T, dv], x [H, T] (every head holds the sequences back to back),
+    cu_seqlens int64 [N + 1], S0 [N, H, dk, dv] or None; T = sum(lengths)."""
+    T = int(sum(lengths))
+    inp = make_inputs(w, device, B=1, T=T, seed=seed)
+    inp = {k_: (None if v_ is None else v_[0]) for k_, v_ in inp.items() if k_ != "S0"}
+    dev = torch.device(device)
+    cu = torch.tensor([0] + list(lengths), dtype=torch.int64).cumsum(0).to(dev)
+    S0 = None
+    if w.s0_std > 0:
+        gen = torch.Generator(device=dev).manual_seed((w.seed if seed is None else seed) + 77)
+        S0 = torch.randn(len(lengths), w.H, w.dk, w.dv, device=dev, dtype=torch.float32,
+                         generator=gen).mul_(w.s0_std)
+    inp["cu_seqlens"] = cu
+    inp["S0"] = S0
+    return inp
+
+
+def make_decode_inputs(w: Workload, device="cpu", seed: Optional[int] = None, B: Optional[int] = None):
+    """One token per (batch, head) with workload w's recipe, plus a state S ~ N(0, 1)
+    per head: q, k [B, H, dk], v [B, H, dv], x [B, H] (or [B, H, dk] per channel),
+    S [B, H, dk, dv] fp32."""
+    B = w.B if B is None else B
+    inp = make_inputs(w, device, B=B, T=1, seed=seed)
+    out = {k_: inp[k_][:, :, 0].contiguous() for k_ in ("q", "k", "v", "x")}
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev).manual_seed((w.seed if seed is None else seed) + 99)
+    out["S"] = torch.randn(B, w.H, w.dk, w.dv, device=dev, dtype=torch.float32, generator=gen)
+    return out
 
 
 def to_numpy_bits(t: torch.Tensor):

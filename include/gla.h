@@ -218,6 +218,43 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
                            void* workspace, size_t* workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode and packed sequences. */
+
+/* One recurrent step for every head, for generating one token at a time with
+ * the state carried between calls [LCT §3.1, §3.2]:
+ *     S <- diag(a) S + k v^T   (in place),   o = S^T q,   a = e^{g(x)}.
+ *   q, k [B][H][dk], v [B][H][dv] in `dtype`; x [B][H] fp32, or [B][H][dk] when
+ *   per_channel = 1 (one decay per key channel, as gla_chunk_fwd_pc);
+ *   S [B][H][dk][dv] fp32, read and overwritten (16-byte aligned); o [B][H][dv]
+ *   fp32 (16-byte aligned).  dk, dv in {64, 128}.  S and o must not overlap each
+ *   other or any input.  No workspace; errors as gla_chunk_fwd.  A step over S
+ *   equals gla_chunk_fwd over one token with S0 = S (up to rounding). */
+gla_status_t gla_decode_step(const void* q, const void* k, const void* v, const float* x,
+                             float* S, float* o, int B, int H, int dk, int dv,
+                             gla_dtype_t dtype, gla_gate_t gate, int per_channel, void* stream);
+
+/* Forward over N packed sequences of different lengths (the scalar-decay
+ * method of gla_chunk_fwd, chunks restarting at every sequence start).
+ *   q, k [H][T][dk], v [H][T][dv], x [H][T], o [H][T][dv]: every head holds the
+ *   N sequences back to back, sequence n in rows [cu_seqlens[n], cu_seqlens[n+1]);
+ *   T = total rows.
+ *   cu_seqlens: N+1 nondecreasing int64 offsets in device memory, cu_seqlens[0] >= 0,
+ *   cu_seqlens[N] <= T, no sequence longer than max_seqlen (host value, <= T).  They
+ *   are read on the device only: offsets outside [0, T] are clamped and longer
+ *   sequences cut to max_seqlen, which yields wrong values but never an access
+ *   outside the tensors.  Rows covered by no sequence are not written in o.
+ *   S0, S_T [N][H][dk][dv] fp32 (S0 may be NULL), one state per sequence and head.
+ * Plan: the device default for N heads groups of max_seqlen tokens; every sequence
+ * gets the same number of segments.  workspace == NULL returns the size.  Errors
+ * as gla_chunk_fwd. */
+gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* x,
+                                  const float* S0, float* o, float* S_T,
+                                  const long long* cu_seqlens, int N, int H, long long T,
+                                  long long max_seqlen, int dk, int dv,
+                                  gla_dtype_t dtype, gla_gate_t gate, gla_path_t path,
+                                  void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Per-channel decay.  The same chunked method with one decay per key channel
  * (the per-position decay of [LCT §3.1] read as a vector over the key
  * dimension):

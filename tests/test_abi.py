@@ -207,3 +207,64 @@ def test_backward_workspace_query_for_an_empty_sequence(lib):
     assert rc == NULL
     rc, _ = bwd(lib, B=2, H=3, T=0, dk=64, dv=128, ws=0x10000000, wsz=need - 1)
     assert rc == WORKSPACE
+
+
+def test_plan_check_accepts_every_built_bf16_slice(lib):
+    # full-width slices of dk = 64 heads exist only as wave-specialised kernels; the
+    # check must accept them like the rest
+    for dk in (64, 128):
+        for split in (1, 2, 4):
+            assert lib.gla_plan_check(4, 16, 1024, dk, 128, BF16, UNIFIED, P(1, split)) == OK, (dk, split)
+            assert lib.gla_plan_check(4, 16, 1024, dk, 128, BF16, DIAG, P(1, split)) == OK, (dk, split)
+
+
+def test_per_channel_plan_and_validation(lib):
+    assert lib.gla_plan_check_pc(1, 2, 256, 64, 128, BF16, P(1, 1)) == OK
+    assert lib.gla_plan_check_pc(1, 2, 256, 128, 128, BF16, P(4, 2)) == OK
+    assert lib.gla_plan_check_pc(1, 2, 256, 128, 128, BF16, P(1, 4)) == PLAN
+    assert lib.gla_plan_check_pc(1, 2, 256, 128, 64, F32, P(1, 1)) == UNSUP
+    assert lib.gla_plan_check_pc(1, 2, 256, 64, 64, F32, P(1, 1)) == OK
+    assert lib.gla_plan_check_pc(1, 2, 256, 64, 64, F32, P(5, 1)) == PLAN  # 4 chunks
+    n = ctypes.c_size_t(0)
+    fwd_pc = lambda **kw: lib.gla_chunk_fwd_pc(
+        kw.get("q", 0x1000), 0x2000, 0x3000, 0x4000, None, 0x5000, 0x6000, 1, 2, kw.get("T", 256), 64, 64, BF16,
+        kw.get("gate", BOUNDED), P(*kw.get("plan", (2, 1))), kw.get("ws", None), kw.get("nb", ctypes.byref(n)), None)
+    assert fwd_pc(nb=None) == NULL
+    assert fwd_pc(gate=4) == ARG
+    assert fwd_pc(T=-2) == SHAPE
+    assert fwd_pc() == OK and n.value >= 256  # size query with an explicit plan: no device call
+    need = n.value
+    n.value = need - 1
+    assert fwd_pc(ws=0x10000000) == WORKSPACE
+    n.value = need
+    assert fwd_pc(ws=0x10000100, q=None) == NULL
+
+
+def test_decode_step_validation(lib):
+    def dec(**kw):
+        return lib.gla_decode_step(kw.get("q", 0x1000), 0x2000, 0x3000, 0x4000, kw.get("S", 0x100000),
+                                   kw.get("o", 0x200000), 2, 3, kw.get("dk", 64), 64, kw.get("dtype", BF16),
+                                   kw.get("gate", BOUNDED), kw.get("pc", 0), None)
+    assert dec(q=None) == NULL
+    assert dec(dk=96) == SHAPE
+    assert dec(dtype=3) == DTYPE
+    assert dec(gate=2) == ARG
+    assert dec(pc=2) == ARG
+    assert dec(S=0x100004) == ALIGN
+    assert dec(o=0x100000 + 4096) == ALIAS  # o inside S
+
+
+def test_varlen_validation_before_any_device_call(lib):
+    n = ctypes.c_size_t(0)
+
+    def var(**kw):
+        return lib.gla_chunk_fwd_varlen(0x1000, 0x2000, 0x3000, 0x4000, None, 0x5000, 0x6000, 0x7000,
+                                        kw.get("N", 3), 2, kw.get("T", 500), kw.get("maxlen", 200), 64, 64,
+                                        kw.get("dtype", BF16), kw.get("gate", BOUNDED), UNIFIED, None,
+                                        kw.get("nb", ctypes.byref(n)), None)
+    assert var(nb=None) == NULL
+    assert var(N=0) == SHAPE
+    assert var(maxlen=501) == SHAPE
+    assert var(maxlen=-1) == SHAPE
+    assert var(dtype=5) == DTYPE
+    assert var(gate=3) == ARG

@@ -136,6 +136,13 @@ def test_many_heads_batch():
     check(inp, w)
 
 
+def test_default_plan_many_heads_dk64_dv128():
+    """Enough heads that the default plan keeps full 128-column slices of dk = 64 heads
+    (built only as wave-specialised kernels)."""
+    w, inp = small(130, B=4, H=16, dk=64, dv=128)
+    check(inp, w)
+
+
 def test_chaining_matches_single_call():
     w, inp = small(64 * 20, H=2, x_mean=-5.0)
     o, ST = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"])
