@@ -87,6 +87,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--backward-only", action="store_true", help="time only the backward pass (profiling)")
     ap.add_argument("--no-per-channel", action="store_true", help="skip the per-channel-decay measurement")
+    ap.add_argument("--no-serving", action="store_true", help="skip the decode and packed-sequence measurements")
+    ap.add_argument("--serving-only", action="store_true", help="time only decode and packed sequences")
     ap.add_argument("--per-channel-only", action="store_true", help="time only the per-channel forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration) and exit")
@@ -339,6 +341,82 @@ def per_channel_result(gla, gin, torch, steps, warmup, cpu_seconds):
     return res
 
 
+def decode_result(gla, gin, torch, steps, warmup, cpu_seconds):
+    """One decode step for every (sequence, head) of a serving batch (gla_decode_step),
+    the state updated in place."""
+    import numpy as np
+    w = gin.WORKLOADS["bf16_decode"]
+    dev = torch.device("cuda:0")
+    inp = gin.make_decode_inputs(w, dev)
+    o = torch.empty(w.B, w.H, w.dv, device=dev)
+    fn = lambda: gla.decode_step(inp["q"], inp["k"], inp["v"], inp["x"], inp["S"], gate=w.gate, o=o)
+    ms_host, ms_ev = time_calls(torch, fn, steps * 10, warmup)
+    es = inp["q"].element_size()
+    bh = w.B * w.H
+    per_head = 2 * w.dk * w.dv * 4 + (2 * w.dk + w.dv) * es + 4 + 4 * w.dv
+    achieved = bh * per_head / (ms_ev / 1e3) / 1e9
+    res = {"what": "gla_decode_step: one token per (sequence, head), fp32 state read and written in place",
+           "workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "steps": steps * 10,
+           "ms_per_step": round(ms_host, 5), "ms_per_step_events": round(ms_ev, 5),
+           "tokens_per_s": round(w.B / (ms_ev / 1e3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": bh * per_head}}
+    if cpu_seconds > 0:
+        import oracle
+        flat = lambda t: t.reshape(bh, 1, *t.shape[2:])
+        args = [gin.to_numpy_bits(flat(inp[n])) for n in ("q", "k", "v")] + \
+               [gin.to_numpy_bits(inp["x"].reshape(bh, 1))]
+        S0 = inp["S"].reshape(bh, w.dk, w.dv).cpu().numpy().astype(np.float64)
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < cpu_seconds:
+            oracle.forward(*args, S0, gate=w.gate)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        res["cpu_baseline"] = {"value": w.B / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+                               "kind": "oracle", "sample": f"the whole step ({bh} heads), {reps} repetitions"}
+    return res
+
+
+def varlen_result(gla, gin, torch, steps, warmup, cpu_seconds):
+    """Forward over a packed batch of sequences of mixed lengths (gla_chunk_fwd_varlen)."""
+    import numpy as np
+    w = gin.WORKLOADS["bf16_varlen_256k"]
+    dev = torch.device("cuda:0")
+    lengths = gin.varlen_lengths(64, w.T, w.seed)
+    inp = gin.make_varlen_inputs(w, lengths, dev)
+    N, H, T = len(lengths), w.H, w.T
+    o = torch.empty(H, T, w.dv, device=dev)
+    ST = torch.empty(N, H, w.dk, w.dv, device=dev)
+    ws = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
+    fn = lambda: gla.chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["x"], inp["cu_seqlens"], max(lengths),
+                                      inp["S0"], gate=w.gate, o=o, S_T=ST, workspace=ws)
+    ms_host, ms_ev = time_calls(torch, fn, steps, warmup)
+    es = inp["q"].element_size()
+    nbytes = H * T * algorithmic_bytes_per_token_head(w.dk, w.dv, es) + N * H * w.dk * w.dv * 4
+    achieved = nbytes / (ms_ev / 1e3) / 1e9
+    res = {"what": "gla_chunk_fwd_varlen: packed sequences, all kernels of the call", "workload": w.name,
+           "sequences": N, "min_len": min(lengths), "max_len": max(lengths), "H": H, "total_tokens": T,
+           "steps": steps, "ms_per_call": round(ms_host, 4), "ms_per_call_events": round(ms_ev, 4),
+           "tokens_per_s": round(T / (ms_ev / 1e3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes}}
+    if cpu_seconds > 0:
+        import oracle
+        cu = [0] + list(np.cumsum(lengths))
+        done, t0 = 0, time.perf_counter()
+        for n in range(N):
+            a, b = int(cu[n]), int(cu[n + 1])
+            oracle.forward(*(gin.to_numpy_bits(inp[t][:, a:b]) for t in ("q", "k", "v", "x")), None, gate=w.gate)
+            done += b - a
+            if time.perf_counter() - t0 > cpu_seconds:
+                break
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": done / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+                               "kind": "oracle", "sample": f"the first {n + 1} of {N} sequences ({done} tokens, "
+                                                           f"all {H} heads), one oracle call per sequence"}
+    return res
+
+
 def backward_result(gla, gin, torch, w, path, steps, warmup):
     t = BackwardTimer(gla, gin, torch, w, path)
     ms_host, ms_ev = t.run(steps, warmup)
@@ -379,6 +457,10 @@ def main():
     path = args.path or "unified"
     torch.cuda.set_device(torch.device("cuda:0"))
     plan = gla.Plan(*(int(s) for s in args.plan.split(","))) if args.plan else None
+    if args.serving_only:
+        print(json.dumps({"decode": decode_result(gla, gin, torch, args.steps, args.warmup, 0.0),
+                          "varlen": varlen_result(gla, gin, torch, args.steps, args.warmup, 0.0)}), flush=True)
+        return
     if args.per_channel_only:
         print(json.dumps({"per_channel": per_channel_result(gla, gin, torch, args.steps, args.warmup, 0.0)}),
               flush=True)
@@ -460,6 +542,10 @@ def main():
     if not args.no_per_channel and not args.plan and w.name == gin.HEADLINE:
         result["per_channel"] = per_channel_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5),
                                                    0.0 if args.no_cpu_baseline else args.cpu_seconds / 2)
+    if not args.no_serving and not args.plan and w.name == gin.HEADLINE:
+        cs = 0.0 if args.no_cpu_baseline else args.cpu_seconds / 4
+        result["decode"] = decode_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5), cs)
+        result["varlen"] = varlen_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5), cs)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
