@@ -23,6 +23,8 @@ pass of the recurrence:
   exponent differences).  Used to pin :func:`forward` on tiny inputs.
 * :func:`forward_pc` / :func:`closed_form_pc` -- the same two formulations for a
   decay with one value per key channel (the state's row d decays by a_t[d]).
+* :func:`forward_delta` / :func:`closed_form_delta` -- the gated delta rule, token by
+  token and as one triangular solve over the sequence.
 * :func:`backward` -- the reverse-mode chain rule of the same recurrence, one token
   at a time, in C (fp64): dq, dk, dv, dx and dS0 from dO and dS_T.
 * :func:`gate` / :func:`chunk_local_cumsum` -- the log-decay of [LCT §3.2] and the
@@ -91,6 +93,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         ctypes.c_int, ctypes.c_int]
     lib.gla_oracle_forward_pc.restype = ctypes.c_int
     lib.gla_oracle_forward_pc.argtypes = lib.gla_oracle_forward.argtypes
+    lib.gla_oracle_forward_delta.restype = ctypes.c_int
+    lib.gla_oracle_forward_delta.argtypes = [
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+        ctypes.c_longlong, ctypes.c_longlong, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_int, ctypes.c_int]
     lib.gla_oracle_backward.restype = ctypes.c_int
     lib.gla_oracle_backward.argtypes = [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -189,6 +197,43 @@ def forward_pc(q: np.ndarray, k: np.ndarray, v: np.ndarray, x: np.ndarray,
         BH, T, dk, dv, gate_id(gate), col_block, nthreads)
     if rc != 0:
         raise ValueError(f"gla_oracle_forward_pc rejected its arguments (rc={rc})")
+    return o, ST
+
+
+def forward_delta(q: np.ndarray, k: np.ndarray, v: np.ndarray, x: np.ndarray, beta: np.ndarray,
+                  S0: Optional[np.ndarray] = None, gate="bounded", nthreads: int = 0,
+                  col_block: int = 16, lib_path: str = LIB_PATH):
+    """Gated delta rule, one token at a time (fp64, in C):
+
+        S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t,  a_t = exp(g(x_t))
+
+    q, k [..., T, dk], v [..., T, dv] as for :func:`forward`; x, beta [..., T] fp32.
+    Returns (o [..., T, dv], S_T [..., dk, dv]) in float64.
+    """
+    kind = _qkv_kind(q)
+    if _qkv_kind(k) != kind or _qkv_kind(v) != kind:
+        raise TypeError("q, k, v must share a storage kind")
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2], q.shape[-1]
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:-1] != q.shape[:-1] or x.shape != lead + (T,) or beta.shape != x.shape:
+        raise ValueError("shape mismatch")
+    BH = int(np.prod(lead)) if lead else 1
+    q, k, v = (np.ascontiguousarray(a) for a in (q, k, v))
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    beta = np.ascontiguousarray(beta, dtype=np.float32)
+    if S0 is not None:
+        S0 = np.ascontiguousarray(S0, dtype=np.float64)
+        if S0.shape != lead + (dk, dv):
+            raise ValueError("S0 shape mismatch")
+    o = np.empty(lead + (T, dv))
+    ST = np.empty(lead + (dk, dv))
+    rc = load(lib_path).gla_oracle_forward_delta(
+        q.ctypes.data, k.ctypes.data, v.ctypes.data, kind, x.ctypes.data, beta.ctypes.data,
+        None if S0 is None else S0.ctypes.data, o.ctypes.data, ST.ctypes.data,
+        BH, T, dk, dv, gate_id(gate), col_block, nthreads)
+    if rc != 0:
+        raise ValueError(f"gla_oracle_forward_delta rejected its arguments (rc={rc})")
     return o, ST
 
 
@@ -341,6 +386,45 @@ def closed_form(q, k, v, x, S0=None, gate="bounded") -> Tuple[np.ndarray, np.nda
 
 
 gate_fn = gate
+
+
+def closed_form_delta(q, k, v, x, beta, S0=None, gate="bounded") -> Tuple[np.ndarray, np.ndarray]:
+    """The gated delta rule over a whole (tiny) sequence as one triangular solve, fp64.
+
+    Writing S_t = a_t S_{t-1} + k_t u_t^T with the effective write
+    u_t = beta_t (v_t - a_t S_{t-1}^T k_t), every u_t is linear in the earlier ones:
+        (I + diag(beta) L) U = diag(beta) (V - diag(D) K S0),
+        L[t, s] = W[t, s] (k_t . k_s) for s < t,
+    with W, D the explicit decay products of :func:`decay_weights`; then
+        o_t = D_t S0^T q_t + sum_{s <= t} W[t, s] (q_t . k_s) u_s,
+        S_T = D_{T-1} S0 + sum_s W[T-1, s] k_s u_s^T.
+    Solved with numpy.linalg.solve; no token loop over the state.
+    """
+    q = _widen(np.asarray(q))
+    k = _widen(np.asarray(k))
+    v = _widen(np.asarray(v))
+    x = np.asarray(x, dtype=np.float64)
+    beta = np.asarray(beta, dtype=np.float64)
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    qf, kf, vf = q.reshape(BH, T, dk), k.reshape(BH, T, dk), v.reshape(BH, T, dv)
+    xf, bf = x.reshape(BH, T), beta.reshape(BH, T)
+    S0f = np.zeros((BH, dk, dv)) if S0 is None else np.asarray(S0, dtype=np.float64).reshape(BH, dk, dv)
+    o = np.zeros((BH, T, dv))
+    ST = np.zeros((BH, dk, dv))
+    for h in range(BH):
+        if T == 0:
+            ST[h] = S0f[h]
+            continue
+        W, D = decay_weights(np.exp(gate_fn(xf[h], gate)))
+        L = np.tril(W * (kf[h] @ kf[h].T), -1)
+        rhs = bf[h][:, None] * (vf[h] - D[:, None] * (kf[h] @ S0f[h]))
+        U = np.linalg.solve(np.eye(T) + bf[h][:, None] * L, rhs)
+        o[h] = D[:, None] * (qf[h] @ S0f[h]) + (W * (qf[h] @ kf[h].T)) @ U
+        ST[h] = D[T - 1] * S0f[h] + kf[h].T @ (W[T - 1][:, None] * U)
+    return o.reshape(lead + (T, dv)), ST.reshape(lead + (dk, dv))
 
 
 def closed_form_pc(q, k, v, x, S0=None, gate="bounded") -> Tuple[np.ndarray, np.ndarray]:

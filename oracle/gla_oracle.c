@@ -280,6 +280,93 @@ int gla_oracle_forward_pc(const void* q, const void* k, const void* v, int qkv_i
   return 0;
 }
 
+/* Gated delta rule.  [LCT §3.1] and [§3.3] name Delta-Net-style structures as the
+ * other family whose chunked form has the same diagonal-tile problem; the pages do
+ * not write their recurrence.  The plainest reading, the gated delta rule with the
+ * same decay gate, is
+ *
+ *     S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t
+ *
+ * with a_t = exp(g(x_t)) one scalar per token and beta_t in [0, 1] a given per-token
+ * write strength (fp32 [BH][T]).  One token at a time, in the order written: the
+ * projection k_t^T S_{t-1}, the decayed erase-and-write, then the read-out. */
+int gla_oracle_forward_delta(const void* q, const void* k, const void* v, int qkv_is_bf16,
+                             const float* x, const float* beta, const double* S0, double* o, double* S_T,
+                             long long BH, long long T, int dk, int dv, int gate, int col_block,
+                             int nthreads) {
+  if (!q || !k || !v || !x || !beta || !o || !S_T) return 1;
+  if (BH < 0 || T < 0 || dk <= 0 || dv <= 0) return 1;
+  if (gate != ORACLE_GATE_BOUNDED_SIGMOID && gate != ORACLE_GATE_NEG_SOFTPLUS) return 1;
+  if (col_block <= 0 || col_block > dv) col_block = dv;
+  const long long ncb = (dv + col_block - 1) / col_block;
+  const long long tasks = BH * ncb;
+#ifdef _OPENMP
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+  (void)nthreads;
+#endif
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long long task = 0; task < tasks; ++task) {
+    const long long bh = task / ncb;
+    const int n0 = (int)(task % ncb) * col_block;
+    const int nc = (n0 + col_block <= dv) ? col_block : dv - n0;
+    double* S = (double*)malloc(sizeof(double) * (size_t)dk * (size_t)nc);
+    double* kt = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* qt = (double*)malloc(sizeof(double) * (size_t)dk);
+    double* vt = (double*)malloc(sizeof(double) * (size_t)nc);
+    double* proj = (double*)malloc(sizeof(double) * (size_t)nc);
+
+    for (int d = 0; d < dk; ++d)
+      for (int n = 0; n < nc; ++n)
+        S[(size_t)d * nc + n] = S0 ? S0[((size_t)bh * dk + d) * dv + n0 + n] : 0.0;
+
+    for (long long t = 0; t < T; ++t) {
+      const size_t row = (size_t)bh * (size_t)T + (size_t)t;
+      const double a = exp(gla_oracle_gate((double)x[row], gate));
+      const double bt = (double)beta[row];
+      for (int d = 0; d < dk; ++d) {
+        kt[d] = widen(k, qkv_is_bf16, row * (size_t)dk + d);
+        qt[d] = widen(q, qkv_is_bf16, row * (size_t)dk + d);
+      }
+      for (int n = 0; n < nc; ++n) vt[n] = widen(v, qkv_is_bf16, row * (size_t)dv + n0 + n);
+      /* proj = S_{t-1}^T k_t  (what the state currently returns for key k_t) */
+      for (int n = 0; n < nc; ++n) {
+        double acc = 0.0;
+        for (int d = 0; d < dk; ++d) acc += S[(size_t)d * nc + n] * kt[d];
+        proj[n] = acc;
+      }
+      /* S_t = a (S - beta k proj^T) + beta k v^T */
+      for (int d = 0; d < dk; ++d)
+        for (int n = 0; n < nc; ++n) {
+#if GLA_ORACLE_MUTANT == 14
+          /* planted: the erase term is not decayed */
+          S[(size_t)d * nc + n] = a * S[(size_t)d * nc + n] - bt * kt[d] * proj[n] + bt * kt[d] * vt[n];
+#elif GLA_ORACLE_MUTANT == 15
+          /* planted: the write is not scaled by beta */
+          S[(size_t)d * nc + n] = a * (S[(size_t)d * nc + n] - bt * kt[d] * proj[n]) + kt[d] * vt[n];
+#else
+          S[(size_t)d * nc + n] = a * (S[(size_t)d * nc + n] - bt * kt[d] * proj[n]) + bt * kt[d] * vt[n];
+#endif
+        }
+      for (int n = 0; n < nc; ++n) {
+        double acc = 0.0;
+        for (int d = 0; d < dk; ++d) acc += S[(size_t)d * nc + n] * qt[d];
+        o[row * (size_t)dv + n0 + n] = acc;
+      }
+    }
+    for (int d = 0; d < dk; ++d)
+      for (int n = 0; n < nc; ++n)
+        S_T[((size_t)bh * dk + d) * dv + n0 + n] = S[(size_t)d * nc + n];
+    free(S);
+    free(kt);
+    free(qt);
+    free(vt);
+    free(proj);
+  }
+  return 0;
+}
+
 /* d g / d x of the gate: bounded -5 sigmoid(x) (1 - sigmoid(x)); negative
  * softplus -softplus(-x) has derivative sigmoid(-x). */
 static double gate_slope(double x, int gate) {
