@@ -71,6 +71,8 @@ _SIGS = {
     "gla_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "gla_chunk_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _ll, _i, _i, _i, _i, _i,
                                   _vp, _psz, _vp]),
+    "gla_chunk_fwd_delta": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i, _vp, _psz,
+                                 _vp]),
     "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
                            _i, _i, _i, _vp, _psz, _vp]),
 }
@@ -387,6 +389,40 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch
     have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     _check("gla_chunk_fwd_varlen", lib.gla_chunk_fwd_varlen(*args(_ptr(workspace)), ctypes.byref(have),
                                                             _stream(dev)))
+    return o, S_T
+
+
+def chunk_fwd_delta(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor, beta: torch.Tensor,
+                    S0: Optional[torch.Tensor] = None, gate="bounded", dv_split: int = 0,
+                    o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Gated delta rule forward: returns (o [B,H,T,dv] fp32, S_T [B,H,dk,dv] fp32) for
+    S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T, o_t = S_t^T q_t.
+
+    As :func:`chunk_fwd`, plus beta: fp32 [B, H, T] write strengths; dv_split: value-column
+    slices per head (0 = device default).
+    """
+    B, H, T, dk, dv = _check_qkv(q, k, v, x, S0)
+    dev = q.device
+    _need(tuple(beta.shape) == (B, H, T) and beta.dtype == torch.float32 and beta.is_cuda and beta.is_contiguous()
+          and beta.device == dev, "beta must be a contiguous fp32 [B, H, T] tensor on q's device")
+    if o is None:
+        o = torch.empty(B, H, T, dv, device=dev, dtype=torch.float32)
+    if S_T is None:
+        S_T = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
+    _need(tuple(o.shape) == (B, H, T, dv) and o.dtype == torch.float32 and o.is_contiguous() and o.device == dev,
+          "o must be fp32 [B, H, T, dv] on q's device")
+    _need(tuple(S_T.shape) == (B, H, dk, dv) and S_T.dtype == torch.float32 and S_T.is_contiguous()
+          and S_T.device == dev, "S_T must be fp32 [B, H, dk, dv] on q's device")
+    lib = load()
+    args = lambda ws: (_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk,
+                       dv, _dtype_code(q), _gate(gate), int(dv_split), ws)
+    need = ctypes.c_size_t(0)
+    _check("gla_chunk_fwd_delta", lib.gla_chunk_fwd_delta(*args(None), ctypes.byref(need), _stream(dev)))
+    if workspace is None or workspace.numel() * workspace.element_size() < need.value:
+        workspace = torch.empty(max(int(need.value), 256), dtype=torch.uint8, device=dev)
+    have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check("gla_chunk_fwd_delta", lib.gla_chunk_fwd_delta(*args(_ptr(workspace)), ctypes.byref(have), _stream(dev)))
     return o, S_T
 
 

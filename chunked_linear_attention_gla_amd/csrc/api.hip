@@ -545,6 +545,86 @@ gla_status_t gla_decode_step(const void* q, const void* k, const void* v, const 
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
+gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, const float* x, const float* beta,
+                                 const float* S0, float* o, float* S_T, int B, int H, long long T, int dk, int dv,
+                                 gla_dtype_t dtype, gla_gate_t gate, int dv_split, void* workspace,
+                                 size_t* workspace_bytes, void* stream) {
+  if (!workspace_bytes) return GLA_ERR_NULL;
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_gate(gate)) return GLA_ERR_ARG;
+  const long long BH = (long long)B * H;
+  const int dt = dtype == GLA_BF16 ? 0 : 1;
+  if (dv_split == 0) {
+    // one workgroup per (head, value slice) runs the chunks in order: narrow the
+    // slices (down to 32 columns) until the heads cover the compute units
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != GLA_OK) return st;
+    dv_split = 1;
+    while (BH * dv_split < cus && dv / (2 * dv_split) >= 32 && gla::delta_config_built(dt, dk, dv, dv / (2 * dv_split)))
+      dv_split *= 2;
+  }
+  if (dv_split < 1 || dv % dv_split) return GLA_ERR_PLAN;
+  if (!gla::delta_config_built(dt, dk, dv, dv / dv_split))
+    return (dtype == GLA_F32 && (dk != 64 || dv != 64)) ? GLA_ERR_UNSUPPORTED : GLA_ERR_PLAN;
+  const size_t es = elem_size(dtype);
+  const size_t b_bytes = align_up((size_t)BH * T * 4);
+  const size_t w_bytes = align_up((size_t)BH * T * dk * es);
+  const size_t u_bytes = align_up((size_t)BH * T * dv * es);
+  const size_t need = std::max(b_bytes + w_bytes + u_bytes, kAlign);
+  if (!workspace) {
+    *workspace_bytes = need;
+    return GLA_OK;
+  }
+  if (*workspace_bytes < need) return GLA_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return GLA_ERR_ALIGN;
+  if (!S_T) return GLA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !x || !beta || !o)) return GLA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(S_T, 16) ||
+      !aligned(S0, 16) || !aligned(x, 4) || !aligned(beta, 4))
+    return GLA_ERR_ALIGN;
+  const Range ins[] = {{q, (size_t)BH * T * dk * es}, {k, (size_t)BH * T * dk * es}, {v, (size_t)BH * T * dv * es},
+                       {x, (size_t)BH * T * 4},       {beta, (size_t)BH * T * 4},    {S0, (size_t)BH * dk * dv * 4}};
+  const Range outs[] = {{o, (size_t)BH * T * dv * 4}, {S_T, (size_t)BH * dk * dv * 4}, {workspace, need}};
+  for (size_t i = 0; i < 3; ++i) {
+    for (const Range& in : ins)
+      if (overlap(outs[i], in)) return GLA_ERR_ALIAS;
+    for (size_t j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], outs[j])) return GLA_ERR_ALIAS;
+  }
+  char* w = (char*)workspace;
+  gla::DeltaParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.b = (float*)w;
+  p.beta = beta;
+  p.S0 = S0;
+  p.o = o;
+  p.ST = S_T;
+  p.W = w + b_bytes;
+  p.U = w + b_bytes + w_bytes;
+  p.T = T;
+  p.dk = dk;
+  p.dv = dv;
+  p.BH = (int)BH;
+  p.nchunks = (int)n_chunks(T);
+  p.nslices = dv_split;
+  p.grid = (int)(BH * dv_split);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (T > 0) {
+    e = gla::launch_gate_cumsum(x, (float*)w, BH, T,
+                                gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus,
+                                false, s);
+    if (e == hipSuccess) e = gla::launch_delta_prep(p, dt, s);
+  }
+  if (e == hipSuccess) e = gla::launch_delta_output(p, dt, s);
+  return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}
+
 gla_status_t gla_plan_check_pc(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
                                const gla_plan_t* plan) {
   gla_status_t st = check_sizes(B, H, T, dk, dv);

@@ -1,0 +1,477 @@
+// delta_kernels.hip -- chunked gated delta rule on gfx950 matrix cores.
+//
+// Source: "Engineering Long-Context Training for Trillion-Parameter MoE Models:
+// Three Key Breakthroughs" (§3.1: Delta-Net-style structures share the chunked
+// computation and its diagonal-tile problem; §3.2 the bounded gate; §3.3 every
+// causal tile on the dense matrix product).  The recurrence, in the plainest
+// reading of a gated delta rule with that decay:
+//     S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = S_t^T q_t.
+//
+// Chunked form.  S_t = a_t S_{t-1} + k_t u_t^T with the effective write
+// u_t = beta_t (v_t - a_t S_{t-1}^T k_t).  Inside a 64-token chunk with
+// cumulative log-decay b (as in the linear-attention kernels) and S_0 the state
+// before the chunk, a_t S_{t-1} = e^{b_t} S_0 + sum_{s<t} e^{b_t - b_s} k_s u_s^T, so
+//     (I + diag(beta) L) U = diag(beta) V - diag(beta e^b) K S_0,
+//     L[t][s] = e^{b_t - b_s} (k_t . k_s)  for s < t.
+// With Tinv = (I + diag(beta) L)^-1 (unit lower triangular):
+//     W = Tinv diag(beta e^b) K,  Ut = Tinv diag(beta) V   (no dependence on S_0)
+//     U = Ut - W S_0
+//     o = e^b (Q S_0) + A U,   A[t][s] = e^{b_t - b_s} (q_t . k_s), s <= t
+//     S_c = e^gamma S_0 + (K e^{gamma - b})^T U
+// i.e. the linear-attention chunk with the values replaced by U.  L and A are
+// causal 64x64 decay-weighted Gram matrices: both come out of the unified tile
+// product of the linear-attention kernels (q or k scaled by e^{b - r_u}, k by
+// e^{r_u - b}, tile scalar e^{r_u(t) - r_u(s)}), safe because the bounded gate
+// keeps a 16-token tile's reciprocal decay below e^80 [§3.2].
+//
+// Two passes:
+//   delta_prep_kernel   one workgroup per (head, chunk), all chunks in parallel:
+//                       L, Tinv (fp32, 16x16 blocks: forward substitution on the
+//                       diagonal blocks, matrix-core products for the others),
+//                       W and Ut, written to the workspace in the operand dtype.
+//   delta_output_kernel one workgroup per (head, slice of value columns), chunks
+//                       in order: U = Ut - W S_0 on the matrix cores, then o and
+//                       the state update as in the linear-attention output pass.
+#include "chunk_common.h"
+
+namespace gla {
+
+namespace {
+
+__device__ __forceinline__ uint32_t dl_row(uint32_t t, uint32_t Tn, uint32_t row_bytes) {
+  return t < Tn ? t * row_bytes : kDroppedOffset;
+}
+
+// acc += X Z for 16x16 fp32 blocks in LDS (X row stride ldx, Z row stride ldz):
+// afterwards lane (g, r16) holds (X Z)[4 g + e][r16] in acc[e].
+__device__ __forceinline__ void mm16(floatx4& acc, const float* X, int ldx, const float* Z, int ldz, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[r * ldx + 4 * s + g], Z[(4 * s + g) * ldz + r], acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ void store16(float* dst, int ld, const floatx4& acc, float sign, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) dst[(4 * g + e) * ld + r] = sign * acc[e];
+}
+
+// Four operand-dtype elements of one row to global memory (row-major [rows][ld]).
+template <typename T>
+__device__ __forceinline__ void store_row4(T* dst, const floatx4& v) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = static_cast<bf16>(v[e]);
+    *reinterpret_cast<bf16x4*>(dst) = w;
+  } else {
+    *reinterpret_cast<floatx4*>(dst) = v;
+  }
+}
+
+// ============================================================================
+// Pass 1: W and Ut of every chunk.
+// ============================================================================
+template <typename T, int DK, int DV>
+struct PrepCfg {
+  static constexpr int NT = 256;
+  static constexpr int PAD = Elem<T>::kPad;
+  static constexpr int QLD = DK + PAD;
+  static constexpr int TLD = 64 + PAD;
+  static constexpr int QU = 8 * DK / NT;
+  static constexpr int VU = 8 * DV / NT;
+  static constexpr int KS = DK / 32;
+  static constexpr int MLD = 65;
+};
+
+template <typename T, int DK, int DV>
+struct PrepSmem {
+  using C = PrepCfg<T, DK, DV>;
+  T kq[64 * C::QLD];              // k_t e^{b_t - r_u(t)}
+  T kh[64 * C::QLD];              // k_s e^{r_u(s) - b_s}
+  T kb[TokTile<T, DK>::SIZE];     // beta_s e^{b_s} k_s, token-major
+  T vb[TokTile<T, DV>::SIZE];     // beta_s v_s, token-major
+  T tb[64 * C::TLD];              // Tinv in the operand dtype
+  float mf[64][C::MLD];           // M = diag(beta) L (strictly lower)
+  float tf[64][C::MLD];           // Tinv (fp32)
+  float scr[4][16][17];
+  float sb[64];
+  float sbeta[64];
+};
+
+template <typename T, int DK, int DV>
+__global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
+  using E = Elem<T>;
+  using C = PrepCfg<T, DK, DV>;
+  __shared__ PrepSmem<T, DK, DV> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const long long bh = blockIdx.x / p.nchunks;
+  const int c = (int)(blockIdx.x - bh * p.nchunks);
+  const uint32_t t0 = (uint32_t)c * kChunk;
+  const uint32_t Tn = (uint32_t)p.T;
+  const rsrc_t rk = make_rsrc(static_cast<const T*>(p.k) + bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
+  const rsrc_t rv = make_rsrc(static_cast<const T*>(p.v) + bh * p.T * DV, Tn * DV * (uint32_t)sizeof(T));
+
+  // ---- operands: loads first, decays after the barrier that publishes b and beta
+  typename E::Vec8 kv[C::QU], vv[C::VU];
+#pragma unroll
+  for (int m = 0; m < C::QU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
+    kv[m] = E::load8(rk, dl_row(t0 + row, Tn, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T));
+  }
+#pragma unroll
+  for (int m = 0; m < C::VU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DV / 8), c8 = u % (DV / 8);
+    vv[m] = E::load8(rv, dl_row(t0 + row, Tn, DV * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T));
+  }
+  if (tid < 64) {
+    const long long t = (long long)t0 + tid;
+    const long long tc = t < p.T ? t : p.T - 1;  // absent tokens: g = 0, beta = 0
+    sm.sb[tid] = p.b[bh * p.T + tc];
+    sm.sbeta[tid] = t < p.T ? p.beta[bh * p.T + t] : 0.0f;
+  }
+  __syncthreads();
+  const auto ref = [&](int u) { return u == 0 ? 0.0f : sm.sb[16 * u - 1]; };
+#pragma unroll
+  for (int m = 0; m < C::QU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
+    const float br = sm.sb[row], r = ref(row >> 4);
+    E::store8_scaled(sm.kq + row * C::QLD + c8 * 8, kv[m], exp_e(br - r));
+    E::store8_scaled(sm.kh + row * C::QLD + c8 * 8, kv[m], exp_e(r - br));
+    TokTile<T, DK>::store8(sm.kb, row, c8 * 8, kv[m], sm.sbeta[row] * exp_e(br));
+  }
+#pragma unroll
+  for (int m = 0; m < C::VU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DV / 8), c8 = u % (DV / 8);
+    TokTile<T, DV>::store8(sm.vb, row, c8 * 8, vv[m], sm.sbeta[row]);
+  }
+  __syncthreads();
+
+  // ---- M = diag(beta) L over the 10 causal tiles, strictly below the diagonal
+#pragma unroll
+  for (int t = 0; t < 10; ++t) {
+    if (t % 4 != wave) continue;  // wave-uniform
+    const int jb = tri_j(t), ib = tri_i(t);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      E::mfma(acc, E::load_frag(sm.kh + (ib * 16 + r16) * C::QLD, ks * 32 + 4 * g),
+              E::load_frag(sm.kq + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+    // acc[e]: row t = 16 jb + r16, column s = 16 ib + 4 g + e
+    const int tr = jb * 16 + r16;
+    const float f = (jb == ib ? 1.0f : exp_e(ref(jb) - ref(ib))) * sm.sbeta[tr];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sm.mf[tr][ib * 16 + 4 * g + e] = (jb != ib || 4 * g + e < r16) ? acc[e] * f : 0.0f;
+  }
+  __syncthreads();
+
+  // ---- Tinv = (I + M)^-1, diagonal blocks by forward substitution (lane = column)
+  if (lane < 16) {
+    const int o = 16 * wave, j = lane;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float s = (i == j) ? 1.0f : 0.0f;
+#pragma unroll
+      for (int q = 0; q < i; ++q) s -= sm.mf[o + i][o + q] * x[q];
+      x[i] = s;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.tf[o + i][o + j] = x[i];
+  }
+  __syncthreads();
+  // block row I, column J < I:  X_IJ = -D_I sum_{J <= K < I} M_IK X_KJ, by distance I - J
+#pragma unroll
+  for (int dist = 1; dist <= 3; ++dist) {
+    const int I = wave, J = wave - dist;
+    if (J >= 0) {  // wave-uniform
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int K = J; K < I; ++K) mm16(acc, &sm.mf[16 * I][16 * K], C::MLD, &sm.tf[16 * K][16 * J], C::MLD, lane);
+      store16(&sm.scr[I][0][0], 17, acc, 1.0f, lane);
+      floatx4 x = {0.f, 0.f, 0.f, 0.f};
+      mm16(x, &sm.tf[16 * I][16 * I], C::MLD, &sm.scr[I][0][0], 17, lane);
+      store16(&sm.tf[16 * I][16 * J], C::MLD, x, -1.0f, lane);
+    }
+    __syncthreads();
+  }
+  // operand copy of Tinv, zero above the diagonal blocks
+  for (int e = tid; e < 64 * 64; e += C::NT) {
+    const int t = e >> 6, s = e & 63;
+    sm.tb[t * C::TLD + s] = E::cvt((s >> 4) <= (t >> 4) ? sm.tf[t][s] : 0.0f);
+  }
+  __syncthreads();
+
+  // ---- W = Tinv (beta e^b K), Ut = Tinv (beta V): wave w owns a quarter of the columns
+  T* Wg = static_cast<T*>(p.W) + bh * p.T * DK;
+  T* Ug = static_cast<T*>(p.U) + bh * p.T * DV;
+  const auto product = [&](const T* tile, int ncol, T* dst, int ld) {
+    for (int cb = wave * (ncol / 4); cb < (wave + 1) * (ncol / 4); cb += 16) {
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks <= jb / 2; ++ks)
+          E::mfma(acc, ncol == DK ? TokTile<T, DK>::load(tile, ks * 32, cb, lane)
+                                  : TokTile<T, DV>::load(tile, ks * 32, cb, lane),
+                  E::load_frag(sm.tb + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
+        // acc[e] = X[t0 + 16 jb + r16][cb + 4 g + e]
+        const long long t = (long long)t0 + jb * 16 + r16;
+        if (t < p.T) store_row4<T>(dst + t * ld + cb + 4 * g, acc);
+      }
+    }
+  };
+  product(sm.kb, DK, Wg, DK);
+  product(sm.vb, DV, Ug, DV);
+}
+
+// ============================================================================
+// Pass 2: the serial chunk loop.
+// ============================================================================
+template <typename T, int DK, int DVS>
+struct DoCfg {
+  static constexpr int NW = DVS / 16;        // waves, 16 value columns each
+  static constexpr int NT = 64 * NW;
+  static constexpr int PAD = Elem<T>::kPad;
+  static constexpr int QLD = DK + PAD;
+  static constexpr int TLD = 64 + PAD;
+  static constexpr int QU = 8 * DK / NT;
+  static constexpr int DB = DK / 16;
+  static constexpr int KS = DK / 32;
+  static_assert(QU >= 1 && QU * NT == 8 * DK, "staging must divide evenly");
+};
+
+template <typename T, int DK, int DVS>
+struct DoSmem {
+  using C = DoCfg<T, DK, DVS>;
+  T qh[64 * C::QLD];
+  T kh[64 * C::QLD];
+  T wn[64 * C::QLD];              // -W
+  T kp[TokTile<T, DK>::SIZE];     // k e^{gamma - b}, token-major
+  T uu[TokTile<T, DVS>::SIZE];    // U of the slice, token-major
+  T a[64 * C::TLD];
+};
+
+template <typename T, int DK, int DVS>
+struct DoStaged {
+  using E = Elem<T>;
+  using C = DoCfg<T, DK, DVS>;
+  typename E::Vec8 q[C::QU], k[C::QU], w[C::QU];
+  floatx4 ut[4];   // Ut[t0 + 16 jb + r16][wcol + 4 g + e]
+  float b;
+
+  __device__ __forceinline__ void load(const rsrc_t& rq, const rsrc_t& rk, const rsrc_t& rw, const rsrc_t& ru,
+                                       const rsrc_t& rb, uint32_t Tn, int dv, uint32_t t0, int wcol, int tid) {
+    const int lane = tid & 63, r16 = lane & 15, g = lane >> 4;
+    const uint32_t tb = t0 + lane;
+    b = buf_load4(rb, (tb < Tn ? tb : Tn - 1) * 4u);
+#pragma unroll
+    for (int m = 0; m < C::QU; ++m) {
+      const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
+      const uint32_t off = dl_row(t0 + row, Tn, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T);
+      q[m] = E::load8(rq, off);
+      k[m] = E::load8(rk, off);
+      w[m] = E::load8(rw, off);
+    }
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      const uint32_t off = dl_row(t0 + jb * 16 + r16, Tn, (uint32_t)dv * (uint32_t)sizeof(T)) +
+                           (wcol + 4 * g) * (uint32_t)sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(ru, (int)off, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(ru, (int)(off + 4u), 0, 0);
+        ut[jb] = floatx4{bf16_bits_to_f32(lo & 0xFFFFu), bf16_bits_to_f32(lo >> 16), bf16_bits_to_f32(hi & 0xFFFFu),
+                         bf16_bits_to_f32(hi >> 16)};
+      } else {
+        const uint4 raw = buf_load16(ru, off);
+        ut[jb] = floatx4{__builtin_bit_cast(float, raw.x), __builtin_bit_cast(float, raw.y),
+                         __builtin_bit_cast(float, raw.z), __builtin_bit_cast(float, raw.w)};
+      }
+    }
+  }
+};
+
+template <typename T, int DK, int DVS>
+__global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(DeltaParams p) {
+  using E = Elem<T>;
+  using C = DoCfg<T, DK, DVS>;
+  __shared__ DoSmem<T, DK, DVS> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int L = xcd_linear_index(blockIdx.x, p.grid);
+  const int slice = L % p.nslices;
+  const int bh = L / p.nslices;
+  const int col0 = slice * DVS;
+  const int wcol = col0 + wave * 16;
+  const uint32_t Tn = (uint32_t)p.T;
+  const uint32_t es = (uint32_t)sizeof(T);
+  const rsrc_t rq = make_rsrc(static_cast<const T*>(p.q) + (long long)bh * p.T * DK, Tn * DK * es);
+  const rsrc_t rk = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * es);
+  const rsrc_t rw = make_rsrc(static_cast<const T*>(p.W) + (long long)bh * p.T * DK, Tn * DK * es);
+  const rsrc_t ru = make_rsrc(static_cast<const T*>(p.U) + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * es);
+  const rsrc_t rb = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+  const rsrc_t ro = make_rsrc(p.o + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * 4u);
+
+  // state slice of the wave: S[16 db + 4 g + e][wcol + r16]
+  floatx4 S[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const long long i = (long long)bh * DK * p.dv + (long long)(db * 16 + 4 * g + e) * p.dv + wcol + r16;
+      S[db][e] = p.S0 ? p.S0[i] : 0.0f;
+    }
+  for (int e = tid; e < 2 * 256; e += C::NT) {
+    const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
+    sm.a[(blk * 32 + rr) * C::TLD + blk * 32 + 16 + cc] = E::cvt(0.0f);
+  }
+
+  DoStaged<T, DK, DVS> st;
+  if (p.nchunks > 0) st.load(rq, rk, rw, ru, rb, Tn, p.dv, 0, wcol, tid);
+  for (int c = 0; c < p.nchunks; ++c) {
+    const uint32_t t0 = (uint32_t)c * kChunk;
+    const ChunkDecay cd(st.b);
+    floatx4 ut[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) ut[jb] = st.ut[jb];
+    // ---- (1) operands of chunk c
+#pragma unroll
+    for (int m = 0; m < C::QU; ++m) {
+      const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
+      const float br = cd.at(row), r = cd.r(row >> 4);
+      E::store8_scaled(sm.qh + row * C::QLD + c8 * 8, st.q[m], exp_e(br - r));
+      E::store8_scaled(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(r - br));
+      E::store8_neg(sm.wn + row * C::QLD + c8 * 8, st.w[m]);
+      TokTile<T, DK>::store8(sm.kp, row, c8 * 8, st.k[m], exp_e(cd.gam - br));
+    }
+    // ---- (2) prefetch chunk c + 1 (the last iteration re-reads its own chunk)
+    st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, p.nchunks - 1) * kChunk, wcol, tid);
+    __syncthreads();
+
+    // ---- (3) A over the 10 causal tiles
+#pragma unroll
+    for (int t = 0; t < 10; ++t) {
+      if (t % C::NW != wave) continue;  // wave-uniform
+      const int jb = tri_j(t), ib = tri_i(t);
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks)
+        E::mfma(acc, E::load_frag(sm.kh + (ib * 16 + r16) * C::QLD, ks * 32 + 4 * g),
+                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+      const float f = (jb == ib) ? 1.0f : exp_e(cd.r(jb) - cd.r(ib));
+      float vals[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vals[e] = (jb != ib || 4 * g + e <= r16) ? acc[e] * f : 0.0f;
+      E::store4(sm.a + (jb * 16 + r16) * C::TLD + ib * 16 + 4 * g, vals[0], vals[1], vals[2], vals[3]);
+    }
+
+    // ---- (4) o_inter = e^{r_u} Qh S_0 and U = Ut - W S_0 for the wave's columns
+    floatx4 O[4];
+    {
+      typename E::Frag Sf[C::KS];
+#pragma unroll
+      for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb) {
+        O[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+          E::mfma(O[jb], Sf[ks], E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+          E::mfma(ut[jb], Sf[ks], E::load_frag(sm.wn + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+        }
+        if (jb > 0) O[jb] *= exp_e(cd.r(jb));
+        // ut[jb][e] = U[16 jb + r16][wcol + 4 g + e]
+        const int row = jb * 16 + r16, colr = wcol - col0 + 4 * g;
+        if constexpr (sizeof(T) == 2) {
+          E::store4(sm.uu + row * TokTile<T, DVS>::LD + colr, ut[jb][0], ut[jb][1], ut[jb][2], ut[jb][3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm.uu[(colr + e) * TokTile<T, DVS>::LD + row] = ut[jb][e];
+        }
+      }
+    }
+    __syncthreads();
+
+    // ---- (5) o += A U; S_c = e^gamma S_0 + (k e^{gamma - b})^T U
+    {
+      typename E::Frag Uf[2];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) Uf[ks] = TokTile<T, DVS>::load(sm.uu, ks * 32, wave * 16, lane);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int ks = 0; ks <= jb / 2; ++ks)
+          E::mfma(O[jb], Uf[ks], E::load_frag(sm.a + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
+      const float dec = exp_e(cd.gam);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) S[db] *= dec;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) E::mfma(S[db], TokTile<T, DK>::load(sm.kp, ks * 32, db * 16, lane), Uf[ks]);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+        buf_store16(ro, dl_row(t0 + jb * 16 + r16, Tn, (uint32_t)p.dv * 4u) + (wcol + 4 * g) * 4u, O[jb]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      p.ST[(long long)bh * DK * p.dv + (long long)(db * 16 + 4 * g + e) * p.dv + wcol + r16] = S[db][e];
+}
+
+}  // namespace
+
+bool delta_config_built(int dtype, int dk, int dv, int slice) {
+  if (dk != 64 && dk != 128) return false;
+  if (dv != 64 && dv != 128) return false;
+  if (dtype == 0) return slice == 32 || slice == 64 || slice == 128;
+  return dk == 64 && dv == 64 && (slice == 32 || slice == 64);
+}
+
+hipError_t launch_delta_prep(const DeltaParams& p, int dtype, hipStream_t stream) {
+  const long long blocks = (long long)p.BH * p.nchunks;
+  if (blocks == 0) return hipSuccess;
+  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+#define GLA_DP(TT, DKV, DVV) \
+  hipLaunchKernelGGL((delta_prep_kernel<TT, DKV, DVV>), dim3((unsigned)blocks), dim3(256), 0, stream, p)
+  if (dtype == 0) {
+    if (p.dk == 128 && p.dv == 128) GLA_DP(bf16, 128, 128);
+    else if (p.dk == 128 && p.dv == 64) GLA_DP(bf16, 128, 64);
+    else if (p.dk == 64 && p.dv == 128) GLA_DP(bf16, 64, 128);
+    else if (p.dk == 64 && p.dv == 64) GLA_DP(bf16, 64, 64);
+    else return hipErrorInvalidValue;
+  } else {
+    if (p.dk == 64 && p.dv == 64) GLA_DP(float, 64, 64);
+    else return hipErrorInvalidValue;
+  }
+#undef GLA_DP
+  return hipGetLastError();
+}
+
+hipError_t launch_delta_output(const DeltaParams& p, int dtype, hipStream_t stream) {
+  if (p.grid == 0) return hipSuccess;
+  const int slice = p.dv / p.nslices;
+#define GLA_DO(TT, DKV, DVSV)                                                                                   \
+  if (p.dk == DKV && slice == DVSV) {                                                                            \
+    hipLaunchKernelGGL((delta_output_kernel<TT, DKV, DVSV>), dim3(p.grid), dim3(DoCfg<TT, DKV, DVSV>::NT), 0, \
+                       stream, p);                                                                              \
+    return hipGetLastError();                                                                                    \
+  }
+  if (dtype == 0) {
+    GLA_DO(bf16, 128, 128) GLA_DO(bf16, 128, 64) GLA_DO(bf16, 128, 32)
+    GLA_DO(bf16, 64, 128) GLA_DO(bf16, 64, 64) GLA_DO(bf16, 64, 32)
+  } else {
+    GLA_DO(float, 64, 64) GLA_DO(float, 64, 32)
+  }
+#undef GLA_DO
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gla

@@ -126,6 +126,11 @@ template <> struct Elem<bf16> {
   __device__ static __forceinline__ void store8_raw(bf16* dst, const Vec8& v) {
     *reinterpret_cast<uint4*>(dst) = v.u;
   }
+  // store -v (sign bits flipped: exact)
+  __device__ static __forceinline__ void store8_neg(bf16* dst, const Vec8& v) {
+    constexpr uint32_t m = 0x80008000u;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(v.u.x ^ m, v.u.y ^ m, v.u.z ^ m, v.u.w ^ m);
+  }
   // store 8 elements, each with its own scale
   __device__ static __forceinline__ void store8_vscaled(bf16* dst, const Vec8& v, const float (&s)[8]) {
     bf16x8 o;
@@ -192,6 +197,12 @@ template <> struct Elem<float> {
   __device__ static __forceinline__ void store8_raw(float* dst, const Vec8& v) {
     *reinterpret_cast<float4*>(dst) = v.a;
     *reinterpret_cast<float4*>(dst + 4) = v.b;
+  }
+  __device__ static __forceinline__ void store8_neg(float* dst, const Vec8& v) {
+    constexpr uint32_t m = 0x80000000u;
+    const auto flip = [](float f) { return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) ^ m); };
+    *reinterpret_cast<float4*>(dst) = make_float4(flip(v.a.x), flip(v.a.y), flip(v.a.z), flip(v.a.w));
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(flip(v.b.x), flip(v.b.y), flip(v.b.z), flip(v.b.w));
   }
   __device__ static __forceinline__ void store8_vscaled(float* dst, const Vec8& v, const float (&s)[8]) {
     *reinterpret_cast<float4*>(dst) = make_float4(v.a.x * s[0], v.a.y * s[1], v.a.z * s[2], v.a.w * s[3]);

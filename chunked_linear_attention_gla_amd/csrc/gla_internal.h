@@ -104,6 +104,29 @@ bool pc_config_built(int dtype, int dk, int slice);
 hipError_t launch_pc_segment_states(const PcParams& p, int dtype, hipStream_t stream);
 hipError_t launch_pc_chunk_output(const PcParams& p, int dtype, hipStream_t stream);
 
+// Gated delta rule (delta_kernels.hip).
+struct DeltaParams {
+  const void* q;          // [BH][T][dk]
+  const void* k;          // [BH][T][dk]
+  const void* v;          // [BH][T][dv]
+  const float* b;         // [BH][T] chunk-local cumulative log-decay
+  const float* beta;      // [BH][T] write strength
+  const float* S0;        // [BH][dk][dv] or nullptr
+  float* o;               // [BH][T][dv]
+  float* ST;              // [BH][dk][dv]
+  void* W;                // [BH][T][dk] operand dtype: Tinv diag(beta e^b) K per chunk
+  void* U;                // [BH][T][dv] operand dtype: Tinv diag(beta) V per chunk
+  long long T;
+  int dk, dv;
+  int BH;
+  int nchunks;
+  int nslices;
+  int grid;
+};
+bool delta_config_built(int dtype, int dk, int dv, int slice);
+hipError_t launch_delta_prep(const DeltaParams& p, int dtype, hipStream_t stream);
+hipError_t launch_delta_output(const DeltaParams& p, int dtype, hipStream_t stream);
+
 // One recurrent step per head (decode.hip): S <- diag(a) S + k v^T in place, o = S^T q.
 // q, k [BH][dk], v [BH][dv] in the operand dtype; x [BH] or, per_channel, [BH][dk];
 // S [BH][dk][dv] and o [BH][dv] fp32.  dk, dv <= 128, dv a multiple of 4.

@@ -11,6 +11,7 @@ Workload recipe, shared by every named workload:
   x ~ N(x_mean, x_std), one fp32 scalar per (batch, head, token), or per
       (batch, head, token, key channel) for the per-channel-decay workloads
   S0 ~ N(0, s0_std) fp32 when s0_std > 0, else absent (zero initial state)
+  beta ~ U(0, 1) fp32 per (batch, head, token), delta-rule workloads only (drawn last)
 q, k, v are stored in bf16 (round-to-nearest-even, torch's cast) or fp32; x, S0
 always fp32.  N(m, s) means mean m and standard deviation s.  Draws happen in the
 order q, k, v, x, S0 from one torch generator seeded with the workload's seed on
@@ -45,6 +46,7 @@ class Workload:
     seed: int
     note: str = ""
     per_channel: bool = False  # x has one value per key channel: [B, H, T, dk]
+    delta: bool = False        # also draw beta ~ U(0, 1) per (batch, head, token): delta-rule write strength
 
     @property
     def tokens(self) -> int:
@@ -73,6 +75,8 @@ WORKLOADS: Dict[str, Workload] = {
                             "serving step: 64 sequences x 32 heads, one token each, fp32 state carried"),
     "bf16_varlen_256k": Workload("bf16_varlen_256k", 1, 16, 262144, 128, 128, "bf16", 0.0, 1.0, 0.0, "bounded",
                                  1007, "64 packed sequences, log-uniform length mix, 256K tokens in total"),
+    "bf16_64k_delta": Workload("bf16_64k_delta", 1, 32, 65536, 128, 128, "bf16", 0.0, 1.0, 0.0, "bounded", 1008,
+                               "gated delta rule: beta ~ U(0, 1) per token, unit-norm keys", delta=True),
     "bf16_64k_pc": Workload("bf16_64k_pc", 1, 32, 65536, 128, 128, "bf16", 4.0, 1.0, 0.0, "bounded", 1005,
                             "per-channel decay: x per (token, key channel), same shapes and regime",
                             per_channel=True),
@@ -125,7 +129,10 @@ def make_inputs(w: Workload, device="cpu", *, T: Optional[int] = None, H: Option
     S0 = None
     if w.s0_std > 0:
         S0 = torch.randn(B, H, w.dk, w.dv, **f32).mul_(w.s0_std)
-    return dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), x=x.contiguous(), S0=S0)
+    out = dict(q=q.contiguous(), k=k.contiguous(), v=v.contiguous(), x=x.contiguous(), S0=S0)
+    if w.delta:
+        out["beta"] = torch.rand(B, H, T, **f32)
+    return out
 
 
 def varlen_lengths(n: int, total: int, seed: int, min_len: int = 1) -> list:

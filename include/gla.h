@@ -218,6 +218,30 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
                            void* workspace, size_t* workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Gated delta rule.  [LCT §3.1, §3.3] name Delta-Net-style structures as the
+ * other family with the same chunked diagonal-tile problem; the recurrence here
+ * is the gated delta rule with the same decay gate:
+ *     S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,  o_t = S_t^T q_t,
+ *     a_t = e^{g(x_t)}.
+ * Chunked with an exact triangular solve per 64-token chunk: the effective writes
+ * U = Tinv diag(beta) V - Tinv diag(beta e^b) K S_0 with Tinv = (I + diag(beta) L)^-1,
+ * L the decay-weighted Gram matrix of the chunk's keys; both L and the attention
+ * matrix come from the unified 16-token-tile product (no diagonal branch).
+ *   beta [B][H][T] fp32 (a write strength, normally in [0, 1]); other arguments as
+ *   for gla_chunk_fwd (S0 may be NULL).
+ *   dv_split: value columns are split into dv / dv_split slices, one workgroup per
+ *   (head, slice) running the chunks in order; 0 = default for this device.
+ * Built: bf16 with dk, dv in {64, 128} and slices of 32, 64 or 128 columns; fp32
+ * with dk = dv = 64 and slices of 32 or 64.  Others: GLA_ERR_UNSUPPORTED or
+ * GLA_ERR_PLAN.  The workspace holds b and the per-chunk W, U (operand dtype);
+ * workspace == NULL returns its size.  Errors and validation as gla_chunk_fwd. */
+gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, const float* x,
+                                 const float* beta, const float* S0, float* o, float* S_T,
+                                 int B, int H, long long T, int dk, int dv,
+                                 gla_dtype_t dtype, gla_gate_t gate, int dv_split,
+                                 void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Decode and packed sequences. */
 
 /* One recurrent step for every head, for generating one token at a time with
