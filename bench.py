@@ -88,6 +88,8 @@ def parse():
     ap.add_argument("--backward-only", action="store_true", help="time only the backward pass (profiling)")
     ap.add_argument("--no-per-channel", action="store_true", help="skip the per-channel-decay measurement")
     ap.add_argument("--no-serving", action="store_true", help="skip the decode and packed-sequence measurements")
+    ap.add_argument("--no-delta", action="store_true", help="skip the gated-delta-rule measurement")
+    ap.add_argument("--delta-only", action="store_true", help="time only the gated delta rule")
     ap.add_argument("--serving-only", action="store_true", help="time only decode and packed sequences")
     ap.add_argument("--per-channel-only", action="store_true", help="time only the per-channel forward")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -417,6 +419,49 @@ def varlen_result(gla, gin, torch, steps, warmup, cpu_seconds):
     return res
 
 
+def delta_result(gla, gin, torch, steps, warmup, cpu_seconds):
+    """The chunked gated delta rule (gla_chunk_fwd_delta: gate + cumsum, the parallel
+    per-chunk solve, the serial output pass) on its 64K workload."""
+    import numpy as np
+    w = gin.WORKLOADS["bf16_64k_delta"]
+    dev = torch.device("cuda:0")
+    inp = gin.make_inputs(w, dev)
+    B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+    o = torch.empty(B, H, T, dv, device=dev)
+    ST = torch.empty(B, H, dk, dv, device=dev)
+    ws = torch.empty(B * H * T * (4 + 2 * (dk + dv)) + (1 << 20), dtype=torch.uint8, device=dev)
+    fn = lambda: gla.chunk_fwd_delta(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["S0"], gate=w.gate,
+                                     o=o, S_T=ST, workspace=ws)
+    ms_host, ms_ev = time_calls(torch, fn, steps, warmup)
+    es = inp["q"].element_size()
+    # q, k, v, x, beta in; o out (the per-chunk W and U are implementation traffic)
+    per_th = (2 * dk + dv) * es + 8 + 4 * dv
+    nbytes = B * H * T * per_th + B * H * dk * dv * 4
+    achieved = nbytes / (ms_ev / 1e3) / 1e9
+    res = {"what": "gla_chunk_fwd_delta: gated delta rule forward, all kernels of the call", "workload": w.name,
+           "x": f"N({w.x_mean},{w.x_std})", "beta": "U(0,1)", "steps": steps,
+           "ms_per_call": round(ms_host, 4), "ms_per_call_events": round(ms_ev, 4),
+           "tokens_per_s": round(B * T / (ms_ev / 1e3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes}}
+    if cpu_seconds > 0:
+        import oracle
+        flat = lambda t: t.reshape(B * H, *t.shape[2:])
+
+        def run(Tn):
+            args = [gin.to_numpy_bits(flat(inp[n])[:, :Tn]) for n in ("q", "k", "v", "x", "beta")]
+            t0 = time.perf_counter()
+            oracle.forward_delta(*args, None, gate=w.gate)
+            return time.perf_counter() - t0
+        dt0 = run(256)
+        Tn = int(min(T, max(256, cpu_seconds / max(dt0, 1e-6) * 256))) // 64 * 64
+        dt = run(Tn)
+        res["cpu_baseline"] = {"value": B * Tn / dt, "unit": "tokens/s", "cores": oracle.max_threads(),
+                               "kind": "oracle", "sample": f"all {B * H} heads, first {Tn} of {T} tokens; "
+                                                           f"fp64 token-by-token delta rule; {dt:.1f} s"}
+    return res
+
+
 def backward_result(gla, gin, torch, w, path, steps, warmup):
     t = BackwardTimer(gla, gin, torch, w, path)
     ms_host, ms_ev = t.run(steps, warmup)
@@ -457,6 +502,9 @@ def main():
     path = args.path or "unified"
     torch.cuda.set_device(torch.device("cuda:0"))
     plan = gla.Plan(*(int(s) for s in args.plan.split(","))) if args.plan else None
+    if args.delta_only:
+        print(json.dumps({"delta": delta_result(gla, gin, torch, args.steps, args.warmup, 0.0)}), flush=True)
+        return
     if args.serving_only:
         print(json.dumps({"decode": decode_result(gla, gin, torch, args.steps, args.warmup, 0.0),
                           "varlen": varlen_result(gla, gin, torch, args.steps, args.warmup, 0.0)}), flush=True)
@@ -546,6 +594,9 @@ def main():
         cs = 0.0 if args.no_cpu_baseline else args.cpu_seconds / 4
         result["decode"] = decode_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5), cs)
         result["varlen"] = varlen_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5), cs)
+    if not args.no_delta and not args.plan and w.name == gin.HEADLINE:
+        result["delta"] = delta_result(gla, gin, torch, min(args.steps, 10), min(args.warmup, 3),
+                                       0.0 if args.no_cpu_baseline else args.cpu_seconds / 4)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
