@@ -429,9 +429,11 @@ def delta_result(gla, gin, torch, steps, warmup, cpu_seconds):
     B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
     o = torch.empty(B, H, T, dv, device=dev)
     ST = torch.empty(B, H, dk, dv, device=dev)
-    ws = torch.empty(B * H * T * (4 + 2 * (dk + dv)) + (1 << 20), dtype=torch.uint8, device=dev)
+    plan = gla.plan_default_delta(B, H, T, dk, dv)
+    ws = torch.empty(B * H * (T * (4 + 2 * (dk + dv)) + plan.segments * dk * (dk + dv) * 4) + (1 << 20),
+                     dtype=torch.uint8, device=dev)
     fn = lambda: gla.chunk_fwd_delta(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["S0"], gate=w.gate,
-                                     o=o, S_T=ST, workspace=ws)
+                                     plan=plan, o=o, S_T=ST, workspace=ws)
     ms_host, ms_ev = time_calls(torch, fn, steps, warmup)
     es = inp["q"].element_size()
     # q, k, v, x, beta in; o out (the per-chunk W and U are implementation traffic)
@@ -440,6 +442,7 @@ def delta_result(gla, gin, torch, steps, warmup, cpu_seconds):
     achieved = nbytes / (ms_ev / 1e3) / 1e9
     res = {"what": "gla_chunk_fwd_delta: gated delta rule forward, all kernels of the call", "workload": w.name,
            "x": f"N({w.x_mean},{w.x_std})", "beta": "U(0,1)", "steps": steps,
+           "plan": {"segments": plan.segments, "dv_split": plan.dv_split},
            "ms_per_call": round(ms_host, 4), "ms_per_call_events": round(ms_ev, 4),
            "tokens_per_s": round(B * T / (ms_ev / 1e3), 1),
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -71,8 +71,10 @@ _SIGS = {
     "gla_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "gla_chunk_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _ll, _i, _i, _i, _i, _i,
                                   _vp, _psz, _vp]),
-    "gla_chunk_fwd_delta": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i, _vp, _psz,
-                                 _vp]),
+    "gla_plan_default_delta": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
+    "gla_plan_check_delta": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
+    "gla_chunk_fwd_delta": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan, _vp,
+                                 _psz, _vp]),
     "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
                            _i, _i, _i, _vp, _psz, _vp]),
 }
@@ -277,6 +279,12 @@ def plan_default_pc(B: int, H: int, T: int, dk: int, dv: int, dtype=GLA_BF16) ->
     return Plan(cp.segments, cp.dv_split)
 
 
+def plan_default_delta(B: int, H: int, T: int, dk: int, dv: int, dtype=GLA_BF16) -> Plan:
+    cp = _CPlan()
+    _check("gla_plan_default_delta", load().gla_plan_default_delta(B, H, T, dk, dv, dtype, ctypes.byref(cp)))
+    return Plan(cp.segments, cp.dv_split)
+
+
 def plan_check_pc(B: int, H: int, T: int, dk: int, dv: int, plan: Plan, dtype=GLA_BF16) -> int:
     """Status code of gla_plan_check_pc (0 = valid)."""
     return int(load().gla_plan_check_pc(B, H, T, dk, dv, dtype, _cplan(plan)))
@@ -393,14 +401,14 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch
 
 
 def chunk_fwd_delta(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor, beta: torch.Tensor,
-                    S0: Optional[torch.Tensor] = None, gate="bounded", dv_split: int = 0,
+                    S0: Optional[torch.Tensor] = None, gate="bounded", plan: Optional[Plan] = None,
                     o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Gated delta rule forward: returns (o [B,H,T,dv] fp32, S_T [B,H,dk,dv] fp32) for
     S_t = a_t (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T, o_t = S_t^T q_t.
 
-    As :func:`chunk_fwd`, plus beta: fp32 [B, H, T] write strengths; dv_split: value-column
-    slices per head (0 = device default).
+    As :func:`chunk_fwd`, plus beta: fp32 [B, H, T] write strengths; plan: (segments,
+    dv_split) or None for the device default.
     """
     B, H, T, dk, dv = _check_qkv(q, k, v, x, S0)
     dev = q.device
@@ -415,8 +423,9 @@ def chunk_fwd_delta(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.
     _need(tuple(S_T.shape) == (B, H, dk, dv) and S_T.dtype == torch.float32 and S_T.is_contiguous()
           and S_T.device == dev, "S_T must be fp32 [B, H, dk, dv] on q's device")
     lib = load()
+    cplan = _cplan(plan)
     args = lambda ws: (_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(beta), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk,
-                       dv, _dtype_code(q), _gate(gate), int(dv_split), ws)
+                       dv, _dtype_code(q), _gate(gate), cplan, ws)
     need = ctypes.c_size_t(0)
     _check("gla_chunk_fwd_delta", lib.gla_chunk_fwd_delta(*args(None), ctypes.byref(need), _stream(dev)))
     if workspace is None or workspace.numel() * workspace.element_size() < need.value:

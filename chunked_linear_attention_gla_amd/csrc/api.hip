@@ -545,35 +545,70 @@ gla_status_t gla_decode_step(const void* q, const void* k, const void* v, const 
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
+gla_status_t gla_plan_check_delta(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                                  const gla_plan_t* plan) {
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!plan) return GLA_ERR_NULL;
+  const long long nc = n_chunks(T);
+  if (plan->segments < 1 || plan->segments > GLA_MAX_SEGMENTS) return GLA_ERR_PLAN;
+  if (plan->segments > std::max(1LL, nc)) return GLA_ERR_PLAN;
+  const int sp = plan->dv_split;
+  if (sp < 1 || dv % sp) return GLA_ERR_PLAN;
+  if (!gla::delta_config_built(dtype == GLA_BF16 ? 0 : 1, dk, dv, dv / sp))
+    return (dtype == GLA_F32 && (dk != 64 || dv != 64)) ? GLA_ERR_UNSUPPORTED : GLA_ERR_PLAN;
+  return GLA_OK;
+}
+
+gla_status_t gla_plan_default_delta(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                                    gla_plan_t* plan) {
+  if (!plan) return GLA_ERR_NULL;
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  int cus = 0;
+  st = device_cus(&cus);
+  if (st != GLA_OK) return st;
+  // whole value rows per workgroup (16 columns per wave; fp32: 64-column slices),
+  // then sequence segments until the grid covers the compute units
+  const long long BH = (long long)B * H;
+  const long long nc = n_chunks(T);
+  const int split = dtype == GLA_F32 ? dv / 64 : 1;
+  int segs = 1;
+  while (segs < GLA_MAX_SEGMENTS && BH * split * segs < cus && nc / (2LL * segs) >= 4) segs *= 2;
+  plan->segments = segs;
+  plan->dv_split = split;
+  return gla_plan_check_delta(B, H, T, dk, dv, dtype, plan);
+}
+
 gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, const float* x, const float* beta,
                                  const float* S0, float* o, float* S_T, int B, int H, long long T, int dk, int dv,
-                                 gla_dtype_t dtype, gla_gate_t gate, int dv_split, void* workspace,
+                                 gla_dtype_t dtype, gla_gate_t gate, const gla_plan_t* plan, void* workspace,
                                  size_t* workspace_bytes, void* stream) {
   if (!workspace_bytes) return GLA_ERR_NULL;
   gla_status_t st = check_sizes(B, H, T, dk, dv);
   if (st != GLA_OK) return st;
   if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
   if (!valid_gate(gate)) return GLA_ERR_ARG;
+  gla_plan_t pl;
+  if (plan) {
+    st = gla_plan_check_delta(B, H, T, dk, dv, dtype, plan);
+    if (st != GLA_OK) return st;
+    pl = *plan;
+  } else {
+    st = gla_plan_default_delta(B, H, T, dk, dv, dtype, &pl);
+    if (st != GLA_OK) return st;
+  }
   const long long BH = (long long)B * H;
   const int dt = dtype == GLA_BF16 ? 0 : 1;
-  if (dv_split == 0) {
-    // one workgroup per (head, value slice) runs the chunks in order: narrow the
-    // slices (down to 32 columns) until the heads cover the compute units
-    int cus = 0;
-    st = device_cus(&cus);
-    if (st != GLA_OK) return st;
-    dv_split = 1;
-    while (BH * dv_split < cus && dv / (2 * dv_split) >= 32 && gla::delta_config_built(dt, dk, dv, dv / (2 * dv_split)))
-      dv_split *= 2;
-  }
-  if (dv_split < 1 || dv % dv_split) return GLA_ERR_PLAN;
-  if (!gla::delta_config_built(dt, dk, dv, dv / dv_split))
-    return (dtype == GLA_F32 && (dk != 64 || dv != 64)) ? GLA_ERR_UNSUPPORTED : GLA_ERR_PLAN;
   const size_t es = elem_size(dtype);
   const size_t b_bytes = align_up((size_t)BH * T * 4);
   const size_t w_bytes = align_up((size_t)BH * T * dk * es);
   const size_t u_bytes = align_up((size_t)BH * T * dv * es);
-  const size_t need = std::max(b_bytes + w_bytes + u_bytes, kAlign);
+  const size_t h_bytes = pl.segments > 1 ? align_up((size_t)BH * (pl.segments - 1) * dk * dv * 4) : 0;
+  const size_t f_bytes = pl.segments > 1 ? align_up((size_t)BH * (pl.segments - 1) * dk * dk * 4) : 0;
+  const size_t need = std::max(b_bytes + w_bytes + u_bytes + h_bytes + f_bytes, kAlign);
   if (!workspace) {
     *workspace_bytes = need;
     return GLA_OK;
@@ -606,13 +641,16 @@ gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, co
   p.ST = S_T;
   p.W = w + b_bytes;
   p.U = w + b_bytes + w_bytes;
+  p.seg_state = pl.segments > 1 ? (float*)(w + b_bytes + w_bytes + u_bytes) : nullptr;
+  p.seg_phi = pl.segments > 1 ? (float*)(w + b_bytes + w_bytes + u_bytes + h_bytes) : nullptr;
   p.T = T;
   p.dk = dk;
   p.dv = dv;
   p.BH = (int)BH;
   p.nchunks = (int)n_chunks(T);
-  p.nslices = dv_split;
-  p.grid = (int)(BH * dv_split);
+  p.nslices = pl.dv_split;
+  p.segments = pl.segments;
+  p.grid = (int)(BH * pl.dv_split * pl.segments);
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
   if (T > 0) {
@@ -620,6 +658,7 @@ gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, co
                                 gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus,
                                 false, s);
     if (e == hipSuccess) e = gla::launch_delta_prep(p, dt, s);
+    if (e == hipSuccess) e = gla::launch_delta_segments(p, dt, s);
   }
   if (e == hipSuccess) e = gla::launch_delta_output(p, dt, s);
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;

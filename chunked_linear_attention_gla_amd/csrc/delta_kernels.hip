@@ -29,9 +29,14 @@
 //                       L, Tinv (fp32, 16x16 blocks: forward substitution on the
 //                       diagonal blocks, matrix-core products for the others),
 //                       W and Ut, written to the workspace in the operand dtype.
-//   delta_output_kernel one workgroup per (head, slice of value columns), chunks
-//                       in order: U = Ut - W S_0 on the matrix cores, then o and
-//                       the state update as in the linear-attention output pass.
+//   delta_segment_kernel for sequence segments: the affine map S_end = Phi S_start
+//                       + H of every segment but the last (Phi = prod of the chunk
+//                       transitions e^gamma I - (k e^{gamma-b})^T W, run as dk extra
+//                       columns from the identity with no writes).
+//   delta_output_kernel one workgroup per (head, slice of value columns, segment),
+//                       chunks in order from the folded start state: U = Ut - W S_0
+//                       on the matrix cores, then o and the state update as in the
+//                       linear-attention output pass.
 #include "chunk_common.h"
 
 namespace gla {
@@ -229,7 +234,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
 }
 
 // ============================================================================
-// Pass 2: the serial chunk loop.
+// Pass 2 (and the segment pre-pass): chunks in order.
 // ============================================================================
 template <typename T, int DK, int DVS>
 struct DoCfg {
@@ -256,11 +261,21 @@ struct DoSmem {
 };
 
 template <typename T, int DK, int DVS>
+struct DsSmem {
+  using C = DoCfg<T, DK, DVS>;
+  T wn[64 * C::QLD];
+  T kp[TokTile<T, DK>::SIZE];
+  T uu[TokTile<T, DVS>::SIZE];
+};
+
+// One chunk of (q,) k, W, Ut and b on its way to LDS / registers.  Ut lands directly
+// in the accumulator layout: ut[jb][e] = Ut[t0 + 16 jb + r16][wcol + 4 g + e].
+template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_U>
 struct DoStaged {
   using E = Elem<T>;
   using C = DoCfg<T, DK, DVS>;
-  typename E::Vec8 q[C::QU], k[C::QU], w[C::QU];
-  floatx4 ut[4];   // Ut[t0 + 16 jb + r16][wcol + 4 g + e]
+  typename E::Vec8 q[LOAD_Q ? C::QU : 1], k[C::QU], w[C::QU];
+  floatx4 ut[4];
   float b;
 
   __device__ __forceinline__ void load(const rsrc_t& rq, const rsrc_t& rk, const rsrc_t& rw, const rsrc_t& ru,
@@ -272,12 +287,16 @@ struct DoStaged {
     for (int m = 0; m < C::QU; ++m) {
       const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
       const uint32_t off = dl_row(t0 + row, Tn, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T);
-      q[m] = E::load8(rq, off);
+      if (LOAD_Q) q[m] = E::load8(rq, off);
       k[m] = E::load8(rk, off);
       w[m] = E::load8(rw, off);
     }
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
+      if (!LOAD_U) {
+        ut[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        continue;
+      }
       const uint32_t off = dl_row(t0 + jb * 16 + r16, Tn, (uint32_t)dv * (uint32_t)sizeof(T)) +
                            (wcol + 4 * g) * (uint32_t)sizeof(T);
       if constexpr (sizeof(T) == 2) {
@@ -294,9 +313,128 @@ struct DoStaged {
   }
 };
 
+// -W and k e^{gamma - b} of the staged chunk into LDS.
+template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_U>
+__device__ __forceinline__ void stage_w_kp(T* wn, T* kp, const DoStaged<T, DK, DVS, LOAD_Q, LOAD_U>& st,
+                                           const ChunkDecay& cd, int tid) {
+  using E = Elem<T>;
+  using C = DoCfg<T, DK, DVS>;
+#pragma unroll
+  for (int m = 0; m < C::QU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
+    E::store8_neg(wn + row * C::QLD + c8 * 8, st.w[m]);
+    TokTile<T, DK>::store8(kp, row, c8 * 8, st.k[m], exp_e(cd.gam - cd.at(row)));
+  }
+}
+
+// U = Ut - W S_0 for the wave's 16 columns (S_0 as operand fragments Sf), written to
+// the token-major LDS tile at slice column colr.
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void effective_writes(floatx4 (&ut)[4], const typename Elem<T>::Frag (&Sf)[DK / 32],
+                                                 const T* wn, T* uu, int colr, int lane) {
+  using E = Elem<T>;
+  using C = DoCfg<T, DK, DVS>;
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      E::mfma(ut[jb], Sf[ks], E::load_frag(wn + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+    // ut[jb][e] = U[16 jb + r16][colr + 4 g + e]
+    const int row = jb * 16 + r16;
+    if constexpr (sizeof(T) == 2) {
+      E::store4(uu + row * TokTile<T, DVS>::LD + colr + 4 * g, ut[jb][0], ut[jb][1], ut[jb][2], ut[jb][3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) uu[(colr + 4 * g + e) * TokTile<T, DVS>::LD + row] = ut[jb][e];
+    }
+  }
+}
+
+// S <- e^gamma S + (k e^{gamma - b})^T U
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void delta_state_update(floatx4 (&S)[DK / 16], const typename Elem<T>::Frag (&Uf)[2],
+                                                   const T* kp, float dec, int lane) {
+  using E = Elem<T>;
+  using C = DoCfg<T, DK, DVS>;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db) S[db] *= dec;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) E::mfma(S[db], TokTile<T, DK>::load(kp, ks * 32, db * 16, lane), Uf[ks]);
+}
+
+// Segment pre-pass: for every segment but the last, run its chunks from a zero
+// state (PHI = false: the local state H, value columns) or from the identity with
+// no writes (PHI = true: the segment's state transition, dk columns), i.e. the
+// affine map S_end = Phi S_start + H.  One workgroup per (head, segment, slice).
+template <typename T, int DK, int NCOL, bool PHI>
+__global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel(DeltaParams p) {
+  using E = Elem<T>;
+  using C = DoCfg<T, DK, NCOL>;
+  __shared__ DsSmem<T, DK, NCOL> sm;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int r16 = lane & 15, g = lane >> 4;
+  const int nseg = p.segments - 1;
+  const int ncol = PHI ? DK : p.dv;
+  const int nsl = ncol / NCOL;
+  const int L = xcd_linear_index(blockIdx.x, p.BH * nseg * nsl);
+  const int slice = L % nsl;
+  const int rest = L / nsl;
+  const int seg = rest % nseg;
+  const int bh = rest / nseg;
+  const int col0 = slice * NCOL;
+  const int wcol = col0 + wave * 16;
+  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
+  const uint32_t Tn = (uint32_t)p.T;
+  const uint32_t es = (uint32_t)sizeof(T);
+  const rsrc_t rk = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * es);
+  const rsrc_t rw = make_rsrc(static_cast<const T*>(p.W) + (long long)bh * p.T * DK, Tn * DK * es);
+  const rsrc_t ru = make_rsrc(static_cast<const T*>(p.U) + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * es);
+  const rsrc_t rb = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+
+  floatx4 S[C::DB];
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[db][e] = (PHI && db * 16 + 4 * g + e == wcol + r16) ? 1.0f : 0.0f;
+
+  DoStaged<T, DK, NCOL, false, !PHI> st;
+  if (c_begin < c_end) st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_begin * kChunk, wcol, tid);
+  for (int c = c_begin; c < c_end; ++c) {
+    const ChunkDecay cd(st.b);
+    floatx4 ut[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) ut[jb] = st.ut[jb];
+    stage_w_kp<T, DK, NCOL, false, !PHI>(sm.wn, sm.kp, st, cd, tid);
+    st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, wcol, tid);
+    __syncthreads();
+    typename E::Frag Sf[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
+    effective_writes<T, DK, NCOL>(ut, Sf, sm.wn, sm.uu, wave * 16, lane);
+    __syncthreads();
+    typename E::Frag Uf[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) Uf[ks] = TokTile<T, NCOL>::load(sm.uu, ks * 32, wave * 16, lane);
+    delta_state_update<T, DK, NCOL>(S, Uf, sm.kp, exp_e(cd.gam), lane);
+    __syncthreads();
+  }
+  float* dst = PHI ? p.seg_phi + ((long long)bh * nseg + seg) * DK * DK
+                   : p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv;
+#pragma unroll
+  for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dst[(long long)(db * 16 + 4 * g + e) * ncol + wcol + r16] = S[db][e];
+}
+
 template <typename T, int DK, int DVS>
 __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(DeltaParams p) {
   using E = Elem<T>;
+  using F = Elem<float>;
   using C = DoCfg<T, DK, DVS>;
   __shared__ DoSmem<T, DK, DVS> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -304,9 +442,13 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
   const int r16 = lane & 15, g = lane >> 4;
   const int L = xcd_linear_index(blockIdx.x, p.grid);
   const int slice = L % p.nslices;
-  const int bh = L / p.nslices;
+  const int rest = L / p.nslices;
+  const int seg = rest % p.segments;
+  const int bh = rest / p.segments;
   const int col0 = slice * DVS;
   const int wcol = col0 + wave * 16;
+  const int c_begin = (int)((long long)seg * p.nchunks / p.segments);
+  const int c_end = (int)((long long)(seg + 1) * p.nchunks / p.segments);
   const uint32_t Tn = (uint32_t)p.T;
   const uint32_t es = (uint32_t)sizeof(T);
   const rsrc_t rq = make_rsrc(static_cast<const T*>(p.q) + (long long)bh * p.T * DK, Tn * DK * es);
@@ -316,7 +458,8 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
   const rsrc_t rb = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
   const rsrc_t ro = make_rsrc(p.o + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * 4u);
 
-  // state slice of the wave: S[16 db + 4 g + e][wcol + r16]
+  // ---- initial state: S0 (or zero), then S <- Phi_p S + H_p over the earlier
+  //      segments, in fp32 on the matrix cores.  Slice of the wave: S[16 db + 4 g + e][wcol + r16]
   floatx4 S[C::DB];
 #pragma unroll
   for (int db = 0; db < C::DB; ++db)
@@ -325,14 +468,37 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       const long long i = (long long)bh * DK * p.dv + (long long)(db * 16 + 4 * g + e) * p.dv + wcol + r16;
       S[db][e] = p.S0 ? p.S0[i] : 0.0f;
     }
+  for (int ps = 0; ps < seg; ++ps) {
+    const float* Phi = p.seg_phi + ((long long)bh * (p.segments - 1) + ps) * DK * DK;
+    const float* Hs = p.seg_state + ((long long)bh * (p.segments - 1) + ps) * DK * p.dv;
+    floatx4 N[C::DB];
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db) N[db] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+      const F::Frag sf = F::from_acc(S[2 * ks], S[2 * ks + 1]);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        const float* row = Phi + (long long)(db * 16 + r16) * DK + ks * 32 + 4 * g;
+        F::Frag pf;
+        pf.lo = *reinterpret_cast<const floatx4*>(row);
+        pf.hi = *reinterpret_cast<const floatx4*>(row + 16);
+        F::mfma(N[db], pf, sf);  // N[db][e] = (Phi S)[16 db + 4 g + e][wcol + r16]
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[db][e] = N[db][e] + Hs[(long long)(db * 16 + 4 * g + e) * p.dv + wcol + r16];
+  }
   for (int e = tid; e < 2 * 256; e += C::NT) {
     const int blk = e >> 8, rr = (e >> 4) & 15, cc = e & 15;
     sm.a[(blk * 32 + rr) * C::TLD + blk * 32 + 16 + cc] = E::cvt(0.0f);
   }
 
-  DoStaged<T, DK, DVS> st;
-  if (p.nchunks > 0) st.load(rq, rk, rw, ru, rb, Tn, p.dv, 0, wcol, tid);
-  for (int c = 0; c < p.nchunks; ++c) {
+  DoStaged<T, DK, DVS, true, true> st;
+  if (c_begin < c_end) st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_begin * kChunk, wcol, tid);
+  for (int c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)c * kChunk;
     const ChunkDecay cd(st.b);
     floatx4 ut[4];
@@ -345,11 +511,10 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       const float br = cd.at(row), r = cd.r(row >> 4);
       E::store8_scaled(sm.qh + row * C::QLD + c8 * 8, st.q[m], exp_e(br - r));
       E::store8_scaled(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(r - br));
-      E::store8_neg(sm.wn + row * C::QLD + c8 * 8, st.w[m]);
-      TokTile<T, DK>::store8(sm.kp, row, c8 * 8, st.k[m], exp_e(cd.gam - br));
     }
+    stage_w_kp<T, DK, DVS, true, true>(sm.wn, sm.kp, st, cd, tid);
     // ---- (2) prefetch chunk c + 1 (the last iteration re-reads its own chunk)
-    st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, p.nchunks - 1) * kChunk, wcol, tid);
+    st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, wcol, tid);
     __syncthreads();
 
     // ---- (3) A over the 10 causal tiles
@@ -379,20 +544,11 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       for (int jb = 0; jb < 4; ++jb) {
         O[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
+        for (int ks = 0; ks < C::KS; ++ks)
           E::mfma(O[jb], Sf[ks], E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
-          E::mfma(ut[jb], Sf[ks], E::load_frag(sm.wn + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
-        }
         if (jb > 0) O[jb] *= exp_e(cd.r(jb));
-        // ut[jb][e] = U[16 jb + r16][wcol + 4 g + e]
-        const int row = jb * 16 + r16, colr = wcol - col0 + 4 * g;
-        if constexpr (sizeof(T) == 2) {
-          E::store4(sm.uu + row * TokTile<T, DVS>::LD + colr, ut[jb][0], ut[jb][1], ut[jb][2], ut[jb][3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sm.uu[(colr + e) * TokTile<T, DVS>::LD + row] = ut[jb][e];
-        }
       }
+      effective_writes<T, DK, DVS>(ut, Sf, sm.wn, sm.uu, wave * 16, lane);
     }
     __syncthreads();
 
@@ -406,24 +562,20 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
 #pragma unroll
         for (int ks = 0; ks <= jb / 2; ++ks)
           E::mfma(O[jb], Uf[ks], E::load_frag(sm.a + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
-      const float dec = exp_e(cd.gam);
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) S[db] *= dec;
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) E::mfma(S[db], TokTile<T, DK>::load(sm.kp, ks * 32, db * 16, lane), Uf[ks]);
+      delta_state_update<T, DK, DVS>(S, Uf, sm.kp, exp_e(cd.gam), lane);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
         buf_store16(ro, dl_row(t0 + jb * 16 + r16, Tn, (uint32_t)p.dv * 4u) + (wcol + 4 * g) * 4u, O[jb]);
     }
     __syncthreads();
   }
+  if (seg == p.segments - 1) {
 #pragma unroll
-  for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      p.ST[(long long)bh * DK * p.dv + (long long)(db * 16 + 4 * g + e) * p.dv + wcol + r16] = S[db][e];
+      for (int e = 0; e < 4; ++e)
+        p.ST[(long long)bh * DK * p.dv + (long long)(db * 16 + 4 * g + e) * p.dv + wcol + r16] = S[db][e];
+  }
 }
 
 }  // namespace
@@ -452,6 +604,30 @@ hipError_t launch_delta_prep(const DeltaParams& p, int dtype, hipStream_t stream
     else return hipErrorInvalidValue;
   }
 #undef GLA_DP
+  return hipGetLastError();
+}
+
+// Segment pre-pass: 64-column slices of the local states (dv columns) and of the
+// transitions (dk columns).
+hipError_t launch_delta_segments(const DeltaParams& p, int dtype, hipStream_t stream) {
+  if (p.segments <= 1) return hipSuccess;
+  const long long units = (long long)p.BH * (p.segments - 1);
+  const long long gh = units * (p.dv / 64), gp = units * (p.dk / 64);
+  if (gh > 0x7FFFFFFFLL || gp > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+#define GLA_DS(TT, DKV)                                                                                         \
+  do {                                                                                                          \
+    hipLaunchKernelGGL((delta_segment_kernel<TT, DKV, 64, false>), dim3((unsigned)gh), dim3(256), 0, stream, p); \
+    hipLaunchKernelGGL((delta_segment_kernel<TT, DKV, 64, true>), dim3((unsigned)gp), dim3(256), 0, stream, p);  \
+  } while (0)
+  if (dtype == 0) {
+    if (p.dk == 128) GLA_DS(bf16, 128);
+    else if (p.dk == 64) GLA_DS(bf16, 64);
+    else return hipErrorInvalidValue;
+  } else {
+    if (p.dk == 64) GLA_DS(float, 64);
+    else return hipErrorInvalidValue;
+  }
+#undef GLA_DS
   return hipGetLastError();
 }
 

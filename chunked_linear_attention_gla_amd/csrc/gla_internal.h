@@ -116,14 +116,18 @@ struct DeltaParams {
   float* ST;              // [BH][dk][dv]
   void* W;                // [BH][T][dk] operand dtype: Tinv diag(beta e^b) K per chunk
   void* U;                // [BH][T][dv] operand dtype: Tinv diag(beta) V per chunk
+  float* seg_state;       // [BH][segments-1][dk][dv] local final state of each segment
+  float* seg_phi;         // [BH][segments-1][dk][dk] state transition of each segment
   long long T;
   int dk, dv;
   int BH;
   int nchunks;
   int nslices;
+  int segments;
   int grid;
 };
 bool delta_config_built(int dtype, int dk, int dv, int slice);
+hipError_t launch_delta_segments(const DeltaParams& p, int dtype, hipStream_t stream);
 hipError_t launch_delta_prep(const DeltaParams& p, int dtype, hipStream_t stream);
 hipError_t launch_delta_output(const DeltaParams& p, int dtype, hipStream_t stream);
 

@@ -229,16 +229,24 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
  * matrix come from the unified 16-token-tile product (no diagonal branch).
  *   beta [B][H][T] fp32 (a write strength, normally in [0, 1]); other arguments as
  *   for gla_chunk_fwd (S0 may be NULL).
- *   dv_split: value columns are split into dv / dv_split slices, one workgroup per
- *   (head, slice) running the chunks in order; 0 = default for this device.
+ *   plan: NULL = gla_plan_default_delta; dv_split value-column slices (one
+ *   workgroup per head, slice and segment; 16 columns per wave), segments as in
+ *   gla_chunk_fwd.  Segments after the first start from S0 folded with the earlier
+ *   segments' affine maps S_end = Phi S_start + H, computed by a pre-pass (Phi is the
+ *   product of the chunk transitions e^gamma I - (k e^{gamma-b})^T W, dk x dk).
  * Built: bf16 with dk, dv in {64, 128} and slices of 32, 64 or 128 columns; fp32
  * with dk = dv = 64 and slices of 32 or 64.  Others: GLA_ERR_UNSUPPORTED or
- * GLA_ERR_PLAN.  The workspace holds b and the per-chunk W, U (operand dtype);
- * workspace == NULL returns its size.  Errors and validation as gla_chunk_fwd. */
+ * GLA_ERR_PLAN.  The workspace holds b, the per-chunk W, U (operand dtype) and the
+ * segment maps; workspace == NULL returns its size.  Errors and validation as
+ * gla_chunk_fwd. */
+gla_status_t gla_plan_default_delta(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                                    gla_plan_t* plan);
+gla_status_t gla_plan_check_delta(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
+                                  const gla_plan_t* plan);
 gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, const float* x,
                                  const float* beta, const float* S0, float* o, float* S_T,
                                  int B, int H, long long T, int dk, int dv,
-                                 gla_dtype_t dtype, gla_gate_t gate, int dv_split,
+                                 gla_dtype_t dtype, gla_gate_t gate, const gla_plan_t* plan,
                                  void* workspace, size_t* workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

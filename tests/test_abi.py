@@ -276,21 +276,25 @@ def test_delta_validation_and_workspace_query(lib):
     def dl(**kw):
         return lib.gla_chunk_fwd_delta(kw.get("q", 0x1000), 0x2000, 0x3000, 0x4000, kw.get("beta", 0x5000), None,
                                        0x6000, 0x7000, 1, 2, kw.get("T", 100), kw.get("dk", 64), kw.get("dv", 64),
-                                       kw.get("dtype", BF16), kw.get("gate", BOUNDED), kw.get("split", 2),
+                                       kw.get("dtype", BF16), kw.get("gate", BOUNDED), P(*kw.get("plan", (1, 2))),
                                        kw.get("ws", None), kw.get("nb", ctypes.byref(n)), None)
     assert dl(nb=None) == NULL
     assert dl(dk=96) == SHAPE
     assert dl(dtype=4) == DTYPE
     assert dl(gate=7) == ARG
-    assert dl(split=3) == PLAN
-    assert dl(split=4) == PLAN          # 16-column slices are not built
-    assert dl(dtype=F32, dk=128, dv=64, split=1) == UNSUP
-    assert dl() == OK                   # explicit split: size query without a device
+    assert dl(plan=(1, 3)) == PLAN
+    assert dl(plan=(1, 4)) == PLAN          # 16-column slices are not built
+    assert dl(plan=(3, 1)) == PLAN          # 100 tokens are 2 chunks
+    assert dl(dtype=F32, dk=128, dv=64, plan=(1, 1)) == UNSUP
+    assert lib.gla_plan_check_delta(1, 2, 1000, 128, 128, BF16, P(8, 1)) == OK
+    assert dl() == OK                       # explicit plan: size query without a device
     es = 2
     align = lambda b: (b + 255) // 256 * 256
     assert n.value == align(2 * 100 * 4) + align(2 * 100 * 64 * es) + align(2 * 100 * 64 * es)
+    assert dl(plan=(2, 1)) == OK            # two segments add one local state and one transition per head
+    assert n.value == (align(2 * 100 * 4) + 2 * align(2 * 100 * 64 * es) + align(2 * 64 * 64 * 4)
+                       + align(2 * 64 * 64 * 4))
     need = n.value
-    n.value = need
-    assert dl(ws=0x10000000, beta=None) == NULL
+    assert dl(plan=(2, 1), ws=0x10000000, beta=None) == NULL
     n.value = need - 1
-    assert dl(ws=0x10000000) == WORKSPACE
+    assert dl(plan=(2, 1), ws=0x10000000) == WORKSPACE

@@ -29,9 +29,9 @@ def oracle_delta(inp, gate="bounded"):
                                 gate=gate)
 
 
-def check(w, inp, dv_split=0, gate="bounded", tol=None):
+def check(w, inp, plan=None, gate="bounded", tol=None):
     o, ST = gla.chunk_fwd_delta(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["S0"], gate=gate,
-                                dv_split=dv_split)
+                                plan=plan)
     torch.cuda.synchronize()
     o_ref, S_ref = oracle_delta(inp, gate)
     B, H, T, dv = o.shape
@@ -77,13 +77,36 @@ def test_zero_write_strength_only_decays():
                                          (64, 64, 2)])
 def test_head_dims_and_slices(dk, dv, split):
     w, inp = make(64 * 5 + 9, dk=dk, dv=dv)
-    check(w, inp, dv_split=split)
+    check(w, inp, plan=gla.Plan(1, split))
+
+
+@pytest.mark.parametrize("segments,split", [(2, 1), (3, 2), (8, 1), (5, 4)])
+def test_segmented_plans(segments, split):
+    """Segments after the first start from S0 folded with the earlier segments'
+    affine maps; weak decay so the carried state matters."""
+    w, inp = make(64 * 24 + 11, H=2, x_mean=-5.0)
+    check(w, inp, plan=gla.Plan(segments, split))
+
+
+def test_segmented_pure_delta_rule():
+    """beta = 1, a = 1: the segment transitions are products of projections."""
+    w, inp = make(64 * 16 + 3, H=2)
+    inp["beta"].fill_(1.0)
+    inp["x"].fill_(float("-inf"))
+    check(w, inp, plan=gla.Plan(4, 1))
+
+
+def test_default_plan_long_sequence():
+    w, inp = make(64 * 64 + 31, H=2, x_mean=-4.0, s0=0.0)
+    inp["S0"] = None
+    check(w, inp)
 
 
 def test_fp32_path():
     w, inp = make(64 * 4 + 3, H=2, dk=64, dv=64, qkv="f32")
     check(w, inp)
-    check(w, inp, dv_split=2)
+    check(w, inp, plan=gla.Plan(1, 2))
+    check(w, inp, plan=gla.Plan(3, 1))
 
 
 def test_without_initial_state_and_softplus_gate():
