@@ -90,15 +90,26 @@ struct PrepCfg {
   static constexpr int MLD = 65;
 };
 
+// LDS regions are reused across the phases of the pass (keys for L, then the
+// right-hand sides of the products; M, then Tinv in the operand dtype), which keeps
+// two workgroups on a compute unit.
 template <typename T, int DK, int DV>
 struct PrepSmem {
   using C = PrepCfg<T, DK, DV>;
-  T kq[64 * C::QLD];              // k_t e^{b_t - r_u(t)}
-  T kh[64 * C::QLD];              // k_s e^{r_u(s) - b_s}
-  T kb[TokTile<T, DK>::SIZE];     // beta_s e^{b_s} k_s, token-major
-  T vb[TokTile<T, DV>::SIZE];     // beta_s v_s, token-major
-  T tb[64 * C::TLD];              // Tinv in the operand dtype
-  float mf[64][C::MLD];           // M = diag(beta) L (strictly lower)
+  union {
+    struct {
+      T kq[64 * C::QLD];          // k_t e^{b_t - r_u(t)}
+      T kh[64 * C::QLD];          // k_s e^{r_u(s) - b_s}
+    } l;
+    struct {
+      T kb[TokTile<T, DK>::SIZE]; // beta_s e^{b_s} k_s, token-major
+      T vb[TokTile<T, DV>::SIZE]; // beta_s v_s, token-major
+    } r;
+  } u1;
+  union {
+    float mf[64][C::MLD];         // M = diag(beta) L (strictly lower)
+    T tb[64 * C::TLD];            // Tinv in the operand dtype
+  } u2;
   float tf[64][C::MLD];           // Tinv (fp32)
   float scr[4][16][17];
   float sb[64];
@@ -144,14 +155,8 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
     const float br = sm.sb[row], r = ref(row >> 4);
-    E::store8_scaled(sm.kq + row * C::QLD + c8 * 8, kv[m], exp_e(br - r));
-    E::store8_scaled(sm.kh + row * C::QLD + c8 * 8, kv[m], exp_e(r - br));
-    TokTile<T, DK>::store8(sm.kb, row, c8 * 8, kv[m], sm.sbeta[row] * exp_e(br));
-  }
-#pragma unroll
-  for (int m = 0; m < C::VU; ++m) {
-    const int u = tid + m * C::NT, row = u / (DV / 8), c8 = u % (DV / 8);
-    TokTile<T, DV>::store8(sm.vb, row, c8 * 8, vv[m], sm.sbeta[row]);
+    E::store8_scaled(sm.u1.l.kq + row * C::QLD + c8 * 8, kv[m], exp_e(br - r));
+    E::store8_scaled(sm.u1.l.kh + row * C::QLD + c8 * 8, kv[m], exp_e(r - br));
   }
   __syncthreads();
 
@@ -163,14 +168,14 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      E::mfma(acc, E::load_frag(sm.kh + (ib * 16 + r16) * C::QLD, ks * 32 + 4 * g),
-              E::load_frag(sm.kq + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+      E::mfma(acc, E::load_frag(sm.u1.l.kh + (ib * 16 + r16) * C::QLD, ks * 32 + 4 * g),
+              E::load_frag(sm.u1.l.kq + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
     // acc[e]: row t = 16 jb + r16, column s = 16 ib + 4 g + e
     const int tr = jb * 16 + r16;
     const float f = (jb == ib ? 1.0f : exp_e(ref(jb) - ref(ib))) * sm.sbeta[tr];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      sm.mf[tr][ib * 16 + 4 * g + e] = (jb != ib || 4 * g + e < r16) ? acc[e] * f : 0.0f;
+      sm.u2.mf[tr][ib * 16 + 4 * g + e] = (jb != ib || 4 * g + e < r16) ? acc[e] * f : 0.0f;
   }
   __syncthreads();
 
@@ -182,7 +187,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     for (int i = 0; i < 16; ++i) {
       float s = (i == j) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int q = 0; q < i; ++q) s -= sm.mf[o + i][o + q] * x[q];
+      for (int q = 0; q < i; ++q) s -= sm.u2.mf[o + i][o + q] * x[q];
       x[i] = s;
     }
 #pragma unroll
@@ -195,7 +200,8 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     const int I = wave, J = wave - dist;
     if (J >= 0) {  // wave-uniform
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int K = J; K < I; ++K) mm16(acc, &sm.mf[16 * I][16 * K], C::MLD, &sm.tf[16 * K][16 * J], C::MLD, lane);
+      for (int K = J; K < I; ++K)
+        mm16(acc, &sm.u2.mf[16 * I][16 * K], C::MLD, &sm.tf[16 * K][16 * J], C::MLD, lane);
       store16(&sm.scr[I][0][0], 17, acc, 1.0f, lane);
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
       mm16(x, &sm.tf[16 * I][16 * I], C::MLD, &sm.scr[I][0][0], 17, lane);
@@ -203,10 +209,21 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     }
     __syncthreads();
   }
-  // operand copy of Tinv, zero above the diagonal blocks
+  // operand copy of Tinv (over M, no longer read), zero above the diagonal blocks;
+  // right-hand sides of the products (over the keys for L, no longer read)
   for (int e = tid; e < 64 * 64; e += C::NT) {
     const int t = e >> 6, s = e & 63;
-    sm.tb[t * C::TLD + s] = E::cvt((s >> 4) <= (t >> 4) ? sm.tf[t][s] : 0.0f);
+    sm.u2.tb[t * C::TLD + s] = E::cvt((s >> 4) <= (t >> 4) ? sm.tf[t][s] : 0.0f);
+  }
+#pragma unroll
+  for (int m = 0; m < C::QU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
+    TokTile<T, DK>::store8(sm.u1.r.kb, row, c8 * 8, kv[m], sm.sbeta[row] * exp_e(sm.sb[row]));
+  }
+#pragma unroll
+  for (int m = 0; m < C::VU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DV / 8), c8 = u % (DV / 8);
+    TokTile<T, DV>::store8(sm.u1.r.vb, row, c8 * 8, vv[m], sm.sbeta[row]);
   }
   __syncthreads();
 
@@ -222,15 +239,15 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
         for (int ks = 0; ks <= jb / 2; ++ks)
           E::mfma(acc, ncol == DK ? TokTile<T, DK>::load(tile, ks * 32, cb, lane)
                                   : TokTile<T, DV>::load(tile, ks * 32, cb, lane),
-                  E::load_frag(sm.tb + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
+                  E::load_frag(sm.u2.tb + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
         // acc[e] = X[t0 + 16 jb + r16][cb + 4 g + e]
         const long long t = (long long)t0 + jb * 16 + r16;
         if (t < p.T) store_row4<T>(dst + t * ld + cb + 4 * g, acc);
       }
     }
   };
-  product(sm.kb, DK, Wg, DK);
-  product(sm.vb, DV, Ug, DV);
+  product(sm.u1.r.kb, DK, Wg, DK);
+  product(sm.u1.r.vb, DV, Ug, DV);
 }
 
 // ============================================================================
