@@ -38,22 +38,35 @@ namespace gla {
 
 namespace {
 
+// 16 value columns per wave; in staging, HALVES waves share one 16-token tile of
+// the chunk, each taking DK / HALVES of its columns.
 template <typename T, int DK, int DVS>
 struct PcCfg {
-  static constexpr int NW = 4;                 // waves: one 16-token tile each in staging
+  static constexpr int HALVES = DVS / 64;      // waves staging one tile
+  static constexpr int NW = 4 * HALVES;
   static constexpr int NT = 64 * NW;
-  static constexpr int CPW = DVS / NW;         // value columns per wave
-  static constexpr int NB = CPW / 16;          // 16-column blocks per wave
+  static constexpr int CPW = DVS / NW;         // value columns per wave (16)
+  static constexpr int NB = CPW / 16;          // 16-column blocks per wave (1)
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int QLD = DK + PAD;
   static constexpr int TLD = 64 + PAD;
   static constexpr int C8 = DK / 8;            // 8-column groups of a row
-  static constexpr int RG = 64 / C8;           // lanes of one column group within a tile
+  static constexpr int C8W = C8 / HALVES;      // ... staged by one wave
+  static constexpr int RG = 64 / C8W;          // lanes of one column group within a tile
   static constexpr int R = 16 / RG;            // rows of the tile per lane
   static constexpr int VU = 8 * DVS / NT;      // 8-element v units per thread
   static constexpr int DB = DK / 16;
   static constexpr int KS = DK / 32;
-  static_assert(NB >= 1 && NB <= 2 && R >= 1 && VU >= 1, "unsupported shape");
+  static_assert(NB == 1 && R >= 1 && VU >= 1 && C8W >= 1, "unsupported shape");
+};
+
+// Staging position of a lane: the tile its wave stages, its 8-column group and its
+// row group within the tile (rows rg * R .. rg * R + R - 1).
+template <typename C>
+struct PcLane {
+  int tile, c8, rg;
+  __device__ __forceinline__ PcLane(int wave, int lane)
+      : tile(wave & 3), c8((wave >> 2) * C::C8W + lane % C::C8W), rg(lane / C::C8W) {}
 };
 
 template <typename T, int DK, int DVS>
@@ -99,10 +112,11 @@ struct PcStaged {
 
   __device__ __forceinline__ void load(const PcBuffers& hb, uint32_t Tn, int dv, uint32_t t0, int col0, int wave,
                                        int lane, int tid) {
-    const int c8 = lane % C::C8, rg = lane / C::C8;
+    const PcLane<C> pl(wave, lane);
+    const int c8 = pl.c8;
 #pragma unroll
     for (int m = 0; m < C::R; ++m) {
-      const uint32_t t = t0 + 16 * wave + rg * C::R + m;
+      const uint32_t t = t0 + 16 * pl.tile + pl.rg * C::R + m;
       const uint32_t off = pc_row(t, Tn, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T);
       if (LOAD_Q) q[m] = E::load8(hb.q, off);
       k[m] = E::load8(hb.k, off);
@@ -135,16 +149,17 @@ __device__ __forceinline__ float f4_get(const float4& v, int e) {
 
 // Tile-local inclusive cumulative log-decay lam.v[m][e] = b - r_u of the lane's rows
 // (row rg*R + m of the wave's tile, channel 8*c8 + e); absent tokens have g = 0.
-// The lanes of the tile's last row group publish the tile totals to tau[wave].
+// The lanes of the tile's last row group publish the tile totals to tau[tile].
 template <typename T, int DK, int DVS, bool LOAD_Q>
 __device__ __forceinline__ void tile_log_decay(PcLam<T, DK, DVS>& lam,
                                                const PcStaged<T, DK, DVS, LOAD_Q>& st, float (*tau)[DK],
                                                uint32_t t0, uint32_t Tn, int gate, int wave, int lane) {
   using C = PcCfg<T, DK, DVS>;
-  const int c8 = lane % C::C8, rg = lane / C::C8;
+  const PcLane<C> pl(wave, lane);
+  const int c8 = pl.c8, rg = pl.rg;
 #pragma unroll
   for (int m = 0; m < C::R; ++m) {
-    const bool valid = t0 + 16 * wave + rg * C::R + m < Tn;
+    const bool valid = t0 + 16 * pl.tile + rg * C::R + m < Tn;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float xv = f4_get(st.x[m][e >> 2], e & 3);
@@ -158,7 +173,7 @@ __device__ __forceinline__ void tile_log_decay(PcLam<T, DK, DVS>& lam,
     const float tot = lam.v[C::R - 1][e];
     float incl = tot;
 #pragma unroll
-    for (int off = C::C8; off < 64; off <<= 1) {
+    for (int off = C::C8W; off < 64; off <<= 1) {
       const float y = __shfl_up(incl, off);
       if (lane >= off) incl += y;
     }
@@ -167,9 +182,9 @@ __device__ __forceinline__ void tile_log_decay(PcLam<T, DK, DVS>& lam,
     for (int m = 0; m < C::R; ++m) lam.v[m][e] += ex;
   }
   if (rg == C::RG - 1) {
-    *reinterpret_cast<float4*>(&tau[wave][c8 * 8]) =
+    *reinterpret_cast<float4*>(&tau[pl.tile][c8 * 8]) =
         make_float4(lam.v[C::R - 1][0], lam.v[C::R - 1][1], lam.v[C::R - 1][2], lam.v[C::R - 1][3]);
-    *reinterpret_cast<float4*>(&tau[wave][c8 * 8 + 4]) =
+    *reinterpret_cast<float4*>(&tau[pl.tile][c8 * 8 + 4]) =
         make_float4(lam.v[C::R - 1][4], lam.v[C::R - 1][5], lam.v[C::R - 1][6], lam.v[C::R - 1][7]);
   }
 }
@@ -186,21 +201,22 @@ __device__ __forceinline__ void read_tau(float (&tv)[4][8], const float (*tau)[D
   }
 }
 
-// k_i e^{gamma - b_i} (token-major) for the wave's tile and, from the lanes of wave 0
-// and row group 0 (which together cover every channel once), e^{gamma}.
+// k_i e^{gamma - b_i} (token-major) for the wave's tile and, from the lanes of tile 0's
+// waves and row group 0 (which together cover every channel once), e^{gamma}.
 template <typename T, int DK, int DVS, bool LOAD_Q>
 __device__ __forceinline__ void stage_state_side(T* kp, float* eg, const PcStaged<T, DK, DVS, LOAD_Q>& st,
                                                  const PcLam<T, DK, DVS>& lam,
                                                  const float (&tv)[4][8], int wave, int lane) {
   using C = PcCfg<T, DK, DVS>;
-  const int c8 = lane % C::C8, rg = lane / C::C8;
-  float G[8];  // sum of the totals of this tile and the later ones: gamma - r_wave
+  const PcLane<C> pl(wave, lane);
+  const int c8 = pl.c8, rg = pl.rg;
+  float G[8];  // sum of the totals of this tile and the later ones: gamma - r_tile
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     float s = 0.0f;
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      if (u >= wave) s += tv[u][e];
+      if (u >= pl.tile) s += tv[u][e];
     G[e] = s;
   }
 #pragma unroll
@@ -208,9 +224,9 @@ __device__ __forceinline__ void stage_state_side(T* kp, float* eg, const PcStage
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = exp_e(G[e] - lam.v[m][e]);
-    TokTile<T, DK>::store8_v(kp, 16 * wave + rg * C::R + m, c8 * 8, st.k[m], f);
+    TokTile<T, DK>::store8_v(kp, 16 * pl.tile + rg * C::R + m, c8 * 8, st.k[m], f);
   }
-  if (wave == 0 && rg == 0) {
+  if (pl.tile == 0 && rg == 0) {
     float f[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) f[e] = exp_e(G[e]);
@@ -290,7 +306,7 @@ __device__ __forceinline__ void pc_store_state(const PcState<T, DK, DVS>& S, flo
 // of every segment but the last.
 // ============================================================================
 template <typename T, int DK, int DVS>
-__global__ void __launch_bounds__(256) pc_segment_state_kernel(PcParams p) {
+__global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_segment_state_kernel(PcParams p) {
   using C = PcCfg<T, DK, DVS>;
   __shared__ PcSegSmem<T, DK, DVS> sm;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -318,7 +334,8 @@ __global__ void __launch_bounds__(256) pc_segment_state_kernel(PcParams p) {
   for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) S.s[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float gsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // wave 0, row group 0: segment log-decay
+  float gsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // tile 0, row group 0: segment log-decay
+  const PcLane<C> pl(wave, lane);
 
   PcStaged<T, DK, DVS, false> st;
   if (c_begin < c_end) st.load(hb, Tn, p.dv, (uint32_t)c_begin * kChunk, col0, wave, lane, tid);
@@ -328,7 +345,7 @@ __global__ void __launch_bounds__(256) pc_segment_state_kernel(PcParams p) {
     tile_log_decay<T, DK, DVS, false>(lam, st, sm.tau, t0, Tn, p.gate, wave, lane);
     __syncthreads();
     float tv[4][8];
-    read_tau<DK>(tv, sm.tau, (lane % C::C8) * 8);
+    read_tau<DK>(tv, sm.tau, pl.c8 * 8);
     stage_state_side<T, DK, DVS, false>(sm.kp, sm.eg, st, lam, tv, wave, lane);
     stage_v<T, DK, DVS, false>(sm.vv, st, tid);
 #pragma unroll
@@ -341,8 +358,8 @@ __global__ void __launch_bounds__(256) pc_segment_state_kernel(PcParams p) {
     __syncthreads();
   }
   pc_store_state<T, DK, DVS>(S, p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv, p.dv, wcol, g, r16);
-  if (slice == 0 && wave == 0 && lane < C::C8) {
-    float* dst = p.seg_decay + ((long long)bh * p.segments + seg) * DK + lane * 8;
+  if (slice == 0 && pl.tile == 0 && pl.rg == 0) {
+    float* dst = p.seg_decay + ((long long)bh * p.segments + seg) * DK + pl.c8 * 8;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dst[e] = gsum[e];
   }
@@ -352,14 +369,15 @@ __global__ void __launch_bounds__(256) pc_segment_state_kernel(PcParams p) {
 // Fused output pass.
 // ============================================================================
 template <typename T, int DK, int DVS>
-__global__ void __launch_bounds__(256) pc_chunk_output_kernel(PcParams p) {
+__global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kernel(PcParams p) {
   using E = Elem<T>;
   using C = PcCfg<T, DK, DVS>;
   __shared__ PcSmem<T, DK, DVS> sm;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int c8 = lane % C::C8, rg = lane / C::C8;
+  const PcLane<C> pl(wave, lane);
+  const int c8 = pl.c8, rg = pl.rg, tile = pl.tile;
   const int L = xcd_linear_index(blockIdx.x, p.grid);
   const int slice = L % p.nslices;
   const int rest = L / p.nslices;
@@ -425,7 +443,7 @@ __global__ void __launch_bounds__(256) pc_chunk_output_kernel(PcParams p) {
       float f[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = exp_e(lam.v[m][e]);
-      E::store8_vscaled(sm.qh + (16 * wave + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f);
+      E::store8_vscaled(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f);
     }
     __syncthreads();
 
@@ -435,28 +453,28 @@ __global__ void __launch_bounds__(256) pc_chunk_output_kernel(PcParams p) {
       read_tau<DK>(tv, sm.tau, c8 * 8);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (u < wave) continue;  // wave-uniform: key tile `wave` serves query tiles u >= wave
-        float D[8];              // r_u - r_wave
+        if (u < tile) continue;  // wave-uniform: key tile `tile` serves query tiles u >= tile
+        float D[8];              // r_u - r_tile
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           float s = 0.0f;
 #pragma unroll
           for (int w = 0; w < 4; ++w)
-            if (w >= wave && w < u) s += tv[w][e];
+            if (w >= tile && w < u) s += tv[w][e];
           D[e] = s;
         }
-        T* tile = sm.kt + (u * (u + 1) / 2 + wave) * 16 * C::QLD;
+        T* kt = sm.kt + (u * (u + 1) / 2 + tile) * 16 * C::QLD;
 #pragma unroll
         for (int m = 0; m < C::R; ++m) {
           float f[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) f[e] = exp_e(D[e] - lam.v[m][e]);
-          E::store8_vscaled(tile + (rg * C::R + m) * C::QLD + c8 * 8, st.k[m], f);
+          E::store8_vscaled(kt + (rg * C::R + m) * C::QLD + c8 * 8, st.k[m], f);
         }
       }
       stage_state_side<T, DK, DVS, true>(sm.kp, sm.eg, st, lam, tv, wave, lane);
       stage_v<T, DK, DVS, true>(sm.vv, st, tid);
-      if (wave == 1 && rg == 0) {
+      if (tile == 1 && rg == 0) {
         float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
