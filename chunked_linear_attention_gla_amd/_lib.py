@@ -70,7 +70,7 @@ _SIGS = {
                               _vp, _psz, _vp]),
     "gla_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _i, _vp]),
     "gla_chunk_fwd_varlen": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _ll, _i, _i, _i, _i, _i,
-                                  _vp, _psz, _vp]),
+                                  _pplan, _vp, _psz, _vp]),
     "gla_plan_default_delta": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
     "gla_plan_check_delta": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
     "gla_chunk_fwd_delta": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan, _vp,
@@ -355,14 +355,15 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tens
 
 def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor, cu_seqlens: torch.Tensor,
                      max_seqlen: int, S0: Optional[torch.Tensor] = None, gate="bounded", path="unified",
-                     o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
+                     plan: Optional[Plan] = None, o: Optional[torch.Tensor] = None, S_T: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     """Forward over packed sequences: returns (o [H, T, dv] fp32, S_T [N, H, dk, dv] fp32).
 
     q, k: [H, T, dk], v: [H, T, dv], x: fp32 [H, T] -- every head holds the N sequences back
     to back; cu_seqlens: int64 [N + 1] offsets on the device (sequence n is rows
     cu_seqlens[n]:cu_seqlens[n+1]); max_seqlen: the longest sequence (host int);
-    S0: fp32 [N, H, dk, dv] or None.  Rows covered by no sequence are left unwritten in o.
+    S0: fp32 [N, H, dk, dv] or None; plan: (segments per sequence, dv_split) or None for the
+    default.  Rows covered by no sequence are left unwritten in o.
     """
     _need(q.dim() == 3 and k.shape == q.shape and v.dim() == 3 and v.shape[:2] == q.shape[:2],
           "q, k must be [H, T, dk] and v [H, T, dv]")
@@ -388,8 +389,9 @@ def chunk_fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch
     _need(tuple(S_T.shape) == (N, H, dk, dv) and S_T.dtype == torch.float32 and S_T.is_contiguous()
           and S_T.device == dev, "S_T must be fp32 [N, H, dk, dv] on q's device")
     lib = load()
+    cplan = _cplan(plan)
     args = lambda ws: (_ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(o), _ptr(S_T), _ptr(cu_seqlens), N, H,
-                       T, int(max_seqlen), dk, dv, _dtype_code(q), _gate(gate), _path(path), ws)
+                       T, int(max_seqlen), dk, dv, _dtype_code(q), _gate(gate), _path(path), cplan, ws)
     need = ctypes.c_size_t(0)
     _check("gla_chunk_fwd_varlen", lib.gla_chunk_fwd_varlen(*args(None), ctypes.byref(need), _stream(dev)))
     if workspace is None or workspace.numel() * workspace.element_size() < need.value:

@@ -142,6 +142,7 @@ gla::ChunkParams make_params(const void* q, const void* k, const void* v, const 
   p.state_out = nullptr;
   p.cu_seqlens = nullptr;
   p.H = H;
+  p.unit_order = nullptr;
   return p;
 }
 
@@ -455,7 +456,8 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
 gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* x, const float* S0,
                                   float* o, float* S_T, const long long* cu_seqlens, int N, int H, long long T,
                                   long long max_seqlen, int dk, int dv, gla_dtype_t dtype, gla_gate_t gate,
-                                  gla_path_t path, void* workspace, size_t* workspace_bytes, void* stream) {
+                                  gla_path_t path, const gla_plan_t* plan, void* workspace,
+                                  size_t* workspace_bytes, void* stream) {
   if (!workspace_bytes) return GLA_ERR_NULL;
   if (N < 1) return GLA_ERR_SHAPE;
   gla_status_t st = check_sizes(N, H, T, dk, dv);
@@ -463,22 +465,29 @@ gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
   if (max_seqlen < 0 || max_seqlen > T) return GLA_ERR_SHAPE;
   if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
   if (!valid_gate(gate) || !valid_path(path)) return GLA_ERR_ARG;
-  int cus = 0;
-  st = device_cus(&cus);
-  if (st != GLA_OK) return st;
   // the plan is sized by the longest sequence; every sequence is cut into the same
   // number of segments
   gla_plan_t pl;
-  st = default_plan_for(N, H, max_seqlen, dk, dv, dtype, path, cus, &pl);
-  if (st != GLA_OK) return st;
+  if (plan) {
+    st = plan_check_impl(N, H, max_seqlen, dk, dv, dtype, path, plan);
+    if (st != GLA_OK) return st;
+    pl = *plan;
+  } else {
+    int cus = 0;
+    st = device_cus(&cus);
+    if (st != GLA_OK) return st;
+    st = default_plan_for(N, H, max_seqlen, dk, dv, dtype, path, cus, &pl);
+    if (st != GLA_OK) return st;
+  }
   const long long NH = (long long)N * H;
   const size_t b_bytes = align_up((size_t)H * (size_t)T * 4);
   const size_t s_bytes = seg_bytes(NH, dk, dv, pl.segments);
+  const size_t o_bytes = align_up((size_t)N * 4);
   if (!workspace) {
-    *workspace_bytes = std::max(b_bytes + s_bytes, kAlign);
+    *workspace_bytes = b_bytes + s_bytes + o_bytes;
     return GLA_OK;
   }
-  if (*workspace_bytes < b_bytes + s_bytes) return GLA_ERR_WORKSPACE;
+  if (*workspace_bytes < b_bytes + s_bytes + o_bytes) return GLA_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return GLA_ERR_ALIGN;
   if (!S_T || !cu_seqlens) return GLA_ERR_NULL;
   if (T > 0 && (!q || !k || !v || !x || !o)) return GLA_ERR_NULL;
@@ -489,7 +498,8 @@ gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
   const Range ins[] = {{q, (size_t)H * T * dk * es},      {k, (size_t)H * T * dk * es},
                        {v, (size_t)H * T * dv * es},      {x, (size_t)H * T * 4},
                        {S0, (size_t)NH * dk * dv * 4},    {cu_seqlens, (size_t)(N + 1) * 8}};
-  const Range outs[] = {{o, (size_t)H * T * dv * 4}, {S_T, (size_t)NH * dk * dv * 4}, {workspace, b_bytes + s_bytes}};
+  const Range outs[] = {{o, (size_t)H * T * dv * 4}, {S_T, (size_t)NH * dk * dv * 4},
+                        {workspace, b_bytes + s_bytes + o_bytes}};
   for (size_t i = 0; i < 3; ++i) {
     for (const Range& in : ins)
       if (overlap(outs[i], in)) return GLA_ERR_ALIAS;
@@ -501,12 +511,16 @@ gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
   hipStream_t s = (hipStream_t)stream;
   const int dt = dtype == GLA_BF16 ? 0 : 1;
   const long long max_chunks = n_chunks(max_seqlen);
-  hipError_t e = gla::launch_gate_cumsum_varlen(
+  int* order = (int*)((char*)workspace + b_bytes + s_bytes);
+  hipError_t e = gla::launch_varlen_order(cu_seqlens, N, T, max_chunks, order, s);
+  if (e == hipSuccess)
+    e = gla::launch_gate_cumsum_varlen(
       x, bbuf, cu_seqlens, N, H, T, max_chunks,
       gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus, s);
   gla::ChunkParams p = make_params(q, k, v, bbuf, S0, o, S_T, N, H, T, dk, dv, pl, seg);
   p.cu_seqlens = cu_seqlens;
   p.nchunks = (int)max_chunks;
+  p.unit_order = order;
   if (e == hipSuccess && pl.segments > 1) {
     p.grid = (int)(NH * pl.dv_split * (pl.segments - 1));
     e = gla::launch_segment_states(p, dt, s);

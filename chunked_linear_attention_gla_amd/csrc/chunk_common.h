@@ -37,6 +37,19 @@ __host__ __device__ constexpr int off_i(int t) { return t - (off_j(t) - 1) * off
 static_assert(tri_j(9) == 3 && tri_i(9) == 3 && tri_j(4) == 2 && tri_i(4) == 1, "tile numbering");
 static_assert(off_j(5) == 3 && off_i(5) == 2 && off_j(2) == 2 && off_i(2) == 1, "tile numbering");
 
+// Work index of this workgroup: consecutive indices on one XCD for the dense layout;
+// plain dispatch order for packed sequences, whose units are then taken longest first.
+__device__ __forceinline__ int work_index(const ChunkParams& p) {
+  return p.unit_order ? (int)blockIdx.x : xcd_linear_index(blockIdx.x, p.grid);
+}
+
+// Unit (sequence n, head h) -> n * H + h of the r-th unit in work order.
+__device__ __forceinline__ int unit_of(const ChunkParams& p, int r) {
+  if (!p.unit_order) return r;
+  const int i = r / p.H;
+  return p.unit_order[i] * p.H + (r - i * p.H);
+}
+
 // Rows of one work unit (a head of the dense layout, or one sequence of one head
 // when sequences are packed) in the streamed tensors.
 struct HeadSpan {

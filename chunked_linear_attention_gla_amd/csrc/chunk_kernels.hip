@@ -135,11 +135,11 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int nseg = p.segments - 1;
-  const int L = xcd_linear_index(blockIdx.x, p.grid);
+  const int L = work_index(p);
   const int slice = L % p.nslices;
   const int rest = L / p.nslices;
   const int seg = rest % nseg;
-  const int bh = rest / nseg;
+  const int bh = unit_of(p, rest / nseg);
   const int col0 = slice * DVS;
   const int wcol = col0 + wave * C::CPW;
   const HeadSpan span = head_span(p, bh);
@@ -195,11 +195,11 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int L = xcd_linear_index(blockIdx.x, p.grid);
+  const int L = work_index(p);
   const int slice = L % p.nslices;
   const int rest = L / p.nslices;
   const int seg = rest % p.segments;
-  const int bh = rest / p.segments;
+  const int bh = unit_of(p, rest / p.segments);
   const int col0 = slice * DVS;
   const int wcol = col0 + wave * C::CPW;
   const HeadSpan span = head_span(p, bh);

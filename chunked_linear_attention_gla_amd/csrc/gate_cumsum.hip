@@ -94,6 +94,59 @@ __global__ void __launch_bounds__(256) gate_cumsum_varlen_kernel(const float* __
   if (valid) b[row] = s;
 }
 
+constexpr int kOrderThreads = 1024;
+constexpr int kOrderBuckets = 8192;
+
+__global__ void __launch_bounds__(kOrderThreads) varlen_order_kernel(const long long* __restrict__ cu, int N,
+                                                                      long long T, long long max_chunks,
+                                                                      int* __restrict__ order) {
+  __shared__ int hist[kOrderBuckets];
+  __shared__ int part[kOrderThreads];
+  const int tid = threadIdx.x;
+  const auto bucket = [&](int n) {
+    long long a = cu[n], e = cu[n + 1];
+    a = a < 0 ? 0 : (a > T ? T : a);
+    e = e < a ? a : (e > T ? T : e);
+    long long c = (e - a + kChunk - 1) / kChunk;
+    if (c > max_chunks) c = max_chunks;
+    // descending: the longest sequences get the first buckets
+    const long long scaled = max_chunks < kOrderBuckets ? c : c * (kOrderBuckets - 1) / max_chunks;
+    return (int)(kOrderBuckets - 1 - scaled);
+  };
+  for (int i = tid; i < kOrderBuckets; i += kOrderThreads) hist[i] = 0;
+  __syncthreads();
+  for (int n = tid; n < N; n += kOrderThreads) atomicAdd(&hist[bucket(n)], 1);
+  __syncthreads();
+  // exclusive prefix over the buckets: 8 per thread, then across threads
+  constexpr int per = kOrderBuckets / kOrderThreads;
+  int local = 0;
+  for (int j = 0; j < per; ++j) local += hist[tid * per + j];
+  part[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kOrderThreads; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = part[tid] - local;
+  for (int j = 0; j < per; ++j) {
+    const int h = hist[tid * per + j];
+    hist[tid * per + j] = run;
+    run += h;
+  }
+  __syncthreads();
+  for (int n = tid; n < N; n += kOrderThreads) order[atomicAdd(&hist[bucket(n)], 1)] = n;
+}
+
+hipError_t launch_varlen_order(const long long* cu_seqlens, int N, long long T, long long max_chunks, int* order,
+                               hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(varlen_order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, cu_seqlens, N, T,
+                     max_chunks < 1 ? 1 : max_chunks, order);
+  return hipGetLastError();
+}
+
 hipError_t launch_gate_cumsum_varlen(const float* x, float* b, const long long* cu_seqlens, int N, int H,
                                      long long T, long long max_chunks, int gate, hipStream_t stream) {
   const long long total = (long long)N * H * max_chunks;

@@ -41,6 +41,8 @@ struct ChunkParams {
                           //    unit bh = n * H + h is sequence n of head h, and nchunks is
                           //    the largest sequence's chunk count
   int H;                  // heads (packed sequences only)
+  const int* unit_order;  // packed sequences: sequence indices, longest first (the work
+                          //    order); nullptr: dense order
 };
 
 // Byte offset of logical token t's row in a per-unit tensor of T rows with rows of
@@ -64,6 +66,10 @@ hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long 
 // Packed sequences: x and b are [H][T] (T = total tokens), sequence n of every head
 // covers rows [cu_seqlens[n], cu_seqlens[n+1]) and restarts its chunks there; at most
 // max_chunks chunks per sequence.
+// order[0..N) = the sequences by chunk count, longest first (one workgroup, counting
+// sort; the order among equal counts is unspecified and changes no result).
+hipError_t launch_varlen_order(const long long* cu_seqlens, int N, long long T, long long max_chunks, int* order,
+                               hipStream_t stream);
 hipError_t launch_gate_cumsum_varlen(const float* x, float* b, const long long* cu_seqlens, int N, int H,
                                      long long T, long long max_chunks, int gate, hipStream_t stream);
 

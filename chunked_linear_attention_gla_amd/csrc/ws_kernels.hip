@@ -207,11 +207,11 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool compute = wave < W::NCW;  // wave-uniform role
   const int r16 = lane & 15, g = lane >> 4;
-  const int L = xcd_linear_index(blockIdx.x, p.grid);
+  const int L = work_index(p);
   const int slice = L % p.nslices;
   const int rest = L / p.nslices;
   const int seg = rest % p.segments;
-  const int bh = rest / p.segments;
+  const int bh = unit_of(p, rest / p.segments);
   const int col0 = slice * DVS;
   const int cw = compute ? wave : 0;             // compute-wave index
   const int sw = compute ? 0 : wave - W::NCW;    // staging-wave index
@@ -414,11 +414,11 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
   const bool compute = wave < W::NCW;
   const int r16 = lane & 15, g = lane >> 4;
   const int nseg = p.segments - 1;
-  const int L = xcd_linear_index(blockIdx.x, p.grid);
+  const int L = work_index(p);
   const int slice = L % p.nslices;
   const int rest = L / p.nslices;
   const int seg = rest % nseg;
-  const int bh = rest / nseg;
+  const int bh = unit_of(p, rest / nseg);
   const int col0 = slice * DVS;
   const int cw = compute ? wave : 0;
   const int sw = compute ? 0 : wave - W::NCW;

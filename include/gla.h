@@ -276,14 +276,16 @@ gla_status_t gla_decode_step(const void* q, const void* k, const void* v, const 
  *   sequences cut to max_seqlen, which yields wrong values but never an access
  *   outside the tensors.  Rows covered by no sequence are not written in o.
  *   S0, S_T [N][H][dk][dv] fp32 (S0 may be NULL), one state per sequence and head.
- * Plan: the device default for N heads groups of max_seqlen tokens; every sequence
- * gets the same number of segments.  workspace == NULL returns the size.  Errors
- * as gla_chunk_fwd. */
+ * plan: NULL = the device default for N x H units of max_seqlen tokens; an explicit
+ * plan is checked as for gla_chunk_fwd_plan with T = max_seqlen.  Every sequence is
+ * cut into the plan's number of segments.  workspace == NULL returns the size.
+ * Errors as gla_chunk_fwd. */
 gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, const float* x,
                                   const float* S0, float* o, float* S_T,
                                   const long long* cu_seqlens, int N, int H, long long T,
                                   long long max_seqlen, int dk, int dv,
                                   gla_dtype_t dtype, gla_gate_t gate, gla_path_t path,
+                                  const gla_plan_t* plan,
                                   void* workspace, size_t* workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

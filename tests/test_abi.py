@@ -260,7 +260,8 @@ def test_varlen_validation_before_any_device_call(lib):
     def var(**kw):
         return lib.gla_chunk_fwd_varlen(0x1000, 0x2000, 0x3000, 0x4000, None, 0x5000, 0x6000, 0x7000,
                                         kw.get("N", 3), 2, kw.get("T", 500), kw.get("maxlen", 200), 64, 64,
-                                        kw.get("dtype", BF16), kw.get("gate", BOUNDED), UNIFIED, None,
+                                        kw.get("dtype", BF16), kw.get("gate", BOUNDED), UNIFIED,
+                                        P(*kw["plan"]) if "plan" in kw else None, None,
                                         kw.get("nb", ctypes.byref(n)), None)
     assert var(nb=None) == NULL
     assert var(N=0) == SHAPE
@@ -268,6 +269,11 @@ def test_varlen_validation_before_any_device_call(lib):
     assert var(maxlen=-1) == SHAPE
     assert var(dtype=5) == DTYPE
     assert var(gate=3) == ARG
+    assert var(plan=(5, 1)) == PLAN       # 200 tokens are 4 chunks
+    assert var(plan=(4, 1)) == OK         # explicit plan: size query without a device
+    align = lambda b: (b + 255) // 256 * 256
+    # b, the local states and decays of 3 segments, the work order of the 3 sequences
+    assert n.value == align(2 * 500 * 4) + align(3 * 2 * 3 * 64 * 64 * 4) + align(3 * 2 * 4 * 4) + align(3 * 4)
 
 
 def test_delta_validation_and_workspace_query(lib):

@@ -72,12 +72,12 @@ def test_decode_chain_matches_chunked_forward(per_channel):
 
 # ------------------------------------------------------------------------------ packed sequences
 
-def varlen_check(w, lengths, gate="bounded", path="unified", tol=None, seed=None):
+def varlen_check(w, lengths, gate="bounded", path="unified", tol=None, seed=None, plan=None):
     dev = device()
     inp = gin.make_varlen_inputs(w, lengths, dev, seed=seed)
     max_len = max(lengths) if lengths else 0
     o, ST = gla.chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["x"], inp["cu_seqlens"], max_len, inp["S0"],
-                                 gate=gate, path=path)
+                                 gate=gate, path=path, plan=plan)
     torch.cuda.synchronize()
     tol = TOL[w.qkv_dtype] if tol is None else tol
     cu = [0] + list(np.cumsum(lengths))
@@ -104,6 +104,14 @@ def test_varlen_long_sequences_use_segments():
     """Long enough for the default plan to cut every sequence into segments."""
     w = VAR.with_(H=2, x_mean=-5.0)
     varlen_check(w, [4100, 37, 2500, 0, 64 * 40])
+
+
+@pytest.mark.parametrize("segments", [2, 4, 7])
+def test_varlen_explicit_segments(segments):
+    """Every sequence cut into the same number of segments, including sequences shorter
+    than that many chunks (empty segments) and empty sequences."""
+    w = VAR.with_(H=2, s0_std=0.1, x_mean=-5.0)
+    varlen_check(w, [64 * 9 + 5, 3, 0, 64 * 2, 1000], plan=gla.Plan(segments, 1))
 
 
 def test_varlen_length_mix_sample():
