@@ -139,6 +139,7 @@ gla::ChunkParams make_params(const void* q, const void* k, const void* v, const 
   p.pad = 0;
   p.Tl = T;
   p.s0_transposed = 0;
+  p.seg_transposed = 0;
   p.state_out = nullptr;
   p.cu_seqlens = nullptr;
   p.H = H;
@@ -416,12 +417,11 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
   if (T > 0) {
     e = gla::launch_gate_cumsum(x, b, BH, T, g, false, s);
     if (e == hipSuccess) e = gla::launch_gate_cumsum(x, br, BH, T, g, true, s);
-    // one forward-shaped pass: segment pre-pass (when segmented) and output pass.  A
+    // forward-shaped passes: segment pre-pass (when segmented) and output pass.  A
     // reversed pass reads its rows back to front behind `pad` zero rows, so that its
     // chunks are the forward chunks in reverse order.
-    const auto pass = [&](const void* pq, const void* pk, const void* pv, const float* pb, const float* ps0,
-                          int s0t, int rev, float* po, float* pst, void* chunk_states, int sdk, int sdv,
-                          const gla_plan_t& pl) {
+    const auto make = [&](const void* pq, const void* pk, const void* pv, const float* pb, const float* ps0,
+                          int s0t, int rev, float* po, float* pst, int sdk, int sdv, const gla_plan_t& pl) {
       gla::ChunkParams p = make_params(pq, pk, pv, pb, ps0, po, pst, B, H, T, sdk, sdv, pl, seg);
       p.reverse = rev;
       p.s0_transposed = s0t;
@@ -429,24 +429,39 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
         p.pad = pad;
         p.Tl = T + pad;
       }
-      hipError_t r = hipSuccess;
-      if (pl.segments > 1) {
-        p.grid = (int)(BH * pl.dv_split * (pl.segments - 1));
-        r = gla::launch_segment_states(p, dt, s);
-      }
-      if (r == hipSuccess) {
-        p.state_out = chunk_states;
-        p.grid = (int)(BH * pl.dv_split * pl.segments);
-        r = gla::launch_chunk_output(p, dt, diag, s);
-      }
-      return r;
+      return p;
+    };
+    const auto prepass = [&](gla::ChunkParams p, const gla_plan_t& pl) {
+      if (pl.segments <= 1) return hipSuccess;
+      p.grid = (int)(BH * pl.dv_split * (pl.segments - 1));
+      return gla::launch_segment_states(p, dt, s);
+    };
+    const auto output = [&](gla::ChunkParams p, const gla_plan_t& pl, void* chunk_states) {
+      p.state_out = chunk_states;
+      p.grid = (int)(BH * pl.dv_split * pl.segments);
+      return gla::launch_chunk_output(p, dt, diag, s);
     };
     // dq = forward(dO, v, k) from S0^T; stores S^T before every chunk
-    if (e == hipSuccess) e = pass(dO, v, k, b, S0, 1, 0, dq, STt, Sfw, dv_, dk_, pa);
-    // dk = reversed forward(v, dO, q) from dS_T^T; stores D^T after every chunk
-    if (e == hipSuccess) e = pass(v, dO, q, br, dS_T, 1, 1, dk, Sdk, Sbw, dv_, dk_, pa);
-    // dv = reversed forward(k, q, dO) from dS_T; its final state is D_0
-    if (e == hipSuccess) e = pass(k, q, dO, br, dS_T, 0, 1, dv, D0, nullptr, dk_, dv_, pc);
+    const gla::ChunkParams pdq = make(dO, v, k, b, S0, 1, 0, dq, STt, dv_, dk_, pa);
+    if (e == hipSuccess) e = prepass(pdq, pa);
+    if (e == hipSuccess) e = output(pdq, pa, Sfw);
+    // dk = reversed forward(v, dO, q) from dS_T^T (stores D^T after every chunk) and
+    // dv = reversed forward(k, q, dO) from dS_T (final state D_0) carry the same state
+    // gradient, transposed, under the same decays: with equal segment counts the dk
+    // pass starts its segments from the dv pass's segment states, read transposed
+    gla::ChunkParams pdk = make(v, dO, q, br, dS_T, 1, 1, dk, Sdk, dv_, dk_, pa);
+    const gla::ChunkParams pdv = make(k, q, dO, br, dS_T, 0, 1, dv, D0, dk_, dv_, pc);
+    if (pa.segments == pc.segments) {
+      pdk.seg_transposed = 1;
+      if (e == hipSuccess) e = prepass(pdv, pc);
+      if (e == hipSuccess) e = output(pdk, pa, Sbw);
+      if (e == hipSuccess) e = output(pdv, pc, nullptr);
+    } else {
+      if (e == hipSuccess) e = prepass(pdk, pa);
+      if (e == hipSuccess) e = output(pdk, pa, Sbw);
+      if (e == hipSuccess) e = prepass(pdv, pc);
+      if (e == hipSuccess) e = output(pdv, pc, nullptr);
+    }
     if (e == hipSuccess) e = gla::launch_grad_dx(q, k, v, dO, b, x, Sfw, Sbw, dx, BH, T, dk_, dv_, dt, g, s);
   }
   if (e == hipSuccess) e = gla::launch_grad_ds0(D0, b, dS_T, dS0, BH, T, dk_, dv_, s);

@@ -200,7 +200,7 @@ __device__ __forceinline__ void load_initial_state(StateAcc<T, DK, DVS>& S, cons
         for (int e = 0; e < 4; ++e) {
           const int d = db * 16 + 4 * g + e;
           const int n = wcol + nb * 16 + r16;
-          S.s[nb][db][e] = f * S.s[nb][db][e] + H[(long long)d * p.dv + n];
+          S.s[nb][db][e] = f * S.s[nb][db][e] + (p.seg_transposed ? H[(long long)n * DK + d] : H[(long long)d * p.dv + n]);
         }
   }
 }

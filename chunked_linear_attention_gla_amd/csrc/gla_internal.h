@@ -32,6 +32,8 @@ struct ChunkParams {
                           //    one, so that logical chunks line up with the stored chunks
   long long Tl;           // logical length, T + pad: per-head length and stride of b
   int s0_transposed;      // 1: S0 is stored [dv][dk] (the transpose of the state)
+  int seg_transposed;     // 1: the segment states are those of the transposed pass
+                          //    ([dv][dk] per segment; same decays)
   void* state_out;        // optional: the state before every chunk, in the operand dtype,
                           //    in MFMA-fragment order (see store_chunk_state); a reversed
                           //    pass stores logical chunk c at chunk nchunks-1-c
