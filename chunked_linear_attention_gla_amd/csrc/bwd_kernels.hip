@@ -69,16 +69,29 @@ __device__ __forceinline__ float gate_slope(float x) {
   return -5.0f * sg * (1.0f - sg);                      // d/dx -5 sigmoid(x)
 }
 
-// 64 rows of a per-head [T][ncol] tensor into LDS (zeros past the end).
+// 64 rows of a per-head [T][ncol] tensor, 8-element units spread over the threads:
+// all loads are issued first (load), the LDS stores come after (store), so a
+// workgroup has its whole chunk in flight at once.  Rows past the end read zeros.
 template <typename T, int NCOL, int LD, int NT>
-__device__ __forceinline__ void stage_rows(T* dst, rsrc_t r, uint32_t t0, int tid) {
-  using E = Elem<T>;
+struct RowStage {
+  static constexpr int U = 64 * NCOL / 8 / NT;
+  static_assert(U >= 1 && U * NT * 8 == 64 * NCOL, "units must divide evenly");
+  typename Elem<T>::Vec8 r[U];
+  __device__ __forceinline__ void load(rsrc_t src, uint32_t t0, int tid) {
 #pragma unroll
-  for (int u = tid; u < 64 * NCOL / 8; u += NT) {
-    const int row = u / (NCOL / 8), c8 = u % (NCOL / 8);
-    E::store8_raw(dst + row * LD + c8 * 8, E::load8(r, ((t0 + row) * NCOL + c8 * 8) * (uint32_t)sizeof(T)));
+    for (int m = 0; m < U; ++m) {
+      const int u = tid + m * NT, row = u / (NCOL / 8), c8 = u % (NCOL / 8);
+      r[m] = Elem<T>::load8(src, ((t0 + row) * NCOL + c8 * 8) * (uint32_t)sizeof(T));
+    }
   }
-}
+  __device__ __forceinline__ void store(T* dst, int tid) const {
+#pragma unroll
+    for (int m = 0; m < U; ++m) {
+      const int u = tid + m * NT, row = u / (NCOL / 8), c8 = u % (NCOL / 8);
+      Elem<T>::store8_raw(dst + row * LD + c8 * 8, r[m]);
+    }
+  }
+};
 
 // A stored chunk state (fragment order, see store_chunk_state) of one 32-column group.
 template <typename T, int DB>
@@ -112,29 +125,41 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) grad_dx_kernel(
   const uint32_t t0 = (uint32_t)c * kChunk;
   const uint32_t Tn = (uint32_t)Tlen;
 
-  // ---- operands of the chunk (raw) and its cumulative log-decay
-  stage_rows<T, DK, X::LDK, X::NT>(sm.q, make_rsrc(q + bh * Tlen * DK, Tn * DK * (uint32_t)sizeof(T)), t0, tid);
-  stage_rows<T, DK, X::LDK, X::NT>(sm.k, make_rsrc(k + bh * Tlen * DK, Tn * DK * (uint32_t)sizeof(T)), t0, tid);
-  stage_rows<T, DV, X::LDV, X::NT>(sm.v, make_rsrc(v + bh * Tlen * DV, Tn * DV * (uint32_t)sizeof(T)), t0, tid);
-  stage_rows<T, DV, X::LDV, X::NT>(sm.g, make_rsrc(dO + bh * Tlen * DV, Tn * DV * (uint32_t)sizeof(T)), t0, tid);
+  // ---- operands of the chunk (raw) and its cumulative log-decay: every load of the
+  //      chunk, including this wave's 32-column slices of S^T (before the chunk) and D^T
+  //      (after it), is issued before the first LDS store
+  float bval = 0.0f;
   if (tid < 64) {
     const long long tt = (long long)t0 + tid;
-    sm.b[tid] = b[bh * Tlen + (tt < Tlen ? tt : Tlen - 1)];
+    bval = b[bh * Tlen + (tt < Tlen ? tt : Tlen - 1)];
   }
-
-  // ---- this wave's 32-column slices of S^T (before the chunk) and D^T (after it)
+  RowStage<T, DK, X::LDK, X::NT> sq, sk;
+  RowStage<T, DV, X::LDV, X::NT> svv, sg;
+  sq.load(make_rsrc(q + bh * Tlen * DK, Tn * DK * (uint32_t)sizeof(T)), t0, tid);
+  sk.load(make_rsrc(k + bh * Tlen * DK, Tn * DK * (uint32_t)sizeof(T)), t0, tid);
+  svv.load(make_rsrc(v + bh * Tlen * DV, Tn * DV * (uint32_t)sizeof(T)), t0, tid);
+  sg.load(make_rsrc(dO + bh * Tlen * DV, Tn * DV * (uint32_t)sizeof(T)), t0, tid);
   const long long sidx = (((bh * nchunks + c) * (DK / 32) + w) * 2) * (long long)X::DB * 256;
   floatx4 sv[2][X::DB], ev[2][X::DB];
-  float z = 0.0f;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int db = 0; db < X::DB; ++db) {
       sv[nb][db] = load_state4<T, X::DB>(Sfw + sidx, nb, db, lane);
       ev[nb][db] = load_state4<T, X::DB>(Sbw + sidx, nb, db, lane);
+    }
+  sq.store(sm.q, tid);
+  sk.store(sm.k, tid);
+  svv.store(sm.v, tid);
+  sg.store(sm.g, tid);
+  if (tid < 64) sm.b[tid] = bval;
+  float z = 0.0f;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int db = 0; db < X::DB; ++db)
 #pragma unroll
       for (int e = 0; e < 4; ++e) z += sv[nb][db][e] * ev[nb][db][e];
-    }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
   if (lane == 0) sm.zpart[w] = z;
