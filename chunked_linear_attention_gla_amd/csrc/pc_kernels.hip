@@ -72,12 +72,12 @@ struct PcLane {
 template <typename T, int DK, int DVS>
 struct PcSmem {
   using C = PcCfg<T, DK, DVS>;
-  T qh[64 * C::QLD];                // Qh_j = q_j e^{b_j - r_u(j)}
+  T qh[2][64 * C::QLD];             // Qh_j = q_j e^{b_j - r_u(j)}, by chunk parity
   T kt[10 * 16 * C::QLD];           // causal tile t = (u, v): k_i e^{r_u - b_i}, i in tile v
   T kp[TokTile<T, DK>::SIZE];       // k_i e^{gamma - b_i}, token-major
   T vv[TokTile<T, DVS>::SIZE];      // v, token-major
   T a[64 * C::TLD];                 // A[j][i]
-  float tau[4][DK];                 // per-tile sums of g, per channel
+  float tau[2][4][DK];              // per-tile sums of g, per channel, by chunk parity
   float er[4][DK];                  // e^{r_u}
   float eg[DK];                     // e^{gamma}
 };
@@ -86,7 +86,7 @@ template <typename T, int DK, int DVS>
 struct PcSegSmem {
   T kp[TokTile<T, DK>::SIZE];
   T vv[TokTile<T, DVS>::SIZE];
-  float tau[4][DK];
+  float tau[2][4][DK];
   float eg[DK];
 };
 
@@ -339,13 +339,18 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_segment_state_kern
 
   PcStaged<T, DK, DVS, false> st;
   if (c_begin < c_end) st.load(hb, Tn, p.dv, (uint32_t)c_begin * kChunk, col0, wave, lane, tid);
+  // Two barriers per chunk: the tile totals alternate between two buffers, so a wave
+  // may publish chunk c + 1's totals while others still update the state of chunk c;
+  // everything else chunk c + 1 writes comes after the barrier that all waves reach
+  // only once they are done with chunk c.
   for (int c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)c * kChunk;
+    float (*tau)[DK] = sm.tau[(c - c_begin) & 1];
     PcLam<T, DK, DVS> lam;
-    tile_log_decay<T, DK, DVS, false>(lam, st, sm.tau, t0, Tn, p.gate, wave, lane);
+    tile_log_decay<T, DK, DVS, false>(lam, st, tau, t0, Tn, p.gate, wave, lane);
     __syncthreads();
     float tv[4][8];
-    read_tau<DK>(tv, sm.tau, pl.c8 * 8);
+    read_tau<DK>(tv, tau, pl.c8 * 8);
     stage_state_side<T, DK, DVS, false>(sm.kp, sm.eg, st, lam, tv, wave, lane);
     stage_v<T, DK, DVS, false>(sm.vv, st, tid);
 #pragma unroll
@@ -355,7 +360,6 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_segment_state_kern
     PcVFrags<T, DK, DVS> Vf;
     pc_load_v_frags<T, DK, DVS>(Vf, sm.vv, wave, lane);
     pc_state_update<T, DK, DVS>(S, Vf, sm.kp, sm.eg, lane);
-    __syncthreads();
   }
   pc_store_state<T, DK, DVS>(S, p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv, p.dv, wcol, g, r16);
   if (slice == 0 && pl.tile == 0 && pl.rg == 0) {
@@ -437,20 +441,23 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
 
     // ---- (1) gate and tile-local cumulative log-decay; Qh needs nothing else
     PcLam<T, DK, DVS> lam;
-    tile_log_decay<T, DK, DVS, true>(lam, st, sm.tau, t0, Tn, p.gate, wave, lane);
+    const int par = (c - c_begin) & 1;
+    float (*tau)[DK] = sm.tau[par];
+    T* qh = sm.qh[par];
+    tile_log_decay<T, DK, DVS, true>(lam, st, tau, t0, Tn, p.gate, wave, lane);
 #pragma unroll
     for (int m = 0; m < C::R; ++m) {
       float f[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) f[e] = exp_e(lam.v[m][e]);
-      E::store8_vscaled(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f);
+      E::store8_vscaled(qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f);
     }
     __syncthreads();
 
     // ---- (2) key operands of every query tile, the state-side operands, e^{r_u}
     {
       float tv[4][8];
-      read_tau<DK>(tv, sm.tau, c8 * 8);
+      read_tau<DK>(tv, tau, c8 * 8);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (u < tile) continue;  // wave-uniform: key tile `tile` serves query tiles u >= tile
@@ -502,7 +509,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
         E::mfma(acc, E::load_frag(sm.kt + (t * 16 + r16) * C::QLD, ks * 32 + 4 * g),
-                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+                E::load_frag(qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
       // acc[e]: j = 16 jb + r16, i = 16 ib + 4 g + e; causal select on the diagonal tile
       float vals[4];
 #pragma unroll
@@ -522,7 +529,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const typename E::Frag qb = E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g);
+          const typename E::Frag qb = E::load_frag(qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g);
           const floatx4 f0 = *reinterpret_cast<const floatx4*>(&sm.er[jb][32 * ks + 4 * g]);
           const floatx4 f1 = *reinterpret_cast<const floatx4*>(&sm.er[jb][32 * ks + 16 + 4 * g]);
 #pragma unroll
@@ -548,7 +555,8 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
           buf_store16(hb.o, pc_row(t0 + jb * 16 + r16, Tn, (uint32_t)p.dv * 4u) + (wcol + nb * 16 + 4 * g) * 4u,
                       O[jb][nb]);
     }
-    __syncthreads();
+    // no barrier here: Qh and the tile totals of chunk c + 1 go to the other buffers,
+    // and the rest of its operands are written after its first barrier
   }
 
   if (seg == p.segments - 1) pc_store_state<T, DK, DVS>(S, p.ST + (long long)bh * DK * p.dv, p.dv, wcol, g, r16);
