@@ -36,16 +36,15 @@ __device__ __forceinline__ float exp_e(float x) {
 
 // Log-decay gates ("Engineering Long-Context Training for Trillion-Parameter MoE
 // Models: Three Key Breakthroughs", §3.2).
-// g = -5 * sigmoid(x), sigmoid evaluated without overflow for either sign of x.
+// g = -5 * sigmoid(x).  With t = e^{-|x|} in [0, 1], sigmoid(x) is 1 / (1 + t) for
+// x >= 0 and t / (1 + t) for x < 0: nothing overflows for either sign, and one
+// hardware reciprocal (1 ulp) replaces an IEEE division per branch, so the gate costs
+// two transcendentals and no divergent branch (it runs once per token and channel
+// inside the per-channel kernels).
 __device__ __forceinline__ float gate_bounded_sigmoid(float x) {
-  float s;
-  if (x >= 0.0f) {
-    s = 1.0f / (1.0f + exp_e(-x));
-  } else {
-    const float e = exp_e(x);
-    s = e / (1.0f + e);
-  }
-  return -5.0f * s;
+  const float t = exp_e(-fabsf(x));
+  const float r = __builtin_amdgcn_rcpf(1.0f + t);
+  return -5.0f * (x >= 0.0f ? r : t * r);
 }
 
 // g = -softplus(-x) = -(max(-x, 0) + log1p(e^-|x|)) = log sigmoid(x)
