@@ -29,10 +29,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kChunk = 64;  // tokens per chunk
 constexpr int kTile = 16;   // tokens per tile (the bounded-decay safe length)
 
-// e^x as 2^(x log2 e) on the hardware exp2 (v_exp_f32).  e^-inf = 0, e^+inf = inf.
-__device__ __forceinline__ float exp_e(float x) {
-  return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
-}
+constexpr float kLog2e = 1.4426950408889634f;
+
+// 2^x on the hardware exp2 (v_exp_f32).  2^-inf = 0, 2^+inf = inf.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// e^x as 2^(x log2 e).
+__device__ __forceinline__ float exp_e(float x) { return exp2_hw(x * kLog2e); }
 
 // Log-decay gates ("Engineering Long-Context Training for Trillion-Parameter MoE
 // Models: Three Key Breakthroughs", §3.2).
@@ -41,11 +44,13 @@ __device__ __forceinline__ float exp_e(float x) {
 // hardware reciprocal (1 ulp) replaces an IEEE division per branch, so the gate costs
 // two transcendentals and no divergent branch (it runs once per token and channel
 // inside the per-channel kernels).
-__device__ __forceinline__ float gate_bounded_sigmoid(float x) {
+__device__ __forceinline__ float sigmoid_hw(float x) {
   const float t = exp_e(-fabsf(x));
   const float r = __builtin_amdgcn_rcpf(1.0f + t);
-  return -5.0f * (x >= 0.0f ? r : t * r);
+  return x >= 0.0f ? r : t * r;
 }
+
+__device__ __forceinline__ float gate_bounded_sigmoid(float x) { return -5.0f * sigmoid_hw(x); }
 
 // g = -softplus(-x) = -(max(-x, 0) + log1p(e^-|x|)) = log sigmoid(x)
 __device__ __forceinline__ float gate_neg_softplus(float x) {

@@ -97,7 +97,7 @@ struct PcParams {
   float* o;               // [BH][T][dv]
   float* ST;              // [BH][dk][dv]
   float* seg_state;       // [BH][segments-1][dk][dv]  local final states
-  float* seg_decay;       // [BH][segments][dk]        per-channel log-decay of each segment
+  float* seg_decay;       // [BH][segments][dk]        per-channel log2-decay of each segment
   long long T;
   int dk, dv;
   int BH;

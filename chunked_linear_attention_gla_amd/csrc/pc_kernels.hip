@@ -27,7 +27,13 @@
 // The gate and the cumulative sum are fused into the kernels: each of the four
 // waves stages one 16-token tile of the chunk (lane = column group x row group),
 // scans g down its rows in registers and across lanes with shuffles, and publishes
-// the tile's total per channel; r_u and gamma are sums of those totals.
+// the tile's total per channel; r_u and gamma are sums of those totals.  Inside
+// these kernels every log-decay (g, b, r, gamma, the segment totals) is kept in
+// base 2, g log2 e, so that each weight is one hardware exp2 of a difference.
+//
+// The inter-chunk term is computed as (q_j e^{b_j}) S_{c-1}: the same product as
+// Qh_j e^{r_u} S_{c-1}, with the state converted to the matrix-core type once per
+// chunk instead of once per query tile.
 //
 // Work decomposition as in the scalar kernels: one workgroup per (head, value slice,
 // segment); segments after the first start from the state assembled from the
@@ -72,13 +78,13 @@ struct PcLane {
 template <typename T, int DK, int DVS>
 struct PcSmem {
   using C = PcCfg<T, DK, DVS>;
-  T qh[2][64 * C::QLD];             // Qh_j = q_j e^{b_j - r_u(j)}, by chunk parity
+  T qh[64 * C::QLD];                // Qh_j = q_j e^{b_j - r_u(j)}
+  T qe[64 * C::QLD];                // q_j e^{b_j}
   T kt[10 * 16 * C::QLD];           // causal tile t = (u, v): k_i e^{r_u - b_i}, i in tile v
   T kp[TokTile<T, DK>::SIZE];       // k_i e^{gamma - b_i}, token-major
   T vv[TokTile<T, DVS>::SIZE];      // v, token-major
   T a[64 * C::TLD];                 // A[j][i]
   float tau[2][4][DK];              // per-tile sums of g, per channel, by chunk parity
-  float er[4][DK];                  // e^{r_u}
   float eg[DK];                     // e^{gamma}
 };
 
@@ -137,7 +143,12 @@ struct PcStaged {
   }
 };
 
-// Tile-local cumulative log-decay of the lane's rows (see tile_log_decay).
+// Log-decay of one channel in base 2: g log2 e.
+__device__ __forceinline__ float pc_log2_gate(float x, int gate) {
+  return gate == kGateBoundedSigmoid ? (-5.0f * kLog2e) * sigmoid_hw(x) : kLog2e * gate_neg_softplus(x);
+}
+
+// Tile-local cumulative log2-decay of the lane's rows (see tile_log_decay).
 template <typename T, int DK, int DVS>
 struct PcLam {
   float v[PcCfg<T, DK, DVS>::R][8];
@@ -147,7 +158,7 @@ __device__ __forceinline__ float f4_get(const float4& v, int e) {
   return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
 }
 
-// Tile-local inclusive cumulative log-decay lam.v[m][e] = b - r_u of the lane's rows
+// Tile-local inclusive cumulative log2-decay lam.v[m][e] = b - r_u of the lane's rows
 // (row rg*R + m of the wave's tile, channel 8*c8 + e); absent tokens have g = 0.
 // The lanes of the tile's last row group publish the tile totals to tau[tile].
 template <typename T, int DK, int DVS, bool LOAD_Q>
@@ -163,7 +174,7 @@ __device__ __forceinline__ void tile_log_decay(PcLam<T, DK, DVS>& lam,
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float xv = f4_get(st.x[m][e >> 2], e & 3);
-      const float g = gate == kGateBoundedSigmoid ? gate_bounded_sigmoid(xv) : gate_neg_softplus(xv);
+      const float g = pc_log2_gate(xv, gate);
       lam.v[m][e] = (valid ? g : 0.0f) + (m > 0 ? lam.v[m - 1][e] : 0.0f);
     }
   }
@@ -223,13 +234,13 @@ __device__ __forceinline__ void stage_state_side(T* kp, float* eg, const PcStage
   for (int m = 0; m < C::R; ++m) {
     float f[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = exp_e(G[e] - lam.v[m][e]);
+    for (int e = 0; e < 8; ++e) f[e] = exp2_hw(G[e] - lam.v[m][e]);
     TokTile<T, DK>::store8_v(kp, 16 * pl.tile + rg * C::R + m, c8 * 8, st.k[m], f);
   }
   if (pl.tile == 0 && rg == 0) {
     float f[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = exp_e(G[e]);
+    for (int e = 0; e < 8; ++e) f[e] = exp2_hw(G[e]);
     *reinterpret_cast<float4*>(&eg[c8 * 8]) = make_float4(f[0], f[1], f[2], f[3]);
     *reinterpret_cast<float4*>(&eg[c8 * 8 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
   }
@@ -421,7 +432,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int d = db * 16 + 4 * g + e;
-            S.s[nb][db][e] = exp_e(G[d]) * S.s[nb][db][e] + H[(long long)d * p.dv + wcol + nb * 16 + r16];
+            S.s[nb][db][e] = exp2_hw(G[d]) * S.s[nb][db][e] + H[(long long)d * p.dv + wcol + nb * 16 + r16];
           }
     }
   }
@@ -441,23 +452,39 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
 
     // ---- (1) gate and tile-local cumulative log-decay; Qh needs nothing else
     PcLam<T, DK, DVS> lam;
-    const int par = (c - c_begin) & 1;
-    float (*tau)[DK] = sm.tau[par];
-    T* qh = sm.qh[par];
+    float (*tau)[DK] = sm.tau[(c - c_begin) & 1];
     tile_log_decay<T, DK, DVS, true>(lam, st, tau, t0, Tn, p.gate, wave, lane);
+    float fq[C::R][8];  // e^{b_j - r_u}
 #pragma unroll
     for (int m = 0; m < C::R; ++m) {
-      float f[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = exp_e(lam.v[m][e]);
-      E::store8_vscaled(qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f);
+      for (int e = 0; e < 8; ++e) fq[m][e] = exp2_hw(lam.v[m][e]);
+      E::store8_vscaled(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], fq[m]);
     }
     __syncthreads();
 
-    // ---- (2) key operands of every query tile, the state-side operands, e^{r_u}
+    // ---- (2) key operands of every query tile, the state-side operands, q e^{b}
     {
       float tv[4][8];
       read_tau<DK>(tv, tau, c8 * 8);
+      {
+        float er[8];  // e^{r_tile}
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float s = 0.0f;
+#pragma unroll
+          for (int w = 0; w < 4; ++w)
+            if (w < tile) s += tv[w][e];
+          er[e] = exp2_hw(s);
+        }
+#pragma unroll
+        for (int m = 0; m < C::R; ++m) {
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = fq[m][e] * er[e];
+          E::store8_vscaled(sm.qe + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (u < tile) continue;  // wave-uniform: key tile `tile` serves query tiles u >= tile
@@ -475,25 +502,12 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         for (int m = 0; m < C::R; ++m) {
           float f[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = exp_e(D[e] - lam.v[m][e]);
+          for (int e = 0; e < 8; ++e) f[e] = exp2_hw(D[e] - lam.v[m][e]);
           E::store8_vscaled(kt + (rg * C::R + m) * C::QLD + c8 * 8, st.k[m], f);
         }
       }
       stage_state_side<T, DK, DVS, true>(sm.kp, sm.eg, st, lam, tv, wave, lane);
       stage_v<T, DK, DVS, true>(sm.vv, st, tid);
-      if (tile == 1 && rg == 0) {
-        float r[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float f[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = exp_e(r[e]);
-          *reinterpret_cast<float4*>(&sm.er[u][c8 * 8]) = make_float4(f[0], f[1], f[2], f[3]);
-          *reinterpret_cast<float4*>(&sm.er[u][c8 * 8 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) r[e] += tv[u][e];
-        }
-      }
     }
     // prefetch chunk c + 1 (the last iteration re-reads its own chunk so that every
     // iteration issues the same loads)
@@ -509,7 +523,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
         E::mfma(acc, E::load_frag(sm.kt + (t * 16 + r16) * C::QLD, ks * 32 + 4 * g),
-                E::load_frag(qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
       // acc[e]: j = 16 jb + r16, i = 16 ib + 4 g + e; causal select on the diagonal tile
       float vals[4];
 #pragma unroll
@@ -518,10 +532,16 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
     }
     __syncthreads();
 
-    // ---- (4) o = Qh (e^{r_u} S_{c-1}) + A V for this wave's columns; then S_c
+    // ---- (4) o = (q e^{b}) S_{c-1} + A V for this wave's columns; then S_c
     {
       PcVFrags<T, DK, DVS> Vf;
       pc_load_v_frags<T, DK, DVS>(Vf, sm.vv, wave, lane);
+      // rows 32 ks + 4 g + e and 32 ks + 16 + 4 g + e of the state
+      typename E::Frag sf[C::NB][C::KS];
+#pragma unroll
+      for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) sf[nb][ks] = E::from_acc(S.s[nb][2 * ks], S.s[nb][2 * ks + 1]);
       floatx4 O[4][C::NB];
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
@@ -529,15 +549,9 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const typename E::Frag qb = E::load_frag(qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g);
-          const floatx4 f0 = *reinterpret_cast<const floatx4*>(&sm.er[jb][32 * ks + 4 * g]);
-          const floatx4 f1 = *reinterpret_cast<const floatx4*>(&sm.er[jb][32 * ks + 16 + 4 * g]);
+          const typename E::Frag qb = E::load_frag(sm.qe + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g);
 #pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) {
-            // rows 32 ks + 4 g + e and 32 ks + 16 + 4 g + e of the state, scaled by e^{r_jb}
-            const typename E::Frag sf = E::from_acc(S.s[nb][2 * ks] * f0, S.s[nb][2 * ks + 1] * f1);
-            E::mfma(O[jb][nb], sf, qb);
-          }
+          for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], sf[nb][ks], qb);
         }
 #pragma unroll
         for (int ks = 0; ks <= jb / 2; ++ks) {
@@ -555,8 +569,9 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
           buf_store16(hb.o, pc_row(t0 + jb * 16 + r16, Tn, (uint32_t)p.dv * 4u) + (wcol + nb * 16 + 4 * g) * 4u,
                       O[jb][nb]);
     }
-    // no barrier here: Qh and the tile totals of chunk c + 1 go to the other buffers,
-    // and the rest of its operands are written after its first barrier
+    // no barrier here: chunk c + 1 writes Qh (read only in step 3, before the last
+    // barrier) and the other tile-total buffer before its first barrier, and the rest of
+    // its operands after it
   }
 
   if (seg == p.segments - 1) pc_store_state<T, DK, DVS>(S, p.ST + (long long)bh * DK * p.dv, p.dv, wcol, g, r16);
