@@ -485,28 +485,39 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
           E::store8_vscaled(sm.qe + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f);
         }
       }
+      // Key tile `tile` serves the query tiles u >= tile as K^(u) = k e^{r_u - b}, and the
+      // state update as k e^{gamma - b}.  Along that chain the factor of row i goes
+      // e^{r_tile - b_i} -> e^{r_{tile+1} - b_i} -> ... -> e^{gamma - b_i}, each step a
+      // multiply by e^{tau_u} (tile u's total, one per channel): the factors only shrink,
+      // so a step underflows only where the true weight does.
+      float kf[C::R][8];
+#pragma unroll
+      for (int m = 0; m < C::R; ++m)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kf[m][e] = exp2_hw(-lam.v[m][e]);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (u < tile) continue;  // wave-uniform: key tile `tile` serves query tiles u >= tile
-        float D[8];              // r_u - r_tile
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          float s = 0.0f;
-#pragma unroll
-          for (int w = 0; w < 4; ++w)
-            if (w >= tile && w < u) s += tv[w][e];
-          D[e] = s;
-        }
+        if (u < tile) continue;  // wave-uniform
         T* kt = sm.kt + (u * (u + 1) / 2 + tile) * 16 * C::QLD;
 #pragma unroll
-        for (int m = 0; m < C::R; ++m) {
-          float f[8];
+        for (int m = 0; m < C::R; ++m) E::store8_vscaled(kt + (rg * C::R + m) * C::QLD + c8 * 8, st.k[m], kf[m]);
+        float step[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = exp2_hw(D[e] - lam.v[m][e]);
-          E::store8_vscaled(kt + (rg * C::R + m) * C::QLD + c8 * 8, st.k[m], f);
-        }
+        for (int e = 0; e < 8; ++e) step[e] = exp2_hw(tv[u][e]);
+#pragma unroll
+        for (int m = 0; m < C::R; ++m)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) kf[m][e] *= step[e];
       }
-      stage_state_side<T, DK, DVS, true>(sm.kp, sm.eg, st, lam, tv, wave, lane);
+#pragma unroll
+      for (int m = 0; m < C::R; ++m) TokTile<T, DK>::store8_v(sm.kp, 16 * tile + rg * C::R + m, c8 * 8, st.k[m], kf[m]);
+      if (tile == 0 && rg == 0) {  // e^{gamma}: these lanes cover every channel once
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = exp2_hw(tv[0][e] + tv[1][e] + tv[2][e] + tv[3][e]);
+        *reinterpret_cast<float4*>(&sm.eg[c8 * 8]) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4*>(&sm.eg[c8 * 8 + 4]) = make_float4(f[4], f[5], f[6], f[7]);
+      }
       stage_v<T, DK, DVS, true>(sm.vv, st, tid);
     }
     // prefetch chunk c + 1 (the last iteration re-reads its own chunk so that every
