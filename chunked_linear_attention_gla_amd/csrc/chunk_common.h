@@ -17,7 +17,8 @@ struct Cfg {
 
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int QLD = DK + PAD;   // row stride of Qh, Kh (and raw q, k)
-  static constexpr int TLD = 64 + PAD;   // row stride of the attention matrix A
+  static constexpr int TLD = 64 + 4;     // row stride of the attention matrix A (8-byte stores and
+                                         // fragment reads of the bf16 tile are conflict-free)
   static constexpr int QU = 8 * DK / NT;   // 8-element q (and k) units per thread per chunk
   static constexpr int VU = 8 * DVS / NT;  // 8-element v units per thread per chunk
   static constexpr int DB = DK / 16;       // 16-row blocks of the key dimension
@@ -138,7 +139,8 @@ struct VFrags {
   typename Elem<T>::Frag f[Cfg<T, DK, DVS>::NB][2];
 };
 
-template <typename T, int DK, int DVS>
+// kp: token-major [64][KLD]
+template <typename T, int DK, int DVS, int KLD = DK + 16>
 __device__ __forceinline__ void state_update(StateAcc<T, DK, DVS>& S, const VFrags<T, DK, DVS>& Vf,
                                              const T* kp, float decay, int lane) {
   using E = Elem<T>;
@@ -151,21 +153,22 @@ __device__ __forceinline__ void state_update(StateAcc<T, DK, DVS>& S, const VFra
   for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) {
-      const typename E::Frag ka = TokTile<T, DK>::load(kp, ks * 32, db * 16, lane);
+      const typename E::Frag ka = TokTile<T, DK, KLD>::load(kp, ks * 32, db * 16, lane);
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb) E::mfma(S.s[nb][db], ka, Vf.f[nb][ks]);
     }
   }
 }
 
-// v fragments of one wave's columns for both token K-steps of the chunk
-template <typename T, int DK, int DVS>
+// v fragments of one wave's columns for both token K-steps of the chunk; vv: [64][VLD]
+template <typename T, int DK, int DVS, int VLD = DVS + 16>
 __device__ __forceinline__ void load_v_frags(VFrags<T, DK, DVS>& Vf, const T* vv, int wave, int lane) {
   using C = Cfg<T, DK, DVS>;
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Vf.f[nb][ks] = TokTile<T, DVS>::load(vv, ks * 32, wave * C::CPW + nb * 16, lane);
+    for (int ks = 0; ks < 2; ++ks)
+      Vf.f[nb][ks] = TokTile<T, DVS, VLD>::load(vv, ks * 32, wave * C::CPW + nb * 16, lane);
 }
 
 // Initial state of a segment: S0 (or zero; stored [dv][dk] when s0_transposed),

@@ -83,11 +83,16 @@ struct PrepCfg {
   static constexpr int NT = 256;
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int QLD = DK + PAD;
-  static constexpr int TLD = 64 + PAD;
+  static constexpr int TLD = 64 + 4;   // A row stride: its 8-byte stores and fragment reads are conflict-free
   static constexpr int QU = 8 * DK / NT;
   static constexpr int VU = 8 * DV / NT;
   static constexpr int KS = DK / 32;
-  static constexpr int MLD = 65;
+  // fp32 16x16 blocks: M is read as the left operand of the fp32 products (row r,
+  // column 4s + g: conflict-free at a stride of 2 mod 32 words); Tinv is read as both
+  // operands and written by store16, for which 68 is the best single stride
+  static constexpr int MLD = 66;
+  static constexpr int FLD = 68;
+  static constexpr int SLD = 20;  // scratch blocks: written by store16, read as the right operand
 };
 
 // LDS regions are reused across the phases of the pass (keys for L, then the
@@ -110,8 +115,8 @@ struct PrepSmem {
     float mf[64][C::MLD];         // M = diag(beta) L (strictly lower)
     T tb[64 * C::TLD];            // Tinv in the operand dtype
   } u2;
-  float tf[64][C::MLD];           // Tinv (fp32)
-  float scr[4][16][17];
+  float tf[64][C::FLD];           // Tinv (fp32)
+  float scr[4][16][C::SLD];
   float sb[64];
   float sbeta[64];
 };
@@ -201,11 +206,11 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     if (J >= 0) {  // wave-uniform
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int K = J; K < I; ++K)
-        mm16(acc, &sm.u2.mf[16 * I][16 * K], C::MLD, &sm.tf[16 * K][16 * J], C::MLD, lane);
-      store16(&sm.scr[I][0][0], 17, acc, 1.0f, lane);
+        mm16(acc, &sm.u2.mf[16 * I][16 * K], C::MLD, &sm.tf[16 * K][16 * J], C::FLD, lane);
+      store16(&sm.scr[I][0][0], C::SLD, acc, 1.0f, lane);
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
-      mm16(x, &sm.tf[16 * I][16 * I], C::MLD, &sm.scr[I][0][0], 17, lane);
-      store16(&sm.tf[16 * I][16 * J], C::MLD, x, -1.0f, lane);
+      mm16(x, &sm.tf[16 * I][16 * I], C::FLD, &sm.scr[I][0][0], C::SLD, lane);
+      store16(&sm.tf[16 * I][16 * J], C::FLD, x, -1.0f, lane);
     }
     __syncthreads();
   }
@@ -259,12 +264,17 @@ struct DoCfg {
   static constexpr int NT = 64 * NW;
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int QLD = DK + PAD;
-  static constexpr int TLD = 64 + PAD;
+  static constexpr int TLD = 64 + 4;   // A row stride: its 8-byte stores and fragment reads are conflict-free
   static constexpr int QU = 8 * DK / NT;
   static constexpr int DB = DK / 16;
   static constexpr int KS = DK / 32;
   static_assert(QU >= 1 && QU * NT == 8 * DK, "staging must divide evenly");
 };
+
+// U is written with 8-byte stores in the accumulator layout, which conflict less at a
+// row stride of NCOL + 8 than at the NCOL + 16 of the other token-major tiles.
+template <typename T, int NCOL>
+using UTile = TokTile<T, NCOL, NCOL + 8>;
 
 template <typename T, int DK, int DVS>
 struct DoSmem {
@@ -273,7 +283,7 @@ struct DoSmem {
   T kh[64 * C::QLD];
   T wn[64 * C::QLD];              // -W
   T kp[TokTile<T, DK>::SIZE];     // k e^{gamma - b}, token-major
-  T uu[TokTile<T, DVS>::SIZE];    // U of the slice, token-major
+  T uu[UTile<T, DVS>::SIZE];      // U of the slice, token-major
   T a[64 * C::TLD];
 };
 
@@ -282,7 +292,7 @@ struct DsSmem {
   using C = DoCfg<T, DK, DVS>;
   T wn[64 * C::QLD];
   T kp[TokTile<T, DK>::SIZE];
-  T uu[TokTile<T, DVS>::SIZE];
+  T uu[UTile<T, DVS>::SIZE];
 };
 
 // One chunk of (q,) k, W, Ut and b on its way to LDS / registers.  Ut lands directly
@@ -360,10 +370,10 @@ __device__ __forceinline__ void effective_writes(floatx4 (&ut)[4], const typenam
     // ut[jb][e] = U[16 jb + r16][colr + 4 g + e]
     const int row = jb * 16 + r16;
     if constexpr (sizeof(T) == 2) {
-      E::store4(uu + row * TokTile<T, DVS>::LD + colr + 4 * g, ut[jb][0], ut[jb][1], ut[jb][2], ut[jb][3]);
+      E::store4(uu + row * UTile<T, DVS>::LD + colr + 4 * g, ut[jb][0], ut[jb][1], ut[jb][2], ut[jb][3]);
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) uu[(colr + 4 * g + e) * TokTile<T, DVS>::LD + row] = ut[jb][e];
+      for (int e = 0; e < 4; ++e) uu[(colr + 4 * g + e) * UTile<T, DVS>::LD + row] = ut[jb][e];
     }
   }
 }
@@ -436,7 +446,7 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
     __syncthreads();
     typename E::Frag Uf[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Uf[ks] = TokTile<T, NCOL>::load(sm.uu, ks * 32, wave * 16, lane);
+    for (int ks = 0; ks < 2; ++ks) Uf[ks] = UTile<T, NCOL>::load(sm.uu, ks * 32, wave * 16, lane);
     delta_state_update<T, DK, NCOL>(S, Uf, sm.kp, exp_e(cd.gam), lane);
     __syncthreads();
   }
@@ -573,7 +583,7 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
     {
       typename E::Frag Uf[2];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) Uf[ks] = TokTile<T, DVS>::load(sm.uu, ks * 32, wave * 16, lane);
+      for (int ks = 0; ks < 2; ++ks) Uf[ks] = UTile<T, DVS>::load(sm.uu, ks * 32, wave * 16, lane);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll

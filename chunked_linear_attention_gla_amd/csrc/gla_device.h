@@ -249,10 +249,16 @@ template <> struct Elem<float> {
 // first half of the fragment; rows 16 further give the second half.
 // fp32: there is no 32-bit transpose read, so the tile is stored transposed
 // [NCOL][64 tokens] and read with ordinary fragment loads.
-template <typename T, int NCOL> struct TokTile;
+// LDX: row stride in elements.  One transposing read covers 8 rows x 32 bytes per
+// 32-lane half; a stride of NCOL + 16 (an odd multiple of 8 banks) puts those rows in
+// disjoint banks, where NCOL + 8 costs a 2-way bank conflict on every read (measured
+// with SQ_LDS_BANK_CONFLICT).  A tile that is also written with 8-byte stores in the
+// accumulator layout (16 rows of one column piece per store cycle) is better at
+// NCOL + 8: those stores are 2-way there and 4-way at NCOL + 16.
+template <typename T, int NCOL, int LDX = NCOL + 16> struct TokTile;
 
-template <int NCOL> struct TokTile<bf16, NCOL> {
-  static constexpr int LD = NCOL + 8;    // row stride (elements) of [token][col]
+template <int NCOL, int LDX> struct TokTile<bf16, NCOL, LDX> {
+  static constexpr int LD = LDX;         // row stride (elements) of [token][col]
   static constexpr int SIZE = 64 * LD;
   using E = Elem<bf16>;
   __device__ static __forceinline__ void store8(bf16* t, int row, int col, const E::Vec8& v, float s) {
@@ -278,7 +284,7 @@ template <int NCOL> struct TokTile<bf16, NCOL> {
   }
 };
 
-template <int NCOL> struct TokTile<float, NCOL> {
+template <int NCOL, int LDX> struct TokTile<float, NCOL, LDX> {
   static constexpr int LD = 64 + 4;      // row stride (elements) of [col][token]
   static constexpr int SIZE = NCOL * LD;
   using E = Elem<float>;

@@ -55,7 +55,7 @@ struct PcCfg {
   static constexpr int NB = CPW / 16;          // 16-column blocks per wave (1)
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int QLD = DK + PAD;
-  static constexpr int TLD = 64 + PAD;
+  static constexpr int TLD = 64 + 4;   // A row stride: its 8-byte stores and fragment reads are conflict-free
   static constexpr int C8 = DK / 8;            // 8-column groups of a row
   static constexpr int C8W = C8 / HALVES;      // ... staged by one wave
   static constexpr int RG = 64 / C8W;          // lanes of one column group within a tile

@@ -51,22 +51,25 @@ struct WsCfg {
   static constexpr int NSW = 4;              // staging waves
   static constexpr int NT = 64 * (NCW + NSW);
   static constexpr int SNT = 64 * NSW;       // staging threads
-  static constexpr int LD = DK + 8;          // row stride of qh, kh, kp (= TokTile<bf16, DK>::LD)
-  static constexpr int VLD = DVS + 8;        // row stride of vv (= TokTile<bf16, DVS>::LD)
+  static constexpr int LD = DK + 8;          // row stride of qh, kh (row-major fragment reads)
+  // row strides of the token-major kp and vv: 16 elements of padding make their
+  // transposing reads conflict-free; the ablation, 4 KB short of room, keeps 8
+  static constexpr int KLD = DK + (DIAG ? 8 : 16);
+  static constexpr int VLD = DVS + (DIAG ? 8 : 16);
   static constexpr int TLD = 64 + 4;         // row stride of A
   static constexpr int QU = 8 * DK / SNT;    // 16-byte q (and k) pieces per staging thread
   static constexpr int VU = 8 * DVS / SNT;   // 16-byte v pieces per staging thread
   static constexpr int PIECES = DK / 8;      // 16-byte pieces per q/k row
   static_assert(QU >= 1 && QU * SNT == 8 * DK, "q staging must divide evenly");
   static_assert(VU >= 1 && VU * SNT == 8 * DVS, "v staging must divide evenly");
-  static_assert(TokTile<bf16, DK>::LD == LD && TokTile<bf16, DVS>::LD == VLD, "tile strides");
+
 };
 
 template <int DK, int DVS, bool DIAG>
 struct WsSmem {
   using W = WsCfg<DK, DVS, DIAG>;
   bf16 qh[2][64 * W::LD];          // Qh[j][d]
-  bf16 kp[2][64 * W::LD];          // k_i e^{gamma - b_i}, [i][d]
+  bf16 kp[2][64 * W::KLD];         // k_i e^{gamma - b_i}, [i][d]
   bf16 vv[2][64 * W::VLD];         // v[i][n]
   bf16 kh[64 * W::LD];             // Kh[i][d]
   bf16 a[64 * W::TLD];             // A[j][i]
@@ -265,7 +268,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) Sf[nb][ks] = E::from_acc(S.s[nb][2 * ks], S.s[nb][2 * ks + 1]);
       VFrags<bf16, DK, DVS> Vf;
-      load_v_frags<bf16, DK, DVS>(Vf, sm.vv[slot], cw, lane);
+      load_v_frags<bf16, DK, DVS, W::VLD>(Vf, sm.vv[slot], cw, lane);
 
       floatx4 O[4][C::NB];
 #pragma unroll
@@ -298,7 +301,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
           for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], Vf.f[nb][ks], ab);
         }
       }
-      state_update<bf16, DK, DVS>(S, Vf, sm.kp[slot], exp_e(cd.gam), lane);
+      state_update<bf16, DK, DVS, W::KLD>(S, Vf, sm.kp[slot], exp_e(cd.gam), lane);
       // lane holds o[t0 + 16 jb + r16][wcol + 16 nb + 4 g + 0..3]; rows outside the
       // head get an out-of-range offset and are dropped
 #pragma unroll
@@ -329,7 +332,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         kv.u = stg.k[m];
         E::store8_scaled(sm.qh[ns] + row * W::LD + c8 * 8, qv, exp_e(brow[m] - rj));
         E::store8_scaled(sm.kh + row * W::LD + c8 * 8, kv, exp_e((DIAG ? cd.end(tile) : rj) - brow[m]));
-        E::store8_scaled(sm.kp[ns] + row * W::LD + c8 * 8, kv, exp_e(cd.gam - brow[m]));
+        E::store8_scaled(sm.kp[ns] + row * W::KLD + c8 * 8, kv, exp_e(cd.gam - brow[m]));
         if (DIAG) {
           *reinterpret_cast<uint4*>(sm.qr + row * DK + raw_piece(c8, row) * 8) = stg.q[m];
           *reinterpret_cast<uint4*>(sm.kr + row * DK + raw_piece(c8, row) * 8) = stg.k[m];
@@ -403,7 +406,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
 template <int DK, int DVS>
 struct WsSegSmem {
   using W = WsCfg<DK, DVS, false>;
-  bf16 kp[2][64 * W::LD];   // k_i e^{gamma - b_i}, [i][d]
+  bf16 kp[2][64 * W::KLD];  // k_i e^{gamma - b_i}, [i][d]
   bf16 vv[2][64 * W::VLD];  // v[i][n]
   float gam[2];             // gamma of the chunk in each buffer set
 };
@@ -446,8 +449,8 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
       const float gam = sm.gam[slot];
       gsum += gam;
       VFrags<bf16, DK, DVS> Vf;
-      load_v_frags<bf16, DK, DVS>(Vf, sm.vv[slot], cw, lane);
-      state_update<bf16, DK, DVS>(S, Vf, sm.kp[slot], exp_e(gam), lane);
+      load_v_frags<bf16, DK, DVS, W::VLD>(Vf, sm.vv[slot], cw, lane);
+      state_update<bf16, DK, DVS, W::KLD>(S, Vf, sm.kp[slot], exp_e(gam), lane);
       __syncthreads();
     }
     store_state<bf16, DK, DVS>(S, p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv, p.dv, wcol, g, r16);
@@ -465,7 +468,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
         const int row = u / (DK / 8), c8 = u % (DK / 8);
         E::Vec8 kv;
         kv.u = stg.k[m];
-        E::store8_scaled(sm.kp[ns] + row * W::LD + c8 * 8, kv, exp_e(cd.gam - brow[m]));
+        E::store8_scaled(sm.kp[ns] + row * W::KLD + c8 * 8, kv, exp_e(cd.gam - brow[m]));
       }
 #pragma unroll
       for (int m = 0; m < W::VU; ++m) {
