@@ -116,7 +116,7 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) grad_dx_kernel(
     float* __restrict__ dx, long long Tlen, int nchunks) {
   using X = DxCfg<T, DK, DV>;
   using E = Elem<T>;
-  __shared__ DxSmem<T, DK, DV> sm;
+  __shared__ __attribute__((aligned(16))) DxSmem<T, DK, DV> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;

@@ -130,7 +130,7 @@ __device__ __forceinline__ void stage_state_operands(T* kp, T* vv, const Staged<
 template <typename T, int DK, int DVS>
 __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(ChunkParams p) {
   using C = Cfg<T, DK, DVS>;
-  __shared__ SegSmem<T, DK, DVS> sm;
+  __shared__ __attribute__((aligned(16))) SegSmem<T, DK, DVS> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -191,7 +191,7 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT))
 __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chunk_output_kernel(ChunkParams p) {
   using E = Elem<T>;
   using C = Cfg<T, DK, DVS>;
-  __shared__ OutSmem<T, DK, DVS, DIAG> sm;
+  __shared__ __attribute__((aligned(16))) OutSmem<T, DK, DVS, DIAG> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;

@@ -125,7 +125,7 @@ template <typename T, int DK, int DV>
 __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   using E = Elem<T>;
   using C = PrepCfg<T, DK, DV>;
-  __shared__ PrepSmem<T, DK, DV> sm;
+  __shared__ __attribute__((aligned(16))) PrepSmem<T, DK, DV> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -400,7 +400,7 @@ template <typename T, int DK, int NCOL, bool PHI>
 __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel(DeltaParams p) {
   using E = Elem<T>;
   using C = DoCfg<T, DK, NCOL>;
-  __shared__ DsSmem<T, DK, NCOL> sm;
+  __shared__ __attribute__((aligned(16))) DsSmem<T, DK, NCOL> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -463,7 +463,7 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
   using E = Elem<T>;
   using F = Elem<float>;
   using C = DoCfg<T, DK, DVS>;
-  __shared__ DoSmem<T, DK, DVS> sm;
+  __shared__ __attribute__((aligned(16))) DoSmem<T, DK, DVS> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;

@@ -319,7 +319,7 @@ __device__ __forceinline__ void pc_store_state(const PcState<T, DK, DVS>& S, flo
 template <typename T, int DK, int DVS>
 __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_segment_state_kernel(PcParams p) {
   using C = PcCfg<T, DK, DVS>;
-  __shared__ PcSegSmem<T, DK, DVS> sm;
+  __shared__ __attribute__((aligned(16))) PcSegSmem<T, DK, DVS> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
@@ -387,7 +387,7 @@ template <typename T, int DK, int DVS>
 __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kernel(PcParams p) {
   using E = Elem<T>;
   using C = PcCfg<T, DK, DVS>;
-  __shared__ PcSmem<T, DK, DVS> sm;
+  __shared__ __attribute__((aligned(16))) PcSmem<T, DK, DVS> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;

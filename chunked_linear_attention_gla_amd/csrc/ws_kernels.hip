@@ -210,7 +210,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
   using W = WsCfg<DK, DVS, DIAG>;
   using C = typename W::C;
   using E = Elem<bf16>;
-  __shared__ WsSmem<DK, DVS, DIAG> sm;
+  __shared__ __attribute__((aligned(16))) WsSmem<DK, DVS, DIAG> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool compute = wave < W::NCW;  // wave-uniform role
@@ -416,7 +416,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
   using W = WsCfg<DK, DVS, false>;
   using C = typename W::C;
   using E = Elem<bf16>;
-  __shared__ WsSegSmem<DK, DVS> sm;
+  __shared__ __attribute__((aligned(16))) WsSegSmem<DK, DVS> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool compute = wave < W::NCW;
