@@ -95,9 +95,11 @@ struct PrepCfg {
   static constexpr int SLD = 20;  // scratch blocks: written by store16, read as the right operand
 };
 
-// LDS regions are reused across the phases of the pass (keys for L, then the
-// right-hand sides of the products; M, then Tinv in the operand dtype), which keeps
-// two workgroups on a compute unit.
+// LDS regions are reused across the phases of the pass: u1 holds the keys for L,
+// then Tinv in fp32 with its scratch blocks, then the right-hand sides of the
+// products; u2 holds M, then Tinv in the operand dtype.  At d = 128 that is 53 KB,
+// three workgroups per compute unit (the pass is a chain of short phases between
+// barriers, so the workgroups in flight set its speed).
 template <typename T, int DK, int DV>
 struct PrepSmem {
   using C = PrepCfg<T, DK, DV>;
@@ -107,6 +109,10 @@ struct PrepSmem {
       T kh[64 * C::QLD];          // k_s e^{r_u(s) - b_s}
     } l;
     struct {
+      float tf[64][C::FLD];       // Tinv (fp32)
+      float scr[4][16][C::SLD];
+    } t;
+    struct {
       T kb[TokTile<T, DK>::SIZE]; // beta_s e^{b_s} k_s, token-major
       T vb[TokTile<T, DV>::SIZE]; // beta_s v_s, token-major
     } r;
@@ -115,8 +121,6 @@ struct PrepSmem {
     float mf[64][C::MLD];         // M = diag(beta) L (strictly lower)
     T tb[64 * C::TLD];            // Tinv in the operand dtype
   } u2;
-  float tf[64][C::FLD];           // Tinv (fp32)
-  float scr[4][16][C::SLD];
   float sb[64];
   float sbeta[64];
 };
@@ -196,7 +200,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
       x[i] = s;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.tf[o + i][o + j] = x[i];
+    for (int i = 0; i < 16; ++i) sm.u1.t.tf[o + i][o + j] = x[i];
   }
   __syncthreads();
   // block row I, column J < I:  X_IJ = -D_I sum_{J <= K < I} M_IK X_KJ, by distance I - J
@@ -206,20 +210,21 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     if (J >= 0) {  // wave-uniform
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int K = J; K < I; ++K)
-        mm16(acc, &sm.u2.mf[16 * I][16 * K], C::MLD, &sm.tf[16 * K][16 * J], C::FLD, lane);
-      store16(&sm.scr[I][0][0], C::SLD, acc, 1.0f, lane);
+        mm16(acc, &sm.u2.mf[16 * I][16 * K], C::MLD, &sm.u1.t.tf[16 * K][16 * J], C::FLD, lane);
+      store16(&sm.u1.t.scr[I][0][0], C::SLD, acc, 1.0f, lane);
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
-      mm16(x, &sm.tf[16 * I][16 * I], C::FLD, &sm.scr[I][0][0], C::SLD, lane);
-      store16(&sm.tf[16 * I][16 * J], C::FLD, x, -1.0f, lane);
+      mm16(x, &sm.u1.t.tf[16 * I][16 * I], C::FLD, &sm.u1.t.scr[I][0][0], C::SLD, lane);
+      store16(&sm.u1.t.tf[16 * I][16 * J], C::FLD, x, -1.0f, lane);
     }
     __syncthreads();
   }
   // operand copy of Tinv (over M, no longer read), zero above the diagonal blocks;
-  // right-hand sides of the products (over the keys for L, no longer read)
+  // then the right-hand sides of the products over the fp32 Tinv
   for (int e = tid; e < 64 * 64; e += C::NT) {
     const int t = e >> 6, s = e & 63;
-    sm.u2.tb[t * C::TLD + s] = E::cvt((s >> 4) <= (t >> 4) ? sm.tf[t][s] : 0.0f);
+    sm.u2.tb[t * C::TLD + s] = E::cvt((s >> 4) <= (t >> 4) ? sm.u1.t.tf[t][s] : 0.0f);
   }
+  __syncthreads();
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
