@@ -490,9 +490,9 @@ def backward_result(gla, gin, torch, w, path, steps, warmup):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (this build has no "
-              f"multi-GPU path; heads shard across GPUs with no communication, see DESIGN.md)",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (there is no "
+              f"multi-GPU path; (batch, head) pairs are independent, so heads would shard across "
+              f"GPUs with no communication)", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.copy_calibration:
