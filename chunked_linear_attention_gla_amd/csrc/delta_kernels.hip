@@ -47,6 +47,22 @@ __device__ __forceinline__ uint32_t dl_row(uint32_t t, uint32_t Tn, uint32_t row
   return t < Tn ? t * row_bytes : kDroppedOffset;
 }
 
+// Row-major bf16 tiles read as MFMA fragments (Qh, Kh, -W, the key operands of L): a
+// fragment read (ds_read2_b64) takes one 8-byte piece from each of 16 rows, and at a
+// row stride of 136 elements rows r and r + 8 fall on the same bank pair, a 2-way
+// conflict on every read.  Rows with bit 3 set therefore hold each 16-byte group with
+// its 8-byte halves swapped: element column c of row r is at c ^ frag_swz<T>(r).  The
+// staging loops below give each wave whole 8-row groups (the row advances by a
+// multiple of 16 per pass), so a store's swap is wave-uniform.
+template <typename T>
+__device__ __forceinline__ int frag_swz(int row) {
+  return Elem<T>::kSwizzle ? (row & 8) >> 1 : 0;
+}
+template <typename T>
+__device__ __forceinline__ bool frag_swap(int row) {
+  return __builtin_amdgcn_readfirstlane(frag_swz<T>(row)) != 0;
+}
+
 // acc += X Z for 16x16 fp32 blocks in LDS (X row stride ldx, Z row stride ldz):
 // afterwards lane (g, r16) holds (X Z)[4 g + e][r16] in acc[e].
 __device__ __forceinline__ void mm16(floatx4& acc, const float* X, int ldx, const float* Z, int ldz, int lane) {
@@ -164,8 +180,9 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
     const float br = sm.sb[row], r = ref(row >> 4);
-    E::store8_scaled(sm.u1.l.kq + row * C::QLD + c8 * 8, kv[m], exp_e(br - r));
-    E::store8_scaled(sm.u1.l.kh + row * C::QLD + c8 * 8, kv[m], exp_e(r - br));
+    const bool sw = frag_swap<T>(row);
+    E::store8_scaled_sw(sm.u1.l.kq + row * C::QLD + c8 * 8, kv[m], exp_e(br - r), sw);
+    E::store8_scaled_sw(sm.u1.l.kh + row * C::QLD + c8 * 8, kv[m], exp_e(r - br), sw);
   }
   __syncthreads();
 
@@ -177,8 +194,8 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      E::mfma(acc, E::load_frag(sm.u1.l.kh + (ib * 16 + r16) * C::QLD, ks * 32 + 4 * g),
-              E::load_frag(sm.u1.l.kq + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+      E::mfma(acc, E::load_frag(sm.u1.l.kh + (ib * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))),
+              E::load_frag(sm.u1.l.kq + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
     // acc[e]: row t = 16 jb + r16, column s = 16 ib + 4 g + e
     const int tr = jb * 16 + r16;
     const float f = (jb == ib ? 1.0f : exp_e(ref(jb) - ref(ib))) * sm.sbeta[tr];
@@ -354,7 +371,7 @@ __device__ __forceinline__ void stage_w_kp(T* wn, T* kp, const DoStaged<T, DK, D
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
-    E::store8_neg(wn + row * C::QLD + c8 * 8, st.w[m]);
+    E::store8_neg_sw(wn + row * C::QLD + c8 * 8, st.w[m], frag_swap<T>(row));
     TokTile<T, DK>::store8(kp, row, c8 * 8, st.k[m], exp_e(cd.gam - cd.at(row)));
   }
 }
@@ -371,7 +388,7 @@ __device__ __forceinline__ void effective_writes(floatx4 (&ut)[4], const typenam
   for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      E::mfma(ut[jb], Sf[ks], E::load_frag(wn + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+      E::mfma(ut[jb], Sf[ks], E::load_frag(wn + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
     // ut[jb][e] = U[16 jb + r16][colr + 4 g + e]
     const int row = jb * 16 + r16;
     if constexpr (sizeof(T) == 2) {
@@ -541,8 +558,9 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
     for (int m = 0; m < C::QU; ++m) {
       const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
       const float br = cd.at(row), r = cd.r(row >> 4);
-      E::store8_scaled(sm.qh + row * C::QLD + c8 * 8, st.q[m], exp_e(br - r));
-      E::store8_scaled(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(r - br));
+      const bool sw = frag_swap<T>(row);
+      E::store8_scaled_sw(sm.qh + row * C::QLD + c8 * 8, st.q[m], exp_e(br - r), sw);
+      E::store8_scaled_sw(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(r - br), sw);
     }
     stage_w_kp<T, DK, DVS, true, true>(sm.wn, sm.kp, st, cd, tid);
     // ---- (2) prefetch chunk c + 1 (the last iteration re-reads its own chunk)
@@ -557,8 +575,8 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        E::mfma(acc, E::load_frag(sm.kh + (ib * 16 + r16) * C::QLD, ks * 32 + 4 * g),
-                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+        E::mfma(acc, E::load_frag(sm.kh + (ib * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))),
+                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
       const float f = (jb == ib) ? 1.0f : exp_e(cd.r(jb) - cd.r(ib));
       float vals[4];
 #pragma unroll
@@ -577,7 +595,7 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
         O[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks)
-          E::mfma(O[jb], Sf[ks], E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+          E::mfma(O[jb], Sf[ks], E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
         if (jb > 0) O[jb] *= exp_e(cd.r(jb));
       }
       effective_writes<T, DK, DVS>(ut, Sf, sm.wn, sm.uu, wave * 16, lane);

@@ -135,6 +135,21 @@ template <> struct Elem<bf16> {
     constexpr uint32_t m = 0x80008000u;
     *reinterpret_cast<uint4*>(dst) = make_uint4(v.u.x ^ m, v.u.y ^ m, v.u.z ^ m, v.u.w ^ m);
   }
+  // The same two stores into a row that holds each 16-byte group with its two 8-byte
+  // halves swapped when `swap` (a fragment-read swizzle; see the kernels using it).
+  static constexpr bool kSwizzle = true;
+  __device__ static __forceinline__ void store8_scaled_sw(bf16* dst, const Vec8& v, float s, bool swap) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = cvt(get(v, e) * s);
+    if (swap) o = __builtin_shufflevector(o, o, 4, 5, 6, 7, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x8*>(dst) = o;
+  }
+  __device__ static __forceinline__ void store8_neg_sw(bf16* dst, const Vec8& v, bool swap) {
+    constexpr uint32_t m = 0x80008000u;
+    const uint4 n = make_uint4(v.u.x ^ m, v.u.y ^ m, v.u.z ^ m, v.u.w ^ m);
+    *reinterpret_cast<uint4*>(dst) = swap ? make_uint4(n.z, n.w, n.x, n.y) : n;
+  }
   // store 8 elements, each with its own scale
   __device__ static __forceinline__ void store8_vscaled(bf16* dst, const Vec8& v, const float (&s)[8]) {
     bf16x8 o;
@@ -208,6 +223,12 @@ template <> struct Elem<float> {
     *reinterpret_cast<float4*>(dst) = make_float4(flip(v.a.x), flip(v.a.y), flip(v.a.z), flip(v.a.w));
     *reinterpret_cast<float4*>(dst + 4) = make_float4(flip(v.b.x), flip(v.b.y), flip(v.b.z), flip(v.b.w));
   }
+  // fp32 tiles are not swizzled (their fragment reads are 16-byte pieces)
+  static constexpr bool kSwizzle = false;
+  __device__ static __forceinline__ void store8_scaled_sw(float* dst, const Vec8& v, float s, bool) {
+    store8_scaled(dst, v, s);
+  }
+  __device__ static __forceinline__ void store8_neg_sw(float* dst, const Vec8& v, bool) { store8_neg(dst, v); }
   __device__ static __forceinline__ void store8_vscaled(float* dst, const Vec8& v, const float (&s)[8]) {
     *reinterpret_cast<float4*>(dst) = make_float4(v.a.x * s[0], v.a.y * s[1], v.a.z * s[2], v.a.w * s[3]);
     *reinterpret_cast<float4*>(dst + 4) = make_float4(v.b.x * s[4], v.b.y * s[5], v.b.z * s[6], v.b.w * s[7]);
