@@ -145,6 +145,13 @@ template <> struct Elem<bf16> {
     if (swap) o = __builtin_shufflevector(o, o, 4, 5, 6, 7, 0, 1, 2, 3);
     *reinterpret_cast<bf16x8*>(dst) = o;
   }
+  __device__ static __forceinline__ void store8_vscaled_sw(bf16* dst, const Vec8& v, const float (&s)[8], bool swap) {
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = cvt(get(v, e) * s[e]);
+    if (swap) o = __builtin_shufflevector(o, o, 4, 5, 6, 7, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x8*>(dst) = o;
+  }
   __device__ static __forceinline__ void store8_neg_sw(bf16* dst, const Vec8& v, bool swap) {
     constexpr uint32_t m = 0x80008000u;
     const uint4 n = make_uint4(v.u.x ^ m, v.u.y ^ m, v.u.z ^ m, v.u.w ^ m);
@@ -229,6 +236,9 @@ template <> struct Elem<float> {
     store8_scaled(dst, v, s);
   }
   __device__ static __forceinline__ void store8_neg_sw(float* dst, const Vec8& v, bool) { store8_neg(dst, v); }
+  __device__ static __forceinline__ void store8_vscaled_sw(float* dst, const Vec8& v, const float (&s)[8], bool) {
+    store8_vscaled(dst, v, s);
+  }
   __device__ static __forceinline__ void store8_vscaled(float* dst, const Vec8& v, const float (&s)[8]) {
     *reinterpret_cast<float4*>(dst) = make_float4(v.a.x * s[0], v.a.y * s[1], v.a.z * s[2], v.a.w * s[3]);
     *reinterpret_cast<float4*>(dst + 4) = make_float4(v.b.x * s[4], v.b.y * s[5], v.b.z * s[6], v.b.w * s[7]);

@@ -143,6 +143,15 @@ struct PcStaged {
   }
 };
 
+// Qh, q e^b and the key tiles are read as MFMA fragments (ds_read2_b64: one 8-byte
+// piece from each of 16 rows); at a row stride of 136 elements rows r and r + 8 share
+// a bank pair.  Rows with bit 3 set hold each 16-byte group with its 8-byte halves
+// swapped, so element column c of row r is at c ^ pc_swz<T>(r) (bf16 only).
+template <typename T>
+__device__ __forceinline__ int pc_swz(int row) {
+  return Elem<T>::kSwizzle ? (row & 8) >> 1 : 0;
+}
+
 // Log-decay of one channel in base 2: g log2 e.
 __device__ __forceinline__ float pc_log2_gate(float x, int gate) {
   return gate == kGateBoundedSigmoid ? (-5.0f * kLog2e) * sigmoid_hw(x) : kLog2e * gate_neg_softplus(x);
@@ -459,7 +468,8 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
     for (int m = 0; m < C::R; ++m) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) fq[m][e] = exp2_hw(lam.v[m][e]);
-      E::store8_vscaled(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], fq[m]);
+      E::store8_vscaled_sw(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], fq[m],
+                           pc_swz<T>(rg * C::R + m) != 0);
     }
     __syncthreads();
 
@@ -482,7 +492,8 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
           float f[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) f[e] = fq[m][e] * er[e];
-          E::store8_vscaled(sm.qe + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f);
+          E::store8_vscaled_sw(sm.qe + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f,
+                               pc_swz<T>(rg * C::R + m) != 0);
         }
       }
       // Key tile `tile` serves the query tiles u >= tile as K^(u) = k e^{r_u - b}, and the
@@ -500,7 +511,8 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         if (u < tile) continue;  // wave-uniform
         T* kt = sm.kt + (u * (u + 1) / 2 + tile) * 16 * C::QLD;
 #pragma unroll
-        for (int m = 0; m < C::R; ++m) E::store8_vscaled(kt + (rg * C::R + m) * C::QLD + c8 * 8, st.k[m], kf[m]);
+        for (int m = 0; m < C::R; ++m)
+          E::store8_vscaled_sw(kt + (rg * C::R + m) * C::QLD + c8 * 8, st.k[m], kf[m], pc_swz<T>(rg * C::R + m) != 0);
         float step[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) step[e] = exp2_hw(tv[u][e]);
@@ -533,8 +545,8 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        E::mfma(acc, E::load_frag(sm.kt + (t * 16 + r16) * C::QLD, ks * 32 + 4 * g),
-                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g));
+        E::mfma(acc, E::load_frag(sm.kt + (t * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ pc_swz<T>(r16))),
+                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ pc_swz<T>(r16))));
       // acc[e]: j = 16 jb + r16, i = 16 ib + 4 g + e; causal select on the diagonal tile
       float vals[4];
 #pragma unroll
@@ -560,7 +572,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const typename E::Frag qb = E::load_frag(sm.qe + (jb * 16 + r16) * C::QLD, ks * 32 + 4 * g);
+          const typename E::Frag qb = E::load_frag(sm.qe + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ pc_swz<T>(r16)));
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], sf[nb][ks], qb);
         }
