@@ -32,6 +32,11 @@ def compile_command(out: str = LIB, extra=()) -> list:
         hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         # keep hipcc from forming packed fp32 arithmetic (v_pk_*_f32)
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # start every block that is only reached by a jump (loop heads among them) on a
+        # 64-byte boundary; the padding is never executed.  Measured on the 64K-token
+        # output pass: unaligned builds ran 0.545 or 0.58 ms depending on where an
+        # unrelated code change left the loop heads; aligned builds run 0.545 ms
+        "-mllvm", "-align-all-nofallthru-blocks=6",
         "-Wall", "-Wno-unused-function",
         f"-I{INCLUDE}", f"-I{CSRC}",
         *[os.path.join(CSRC, s) for s in SOURCES],

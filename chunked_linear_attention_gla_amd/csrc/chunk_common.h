@@ -171,14 +171,19 @@ __device__ __forceinline__ void load_v_frags(VFrags<T, DK, DVS>& Vf, const T* vv
       Vf.f[nb][ks] = TokTile<T, DVS, VLD>::load(vv, ks * 32, wave * C::CPW + nb * 16, lane);
 }
 
-// Initial state of a segment: S0 (or zero; stored [dv][dk] when s0_transposed),
-// folded with the local final states of the earlier segments of the same head,
-// S <- e^{Gamma_p} S + H_p for p < seg.
+// Initial state of a segment: S0 (or zero; stored [dv][dk] when s0_transposed)
+// decayed over the earlier segments of the same unit, plus the state P_{seg-1}
+// that the segment prefix scan leaves for them (reached from a zero state at the
+// unit's start; stored transposed when seg_transposed):
+//   S = e^{Gamma_0 + .. + Gamma_{seg-1}} S0 + P_{seg-1}.
+// All loads are issued before the first use, so this is one round trip to memory.
 // The wave's slice of S: d = 16 db + 4 g + e, n = wcol + 16 nb + r16.
 template <typename T, int DK, int DVS>
 __device__ __forceinline__ void load_initial_state(StateAcc<T, DK, DVS>& S, const ChunkParams& p, int bh, int seg,
                                                    int wcol, int g, int r16) {
   using C = Cfg<T, DK, DVS>;
+  const long long i0 = (long long)bh * DK * p.dv;
+  floatx4 s0[C::NB][C::DB], pre[C::NB][C::DB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
@@ -187,25 +192,36 @@ __device__ __forceinline__ void load_initial_state(StateAcc<T, DK, DVS>& S, cons
       for (int e = 0; e < 4; ++e) {
         const int d = db * 16 + 4 * g + e;
         const int n = wcol + nb * 16 + r16;
-        const long long i0 = (long long)bh * DK * p.dv;
-        S.s[nb][db][e] = !p.S0 ? 0.0f
-                         : p.s0_transposed ? p.S0[i0 + (long long)n * DK + d]
-                                           : p.S0[i0 + (long long)d * p.dv + n];
+        s0[nb][db][e] = !p.S0 ? 0.0f
+                        : p.s0_transposed ? p.S0[i0 + (long long)n * DK + d]
+                                          : p.S0[i0 + (long long)d * p.dv + n];
       }
-  for (int ps = 0; ps < seg; ++ps) {
-    const float f = exp_e(p.seg_decay[(long long)bh * p.segments + ps]);
-    const float* H = p.seg_state + ((long long)bh * (p.segments - 1) + ps) * DK * p.dv;
+  const float* P = seg > 0 ? p.seg_state + ((long long)bh * (p.segments - 1) + seg - 1) * DK * p.dv : nullptr;
 #pragma unroll
-    for (int nb = 0; nb < C::NB; ++nb)
+  for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db)
+    for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = db * 16 + 4 * g + e;
-          const int n = wcol + nb * 16 + r16;
-          S.s[nb][db][e] = f * S.s[nb][db][e] + (p.seg_transposed ? H[(long long)n * DK + d] : H[(long long)d * p.dv + n]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int d = db * 16 + 4 * g + e;
+        const int n = wcol + nb * 16 + r16;
+        pre[nb][db][e] = !P ? 0.0f : p.seg_transposed ? P[(long long)n * DK + d] : P[(long long)d * p.dv + n];
+      }
+  // e^{sum of the earlier segments' log-decays}: lane ps holds Gamma_ps (seg <= 63)
+  float f0 = 1.0f;
+  if (p.S0 && seg > 0) {
+    const int lane = g * 16 + r16;
+    float gl = lane < seg ? p.seg_decay[(long long)bh * p.segments + lane] : 0.0f;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) gl += __shfl_xor(gl, off);
+    f0 = exp_e(gl);
   }
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+    for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S.s[nb][db][e] = f0 * s0[nb][db][e] + pre[nb][db][e];
 }
 
 // Per-chunk state storage (for the backward pass): the state before each chunk,

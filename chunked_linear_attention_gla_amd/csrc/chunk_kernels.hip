@@ -460,11 +460,58 @@ bool chunk_config_built(int dtype, int dk, int slice, bool diag) {
   return dispatch(dtype, dk, slice, diag, ProbeFn{}) == hipSuccess;
 }
 
+// Segment prefix scan, in place: the local final states H_0 .. H_{P-2} of a unit
+// (from zero states, as the pre-pass leaves them) become the states reached from a
+// zero state at the start of the unit,
+//   P_0 = H_0,   P_p = e^{Gamma_p} P_{p-1} + H_p,
+// so that segment p > 0 starts from e^{Gamma_0 + .. + Gamma_{p-1}} S0 + P_{p-1}: one
+// state read per output workgroup instead of a chain of p dependent reads.  Thread =
+// 4 consecutive elements of one unit's states; its loads are issued in batches of 8
+// segments ahead of the arithmetic that consumes them.
+constexpr int kPrefixThreads = 256;
+constexpr int kPrefixBatch = 8;
+
+__global__ void __launch_bounds__(kPrefixThreads) segment_prefix_kernel(float* seg_state, const float* seg_decay,
+                                                                        int segments, int per_state4, int units) {
+  const long long gid = (long long)blockIdx.x * kPrefixThreads + threadIdx.x;
+  const int unit = (int)(gid / per_state4);
+  if (unit >= units) return;
+  const int e4 = (int)(gid - (long long)unit * per_state4);
+  const int nseg = segments - 1;
+  floatx4* H = reinterpret_cast<floatx4*>(seg_state) + (long long)unit * nseg * per_state4 + e4;
+  const float* G = seg_decay + (long long)unit * segments;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < nseg; p0 += kPrefixBatch) {
+    floatx4 h[kPrefixBatch];
+#pragma unroll
+    for (int j = 0; j < kPrefixBatch; ++j) h[j] = H[(long long)min(p0 + j, nseg - 1) * per_state4];
+#pragma unroll
+    for (int j = 0; j < kPrefixBatch; ++j) {
+      const int ps = p0 + j;
+      if (ps < nseg) {
+        acc = ps == 0 ? h[j] : exp_e(G[ps]) * acc + h[j];
+        H[(long long)ps * per_state4] = acc;
+      }
+    }
+  }
+}
+
+hipError_t launch_segment_prefix(const ChunkParams& p, hipStream_t stream) {
+  const int per_state4 = p.dk * p.dv / 4;
+  const long long threads = (long long)p.BH * per_state4;
+  const int blocks = (int)((threads + kPrefixThreads - 1) / kPrefixThreads);
+  hipLaunchKernelGGL(segment_prefix_kernel, dim3(blocks), dim3(kPrefixThreads), 0, stream, p.seg_state,
+                     p.seg_decay, p.segments, per_state4, p.BH);
+  return hipGetLastError();
+}
+
 hipError_t launch_segment_states(const ChunkParams& p, int dtype, hipStream_t stream) {
   if (p.segments <= 1 || p.grid == 0) return hipSuccess;
-  if (ws_kernels_supported(dtype, p.dk, p.dv / p.nslices))
-    return launch_segment_states_ws(p, p.dk, p.dv / p.nslices, stream);
-  return dispatch(dtype, p.dk, p.dv / p.nslices, false, SegFn{p, stream});
+  hipError_t e = ws_kernels_supported(dtype, p.dk, p.dv / p.nslices)
+                     ? launch_segment_states_ws(p, p.dk, p.dv / p.nslices, stream)
+                     : dispatch(dtype, p.dk, p.dv / p.nslices, false, SegFn{p, stream});
+  if (e != hipSuccess || p.segments <= 2) return e;  // a single local state is already its own prefix
+  return launch_segment_prefix(p, stream);
 }
 
 hipError_t launch_chunk_output(const ChunkParams& p, int dtype, bool diag, hipStream_t stream) {
