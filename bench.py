@@ -108,6 +108,27 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
 
 
+def device_copy_rate(torch, nbytes: int = 1 << 30, reps: int = 10) -> dict:
+    """Plain device-to-device copy on the same GPU (torch's copy kernel), for context: what
+    a flat stream of reads and writes reaches here, beside the 8 TB/s published peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(reps):
+        dst.copy_(src)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    gbs = 2 * nbytes / (ms / 1e3) / 1e9
+    del src, dst
+    return {"what": "device-to-device copy of 1 GiB (bytes read + written per second)", "ms": round(ms, 4),
+            "GB_per_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(w, target_s: float, per_channel: bool = False):
     """Time the fp64 oracle on a bounded sample of the workload (all heads, a prefix of
     the sequence sized to take about target_s seconds on this host)."""
@@ -569,6 +590,7 @@ def main():
             "algorithmic_bytes_per_launch": bytes_out,
             "avg_launch_ms": round(ms_out, 4),
         },
+        "context": {"device_copy": device_copy_rate(torch)},
     }
     if w.name == gin.HEADLINE and path == "unified" and not args.plan and not args.no_ablation:
         # the pages' comparison: conventional gate + diagonal branch against the unified
