@@ -16,7 +16,8 @@ struct ChunkParams {
   const float* S0;        // [BH][dk][dv] or nullptr
   float* o;               // [BH][T][dv]
   float* ST;              // [BH][dk][dv]
-  float* seg_state;       // [BH][segments-1][dk][dv]  local final states
+  float* seg_state;       // [BH][segments-1][dk][dv]  local final states, then (after the prefix
+                          //                           scan) the states reached from zero
   float* seg_decay;       // [BH][segments]            total log-decay per segment
   long long T;
   int dk, dv;

@@ -97,8 +97,9 @@ typedef enum {
 /* Launch plan.  Each head's value columns are cut into dv_split slices and its
  * sequence into `segments` contiguous runs of chunks (segment p owns chunks
  * [p*nc/segments, (p+1)*nc/segments), nc = ceil(T/64)); every (head, slice,
- * segment) is one workgroup.  segments > 1 adds a pre-pass that computes each
- * segment's local final state (gla_segment_states).  Results do not depend on
+ * segment) is one workgroup.  segments > 1 adds a pre-pass that computes the
+ * state at the end of every segment but the last (gla_segment_states), so that
+ * each segment can start from its own initial state.  Results do not depend on
  * the plan beyond floating-point summation order. */
 typedef struct {
   int segments;  /* 1 .. GLA_MAX_SEGMENTS, and at most the number of chunks (>= 1 when T = 0) */
@@ -142,9 +143,13 @@ gla_status_t gla_gate_cumsum(const float* x, float* b, int B, int H, long long T
 
 /* Segment pre-pass (only meaningful when plan->segments > 1).  For every head
  * and every segment p but the last, runs the state recurrence over the
- * segment's chunks from a zero state and stores its final state H_p and its
- * total log-decay Gamma_p into `seg_ws` (gla_segment_workspace_size bytes).
- * Uses k, v and b (from gla_gate_cumsum).  Does nothing when segments == 1. */
+ * segment's chunks from a zero state (local final state H_p, total log-decay
+ * Gamma_p), then combines the segments in order, so that `seg_ws`
+ * (gla_segment_workspace_size bytes) receives Gamma_p and
+ *   P_0 = H_0,  P_p = e^{Gamma_p} P_{p-1} + H_p,
+ * the state at the end of segment p reached from a zero state at the start of
+ * the head (gla_chunk_output adds the decayed S0).  Uses k, v and b (from
+ * gla_gate_cumsum).  Does nothing when segments == 1. */
 gla_status_t gla_segment_states(const void* k, const void* v, const float* b,
                                 int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
                                 const gla_plan_t* plan, void* seg_ws, size_t seg_ws_bytes,

@@ -54,6 +54,34 @@ def test_gate_cumsum_matches_fp64(gate, T):
     assert np.all(np.abs(got - ref) <= 1e-6 * np.abs(ref) + 1e-6)
 
 
+@pytest.mark.parametrize("qkv,segments", [("f32", 3), ("f32", 11), ("bf16", 11)])
+def test_segment_states_are_prefix_states(qkv, segments):
+    """Stage entry point gla_segment_states: for every segment p but the last, the
+    workspace holds the segment's total log-decay and the state at the end of segment
+    p reached from a zero state at the start of the head (the pre-pass's local states
+    combined in order).  11 segments exercise the prefix scan's batches of 8."""
+    w, inp = small(64 * 23 + 7, H=2, qkv=qkv, dk=64, dv=64, s0=0.0, x_mean=-6.0, seed=21)
+    plan = gla.Plan(segments, 1)
+    B, H, T = w.B, w.H, w.T
+    b = gla.gate_cumsum(inp["x"])
+    ws = torch.zeros(gla.segment_workspace_size(B, H, T, w.dk, w.dv, plan), dtype=torch.uint8, device=device())
+    gla.segment_states(inp["k"], inp["v"], b, plan, ws)
+    torch.cuda.synchronize()
+    nst = B * H * (segments - 1) * w.dk * w.dv
+    states = ws[: nst * 4].view(torch.float32).reshape(B * H, segments - 1, w.dk, w.dv).cpu().double().numpy()
+    decays = ws[nst * 4: nst * 4 + B * H * segments * 4].view(torch.float32).reshape(B * H, segments)
+    decays = decays.cpu().double().numpy()
+    nc = (T + 63) // 64
+    g = oracle.gate(inp["x"].reshape(B * H, T).cpu().numpy().astype(np.float64))
+    for p in range(segments - 1):
+        t_beg = min(T, p * nc // segments * 64)
+        t_end = min(T, (p + 1) * nc // segments * 64)
+        _, S_ref = oracle_heads(inp, T=t_end)
+        assert rel(states[:, p], S_ref) <= TOL[qkv], p
+        ref_g = g[:, t_beg:t_end].sum(axis=1)
+        assert np.all(np.abs(decays[:, p] - ref_g) <= 1e-5 * np.abs(ref_g) + 1e-4), p
+
+
 def test_bounded_gate_tile_sums_above_minus_80():
     dev = device()
     g = torch.Generator(device=dev).manual_seed(4)
