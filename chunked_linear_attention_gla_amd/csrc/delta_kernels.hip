@@ -133,7 +133,7 @@ struct PrepSmem {
       T vb[TokTile<T, DV>::SIZE]; // beta_s v_s, token-major
     } r;
   } u1;
-  union {
+  union alignas(16) {             // 16-byte aligned: Tinv's operand copy is written 4 elements at a time
     float mf[64][C::MLD];         // M = diag(beta) L (strictly lower)
     T tb[64 * C::TLD];            // Tinv in the operand dtype
   } u2;
@@ -237,9 +237,15 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   }
   // operand copy of Tinv (over M, no longer read), zero above the diagonal blocks;
   // then the right-hand sides of the products over the fp32 Tinv
-  for (int e = tid; e < 64 * 64; e += C::NT) {
-    const int t = e >> 6, s = e & 63;
-    sm.u2.tb[t * C::TLD + s] = E::cvt((s >> 4) <= (t >> 4) ? sm.u1.t.tf[t][s] : 0.0f);
+  // (8 consecutive elements of a row per thread and step: one 16-column block, so one
+  // select for all 8; two float4 reads and two 4-element stores)
+  for (int e = tid; e < 64 * 8; e += C::NT) {
+    const int t = e >> 3, s = (e & 7) * 8;
+    const bool keep = (s >> 4) <= (t >> 4);
+    const float4 lo = keep ? *reinterpret_cast<const float4*>(&sm.u1.t.tf[t][s]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 hi = keep ? *reinterpret_cast<const float4*>(&sm.u1.t.tf[t][s + 4]) : make_float4(0.f, 0.f, 0.f, 0.f);
+    E::store4(sm.u2.tb + t * C::TLD + s, lo.x, lo.y, lo.z, lo.w);
+    E::store4(sm.u2.tb + t * C::TLD + s + 4, hi.x, hi.y, hi.z, hi.w);
   }
   __syncthreads();
 #pragma unroll
