@@ -127,6 +127,36 @@ struct ChunkDecay {
   __device__ __forceinline__ float at(int j) const { return __shfl(b, j); }
 };
 
+// First chunk of [c_begin, c_end) that a segment pre-pass has to run, and the
+// segment's total log-decay.  The state update multiplies the carried state by
+// e^{gamma_c}; where that factor is exactly zero in fp32 (gamma_c below about -103.3),
+// the state after chunk c does not depend on anything before it.  So the pass may
+// start at the last such chunk from a zero state and end with the same local state,
+// bit for bit (up to the sign of an exact zero).  gamma_c = b at the chunk's last token,
+// read as the pass itself reads it.  Same results in every lane of the wave.
+__device__ __forceinline__ int segment_first_live_chunk(const HeadBuffers& hb, int c_begin, int c_end,
+                                                        float& gsum) {
+  const int lane = threadIdx.x & 63;
+  int last_zero = -1;
+  float s = 0.0f;
+  for (int c0 = c_begin; c0 < c_end; c0 += 64) {  // wave-uniform
+    const int c = c0 + lane;
+    if (c < c_end) {
+      const uint32_t t = (uint32_t)c * kChunk + (kChunk - 1);
+      const float gam = buf_load4(hb.b, (t < hb.Tl ? t : hb.Tl - 1) * 4u);
+      if (exp_e(gam) == 0.0f) last_zero = c;
+      s += gam;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    last_zero = max(last_zero, __shfl_xor(last_zero, off));
+    s += __shfl_xor(s, off);
+  }
+  gsum = s;
+  return last_zero >= 0 ? last_zero : c_begin;
+}
+
 // fp32 state slice of one wave: S[d = 16 db + 4 g + e][n = 16 nb + r16], e = 0..3
 template <typename T, int DK, int DVS>
 struct StateAcc {

@@ -152,15 +152,15 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
   for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) S.s[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float gsum = 0.0f;  // total log-decay of the segment
+  float gsum;  // total log-decay of the segment
+  const int c_first = segment_first_live_chunk(hb, c_begin, c_end, gsum);
 
   Staged<T, DK, DVS, false> st;
-  if (c_begin < c_end) st.load(hb, p, (uint32_t)c_begin * kChunk, col0, tid);
-  for (int c = c_begin; c < c_end; ++c) {
+  if (c_first < c_end) st.load(hb, p, (uint32_t)c_first * kChunk, col0, tid);
+  for (int c = c_first; c < c_end; ++c) {
     const ChunkDecay cd(st.b);
     const RowB<T, DK, DVS> brow(cd, tid);
     stage_state_operands<T, DK, DVS, false>(sm.kp, sm.vv, st, cd, brow, tid);
-    gsum += cd.gam;
     // prefetch the next chunk (the last iteration re-reads its own chunk so that
     // every iteration issues the same loads)
     st.load(hb, p, (uint32_t)min(c + 1, c_end - 1) * kChunk, col0, tid);

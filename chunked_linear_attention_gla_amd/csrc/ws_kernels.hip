@@ -435,6 +435,10 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
   const HeadSpan span = head_span(p, bh);
   const int c_begin = (int)((long long)seg * span.nchunks / p.segments);
   const int c_end = (int)((long long)(seg + 1) * span.nchunks / p.segments);
+  const HeadBuffers hb = head_buffers<bf16, DK>(p, span);
+  // every wave finds the first chunk to run (and the segment's log-decay) itself
+  float gsum;  // total log-decay of the segment
+  const int c_first = segment_first_live_chunk(hb, c_begin, c_end, gsum);
 
   if (compute) {
     StateAcc<bf16, DK, DVS> S;
@@ -442,12 +446,10 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
     for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
       for (int db = 0; db < C::DB; ++db) S.s[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float gsum = 0.0f;  // total log-decay of the segment
     __syncthreads();
-    for (int c = c_begin; c < c_end; ++c) {
-      const int slot = (c - c_begin) & 1;
+    for (int c = c_first; c < c_end; ++c) {
+      const int slot = (c - c_first) & 1;
       const float gam = sm.gam[slot];
-      gsum += gam;
       VFrags<bf16, DK, DVS> Vf;
       load_v_frags<bf16, DK, DVS, W::VLD>(Vf, sm.vv[slot], cw, lane);
       state_update<bf16, DK, DVS, W::KLD>(S, Vf, sm.kp[slot], exp_e(gam), lane);
@@ -456,7 +458,6 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
     store_state<bf16, DK, DVS>(S, p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv, p.dv, wcol, g, r16);
     if (slice == 0 && tid == 0) p.seg_decay[(long long)bh * p.segments + seg] = gsum;
   } else {
-    const HeadBuffers hb = head_buffers<bf16, DK>(p, span);
     const auto stage = [&](const WsStaged<DK, DVS, false>& stg, int ns) {
       const ChunkDecay cd(stg.b);
       float brow[W::QU];
@@ -479,16 +480,16 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
       if (sw == 0 && lane == 0) sm.gam[ns] = cd.gam;
     };
     const auto chunk_t0 = [&](int c) { return (uint32_t)min(c, c_end - 1) * kChunk; };
-    // register set s0: chunks at even offsets from c_begin, s1: odd offsets
+    // register set s0: chunks at even offsets from c_first, s1: odd offsets
     WsStaged<DK, DVS, false> s0, s1;
-    if (c_begin < c_end) {
-      s0.load(hb, p, chunk_t0(c_begin), col0, st);
+    if (c_first < c_end) {
+      s0.load(hb, p, chunk_t0(c_first), col0, st);
       stage(s0, 0);
-      s1.load(hb, p, chunk_t0(c_begin + 1), col0, st);
-      s0.load(hb, p, chunk_t0(c_begin + 2), col0, st);
+      s1.load(hb, p, chunk_t0(c_first + 1), col0, st);
+      s0.load(hb, p, chunk_t0(c_first + 2), col0, st);
     }
     __syncthreads();
-    int c = c_begin;
+    int c = c_first;
     for (; c + 1 < c_end; c += 2) {
       stage(s1, 1);
       s1.load(hb, p, chunk_t0(c + 3), col0, st);

@@ -54,13 +54,20 @@ def test_gate_cumsum_matches_fp64(gate, T):
     assert np.all(np.abs(got - ref) <= 1e-6 * np.abs(ref) + 1e-6)
 
 
-@pytest.mark.parametrize("qkv,segments", [("f32", 3), ("f32", 11), ("bf16", 11)])
-def test_segment_states_are_prefix_states(qkv, segments):
+@pytest.mark.parametrize("qkv,segments,bursts", [("f32", 3, False), ("f32", 11, False), ("bf16", 11, False),
+                                                 ("f32", 3, True), ("bf16", 5, True)])
+def test_segment_states_are_prefix_states(qkv, segments, bursts):
     """Stage entry point gla_segment_states: for every segment p but the last, the
     workspace holds the segment's total log-decay and the state at the end of segment
     p reached from a zero state at the start of the head (the pre-pass's local states
-    combined in order).  11 segments exercise the prefix scan's batches of 8."""
+    combined in order).  11 segments exercise the prefix scan's batches of 8.  With
+    bursts, a few whole chunks have x = +8 (chunk log-decay about -320, whose e^ is
+    zero in fp32) inside weak-decay segments: the pre-pass then starts at the last such
+    chunk of each segment, and the states must still match the fp64 recurrence."""
     w, inp = small(64 * 23 + 7, H=2, qkv=qkv, dk=64, dv=64, s0=0.0, x_mean=-6.0, seed=21)
+    if bursts:
+        for ch in (1, 5, 6, 13, 17):
+            inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
     plan = gla.Plan(segments, 1)
     B, H, T = w.B, w.H, w.T
     b = gla.gate_cumsum(inp["x"])
@@ -93,6 +100,18 @@ def test_bounded_gate_tile_sums_above_minus_80():
 
 
 # ------------------------------------------------------------------------------ forward parity
+
+@pytest.mark.parametrize("qkv,segments", [("bf16", 5), ("bf16", 16), ("f32", 4)])
+def test_decay_bursts_segmented(qkv, segments):
+    """Weak decay with whole chunks of strong decay (x = +8) at and around segment
+    boundaries: the segment pre-pass starts at each segment's last such chunk; o and
+    S_T against the fp64 oracle, with S0 carried through the first segment."""
+    w, inp = small(64 * 37 + 21, H=2, qkv=qkv, dk=64, dv=64, x_mean=-6.0, seed=23)
+    nc = (w.T + 63) // 64
+    for ch in sorted({1, 2, nc // segments, nc // segments - 1, 2 * nc // segments, nc - 2}):
+        inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
+    check(inp, w, plan=gla.Plan(segments, 1))
+
 
 @pytest.mark.parametrize("T", [64, 200, 640, 1000])
 def test_bf16_default_plan(T):
