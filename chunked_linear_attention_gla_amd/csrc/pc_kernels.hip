@@ -357,15 +357,44 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_segment_state_kern
   float gsum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // tile 0, row group 0: segment log-decay
   const PcLane<C> pl(wave, lane);
 
+  // Exact truncation: the state update multiplies state row d by e^{gamma_c[d]}; if
+  // that factor is exactly zero in fp32 for every channel of chunk c, the state after
+  // c does not depend on anything before it, and the pass may start there from a zero
+  // state with the same result.  The last two chunks of the segment are candidates;
+  // their factors are computed by the same code, in the same order, as in the pass.
+  // The segment log-decay then sums only the chunks run; the skipped decay would not
+  // change it: it is below -150 (base 2) either way, so its exp2 is the same zero.
+  __shared__ int live_flag[2];  // one per candidate: no flag is cleared while it may be read
+  if (tid < 2) live_flag[tid] = 0;
+  int c_first = c_begin;
+  for (int cand = c_end - 1, i = 0; cand >= c_begin && i < 2; --cand, ++i) {  // uniform
+    PcStaged<T, DK, DVS, false> sc;
+    sc.load(hb, Tn, p.dv, (uint32_t)cand * kChunk, col0, wave, lane, tid);
+    PcLam<T, DK, DVS> lc;
+    tile_log_decay<T, DK, DVS, false>(lc, sc, sm.tau[0], (uint32_t)cand * kChunk, Tn, p.gate, wave, lane);
+    __syncthreads();
+    for (int d = tid; d < DK; d += C::NT) {
+      float s = 0.0f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) s += sm.tau[0][u][d];
+      if (exp2_hw(s) != 0.0f) live_flag[i] = 1;
+    }
+    __syncthreads();  // also orders the reads of tau before it is written again
+    if (!live_flag[i]) {
+      c_first = cand;
+      break;
+    }
+  }
+
   PcStaged<T, DK, DVS, false> st;
-  if (c_begin < c_end) st.load(hb, Tn, p.dv, (uint32_t)c_begin * kChunk, col0, wave, lane, tid);
+  if (c_first < c_end) st.load(hb, Tn, p.dv, (uint32_t)c_first * kChunk, col0, wave, lane, tid);
   // Two barriers per chunk: the tile totals alternate between two buffers, so a wave
   // may publish chunk c + 1's totals while others still update the state of chunk c;
   // everything else chunk c + 1 writes comes after the barrier that all waves reach
   // only once they are done with chunk c.
-  for (int c = c_begin; c < c_end; ++c) {
+  for (int c = c_first; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)c * kChunk;
-    float (*tau)[DK] = sm.tau[(c - c_begin) & 1];
+    float (*tau)[DK] = sm.tau[(c - c_first) & 1];
     PcLam<T, DK, DVS> lam;
     tile_log_decay<T, DK, DVS, false>(lam, st, tau, t0, Tn, p.gate, wave, lane);
     __syncthreads();

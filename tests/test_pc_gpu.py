@@ -57,6 +57,23 @@ def test_decay_regimes(regime, x_mean, x_std):
     check(w, inp)
 
 
+@pytest.mark.parametrize("qkv,segments,partial", [("bf16", 4, False), ("bf16", 6, True), ("f32", 3, False)])
+def test_decay_bursts_segmented(qkv, segments, partial):
+    """Weak decay with whole chunks of strong decay (x = +8 in every channel) at the
+    ends of segments, where the segment pre-pass may start its recurrence.  partial:
+    in one of those chunks a single channel keeps its weak decay, so that chunk does
+    not cut the state and the pass must run further back."""
+    dk = dv = 64 if qkv == "f32" else 128
+    w, inp = make(64 * 26 + 9, H=2, qkv=qkv, dk=dk, dv=dv, x_mean=-6.0, seed=31)
+    nc = (w.T + 63) // 64
+    ends = [(p + 1) * nc // segments - 1 for p in range(segments - 1)]
+    for ch in ends + [e - 1 for e in ends]:
+        inp["x"][:, :, ch * 64:(ch + 1) * 64, :] = 8.0
+    if partial:
+        inp["x"][:, :, ends[0] * 64:(ends[0] + 1) * 64, 5] = -6.0
+    check(w, inp, plan=gla.Plan(segments, 1))
+
+
 def test_extreme_channels():
     """Some channels with x = +inf (g = -5 exactly: the bound) and some with x = -inf
     (a = 1), mixed with ordinary values in the same tiles."""
