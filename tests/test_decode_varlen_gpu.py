@@ -72,9 +72,11 @@ def test_decode_chain_matches_chunked_forward(per_channel):
 
 # ------------------------------------------------------------------------------ packed sequences
 
-def varlen_check(w, lengths, gate="bounded", path="unified", tol=None, seed=None, plan=None):
+def varlen_check(w, lengths, gate="bounded", path="unified", tol=None, seed=None, plan=None, edit_x=None):
     dev = device()
     inp = gin.make_varlen_inputs(w, lengths, dev, seed=seed)
+    if edit_x is not None:
+        edit_x(inp["x"], [0] + list(np.cumsum(lengths)))
     max_len = max(lengths) if lengths else 0
     o, ST = gla.chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["x"], inp["cu_seqlens"], max_len, inp["S0"],
                                  gate=gate, path=path, plan=plan)
@@ -112,6 +114,24 @@ def test_varlen_explicit_segments(segments):
     than that many chunks (empty segments) and empty sequences."""
     w = VAR.with_(H=2, s0_std=0.1, x_mean=-5.0)
     varlen_check(w, [64 * 9 + 5, 3, 0, 64 * 2, 1000], plan=gla.Plan(segments, 1))
+
+
+@pytest.mark.parametrize("segments", [3, 5])
+def test_varlen_segments_with_decay_bursts(segments):
+    """Weak decay with whole chunks of strong decay (x = +8) just before each segment
+    end of every sequence: the segment pre-pass of each sequence starts at such a chunk."""
+    lengths = [64 * 11 + 5, 3, 0, 64 * 4, 1300]
+
+    def bursts(x, cu):
+        for n, L in enumerate(lengths):
+            nc = (L + 63) // 64
+            for p in range(segments - 1):
+                c = (p + 1) * nc // segments - 1
+                if c >= 0 and (c + 1) * 64 <= L:
+                    x[:, cu[n] + c * 64: cu[n] + (c + 1) * 64] = 8.0
+
+    w = VAR.with_(H=2, s0_std=0.1, x_mean=-5.0)
+    varlen_check(w, lengths, plan=gla.Plan(segments, 1), edit_x=bursts)
 
 
 def test_varlen_length_mix_sample():
