@@ -608,6 +608,20 @@ def main():
         abl["unified_speedup_output_kernel"] = round(
             abl["diag_branch"]["chunk_output_ms"] / abl["unified"]["chunk_output_ms"], 3)
         result["ablation"] = abl
+    if w.name == gin.HEADLINE and path == "unified" and not args.plan and not args.no_ablation:
+        # the same shapes with weakly decaying gates: no chunk's decay factor underflows,
+        # so the segment pre-pass runs every chunk of its segments (nothing truncated)
+        ww = w.with_(x_mean=-6.0, x_std=1.0)
+        steps_w = min(args.steps, 20)
+        t = StepTimer(gla, gin, torch, ww, path)
+        ms_w, st_w = t.run(steps_w, min(args.warmup, 5))
+        del t
+        result["weak_decay"] = {
+            "what": "same shapes, x ~ N(-6,1): the segment pre-pass runs every chunk (no exact truncation)",
+            "x": f"N({ww.x_mean},{ww.x_std})", "steps": steps_w, "ms_per_step": round(ms_w, 4),
+            "stage_ms": {"gate_cumsum": round(st_w[0], 4), "segment_states": round(st_w[1], 4),
+                         "chunk_output": round(st_w[2], 4)},
+            "tokens_per_s": round(ww.B * ww.T / (ms_w / 1e3), 1)}
     if not args.no_backward and not args.plan:
         result["backward"] = backward_result(gla, gin, torch, w, path, min(args.steps, 20), min(args.warmup, 5))
         if not args.no_cpu_baseline:
