@@ -321,6 +321,7 @@ struct DsSmem {
   T wn[64 * C::QLD];
   T kp[TokTile<T, DK>::SIZE];
   T uu[UTile<T, DVS>::SIZE];
+  int nonzero[2][C::NW];  // transition half: per wave, whether its columns are nonzero, by chunk parity
 };
 
 // One chunk of (q,) k, W, Ut and b on its way to LDS / registers.  Ut lands directly
@@ -476,8 +477,28 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) Uf[ks] = UTile<T, NCOL>::load(sm.uu, ks * 32, wave * 16, lane);
     delta_state_update<T, DK, NCOL>(S, Uf, sm.kp, exp_e(cd.gam), lane);
+    if constexpr (PHI) {
+      // Once this workgroup's columns of the running transition product are all
+      // exactly zero, every later chunk leaves them zero: stop.  Each wave posts
+      // whether its columns hold a nonzero value (slots by chunk parity, so that no
+      // slot is written while another wave may still read it).
+      bool nz = false;
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nz |= S[db][e] != 0.0f;
+      if (lane == 0) sm.nonzero[(c - c_begin) & 1][wave] = __ballot(nz) != 0ull;
+    }
     __syncthreads();
+    if constexpr (PHI) {
+      const int par = (c - c_begin) & 1;
+      int any = 0;
+#pragma unroll
+      for (int w = 0; w < C::NW; ++w) any |= sm.nonzero[par][w];
+      if (!any) break;
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the prefetch of a chunk not run is not left in flight
   float* dst = PHI ? p.seg_phi + ((long long)bh * nseg + seg) * DK * DK
                    : p.seg_state + ((long long)bh * nseg + seg) * DK * p.dv;
 #pragma unroll
