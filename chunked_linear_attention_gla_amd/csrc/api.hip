@@ -62,7 +62,7 @@ gla_status_t plan_check_impl(int B, int H, long long T, int dk, int dv, gla_dtyp
   const int slice = dv / s;
   if (slice != 16 && slice != 32 && slice != 64 && slice != 128) return GLA_ERR_PLAN;
   if (!gla::chunk_config_built(dtype == GLA_BF16 ? 0 : 1, dk, slice, path == GLA_PATH_DIAG_BRANCH)) {
-    // a valid plan shape that this build has no kernel for
+    // a valid plan shape that the library has no kernel for
     if (dtype == GLA_F32 && path == GLA_PATH_DIAG_BRANCH && dk != 64) return GLA_ERR_UNSUPPORTED;
     return GLA_ERR_PLAN;
   }
