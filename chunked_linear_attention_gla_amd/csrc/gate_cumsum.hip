@@ -39,29 +39,51 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
   return v + off;
 }
 
+// Each wavefront takes kGateChunksPerWave consecutive chunks and issues all their
+// loads before the first scan, so one memory round trip covers several chunks.
+constexpr int kGateChunksPerWave = 8;
+
 template <int GATE, bool REV>
 __global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restrict__ x,
                                                           float* __restrict__ b, long long T,
                                                           long long chunks_per_head,
                                                           long long total_chunks) {
   const int lane = threadIdx.x & 63;
-  const long long chunk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (chunk >= total_chunks) return;  // uniform across the wavefront
-  const long long bh = chunk / chunks_per_head;
-  const long long t = (chunk - bh * chunks_per_head) * kChunk + lane;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const long long first = ((long long)blockIdx.x * 4 + wave) * kGateChunksPerWave;
+  if (first >= total_chunks) return;  // uniform across the wavefront
   // REV: the reversed sequence has pad absent tokens first, then original tokens
   // T-1 .. 0; logical token t > pad takes the gate of original token T + pad - t
   // (the token after it in original order), t <= pad none (g = 0)
   const long long pad = REV ? (kChunk - T % kChunk) % kChunk : 0;
   const long long Tl = T + pad;
-  const bool valid = t < Tl;
-  float g = 0.0f;
-  if (valid && (!REV || t > pad)) {
-    const float xv = x[bh * T + (REV ? T + pad - t : t)];
-    g = (GATE == kGateBoundedSigmoid) ? gate_bounded_sigmoid(xv) : gate_neg_softplus(xv);
+  long long bh = first / chunks_per_head;
+  long long c = first - bh * chunks_per_head;
+  float g[kGateChunksPerWave];
+  long long dst[kGateChunksPerWave];
+  bool valid[kGateChunksPerWave];
+#pragma unroll
+  for (int i = 0; i < kGateChunksPerWave; ++i) {
+    const long long t = c * kChunk + lane;
+    valid[i] = first + i < total_chunks && t < Tl;
+    dst[i] = bh * Tl + t;
+    // unconditional load (token 0 of x stands in for absent tokens) so that the
+    // compiler issues every load of the wavefront before the first gate
+    const bool has_gate = valid[i] && (!REV || t > pad);
+    const float xv = x[has_gate ? bh * T + (REV ? T + pad - t : t) : 0];
+    const float gv = (GATE == kGateBoundedSigmoid) ? gate_bounded_sigmoid(xv) : gate_neg_softplus(xv);
+    g[i] = has_gate ? gv : 0.0f;
+    if (++c == chunks_per_head) {
+      c = 0;
+      ++bh;
+    }
   }
-  const float s = wave_inclusive_scan(g, lane);
-  if (valid) b[bh * Tl + t] = s;
+#pragma unroll
+  for (int i = 0; i < kGateChunksPerWave; ++i) {
+    if (first + i >= total_chunks) break;  // uniform across the wavefront
+    const float s = wave_inclusive_scan(g[i], lane);
+    if (valid[i]) b[dst[i]] = s;
+  }
 }
 
 // Packed sequences: wavefront `chunk` of unit bh = n * H + h covers tokens
@@ -168,7 +190,7 @@ hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long 
   const long long cph = (T + kChunk - 1) / kChunk;
   const long long total = BH * cph;
   if (total == 0) return hipSuccess;
-  const long long blocks = (total + 3) / 4;
+  const long long blocks = (total + 4 * kGateChunksPerWave - 1) / (4 * kGateChunksPerWave);
   if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)blocks), block(256);
   if (gate == kGateBoundedSigmoid) {
