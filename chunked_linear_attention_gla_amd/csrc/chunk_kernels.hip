@@ -467,14 +467,20 @@ bool chunk_config_built(int dtype, int dk, int slice, bool diag) {
 // so that segment p > 0 starts from e^{Gamma_0 + .. + Gamma_{p-1}} S0 + P_{p-1}: one
 // state read per output workgroup instead of a chain of p dependent reads.  Thread =
 // 4 consecutive elements of one unit's states; its loads are issued in batches of 8
-// segments ahead of the arithmetic that consumes them.
+// segments ahead of the arithmetic that consumes them.  A workgroup lies within one
+// unit (per_state4 is a multiple of the block size), so whether a batch can be
+// skipped is uniform, and its decays are read before any state moves.  Where e^{Gamma_p} is exactly zero in fp32,
+// P_p = H_p (up to the sign of an exact zero) is already in place; a batch whose
+// factors are all zero, and whose last state the next batch does not carry forward,
+// is skipped without touching memory.
 constexpr int kPrefixThreads = 256;
 constexpr int kPrefixBatch = 8;
 
-__global__ void __launch_bounds__(kPrefixThreads) segment_prefix_kernel(float* seg_state, const float* seg_decay,
+__global__ void __launch_bounds__(kPrefixThreads) segment_prefix_kernel(float* __restrict__ seg_state,
+                                                                        const float* __restrict__ seg_decay,
                                                                         int segments, int per_state4, int units) {
   const long long gid = (long long)blockIdx.x * kPrefixThreads + threadIdx.x;
-  const int unit = (int)(gid / per_state4);
+  const int unit = __builtin_amdgcn_readfirstlane((int)(gid / per_state4));
   if (unit >= units) return;
   const int e4 = (int)(gid - (long long)unit * per_state4);
   const int nseg = segments - 1;
@@ -482,16 +488,31 @@ __global__ void __launch_bounds__(kPrefixThreads) segment_prefix_kernel(float* s
   const float* G = seg_decay + (long long)unit * segments;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int p0 = 0; p0 < nseg; p0 += kPrefixBatch) {
+    // f[j] = e^{Gamma_{p0+j}} for 0 < p0 + j < nseg, else 0 (no carry into P_0 or past the end)
+    // (lane j reads Gamma_{p0+j}: one load for the batch, then one readlane per factor)
+    const float el = exp_e(G[min(p0 + (int)(threadIdx.x & 63), nseg - 1)]);
+    float f[kPrefixBatch + 1];
+    bool live = false;
+#pragma unroll
+    for (int j = 0; j <= kPrefixBatch; ++j) {
+      const int ps = p0 + j;
+      const float e = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, el), j));
+      f[j] = ps > 0 && ps < nseg ? e : 0.0f;
+      live |= f[j] != 0.0f;
+    }
+    if (!live) {  // uniform across the workgroup
+      acc = floatx4{0.f, 0.f, 0.f, 0.f};
+      continue;
+    }
     floatx4 h[kPrefixBatch];
 #pragma unroll
     for (int j = 0; j < kPrefixBatch; ++j) h[j] = H[(long long)min(p0 + j, nseg - 1) * per_state4];
 #pragma unroll
     for (int j = 0; j < kPrefixBatch; ++j) {
       const int ps = p0 + j;
-      if (ps < nseg) {
-        acc = ps == 0 ? h[j] : exp_e(G[ps]) * acc + h[j];
-        H[(long long)ps * per_state4] = acc;
-      }
+      if (ps >= nseg) break;
+      acc = ps == 0 ? h[j] : f[j] * acc + h[j];
+      if (ps > 0) H[(long long)ps * per_state4] = acc;
     }
   }
 }
