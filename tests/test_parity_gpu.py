@@ -54,8 +54,9 @@ def test_gate_cumsum_matches_fp64(gate, T):
     assert np.all(np.abs(got - ref) <= 1e-6 * np.abs(ref) + 1e-6)
 
 
-@pytest.mark.parametrize("qkv,segments,bursts", [("f32", 3, False), ("f32", 11, False), ("bf16", 11, False),
-                                                 ("f32", 3, True), ("bf16", 5, True)])
+@pytest.mark.parametrize("qkv,segments,bursts", [("f32", 3, "none"), ("f32", 11, "none"), ("bf16", 11, "none"),
+                                                 ("f32", 3, "bursts"), ("bf16", 5, "bursts"),
+                                                 ("f32", 20, "front"), ("bf16", 20, "front")])
 def test_segment_states_are_prefix_states(qkv, segments, bursts):
     """Stage entry point gla_segment_states: for every segment p but the last, the
     workspace holds the segment's total log-decay and the state at the end of segment
@@ -63,11 +64,16 @@ def test_segment_states_are_prefix_states(qkv, segments, bursts):
     combined in order).  11 segments exercise the prefix scan's batches of 8.  With
     bursts, a few whole chunks have x = +8 (chunk log-decay about -320, whose e^ is
     zero in fp32) inside weak-decay segments: the pre-pass then starts at the last such
-    chunk of each segment, and the states must still match the fp64 recurrence."""
+    chunk of each segment, and the states must still match the fp64 recurrence.
+    front: x = +8 over the first 12 of 24 chunks, so segments 0-9 of 20 have a zero
+    decay factor: the scan's first batch (segments 1-8) has nothing to combine, and the
+    next batch carries segment 9's state (its own local state) into segment 10."""
     w, inp = small(64 * 23 + 7, H=2, qkv=qkv, dk=64, dv=64, s0=0.0, x_mean=-6.0, seed=21)
-    if bursts:
+    if bursts == "bursts":
         for ch in (1, 5, 6, 13, 17):
             inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
+    elif bursts == "front":
+        inp["x"][:, :, :12 * 64] = 8.0
     plan = gla.Plan(segments, 1)
     B, H, T = w.B, w.H, w.T
     b = gla.gate_cumsum(inp["x"])
@@ -111,6 +117,16 @@ def test_decay_bursts_segmented(qkv, segments):
     for ch in sorted({1, 2, nc // segments, nc // segments - 1, 2 * nc // segments, nc - 2}):
         inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
     check(inp, w, plan=gla.Plan(segments, 1))
+
+
+@pytest.mark.parametrize("qkv,dk", [("bf16", 128), ("f32", 64)])
+def test_strong_front_weak_tail_segmented(qkv, dk):
+    """x = +8 over the first half of the sequence and weak decay after it, with 24
+    segments: the prefix scan skips its first batch (every factor zero), combines the
+    rest, and the output pass starts each segment from those states (S0 given)."""
+    w, inp = small(64 * 48 + 5, H=2, qkv=qkv, dk=dk, dv=dk, x_mean=-6.0, seed=29)
+    inp["x"][:, :, :24 * 64] = 8.0
+    check(inp, w, plan=gla.Plan(24, 1))
 
 
 @pytest.mark.parametrize("T", [64, 200, 640, 1000])
