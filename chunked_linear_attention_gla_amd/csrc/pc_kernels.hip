@@ -152,9 +152,14 @@ __device__ __forceinline__ int pc_swz(int row) {
   return Elem<T>::kSwizzle ? (row & 8) >> 1 : 0;
 }
 
-// Log-decay of one channel in base 2: g log2 e.
+// Log-decay of one channel in base 2: g log2 e.  The bounded gate evaluates
+// sigmoid(x) = 1 / (1 + e^{-x}) directly: a sum of positive terms, so no
+// cancellation; e^{-x} = inf (x below about -88.7) gives exactly 0 and x = +inf gives
+// 1, the limits.  One multiply, two transcendentals, one add and the final scale per
+// element, where the sign-split form needs three more operations.
 __device__ __forceinline__ float pc_log2_gate(float x, int gate) {
-  return gate == kGateBoundedSigmoid ? (-5.0f * kLog2e) * sigmoid_hw(x) : kLog2e * gate_neg_softplus(x);
+  return gate == kGateBoundedSigmoid ? (-5.0f * kLog2e) * __builtin_amdgcn_rcpf(1.0f + exp2_hw(x * -kLog2e))
+                                     : kLog2e * gate_neg_softplus(x);
 }
 
 // Tile-local cumulative log2-decay of the lane's rows (see tile_log_decay).
