@@ -469,10 +469,10 @@ bool chunk_config_built(int dtype, int dk, int slice, bool diag) {
 // 4 consecutive elements of one unit's states; its loads are issued in batches of 8
 // segments ahead of the arithmetic that consumes them.  A workgroup lies within one
 // unit (per_state4 is a multiple of the block size), so whether a batch can be
-// skipped is uniform, and its decays are read before any state moves.  Where e^{Gamma_p} is exactly zero in fp32,
-// P_p = H_p (up to the sign of an exact zero) is already in place; a batch whose
-// factors are all zero, and whose last state the next batch does not carry forward,
-// is skipped without touching memory.
+// skipped is uniform, and its decays are read before any state moves.  Where
+// e^{Gamma_p} is exactly zero in fp32, P_p = H_p (up to the sign of an exact zero) is
+// already in place; a batch whose factors are all zero, and whose last state the next
+// batch does not carry forward, is skipped without touching memory.
 constexpr int kPrefixThreads = 256;
 constexpr int kPrefixBatch = 8;
 
