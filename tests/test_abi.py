@@ -92,6 +92,21 @@ def test_bad_sizes_and_enums(lib, kw, code):
     assert rc == code
 
 
+def test_size_limits(lib):
+    """One head's q, k, v and o are addressed through 32-bit buffer descriptors, so
+    T * max(dk, dv) * 4 bytes may not exceed 0xFFFF0000; B * H is capped at 2^24.
+    A workspace query exactly at the limit is accepted (no device work), one chunk
+    past it is rejected before anything else."""
+    t_max = 0xFFFF0000 // (128 * 4)  # 8388480 tokens, a multiple of 64
+    rc, n = fwd(lib, B=1, H=1, T=t_max, dk=128, dv=128, plan=(1, 1))
+    assert rc == OK and n >= t_max * 4
+    assert fwd(lib, B=1, H=1, T=t_max + 64, dk=128, dv=128, plan=(1, 1))[0] == SHAPE
+    assert fwd(lib, B=1, H=1, T=2 * t_max, dk=64, dv=64, plan=(1, 1))[0] == OK
+    assert fwd(lib, B=1, H=1, T=2 * t_max + 64, dk=64, dv=64, plan=(1, 1))[0] == SHAPE
+    assert fwd(lib, B=1 << 12, H=1 << 12, T=64, plan=(1, 1))[0] == OK
+    assert fwd(lib, B=1 << 13, H=1 << 12, T=64, plan=(1, 1))[0] == SHAPE
+
+
 def test_fp32_diag_branch_needs_dk64(lib):
     rc, _ = fwd(lib, dtype=F32, path=DIAG, dk=128, dv=64, plan=(1, 1))
     assert rc == UNSUP
