@@ -101,3 +101,32 @@ def test_bf16_1m_prefix_and_continuity():
     o_r, S_r = run(rest)
     assert gpu_rel(o_r, o[:, :, P:]) <= CHAIN_TOL
     assert gpu_rel(S_r, ST) <= CHAIN_TOL
+
+
+def test_bf16_largest_head_extent():
+    """The largest sequence the ABI accepts for one head at dk = dv = 128: o spans
+    0xFFFF0000 bytes, so its byte offsets pass 2^31 halfway (token 4194304).  Whole
+    chunks with x = +8 (chunk decay about e^-320, exactly 0 in fp32) are planted before
+    the checked windows, so the fp64 oracle restarted from a zero state at such a
+    chunk yields the outputs after it (the earlier past enters with weight ~1e-139).
+    Checked: the first 256 tokens (with S0), four chunks across the 2^31-byte offset of
+    o, the last two chunks and S_T."""
+    t_max = 0xFFFF0000 // (128 * 4)
+    w = gin.WORKLOADS["bf16_1m"].with_(B=1, H=1, T=t_max, s0_std=0.1, seed=4242)
+    inp = gin.make_inputs(w, device())
+    mid = (1 << 31) // (128 * 4) // 64  # first chunk whose o rows lie past 2^31 bytes
+    last = t_max // 64
+    for ch in (mid - 3, last - 3):
+        inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
+    o, ST = run(inp)
+    assert torch.isfinite(o[:, :, :256]).all() and torch.isfinite(ST).all()
+    check_heads(inp, o, None, [0], T=256)
+    zero = torch.zeros(1, 1, 128, 128, device=device())
+    for a, c, b in ((mid - 3, mid - 2, mid + 2), (last - 3, last - 2, last)):
+        sub = tslice(inp, a * 64, b * 64)
+        o_ref, S_ref = oracle_heads(sub, [0], S0=zero)
+        got = o[0, 0, c * 64:b * 64].cpu().double().numpy()
+        assert np.isfinite(got).all()
+        assert rel(got, o_ref[0, (c - a) * 64:]) <= TOL["bf16"], (a, b)
+        if b == last:
+            assert rel(ST[0, 0].cpu().double().numpy(), S_ref[0]) <= TOL["bf16"]
