@@ -24,7 +24,7 @@ def oracle_pc(inp, gate="bounded", S0="inp"):
     q, k, v, x = inp["q"], inp["k"], inp["v"], inp["x"]
     B, H = q.shape[:2]
     flat = lambda t: t.reshape(B * H, *t.shape[2:])
-    s0 = inp["S0"] if S0 == "inp" else S0
+    s0 = inp["S0"] if isinstance(S0, str) else S0
     s0n = None if s0 is None else flat(s0).cpu().numpy().astype(np.float64)
     return oracle.forward_pc(*(gin.to_numpy_bits(flat(t)) for t in (q, k, v, x)), s0n, gate=gate)
 
@@ -159,3 +159,34 @@ def test_repeat_calls_are_bitwise_identical():
     o2, S2 = gla.chunk_fwd_pc(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], plan=gla.Plan(4, 1))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_largest_head_extent():
+    """The largest sequence the ABI accepts for one head at dk = dv = 128: x (fp32 per
+    channel) and o span 0xFFFF0000 bytes, so their byte offsets pass 2^31 at token
+    4194304.  Whole chunks with x = +8 in every channel (chunk decay about e^-320,
+    exactly 0 in fp32) are planted before the checked windows, so the fp64 oracle
+    restarted from a zero state at such a chunk yields the outputs after it.  Checked:
+    the first 192 tokens (with S0), four chunks across the 2^31-byte offset, the last
+    two chunks and S_T."""
+    t_max = 0xFFFF0000 // (128 * 4)
+    w, inp = make(t_max, H=1, seed=4243)
+    mid = (1 << 31) // (128 * 4) // 64
+    last = t_max // 64
+    for ch in (mid - 3, last - 3):
+        inp["x"][:, :, ch * 64:(ch + 1) * 64, :] = 8.0
+    o, ST = gla.chunk_fwd_pc(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"])
+    torch.cuda.synchronize()
+    head = {n: inp[n][:, :, :192].contiguous() for n in ("q", "k", "v", "x")}
+    head["S0"] = inp["S0"]
+    o_ref, _ = oracle_pc(head)
+    assert rel(o[0, 0, :192].cpu().double().numpy(), o_ref[0]) <= TOL["bf16"]
+    zero = torch.zeros(1, 1, 128, 128, device=device())
+    for a, c, b in ((mid - 3, mid - 2, mid + 2), (last - 3, last - 2, last)):
+        sub = {n: inp[n][:, :, a * 64:b * 64].contiguous() for n in ("q", "k", "v", "x")}
+        o_ref, S_ref = oracle_pc(sub, S0=zero)
+        got = o[0, 0, c * 64:b * 64].cpu().double().numpy()
+        assert np.isfinite(got).all()
+        assert rel(got, o_ref[0, (c - a) * 64:]) <= TOL["bf16"], (a, b)
+        if b == last:
+            assert rel(ST[0, 0].cpu().double().numpy(), S_ref[0]) <= TOL["bf16"]
