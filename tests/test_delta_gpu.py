@@ -133,3 +133,34 @@ def test_empty_sequence_returns_initial_state():
     o, ST = gla.chunk_fwd_delta(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["S0"])
     torch.cuda.synchronize()
     assert o.numel() == 0 and torch.equal(ST, inp["S0"])
+
+
+def test_largest_head_extent():
+    """The largest sequence the ABI accepts for one head at dk = dv = 128 (o spans
+    0xFFFF0000 bytes; its byte offsets pass 2^31 at token 4194304).  Whole chunks with
+    x = +8 are planted before the checked windows: the state's transition over such a
+    chunk, e^gamma I - K~^T W, is of order e^-320, so the fp64 oracle restarted from a
+    zero state there yields the outputs after it.  Checked: the first 192 tokens (with
+    S0), four chunks across the 2^31-byte offset of o, the last two chunks and S_T."""
+    t_max = 0xFFFF0000 // (128 * 4)
+    w, inp = make(t_max, H=1, seed=4244)
+    mid = (1 << 31) // (128 * 4) // 64
+    last = t_max // 64
+    for ch in (mid - 3, last - 3):
+        inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
+    o, ST = gla.chunk_fwd_delta(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["S0"])
+    torch.cuda.synchronize()
+    names = ("q", "k", "v", "x", "beta")
+    head = {n: inp[n][:, :, :192].contiguous() for n in names}
+    head["S0"] = inp["S0"]
+    o_ref, _ = oracle_delta(head)
+    assert rel(o[0, 0, :192].cpu().double().numpy(), o_ref[0]) <= TOL["bf16"]
+    for a, c, b in ((mid - 3, mid - 2, mid + 2), (last - 3, last - 2, last)):
+        sub = {n: inp[n][:, :, a * 64:b * 64].contiguous() for n in names}
+        sub["S0"] = None
+        o_ref, S_ref = oracle_delta(sub)
+        got = o[0, 0, c * 64:b * 64].cpu().double().numpy()
+        assert np.isfinite(got).all()
+        assert rel(got, o_ref[0, (c - a) * 64:]) <= TOL["bf16"], (a, b)
+        if b == last:
+            assert rel(ST[0, 0].cpu().double().numpy(), S_ref[0]) <= TOL["bf16"]
