@@ -101,3 +101,33 @@ def test_empty_sequence_gradient_is_dst():
     torch.cuda.synchronize()
     assert dq.numel() == 0 and dx.numel() == 0
     assert torch.equal(dS0, dST)
+
+
+def test_largest_head_extent():
+    """The largest sequence the ABI accepts for one head at dk = dv = 128: dq, dk and dv
+    span 0xFFFF0000 bytes (offsets past 2^31 at token 4194304) and each array of
+    per-chunk states 4.3 GB.  Whole chunks with x = +8 (decay about e^-320 across
+    the chunk) cut the sequence on both sides of each checked window: dq looks only
+    back, dk, dv look only forward and dx at pairs across each token, so the fp64
+    oracle run over the window from a zero state yields the gradients inside it.
+    Checked: the first two chunks (with S0) and dS0, four chunks across the 2^31-byte
+    offset, the last two chunks (with dS_T)."""
+    t_max = 0xFFFF0000 // (128 * 4)
+    w, inp, dO, dST = make(t_max, H=1, seed=4245)
+    mid = (1 << 31) // (128 * 4) // 64
+    last = t_max // 64
+    for ch in (2, mid - 3, mid + 2, last - 3):
+        inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
+    got = gla.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["x"], dO, inp["S0"], dST)
+    torch.cuda.synchronize()
+    for a, c0, c1, b in ((0, 0, 2, 3), (mid - 3, mid - 2, mid + 2, mid + 3), (last - 3, last - 2, last, last)):
+        sub = {n: inp[n][:, :, a * 64:b * 64].contiguous() for n in ("q", "k", "v", "x")}
+        sub["S0"] = inp["S0"] if a == 0 else None
+        ref = oracle_grads(sub, dO[:, :, a * 64:b * 64].contiguous(), dST if b == last else None, "bounded")
+        lo, hi = (c0 - a) * 64, (c1 - a) * 64
+        for name, g_, r_ in zip(NAMES[:4], got[:4], ref[:4]):
+            g_ = g_[0, 0, c0 * 64:c1 * 64].double().cpu().numpy()
+            assert np.isfinite(g_).all(), (name, a)
+            assert rel(g_, r_[0, lo:hi]) <= TOL["bf16"], (name, a)
+        if a == 0:
+            assert rel(got[4][0, 0].double().cpu().numpy(), ref[4][0]) <= TOL["bf16"]
