@@ -7,9 +7,9 @@
 // b[t] = sum_{i in chunk(t), i <= t} g(x[i]) is log Gamma restarted at each 64-token
 // chunk.  The chunk kernels read every decay factor they need from b: the
 // tile-start prefix r_u = b[16u - 1], the chunk total gamma = b[63] and
-// differences of entries.  One 64-lane wavefront owns one chunk, lane j owning
-// token j, and forms the inclusive scan with DPP row shifts inside each 16-lane
-// row followed by the three row totals read across lanes.
+// differences of entries.  A 64-lane wavefront scans one chunk at a time, lane j
+// owning token j, and forms the inclusive scan with DPP row shifts inside each
+// 16-lane row followed by the three row totals read across lanes.
 #include "gla_device.h"
 #include "gla_internal.h"
 
