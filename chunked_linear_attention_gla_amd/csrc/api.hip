@@ -75,6 +75,13 @@ size_t seg_bytes(long long BH, int dk, int dv, int segments) {
          align_up((size_t)BH * (size_t)segments * 4);
 }
 
+// Workspace of the forward pass: b, then the segment workspace.  Never 0 (T = 0 has
+// neither): a caller that allocates what the query reports then holds a non-NULL
+// buffer, which the call does not mistake for another size query.
+size_t fwd_workspace_bytes(long long BH, long long T, int dk, int dv, int segments) {
+  return std::max(align_up((size_t)BH * (size_t)T * 4) + seg_bytes(BH, dk, dv, segments), kAlign);
+}
+
 // Default plan.  Measured on MI355X (256 CUs): one workgroup per CU, each owning a
 // full-width value slice, is fastest; segments are added until the grid covers the
 // CUs (a segment costs one extra read of k and v, a narrower value slice costs a
@@ -211,8 +218,7 @@ gla_status_t gla_workspace_size(int B, int H, long long T, int dk, int dv, gla_d
     st = gla_plan_default(B, H, T, dk, dv, dtype, path, &pl);
     if (st != GLA_OK) return st;
   }
-  const long long BH = (long long)B * H;
-  *bytes = align_up((size_t)BH * (size_t)T * 4) + seg_bytes(BH, dk, dv, pl.segments);
+  *bytes = fwd_workspace_bytes((long long)B * H, T, dk, dv, pl.segments);
   return GLA_OK;
 }
 
@@ -304,17 +310,18 @@ gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, con
   const long long BH = (long long)B * H;
   const size_t b_bytes = align_up((size_t)BH * (size_t)T * 4);
   const size_t s_bytes = seg_bytes(BH, dk, dv, pl.segments);
+  const size_t need = fwd_workspace_bytes(BH, T, dk, dv, pl.segments);
   if (!workspace) {
-    *workspace_bytes = b_bytes + s_bytes;
+    *workspace_bytes = need;
     return GLA_OK;
   }
-  if (*workspace_bytes < b_bytes + s_bytes) return GLA_ERR_WORKSPACE;
+  if (*workspace_bytes < need) return GLA_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return GLA_ERR_ALIGN;
   if (!S_T) return GLA_ERR_NULL;
   if (T > 0 && (!q || !k || !v || !x || !o)) return GLA_ERR_NULL;
   if (!aligned(x, 4)) return GLA_ERR_ALIGN;
   const size_t es = elem_size(dtype);
-  const Range rws{workspace, b_bytes + s_bytes};
+  const Range rws{workspace, need};
   const Range ins[] = {{q, (size_t)BH * T * dk * es}, {k, (size_t)BH * T * dk * es}, {v, (size_t)BH * T * dv * es},
                        {x, (size_t)BH * T * 4},       {S0, (size_t)BH * dk * dv * 4}, {o, (size_t)BH * T * dv * 4},
                        {S_T, (size_t)BH * dk * dv * 4}};

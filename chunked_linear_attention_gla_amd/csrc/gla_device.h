@@ -52,10 +52,17 @@ __device__ __forceinline__ float sigmoid_hw(float x) {
 
 __device__ __forceinline__ float gate_bounded_sigmoid(float x) { return -5.0f * sigmoid_hw(x); }
 
-// g = -softplus(-x) = -(max(-x, 0) + log1p(e^-|x|)) = log sigmoid(x)
+// g = -softplus(-x) = -(max(-x, 0) + log1p(e^-|x|)) = log sigmoid(x), floored at
+// kSoftplusFloor.  The gate is unbounded below (x = -inf gives g = -inf, a = 0); the
+// chunked paths take differences of cumulative sums of g, where -inf - -inf would be
+// NaN.  At the floor e^g is already exactly 0 in fp32 (2^-184.7), so a = 0 is kept and
+// every decay product through such a token is an exact zero, while the cumulative
+// sums stay finite.  NaN input still gives NaN (the comparison is false for NaN).
+constexpr float kSoftplusFloor = -128.0f;
 __device__ __forceinline__ float gate_neg_softplus(float x) {
   const float z = -x;
-  return -(fmaxf(z, 0.0f) + log1pf(exp_e(-fabsf(z))));
+  const float g = -(fmaxf(z, 0.0f) + log1pf(exp_e(-fabsf(z))));
+  return g < kSoftplusFloor ? kSoftplusFloor : g;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {

@@ -85,7 +85,8 @@ typedef enum { GLA_BF16 = 0, GLA_F32 = 1 } gla_dtype_t;   /* storage of q, k, v 
 /* Log-decay g(x) [LCT §3.2]. */
 typedef enum {
   GLA_GATE_BOUNDED_SIGMOID = 0, /* g = -5 * sigmoid(x), range (-5, 0) (the product) */
-  GLA_GATE_NEG_SOFTPLUS = 1     /* g = -softplus(-x) = log sigmoid(x), range (-inf, 0) */
+  GLA_GATE_NEG_SOFTPLUS = 1     /* g = -softplus(-x) = log sigmoid(x), range (-inf, 0);
+                                   evaluated as max(g, -128): e^-128 is 0 in fp32 */
 } gla_gate_t;
 
 /* How the causal tiles of a chunk are computed. */
@@ -137,7 +138,9 @@ gla_status_t gla_workspace_size(int B, int H, long long T, int dk, int dv, gla_d
  * i.e. log Gamma restarted at every chunk boundary, computed by one 64-lane
  * wavefront scan per chunk.  x and b: [B][H][T] fp32 (b may not overlap x).
  * Non-finite x follows the gate's limits: x = +inf gives g = -5 (bounded) or
- * 0 (softplus); x = -inf gives g = 0 (bounded) or -inf (softplus); NaN gives NaN. */
+ * 0 (softplus); x = -inf gives g = 0 (bounded).  The softplus gate is floored at
+ * g = -128 (x = -inf included), where a = e^g is already exactly 0 in fp32, so a
+ * zero decay is kept while b stays finite.  NaN gives NaN. */
 gla_status_t gla_gate_cumsum(const float* x, float* b, int B, int H, long long T,
                              gla_gate_t gate, void* stream);
 

@@ -125,7 +125,20 @@ def test_ragged_and_empty_lengths_are_accepted(lib):
     for T in (0, 1, 63, 65, 200):
         rc, n = fwd(lib, T=T, plan=(1, 1))
         assert rc == OK
-        assert n == (2 * T * 4 + 255) // 256 * 256
+        assert n == max((2 * T * 4 + 255) // 256 * 256, 256)
+
+
+def test_empty_sequence_workspace_query_is_never_zero(lib):
+    """T = 0 still writes S_T, so the call must not be mistaken for a size query: a
+    caller that allocates exactly what the query reports gets a non-NULL buffer only if
+    the size is not 0.  Both queries report at least 256 bytes."""
+    rc, n = fwd(lib, B=2, H=3, T=0, dk=128, dv=128, plan=(1, 1))
+    assert rc == OK and n >= 256
+    n2 = ctypes.c_size_t(0)
+    assert lib.gla_workspace_size(2, 3, 0, 128, 128, BF16, UNIFIED, P(1, 1), ctypes.byref(n2)) == OK
+    assert n2.value == n
+    # one byte short of the reported size is rejected before any device call
+    assert fwd(lib, B=2, H=3, T=0, dk=128, dv=128, plan=(1, 1), ws=0x10000000, wsz=n - 1)[0] == WORKSPACE
 
 
 def test_workspace_too_small_and_misaligned(lib):

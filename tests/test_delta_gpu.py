@@ -8,7 +8,7 @@ import torch
 import oracle
 import chunked_linear_attention_gla_amd as gla
 from chunked_linear_attention_gla_amd import inputs as gin
-from gpu_util import CHAIN_TOL, TOL, device, rel
+from gpu_util import CHAIN_TOL, CHAIN_TOL_DELTA, TOL, device, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +125,7 @@ def test_chaining_matches_single_call():
     ob, Sb = gla.chunk_fwd_delta(*(cut(t, s, 640) for t in (q, k, v, x, be)), Sa)
     torch.cuda.synchronize()
     assert rel(torch.cat([oa, ob], 2).cpu().double().numpy(), o.cpu().double().numpy()) <= CHAIN_TOL
-    assert rel(Sb.cpu().double().numpy(), ST.cpu().double().numpy()) <= CHAIN_TOL
+    assert rel(Sb.cpu().double().numpy(), ST.cpu().double().numpy()) <= CHAIN_TOL_DELTA
 
 
 def test_empty_sequence_returns_initial_state():

@@ -2,14 +2,14 @@
 times).  The fp64 oracle runs on sampled heads (whole sequence) or on a prefix (all
 heads); properties that hold at any size (chaining, finiteness, determinism) cover
 the rest.  Bar: max |gpu - ref| / max |ref| <= 2e-2 (bf16 operands), separately for
-o and S_T; chained vs single GPU calls <= CHAIN_TOL."""
+o and S_T; chained vs single GPU calls <= CHAIN_TOL on o, <= CHAIN_TOL_STATE on S_T."""
 import numpy as np
 import pytest
 import torch
 
 import chunked_linear_attention_gla_amd as gla
 from chunked_linear_attention_gla_amd import inputs as gin
-from gpu_util import CHAIN_TOL, TOL, device, gpu_heads, gpu_rel, oracle_heads, rel
+from gpu_util import CHAIN_TOL, CHAIN_TOL_STATE, TOL, device, gpu_heads, gpu_rel, oracle_heads, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -77,7 +77,7 @@ def test_bf16_256k_chained_continuation():
     o2, S2 = run(second)
     assert gpu_rel(o1, o[:, :, :T1]) <= CHAIN_TOL
     assert gpu_rel(o2, o[:, :, T1:]) <= CHAIN_TOL
-    assert gpu_rel(S2, ST) <= CHAIN_TOL
+    assert gpu_rel(S2, ST) <= CHAIN_TOL_STATE
     check_heads(inp, o, ST, heads=[7])
 
 
@@ -100,7 +100,7 @@ def test_bf16_1m_prefix_and_continuity():
     rest["S0"] = S_p
     o_r, S_r = run(rest)
     assert gpu_rel(o_r, o[:, :, P:]) <= CHAIN_TOL
-    assert gpu_rel(S_r, ST) <= CHAIN_TOL
+    assert gpu_rel(S_r, ST) <= CHAIN_TOL_STATE
 
 
 def test_bf16_largest_head_extent():

@@ -8,7 +8,7 @@ import torch
 import oracle
 import chunked_linear_attention_gla_amd as gla
 from chunked_linear_attention_gla_amd import inputs as gin
-from gpu_util import CHAIN_TOL, TOL, device, gpu_heads, oracle_heads, rel
+from gpu_util import CHAIN_TOL, CHAIN_TOL_STATE, TOL, device, gpu_heads, oracle_heads, rel
 
 pytestmark = pytest.mark.gpu
 
@@ -45,11 +45,15 @@ def test_gate_cumsum_matches_fp64(gate, T):
     g = torch.Generator(device=dev).manual_seed(3)
     x = torch.randn(2, 3, T, device=dev, generator=g) * 3.0
     x[0, 0, 0] = float("inf")
-    x[1, 2, -1] = float("-inf") if gate == "bounded" else 50.0
+    x[1, 2, -1] = float("-inf")
+    x[1, 1, T // 2] = 50.0
     b = gla.gate_cumsum(x, gate=gate)
     torch.cuda.synchronize()
     xn = x.cpu().numpy()
-    ref = oracle.chunk_local_cumsum(np.pad(oracle.gate(xn, gate), [(0, 0), (0, 0), (0, (-T) % 64)]))[..., :T]
+    gref = oracle.gate(xn, gate)
+    if gate == "neg_softplus":
+        gref = np.maximum(gref, -128.0)  # the stage's documented floor (e^-128 is 0 in fp32)
+    ref = oracle.chunk_local_cumsum(np.pad(gref, [(0, 0), (0, 0), (0, (-T) % 64)]))[..., :T]
     got = b.cpu().double().numpy()
     assert np.all(np.abs(got - ref) <= 1e-6 * np.abs(ref) + 1e-6)
 
@@ -215,7 +219,55 @@ def test_chaining_matches_single_call():
     o2, S2 = gla.chunk_fwd(*(sl(inp[n], T1, None) for n in "qkvx"), S1)
     torch.cuda.synchronize()
     assert rel(torch.cat([o1, o2], 2).cpu().numpy(), o.cpu().numpy()) <= CHAIN_TOL
-    assert rel(S2.cpu().numpy(), ST.cpu().numpy()) <= CHAIN_TOL
+    assert rel(S2.cpu().numpy(), ST.cpu().numpy()) <= CHAIN_TOL_STATE
+
+
+@pytest.mark.parametrize("qkv", ["bf16", "f32"])
+def test_chaining_weak_decay_state_handover(qkv):
+    """Weak decay (x ~ N(-7,1): a ~ 0.995 per token) and a short second call (two
+    chunks), so the chained S_T depends strongly on the handed-over state: starting
+    the second call from zero instead moves S_T by far more than the bound.  The
+    single call runs a segmented plan (4 segments), the chained calls one segment each,
+    so the two sum the state in different orders."""
+    w, inp = small(64 * 12, H=2, x_mean=-7.0, qkv=qkv, seed=31)
+    o, ST = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], plan=gla.Plan(4, 1))
+    T1 = 64 * 10
+    sl = lambda t, a, b: t[:, :, a:b].contiguous()
+    o1, S1 = gla.chunk_fwd(*(sl(inp[n], 0, T1) for n in "qkvx"), inp["S0"], plan=gla.Plan(1, 1))
+    o2, S2 = gla.chunk_fwd(*(sl(inp[n], T1, None) for n in "qkvx"), S1, plan=gla.Plan(1, 1))
+    _, Sz = gla.chunk_fwd(*(sl(inp[n], T1, None) for n in "qkvx"), None, plan=gla.Plan(1, 1))
+    torch.cuda.synchronize()
+    es = rel(S2.cpu().double().numpy(), ST.cpu().double().numpy())
+    assert es <= CHAIN_TOL_STATE, es
+    assert rel(Sz.cpu().double().numpy(), ST.cpu().double().numpy()) > 0.1  # S_T does depend on S1
+    tol_o = CHAIN_TOL if qkv == "bf16" else CHAIN_TOL_STATE
+    assert rel(torch.cat([o1, o2], 2).cpu().double().numpy(), o.cpu().double().numpy()) <= tol_o
+    # and the single call against the fp64 oracle
+    o_ref, S_ref = oracle_heads(inp)
+    assert rel(ST.reshape(2, 128, 128).cpu().double().numpy(), S_ref) <= TOL[qkv]
+
+
+def test_empty_sequence_through_the_c_abi_with_queried_workspace():
+    """T = 0 through gla_chunk_fwd itself: the workspace is sized from the library's
+    own query and the call must write S_T = S0 (a 0-byte query would make a caller pass
+    a NULL workspace, which the library reads as another size query)."""
+    import ctypes
+    from chunked_linear_attention_gla_amd import _lib
+    lib = _lib.load()
+    dev = device()
+    B, H, d = 2, 3, 128
+    S0 = torch.randn(B, H, d, d, device=dev)
+    ST = torch.full_like(S0, float("nan"))
+    need = ctypes.c_size_t(0)
+    rc = lib.gla_chunk_fwd(None, None, None, None, S0.data_ptr(), None, ST.data_ptr(), B, H, 0, d, d, 0, 0, 0,
+                           None, ctypes.byref(need), None)
+    assert rc == 0 and need.value > 0
+    ws = torch.empty(need.value, dtype=torch.uint8, device=dev)
+    n = ctypes.c_size_t(need.value)
+    rc = lib.gla_chunk_fwd(None, None, None, None, S0.data_ptr(), None, ST.data_ptr(), B, H, 0, d, d, 0, 0, 0,
+                           ws.data_ptr(), ctypes.byref(n), torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert rc == 0 and torch.equal(ST, S0)
 
 
 def test_repeat_calls_are_bitwise_identical():
@@ -263,3 +315,52 @@ def test_forced_overflow_breaks_only_the_unified_factorisation():
     torch.cuda.synchronize()
     assert not torch.isfinite(o_u).all()
     check(inp, w, path="diag_branch", gate="neg_softplus")
+
+
+@pytest.mark.parametrize("qkv,dk", [("bf16", 128), ("f32", 64)])
+def test_softplus_gate_at_minus_infinity(qkv, dk):
+    """x = -inf under the softplus gate is a zero decay (a = 0) in the oracle.  The
+    kernels floor that gate at g = -128, whose exponential is already exactly 0 in fp32,
+    so cumulative log-decays stay finite: isolated tokens, a pair, and a whole chunk at
+    -inf, through the diagonal-branch path (the path built for that gate), against the
+    fp64 oracle with its exact a = 0."""
+    w, inp = small(64 * 5 + 9, H=2, dk=dk, dv=64, qkv=qkv, x_mean=-2.0, gate="neg_softplus", seed=41)
+    inp["x"][0, 0, [3, 70, 71, 150, 320]] = float("-inf")
+    inp["x"][0, 1, 64:128] = float("-inf")
+    check(inp, w, path="diag_branch", gate="neg_softplus")
+    check(inp, w, path="diag_branch", gate="neg_softplus", plan=gla.Plan(3, 1))
+
+
+def test_softplus_gate_at_minus_infinity_backward_and_decode():
+    """The same zero decays through the backward pass (diagonal-branch path, all five
+    gradients) and the decode step, against the fp64 oracles."""
+    dev = device()
+    w, inp = small(64 * 3 + 5, H=2, dk=64, dv=64, x_mean=-2.0, gate="neg_softplus", seed=43)
+    inp["x"][0, 0, [0, 5, 64, 65, 100]] = float("-inf")
+    inp["x"][0, 1, 128:192] = float("-inf")
+    gen = torch.Generator(device=dev).manual_seed(44)
+    dO = torch.randn(1, 2, w.T, 64, device=dev, generator=gen).to(torch.bfloat16)
+    dST = torch.randn(1, 2, 64, 64, device=dev, generator=gen) * 0.1
+    got = gla.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["x"], dO, inp["S0"], dST, gate="neg_softplus",
+                        path="diag_branch")
+    torch.cuda.synchronize()
+    flat = lambda t: t.reshape(2, *t.shape[2:])
+    ref = oracle.backward(*(gin.to_numpy_bits(flat(inp[n])) for n in ("q", "k", "v", "x")),
+                          flat(dO).cpu().double().numpy(), flat(inp["S0"]).cpu().double().numpy(),
+                          flat(dST).cpu().double().numpy(), gate="neg_softplus")
+    for name, g_, r_ in zip(("dq", "dk", "dv", "dx", "dS0"), got, ref):
+        g_ = g_.reshape(r_.shape).cpu().double().numpy()
+        assert np.isfinite(g_).all() and rel(g_, r_) <= TOL["bf16"], name
+    # decode: one token at x = -inf replaces the state by k v^T
+    wd = gin.WORKLOADS["bf16_decode"].with_(B=2, H=3, dk=64, dv=64, gate="neg_softplus")
+    dinp = gin.make_decode_inputs(wd, dev)
+    dinp["x"][0, 1] = float("-inf")
+    S_in = dinp["S"].clone()
+    od = gla.decode_step(dinp["q"], dinp["k"], dinp["v"], dinp["x"], dinp["S"], gate="neg_softplus")
+    torch.cuda.synchronize()
+    f1 = lambda t: t.reshape(6, 1, *t.shape[2:])
+    o_ref, S_ref = oracle.forward(*(gin.to_numpy_bits(f1(dinp[n])) for n in ("q", "k", "v")),
+                                  gin.to_numpy_bits(dinp["x"].reshape(6, 1)),
+                                  S_in.reshape(6, 64, 64).cpu().numpy().astype(np.float64), gate="neg_softplus")
+    assert rel(od.reshape(6, 1, 64).cpu().double().numpy(), o_ref) <= TOL["bf16"]
+    assert rel(dinp["S"].reshape(6, 64, 64).cpu().double().numpy(), S_ref) <= TOL["bf16"]
