@@ -2,9 +2,15 @@
 """Throughput of the bounded-decay chunked GLA forward pass on one MI355X.
 
 One step is one pass of the whole hot path over one batch of synthetic input that
-is already resident in HBM: the gate + chunk-local cumulative log-decay kernel,
-the segment pre-pass (when the plan has several segments) and the fused chunk
-output kernel, enqueued through the C ABI on the current stream.
+is already resident in HBM: the segment pre-pass (when the plan has several
+segments) and the fused chunk output kernel, both forming the gate and the
+chunk-local cumulative log-decay from x themselves, enqueued through the C ABI on
+the current stream.
+
+The device is brought to steady clocks before the warm-up steps (the settle phase:
+the step repeated for --settle-s seconds): from process start the output kernel
+runs ~14 % slower over its first ~25 ms of load while the clocks ramp up, and a
+short warm-up would time that ramp instead of the steady state.
 
 Prints one JSON line.  `value` is tokens/s (batch * sequence tokens, all heads) of
 the whole step; `roofline` is the fused output kernel (the dominant kernel): its
@@ -82,6 +88,8 @@ def parse():
     ap.add_argument("--path", default=None, help="unified (default) or diag_branch")
     ap.add_argument("--plan", default=None, help="segments,dv_split (default: the library's plan)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of repeated steps before the warm-up, so that timing starts at steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-ablation", action="store_true", help="skip the diagonal-branch comparison")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward-pass measurement")
@@ -127,6 +135,42 @@ def device_copy_rate(torch, nbytes: int = 1 << 30, reps: int = 10) -> dict:
     del src, dst
     return {"what": "device-to-device copy of 1 GiB (bytes read + written per second)", "ms": round(ms, 4),
             "GB_per_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def settle(torch, fn, seconds: float) -> float:
+    """Repeat fn (enqueueing GPU work) for about `seconds` of wall time, synchronising every
+    few calls, so that the device's clocks have ramped up before anything is timed.
+    Returns the seconds spent."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            fn()
+        torch.cuda.synchronize()
+    return round(time.perf_counter() - t0, 3)
+
+
+def stream_ceiling(gla, torch, nbytes: int, reps: int = 10) -> dict:
+    """The forward's byte mix (3 x nbytes read, 2 x nbytes written: q, k, v and o of the
+    headline step) as one flat grid-stride stream (gla_bench_stream, a HIP kernel of this
+    library): the practical streaming rate of this device for that mix."""
+    dev = torch.device("cuda:0")
+    a = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+    b, c = torch.ones_like(a), torch.ones_like(a)
+    out = torch.empty(2 * nbytes, dtype=torch.uint8, device=dev)
+    fn = lambda: gla.bench_stream(a, b, c, out)
+    settle(torch, fn, 0.1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        fn()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    gbs = 5 * nbytes / (ms / 1e3) / 1e9
+    del a, b, c, out
+    return {"what": f"flat grid-stride stream of the step's byte mix (3 x {nbytes >> 20} MiB read, "
+                    f"{2 * nbytes >> 20} MiB written; gla_bench_stream, 8192 workgroups)",
+            "ms": round(ms, 4), "GB_per_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(w, target_s: float, per_channel: bool = False):
@@ -213,8 +257,9 @@ def load_traffic(kernel: str, workload: str, plan, path: str):
 
 class StepTimer:
     """One workload, one path: inputs, outputs and workspace on the device, and a step
-    that enqueues the gate + cumsum kernel, the segment pre-pass and the output pass,
-    with optional HIP events between them on the current stream."""
+    that enqueues the segment pre-pass and the output pass (both forming the gate and
+    the chunk-local cumulative log-decay from x), with optional HIP events between them
+    on the current stream."""
 
     def __init__(self, gla, gin, torch, w, path, plan=None):
         dev = torch.device("cuda:0")
@@ -228,7 +273,6 @@ class StepTimer:
         self.plan = plan or gla.plan_default(B, H, T, dk, dv, dt_code, path)
         self.o = torch.empty(B, H, T, dv, device=dev, dtype=torch.float32)
         self.ST = torch.empty(B, H, dk, dv, device=dev, dtype=torch.float32)
-        self.b = torch.empty(B, H, T, device=dev, dtype=torch.float32)
         seg_bytes = gla.segment_workspace_size(B, H, T, dk, dv, self.plan)
         self.seg = torch.empty(max(seg_bytes, 256), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
@@ -237,32 +281,31 @@ class StepTimer:
         gla, plan = self.gla, self.plan
         if evs is not None:
             evs[0].record()
-        gla.gate_cumsum(self.x, gate=self.w.gate, out=self.b)
+        if plan.segments > 1:
+            gla.segment_states(self.k, self.v, self.x, plan, self.seg, gate=self.w.gate)
         if evs is not None:
             evs[1].record()
-        if plan.segments > 1:
-            gla.segment_states(self.k, self.v, self.b, plan, self.seg)
+        gla.chunk_output(self.q, self.k, self.v, self.x, self.S0, plan, self.seg if plan.segments > 1 else None,
+                         self.o, self.ST, gate=self.w.gate, path=self.path)
         if evs is not None:
             evs[2].record()
-        gla.chunk_output(self.q, self.k, self.v, self.b, self.S0, plan, self.seg if plan.segments > 1 else None,
-                         self.o, self.ST, path=self.path)
-        if evs is not None:
-            evs[3].record()
 
-    def run(self, steps, warmup):
-        """Returns (ms per step from the host clock, [gate, pre-pass, output] ms from events)."""
+    def run(self, steps, warmup, settle_s=0.0):
+        """Returns (ms per step from the host clock, [pre-pass, output] ms from events)."""
         torch = self.torch
+        if settle_s > 0:
+            settle(torch, self.step, settle_s)
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
-        events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             self.step(events[i])
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        stage = [sum(e[j].elapsed_time(e[j + 1]) for e in events) / steps for j in range(3)]
+        stage = [sum(e[j].elapsed_time(e[j + 1]) for e in events) / steps for j in range(2)]
         return elapsed * 1e3 / steps, stage
 
 
@@ -294,9 +337,11 @@ class BackwardTimer:
         self.gla.chunk_bwd(self.q, self.k, self.v, self.x, self.dO, self.S0, self.dST, gate=self.w.gate,
                            path=self.path, workspace=self.ws, out=self.out)
 
-    def run(self, steps, warmup):
+    def run(self, steps, warmup, settle_s=0.0):
         """Returns (ms per call from the host clock, ms per call from events)."""
         torch = self.torch
+        if settle_s > 0:
+            settle(torch, self.step, settle_s)
         for _ in range(warmup):
             self.step()
         torch.cuda.synchronize()
@@ -311,8 +356,11 @@ class BackwardTimer:
         return elapsed * 1e3 / steps, ev[0].elapsed_time(ev[steps]) / steps
 
 
-def time_calls(torch, fn, steps, warmup):
-    """(ms per call from the host clock, ms per call from HIP events on the current stream)."""
+def time_calls(torch, fn, steps, warmup, settle_s=0.3):
+    """(ms per call from the host clock, ms per call from HIP events on the current stream),
+    after settle_s seconds of repeated calls (steady clocks) and `warmup` calls."""
+    if settle_s > 0:
+        settle(torch, fn, settle_s)
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -364,26 +412,43 @@ def per_channel_result(gla, gin, torch, steps, warmup, cpu_seconds):
     return res
 
 
-def decode_result(gla, gin, torch, steps, warmup, cpu_seconds):
+def decode_result(gla, gin, torch, steps, warmup, cpu_seconds, sets: int = 6):
     """One decode step for every (sequence, head) of a serving batch (gla_decode_step),
-    the state updated in place."""
+    the state updated in place.  The timed steps rotate over `sets` independent batches
+    (inputs and states), 128 MiB of state each, so that the 768 MiB they span exceed the
+    256 MB Infinity Cache and every step streams its state from HBM; the same step
+    repeated on one batch (its state then stays cache-resident) is reported beside it."""
     import numpy as np
     w = gin.WORKLOADS["bf16_decode"]
     dev = torch.device("cuda:0")
-    inp = gin.make_decode_inputs(w, dev)
+    batches = [gin.make_decode_inputs(w, dev, seed=w.seed + 1000 * i) for i in range(sets)]
+    inp = batches[0]
     o = torch.empty(w.B, w.H, w.dv, device=dev)
-    fn = lambda: gla.decode_step(inp["q"], inp["k"], inp["v"], inp["x"], inp["S"], gate=w.gate, o=o)
-    ms_host, ms_ev = time_calls(torch, fn, steps * 10, warmup)
+    step = lambda b_: gla.decode_step(b_["q"], b_["k"], b_["v"], b_["x"], b_["S"], gate=w.gate, o=o)
+    it = [0]
+
+    def rotating():
+        step(batches[it[0] % sets])
+        it[0] += 1
+    n_steps = steps * 10 // sets * sets
+    ms_host, ms_ev = time_calls(torch, rotating, n_steps, warmup)
+    _, ms_res = time_calls(torch, lambda: step(inp), steps * 10, warmup, settle_s=0.05)
     es = inp["q"].element_size()
     bh = w.B * w.H
     per_head = 2 * w.dk * w.dv * 4 + (2 * w.dk + w.dv) * es + 4 + 4 * w.dv
     achieved = bh * per_head / (ms_ev / 1e3) / 1e9
     res = {"what": "gla_decode_step: one token per (sequence, head), fp32 state read and written in place",
-           "workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "steps": steps * 10,
+           "workload": w.name, "B": w.B, "H": w.H, "dk": w.dk, "dv": w.dv, "steps": n_steps,
+           "state_sets": sets, "state_MiB_total": sets * bh * w.dk * w.dv * 4 >> 20,
            "ms_per_step": round(ms_host, 5), "ms_per_step_events": round(ms_ev, 5),
            "tokens_per_s": round(w.B / (ms_ev / 1e3), 1),
            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": bh * per_head}}
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_step": bh * per_head},
+           "cache_resident": {
+               "what": "the same step repeated on one batch: its 128 MiB state stays in the Infinity Cache, "
+                       "so this rate is not an HBM figure",
+               "ms_per_step_events": round(ms_res, 5),
+               "GB_per_s": round(bh * per_head / (ms_res / 1e3) / 1e9, 1)}}
     if cpu_seconds > 0:
         import oracle
         flat = lambda t: t.reshape(bh, 1, *t.shape[2:])
@@ -486,9 +551,9 @@ def delta_result(gla, gin, torch, steps, warmup, cpu_seconds):
     return res
 
 
-def backward_result(gla, gin, torch, w, path, steps, warmup):
+def backward_result(gla, gin, torch, w, path, steps, warmup, settle_s=0.3):
     t = BackwardTimer(gla, gin, torch, w, path)
-    ms_host, ms_ev = t.run(steps, warmup)
+    ms_host, ms_ev = t.run(steps, warmup, settle_s)
     B, H, T, dk, dv = t.shape
     es = t.q.element_size()
     del t
@@ -543,7 +608,7 @@ def main():
         return
     timer = StepTimer(gla, gin, torch, w, path, plan)
     plan = timer.plan
-    ms_step, (ms_gate, ms_seg, ms_out) = timer.run(args.steps, args.warmup)
+    ms_step, (ms_seg, ms_out) = timer.run(args.steps, args.warmup, args.settle_s)
     B, H, T, dk, dv = timer.shape
     es = timer.q.element_size()
     S0 = timer.S0
@@ -577,8 +642,8 @@ def main():
                    "plan": {"segments": plan.segments, "dv_split": plan.dv_split}},
         "tflops": round(tflops, 2),
         "tflops_frac_bf16_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
-        "stage_ms": {"gate_cumsum": round(ms_gate, 4), "segment_states": round(ms_seg, 4),
-                     "chunk_output": round(ms_out, 4)},
+        "settle_s": args.settle_s,
+        "stage_ms": {"segment_states": round(ms_seg, 4), "chunk_output": round(ms_out, 4)},
         "roofline": {
             "kernel": kname,
             "bound": "hbm",
@@ -590,7 +655,8 @@ def main():
             "algorithmic_bytes_per_launch": bytes_out,
             "avg_launch_ms": round(ms_out, 4),
         },
-        "context": {"device_copy": device_copy_rate(torch)},
+        "context": {"device_copy": device_copy_rate(torch),
+                    "stream_ceiling": stream_ceiling(gla, torch, B * H * T * dk * es)},
     }
     if w.name == gin.HEADLINE and path == "unified" and not args.plan and not args.no_ablation:
         # the pages' comparison: conventional gate + diagonal branch against the unified
@@ -600,8 +666,8 @@ def main():
         abl = {"workload": wa.name, "gate": wa.gate, "x": f"N({wa.x_mean},{wa.x_std})", "steps": steps_a}
         for p_ in ("diag_branch", "unified"):
             t = StepTimer(gla, gin, torch, wa, p_)
-            ms_a, st_a = t.run(steps_a, min(args.warmup, 5))
-            abl[p_] = {"ms_per_step": round(ms_a, 4), "chunk_output_ms": round(st_a[2], 4),
+            ms_a, st_a = t.run(steps_a, min(args.warmup, 5), args.settle_s)
+            abl[p_] = {"ms_per_step": round(ms_a, 4), "chunk_output_ms": round(st_a[1], 4),
                        "tokens_per_s": round(wa.B * wa.T / (ms_a / 1e3), 1)}
             del t
         abl["unified_speedup_step"] = round(abl["diag_branch"]["ms_per_step"] / abl["unified"]["ms_per_step"], 3)
@@ -614,16 +680,16 @@ def main():
         ww = w.with_(x_mean=-6.0, x_std=1.0)
         steps_w = min(args.steps, 20)
         t = StepTimer(gla, gin, torch, ww, path)
-        ms_w, st_w = t.run(steps_w, min(args.warmup, 5))
+        ms_w, st_w = t.run(steps_w, min(args.warmup, 5), args.settle_s)
         del t
         result["weak_decay"] = {
             "what": "same shapes, x ~ N(-6,1): the segment pre-pass runs every chunk (no exact truncation)",
             "x": f"N({ww.x_mean},{ww.x_std})", "steps": steps_w, "ms_per_step": round(ms_w, 4),
-            "stage_ms": {"gate_cumsum": round(st_w[0], 4), "segment_states": round(st_w[1], 4),
-                         "chunk_output": round(st_w[2], 4)},
+            "stage_ms": {"segment_states": round(st_w[0], 4), "chunk_output": round(st_w[1], 4)},
             "tokens_per_s": round(ww.B * ww.T / (ms_w / 1e3), 1)}
     if not args.no_backward and not args.plan:
-        result["backward"] = backward_result(gla, gin, torch, w, path, min(args.steps, 20), min(args.warmup, 5))
+        result["backward"] = backward_result(gla, gin, torch, w, path, min(args.steps, 20), min(args.warmup, 5),
+                                             args.settle_s)
         if not args.no_cpu_baseline:
             result["backward"]["cpu_baseline"] = cpu_baseline_backward(w, args.cpu_seconds / 2)
     if not args.no_per_channel and not args.plan and w.name == gin.HEADLINE:

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgla.so")
 SOURCES = ["gate_cumsum.hip", "chunk_kernels.hip", "ws_kernels.hip", "bwd_kernels.hip", "pc_kernels.hip",
-           "decode.hip", "delta_kernels.hip", "api.hip"]
+           "decode.hip", "delta_kernels.hip", "bench_stream.hip", "api.hip"]
 ARCH = os.environ.get("GLA_OFFLOAD_ARCH", "gfx950")
 
 

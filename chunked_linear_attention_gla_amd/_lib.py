@@ -57,8 +57,8 @@ _SIGS = {
     "gla_segment_workspace_size": (_i, [_i, _i, _ll, _i, _i, _pplan, _psz]),
     "gla_workspace_size": (_i, [_i, _i, _ll, _i, _i, _i, _i, _pplan, _psz]),
     "gla_gate_cumsum": (_i, [_vp, _vp, _i, _i, _ll, _i, _vp]),
-    "gla_segment_states": (_i, [_vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _pplan, _vp, _sz, _vp]),
-    "gla_chunk_output": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan,
+    "gla_segment_states": (_i, [_vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan, _vp, _sz, _vp]),
+    "gla_chunk_output": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i, _pplan,
                               _vp, _sz, _vp]),
     "gla_chunk_fwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i,
                            _vp, _psz, _vp]),
@@ -75,6 +75,7 @@ _SIGS = {
     "gla_plan_check_delta": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
     "gla_chunk_fwd_delta": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan, _vp,
                                  _psz, _vp]),
+    "gla_bench_stream": (_i, [_vp, _vp, _vp, _vp, ctypes.c_ulonglong, _i, _vp]),
     "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
                            _i, _i, _i, _vp, _psz, _vp]),
 }
@@ -214,27 +215,28 @@ def gate_cumsum(x: torch.Tensor, gate="bounded", out: Optional[torch.Tensor] = N
     return out
 
 
-def segment_states(k: torch.Tensor, v: torch.Tensor, b: torch.Tensor, plan: Plan, seg_ws: torch.Tensor) -> None:
-    """Segment pre-pass into seg_ws (uint8 tensor of segment_workspace_size bytes)."""
-    B, H, T, dk, dv = _check_qkv(k, k, v)
-    _need(tuple(b.shape) == (B, H, T) and b.dtype == torch.float32 and b.is_contiguous(), "b must be fp32 [B,H,T]")
+def segment_states(k: torch.Tensor, v: torch.Tensor, x: torch.Tensor, plan: Plan, seg_ws: torch.Tensor,
+                   gate="bounded") -> None:
+    """Segment pre-pass into seg_ws (uint8 tensor of segment_workspace_size bytes); x is the
+    fp32 [B, H, T] gate pre-activation."""
+    B, H, T, dk, dv = _check_qkv(k, k, v, x)
     _check("gla_segment_states", load().gla_segment_states(
-        _ptr(k), _ptr(v), _ptr(b), B, H, T, dk, dv, _dtype_code(k), _cplan(plan), _ptr(seg_ws),
+        _ptr(k), _ptr(v), _ptr(x), B, H, T, dk, dv, _dtype_code(k), _gate(gate), _cplan(plan), _ptr(seg_ws),
         seg_ws.numel() * seg_ws.element_size(), _stream(k.device)))
 
 
-def chunk_output(q, k, v, b, S0, plan: Plan, seg_ws: Optional[torch.Tensor], o: torch.Tensor,
-                 S_T: torch.Tensor, path="unified") -> None:
-    """Fused output pass (o and S_T written in place)."""
-    B, H, T, dk, dv = _check_qkv(q, k, v, None, S0)
-    _need(tuple(b.shape) == (B, H, T) and b.dtype == torch.float32 and b.is_contiguous(), "b must be fp32 [B,H,T]")
+def chunk_output(q, k, v, x, S0, plan: Plan, seg_ws: Optional[torch.Tensor], o: torch.Tensor,
+                 S_T: torch.Tensor, gate="bounded", path="unified") -> None:
+    """Fused output pass (o and S_T written in place); x is the fp32 [B, H, T] gate
+    pre-activation."""
+    B, H, T, dk, dv = _check_qkv(q, k, v, x, S0)
     _need(tuple(o.shape) == (B, H, T, dv) and o.dtype == torch.float32 and o.is_contiguous(), "o must be fp32 [B,H,T,dv]")
     _need(tuple(S_T.shape) == (B, H, dk, dv) and S_T.dtype == torch.float32 and S_T.is_contiguous(),
           "S_T must be fp32 [B,H,dk,dv]")
     nbytes = 0 if seg_ws is None else seg_ws.numel() * seg_ws.element_size()
     _check("gla_chunk_output", load().gla_chunk_output(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(b), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, _dtype_code(q),
-        _path(path), _cplan(plan), _ptr(seg_ws), nbytes, _stream(q.device)))
+        _ptr(q), _ptr(k), _ptr(v), _ptr(x), _ptr(S0), _ptr(o), _ptr(S_T), B, H, T, dk, dv, _dtype_code(q),
+        _gate(gate), _path(path), _cplan(plan), _ptr(seg_ws), nbytes, _stream(q.device)))
 
 
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor,
@@ -473,3 +475,15 @@ def chunk_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, x: torch.Tensor
     have = ctypes.c_size_t(workspace.numel() * workspace.element_size())
     _check("gla_chunk_bwd", lib.gla_chunk_bwd(*args(_ptr(workspace)), ctypes.byref(have), _stream(dev)))
     return dq, dk_, dv_, dx, dS0
+
+
+def bench_stream(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor, out: torch.Tensor, grid: int = 8192) -> None:
+    """Measurement helper: the forward's byte mix as one flat stream (gla_bench_stream).
+    a, b, c: tensors of n bytes (n a multiple of 16); out: 2n bytes; all on one GPU."""
+    nb = a.numel() * a.element_size()
+    _need(nb % 16 == 0 and all(t.numel() * t.element_size() == nb for t in (b, c)), "a, b, c must have n bytes")
+    _need(out.numel() * out.element_size() == 2 * nb, "out must have 2n bytes")
+    for t in (a, b, c, out):
+        _need(t.is_cuda and t.is_contiguous() and t.device == a.device, "tensors must be contiguous on one GPU")
+    _check("gla_bench_stream", load().gla_bench_stream(_ptr(a), _ptr(b), _ptr(c), _ptr(out), nb // 16, grid,
+                                                       _stream(a.device)))

@@ -75,11 +75,12 @@ size_t seg_bytes(long long BH, int dk, int dv, int segments) {
          align_up((size_t)BH * (size_t)segments * 4);
 }
 
-// Workspace of the forward pass: b, then the segment workspace.  Never 0 (T = 0 has
-// neither): a caller that allocates what the query reports then holds a non-NULL
-// buffer, which the call does not mistake for another size query.
-size_t fwd_workspace_bytes(long long BH, long long T, int dk, int dv, int segments) {
-  return std::max(align_up((size_t)BH * (size_t)T * 4) + seg_bytes(BH, dk, dv, segments), kAlign);
+// Workspace of the forward pass: the segment workspace (the kernels form the
+// cumulative log-decays from x themselves).  Never 0: a caller that allocates what
+// the query reports then holds a non-NULL buffer, which the call does not mistake
+// for another size query (T = 0 still writes S_T).
+size_t fwd_workspace_bytes(long long BH, int dk, int dv, int segments) {
+  return std::max(seg_bytes(BH, dk, dv, segments), kAlign);
 }
 
 // Default plan.  Measured on MI355X (256 CUs): one workgroup per CU, each owning a
@@ -124,6 +125,8 @@ gla::ChunkParams make_params(const void* q, const void* k, const void* v, const 
   p.k = k;
   p.v = v;
   p.b = b;
+  p.x = nullptr;
+  p.gate = gla::kGateBoundedSigmoid;
   p.S0 = S0;
   p.o = o;
   p.ST = S_T;
@@ -218,7 +221,7 @@ gla_status_t gla_workspace_size(int B, int H, long long T, int dk, int dv, gla_d
     st = gla_plan_default(B, H, T, dk, dv, dtype, path, &pl);
     if (st != GLA_OK) return st;
   }
-  *bytes = fwd_workspace_bytes((long long)B * H, T, dk, dv, pl.segments);
+  *bytes = fwd_workspace_bytes((long long)B * H, dk, dv, pl.segments);
   return GLA_OK;
 }
 
@@ -238,51 +241,57 @@ gla_status_t gla_gate_cumsum(const float* x, float* b, int B, int H, long long T
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
-gla_status_t gla_segment_states(const void* k, const void* v, const float* b, int B, int H, long long T, int dk,
-                                int dv, gla_dtype_t dtype, const gla_plan_t* plan, void* seg_ws,
+gla_status_t gla_segment_states(const void* k, const void* v, const float* x, int B, int H, long long T, int dk,
+                                int dv, gla_dtype_t dtype, gla_gate_t gate, const gla_plan_t* plan, void* seg_ws,
                                 size_t seg_ws_bytes, void* stream) {
   gla_status_t st = plan_check_impl(B, H, T, dk, dv, dtype, GLA_PATH_UNIFIED, plan);
   if (st != GLA_OK) return st;
+  if (!valid_gate(gate)) return GLA_ERR_ARG;
   if (plan->segments <= 1 || T == 0) return GLA_OK;
-  if (!k || !v || !b) return GLA_ERR_NULL;
+  if (!k || !v || !x) return GLA_ERR_NULL;
   const long long BH = (long long)B * H;
   const size_t need = seg_bytes(BH, dk, dv, plan->segments);
   if (!seg_ws || seg_ws_bytes < need) return GLA_ERR_WORKSPACE;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(b, 4) || !aligned(seg_ws, kAlign)) return GLA_ERR_ALIGN;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(x, 4) || !aligned(seg_ws, kAlign)) return GLA_ERR_ALIGN;
   const size_t es = elem_size(dtype);
   const Range ws{seg_ws, need};
   if (overlap(ws, {k, (size_t)BH * T * dk * es}) || overlap(ws, {v, (size_t)BH * T * dv * es}) ||
-      overlap(ws, {b, (size_t)BH * T * 4}))
+      overlap(ws, {x, (size_t)BH * T * 4}))
     return GLA_ERR_ALIAS;
-  gla::ChunkParams p = make_params(nullptr, k, v, b, nullptr, nullptr, nullptr, B, H, T, dk, dv, *plan, seg_ws);
+  gla::ChunkParams p = make_params(nullptr, k, v, nullptr, nullptr, nullptr, nullptr, B, H, T, dk, dv, *plan, seg_ws);
+  p.x = x;
+  p.gate = gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus;
   p.grid = (int)(BH * plan->dv_split * (plan->segments - 1));
   hipError_t e = gla::launch_segment_states(p, dtype == GLA_BF16 ? 0 : 1, (hipStream_t)stream);
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;
 }
 
-gla_status_t gla_chunk_output(const void* q, const void* k, const void* v, const float* b, const float* S0,
+gla_status_t gla_chunk_output(const void* q, const void* k, const void* v, const float* x, const float* S0,
                               float* o, float* S_T, int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
-                              gla_path_t path, const gla_plan_t* plan, const void* seg_ws, size_t seg_ws_bytes,
-                              void* stream) {
+                              gla_gate_t gate, gla_path_t path, const gla_plan_t* plan, const void* seg_ws,
+                              size_t seg_ws_bytes, void* stream) {
   gla_status_t st = plan_check_impl(B, H, T, dk, dv, dtype, path, plan);
   if (st != GLA_OK) return st;
+  if (!valid_gate(gate)) return GLA_ERR_ARG;
   if (!S_T) return GLA_ERR_NULL;
-  if (T > 0 && (!q || !k || !v || !b || !o)) return GLA_ERR_NULL;
+  if (T > 0 && (!q || !k || !v || !x || !o)) return GLA_ERR_NULL;
   const long long BH = (long long)B * H;
   const size_t es = elem_size(dtype);
   const size_t need = seg_bytes(BH, dk, dv, plan->segments);
   if (plan->segments > 1 && (!seg_ws || seg_ws_bytes < need)) return GLA_ERR_WORKSPACE;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16) || !aligned(S_T, 16) ||
-      !aligned(S0, 16) || !aligned(b, 4))
+      !aligned(S0, 16) || !aligned(x, 4))
     return GLA_ERR_ALIGN;
   const Range rq{q, (size_t)BH * T * dk * es}, rk{k, (size_t)BH * T * dk * es}, rv{v, (size_t)BH * T * dv * es};
-  const Range rb{b, (size_t)BH * T * 4}, rs0{S0, (size_t)BH * dk * dv * 4};
+  const Range rx{x, (size_t)BH * T * 4}, rs0{S0, (size_t)BH * dk * dv * 4};
   const Range ro{o, (size_t)BH * T * dv * 4}, rst{S_T, (size_t)BH * dk * dv * 4};
   const Range rws{plan->segments > 1 ? seg_ws : nullptr, need};
-  for (const Range& in : {rq, rk, rv, rb, rs0, rws})
+  for (const Range& in : {rq, rk, rv, rx, rs0, rws})
     if (overlap(ro, in) || overlap(rst, in)) return GLA_ERR_ALIAS;
   if (overlap(ro, rst)) return GLA_ERR_ALIAS;
-  gla::ChunkParams p = make_params(q, k, v, b, S0, o, S_T, B, H, T, dk, dv, *plan, seg_ws);
+  gla::ChunkParams p = make_params(q, k, v, nullptr, S0, o, S_T, B, H, T, dk, dv, *plan, seg_ws);
+  p.x = x;
+  p.gate = gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus;
   p.grid = (int)(BH * plan->dv_split * plan->segments);
   hipError_t e = gla::launch_chunk_output(p, dtype == GLA_BF16 ? 0 : 1, path == GLA_PATH_DIAG_BRANCH,
                                           (hipStream_t)stream);
@@ -308,9 +317,8 @@ gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, con
     if (st != GLA_OK) return st;
   }
   const long long BH = (long long)B * H;
-  const size_t b_bytes = align_up((size_t)BH * (size_t)T * 4);
   const size_t s_bytes = seg_bytes(BH, dk, dv, pl.segments);
-  const size_t need = fwd_workspace_bytes(BH, T, dk, dv, pl.segments);
+  const size_t need = fwd_workspace_bytes(BH, dk, dv, pl.segments);
   if (!workspace) {
     *workspace_bytes = need;
     return GLA_OK;
@@ -328,8 +336,7 @@ gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, con
   for (const Range& r : ins)
     if (overlap(rws, r)) return GLA_ERR_ALIAS;
   if (overlap(ins[5], ins[3]) || overlap(ins[6], ins[3])) return GLA_ERR_ALIAS;  // o, S_T vs x
-  float* bbuf = (float*)workspace;
-  void* seg = (char*)workspace + b_bytes;
+  void* seg = workspace;
   // Validate the output pass fully before enqueueing anything.
   {
     const Range rq = ins[0], rk = ins[1], rv = ins[2], rs0 = ins[4], ro = ins[5], rst = ins[6];
@@ -340,13 +347,11 @@ gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, con
       if (overlap(ro, in) || overlap(rst, in)) return GLA_ERR_ALIAS;
     if (overlap(ro, rst)) return GLA_ERR_ALIAS;
   }
-  st = gla_gate_cumsum(x, bbuf, B, H, T, gate, stream);
-  if (st != GLA_OK) return st;
   if (pl.segments > 1) {
-    st = gla_segment_states(k, v, bbuf, B, H, T, dk, dv, dtype, &pl, seg, s_bytes, stream);
+    st = gla_segment_states(k, v, x, B, H, T, dk, dv, dtype, gate, &pl, seg, s_bytes, stream);
     if (st != GLA_OK) return st;
   }
-  return gla_chunk_output(q, k, v, bbuf, S0, o, S_T, B, H, T, dk, dv, dtype, path, &pl, seg, s_bytes, stream);
+  return gla_chunk_output(q, k, v, x, S0, o, S_T, B, H, T, dk, dv, dtype, gate, path, &pl, seg, s_bytes, stream);
 }
 
 gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const float* x, const float* S0,
@@ -502,14 +507,13 @@ gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
     if (st != GLA_OK) return st;
   }
   const long long NH = (long long)N * H;
-  const size_t b_bytes = align_up((size_t)H * (size_t)T * 4);
   const size_t s_bytes = seg_bytes(NH, dk, dv, pl.segments);
   const size_t o_bytes = align_up((size_t)N * 4);
   if (!workspace) {
-    *workspace_bytes = b_bytes + s_bytes + o_bytes;
+    *workspace_bytes = s_bytes + o_bytes;
     return GLA_OK;
   }
-  if (*workspace_bytes < b_bytes + s_bytes + o_bytes) return GLA_ERR_WORKSPACE;
+  if (*workspace_bytes < s_bytes + o_bytes) return GLA_ERR_WORKSPACE;
   if (!aligned(workspace, kAlign)) return GLA_ERR_ALIGN;
   if (!S_T || !cu_seqlens) return GLA_ERR_NULL;
   if (T > 0 && (!q || !k || !v || !x || !o)) return GLA_ERR_NULL;
@@ -521,25 +525,22 @@ gla_status_t gla_chunk_fwd_varlen(const void* q, const void* k, const void* v, c
                        {v, (size_t)H * T * dv * es},      {x, (size_t)H * T * 4},
                        {S0, (size_t)NH * dk * dv * 4},    {cu_seqlens, (size_t)(N + 1) * 8}};
   const Range outs[] = {{o, (size_t)H * T * dv * 4}, {S_T, (size_t)NH * dk * dv * 4},
-                        {workspace, b_bytes + s_bytes + o_bytes}};
+                        {workspace, s_bytes + o_bytes}};
   for (size_t i = 0; i < 3; ++i) {
     for (const Range& in : ins)
       if (overlap(outs[i], in)) return GLA_ERR_ALIAS;
     for (size_t j = i + 1; j < 3; ++j)
       if (overlap(outs[i], outs[j])) return GLA_ERR_ALIAS;
   }
-  float* bbuf = (float*)workspace;
-  void* seg = (char*)workspace + b_bytes;
+  void* seg = workspace;
   hipStream_t s = (hipStream_t)stream;
   const int dt = dtype == GLA_BF16 ? 0 : 1;
   const long long max_chunks = n_chunks(max_seqlen);
-  int* order = (int*)((char*)workspace + b_bytes + s_bytes);
+  int* order = (int*)((char*)workspace + s_bytes);
   hipError_t e = gla::launch_varlen_order(cu_seqlens, N, T, max_chunks, order, s);
-  if (e == hipSuccess)
-    e = gla::launch_gate_cumsum_varlen(
-      x, bbuf, cu_seqlens, N, H, T, max_chunks,
-      gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus, s);
-  gla::ChunkParams p = make_params(q, k, v, bbuf, S0, o, S_T, N, H, T, dk, dv, pl, seg);
+  gla::ChunkParams p = make_params(q, k, v, nullptr, S0, o, S_T, N, H, T, dk, dv, pl, seg);
+  p.x = x;
+  p.gate = gate == GLA_GATE_BOUNDED_SIGMOID ? gla::kGateBoundedSigmoid : gla::kGateNegSoftplus;
   p.cu_seqlens = cu_seqlens;
   p.nchunks = (int)max_chunks;
   p.unit_order = order;

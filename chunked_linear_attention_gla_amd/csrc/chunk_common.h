@@ -90,7 +90,7 @@ __device__ __forceinline__ HeadSpan head_span(const ChunkParams& p, int bh) {
 // Per-unit buffer descriptors of the streamed tensors (sized to the unit's rows) and
 // the unit's row counts.
 struct HeadBuffers {
-  rsrc_t q, k, v, b, o;
+  rsrc_t q, k, v, b, x, o;
   uint32_t T, Tl;
 };
 
@@ -101,7 +101,8 @@ __device__ __forceinline__ HeadBuffers head_buffers(const ChunkParams& p, const 
   hb.q = p.q ? make_rsrc(static_cast<const T*>(p.q) + s.row0 * DK, s.T * DK * es) : make_rsrc(nullptr, 0u);
   hb.k = make_rsrc(static_cast<const T*>(p.k) + s.row0 * DK, s.T * DK * es);
   hb.v = make_rsrc(static_cast<const T*>(p.v) + s.row0 * p.dv, s.T * (uint32_t)p.dv * es);
-  hb.b = make_rsrc(p.b + s.brow0, s.Tl * 4u);
+  hb.b = p.b ? make_rsrc(p.b + s.brow0, s.Tl * 4u) : make_rsrc(nullptr, 0u);
+  hb.x = p.x ? make_rsrc(p.x + s.brow0, s.Tl * 4u) : make_rsrc(nullptr, 0u);
   hb.o = p.o ? make_rsrc(p.o + s.row0 * p.dv, s.T * (uint32_t)p.dv * 4u) : make_rsrc(nullptr, 0u);
   hb.T = s.T;
   hb.Tl = s.Tl;
@@ -125,6 +126,39 @@ struct ChunkDecay {
   __device__ __forceinline__ float end(int u) const { return u == 0 ? r1 : u == 1 ? r2 : u == 2 ? r3 : gam; }
   // b of another token of the chunk
   __device__ __forceinline__ float at(int j) const { return __shfl(b, j); }
+};
+
+// ---------------------------------------------------------------- log-decays of a chunk
+//
+// Lane j of a wave needs b_j, the chunk-local cumulative log-decay of token j of the
+// chunk.  It comes either from the b buffer (the backward pass's reversed passes) or
+// from the gate input x: g = gate(x) per token and the 64-lane inclusive scan, the
+// same routine as the gate kernel, so both give the same bits.  The load is issued
+// with the chunk's other prefetch loads (decay_load) and finished when the chunk is
+// staged (decay_finish), so prefetching never waits for it.  Tokens past the unit's
+// end have g = 0: their b repeats the last token's (x path: the scan adds zeros; b
+// path: the load is clamped to the last entry).
+__device__ __forceinline__ float decay_load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0, int lane) {
+  const uint32_t t = t0 + (uint32_t)lane;
+  if (p.b) return buf_load4(hb.b, (t < hb.Tl ? t : hb.Tl - 1) * 4u);
+  return buf_load4(hb.x, t * 4u);  // past the end: out of range, reads 0 (replaced in decay_finish)
+}
+
+__device__ __forceinline__ float gate_of(int gate, float x) {
+  return gate == kGateBoundedSigmoid ? gate_bounded_sigmoid(x) : gate_neg_softplus(x);
+}
+
+__device__ __forceinline__ float decay_finish(const HeadBuffers& hb, const ChunkParams& p, float v, uint32_t t0,
+                                              int lane) {
+  if (p.b) return v;
+  const float g = t0 + (uint32_t)lane < hb.Tl ? gate_of(p.gate, v) : 0.0f;
+  return wave_inclusive_scan(g, lane);
+}
+
+// Shared memory for the workgroup-wide search below (x path).
+struct SegScanSmem {
+  int last_zero[16];
+  float gsum[16];
 };
 
 // First chunk of [c_begin, c_end) that a segment pre-pass has to run, and the
@@ -152,6 +186,50 @@ __device__ __forceinline__ int segment_first_live_chunk(const HeadBuffers& hb, i
   for (int off = 32; off >= 1; off >>= 1) {
     last_zero = max(last_zero, __shfl_xor(last_zero, off));
     s += __shfl_xor(s, off);
+  }
+  gsum = s;
+  return last_zero >= 0 ? last_zero : c_begin;
+}
+
+// The same from the gate input x, with every wave of the workgroup taking part: wave w
+// scans chunks c_begin + 8w .. +7, then + 8 NW, ... (all loads of a batch issued before
+// its first scan), the per-wave results meet in LDS.  gamma_c = lane 63 of the chunk's
+// scan, exactly the value the pass forms when it runs chunk c.  Contains a barrier:
+// every wave of the workgroup must call it.  Same results in every lane.
+template <int NW>
+__device__ __forceinline__ int segment_first_live_chunk_x(const HeadBuffers& hb, const ChunkParams& p, int c_begin,
+                                                          int c_end, float& gsum, SegScanSmem& sh) {
+  static_assert(NW <= 16, "one LDS slot per wave");
+  constexpr int kBatch = 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  int last_zero = -1;
+  float s = 0.0f;
+  for (int c0 = c_begin + wave * kBatch; c0 < c_end; c0 += NW * kBatch) {  // wave-uniform
+    float xv[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) xv[i] = decay_load(hb, p, (uint32_t)min(c0 + i, c_end - 1) * kChunk, lane);
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i;
+      if (c < c_end) {  // wave-uniform
+        const float gam = lane_value(decay_finish(hb, p, xv[i], (uint32_t)c * kChunk, lane), 63);
+        if (exp_e(gam) == 0.0f) last_zero = c;
+        s += gam;
+      }
+    }
+  }
+  if (lane == 0) {
+    sh.last_zero[wave] = last_zero;
+    sh.gsum[wave] = s;
+  }
+  __syncthreads();
+  last_zero = -1;
+  s = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    last_zero = max(last_zero, sh.last_zero[w]);
+    s += sh.gsum[w];
   }
   gsum = s;
   return last_zero >= 0 ? last_zero : c_begin;

@@ -57,6 +57,7 @@ template <typename T, int DK, int DVS>
 struct SegSmem {
   T kp[TokTile<T, DK>::SIZE];
   T vv[TokTile<T, DVS>::SIZE];
+  SegScanSmem scan;  // first chunk to run (x path)
 };
 
 // Per-thread registers holding one chunk of q, k, v (and b) on its way to LDS.
@@ -69,14 +70,14 @@ struct Staged {
   typename E::Vec8 q[LOAD_Q ? C::QU : 1];
   typename E::Vec8 k[C::QU];
   typename E::Vec8 v[C::VU];
-  float b;
+  float b;      // b of the lane's token, or its x until decay() (see decay_load)
+  uint32_t t0;  // first token of the chunk held
 
   // chunk starting at logical token t0 (rows in logical order; see row_offset)
-  __device__ __forceinline__ void load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0, int col0,
+  __device__ __forceinline__ void load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0_, int col0,
                                        int tid) {
-    const uint32_t len = hb.Tl;  // b is in logical order
-    const uint32_t tb = t0 + (tid & 63);
-    b = buf_load4(hb.b, (tb < len ? tb : len - 1) * 4u);
+    t0 = t0_;
+    b = decay_load(hb, p, t0, tid & 63);
 #pragma unroll
     for (int m = 0; m < C::QU; ++m) {
       const int u = tid + m * C::NT;
@@ -92,6 +93,11 @@ struct Staged {
       v[m] = E::load8(hb.v, row_offset(p, hb.T, t0 + row, (uint32_t)p.dv * (uint32_t)sizeof(T)) +
                                 (col0 + c8 * 8) * (uint32_t)sizeof(T));
     }
+  }
+
+  // b of the lane's token (lane = token of the chunk)
+  __device__ __forceinline__ float decay(const HeadBuffers& hb, const ChunkParams& p, int lane) const {
+    return decay_finish(hb, p, b, t0, lane);
   }
 };
 
@@ -153,12 +159,13 @@ __global__ void __launch_bounds__((Cfg<T, DK, DVS>::NT)) segment_state_kernel(Ch
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) S.s[nb][db] = floatx4{0.f, 0.f, 0.f, 0.f};
   float gsum;  // total log-decay of the segment
-  const int c_first = segment_first_live_chunk(hb, c_begin, c_end, gsum);
+  const int c_first = p.b ? segment_first_live_chunk(hb, c_begin, c_end, gsum)
+                          : segment_first_live_chunk_x<C::NW>(hb, p, c_begin, c_end, gsum, sm.scan);
 
   Staged<T, DK, DVS, false> st;
   if (c_first < c_end) st.load(hb, p, (uint32_t)c_first * kChunk, col0, tid);
   for (int c = c_first; c < c_end; ++c) {
-    const ChunkDecay cd(st.b);
+    const ChunkDecay cd(st.decay(hb, p, lane));
     const RowB<T, DK, DVS> brow(cd, tid);
     stage_state_operands<T, DK, DVS, false>(sm.kp, sm.vv, st, cd, brow, tid);
     // prefetch the next chunk (the last iteration re-reads its own chunk so that
@@ -255,7 +262,7 @@ __attribute__((amdgpu_waves_per_eu(out_waves_per_simd<T, DK, DVS, DIAG>()))) chu
     if constexpr (C::NB == 2) {
       if (p.state_out) store_chunk_state<T, DK, DVS>(S, p, bh, c, wcol, lane);
     }
-    const ChunkDecay cd(st.b);
+    const ChunkDecay cd(st.decay(hb, p, lane));
 
     // ---- (1) chunk c: registers -> LDS with the tile-relative decay factors
     {

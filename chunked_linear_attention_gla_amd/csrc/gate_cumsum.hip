@@ -8,36 +8,13 @@
 // chunk.  The chunk kernels read every decay factor they need from b: the
 // tile-start prefix r_u = b[16u - 1], the chunk total gamma = b[63] and
 // differences of entries.  A 64-lane wavefront scans one chunk at a time, lane j
-// owning token j, and forms the inclusive scan with DPP row shifts inside each
-// 16-lane row followed by the three row totals read across lanes.
+// owning token j (wave_inclusive_scan).  The forward kernels run the same scan on x
+// themselves; this kernel serves the backward pass, the delta rule and the stage
+// entry point gla_gate_cumsum.
 #include "gla_device.h"
 #include "gla_internal.h"
 
 namespace gla {
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_or_zero(float v) {
-  // row-local lane shift; lanes whose source falls outside the 16-lane row read 0
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, true));
-}
-
-// inclusive prefix sum over the 64 lanes of the wavefront
-__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
-  v += dpp_or_zero<0x111>(v);  // row_shr:1
-  v += dpp_or_zero<0x112>(v);  // row_shr:2
-  v += dpp_or_zero<0x114>(v);  // row_shr:4
-  v += dpp_or_zero<0x118>(v);  // row_shr:8
-  const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
-  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
-  const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
-  const int row = lane >> 4;
-  float off = 0.0f;
-  if (row >= 1) off = t0;
-  if (row >= 2) off = off + t1;
-  if (row >= 3) off = off + t2;
-  return v + off;
-}
 
 // Each wavefront takes kGateChunksPerWave consecutive chunks and issues all their
 // loads before the first scan, so one memory round trip covers several chunks.
@@ -84,36 +61,6 @@ __global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restric
     const float s = wave_inclusive_scan(g[i], lane);
     if (valid[i]) b[dst[i]] = s;
   }
-}
-
-// Packed sequences: wavefront `chunk` of unit bh = n * H + h covers tokens
-// [cu[n] + 64 c, ...) of head h, so chunks restart at every sequence start.  Offsets
-// are clamped into [0, T] and lengths to max_chunks chunks (inconsistent offsets give
-// wrong values, never an access outside x or b).
-template <int GATE>
-__global__ void __launch_bounds__(256) gate_cumsum_varlen_kernel(const float* __restrict__ x,
-                                                                 float* __restrict__ b,
-                                                                 const long long* __restrict__ cu,
-                                                                 int H, long long T, long long max_chunks,
-                                                                 long long total_chunks) {
-  const int lane = threadIdx.x & 63;
-  const long long chunk = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (chunk >= total_chunks) return;  // uniform across the wavefront
-  const long long bh = chunk / max_chunks;
-  const long long c = chunk - bh * max_chunks;
-  const long long n = bh / H, h = bh - n * H;
-  long long a = cu[n], e = cu[n + 1];
-  a = a < 0 ? 0 : (a > T ? T : a);
-  e = e < a ? a : (e > T ? T : e);
-  if (e - a > max_chunks * kChunk) e = a + max_chunks * kChunk;
-  const long long t = c * kChunk + lane;
-  if (c * kChunk >= e - a) return;  // uniform: the sequence has fewer chunks
-  const bool valid = t < e - a;
-  const long long row = h * T + a + t;
-  float g = 0.0f;
-  if (valid) g = (GATE == kGateBoundedSigmoid) ? gate_bounded_sigmoid(x[row]) : gate_neg_softplus(x[row]);
-  const float s = wave_inclusive_scan(g, lane);
-  if (valid) b[row] = s;
 }
 
 constexpr int kOrderThreads = 1024;
@@ -169,21 +116,6 @@ hipError_t launch_varlen_order(const long long* cu_seqlens, int N, long long T, 
   return hipGetLastError();
 }
 
-hipError_t launch_gate_cumsum_varlen(const float* x, float* b, const long long* cu_seqlens, int N, int H,
-                                     long long T, long long max_chunks, int gate, hipStream_t stream) {
-  const long long total = (long long)N * H * max_chunks;
-  if (total == 0) return hipSuccess;
-  const long long blocks = (total + 3) / 4;
-  if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
-  const dim3 grid((unsigned)blocks), block(256);
-  if (gate == kGateBoundedSigmoid)
-    hipLaunchKernelGGL((gate_cumsum_varlen_kernel<kGateBoundedSigmoid>), grid, block, 0, stream, x, b, cu_seqlens,
-                       H, T, max_chunks, total);
-  else
-    hipLaunchKernelGGL((gate_cumsum_varlen_kernel<kGateNegSoftplus>), grid, block, 0, stream, x, b, cu_seqlens, H,
-                       T, max_chunks, total);
-  return hipGetLastError();
-}
 
 hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long T, int gate,
                               bool reversed_shift, hipStream_t stream) {

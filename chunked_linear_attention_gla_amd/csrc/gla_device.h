@@ -65,6 +65,33 @@ __device__ __forceinline__ float gate_neg_softplus(float x) {
   return g < kSoftplusFloor ? kSoftplusFloor : g;
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_or_zero(float v) {
+  // row-local lane shift; lanes whose source falls outside the 16-lane row read 0
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                               0xF, 0xF, true));
+}
+
+// Inclusive prefix sum over the 64 lanes of the wavefront: DPP row shifts inside each
+// 16-lane row, then the three row totals read across lanes.  Every kernel that forms
+// the chunk-local cumulative log-decay uses this one routine, so they all get the
+// same bits.
+__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
+  v += dpp_or_zero<0x111>(v);  // row_shr:1
+  v += dpp_or_zero<0x112>(v);  // row_shr:2
+  v += dpp_or_zero<0x114>(v);  // row_shr:4
+  v += dpp_or_zero<0x118>(v);  // row_shr:8
+  const float t0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 15));
+  const float t1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  const float t2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 47));
+  const int row = lane >> 4;
+  float off = 0.0f;
+  if (row >= 1) off = t0;
+  if (row >= 2) off = off + t1;
+  if (row >= 3) off = off + t2;
+  return v + off;
+}
+
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }

@@ -12,7 +12,10 @@ struct ChunkParams {
   const void* q;          // [BH][T][dk]
   const void* k;          // [BH][T][dk]
   const void* v;          // [BH][T][dv]
-  const float* b;         // [BH][T] chunk-local cumulative log-decay
+  const float* b;         // [BH][T] chunk-local cumulative log-decay, or nullptr: then the
+                          //    kernels form it themselves from x (gate + 64-lane scan)
+  const float* x;         // [BH][T] gate pre-activation (read when b is nullptr)
+  int gate;               // GateKind of x
   const float* S0;        // [BH][dk][dv] or nullptr
   float* o;               // [BH][T][dv]
   float* ST;              // [BH][dk][dv]
@@ -66,15 +69,13 @@ __host__ __device__ inline unsigned row_offset(const ChunkParams& p, unsigned T,
 // that line up with the forward chunks.
 hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long T, int gate,
                               bool reversed_shift, hipStream_t stream);
-// Packed sequences: x and b are [H][T] (T = total tokens), sequence n of every head
-// covers rows [cu_seqlens[n], cu_seqlens[n+1]) and restarts its chunks there; at most
-// max_chunks chunks per sequence.
+// Packed sequences: q, k, v, x and o are [H][T][.] (T = total tokens), sequence n of
+// every head covers rows [cu_seqlens[n], cu_seqlens[n+1]) and restarts its chunks
+// there; at most max_chunks chunks per sequence.
 // order[0..N) = the sequences by chunk count, longest first (one workgroup, counting
 // sort; the order among equal counts is unspecified and changes no result).
 hipError_t launch_varlen_order(const long long* cu_seqlens, int N, long long T, long long max_chunks, int* order,
                                hipStream_t stream);
-hipError_t launch_gate_cumsum_varlen(const float* x, float* b, const long long* cu_seqlens, int N, int H,
-                                     long long T, long long max_chunks, int gate, hipStream_t stream);
 
 // dtype: 0 = bf16, 1 = fp32.  slice = dv / nslices.  diag: element-wise diagonal tiles.
 bool chunk_config_built(int dtype, int dk, int slice, bool diag);

@@ -95,13 +95,13 @@ struct WsStaged {
   // loads (streaming ones made it 1 % slower).
   static constexpr int kLoadAux = LOAD_Q ? 0 : kAuxStream;
   uint4 q[LOAD_Q ? QU : 1], k[QU], v[VU];
-  float b;
+  float b;      // b of the lane's token, or its x until decay() (see decay_load)
+  uint32_t t0;  // first token of the chunk held
 
   // chunk starting at logical token t0 (rows in logical order; see row_offset)
-  __device__ __forceinline__ void load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0, int col0, int st) {
-    const uint32_t len = hb.Tl;  // b is in logical order
-    const uint32_t tb = t0 + (st & 63);
-    b = buf_load4(hb.b, (tb < len ? tb : len - 1) * 4u);
+  __device__ __forceinline__ void load(const HeadBuffers& hb, const ChunkParams& p, uint32_t t0_, int col0, int st) {
+    t0 = t0_;
+    b = decay_load(hb, p, t0, st & 63);
 #pragma unroll
     for (int m = 0; m < QU; ++m) {
       const int u = st + m * 256;
@@ -116,6 +116,11 @@ struct WsStaged {
       const int row = u / (DVS / 8), c8 = u % (DVS / 8);
       v[m] = buf_load16<kLoadAux>(hb.v, row_offset(p, hb.T, t0 + row, (uint32_t)p.dv * 2u) + (col0 + c8 * 8) * 2u);
     }
+  }
+
+  // b of the lane's token (lane = token of the chunk)
+  __device__ __forceinline__ float decay(const HeadBuffers& hb, const ChunkParams& p, int lane) const {
+    return decay_finish(hb, p, b, t0, lane);
   }
 };
 
@@ -317,7 +322,8 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
     // Staging of one chunk from a register set: -> LDS slot ns (Qh, k e^{gamma-b},
     // v), Kh and b (single buffers), and the raw q, k of the ablation.
     const auto stage = [&](const WsStaged<DK, DVS>& stg, int ns) {
-      const ChunkDecay cd(stg.b);
+      const float bl = stg.decay(hb, p, lane);
+      const ChunkDecay cd(bl);
       float brow[W::QU];
 #pragma unroll
       for (int m = 0; m < W::QU; ++m) brow[m] = cd.at((st + m * 256) / (DK / 8));
@@ -344,7 +350,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         const int row = u / (DVS / 8), c8 = u % (DVS / 8);
         *reinterpret_cast<uint4*>(sm.vv[ns] + row * W::VLD + c8 * 8) = stg.v[m];
       }
-      if (sw == 0) sm.sb[lane] = stg.b;
+      if (sw == 0) sm.sb[lane] = bl;
     };
     // Chunk index of a load: every load is issued, the ones past the segment
     // re-read its last chunk (already in L2), so that the number of loads in
@@ -409,6 +415,7 @@ struct WsSegSmem {
   bf16 kp[2][64 * W::KLD];  // k_i e^{gamma - b_i}, [i][d]
   bf16 vv[2][64 * W::VLD];  // v[i][n]
   float gam[2];             // gamma of the chunk in each buffer set
+  SegScanSmem scan;         // first chunk to run (x path)
 };
 
 template <int DK, int DVS>
@@ -436,9 +443,11 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
   const int c_begin = (int)((long long)seg * span.nchunks / p.segments);
   const int c_end = (int)((long long)(seg + 1) * span.nchunks / p.segments);
   const HeadBuffers hb = head_buffers<bf16, DK>(p, span);
-  // every wave finds the first chunk to run (and the segment's log-decay) itself
+  // first chunk to run and the segment's log-decay: from b every wave finds them
+  // itself; from x the waves share the chunk scans (one barrier)
   float gsum;  // total log-decay of the segment
-  const int c_first = segment_first_live_chunk(hb, c_begin, c_end, gsum);
+  const int c_first = p.b ? segment_first_live_chunk(hb, c_begin, c_end, gsum)
+                          : segment_first_live_chunk_x<W::NCW + W::NSW>(hb, p, c_begin, c_end, gsum, sm.scan);
 
   if (compute) {
     StateAcc<bf16, DK, DVS> S;
@@ -459,7 +468,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
     if (slice == 0 && tid == 0) p.seg_decay[(long long)bh * p.segments + seg] = gsum;
   } else {
     const auto stage = [&](const WsStaged<DK, DVS, false>& stg, int ns) {
-      const ChunkDecay cd(stg.b);
+      const ChunkDecay cd(stg.decay(hb, p, lane));
       float brow[W::QU];
 #pragma unroll
       for (int m = 0; m < W::QU; ++m) brow[m] = cd.at((st + m * 256) / (DK / 8));

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define GLA_ABI_VERSION 1
+#define GLA_ABI_VERSION 2
 #define GLA_CHUNK 64          /* tokens per chunk */
 #define GLA_TILE 16           /* tokens per tile inside a chunk [LCT §3.2] */
 #define GLA_MAX_SEGMENTS 64   /* upper bound on gla_plan_t.segments */
@@ -127,9 +127,10 @@ gla_status_t gla_plan_check(int B, int H, long long T, int dk, int dv, gla_dtype
 gla_status_t gla_segment_workspace_size(int B, int H, long long T, int dk, int dv,
                                         const gla_plan_t* plan, size_t* bytes);
 
-/* Bytes of workspace gla_chunk_fwd needs: the chunk-local cumulative log-decay
- * b (B*H*T fp32) plus the segment workspace of `plan`.  plan == NULL means the
- * default plan of the current device (a HIP query).  Host only, enqueues nothing. */
+/* Bytes of workspace gla_chunk_fwd needs: the segment workspace of `plan`, and at
+ * least 256 (never 0, so a buffer allocated from the query is never NULL).
+ * plan == NULL means the default plan of the current device (a HIP query).  Host
+ * only, enqueues nothing. */
 gla_status_t gla_workspace_size(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
                                 gla_path_t path, const gla_plan_t* plan, size_t* bytes);
 
@@ -137,6 +138,8 @@ gla_status_t gla_workspace_size(int B, int H, long long T, int dk, int dv, gla_d
  *   b[t] = sum over the tokens i of t's 64-token chunk with i <= t of g(x[i]),
  * i.e. log Gamma restarted at every chunk boundary, computed by one 64-lane
  * wavefront scan per chunk.  x and b: [B][H][T] fp32 (b may not overlap x).
+ * The forward entry points form the same b inside their kernels (same scan, same
+ * bits); this call exposes the stage on its own.
  * Non-finite x follows the gate's limits: x = +inf gives g = -5 (bounded) or
  * 0 (softplus); x = -inf gives g = 0 (bounded).  The softplus gate is floored at
  * g = -128 (x = -inf included), where a = e^g is already exactly 0 in fp32, so a
@@ -151,28 +154,31 @@ gla_status_t gla_gate_cumsum(const float* x, float* b, int B, int H, long long T
  * (gla_segment_workspace_size bytes) receives Gamma_p and
  *   P_0 = H_0,  P_p = e^{Gamma_p} P_{p-1} + H_p,
  * the state at the end of segment p reached from a zero state at the start of
- * the head (gla_chunk_output adds the decayed S0).  Uses k, v and b (from
- * gla_gate_cumsum).  Does nothing when segments == 1. */
-gla_status_t gla_segment_states(const void* k, const void* v, const float* b,
+ * the head (gla_chunk_output adds the decayed S0).  Uses k, v and the gate input
+ * x [B][H][T] fp32 (gate and chunk-local cumulative sum formed in the kernel, as
+ * gla_gate_cumsum would).  Does nothing when segments == 1. */
+gla_status_t gla_segment_states(const void* k, const void* v, const float* x,
                                 int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
-                                const gla_plan_t* plan, void* seg_ws, size_t seg_ws_bytes,
-                                void* stream);
+                                gla_gate_t gate, const gla_plan_t* plan, void* seg_ws,
+                                size_t seg_ws_bytes, void* stream);
 
-/* Fused chunk output pass: for every chunk, the intra-chunk causal product
- * (q*Gamma)(k/Gamma)^T V, the inter-chunk term (q*Gamma) S, and the decayed
- * state update, o written once, S_T written by the last segment [LCT §3.1-§3.3].
- * b from gla_gate_cumsum; seg_ws from gla_segment_states with the same plan
- * (ignored when plan->segments == 1).  S0 may be NULL.  o and S_T must not
- * overlap any input; S_T must not overlap S0. */
-gla_status_t gla_chunk_output(const void* q, const void* k, const void* v, const float* b,
+/* Fused chunk output pass: for every chunk, the gate and chunk-local cumulative
+ * log-decay of x, the intra-chunk causal product (q*Gamma)(k/Gamma)^T V, the
+ * inter-chunk term (q*Gamma) S, and the decayed state update, o written once,
+ * S_T written by the last segment [LCT §3.1-§3.3].  seg_ws from
+ * gla_segment_states with the same plan and gate (ignored when
+ * plan->segments == 1).  S0 may be NULL.  o and S_T must not overlap any input;
+ * S_T must not overlap S0. */
+gla_status_t gla_chunk_output(const void* q, const void* k, const void* v, const float* x,
                               const float* S0, float* o, float* S_T,
                               int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
-                              gla_path_t path, const gla_plan_t* plan,
+                              gla_gate_t gate, gla_path_t path, const gla_plan_t* plan,
                               const void* seg_ws, size_t seg_ws_bytes, void* stream);
 
-/* The whole forward pass: gla_gate_cumsum, gla_segment_states (when the plan
- * has several segments) and gla_chunk_output, enqueued in that order on
- * `stream` with the default plan of the current device.
+/* The whole forward pass: gla_segment_states (when the plan has several
+ * segments) and gla_chunk_output, enqueued in that order on `stream` with the
+ * default plan of the current device; both form the gate and the chunk-local
+ * cumulative log-decay from x in their kernels.
  *   workspace == NULL: *workspace_bytes receives the required size; nothing is
  *                      enqueued (this queries the device for the plan).
  *   otherwise:         *workspace_bytes is the caller's workspace size; a
@@ -324,6 +330,19 @@ gla_status_t gla_chunk_fwd_pc(const void* q, const void* k, const void* v, const
                               int B, int H, long long T, int dk, int dv,
                               gla_dtype_t dtype, gla_gate_t gate, const gla_plan_t* plan,
                               void* workspace, size_t* workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Measurement helper (not part of the method).  A flat grid-stride stream with
+ * the forward pass's byte mix: for every 16-byte unit j < units, one 16-byte load
+ * from each of a, b, c at j and two 16-byte stores to out at 2j and 2j + 1 (48
+ * bytes read for 32 written, the 768 : 512 of q, k, v in bf16 and o in fp32 per
+ * token-head at d = 128).  Its rate is the device's practical streaming ceiling
+ * for that mix, read beside the output pass's achieved bandwidth.  a, b, c: 16 *
+ * units bytes each, out: 32 * units bytes, all device memory, 16-byte aligned, out
+ * overlapping none of the inputs; grid = workgroups of 256 threads (8192 was the
+ * fastest measured).  Enqueued on `stream`; errors as gla_chunk_fwd. */
+gla_status_t gla_bench_stream(const void* a, const void* b, const void* c, void* out,
+                              unsigned long long units, int grid, void* stream);
 
 #ifdef __cplusplus
 }

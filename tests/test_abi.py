@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.gla_abi_version() == 1
+    assert lib.gla_abi_version() == 2
     for code in range(11):
         s = lib.gla_status_string(code).decode()
         assert s.startswith("GLA_")
@@ -67,9 +67,9 @@ def test_workspace_query_with_explicit_plan(lib):
     rc, n = fwd(lib, B=2, H=3, T=1000, dk=128, dv=128, plan=(4, 2))
     assert rc == OK
     bh = 6
-    b_bytes = (bh * 1000 * 4 + 255) // 256 * 256
+    # the kernels form the cumulative log-decays from x: the workspace is the segment workspace
     seg = (bh * 3 * 128 * 128 * 4 + 255) // 256 * 256 + (bh * 4 * 4 + 255) // 256 * 256
-    assert n == b_bytes + seg
+    assert n == seg
     n2 = ctypes.c_size_t(0)
     assert lib.gla_workspace_size(2, 3, 1000, 128, 128, BF16, UNIFIED, P(4, 2), ctypes.byref(n2)) == OK
     assert n2.value == n
@@ -99,7 +99,7 @@ def test_size_limits(lib):
     past it is rejected before anything else."""
     t_max = 0xFFFF0000 // (128 * 4)  # 8388480 tokens, a multiple of 64
     rc, n = fwd(lib, B=1, H=1, T=t_max, dk=128, dv=128, plan=(1, 1))
-    assert rc == OK and n >= t_max * 4
+    assert rc == OK and n == 256  # one segment: no segment workspace
     assert fwd(lib, B=1, H=1, T=t_max + 64, dk=128, dv=128, plan=(1, 1))[0] == SHAPE
     assert fwd(lib, B=1, H=1, T=2 * t_max, dk=64, dv=64, plan=(1, 1))[0] == OK
     assert fwd(lib, B=1, H=1, T=2 * t_max + 64, dk=64, dv=64, plan=(1, 1))[0] == SHAPE
@@ -125,7 +125,7 @@ def test_ragged_and_empty_lengths_are_accepted(lib):
     for T in (0, 1, 63, 65, 200):
         rc, n = fwd(lib, T=T, plan=(1, 1))
         assert rc == OK
-        assert n == max((2 * T * 4 + 255) // 256 * 256, 256)
+        assert n == 256  # one segment: no segment workspace, and never a 0-byte answer
 
 
 def test_empty_sequence_workspace_query_is_never_zero(lib):
@@ -184,14 +184,22 @@ def test_gate_cumsum_validation(lib):
 
 
 def test_stage_entry_points_validate(lib):
-    # segment pre-pass: workspace too small
-    assert lib.gla_segment_states(0x1000, 0x100000, 0x200000, 1, 2, 256, 64, 64, BF16, P(2, 1), 0x10000000, 8,
-                                  None) == WORKSPACE
-    # output pass: S_T overlapping b
+    # segment pre-pass: workspace too small, unknown gate, x misaligned
+    assert lib.gla_segment_states(0x1000, 0x100000, 0x200000, 1, 2, 256, 64, 64, BF16, BOUNDED, P(2, 1),
+                                  0x10000000, 8, None) == WORKSPACE
+    assert lib.gla_segment_states(0x1000, 0x100000, 0x200000, 1, 2, 256, 64, 64, BF16, 7, P(2, 1),
+                                  0x10000000, 1 << 20, None) == ARG
+    assert lib.gla_segment_states(0x1000, 0x100000, 0x200001, 1, 2, 256, 64, 64, BF16, BOUNDED, P(2, 1),
+                                  0x10000000, 1 << 20, None) == ALIGN
+    # output pass: S_T overlapping x, no plan, x missing, unknown gate
     assert lib.gla_chunk_output(0x1000, 0x100000, 0x200000, 0x300000, None, 0x400000, 0x300000, 1, 2, 256, 64,
-                                64, BF16, UNIFIED, P(1, 1), None, 0, None) == ALIAS
+                                64, BF16, BOUNDED, UNIFIED, P(1, 1), None, 0, None) == ALIAS
     assert lib.gla_chunk_output(0x1000, 0x100000, 0x200000, 0x300000, None, 0x400000, 0x500000, 1, 2, 256, 64,
-                                64, BF16, UNIFIED, None, None, 0, None) == NULL
+                                64, BF16, BOUNDED, UNIFIED, None, None, 0, None) == NULL
+    assert lib.gla_chunk_output(0x1000, 0x100000, 0x200000, None, None, 0x400000, 0x500000, 1, 2, 256, 64,
+                                64, BF16, BOUNDED, UNIFIED, P(1, 1), None, 0, None) == NULL
+    assert lib.gla_chunk_output(0x1000, 0x100000, 0x200000, 0x300000, None, 0x400000, 0x500000, 1, 2, 256, 64,
+                                64, BF16, 5, UNIFIED, P(1, 1), None, 0, None) == ARG
     assert lib.gla_plan_check(1, 2, 256, 64, 64, BF16, UNIFIED, P(2, 4)) == OK
     assert lib.gla_plan_check(1, 2, 256, 64, 64, BF16, UNIFIED, P(2, 8)) == PLAN
 
@@ -300,8 +308,9 @@ def test_varlen_validation_before_any_device_call(lib):
     assert var(plan=(5, 1)) == PLAN       # 200 tokens are 4 chunks
     assert var(plan=(4, 1)) == OK         # explicit plan: size query without a device
     align = lambda b: (b + 255) // 256 * 256
-    # b, the local states and decays of 3 segments, the work order of the 3 sequences
-    assert n.value == align(2 * 500 * 4) + align(3 * 2 * 3 * 64 * 64 * 4) + align(3 * 2 * 4 * 4) + align(3 * 4)
+    # the local states and decays of 3 segments, the work order of the 3 sequences (the
+    # kernels form the cumulative log-decays from x: no b buffer)
+    assert n.value == align(3 * 2 * 3 * 64 * 64 * 4) + align(3 * 2 * 4 * 4) + align(3 * 4)
 
 
 def test_delta_validation_and_workspace_query(lib):

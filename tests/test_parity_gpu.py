@@ -80,9 +80,8 @@ def test_segment_states_are_prefix_states(qkv, segments, bursts):
         inp["x"][:, :, :12 * 64] = 8.0
     plan = gla.Plan(segments, 1)
     B, H, T = w.B, w.H, w.T
-    b = gla.gate_cumsum(inp["x"])
     ws = torch.zeros(gla.segment_workspace_size(B, H, T, w.dk, w.dv, plan), dtype=torch.uint8, device=device())
-    gla.segment_states(inp["k"], inp["v"], b, plan, ws)
+    gla.segment_states(inp["k"], inp["v"], inp["x"], plan, ws)
     torch.cuda.synchronize()
     nst = B * H * (segments - 1) * w.dk * w.dv
     states = ws[: nst * 4].view(torch.float32).reshape(B * H, segments - 1, w.dk, w.dv).cpu().double().numpy()
@@ -229,7 +228,8 @@ def test_chaining_weak_decay_state_handover(qkv):
     the second call from zero instead moves S_T by far more than the bound.  The
     single call runs a segmented plan (4 segments), the chained calls one segment each,
     so the two sum the state in different orders."""
-    w, inp = small(64 * 12, H=2, x_mean=-7.0, qkv=qkv, seed=31)
+    d = 128 if qkv == "bf16" else 64  # the fp32 kernels take slices of at most 64 columns
+    w, inp = small(64 * 12, H=2, x_mean=-7.0, qkv=qkv, seed=31, dk=d, dv=d)
     o, ST = gla.chunk_fwd(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], plan=gla.Plan(4, 1))
     T1 = 64 * 10
     sl = lambda t, a, b: t[:, :, a:b].contiguous()
@@ -244,7 +244,7 @@ def test_chaining_weak_decay_state_handover(qkv):
     assert rel(torch.cat([o1, o2], 2).cpu().double().numpy(), o.cpu().double().numpy()) <= tol_o
     # and the single call against the fp64 oracle
     o_ref, S_ref = oracle_heads(inp)
-    assert rel(ST.reshape(2, 128, 128).cpu().double().numpy(), S_ref) <= TOL[qkv]
+    assert rel(ST.reshape(2, d, d).cpu().double().numpy(), S_ref) <= TOL[qkv]
 
 
 def test_empty_sequence_through_the_c_abi_with_queried_workspace():
