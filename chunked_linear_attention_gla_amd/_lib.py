@@ -75,6 +75,7 @@ _SIGS = {
     "gla_plan_check_delta": (_i, [_i, _i, _ll, _i, _i, _i, _pplan]),
     "gla_chunk_fwd_delta": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _pplan, _vp,
                                  _psz, _vp]),
+    "gla_chunk_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i, _vp]),
     "gla_bench_stream": (_i, [_vp, _vp, _vp, _vp, ctypes.c_ulonglong, _i, _vp]),
     "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
                            _i, _i, _i, _vp, _psz, _vp]),

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "gla.h"
 #include "gla_internal.h"
@@ -831,3 +832,58 @@ gla_status_t gla_chunk_fwd(const void* q, const void* k, const void* v, const fl
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- no-allocation forward
+//
+// The forward's only scratch memory is the segment workspace (the pre-pass's local
+// and prefix states and segment log-decays).  gla_chunk_fwd_noalloc takes it from this
+// file-scope device array instead of a caller's buffer.  Each GPU holds its own copy
+// of the array (at its own address) until the process ends.  In host code the array's
+// name is only a host-side stand-in: the device address is looked up once per device
+// (hipGetSymbolAddress, with that device current) and only that address is passed on.
+// Nothing in it needs to start at zero: every byte a call reads is written earlier in
+// the same call.  Calls that overlap on one GPU share the array and race.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mutex;
+void* scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on first use there).
+gla_status_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GLA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return GLA_ERR_HIP;
+    scratch_ptr[dev] = ptr;
+  }
+  *out = scratch_ptr[dev];
+  return GLA_OK;
+}
+
+}  // namespace
+
+extern "C" gla_status_t gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* x,
+                                              const float* S0, float* o, float* S_T, int B, int H, long long T,
+                                              int dk, int dv, gla_dtype_t dtype, gla_gate_t gate, gla_path_t path,
+                                              void* stream) {
+  gla_status_t st = check_sizes(B, H, T, dk, dv);
+  if (st != GLA_OK) return st;
+  if (!valid_dtype(dtype)) return GLA_ERR_DTYPE;
+  if (!valid_gate(gate) || !valid_path(path)) return GLA_ERR_ARG;
+  gla_plan_t pl;
+  st = gla_plan_default(B, H, T, dk, dv, dtype, path, &pl);
+  if (st != GLA_OK) return st;
+  // the workspace this plan needs must fit the array
+  if (fwd_workspace_bytes((long long)B * H, dk, dv, pl.segments) > kScratchBytes) return GLA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != GLA_OK) return st;
+  size_t n = kScratchBytes;
+  return gla_chunk_fwd_plan(q, k, v, x, S0, o, S_T, B, H, T, dk, dv, dtype, gate, path, &pl, ws, &n, stream);
+}

@@ -191,6 +191,20 @@ gla_status_t gla_chunk_fwd(const void* q, const void* k, const void* v, const fl
                            gla_dtype_t dtype, gla_gate_t gate, gla_path_t path,
                            void* workspace, size_t* workspace_bytes, void* stream);
 
+/* gla_chunk_fwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The segment workspace comes from a 32 MiB device array inside
+ * the library, one per GPU, held until the process ends; the call allocates nothing.  Same default plan, kernels and results
+ * as gla_chunk_fwd.  A plan whose workspace exceeds the array returns
+ * GLA_ERR_WORKSPACE before anything is enqueued (the default plans on a 256-CU
+ * device need at most ~31 MB at dk = dv = 128).  Calls on one GPU share the array:
+ * calls that can overlap on one GPU (different streams without ordering) race and
+ * must be serialised by the caller.  Other errors as gla_chunk_fwd. */
+gla_status_t gla_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const float* x,
+                                   const float* S0, float* o, float* S_T,
+                                   int B, int H, long long T, int dk, int dv,
+                                   gla_dtype_t dtype, gla_gate_t gate, gla_path_t path, void* stream);
+
 /* gla_chunk_fwd with an explicit plan (NULL = default plan). */
 gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, const float* x,
                                 const float* S0, float* o, float* S_T,
