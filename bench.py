@@ -100,6 +100,9 @@ def parse():
     ap.add_argument("--delta-only", action="store_true", help="time only the gated delta rule")
     ap.add_argument("--serving-only", action="store_true", help="time only decode and packed sequences")
     ap.add_argument("--per-channel-only", action="store_true", help="time only the per-channel forward")
+    ap.add_argument("--ramp", type=int, default=0, metavar="N",
+                    help="only time the first N steps from process start, one by one (no settle, no warm-up), "
+                         "and print the output kernel's time per group of 10 launches: the clock ramp")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration) and exit")
     return ap.parse_args()
@@ -379,7 +382,7 @@ def per_channel_bytes_per_token_head(dk: int, dv: int, es: int) -> int:
     return (2 * dk + dv) * es + 4 * dk + 4 * dv
 
 
-def per_channel_result(gla, gin, torch, steps, warmup, cpu_seconds):
+def per_channel_result(gla, gin, torch, steps, warmup, cpu_seconds, settle_s=0.3):
     """The per-channel-decay forward (gla_chunk_fwd_pc: segment pre-pass + output pass)
     on its own 64K workload, timed per call."""
     w = gin.WORKLOADS["bf16_64k_pc"]
@@ -392,7 +395,7 @@ def per_channel_result(gla, gin, torch, steps, warmup, cpu_seconds):
     ws = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     fn = lambda: gla.chunk_fwd_pc(inp["q"], inp["k"], inp["v"], inp["x"], inp["S0"], gate=w.gate, plan=plan,
                                   o=o, S_T=ST, workspace=ws)
-    ms_host, ms_ev = time_calls(torch, fn, steps, warmup)
+    ms_host, ms_ev = time_calls(torch, fn, steps, warmup, settle_s)
     es = inp["q"].element_size()
     del inp, o, ws
     nbytes = B * H * T * per_channel_bytes_per_token_head(dk, dv, es) + B * H * dk * dv * 4
@@ -412,7 +415,7 @@ def per_channel_result(gla, gin, torch, steps, warmup, cpu_seconds):
     return res
 
 
-def decode_result(gla, gin, torch, steps, warmup, cpu_seconds, sets: int = 6):
+def decode_result(gla, gin, torch, steps, warmup, cpu_seconds, sets: int = 6, settle_s=0.3):
     """One decode step for every (sequence, head) of a serving batch (gla_decode_step),
     the state updated in place.  The timed steps rotate over `sets` independent batches
     (inputs and states), 128 MiB of state each, so that the 768 MiB they span exceed the
@@ -431,8 +434,8 @@ def decode_result(gla, gin, torch, steps, warmup, cpu_seconds, sets: int = 6):
         step(batches[it[0] % sets])
         it[0] += 1
     n_steps = steps * 10 // sets * sets
-    ms_host, ms_ev = time_calls(torch, rotating, n_steps, warmup)
-    _, ms_res = time_calls(torch, lambda: step(inp), steps * 10, warmup, settle_s=0.05)
+    ms_host, ms_ev = time_calls(torch, rotating, n_steps, warmup, settle_s)
+    _, ms_res = time_calls(torch, lambda: step(inp), steps * 10, warmup, min(settle_s, 0.05))
     es = inp["q"].element_size()
     bh = w.B * w.H
     per_head = 2 * w.dk * w.dv * 4 + (2 * w.dk + w.dv) * es + 4 + 4 * w.dv
@@ -465,7 +468,7 @@ def decode_result(gla, gin, torch, steps, warmup, cpu_seconds, sets: int = 6):
     return res
 
 
-def varlen_result(gla, gin, torch, steps, warmup, cpu_seconds):
+def varlen_result(gla, gin, torch, steps, warmup, cpu_seconds, settle_s=0.3):
     """Forward over a packed batch of sequences of mixed lengths (gla_chunk_fwd_varlen)."""
     import numpy as np
     w = gin.WORKLOADS["bf16_varlen_256k"]
@@ -478,7 +481,7 @@ def varlen_result(gla, gin, torch, steps, warmup, cpu_seconds):
     ws = torch.empty(1 << 28, dtype=torch.uint8, device=dev)
     fn = lambda: gla.chunk_fwd_varlen(inp["q"], inp["k"], inp["v"], inp["x"], inp["cu_seqlens"], max(lengths),
                                       inp["S0"], gate=w.gate, o=o, S_T=ST, workspace=ws)
-    ms_host, ms_ev = time_calls(torch, fn, steps, warmup)
+    ms_host, ms_ev = time_calls(torch, fn, steps, warmup, settle_s)
     es = inp["q"].element_size()
     nbytes = H * T * algorithmic_bytes_per_token_head(w.dk, w.dv, es) + N * H * w.dk * w.dv * 4
     achieved = nbytes / (ms_ev / 1e3) / 1e9
@@ -505,7 +508,7 @@ def varlen_result(gla, gin, torch, steps, warmup, cpu_seconds):
     return res
 
 
-def delta_result(gla, gin, torch, steps, warmup, cpu_seconds):
+def delta_result(gla, gin, torch, steps, warmup, cpu_seconds, settle_s=0.3):
     """The chunked gated delta rule (gla_chunk_fwd_delta: gate + cumsum, the parallel
     per-chunk solve, the serial output pass) on its 64K workload."""
     import numpy as np
@@ -520,7 +523,7 @@ def delta_result(gla, gin, torch, steps, warmup, cpu_seconds):
                      dtype=torch.uint8, device=dev)
     fn = lambda: gla.chunk_fwd_delta(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["S0"], gate=w.gate,
                                      plan=plan, o=o, S_T=ST, workspace=ws)
-    ms_host, ms_ev = time_calls(torch, fn, steps, warmup)
+    ms_host, ms_ev = time_calls(torch, fn, steps, warmup, settle_s)
     es = inp["q"].element_size()
     # q, k, v, x, beta in; o out (the per-chunk W and U are implementation traffic)
     per_th = (2 * dk + dv) * es + 8 + 4 * dv
@@ -592,22 +595,38 @@ def main():
     torch.cuda.set_device(torch.device("cuda:0"))
     plan = gla.Plan(*(int(s) for s in args.plan.split(","))) if args.plan else None
     if args.delta_only:
-        print(json.dumps({"delta": delta_result(gla, gin, torch, args.steps, args.warmup, 0.0)}), flush=True)
+        print(json.dumps({"delta": delta_result(gla, gin, torch, args.steps, args.warmup, 0.0, args.settle_s)}),
+              flush=True)
         return
     if args.serving_only:
-        print(json.dumps({"decode": decode_result(gla, gin, torch, args.steps, args.warmup, 0.0),
-                          "varlen": varlen_result(gla, gin, torch, args.steps, args.warmup, 0.0)}), flush=True)
+        print(json.dumps({"decode": decode_result(gla, gin, torch, args.steps, args.warmup, 0.0,
+                                                  settle_s=args.settle_s),
+                          "varlen": varlen_result(gla, gin, torch, args.steps, args.warmup, 0.0, args.settle_s)}),
+              flush=True)
         return
     if args.per_channel_only:
-        print(json.dumps({"per_channel": per_channel_result(gla, gin, torch, args.steps, args.warmup, 0.0)}),
-              flush=True)
+        print(json.dumps({"per_channel": per_channel_result(gla, gin, torch, args.steps, args.warmup, 0.0,
+                                                            args.settle_s)}), flush=True)
         return
     if args.backward_only:
         print(json.dumps({"workload": w.name, "backward": backward_result(gla, gin, torch, w, path, args.steps,
-                                                                         args.warmup)}), flush=True)
+                                                                         args.warmup, args.settle_s)}), flush=True)
         return
     timer = StepTimer(gla, gin, torch, w, path, plan)
     plan = timer.plan
+    if args.ramp:
+        # the output kernel launch by launch from the first step of the process on
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.ramp)]
+        for e in evs:
+            timer.step(e)
+        torch.cuda.synchronize()
+        out_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+        groups = [{"launches": f"{i}-{min(i + 9, len(out_us) - 1)}",
+                   "gpu_ms_before": round(sum(e_[0].elapsed_time(e_[2]) for e_ in evs[:i]), 1),
+                   "output_kernel_us_mean": round(sum(out_us[i:i + 10]) / len(out_us[i:i + 10]), 1)}
+                  for i in range(0, len(out_us), 10)]
+        print(json.dumps({"workload": w.name, "ramp": groups}), flush=True)
+        return
     ms_step, (ms_seg, ms_out) = timer.run(args.steps, args.warmup, args.settle_s)
     B, H, T, dk, dv = timer.shape
     es = timer.q.element_size()
@@ -694,14 +713,17 @@ def main():
             result["backward"]["cpu_baseline"] = cpu_baseline_backward(w, args.cpu_seconds / 2)
     if not args.no_per_channel and not args.plan and w.name == gin.HEADLINE:
         result["per_channel"] = per_channel_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5),
-                                                   0.0 if args.no_cpu_baseline else args.cpu_seconds / 2)
+                                                   0.0 if args.no_cpu_baseline else args.cpu_seconds / 2,
+                                                   args.settle_s)
     if not args.no_serving and not args.plan and w.name == gin.HEADLINE:
         cs = 0.0 if args.no_cpu_baseline else args.cpu_seconds / 4
-        result["decode"] = decode_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5), cs)
-        result["varlen"] = varlen_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5), cs)
+        result["decode"] = decode_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5), cs,
+                                         settle_s=args.settle_s)
+        result["varlen"] = varlen_result(gla, gin, torch, min(args.steps, 20), min(args.warmup, 5), cs,
+                                         args.settle_s)
     if not args.no_delta and not args.plan and w.name == gin.HEADLINE:
         result["delta"] = delta_result(gla, gin, torch, min(args.steps, 10), min(args.warmup, 3),
-                                       0.0 if args.no_cpu_baseline else args.cpu_seconds / 4)
+                                       0.0 if args.no_cpu_baseline else args.cpu_seconds / 4, args.settle_s)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)
