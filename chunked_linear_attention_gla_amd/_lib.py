@@ -15,7 +15,8 @@ from typing import NamedTuple, Optional, Tuple
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libgla.so")
+# GLA_LIB_PATH selects another build of the library (the tests' host sanitizer run)
+LIB_PATH = os.environ.get("GLA_LIB_PATH") or os.path.join(_PKG, "libgla.so")
 
 GLA_BF16, GLA_F32 = 0, 1
 GATES = {"bounded": 0, "bounded_sigmoid": 0, "neg_softplus": 1, "softplus": 1}

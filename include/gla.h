@@ -62,11 +62,21 @@ extern "C" {
 #endif
 
 #define GLA_ABI_VERSION 2
+
+/* The enums below are int-sized.  C callers may pass any int value (a wrong one is
+ * rejected with an error code); compiled as C++ they get int as their fixed
+ * underlying type, so every int value is a valid value of the type and checking an
+ * out-of-range argument is well defined. */
+#ifdef __cplusplus
+#define GLA_ENUM_INT : int
+#else
+#define GLA_ENUM_INT
+#endif
 #define GLA_CHUNK 64          /* tokens per chunk */
 #define GLA_TILE 16           /* tokens per tile inside a chunk [LCT §3.2] */
 #define GLA_MAX_SEGMENTS 64   /* upper bound on gla_plan_t.segments */
 
-typedef enum {
+typedef enum GLA_ENUM_INT {
   GLA_OK = 0,
   GLA_ERR_NULL = 1,        /* a required pointer is NULL */
   GLA_ERR_SHAPE = 2,       /* B, H, T, dk or dv out of the supported range */
@@ -80,17 +90,17 @@ typedef enum {
   GLA_ERR_UNSUPPORTED = 10 /* valid enums, but this combination is not built */
 } gla_status_t;
 
-typedef enum { GLA_BF16 = 0, GLA_F32 = 1 } gla_dtype_t;   /* storage of q, k, v */
+typedef enum GLA_ENUM_INT { GLA_BF16 = 0, GLA_F32 = 1 } gla_dtype_t;   /* storage of q, k, v */
 
 /* Log-decay g(x) [LCT §3.2]. */
-typedef enum {
+typedef enum GLA_ENUM_INT {
   GLA_GATE_BOUNDED_SIGMOID = 0, /* g = -5 * sigmoid(x), range (-5, 0) (the product) */
   GLA_GATE_NEG_SOFTPLUS = 1     /* g = -softplus(-x) = log sigmoid(x), range (-inf, 0);
                                    evaluated as max(g, -128): e^-128 is 0 in fp32 */
 } gla_gate_t;
 
 /* How the causal tiles of a chunk are computed. */
-typedef enum {
+typedef enum GLA_ENUM_INT {
   GLA_PATH_UNIFIED = 0,     /* every causal 16x16 tile on MFMA: q*Gamma, k/Gamma (product) */
   GLA_PATH_DIAG_BRANCH = 1  /* off-diagonal tiles on MFMA, diagonal tiles element-wise (ablation) */
 } gla_path_t;

@@ -45,7 +45,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gla_oracle.c")
-LIB_PATH = os.path.join(_HERE, "libgla_oracle.so")
+# GLA_ORACLE_LIB points the tests at another build of the same source (the host
+# sanitizer run builds one with clang's address and undefined-behaviour checks)
+LIB_PATH = os.environ.get("GLA_ORACLE_LIB") or os.path.join(_HERE, "libgla_oracle.so")
 
 GATE_BOUNDED_SIGMOID = 0  # g = -5 * sigmoid(x)          [LCT §3.2] improved form
 GATE_NEG_SOFTPLUS = 1     # g = -softplus(-x) = log sigmoid(x)  conventional, unbounded
