@@ -646,7 +646,8 @@ gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, co
   const size_t u_bytes = align_up((size_t)BH * T * dv * es);
   const size_t h_bytes = pl.segments > 1 ? align_up((size_t)BH * (pl.segments - 1) * dk * dv * 4) : 0;
   const size_t f_bytes = pl.segments > 1 ? align_up((size_t)BH * (pl.segments - 1) * dk * dk * 4) : 0;
-  const size_t need = std::max(b_bytes + w_bytes + u_bytes + h_bytes + f_bytes, kAlign);
+  const size_t r_bytes = pl.segments > 1 ? align_up((size_t)BH * n_chunks(T) * 4) : 0;
+  const size_t need = std::max(b_bytes + w_bytes + u_bytes + h_bytes + f_bytes + r_bytes, kAlign);
   if (!workspace) {
     *workspace_bytes = need;
     return GLA_OK;
@@ -681,6 +682,7 @@ gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, co
   p.U = w + b_bytes + w_bytes;
   p.seg_state = pl.segments > 1 ? (float*)(w + b_bytes + w_bytes + u_bytes) : nullptr;
   p.seg_phi = pl.segments > 1 ? (float*)(w + b_bytes + w_bytes + u_bytes + h_bytes) : nullptr;
+  p.reset = pl.segments > 1 ? (int*)(w + b_bytes + w_bytes + u_bytes + h_bytes + f_bytes) : nullptr;
   p.T = T;
   p.dk = dk;
   p.dv = dv;

@@ -137,8 +137,9 @@ struct PrepSmem {
     float mf[64][C::MLD];         // M = diag(beta) L (strictly lower)
     T tb[64 * C::TLD];            // Tinv in the operand dtype
   } u2;
-  float sb[64];
+  float sb[64];                   // b; at the end, the waves' reset votes
   float sbeta[64];
+  float lk[64];                   // log2 of max_d |k_t[d] e^{gamma - b_t}|, per row
 };
 
 template <typename T, int DK, int DV>
@@ -176,6 +177,8 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   }
   __syncthreads();
   const auto ref = [&](int u) { return u == 0 ? 0.0f : sm.sb[16 * u - 1]; };
+  const int last = (int)(((long long)Tn - 1 - t0) < 63 ? ((long long)Tn - 1 - t0) : 63);
+  const float gam = sm.sb[last];  // the chunk's total log-decay
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
@@ -183,6 +186,14 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     const bool sw = frag_swap<T>(row);
     E::store8_scaled_sw(sm.u1.l.kq + row * C::QLD + c8 * 8, kv[m], exp_e(br - r), sw);
     E::store8_scaled_sw(sm.u1.l.kh + row * C::QLD + c8 * 8, kv[m], exp_e(r - br), sw);
+    // reset test, key side: log2 max_d |k_row[d]| + (gamma - b_row) log2 e (the threads of a
+    // row are DK / 8 consecutive lanes)
+    float mx = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(E::get(kv[m], e)));
+#pragma unroll
+    for (int off = DK / 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (c8 == 0) sm.lk[row] = __builtin_amdgcn_logf(mx) + (gam - br) * kLog2e;
   }
   __syncthreads();
 
@@ -263,7 +274,8 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   // ---- W = Tinv (beta e^b K), Ut = Tinv (beta V): wave w owns a quarter of the columns
   T* Wg = static_cast<T*>(p.W) + bh * p.T * DK;
   T* Ug = static_cast<T*>(p.U) + bh * p.T * DV;
-  const auto product = [&](const T* tile, int ncol, T* dst, int ld) {
+  float wmax[4] = {0.f, 0.f, 0.f, 0.f};  // per jb: this lane's max |W| of row 16 jb + r16 (reset test below)
+  const auto product = [&](const T* tile, int ncol, T* dst, int ld, bool is_w) {
     for (int cb = wave * (ncol / 4); cb < (wave + 1) * (ncol / 4); cb += 16) {
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb) {
@@ -276,11 +288,36 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
         // acc[e] = X[t0 + 16 jb + r16][cb + 4 g + e]
         const long long t = (long long)t0 + jb * 16 + r16;
         if (t < p.T) store_row4<T>(dst + t * ld + cb + 4 * g, acc);
+        if (is_w) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) wmax[jb] = fmaxf(wmax[jb], fabsf(acc[e]));
+        }
       }
     }
   };
-  product(sm.u1.r.kb, DK, Wg, DK);
-  product(sm.u1.r.vb, DV, Ug, DV);
+  // Reset test of the chunk (only when the plan has segments).  The transition
+  // P = e^gamma I - (k e^{gamma-b})^T W has |P[d][e]| <= e^gamma + sum_t |kt_t|max |w_t|max,
+  // so |P H| <= 2^13 2^-127 max|H| once every term is below 2^-127 (64 rows, 128 columns):
+  // the state after this chunk then does not depend on the state before it, to 2^-114
+  // relative.  The terms are compared in log2 (no product underflows on the way);
+  // NaN terms fail the comparison, so they never mark a reset.
+  product(sm.u1.r.kb, DK, Wg, DK, true);
+  product(sm.u1.r.vb, DV, Ug, DV, false);
+  if (p.reset) {
+    bool ok = gam * kLog2e < -127.0f;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      float mx = wmax[jb];
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      ok = ok && (sm.lk[jb * 16 + r16] + __builtin_amdgcn_logf(mx) < -127.0f);
+    }
+    // sb is not read after the staging above: it takes the waves' votes
+    if (lane == 0) sm.sb[wave] = __ballot(!ok) == 0ull ? 1.0f : 0.0f;
+    __syncthreads();
+    if (tid == 0)
+      p.reset[bh * p.nchunks + c] = (sm.sb[0] != 0.0f && sm.sb[1] != 0.0f && sm.sb[2] != 0.0f && sm.sb[3] != 0.0f);
+  }
 }
 
 // ============================================================================
@@ -458,9 +495,25 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
 #pragma unroll
     for (int e = 0; e < 4; ++e) S[db][e] = (PHI && db * 16 + 4 * g + e == wcol + r16) ? 1.0f : 0.0f;
 
+  // The local state (from zero at the segment start) does not depend, to 2^-114 relative,
+  // on anything before the segment's last chunk whose transition marks a reset: start
+  // there from zero.  (The transition half keeps every chunk: it stops by itself once its
+  // product is exactly zero.)
+  int c_first = c_begin;
+  if (!PHI && p.reset) {
+    int lastr = -1;
+    for (int c0 = c_begin; c0 < c_end; c0 += 64) {  // wave-uniform
+      const int cc = c0 + lane;
+      if (cc < c_end && p.reset[(long long)bh * p.nchunks + cc] != 0) lastr = cc;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) lastr = max(lastr, __shfl_xor(lastr, off));
+    if (lastr >= 0) c_first = lastr;
+  }
+
   DoStaged<T, DK, NCOL, false, !PHI> st;
-  if (c_begin < c_end) st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_begin * kChunk, wcol, tid);
-  for (int c = c_begin; c < c_end; ++c) {
+  if (c_first < c_end) st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_first * kChunk, wcol, tid);
+  for (int c = c_first; c < c_end; ++c) {
     const ChunkDecay cd(st.b);
     floatx4 ut[4];
 #pragma unroll
@@ -487,11 +540,11 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
       for (int db = 0; db < C::DB; ++db)
 #pragma unroll
         for (int e = 0; e < 4; ++e) nz |= S[db][e] != 0.0f;
-      if (lane == 0) sm.nonzero[(c - c_begin) & 1][wave] = __ballot(nz) != 0ull;
+      if (lane == 0) sm.nonzero[(c - c_first) & 1][wave] = __ballot(nz) != 0ull;
     }
     __syncthreads();
     if constexpr (PHI) {
-      const int par = (c - c_begin) & 1;
+      const int par = (c - c_first) & 1;
       int any = 0;
 #pragma unroll
       for (int w = 0; w < C::NW; ++w) any |= sm.nonzero[par][w];

@@ -128,6 +128,10 @@ struct DeltaParams {
   void* U;                // [BH][T][dv] operand dtype: Tinv diag(beta) V per chunk
   float* seg_state;       // [BH][segments-1][dk][dv] local final state of each segment
   float* seg_phi;         // [BH][segments-1][dk][dk] state transition of each segment
+  int* reset;             // [BH][nchunks] 1 where the chunk's transition e^gamma I - (k e^{gamma-b})^T W
+                          //    scales any incoming state by less than 2^-114 (written by the
+                          //    per-chunk pass; the local-state half starts at the last such
+                          //    chunk of its segment), or nullptr
   long long T;
   int dk, dv;
   int BH;

@@ -274,9 +274,14 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
  *   product of the chunk transitions e^gamma I - (k e^{gamma-b})^T W, dk x dk).
  * Built: bf16 with dk, dv in {64, 128} and slices of 32, 64 or 128 columns; fp32
  * with dk = dv = 64 and slices of 32 or 64.  Others: GLA_ERR_UNSUPPORTED or
- * GLA_ERR_PLAN.  The workspace holds b, the per-chunk W, U (operand dtype) and the
- * segment maps; workspace == NULL returns its size.  Errors and validation as
- * gla_chunk_fwd. */
+ * GLA_ERR_PLAN.  The workspace holds b, the per-chunk W, U (operand dtype), the
+ * segment maps and one reset flag per chunk; workspace == NULL returns its size.
+ * Errors and validation as gla_chunk_fwd.
+ * Segment pre-pass: a chunk whose transition scales any incoming state by less than
+ * 2^-114 (a bound from the largest |k e^{gamma-b}| and |W| of each token, taken in
+ * log2) is a reset point; a segment's local state is run from a zero state at its
+ * last reset chunk instead of its first chunk.  Results then differ from running the
+ * whole segment by less than 2^-114 of the state's scale. */
 gla_status_t gla_plan_default_delta(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,
                                     gla_plan_t* plan);
 gla_status_t gla_plan_check_delta(int B, int H, long long T, int dk, int dv, gla_dtype_t dtype,

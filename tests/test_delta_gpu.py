@@ -164,3 +164,21 @@ def test_largest_head_extent():
         assert rel(got, o_ref[0, (c - a) * 64:]) <= TOL["bf16"], (a, b)
         if b == last:
             assert rel(ST[0, 0].cpu().double().numpy(), S_ref[0]) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("qkv,beta_one", [("bf16", False), ("bf16", True), ("f32", False)])
+def test_reset_chunks_inside_segments(qkv, beta_one):
+    """Weak decay (the state carries across whole segments) with a few strong-decay
+    chunks (x = +8: chunk log-decay about -320) planted inside the segments.  Their
+    transition e^gamma I - (k e^{gamma-b})^T W is below 2^-114 in size, so the local-state
+    half of the segment pre-pass starts at the last such chunk of each segment instead
+    of the segment start: segment 0 at chunk 7, segment 1 at chunk 19 (two planted in a
+    row), segment 2 at none (no planted chunk: all of its chunks run).  The whole call
+    must still match the fp64 oracle, with beta ~ U(0,1) and with beta = 1."""
+    d = 128 if qkv == "bf16" else 64
+    w, inp = make(64 * 40 + 11, H=2, dk=d, dv=d, qkv=qkv, x_mean=-6.0, seed=23)
+    for ch in (7, 18, 19, 33):
+        inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
+    if beta_one:
+        inp["beta"].fill_(1.0)
+    check(w, inp, plan=gla.Plan(4, 1))
