@@ -375,7 +375,7 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
     pa.segments = pc.segments = 1;
     pa.dv_split = pc.dv_split = 1;
   }
-  // the dq and dk passes store their state before / after every chunk for dx; their
+  // the dq and dk passes store their state before / after every other chunk for dx; their
   // kernels do that for value slices of at least 32 columns
   if (T > 0 && (dk_ / pa.dv_split < 32)) return GLA_ERR_UNSUPPORTED;
   const long long BH = (long long)B * H;
@@ -383,7 +383,8 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
   const size_t es = elem_size(dtype);
   const size_t tok = align_up((size_t)BH * (size_t)T * 4);
   const size_t tokr = align_up((size_t)BH * (size_t)nc * GLA_CHUNK * 4);
-  const size_t chs = align_up((size_t)BH * (size_t)nc * (size_t)dk_ * (size_t)dv_ * es);
+  // one stored state per pair of chunks (see store_chunk_state)
+  const size_t chs = align_up((size_t)BH * (size_t)((nc + 1) / 2) * (size_t)dk_ * (size_t)dv_ * es);
   const size_t stt = align_up((size_t)BH * (size_t)dk_ * (size_t)dv_ * 4);
   const size_t segb = std::max(seg_bytes(BH, dv_, dk_, pa.segments), seg_bytes(BH, dk_, dv_, pc.segments));
   // b | b' (reversed, padded to whole chunks) | per-chunk states of the dq and dk passes |
@@ -454,11 +455,11 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
       p.grid = (int)(BH * pl.dv_split * pl.segments);
       return gla::launch_chunk_output(p, dt, diag, s);
     };
-    // dq = forward(dO, v, k) from S0^T; stores S^T before every chunk
+    // dq = forward(dO, v, k) from S0^T; stores S^T before every even chunk
     const gla::ChunkParams pdq = make(dO, v, k, b, S0, 1, 0, dq, STt, dv_, dk_, pa);
     if (e == hipSuccess) e = prepass(pdq, pa);
     if (e == hipSuccess) e = output(pdq, pa, Sfw);
-    // dk = reversed forward(v, dO, q) from dS_T^T (stores D^T after every chunk) and
+    // dk = reversed forward(v, dO, q) from dS_T^T (stores D^T after every odd chunk) and
     // dv = reversed forward(k, q, dO) from dS_T (final state D_0) carry the same state
     // gradient, transposed, under the same decays: with equal segment counts the dk
     // pass starts its segments from the dv pass's segment states, read transposed

@@ -21,8 +21,10 @@
 // once, so nothing cancels: summing per-token inflows and outflows over the whole
 // sequence (dL/dg_t = sum_{t'>=t} (q.dq - k.dk)_t') is equivalent in exact arithmetic
 // but turns the rounding of dq and dk into errors that grow with T.
-// S_{c-1} (transposed) is stored per chunk by the dq pass, D_{c+1 start} (transposed)
-// by the dk pass; dH_c = a_{first token of c+1} D (dS_T after the last chunk).
+// S_{c-1} (transposed) is stored by the dq pass before every even chunk and D_{c+1 start}
+// (transposed) by the dk pass after every odd chunk and the last one; the dx kernel
+// rebuilds the other state of each chunk from its pair's neighbour chunk.
+// dH_c = a_{first token of c+1} D (dS_T after the last chunk).
 // dx_t = g'(x_t) dL/dg_t with g' the slope of the gate of §3.2.
 #include "chunk_common.h"
 
@@ -39,6 +41,9 @@ struct DxCfg {
   static constexpr int LDV = DV + PAD;          // row stride of v, dO in LDS
   static constexpr int DB = DV / 16;            // state row blocks (state rows run over dv)
   static constexpr int KS = DV / 32;
+  // bf16: two workgroups per CU (LDS allows it); register budget held to match.  fp32
+  // tiles fill the LDS of one CU.
+  static constexpr int kWavesPerSimd = sizeof(T) == 2 ? 2 : 1;
 };
 
 template <typename T, int DK, int DV>
@@ -49,6 +54,7 @@ struct DxSmem {
   T v[64 * X::LDV];
   T g[64 * X::LDV];                             // dO
   float b[64];
+  float bn[64];                                 // the neighbouring chunk's cumulative log-decay
   float rpart[X::NW][64];
   float upart[X::NW][64];
   float zpart[X::NW];
@@ -93,24 +99,85 @@ struct RowStage {
   }
 };
 
-// A stored chunk state (fragment order, see store_chunk_state) of one 32-column group.
-template <typename T, int DB>
-__device__ __forceinline__ floatx4 load_state4(const T* base, int nb, int db, int lane) {
-  const T* src = base + ((nb * DB + db) * 64 + lane) * 4;
-  floatx4 r;
-  if constexpr (sizeof(T) == 2) {
-    typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
-    const bf16x4v w = *reinterpret_cast<const bf16x4v*>(src);
+// Four elements of a stored chunk state (fragment order, see store_chunk_state) as they
+// are stored: bf16 states stay packed (two to a register) until they are used.
+template <typename T> struct StateRaw;
+template <> struct StateRaw<bf16> {
+  using V = bf16x4;
+  __device__ static __forceinline__ V load(const bf16* p) { return *reinterpret_cast<const bf16x4*>(p); }
+  __device__ static __forceinline__ floatx4 f32(V v) {
+    floatx4 r;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) r[e] = static_cast<float>(w[e]);
-  } else {
-    r = *reinterpret_cast<const floatx4*>(src);
+    for (int e = 0; e < 4; ++e) r[e] = static_cast<float>(v[e]);
+    return r;
   }
-  return r;
+  __device__ static __forceinline__ V raw(const floatx4& a) {
+    V r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = static_cast<bf16>(a[e]);
+    return r;
+  }
+  // operand fragment of two accumulator blocks (rows 16 apart), as Elem::from_acc
+  __device__ static __forceinline__ Elem<bf16>::Frag frag(V lo, V hi) {
+    Elem<bf16>::Frag f;
+    f.v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return f;
+  }
+};
+template <> struct StateRaw<float> {
+  using V = floatx4;
+  __device__ static __forceinline__ V load(const float* p) { return *reinterpret_cast<const floatx4*>(p); }
+  __device__ static __forceinline__ floatx4 f32(V v) { return v; }
+  __device__ static __forceinline__ V raw(const floatx4& a) { return a; }
+  __device__ static __forceinline__ Elem<float>::Frag frag(V lo, V hi) { return Elem<float>::from_acc(lo, hi); }
+};
+
+// Operand fragment whose contraction index is the token (kappa order), for column
+// c0 + r16 of a row-major [64][LD] tile.
+template <typename T, int LD>
+__device__ __forceinline__ typename Elem<T>::Frag tok_frag(const T* tile, int k0, int c0, int lane) {
+  if constexpr (sizeof(T) == 2) {
+    return TokTile<T, 16, LD>::load(tile, k0, c0, lane);
+  } else {
+    const int g = lane >> 4, r = lane & 15;
+    typename Elem<T>::Frag f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.lo[e] = tile[(k0 + 4 * g + e) * LD + c0 + r];
+      f.hi[e] = tile[(k0 + 16 + 4 * g + e) * LD + c0 + r];
+    }
+    return f;
+  }
 }
 
+// The same fragment with element e (token k0 + 16 (e / 4) + 4 g + e % 4) multiplied by fac[e].
+template <typename T>
+__device__ __forceinline__ typename Elem<T>::Frag scale_frag(typename Elem<T>::Frag f, const float (&fac)[8]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f.v[e] = static_cast<bf16>(static_cast<float>(f.v[e]) * fac[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      f.lo[e] *= fac[e];
+      f.hi[e] *= fac[4 + e];
+    }
+  }
+  return f;
+}
+
+// One workgroup per chunk c of one head; wave w owns 32 state columns (over dk).  The
+// forward pass stored S^T before each even chunk and the reversed pass D^T after each odd
+// chunk (and after the last chunk), one state per pair of chunks (2m, 2m + 1).  The state
+// missing for chunk c is one chunk step from the stored one of its pair:
+//   odd c:  S^T before c = e^{gamma'} S^T + sum_{s in c-1} e^{gamma' - b'_s} v_s k_s^T,
+//   even c: D^T after c  = sum_{j in c+1} e^{b'_j - b'_0} dO_j q_j^T + e^{gamma' - b'_0} a' D^T,
+// with b', gamma' those of the neighbour chunk c -/+ 1 and a' the decay of the token after
+// chunk c + 1.  The neighbour's two operand tiles pass through the LDS tiles of the same
+// names before the chunk's own; the workgroups of one pair run on one XCD (consecutive
+// work items, see xcd_linear_index), so their shared reads meet in its L2.
 template <typename T, int DK, int DV, int GATE>
-__global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) grad_dx_kernel(
+__global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(DxCfg<T, DK, DV>::kWavesPerSimd))) grad_dx_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, const T* __restrict__ dO,
     const float* __restrict__ b, const float* __restrict__ x, const T* __restrict__ Sfw, const T* __restrict__ Sbw,
     float* __restrict__ dx, long long Tlen, int nchunks) {
@@ -120,46 +187,160 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) grad_dx_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const long long bh = blockIdx.x / nchunks;
-  const int c = (int)(blockIdx.x - bh * nchunks);
-  const uint32_t t0 = (uint32_t)c * kChunk;
+  const int item = xcd_linear_index((int)blockIdx.x, (int)gridDim.x);
+  const long long bh = item / nchunks;
+  const int c = (int)(item - bh * nchunks);
+  const bool odd = (c & 1) != 0;
+  const bool nbr = odd || c + 1 < nchunks;  // uniform: a state to rebuild from the neighbour
+  const int cn = odd ? c - 1 : c + 1;       // the neighbour chunk
+  const uint32_t t0 = (uint32_t)c * kChunk, tn0 = (uint32_t)cn * kChunk;
   const uint32_t Tn = (uint32_t)Tlen;
+  const float* bh_b = b + bh * Tlen;
 
-  // ---- operands of the chunk (raw) and its cumulative log-decay: every load of the
-  //      chunk, including this wave's 32-column slices of S^T (before the chunk) and D^T
-  //      (after it), is issued before the first LDS store
+  // ---- every load first: the chunk's b and operands, the neighbour's b and two operand
+  //      tiles (k, v of c - 1 or q, dO of c + 1), this wave's slices of the pair's states
   float bval = 0.0f;
   if (tid < 64) {
     const long long tt = (long long)t0 + tid;
-    bval = b[bh * Tlen + (tt < Tlen ? tt : Tlen - 1)];
+    bval = bh_b[tt < Tlen ? tt : Tlen - 1];
+  } else if (tid < 128 && nbr) {
+    const long long tt = (long long)tn0 + (tid - 64);
+    bval = bh_b[tt < Tlen ? tt : Tlen - 1];
   }
-  RowStage<T, DK, X::LDK, X::NT> sq, sk;
-  RowStage<T, DV, X::LDV, X::NT> svv, sg;
-  sq.load(make_rsrc(q + bh * Tlen * DK, Tn * DK * (uint32_t)sizeof(T)), t0, tid);
-  sk.load(make_rsrc(k + bh * Tlen * DK, Tn * DK * (uint32_t)sizeof(T)), t0, tid);
-  svv.load(make_rsrc(v + bh * Tlen * DV, Tn * DV * (uint32_t)sizeof(T)), t0, tid);
-  sg.load(make_rsrc(dO + bh * Tlen * DV, Tn * DV * (uint32_t)sizeof(T)), t0, tid);
-  const long long sidx = (((bh * nchunks + c) * (DK / 32) + w) * 2) * (long long)X::DB * 256;
-  floatx4 sv[2][X::DB], ev[2][X::DB];
+  const rsrc_t rq = make_rsrc(q + bh * Tlen * DK, Tn * DK * (uint32_t)sizeof(T));
+  const rsrc_t rk = make_rsrc(k + bh * Tlen * DK, Tn * DK * (uint32_t)sizeof(T));
+  const rsrc_t rv = make_rsrc(v + bh * Tlen * DV, Tn * DV * (uint32_t)sizeof(T));
+  const rsrc_t rg = make_rsrc(dO + bh * Tlen * DV, Tn * DV * (uint32_t)sizeof(T));
+  // The two own tiles that wait for the neighbour's (k, v for odd c; q, dO for even c)
+  // are loaded with everything else where registers allow (bf16 at dk = 128), else
+  // after the rebuild.
+  constexpr bool kEarly = sizeof(T) == 2 && DK == 128;
+  RowStage<T, DK, X::LDK, X::NT> sq, sk, nA;
+  RowStage<T, DV, X::LDV, X::NT> svv, sg, nB;
+  if (nbr) {
+    nA.load(odd ? rk : rq, tn0, tid);
+    nB.load(odd ? rv : rg, tn0, tid);
+    if (odd) {
+      sq.load(rq, t0, tid);
+      sg.load(rg, t0, tid);
+      if constexpr (kEarly) {
+        sk.load(rk, t0, tid);
+        svv.load(rv, t0, tid);
+      }
+    } else {
+      sk.load(rk, t0, tid);
+      svv.load(rv, t0, tid);
+      if constexpr (kEarly) {
+        sq.load(rq, t0, tid);
+        sg.load(rg, t0, tid);
+      }
+    }
+  } else {
+    sq.load(rq, t0, tid);
+    sk.load(rk, t0, tid);
+    svv.load(rv, t0, tid);
+    sg.load(rg, t0, tid);
+  }
+  const long long sidx = (((bh * ((nchunks + 1) / 2) + (c >> 1)) * (DK / 32) + w) * 2) * (long long)X::DB * 256;
+  using RS = StateRaw<T>;
+  typename RS::V sv[2][X::DB], ev[2][X::DB];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int db = 0; db < X::DB; ++db) {
-      sv[nb][db] = load_state4<T, X::DB>(Sfw + sidx, nb, db, lane);
-      ev[nb][db] = load_state4<T, X::DB>(Sbw + sidx, nb, db, lane);
+      sv[nb][db] = RS::load(Sfw + sidx + ((nb * X::DB + db) * 64 + lane) * 4);
+      ev[nb][db] = RS::load(Sbw + sidx + ((nb * X::DB + db) * 64 + lane) * 4);
     }
-  sq.store(sm.q, tid);
-  sk.store(sm.k, tid);
-  svv.store(sm.v, tid);
-  sg.store(sm.g, tid);
   if (tid < 64) sm.b[tid] = bval;
+  else if (tid < 128) sm.bn[tid - 64] = bval;
+
+  // st <- f0 st + sum over the neighbour's tokens s of fexp(s) ta_s tb_s^T: ta the tile
+  // over dv (v or dO), tb the tile over dk (k or q), in fp32 and back to the stored form
+  const auto rebuild = [&](typename RS::V (&st)[2][X::DB], const T* ta, const T* tb, float f0, auto&& fexp) {
+    floatx4 acc[2][X::DB];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int db = 0; db < X::DB; ++db) acc[nb][db] = RS::f32(st[nb][db]) * f0;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      float fac[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fac[e] = fexp(ks * 32 + 16 * (e >> 2) + 4 * g + (e & 3));
+      typename E::Frag fb[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) fb[nb] = tok_frag<T, X::LDK>(tb, ks * 32, 32 * w + 16 * nb, lane);
+#pragma unroll
+      for (int db = 0; db < X::DB; ++db) {
+        const typename E::Frag fa = scale_frag<T>(tok_frag<T, X::LDV>(ta, ks * 32, db * 16, lane), fac);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) E::mfma(acc[nb][db], fa, fb[nb]);
+      }
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int db = 0; db < X::DB; ++db) st[nb][db] = RS::raw(acc[nb][db]);
+  };
+
+  if (nbr) {
+    // the neighbour's tiles go where the chunk's own tiles of those names go later
+    if (odd) {
+      nA.store(sm.k, tid);
+      nB.store(sm.v, tid);
+      sq.store(sm.q, tid);
+      sg.store(sm.g, tid);
+    } else {
+      nA.store(sm.q, tid);
+      nB.store(sm.g, tid);
+      sk.store(sm.k, tid);
+      svv.store(sm.v, tid);
+    }
+    __syncthreads();
+    if (odd) {
+      // S^T before c from S^T before c - 1 (a whole chunk)
+      const float gn = sm.bn[63];
+      rebuild(sv, sm.v, sm.k, exp_e(gn), [&](int s) { return exp_e(gn - sm.bn[s]); });
+    } else {
+      // D^T after c from D^T after c + 1 (rows of c + 1 past the end are zeros)
+      const long long rem = Tlen - 1 - (long long)tn0;
+      const float gn = sm.bn[rem < 63 ? (int)rem : 63], bn0 = sm.bn[0];
+      const long long tnext = (long long)tn0 + kChunk;
+      const float an = tnext < Tlen ? exp_e(bh_b[tnext]) : 1.0f;
+      rebuild(ev, sm.g, sm.q, exp_e(gn - bn0) * an, [&](int j) { return exp_e(sm.bn[j] - bn0); });
+    }
+    if constexpr (!kEarly) {
+      if (odd) {
+        sk.load(rk, t0, tid);
+        svv.load(rv, t0, tid);
+      } else {
+        sq.load(rq, t0, tid);
+        sg.load(rg, t0, tid);
+      }
+    }
+    __syncthreads();
+    if (odd) {
+      sk.store(sm.k, tid);
+      svv.store(sm.v, tid);
+    } else {
+      sq.store(sm.q, tid);
+      sg.store(sm.g, tid);
+    }
+  } else {
+    sq.store(sm.q, tid);
+    sk.store(sm.k, tid);
+    svv.store(sm.v, tid);
+    sg.store(sm.g, tid);
+  }
   float z = 0.0f;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int db = 0; db < X::DB; ++db)
+    for (int db = 0; db < X::DB; ++db) {
+      const floatx4 a4 = RS::f32(sv[nb][db]), b4 = RS::f32(ev[nb][db]);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z += sv[nb][db][e] * ev[nb][db][e];
+      for (int e = 0; e < 4; ++e) z += a4[e] * b4[e];
+    }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
   if (lane == 0) sm.zpart[w] = z;
@@ -172,8 +353,8 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) grad_dx_kernel(
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int ks = 0; ks < X::KS; ++ks) {
-        Sf[nb][ks] = E::from_acc(sv[nb][2 * ks], sv[nb][2 * ks + 1]);
-        Ef[nb][ks] = E::from_acc(ev[nb][2 * ks], ev[nb][2 * ks + 1]);
+        Sf[nb][ks] = RS::frag(sv[nb][2 * ks], sv[nb][2 * ks + 1]);
+        Ef[nb][ks] = RS::frag(ev[nb][2 * ks], ev[nb][2 * ks + 1]);
       }
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
@@ -254,8 +435,7 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) grad_dx_kernel(
     const int last = (int)((Tlen - 1 - (long long)t0) < 63 ? (Tlen - 1 - (long long)t0) : 63);
     const float gam = sm.b[last];
     // dH_c = a D with a the decay of the first token of the next chunk (1 after the last chunk)
-    const long long tn = (long long)t0 + kChunk;
-    const float a = tn < Tlen ? exp_e(b[bh * Tlen + tn]) : 1.0f;
+    const float a = (nbr && !odd) ? exp_e(sm.bn[0]) : ((long long)t0 + kChunk < Tlen ? exp_e(bh_b[t0 + kChunk]) : 1.0f);
     float rs = 0.0f, us = 0.0f, zs = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < X::NW; ++ww) {

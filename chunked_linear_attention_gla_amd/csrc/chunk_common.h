@@ -332,9 +332,12 @@ __device__ __forceinline__ void load_initial_state(StateAcc<T, DK, DVS>& S, cons
       for (int e = 0; e < 4; ++e) S.s[nb][db][e] = f0 * s0[nb][db][e] + pre[nb][db][e];
 }
 
-// Per-chunk state storage (for the backward pass): the state before each chunk,
-// in the operand dtype, in MFMA-fragment order
-//     [bh][chunk][g32 = value column / 32][nb][db][lane][e]
+// Per-chunk state storage (for the backward pass), one state per pair of chunks: the
+// forward pass stores the state before every even chunk, the reversed pass the state
+// after every odd chunk and after the last one (logical chunk index cc, slot cc / 2);
+// the other state of each pair is one chunk step away from the stored one, and the dx
+// kernel takes that step itself.  In the operand dtype, in MFMA-fragment order
+//     [bh][slot][g32 = value column / 32][nb][db][lane][e]
 // so that each lane writes (and a kernel with the same fragment layout later reads)
 // its own 4 consecutive elements: S[16 db + 4 g + e][32 g32 + 16 nb + r16].
 template <typename T, int DK, int DVS>
@@ -343,8 +346,11 @@ __device__ __forceinline__ void store_chunk_state(const StateAcc<T, DK, DVS>& S,
   using C = Cfg<T, DK, DVS>;
   static_assert(C::NB == 2, "chunk states are stored in groups of 32 value columns");
   const int cc = p.reverse ? p.nchunks - 1 - c : c;
+  const bool keep = p.reverse ? ((cc & 1) != 0 || cc == p.nchunks - 1) : (cc & 1) == 0;
+  if (!keep) return;  // wave-uniform
+  const long long slots = (p.nchunks + 1) / 2;
   T* base = static_cast<T*>(p.state_out) +
-            ((((long long)bh * p.nchunks + cc) * (p.dv / 32) + wcol / 32) * 2) * (long long)C::DB * 256;
+            ((((long long)bh * slots + (cc >> 1)) * (p.dv / 32) + wcol / 32) * 2) * (long long)C::DB * 256;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll

@@ -38,9 +38,10 @@ struct ChunkParams {
   int s0_transposed;      // 1: S0 is stored [dv][dk] (the transpose of the state)
   int seg_transposed;     // 1: the segment states are those of the transposed pass
                           //    ([dv][dk] per segment; same decays)
-  void* state_out;        // optional: the state before every chunk, in the operand dtype,
-                          //    in MFMA-fragment order (see store_chunk_state); a reversed
-                          //    pass stores logical chunk c at chunk nchunks-1-c
+  void* state_out;        // optional: one state per pair of chunks, in the operand dtype,
+                          //    in MFMA-fragment order (see store_chunk_state): the state
+                          //    before each even chunk; a reversed pass stores the state after
+                          //    each odd (logical) chunk and after the last one
   const long long* cu_seqlens;  // packed sequences: N+1 token offsets (device memory) into the
                           //    rows of every head; nullptr for the dense [BH][T] layout.  With
                           //    it, q, k, v, o, b are [H][T][.] (T = total tokens), the work

@@ -90,8 +90,11 @@ def test_bf16_backward_diag_branch(gate, x_mean):
     check(w, inp, dO, dST, gate=gate, path="diag_branch")
 
 
-def test_fp32_backward():
-    w, inp, dO, dST = make(64 * 4 + 3, H=2, dk=64, dv=64, qkv="f32")
+@pytest.mark.parametrize("T,dk,dv", [(64 * 4 + 3, 64, 64), (64 * 5 + 17, 128, 128), (64 * 2, 128, 64), (64 * 3, 64, 128)])
+def test_fp32_backward(T, dk, dv):
+    """fp32 operands: the dx kernel stages one chunk of a pair at a time (odd and even
+    chunk counts, whole and ragged last chunks)."""
+    w, inp, dO, dST = make(T, H=2, dk=dk, dv=dv, qkv="f32")
     check(w, inp, dO, dST)
 
 
