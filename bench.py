@@ -103,6 +103,9 @@ def parse():
     ap.add_argument("--ramp", type=int, default=0, metavar="N",
                     help="only time the first N steps from process start, one by one (no settle, no warm-up), "
                          "and print the output kernel's time per group of 10 launches: the clock ramp")
+    ap.add_argument("--ramp-stream", type=int, default=0, metavar="N",
+                    help="only time the first N launches of the flat stream of the step's byte mix "
+                         "(gla_bench_stream) from process start, per group of 10 launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (for counter calibration) and exit")
     return ap.parse_args()
@@ -594,6 +597,24 @@ def main():
     path = args.path or "unified"
     torch.cuda.set_device(torch.device("cuda:0"))
     plan = gla.Plan(*(int(s) for s in args.plan.split(","))) if args.plan else None
+    if args.ramp_stream:
+        # the flat stream of the headline step's bytes, launch by launch from the first one
+        B, H, T, dk, dv = w.B, w.H, w.T, w.dk, w.dv
+        nbytes = B * H * T * dk * 2  # one bf16 operand tensor; o (fp32) is twice that
+        a = torch.ones(nbytes, dtype=torch.uint8, device="cuda:0")
+        b_, c_ = torch.ones_like(a), torch.ones_like(a)
+        out = torch.empty(2 * nbytes, dtype=torch.uint8, device="cuda:0")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.ramp_stream)]
+        for e in evs:
+            e[0].record()
+            gla.bench_stream(a, b_, c_, out)
+            e[1].record()
+        torch.cuda.synchronize()
+        us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+        groups = [{"launches": f"{i}-{min(i + 9, len(us) - 1)}", "gpu_ms_before": round(sum(us[:i]) / 1e3, 1),
+                   "stream_us_mean": round(sum(us[i:i + 10]) / len(us[i:i + 10]), 1)} for i in range(0, len(us), 10)]
+        print(json.dumps({"workload": w.name, "bytes_per_launch": 5 * nbytes, "ramp_stream": groups}), flush=True)
+        return
     if args.delta_only:
         print(json.dumps({"delta": delta_result(gla, gin, torch, args.steps, args.warmup, 0.0, args.settle_s)}),
               flush=True)

@@ -92,8 +92,9 @@ def test_bf16_backward_diag_branch(gate, x_mean):
 
 @pytest.mark.parametrize("T,dk,dv", [(64 * 4 + 3, 64, 64), (64 * 5 + 17, 128, 128), (64 * 2, 128, 64), (64 * 3, 64, 128)])
 def test_fp32_backward(T, dk, dv):
-    """fp32 operands: the dx kernel stages one chunk of a pair at a time (odd and even
-    chunk counts, whole and ragged last chunks)."""
+    """fp32 operands at every head size: odd chunks rebuild the state before them and
+    even chunks the state gradient after them (odd and even chunk counts, whole and
+    ragged last chunks)."""
     w, inp, dO, dST = make(T, H=2, dk=dk, dv=dv, qkv="f32")
     check(w, inp, dO, dST)
 
