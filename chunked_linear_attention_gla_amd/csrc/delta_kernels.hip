@@ -347,7 +347,7 @@ struct DoSmem {
   T qh[64 * C::QLD];
   T kh[64 * C::QLD];
   T wn[64 * C::QLD];              // -W
-  T kp[TokTile<T, DK>::SIZE];     // k e^{gamma - b}, token-major
+  T kp[2][TokTile<T, DK>::SIZE];  // k e^{gamma - b}, token-major, by chunk parity
   T uu[UTile<T, DVS>::SIZE];      // U of the slice, token-major
   T a[64 * C::TLD];
 };
@@ -642,7 +642,8 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       E::store8_scaled_sw(sm.qh + row * C::QLD + c8 * 8, st.q[m], exp_e(br - r), sw);
       E::store8_scaled_sw(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(r - br), sw);
     }
-    stage_w_kp<T, DK, DVS, true, true>(sm.wn, sm.kp, st, cd, tid);
+    T* const kp = sm.kp[(c - c_begin) & 1];
+    stage_w_kp<T, DK, DVS, true, true>(sm.wn, kp, st, cd, tid);
     // ---- (2) prefetch chunk c + 1 (the last iteration re-reads its own chunk)
     st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, wcol, tid);
     __syncthreads();
@@ -692,12 +693,15 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
 #pragma unroll
         for (int ks = 0; ks <= jb / 2; ++ks)
           E::mfma(O[jb], Uf[ks], E::load_frag(sm.a + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
-      delta_state_update<T, DK, DVS>(S, Uf, sm.kp, exp_e(cd.gam), lane);
+      delta_state_update<T, DK, DVS>(S, Uf, kp, exp_e(cd.gam), lane);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
         buf_store16(ro, dl_row(t0 + jb * 16 + r16, Tn, (uint32_t)p.dv * 4u) + (wcol + 4 * g) * 4u, O[jb]);
     }
-    __syncthreads();
+    // No barrier here: the next chunk's staging writes Qh, Kh and -W, last read in (3)
+    // and (4) before this chunk's second barrier, and the other k e^{gamma - b} buffer;
+    // A is rewritten only after its first barrier, and U is read by the wave that
+    // wrote it.
   }
   if (seg == p.segments - 1) {
 #pragma unroll
