@@ -331,9 +331,12 @@ struct DoCfg {
   static constexpr int QLD = DK + PAD;
   static constexpr int TLD = 64 + 4;   // A row stride: its 8-byte stores and fragment reads are conflict-free
   static constexpr int QU = 8 * DK / NT;
+  static constexpr int UU = 8 * DVS / NT;      // 16-byte (bf16) Ut pieces per thread
+  static constexpr int ULD = DVS + PAD;        // row stride of the loaded Ut tile
   static constexpr int DB = DK / 16;
   static constexpr int KS = DK / 32;
   static_assert(QU >= 1 && QU * NT == 8 * DK, "staging must divide evenly");
+  static_assert(UU >= 1 && UU * NT == 8 * DVS, "Ut staging must divide evenly");
 };
 
 // U is written with 8-byte stores in the accumulator layout, which conflict less at a
@@ -349,6 +352,7 @@ struct DoSmem {
   T wn[64 * C::QLD];              // -W
   T kp[2][TokTile<T, DK>::SIZE];  // k e^{gamma - b}, token-major, by chunk parity
   T uu[UTile<T, DVS>::SIZE];      // U of the slice, token-major
+  T ui[64 * C::ULD];              // Ut of the slice as loaded, row-major
   T a[64 * C::TLD];
 };
 
@@ -358,22 +362,24 @@ struct DsSmem {
   T wn[64 * C::QLD];
   T kp[TokTile<T, DK>::SIZE];
   T uu[UTile<T, DVS>::SIZE];
+  T ui[64 * C::ULD];              // Ut of the slice as loaded, row-major
   int nonzero[2][C::NW];  // transition half: per wave, whether its columns are nonzero, by chunk parity
 };
 
-// One chunk of (q,) k, W, Ut and b on its way to LDS / registers.  Ut lands directly
-// in the accumulator layout: ut[jb][e] = Ut[t0 + 16 jb + r16][wcol + 4 g + e].
+// One chunk of (q,) k, W, Ut and b on its way to LDS.  Every operand is loaded in
+// row-contiguous 16-byte pieces; Ut goes to a row-major tile from which each wave
+// reads its columns in the accumulator layout (read_ut).
 template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_U>
 struct DoStaged {
   using E = Elem<T>;
   using C = DoCfg<T, DK, DVS>;
-  typename E::Vec8 q[LOAD_Q ? C::QU : 1], k[C::QU], w[C::QU];
-  floatx4 ut[4];
+  typename E::Vec8 q[LOAD_Q ? C::QU : 1], k[C::QU], w[C::QU], u[LOAD_U ? C::UU : 1];
   float b;
 
+  // chunk at token t0 of the slice starting at value column col0
   __device__ __forceinline__ void load(const rsrc_t& rq, const rsrc_t& rk, const rsrc_t& rw, const rsrc_t& ru,
-                                       const rsrc_t& rb, uint32_t Tn, int dv, uint32_t t0, int wcol, int tid) {
-    const int lane = tid & 63, r16 = lane & 15, g = lane >> 4;
+                                       const rsrc_t& rb, uint32_t Tn, int dv, uint32_t t0, int col0, int tid) {
+    const int lane = tid & 63;
     const uint32_t tb = t0 + lane;
     b = buf_load4(rb, (tb < Tn ? tb : Tn - 1) * 4u);
 #pragma unroll
@@ -384,27 +390,46 @@ struct DoStaged {
       k[m] = E::load8(rk, off);
       w[m] = E::load8(rw, off);
     }
+    if constexpr (LOAD_U) {
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      if (!LOAD_U) {
-        ut[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
-        continue;
+      for (int m = 0; m < C::UU; ++m) {
+        const int v = tid + m * C::NT, row = v / (DVS / 8), c8 = v % (DVS / 8);
+        u[m] = E::load8(ru, dl_row(t0 + row, Tn, (uint32_t)dv * (uint32_t)sizeof(T)) +
+                                (col0 + c8 * 8) * (uint32_t)sizeof(T));
       }
-      const uint32_t off = dl_row(t0 + jb * 16 + r16, Tn, (uint32_t)dv * (uint32_t)sizeof(T)) +
-                           (wcol + 4 * g) * (uint32_t)sizeof(T);
-      if constexpr (sizeof(T) == 2) {
-        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(ru, (int)off, 0, 0);
-        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(ru, (int)(off + 4u), 0, 0);
-        ut[jb] = floatx4{bf16_bits_to_f32(lo & 0xFFFFu), bf16_bits_to_f32(lo >> 16), bf16_bits_to_f32(hi & 0xFFFFu),
-                         bf16_bits_to_f32(hi >> 16)};
-      } else {
-        const uint4 raw = buf_load16(ru, off);
-        ut[jb] = floatx4{__builtin_bit_cast(float, raw.x), __builtin_bit_cast(float, raw.y),
-                         __builtin_bit_cast(float, raw.z), __builtin_bit_cast(float, raw.w)};
+    }
+  }
+
+  // Ut of the chunk into the row-major tile ui
+  __device__ __forceinline__ void store_u(T* ui, int tid) const {
+    if constexpr (LOAD_U) {
+#pragma unroll
+      for (int m = 0; m < C::UU; ++m) {
+        const int v = tid + m * C::NT, row = v / (DVS / 8), c8 = v % (DVS / 8);
+        E::store8_raw(ui + row * C::ULD + c8 * 8, u[m]);
       }
     }
   }
 };
+
+// ut[jb][e] = Ut[16 jb + r16][colr + 4 g + e] from the row-major tile (zeros without Ut)
+template <typename T, int DK, int DVS, bool LOAD_U>
+__device__ __forceinline__ void read_ut(floatx4 (&ut)[4], const T* ui, int colr, int lane) {
+  using C = DoCfg<T, DK, DVS>;
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    if constexpr (!LOAD_U) {
+      ut[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    } else if constexpr (sizeof(T) == 2) {
+      const bf16x4 v = *reinterpret_cast<const bf16x4*>(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g);
+      ut[jb] = floatx4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
+                       static_cast<float>(v[3])};
+    } else {
+      ut[jb] = *reinterpret_cast<const floatx4*>(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g);
+    }
+  }
+}
 
 // -W and k e^{gamma - b} of the staged chunk into LDS.
 template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_U>
@@ -512,15 +537,15 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
   }
 
   DoStaged<T, DK, NCOL, false, !PHI> st;
-  if (c_first < c_end) st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_first * kChunk, wcol, tid);
+  if (c_first < c_end) st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_first * kChunk, col0, tid);
   for (int c = c_first; c < c_end; ++c) {
     const ChunkDecay cd(st.b);
-    floatx4 ut[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) ut[jb] = st.ut[jb];
     stage_w_kp<T, DK, NCOL, false, !PHI>(sm.wn, sm.kp, st, cd, tid);
-    st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, wcol, tid);
+    st.store_u(sm.ui, tid);
+    st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, col0, tid);
     __syncthreads();
+    floatx4 ut[4];
+    read_ut<T, DK, NCOL, !PHI>(ut, sm.ui, wave * 16, lane);
     typename E::Frag Sf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
@@ -626,13 +651,10 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
   }
 
   DoStaged<T, DK, DVS, true, true> st;
-  if (c_begin < c_end) st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_begin * kChunk, wcol, tid);
+  if (c_begin < c_end) st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_begin * kChunk, col0, tid);
   for (int c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)c * kChunk;
     const ChunkDecay cd(st.b);
-    floatx4 ut[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) ut[jb] = st.ut[jb];
     // ---- (1) operands of chunk c
 #pragma unroll
     for (int m = 0; m < C::QU; ++m) {
@@ -644,8 +666,9 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
     }
     T* const kp = sm.kp[(c - c_begin) & 1];
     stage_w_kp<T, DK, DVS, true, true>(sm.wn, kp, st, cd, tid);
+    st.store_u(sm.ui, tid);
     // ---- (2) prefetch chunk c + 1 (the last iteration re-reads its own chunk)
-    st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, wcol, tid);
+    st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, col0, tid);
     __syncthreads();
 
     // ---- (3) A over the 10 causal tiles
@@ -668,6 +691,8 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
     // ---- (4) o_inter = e^{r_u} Qh S_0 and U = Ut - W S_0 for the wave's columns
     floatx4 O[4];
     {
+      floatx4 ut[4];
+      read_ut<T, DK, DVS, true>(ut, sm.ui, wave * 16, lane);
       typename E::Frag Sf[C::KS];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
