@@ -112,26 +112,21 @@ struct PrepCfg {
 };
 
 // LDS regions are reused across the phases of the pass: u1 holds the keys for L,
-// then Tinv in fp32 with its scratch blocks, then the right-hand sides of the
-// products; u2 holds M, then Tinv in the operand dtype.  At d = 128 that is 53 KB,
-// three workgroups per compute unit (the pass is a chain of short phases between
+// then Tinv in fp32 with its scratch blocks, then the right-hand side of one product
+// at a time; u2 holds M, then Tinv in the operand dtype.  At d = 128 that is 40 KB,
+// four workgroups per compute unit (the pass is a chain of short phases between
 // barriers, so the workgroups in flight set its speed).
 template <typename T, int DK, int DV>
 struct PrepSmem {
   using C = PrepCfg<T, DK, DV>;
   union {
-    struct {
-      T kq[64 * C::QLD];          // k_t e^{b_t - r_u(t)}
-      T kh[64 * C::QLD];          // k_s e^{r_u(s) - b_s}
-    } l;
+    T kr[64 * C::QLD];            // k as loaded
     struct {
       float tf[64][C::FLD];       // Tinv (fp32)
       float scr[4][16][C::SLD];
     } t;
-    struct {
-      T kb[TokTile<T, DK>::SIZE]; // beta_s e^{b_s} k_s, token-major
-      T vb[TokTile<T, DV>::SIZE]; // beta_s v_s, token-major
-    } r;
+    T kb[TokTile<T, DK>::SIZE];   // beta_s e^{b_s} k_s, token-major (W's right-hand side)
+    T vb[TokTile<T, DV>::SIZE];   // beta_s v_s, token-major (Ut's, after W)
   } u1;
   union alignas(16) {             // 16-byte aligned: Tinv's operand copy is written 4 elements at a time
     float mf[64][C::MLD];         // M = diag(beta) L (strictly lower)
@@ -176,16 +171,13 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     sm.sbeta[tid] = t < p.T ? p.beta[bh * p.T + t] : 0.0f;
   }
   __syncthreads();
-  const auto ref = [&](int u) { return u == 0 ? 0.0f : sm.sb[16 * u - 1]; };
   const int last = (int)(((long long)Tn - 1 - t0) < 63 ? ((long long)Tn - 1 - t0) : 63);
   const float gam = sm.sb[last];  // the chunk's total log-decay
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
-    const float br = sm.sb[row], r = ref(row >> 4);
-    const bool sw = frag_swap<T>(row);
-    E::store8_scaled_sw(sm.u1.l.kq + row * C::QLD + c8 * 8, kv[m], exp_e(br - r), sw);
-    E::store8_scaled_sw(sm.u1.l.kh + row * C::QLD + c8 * 8, kv[m], exp_e(r - br), sw);
+    const float br = sm.sb[row];
+    E::store8_scaled_sw(sm.u1.kr + row * C::QLD + c8 * 8, kv[m], 1.0f, frag_swap<T>(row));
     // reset test, key side: log2 max_d |k_row[d]| + (gamma - b_row) log2 e (the threads of a
     // row are DK / 8 consecutive lanes)
     float mx = 0.0f;
@@ -197,7 +189,9 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   }
   __syncthreads();
 
-  // ---- M = diag(beta) L over the 10 causal tiles, strictly below the diagonal
+  // ---- M = diag(beta) L over the 10 causal tiles, strictly below the diagonal:
+  //      k_t . k_s on the matrix cores, then the decay e^{b_t - b_s} (<= 1 where kept;
+  //      the masked entries are selected away, never multiplied)
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
     if (t % 4 != wave) continue;  // wave-uniform
@@ -205,14 +199,16 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
-      E::mfma(acc, E::load_frag(sm.u1.l.kh + (ib * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))),
-              E::load_frag(sm.u1.l.kq + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
+      E::mfma(acc, E::load_frag(sm.u1.kr + (ib * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))),
+              E::load_frag(sm.u1.kr + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
     // acc[e]: row t = 16 jb + r16, column s = 16 ib + 4 g + e
     const int tr = jb * 16 + r16;
-    const float f = (jb == ib ? 1.0f : exp_e(ref(jb) - ref(ib))) * sm.sbeta[tr];
+    const float bt = sm.sb[tr], bet = sm.sbeta[tr];
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      sm.u2.mf[tr][ib * 16 + 4 * g + e] = (jb != ib || 4 * g + e < r16) ? acc[e] * f : 0.0f;
+    for (int e = 0; e < 4; ++e) {
+      const int sc = ib * 16 + 4 * g + e;
+      sm.u2.mf[tr][sc] = (jb != ib || 4 * g + e < r16) ? acc[e] * (exp_e(bt - sm.sb[sc]) * bet) : 0.0f;
+    }
   }
   __syncthreads();
 
@@ -247,7 +243,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     __syncthreads();
   }
   // operand copy of Tinv (over M, no longer read), zero above the diagonal blocks;
-  // then the right-hand sides of the products over the fp32 Tinv
+  // then the right-hand sides of the products, one at a time, over the fp32 Tinv
   // (8 consecutive elements of a row per thread and step: one 16-column block, so one
   // select for all 8; two float4 reads and two 4-element stores)
   for (int e = tid; e < 64 * 8; e += C::NT) {
@@ -257,17 +253,6 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     const float4 hi = keep ? *reinterpret_cast<const float4*>(&sm.u1.t.tf[t][s + 4]) : make_float4(0.f, 0.f, 0.f, 0.f);
     E::store4(sm.u2.tb + t * C::TLD + s, lo.x, lo.y, lo.z, lo.w);
     E::store4(sm.u2.tb + t * C::TLD + s + 4, hi.x, hi.y, hi.z, hi.w);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int m = 0; m < C::QU; ++m) {
-    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
-    TokTile<T, DK>::store8(sm.u1.r.kb, row, c8 * 8, kv[m], sm.sbeta[row] * exp_e(sm.sb[row]));
-  }
-#pragma unroll
-  for (int m = 0; m < C::VU; ++m) {
-    const int u = tid + m * C::NT, row = u / (DV / 8), c8 = u % (DV / 8);
-    TokTile<T, DV>::store8(sm.u1.r.vb, row, c8 * 8, vv[m], sm.sbeta[row]);
   }
   __syncthreads();
 
@@ -295,14 +280,28 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
       }
     }
   };
+  // the two right-hand sides take turns in u1
+#pragma unroll
+  for (int m = 0; m < C::QU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
+    TokTile<T, DK>::store8(sm.u1.kb, row, c8 * 8, kv[m], sm.sbeta[row] * exp_e(sm.sb[row]));
+  }
+  __syncthreads();
+  product(sm.u1.kb, DK, Wg, DK, true);
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < C::VU; ++m) {
+    const int u = tid + m * C::NT, row = u / (DV / 8), c8 = u % (DV / 8);
+    TokTile<T, DV>::store8(sm.u1.vb, row, c8 * 8, vv[m], sm.sbeta[row]);
+  }
+  __syncthreads();
+  product(sm.u1.vb, DV, Ug, DV, false);
   // Reset test of the chunk (only when the plan has segments).  The transition
   // P = e^gamma I - (k e^{gamma-b})^T W has |P[d][e]| <= e^gamma + sum_t |kt_t|max |w_t|max,
   // so |P H| <= 2^13 2^-127 max|H| once every term is below 2^-127 (64 rows, 128 columns):
   // the state after this chunk then does not depend on the state before it, to 2^-114
   // relative.  The terms are compared in log2 (no product underflows on the way);
   // NaN terms fail the comparison, so they never mark a reset.
-  product(sm.u1.r.kb, DK, Wg, DK, true);
-  product(sm.u1.r.vb, DV, Ug, DV, false);
   if (p.reset) {
     bool ok = gam * kLog2e < -127.0f;
 #pragma unroll
