@@ -200,6 +200,14 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
   // ---- every load first: the chunk's b and operands, the neighbour's b and two operand
   //      tiles (k, v of c - 1 or q, dO of c + 1), this wave's slices of the pair's states
   float bval = 0.0f;
+  // the combine's per-token inputs (wave 0), loaded now so that they are in by then
+  float xslope = 0.0f, bnext = 0.0f;
+  if (w == 0) {
+    const long long tt = (long long)t0 + lane;
+    xslope = gate_slope<GATE>(x[bh * Tlen + (tt < Tlen ? tt : Tlen - 1)]);
+    const long long tn = (long long)t0 + kChunk;
+    bnext = tn < Tlen ? bh_b[tn] : 0.0f;
+  }
   if (tid < 64) {
     const long long tt = (long long)t0 + tid;
     bval = bh_b[tt < Tlen ? tt : Tlen - 1];
@@ -419,12 +427,16 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
     row += __shfl_xor(row, 16);
     row += __shfl_xor(row, 32);
     if (g == 0) sm.prow[t][r16] = row;
+    // column sums over the 16 lanes of a row group: DPP row shifts, the total lands in
+    // the row's last lane
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float col = pe[e];
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) col += __shfl_xor(col, off);
-      if (r16 == 0) sm.pcol[t][4 * g + e] = col;
+      col += dpp_or_zero<0x111>(col);  // row_shr:1
+      col += dpp_or_zero<0x112>(col);  // row_shr:2
+      col += dpp_or_zero<0x114>(col);  // row_shr:4
+      col += dpp_or_zero<0x118>(col);  // row_shr:8
+      if (r16 == 15) sm.pcol[t][4 * g + e] = col;
     }
   }
   __syncthreads();
@@ -435,7 +447,7 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
     const int last = (int)((Tlen - 1 - (long long)t0) < 63 ? (Tlen - 1 - (long long)t0) : 63);
     const float gam = sm.b[last];
     // dH_c = a D with a the decay of the first token of the next chunk (1 after the last chunk)
-    const float a = (nbr && !odd) ? exp_e(sm.bn[0]) : ((long long)t0 + kChunk < Tlen ? exp_e(bh_b[t0 + kChunk]) : 1.0f);
+    const float a = (nbr && !odd) ? exp_e(sm.bn[0]) : ((long long)t0 + kChunk < Tlen ? exp_e(bnext) : 1.0f);
     float rs = 0.0f, us = 0.0f, zs = 0.0f;
 #pragma unroll
     for (int ww = 0; ww < X::NW; ++ww) {
@@ -455,24 +467,16 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
       if (tri_i(t) == jb) colsum += sm.pcol[t][jr];
     }
     // R_j = sum_{s<j<=j'} P = sum_{t<j} (colsum - rowsum)_t ; inflow suffix ; outflow prefix
-    float d = colsum - rowsum, dincl = d;
-    float rsuf = r, upre = u;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float a1 = __shfl_up(dincl, off);
-      const float a2 = __shfl_down(rsuf, off);
-      const float a3 = __shfl_up(upre, off);
-      if (lane >= off) {
-        dincl += a1;
-        upre += a3;
-      }
-      if (lane + off < 64) rsuf += a2;
-    }
-    const float R = dincl - d;  // exclusive prefix
-    const float uex = upre - u;  // exclusive prefix
+    // (64-lane scans on DPP row shifts; the suffix is the total minus the exclusive prefix)
+    const float d = colsum - rowsum;
+    const float R = wave_inclusive_scan(d, lane) - d;      // exclusive prefix
+    const float rincl = wave_inclusive_scan(r, lane);
+    const float rtot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, rincl), 63));
+    const float rsuf = rtot - (rincl - r);                 // inclusive suffix
+    const float uex = wave_inclusive_scan(u, lane) - u;    // exclusive prefix
     const float dg = R + rsuf + uex + Z;
     const long long tt = (long long)t0 + j;
-    if (tt < Tlen) dx[bh * Tlen + tt] = gate_slope<GATE>(x[bh * Tlen + tt]) * dg;
+    if (tt < Tlen) dx[bh * Tlen + tt] = xslope * dg;
   }
 }
 
