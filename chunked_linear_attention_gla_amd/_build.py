@@ -15,6 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libgla.so")
+# the same sources with the kernels' LDS-bounds checks compiled in (see gla_debug_flags)
+DEBUG_LIB = os.path.join(PKG, "libgla_debug.so")
 SOURCES = ["gate_cumsum.hip", "chunk_kernels.hip", "ws_kernels.hip", "bwd_kernels.hip", "pc_kernels.hip",
            "decode.hip", "delta_kernels.hip", "bench_stream.hip", "api.hip"]
 ARCH = os.environ.get("GLA_OFFLOAD_ARCH", "gfx950")
@@ -56,10 +58,10 @@ def _run(cmd):
     return err
 
 
-def build(out: str = LIB, verbose: bool = False, jobs: int = 0) -> str:
+def build(out: str = LIB, verbose: bool = False, jobs: int = 0, defines=()) -> str:
     """Compiles each source to an object (in parallel) and links them into `out`.
     The kernels of a source are launched from that source, so no relocatable device
-    code is needed."""
+    code is needed.  `defines`: extra -D flags (the debug build)."""
     import concurrent.futures
     import tempfile
     jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
@@ -68,7 +70,7 @@ def build(out: str = LIB, verbose: bool = False, jobs: int = 0) -> str:
         for src in SOURCES:
             obj = os.path.join(tmpd, os.path.splitext(src)[0] + ".o")
             objs.append(obj)
-            cmds.append([hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+            cmds.append([hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj])
         with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
             for cmd, err in zip(cmds, ex.map(_run, cmds)):
                 if verbose:
@@ -84,5 +86,14 @@ def build(out: str = LIB, verbose: bool = False, jobs: int = 0) -> str:
     return out
 
 
+def build_all(verbose: bool = False) -> list:
+    """The release library and the debug-checked one, both in-tree."""
+    import concurrent.futures
+    with concurrent.futures.ThreadPoolExecutor(2) as ex:
+        rel = ex.submit(build, LIB, verbose, 0)
+        dbg = ex.submit(build, DEBUG_LIB, verbose, 0, ("GLA_DEBUG",))
+        return [rel.result(), dbg.result()]
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build_all(verbose=True))

@@ -8,6 +8,7 @@ no fallback: without the built library every call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import NamedTuple, Optional, Tuple
@@ -78,16 +79,14 @@ _SIGS = {
                                  _psz, _vp]),
     "gla_chunk_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i, _vp]),
     "gla_bench_stream": (_i, [_vp, _vp, _vp, _vp, ctypes.c_ulonglong, _i, _vp]),
+    "gla_debug_flags": (_i, [ctypes.POINTER(ctypes.c_uint)]),
+    "gla_debug_selftest": (_i, [_vp, _vp, _vp]),
     "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
                            _i, _i, _i, _vp, _psz, _vp]),
 }
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libgla.so (raises when it has not been built)."""
-    global _lib
-    if _lib is not None:
-        return _lib
+def _open(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m chunked_linear_attention_gla_amd._build`")
     lib = ctypes.CDLL(path)
@@ -95,8 +94,40 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    _lib = lib
     return lib
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgla.so (raises when it has not been built)."""
+    global _lib
+    if _lib is None:
+        _lib = _open(path)
+    return _lib
+
+
+DEBUG_LIB_PATH = os.path.join(_PKG, "libgla_debug.so")
+
+
+@contextlib.contextmanager
+def use_library(path: str = DEBUG_LIB_PATH):
+    """Route every call of this binding through another build of the library (the
+    LDS-checked debug build by default) inside the block; yields that library."""
+    global _lib
+    prev = load()
+    other = _open(path)
+    _lib = other
+    try:
+        yield other
+    finally:
+        _lib = prev
+
+
+def debug_flags(lib: Optional[ctypes.CDLL] = None) -> int:
+    """Read and clear the LDS-check flags of a debug build (gla_debug_flags); raises
+    GLAError (GLA_ERR_UNSUPPORTED) on a release build."""
+    v = ctypes.c_uint(0)
+    _check("gla_debug_flags", (lib or load()).gla_debug_flags(ctypes.byref(v)))
+    return int(v.value)
 
 
 def _check(fn: str, code: int) -> None:

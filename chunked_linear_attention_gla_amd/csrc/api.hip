@@ -890,3 +890,31 @@ extern "C" gla_status_t gla_chunk_fwd_noalloc(const void* q, const void* k, cons
   size_t n = kScratchBytes;
   return gla_chunk_fwd_plan(q, k, v, x, S0, o, S_T, B, H, T, dk, dv, dtype, gate, path, &pl, ws, &n, stream);
 }
+
+extern "C" gla_status_t gla_debug_flags(unsigned int* flags) {
+  if (!flags) return GLA_ERR_NULL;
+#ifdef GLA_DEBUG
+  const unsigned int words[] = {gla::debug_word_gate_cumsum(), gla::debug_word_chunk_kernels(),
+                                gla::debug_word_ws_kernels(),  gla::debug_word_bwd_kernels(),
+                                gla::debug_word_pc_kernels(),  gla::debug_word_decode(),
+                                gla::debug_word_delta_kernels()};
+  unsigned int v = 0;
+  for (unsigned int w : words) {
+    if (w == ~0u) return GLA_ERR_HIP;
+    v |= w;
+  }
+  *flags = v;
+  return GLA_OK;
+#else
+  return GLA_ERR_UNSUPPORTED;
+#endif
+}
+
+extern "C" gla_status_t gla_debug_selftest(const float* probe, float* out, void* stream) {
+  if (!probe || !out) return GLA_ERR_NULL;
+#ifdef GLA_DEBUG
+  return gla::launch_debug_selftest(probe, out, (hipStream_t)stream) == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+#else
+  return GLA_ERR_UNSUPPORTED;
+#endif
+}

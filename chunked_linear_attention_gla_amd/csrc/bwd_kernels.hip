@@ -140,6 +140,8 @@ __device__ __forceinline__ typename Elem<T>::Frag tok_frag(const T* tile, int k0
     return TokTile<T, 16, LD>::load(tile, k0, c0, lane);
   } else {
     const int g = lane >> 4, r = lane & 15;
+    GLA_CHECK_LDS(tile + (k0 + 4 * g) * LD + c0 + r, 4);
+    GLA_CHECK_LDS(tile + (k0 + 16 + 4 * g + 3) * LD + c0 + r, 4);
     typename Elem<T>::Frag f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -537,5 +539,8 @@ hipError_t launch_grad_ds0(const float* D0, const float* b, const float* dST, fl
   hipLaunchKernelGGL(grad_ds0_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, D0, b, dST, dS0, T, nst, total);
   return hipGetLastError();
 }
+
+// debug builds: this unit's LDS-check word (see GLA_CHECK_LDS)
+GLA_DEBUG_ACCESSOR(debug_word_bwd_kernels)
 
 }  // namespace gla

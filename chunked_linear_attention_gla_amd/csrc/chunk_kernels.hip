@@ -549,4 +549,7 @@ hipError_t launch_chunk_output(const ChunkParams& p, int dtype, bool diag, hipSt
   return dispatch(dtype, p.dk, p.dv / p.nslices, diag, OutFn{p, stream});
 }
 
+// debug builds: this unit's LDS-check word (see GLA_CHECK_LDS)
+GLA_DEBUG_ACCESSOR(debug_word_chunk_kernels)
+
 }  // namespace gla

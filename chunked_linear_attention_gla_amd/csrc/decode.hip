@@ -111,4 +111,7 @@ hipError_t launch_decode_step(const void* q, const void* k, const void* v, const
   return hipGetLastError();
 }
 
+// debug builds: this unit's LDS-check word (see GLA_CHECK_LDS)
+GLA_DEBUG_ACCESSOR(debug_word_decode)
+
 }  // namespace gla

@@ -421,10 +421,12 @@ __device__ __forceinline__ void read_ut(floatx4 (&ut)[4], const T* ui, int colr,
     if constexpr (!LOAD_U) {
       ut[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
     } else if constexpr (sizeof(T) == 2) {
+      GLA_CHECK_LDS(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g, 8);
       const bf16x4 v = *reinterpret_cast<const bf16x4*>(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g);
       ut[jb] = floatx4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
                        static_cast<float>(v[3])};
     } else {
+      GLA_CHECK_LDS(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g, 16);
       ut[jb] = *reinterpret_cast<const floatx4*>(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g);
     }
   }
@@ -807,5 +809,8 @@ hipError_t launch_delta_output(const DeltaParams& p, int dtype, hipStream_t stre
 #undef GLA_DO
   return hipErrorInvalidValue;
 }
+
+// debug builds: this unit's LDS-check word (see GLA_CHECK_LDS)
+GLA_DEBUG_ACCESSOR(debug_word_delta_kernels)
 
 }  // namespace gla

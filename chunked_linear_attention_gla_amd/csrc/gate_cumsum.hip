@@ -139,4 +139,28 @@ hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long 
   return hipGetLastError();
 }
 
+#ifdef GLA_DEBUG
+// Self-test of the LDS checks: asks them about an address one element past this
+// kernel's 256-byte LDS allocation and about a global pointer, and accesses neither;
+// both bits must come up.
+__global__ void __launch_bounds__(64) debug_selftest_kernel(const float* g, float* out) {
+  __shared__ float tile[64];
+  tile[threadIdx.x] = (float)threadIdx.x;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    GLA_CHECK_LDS(tile + 64, 4);
+    GLA_CHECK_LDS(g, 4);
+  }
+  out[threadIdx.x] = tile[63 - threadIdx.x];
+}
+
+hipError_t launch_debug_selftest(const float* g, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(debug_selftest_kernel, dim3(1), dim3(64), 0, stream, g, out);
+  return hipGetLastError();
+}
+#endif
+
+// debug builds: this unit's LDS-check word (see GLA_CHECK_LDS)
+GLA_DEBUG_ACCESSOR(debug_word_gate_cumsum)
+
 }  // namespace gla

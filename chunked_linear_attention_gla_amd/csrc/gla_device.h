@@ -31,6 +31,44 @@ constexpr int kTile = 16;   // tokens per tile (the bounded-decay safe length)
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+// ---------------------------------------------------------------- debug checks
+// A library built with -DGLA_DEBUG checks, inside the shared LDS helpers below, that
+// every access reaches LDS and falls inside the workgroup's static LDS allocation.  A
+// failed check sets a bit in a device word of its translation unit and the kernel goes
+// on (the hardware drops LDS accesses past the allocation): checks never trap.  The C
+// entry point gla_debug_flags reads and clears the words.  Release builds compile
+// every check away.
+enum : unsigned { kDebugLdsRange = 1u, kDebugNotLds = 2u };
+#ifdef GLA_DEBUG
+static __device__ unsigned int g_debug_word;
+__device__ __forceinline__ void debug_fail(unsigned bit) { atomicOr(&g_debug_word, bit); }
+__device__ __forceinline__ void debug_check_lds(const void* p, unsigned bytes) {
+  if (!__builtin_amdgcn_is_shared((const __attribute__((address_space(0))) void*)p)) {
+    debug_fail(kDebugNotLds);
+    return;
+  }
+  const unsigned off = (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  if (off + bytes > __builtin_amdgcn_groupstaticsize()) debug_fail(kDebugLdsRange);
+}
+#define GLA_CHECK_LDS(p, bytes) ::gla::debug_check_lds((const void*)(p), (bytes))
+// Host side, one per translation unit: read and clear that unit's word (~0u if the
+// read fails).
+#define GLA_DEBUG_ACCESSOR(NAME)                                                              \
+  unsigned int NAME() {                                                                        \
+    unsigned int v = 0, z = 0;                                                                 \
+    if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_debug_word), sizeof v, 0, hipMemcpyDeviceToHost) != \
+        hipSuccess)                                                                            \
+      return ~0u;                                                                              \
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), &z, sizeof z, 0, hipMemcpyHostToDevice) !=   \
+        hipSuccess)                                                                            \
+      return ~0u;                                                                              \
+    return v;                                                                                  \
+  }
+#else
+#define GLA_CHECK_LDS(p, bytes) ((void)0)
+#define GLA_DEBUG_ACCESSOR(NAME)
+#endif
+
 // 2^x on the hardware exp2 (v_exp_f32).  2^-inf = 0, 2^+inf = inf.
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -156,16 +194,19 @@ template <> struct Elem<bf16> {
   __device__ static __forceinline__ bf16 cvt(float f) { return static_cast<bf16>(f); }
   // store 8 scaled elements as one 16-byte LDS write
   __device__ static __forceinline__ void store8_scaled(bf16* dst, const Vec8& v, float s) {
+    GLA_CHECK_LDS(dst, 16);
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = cvt(get(v, e) * s);
     *reinterpret_cast<bf16x8*>(dst) = o;
   }
   __device__ static __forceinline__ void store8_raw(bf16* dst, const Vec8& v) {
+    GLA_CHECK_LDS(dst, 16);
     *reinterpret_cast<uint4*>(dst) = v.u;
   }
   // store -v (sign bits flipped: exact)
   __device__ static __forceinline__ void store8_neg(bf16* dst, const Vec8& v) {
+    GLA_CHECK_LDS(dst, 16);
     constexpr uint32_t m = 0x80008000u;
     *reinterpret_cast<uint4*>(dst) = make_uint4(v.u.x ^ m, v.u.y ^ m, v.u.z ^ m, v.u.w ^ m);
   }
@@ -173,6 +214,7 @@ template <> struct Elem<bf16> {
   // halves swapped when `swap` (a fragment-read swizzle; see the kernels using it).
   static constexpr bool kSwizzle = true;
   __device__ static __forceinline__ void store8_scaled_sw(bf16* dst, const Vec8& v, float s, bool swap) {
+    GLA_CHECK_LDS(dst, 16);
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = cvt(get(v, e) * s);
@@ -180,6 +222,7 @@ template <> struct Elem<bf16> {
     *reinterpret_cast<bf16x8*>(dst) = o;
   }
   __device__ static __forceinline__ void store8_vscaled_sw(bf16* dst, const Vec8& v, const float (&s)[8], bool swap) {
+    GLA_CHECK_LDS(dst, 16);
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = cvt(get(v, e) * s[e]);
@@ -187,12 +230,14 @@ template <> struct Elem<bf16> {
     *reinterpret_cast<bf16x8*>(dst) = o;
   }
   __device__ static __forceinline__ void store8_neg_sw(bf16* dst, const Vec8& v, bool swap) {
+    GLA_CHECK_LDS(dst, 16);
     constexpr uint32_t m = 0x80008000u;
     const uint4 n = make_uint4(v.u.x ^ m, v.u.y ^ m, v.u.z ^ m, v.u.w ^ m);
     *reinterpret_cast<uint4*>(dst) = swap ? make_uint4(n.z, n.w, n.x, n.y) : n;
   }
   // store 8 elements, each with its own scale
   __device__ static __forceinline__ void store8_vscaled(bf16* dst, const Vec8& v, const float (&s)[8]) {
+    GLA_CHECK_LDS(dst, 16);
     bf16x8 o;
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] = cvt(get(v, e) * s[e]);
@@ -200,6 +245,8 @@ template <> struct Elem<bf16> {
   }
   // two 4-element (8-byte) LDS reads at cols c and c + 16 of one row
   __device__ static __forceinline__ Frag load_frag(const bf16* row, int c) {
+    GLA_CHECK_LDS(row + c, 8);
+    GLA_CHECK_LDS(row + c + 16, 8);
     const bf16x4 lo = *reinterpret_cast<const bf16x4*>(row + c);
     const bf16x4 hi = *reinterpret_cast<const bf16x4*>(row + c + 16);
     Frag f;
@@ -213,6 +260,7 @@ template <> struct Elem<bf16> {
     return f;
   }
   __device__ static __forceinline__ void store4(bf16* dst, float a, float b, float c, float d) {
+    GLA_CHECK_LDS(dst, 8);
     bf16x4 o;
     o[0] = cvt(a); o[1] = cvt(b); o[2] = cvt(c); o[3] = cvt(d);
     *reinterpret_cast<bf16x4*>(dst) = o;
@@ -248,6 +296,7 @@ template <> struct Elem<float> {
   }
   __device__ static __forceinline__ float cvt(float f) { return f; }
   __device__ static __forceinline__ void store8_scaled(float* dst, const Vec8& v, float s) {
+    GLA_CHECK_LDS(dst, 32);
     float4 a = v.a, b = v.b;
     a.x *= s; a.y *= s; a.z *= s; a.w *= s;
     b.x *= s; b.y *= s; b.z *= s; b.w *= s;
@@ -255,10 +304,12 @@ template <> struct Elem<float> {
     *reinterpret_cast<float4*>(dst + 4) = b;
   }
   __device__ static __forceinline__ void store8_raw(float* dst, const Vec8& v) {
+    GLA_CHECK_LDS(dst, 32);
     *reinterpret_cast<float4*>(dst) = v.a;
     *reinterpret_cast<float4*>(dst + 4) = v.b;
   }
   __device__ static __forceinline__ void store8_neg(float* dst, const Vec8& v) {
+    GLA_CHECK_LDS(dst, 32);
     constexpr uint32_t m = 0x80000000u;
     const auto flip = [](float f) { return __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, f) ^ m); };
     *reinterpret_cast<float4*>(dst) = make_float4(flip(v.a.x), flip(v.a.y), flip(v.a.z), flip(v.a.w));
@@ -274,10 +325,13 @@ template <> struct Elem<float> {
     store8_vscaled(dst, v, s);
   }
   __device__ static __forceinline__ void store8_vscaled(float* dst, const Vec8& v, const float (&s)[8]) {
+    GLA_CHECK_LDS(dst, 32);
     *reinterpret_cast<float4*>(dst) = make_float4(v.a.x * s[0], v.a.y * s[1], v.a.z * s[2], v.a.w * s[3]);
     *reinterpret_cast<float4*>(dst + 4) = make_float4(v.b.x * s[4], v.b.y * s[5], v.b.z * s[6], v.b.w * s[7]);
   }
   __device__ static __forceinline__ Frag load_frag(const float* row, int c) {
+    GLA_CHECK_LDS(row + c, 16);
+    GLA_CHECK_LDS(row + c + 16, 16);
     Frag f;
     f.lo = *reinterpret_cast<const floatx4*>(row + c);
     f.hi = *reinterpret_cast<const floatx4*>(row + c + 16);
@@ -287,6 +341,7 @@ template <> struct Elem<float> {
     Frag f; f.lo = a; f.hi = b; return f;
   }
   __device__ static __forceinline__ void store4(float* dst, float a, float b, float c, float d) {
+    GLA_CHECK_LDS(dst, 16);
     floatx4 o = {a, b, c, d};
     *reinterpret_cast<floatx4*>(dst) = o;
   }
@@ -341,6 +396,8 @@ template <int NCOL, int LDX> struct TokTile<bf16, NCOL, LDX> {
     const int s = lane & 15, g = lane >> 4;
     const bf16* p0 = t + (k0 + 4 * g + (s >> 2)) * LD + c0 + 4 * (s & 3);
     const bf16* p1 = p0 + 16 * LD;
+    GLA_CHECK_LDS(p0, 8);
+    GLA_CHECK_LDS(p1, 8);
     const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0));
     const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p1));
     E::Frag f;
@@ -354,14 +411,20 @@ template <int NCOL, int LDX> struct TokTile<float, NCOL, LDX> {
   static constexpr int SIZE = NCOL * LD;
   using E = Elem<float>;
   __device__ static __forceinline__ void store8(float* t, int row, int col, const E::Vec8& v, float s) {
+    GLA_CHECK_LDS(t + col * LD + row, 4);
+    GLA_CHECK_LDS(t + (col + 7) * LD + row, 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = E::get(v, e) * s;
   }
   __device__ static __forceinline__ void store8_raw(float* t, int row, int col, const E::Vec8& v) {
+    GLA_CHECK_LDS(t + col * LD + row, 4);
+    GLA_CHECK_LDS(t + (col + 7) * LD + row, 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = E::get(v, e);
   }
   __device__ static __forceinline__ void store8_v(float* t, int row, int col, const E::Vec8& v, const float (&s)[8]) {
+    GLA_CHECK_LDS(t + col * LD + row, 4);
+    GLA_CHECK_LDS(t + (col + 7) * LD + row, 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = E::get(v, e) * s[e];
   }

@@ -164,4 +164,17 @@ hipError_t launch_grad_dx(const void* q, const void* k, const void* v, const voi
 hipError_t launch_grad_ds0(const float* D0, const float* b, const float* dST, float* dS0, long long BH,
                            long long T, int dk_, int dv_, hipStream_t stream);
 
+#ifdef GLA_DEBUG
+// read and clear the LDS-check word of each kernel translation unit (debug builds)
+unsigned int debug_word_gate_cumsum();
+unsigned int debug_word_chunk_kernels();
+unsigned int debug_word_ws_kernels();
+unsigned int debug_word_bwd_kernels();
+unsigned int debug_word_pc_kernels();
+unsigned int debug_word_decode();
+unsigned int debug_word_delta_kernels();
+// the LDS checks' self-test: one workgroup of 64 threads; out: 64 floats it writes
+hipError_t launch_debug_selftest(const float* g, float* out, hipStream_t stream);
+#endif
+
 }  // namespace gla

@@ -688,4 +688,7 @@ hipError_t launch_pc_chunk_output(const PcParams& p, int dtype, hipStream_t stre
   return pc_dispatch(dtype, p.dk, p.dv / p.nslices, PcOutFn{p, stream});
 }
 
+// debug builds: this unit's LDS-check word (see GLA_CHECK_LDS)
+GLA_DEBUG_ACCESSOR(debug_word_pc_kernels)
+
 }  // namespace gla

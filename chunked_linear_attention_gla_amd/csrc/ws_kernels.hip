@@ -167,6 +167,8 @@ __device__ __forceinline__ void diagonal_pairs(bf16* a, const bf16* qr, const bf
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int rq = u * 16 + jq * 4 + x, rk = u * 16 + iq * 4 + x;
+      GLA_CHECK_LDS(qr + rq * DK + raw_piece(p, rq) * 8, 16);
+      GLA_CHECK_LDS(kr + rk * DK + raw_piece(p, rk) * 8, 16);
       qv[x] = *reinterpret_cast<const uint4*>(qr + rq * DK + raw_piece(p, rq) * 8);
       kv[x] = *reinterpret_cast<const uint4*>(kr + rk * DK + raw_piece(p, rk) * 8);
     }
@@ -340,6 +342,8 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         E::store8_scaled(sm.kh + row * W::LD + c8 * 8, kv, exp_e((DIAG ? cd.end(tile) : rj) - brow[m]));
         E::store8_scaled(sm.kp[ns] + row * W::KLD + c8 * 8, kv, exp_e(cd.gam - brow[m]));
         if (DIAG) {
+          GLA_CHECK_LDS(sm.qr + row * DK + raw_piece(c8, row) * 8, 16);
+          GLA_CHECK_LDS(sm.kr + row * DK + raw_piece(c8, row) * 8, 16);
           *reinterpret_cast<uint4*>(sm.qr + row * DK + raw_piece(c8, row) * 8) = stg.q[m];
           *reinterpret_cast<uint4*>(sm.kr + row * DK + raw_piece(c8, row) * 8) = stg.k[m];
         }
@@ -348,6 +352,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
       for (int m = 0; m < W::VU; ++m) {
         const int u = st + m * 256;
         const int row = u / (DVS / 8), c8 = u % (DVS / 8);
+        GLA_CHECK_LDS(sm.vv[ns] + row * W::VLD + c8 * 8, 16);
         *reinterpret_cast<uint4*>(sm.vv[ns] + row * W::VLD + c8 * 8) = stg.v[m];
       }
       if (sw == 0) sm.sb[lane] = bl;
@@ -484,6 +489,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, false>::NT)) segment_state_ws_
       for (int m = 0; m < W::VU; ++m) {
         const int u = st + m * 256;
         const int row = u / (DVS / 8), c8 = u % (DVS / 8);
+        GLA_CHECK_LDS(sm.vv[ns] + row * W::VLD + c8 * 8, 16);
         *reinterpret_cast<uint4*>(sm.vv[ns] + row * W::VLD + c8 * 8) = stg.v[m];
       }
       if (sw == 0 && lane == 0) sm.gam[ns] = cd.gam;
@@ -546,5 +552,8 @@ hipError_t launch_segment_states_ws(const ChunkParams& p, int dk, int slice, hip
 #undef GLA_WS_CASE
   return hipErrorInvalidValue;
 }
+
+// debug builds: this unit's LDS-check word (see GLA_CHECK_LDS)
+GLA_DEBUG_ACCESSOR(debug_word_ws_kernels)
 
 }  // namespace gla

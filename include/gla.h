@@ -374,6 +374,27 @@ gla_status_t gla_chunk_fwd_pc(const void* q, const void* k, const void* v, const
 gla_status_t gla_bench_stream(const void* a, const void* b, const void* c, void* out,
                               unsigned long long units, int grid, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Debug builds (the library compiled with -DGLA_DEBUG, libgla_debug.so next to
+ * libgla.so): every LDS access made through the kernels' shared load/store
+ * helpers is checked against the workgroup's static LDS allocation.  A failed
+ * check never traps; it sets a bit in a per-device word, which this call reads
+ * (ORed over the library's kernel units) into *flags and clears:
+ *   bit 0: an access past the workgroup's LDS allocation,
+ *   bit 1: an LDS helper handed a pointer that is not in LDS.
+ * Synchronise the device before reading.  Acts on the current device.  Release
+ * builds return GLA_ERR_UNSUPPORTED and leave *flags untouched; NULL flags:
+ * GLA_ERR_NULL; a failed device copy: GLA_ERR_HIP. */
+gla_status_t gla_debug_flags(unsigned int* flags);
+
+/* Self-test of those checks (debug builds): one workgroup asks them about an
+ * address one element past its own 256-byte LDS allocation and about the global
+ * pointer `probe` (device memory, never dereferenced), accessing neither, so both
+ * flag bits come up; `out` (64 floats of device memory) receives values the kernel
+ * computes so that it is not optimised away.  Enqueued on `stream`.  Release
+ * builds: GLA_ERR_UNSUPPORTED. */
+gla_status_t gla_debug_selftest(const float* probe, float* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,27 @@ def test_every_declared_symbol_is_exported(lib):
     assert not missing, missing
 
 
+def test_debug_build_exports_the_same_entry_points():
+    """The LDS-checked debug build is built beside the release library and exports
+    every declared entry point too."""
+    path = _lib.DEBUG_LIB_PATH
+    assert os.path.exists(path), "libgla_debug.so is built by __graft_entry__.build()"
+    dbg = ctypes.CDLL(path)
+    missing = [n for n in declared_functions() if not hasattr(dbg, n)]
+    assert not missing, missing
+
+
+def test_debug_entry_points_on_the_release_build(lib):
+    """The release build compiles the checks away: both debug calls say so, after
+    rejecting NULL pointers, without any device call."""
+    v = ctypes.c_uint(7)
+    assert lib.gla_debug_flags(None) == NULL
+    assert lib.gla_debug_flags(ctypes.byref(v)) == UNSUP and v.value == 7
+    dummy = ctypes.c_void_p(16)
+    assert lib.gla_debug_selftest(None, dummy, None) == NULL
+    assert lib.gla_debug_selftest(dummy, dummy, None) == UNSUP
+
+
 def test_version_and_status_strings(lib):
     assert lib.gla_abi_version() == 2
     for code in range(11):
