@@ -135,3 +135,13 @@ def test_largest_head_extent():
             assert rel(g_, r_[0, lo:hi]) <= TOL["bf16"], (name, a)
         if a == 0:
             assert rel(got[4][0, 0].double().cpu().numpy(), ref[4][0]) <= TOL["bf16"]
+
+
+def test_repeat_calls_are_bitwise_identical():
+    """Same inputs, same gradients, bit for bit (segmented plans in every pass): no
+    atomics or order-dependent reductions in the backward pass."""
+    w, inp, dO, dST = make(64 * 40 + 9, H=2)
+    a = gla.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["x"], dO, inp["S0"], dST)
+    b = gla.chunk_bwd(inp["q"], inp["k"], inp["v"], inp["x"], dO, inp["S0"], dST)
+    torch.cuda.synchronize()
+    assert all(torch.equal(x, y) for x, y in zip(a, b))

@@ -182,3 +182,14 @@ def test_reset_chunks_inside_segments(qkv, beta_one):
     if beta_one:
         inp["beta"].fill_(1.0)
     check(w, inp, plan=gla.Plan(4, 1))
+
+
+def test_repeat_calls_are_bitwise_identical():
+    """Same inputs, same o and S_T bit for bit, with segments (pre-pass with reset
+    flags, folds of the segment maps)."""
+    w, inp = make(64 * 24 + 5, H=2, x_mean=-3.0)
+    args = (inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["S0"])
+    o1, S1 = gla.chunk_fwd_delta(*args, plan=gla.Plan(4, 1))
+    o2, S2 = gla.chunk_fwd_delta(*args, plan=gla.Plan(4, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
