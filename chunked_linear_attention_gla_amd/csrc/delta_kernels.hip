@@ -331,17 +331,11 @@ struct DoCfg {
   static constexpr int TLD = 64 + 4;   // A row stride: its 8-byte stores and fragment reads are conflict-free
   static constexpr int QU = 8 * DK / NT;
   static constexpr int UU = 8 * DVS / NT;      // 16-byte (bf16) Ut pieces per thread
-  static constexpr int ULD = DVS + PAD;        // row stride of the loaded Ut tile
   static constexpr int DB = DK / 16;
   static constexpr int KS = DK / 32;
   static_assert(QU >= 1 && QU * NT == 8 * DK, "staging must divide evenly");
   static_assert(UU >= 1 && UU * NT == 8 * DVS, "Ut staging must divide evenly");
 };
-
-// U is written with 8-byte stores in the accumulator layout, which conflict less at a
-// row stride of NCOL + 8 than at the NCOL + 16 of the other token-major tiles.
-template <typename T, int NCOL>
-using UTile = TokTile<T, NCOL, NCOL + 8>;
 
 template <typename T, int DK, int DVS>
 struct DoSmem {
@@ -350,8 +344,7 @@ struct DoSmem {
   T kh[64 * C::QLD];
   T wn[64 * C::QLD];              // -W
   T kp[2][TokTile<T, DK>::SIZE];  // k e^{gamma - b}, token-major, by chunk parity
-  T uu[UTile<T, DVS>::SIZE];      // U of the slice, token-major
-  T ui[64 * C::ULD];              // Ut of the slice as loaded, row-major
+  T ui[TokTile<T, DVS>::SIZE];    // Ut of the slice, token-major
   T a[64 * C::TLD];
 };
 
@@ -360,14 +353,13 @@ struct DsSmem {
   using C = DoCfg<T, DK, DVS>;
   T wn[64 * C::QLD];
   T kp[TokTile<T, DK>::SIZE];
-  T uu[UTile<T, DVS>::SIZE];
-  T ui[64 * C::ULD];              // Ut of the slice as loaded, row-major
+  T ui[TokTile<T, DVS>::SIZE];    // Ut of the slice, token-major
   int nonzero[2][C::NW];  // transition half: per wave, whether its columns are nonzero, by chunk parity
 };
 
 // One chunk of (q,) k, W, Ut and b on its way to LDS.  Every operand is loaded in
-// row-contiguous 16-byte pieces; Ut goes to a row-major tile from which each wave
-// reads its columns in the accumulator layout (read_ut).
+// row-contiguous 16-byte pieces; Ut goes to a token-major tile from which each wave
+// reads its columns as accumulators of U (effective_writes).
 template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_U>
 struct DoStaged {
   using E = Elem<T>;
@@ -399,38 +391,17 @@ struct DoStaged {
     }
   }
 
-  // Ut of the chunk into the row-major tile ui
+  // Ut of the chunk into the token-major tile ui
   __device__ __forceinline__ void store_u(T* ui, int tid) const {
     if constexpr (LOAD_U) {
 #pragma unroll
       for (int m = 0; m < C::UU; ++m) {
         const int v = tid + m * C::NT, row = v / (DVS / 8), c8 = v % (DVS / 8);
-        E::store8_raw(ui + row * C::ULD + c8 * 8, u[m]);
+        TokTile<T, DVS>::store8_raw(ui, row, c8 * 8, u[m]);
       }
     }
   }
 };
-
-// ut[jb][e] = Ut[16 jb + r16][colr + 4 g + e] from the row-major tile (zeros without Ut)
-template <typename T, int DK, int DVS, bool LOAD_U>
-__device__ __forceinline__ void read_ut(floatx4 (&ut)[4], const T* ui, int colr, int lane) {
-  using C = DoCfg<T, DK, DVS>;
-  const int r16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
-    if constexpr (!LOAD_U) {
-      ut[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    } else if constexpr (sizeof(T) == 2) {
-      GLA_CHECK_LDS(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g, 8);
-      const bf16x4 v = *reinterpret_cast<const bf16x4*>(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g);
-      ut[jb] = floatx4{static_cast<float>(v[0]), static_cast<float>(v[1]), static_cast<float>(v[2]),
-                       static_cast<float>(v[3])};
-    } else {
-      GLA_CHECK_LDS(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g, 16);
-      ut[jb] = *reinterpret_cast<const floatx4*>(ui + (jb * 16 + r16) * C::ULD + colr + 4 * g);
-    }
-  }
-}
 
 // -W and k e^{gamma - b} of the staged chunk into LDS.
 template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_U>
@@ -446,28 +417,44 @@ __device__ __forceinline__ void stage_w_kp(T* wn, T* kp, const DoStaged<T, DK, D
   }
 }
 
-// U = Ut - W S_0 for the wave's 16 columns (S_0 as operand fragments Sf), written to
-// the token-major LDS tile at slice column colr.
-template <typename T, int DK, int DVS>
-__device__ __forceinline__ void effective_writes(floatx4 (&ut)[4], const typename Elem<T>::Frag (&Sf)[DK / 32],
-                                                 const T* wn, T* uu, int colr, int lane) {
+// U = Ut - W S_0 for the wave's 16 columns (S_0 as operand fragments Sf), straight into
+// the operand fragments of A.U and the state update.  The accumulators hold tokens as
+// rows -- U[jb][e] = U[16 jb + 4 g + e][colr + r16], from the product with -W as the
+// left operand -- so two stacked 16-token blocks are already a 32-token K-step fragment
+// (the fragment convention of gla_device.h), and Ut enters as their initial value, read
+// from the token-major tile by the transposing read (zeros without Ut).
+template <typename T, int DK, int DVS, bool LOAD_U>
+__device__ __forceinline__ void effective_writes(typename Elem<T>::Frag (&Uf)[2],
+                                                 const typename Elem<T>::Frag (&Sf)[DK / 32], const T* wn,
+                                                 const T* ui, int colr, int lane) {
   using E = Elem<T>;
   using C = DoCfg<T, DK, DVS>;
   const int r16 = lane & 15, g = lane >> 4;
+  floatx4 U[4];
 #pragma unroll
-  for (int jb = 0; jb < 4; ++jb) {
+  for (int ks = 0; ks < 2; ++ks) {
+    if constexpr (!LOAD_U) {
+      U[2 * ks] = U[2 * ks + 1] = floatx4{0.f, 0.f, 0.f, 0.f};
+    } else if constexpr (sizeof(T) == 2) {
+      const typename E::Frag f = TokTile<T, DVS>::load(ui, ks * 32, colr, lane);
 #pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      E::mfma(ut[jb], Sf[ks], E::load_frag(wn + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
-    // ut[jb][e] = U[16 jb + r16][colr + 4 g + e]
-    const int row = jb * 16 + r16;
-    if constexpr (sizeof(T) == 2) {
-      E::store4(uu + row * UTile<T, DVS>::LD + colr + 4 * g, ut[jb][0], ut[jb][1], ut[jb][2], ut[jb][3]);
+      for (int e = 0; e < 4; ++e) {
+        U[2 * ks][e] = static_cast<float>(f.v[e]);
+        U[2 * ks + 1][e] = static_cast<float>(f.v[4 + e]);
+      }
     } else {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) uu[(colr + 4 * g + e) * UTile<T, DVS>::LD + row] = ut[jb][e];
+      const typename E::Frag f = TokTile<T, DVS>::load(ui, ks * 32, colr, lane);
+      U[2 * ks] = f.lo;
+      U[2 * ks + 1] = f.hi;
     }
   }
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      E::mfma(U[jb], E::load_frag(wn + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))), Sf[ks]);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) Uf[ks] = E::from_acc(U[2 * ks], U[2 * ks + 1]);
 }
 
 // S <- e^gamma S + (k e^{gamma - b})^T U
@@ -545,16 +532,11 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
     st.store_u(sm.ui, tid);
     st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, col0, tid);
     __syncthreads();
-    floatx4 ut[4];
-    read_ut<T, DK, NCOL, !PHI>(ut, sm.ui, wave * 16, lane);
     typename E::Frag Sf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
-    effective_writes<T, DK, NCOL>(ut, Sf, sm.wn, sm.uu, wave * 16, lane);
-    __syncthreads();
     typename E::Frag Uf[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) Uf[ks] = UTile<T, NCOL>::load(sm.uu, ks * 32, wave * 16, lane);
+    effective_writes<T, DK, NCOL, !PHI>(Uf, Sf, sm.wn, sm.ui, wave * 16, lane);
     delta_state_update<T, DK, NCOL>(S, Uf, sm.kp, exp_e(cd.gam), lane);
     if constexpr (PHI) {
       // Once this workgroup's columns of the running transition product are all
@@ -691,9 +673,8 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
 
     // ---- (4) o_inter = e^{r_u} Qh S_0 and U = Ut - W S_0 for the wave's columns
     floatx4 O[4];
+    typename E::Frag Uf[2];
     {
-      floatx4 ut[4];
-      read_ut<T, DK, DVS, true>(ut, sm.ui, wave * 16, lane);
       typename E::Frag Sf[C::KS];
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
@@ -705,15 +686,12 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
           E::mfma(O[jb], Sf[ks], E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
         if (jb > 0) O[jb] *= exp_e(cd.r(jb));
       }
-      effective_writes<T, DK, DVS>(ut, Sf, sm.wn, sm.uu, wave * 16, lane);
+      effective_writes<T, DK, DVS, true>(Uf, Sf, sm.wn, sm.ui, wave * 16, lane);
     }
     __syncthreads();
 
     // ---- (5) o += A U; S_c = e^gamma S_0 + (k e^{gamma - b})^T U
     {
-      typename E::Frag Uf[2];
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) Uf[ks] = UTile<T, DVS>::load(sm.uu, ks * 32, wave * 16, lane);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
@@ -724,10 +702,9 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       for (int jb = 0; jb < 4; ++jb)
         buf_store16(ro, dl_row(t0 + jb * 16 + r16, Tn, (uint32_t)p.dv * 4u) + (wcol + 4 * g) * 4u, O[jb]);
     }
-    // No barrier here: the next chunk's staging writes Qh, Kh and -W, last read in (3)
-    // and (4) before this chunk's second barrier, and the other k e^{gamma - b} buffer;
-    // A is rewritten only after its first barrier, and U is read by the wave that
-    // wrote it.
+    // No barrier here: the next chunk's staging writes Qh, Kh, -W and Ut, last read in
+    // (3) and (4) before this chunk's second barrier, and the other k e^{gamma - b}
+    // buffer; A is rewritten only after its first barrier.
   }
   if (seg == p.segments - 1) {
 #pragma unroll
