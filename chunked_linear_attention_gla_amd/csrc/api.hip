@@ -643,12 +643,11 @@ gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, co
   const int dt = dtype == GLA_BF16 ? 0 : 1;
   const size_t es = elem_size(dtype);
   const size_t b_bytes = align_up((size_t)BH * T * 4);
-  const size_t w_bytes = align_up((size_t)BH * T * dk * es);
-  const size_t u_bytes = align_up((size_t)BH * T * dv * es);
+  const size_t t_bytes = align_up((size_t)BH * n_chunks(T) * GLA_CHUNK * GLA_CHUNK * es);  // Tinv per chunk
   const size_t h_bytes = pl.segments > 1 ? align_up((size_t)BH * (pl.segments - 1) * dk * dv * 4) : 0;
   const size_t f_bytes = pl.segments > 1 ? align_up((size_t)BH * (pl.segments - 1) * dk * dk * 4) : 0;
   const size_t r_bytes = pl.segments > 1 ? align_up((size_t)BH * n_chunks(T) * 4) : 0;
-  const size_t need = std::max(b_bytes + w_bytes + u_bytes + h_bytes + f_bytes + r_bytes, kAlign);
+  const size_t need = std::max(b_bytes + t_bytes + h_bytes + f_bytes + r_bytes, kAlign);
   if (!workspace) {
     *workspace_bytes = need;
     return GLA_OK;
@@ -679,11 +678,10 @@ gla_status_t gla_chunk_fwd_delta(const void* q, const void* k, const void* v, co
   p.S0 = S0;
   p.o = o;
   p.ST = S_T;
-  p.W = w + b_bytes;
-  p.U = w + b_bytes + w_bytes;
-  p.seg_state = pl.segments > 1 ? (float*)(w + b_bytes + w_bytes + u_bytes) : nullptr;
-  p.seg_phi = pl.segments > 1 ? (float*)(w + b_bytes + w_bytes + u_bytes + h_bytes) : nullptr;
-  p.reset = pl.segments > 1 ? (int*)(w + b_bytes + w_bytes + u_bytes + h_bytes + f_bytes) : nullptr;
+  p.Tinv = w + b_bytes;
+  p.seg_state = pl.segments > 1 ? (float*)(w + b_bytes + t_bytes) : nullptr;
+  p.seg_phi = pl.segments > 1 ? (float*)(w + b_bytes + t_bytes + h_bytes) : nullptr;
+  p.reset = pl.segments > 1 ? (int*)(w + b_bytes + t_bytes + h_bytes + f_bytes) : nullptr;
   p.T = T;
   p.dk = dk;
   p.dv = dv;

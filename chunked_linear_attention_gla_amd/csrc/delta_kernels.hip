@@ -78,21 +78,8 @@ __device__ __forceinline__ void store16(float* dst, int ld, const floatx4& acc, 
   for (int e = 0; e < 4; ++e) dst[(4 * g + e) * ld + r] = sign * acc[e];
 }
 
-// Four operand-dtype elements of one row to global memory (row-major [rows][ld]).
-template <typename T>
-__device__ __forceinline__ void store_row4(T* dst, const floatx4& v) {
-  if constexpr (sizeof(T) == 2) {
-    bf16x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = static_cast<bf16>(v[e]);
-    *reinterpret_cast<bf16x4*>(dst) = w;
-  } else {
-    *reinterpret_cast<floatx4*>(dst) = v;
-  }
-}
-
 // ============================================================================
-// Pass 1: W and Ut of every chunk.
+// Pass 1: Tinv = (I + diag(beta) L)^-1 of every chunk (and its reset flag).
 // ============================================================================
 template <typename T, int DK, int DV>
 struct PrepCfg {
@@ -101,7 +88,6 @@ struct PrepCfg {
   static constexpr int QLD = DK + PAD;
   static constexpr int TLD = 64 + 4;   // A row stride: its 8-byte stores and fragment reads are conflict-free
   static constexpr int QU = 8 * DK / NT;
-  static constexpr int VU = 8 * DV / NT;
   static constexpr int KS = DK / 32;
   // fp32 16x16 blocks: M is read as the left operand of the fp32 products (row r,
   // column 4s + g: conflict-free at a stride of 2 mod 32 words); Tinv is read as both
@@ -112,10 +98,10 @@ struct PrepCfg {
 };
 
 // LDS regions are reused across the phases of the pass: u1 holds the keys for L,
-// then Tinv in fp32 with its scratch blocks, then the right-hand side of one product
-// at a time; u2 holds M, then Tinv in the operand dtype.  At d = 128 that is 40 KB,
-// four workgroups per compute unit (the pass is a chain of short phases between
-// barriers, so the workgroups in flight set its speed).
+// then Tinv in fp32 with its scratch blocks, then W's right-hand side (for the reset
+// test); u2 holds M, then Tinv in the operand dtype.  At d = 128 that is 40 KB, four
+// workgroups per compute unit (the pass is a chain of short phases between barriers,
+// so the workgroups in flight set its speed).
 template <typename T, int DK, int DV>
 struct PrepSmem {
   using C = PrepCfg<T, DK, DV>;
@@ -126,7 +112,6 @@ struct PrepSmem {
       float scr[4][16][C::SLD];
     } t;
     T kb[TokTile<T, DK>::SIZE];   // beta_s e^{b_s} k_s, token-major (W's right-hand side)
-    T vb[TokTile<T, DV>::SIZE];   // beta_s v_s, token-major (Ut's, after W)
   } u1;
   union alignas(16) {             // 16-byte aligned: Tinv's operand copy is written 4 elements at a time
     float mf[64][C::MLD];         // M = diag(beta) L (strictly lower)
@@ -150,19 +135,13 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   const uint32_t t0 = (uint32_t)c * kChunk;
   const uint32_t Tn = (uint32_t)p.T;
   const rsrc_t rk = make_rsrc(static_cast<const T*>(p.k) + bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
-  const rsrc_t rv = make_rsrc(static_cast<const T*>(p.v) + bh * p.T * DV, Tn * DV * (uint32_t)sizeof(T));
 
   // ---- operands: loads first, decays after the barrier that publishes b and beta
-  typename E::Vec8 kv[C::QU], vv[C::VU];
+  typename E::Vec8 kv[C::QU];
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
     kv[m] = E::load8(rk, dl_row(t0 + row, Tn, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T));
-  }
-#pragma unroll
-  for (int m = 0; m < C::VU; ++m) {
-    const int u = tid + m * C::NT, row = u / (DV / 8), c8 = u % (DV / 8);
-    vv[m] = E::load8(rv, dl_row(t0 + row, Tn, DV * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T));
   }
   if (tid < 64) {
     const long long t = (long long)t0 + tid;
@@ -242,8 +221,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     }
     __syncthreads();
   }
-  // operand copy of Tinv (over M, no longer read), zero above the diagonal blocks;
-  // then the right-hand sides of the products, one at a time, over the fp32 Tinv
+  // operand copy of Tinv (over M, no longer read), zero above the diagonal blocks
   // (8 consecutive elements of a row per thread and step: one 16-column block, so one
   // select for all 8; two float4 reads and two 4-element stores)
   for (int e = tid; e < 64 * 8; e += C::NT) {
@@ -256,53 +234,51 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   }
   __syncthreads();
 
-  // ---- W = Tinv (beta e^b K), Ut = Tinv (beta V): wave w owns a quarter of the columns
-  T* Wg = static_cast<T*>(p.W) + bh * p.T * DK;
-  T* Ug = static_cast<T*>(p.U) + bh * p.T * DV;
-  float wmax[4] = {0.f, 0.f, 0.f, 0.f};  // per jb: this lane's max |W| of row 16 jb + r16 (reset test below)
-  const auto product = [&](const T* tile, int ncol, T* dst, int ld, bool is_w) {
-    for (int cb = wave * (ncol / 4); cb < (wave + 1) * (ncol / 4); cb += 16) {
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks <= jb / 2; ++ks)
-          E::mfma(acc, ncol == DK ? TokTile<T, DK>::load(tile, ks * 32, cb, lane)
-                                  : TokTile<T, DV>::load(tile, ks * 32, cb, lane),
-                  E::load_frag(sm.u2.tb + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
-        // acc[e] = X[t0 + 16 jb + r16][cb + 4 g + e]
-        const long long t = (long long)t0 + jb * 16 + r16;
-        if (t < p.T) store_row4<T>(dst + t * ld + cb + 4 * g, acc);
-        if (is_w) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) wmax[jb] = fmaxf(wmax[jb], fabsf(acc[e]));
-        }
-      }
+  // ---- Tinv (operand dtype) of the chunk to the workspace, row-major [64][64]: the
+  //      later passes form W and Ut from it and the chunk's k and v
+  T* Tg = static_cast<T*>(p.Tinv) + ((long long)bh * p.nchunks + c) * (64 * 64);
+  for (int e = tid; e < 64 * 8; e += C::NT) {
+    const int t = e >> 3, s = (e & 7) * 8;
+    if constexpr (sizeof(T) == 2) {
+      const uint2 lo = *reinterpret_cast<const uint2*>(sm.u2.tb + t * C::TLD + s);
+      const uint2 hi = *reinterpret_cast<const uint2*>(sm.u2.tb + t * C::TLD + s + 4);
+      *reinterpret_cast<uint4*>(Tg + t * 64 + s) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+    } else {
+      *reinterpret_cast<float4*>(Tg + t * 64 + s) = *reinterpret_cast<const float4*>(sm.u2.tb + t * C::TLD + s);
+      *reinterpret_cast<float4*>(Tg + t * 64 + s + 4) = *reinterpret_cast<const float4*>(sm.u2.tb + t * C::TLD + s + 4);
     }
-  };
-  // the two right-hand sides take turns in u1
+  }
+  if (!p.reset) return;  // uniform: without segments there is no reset test
+
+  // ---- W = Tinv (beta e^b K) for its row maxima (reset test below): wave w owns a
+  //      quarter of the columns
+  float wmax[4] = {0.f, 0.f, 0.f, 0.f};  // per jb: this lane's max |W| of row 16 jb + r16
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
     TokTile<T, DK>::store8(sm.u1.kb, row, c8 * 8, kv[m], sm.sbeta[row] * exp_e(sm.sb[row]));
   }
   __syncthreads();
-  product(sm.u1.kb, DK, Wg, DK, true);
-  __syncthreads();
+  for (int cb = wave * (DK / 4); cb < (wave + 1) * (DK / 4); cb += 16) {
 #pragma unroll
-  for (int m = 0; m < C::VU; ++m) {
-    const int u = tid + m * C::NT, row = u / (DV / 8), c8 = u % (DV / 8);
-    TokTile<T, DV>::store8(sm.u1.vb, row, c8 * 8, vv[m], sm.sbeta[row]);
+    for (int jb = 0; jb < 4; ++jb) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks <= jb / 2; ++ks)
+        E::mfma(acc, TokTile<T, DK>::load(sm.u1.kb, ks * 32, cb, lane),
+                E::load_frag(sm.u2.tb + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
+      // acc[e] = W[t0 + 16 jb + r16][cb + 4 g + e]
+#pragma unroll
+      for (int e = 0; e < 4; ++e) wmax[jb] = fmaxf(wmax[jb], fabsf(acc[e]));
+    }
   }
-  __syncthreads();
-  product(sm.u1.vb, DV, Ug, DV, false);
   // Reset test of the chunk (only when the plan has segments).  The transition
   // P = e^gamma I - (k e^{gamma-b})^T W has |P[d][e]| <= e^gamma + sum_t |kt_t|max |w_t|max,
   // so |P H| <= 2^13 2^-127 max|H| once every term is below 2^-127 (64 rows, 128 columns):
   // the state after this chunk then does not depend on the state before it, to 2^-114
   // relative.  The terms are compared in log2 (no product underflows on the way);
   // NaN terms fail the comparison, so they never mark a reset.
-  if (p.reset) {
+  {
     bool ok = gam * kLog2e < -127.0f;
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
@@ -320,7 +296,11 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
 }
 
 // ============================================================================
-// Pass 2 (and the segment pre-pass): chunks in order.
+// Pass 2 (and the segment pre-pass): chunks in order.  Each chunk's
+// W = Tinv diag(beta e^b) K and Ut = Tinv diag(beta) V (of the slice) are formed here
+// from the chunk's Tinv (pass 1) and the k and v these passes stage anyway: W by all
+// waves into the -W tile, Ut by each wave for its own columns, straight into the
+// accumulators of U (tokens as rows).
 // ============================================================================
 template <typename T, int DK, int DVS>
 struct DoCfg {
@@ -328,13 +308,18 @@ struct DoCfg {
   static constexpr int NT = 64 * NW;
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int QLD = DK + PAD;
-  static constexpr int TLD = 64 + 4;   // A row stride: its 8-byte stores and fragment reads are conflict-free
+  static constexpr int TLD = 64 + 4;   // row stride of A and Tinv: their 8-byte stores and fragment reads are conflict-free
   static constexpr int QU = 8 * DK / NT;
-  static constexpr int UU = 8 * DVS / NT;      // 16-byte (bf16) Ut pieces per thread
+  static constexpr int VU = 8 * DVS / NT;      // 8-element v pieces per thread
+  static constexpr int TU = 64 * 64 / 8 / NT;  // 8-element Tinv pieces per thread
+  static constexpr int WN = DK / 16 < NW ? DK / 16 : NW;  // waves that form W
+  static constexpr int WC = DK / WN;                      // W columns formed per such wave
   static constexpr int DB = DK / 16;
   static constexpr int KS = DK / 32;
   static_assert(QU >= 1 && QU * NT == 8 * DK, "staging must divide evenly");
-  static_assert(UU >= 1 && UU * NT == 8 * DVS, "Ut staging must divide evenly");
+  static_assert(VU >= 1 && VU * NT == 8 * DVS, "v staging must divide evenly");
+  static_assert(TU >= 1 && TU * NT * 8 == 64 * 64, "Tinv staging must divide evenly");
+  static_assert(WC % 16 == 0, "W columns per wave");
 };
 
 template <typename T, int DK, int DVS>
@@ -344,7 +329,9 @@ struct DoSmem {
   T kh[64 * C::QLD];
   T wn[64 * C::QLD];              // -W
   T kp[2][TokTile<T, DK>::SIZE];  // k e^{gamma - b}, token-major, by chunk parity
-  T ui[TokTile<T, DVS>::SIZE];    // Ut of the slice, token-major
+  T kb[TokTile<T, DK>::SIZE];     // beta e^b k, token-major (W's right-hand side)
+  T vb[TokTile<T, DVS>::SIZE];    // beta v of the slice, token-major (Ut's)
+  T tv[64 * C::TLD];              // Tinv
   T a[64 * C::TLD];
 };
 
@@ -353,67 +340,130 @@ struct DsSmem {
   using C = DoCfg<T, DK, DVS>;
   T wn[64 * C::QLD];
   T kp[TokTile<T, DK>::SIZE];
-  T ui[TokTile<T, DVS>::SIZE];    // Ut of the slice, token-major
+  T kb[TokTile<T, DK>::SIZE];
+  T vb[TokTile<T, DVS>::SIZE];
+  T tv[64 * C::TLD];
   int nonzero[2][C::NW];  // transition half: per wave, whether its columns are nonzero, by chunk parity
 };
 
-// One chunk of (q,) k, W, Ut and b on its way to LDS.  Every operand is loaded in
-// row-contiguous 16-byte pieces; Ut goes to a token-major tile from which each wave
-// reads its columns as accumulators of U (effective_writes).
-template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_U>
+// One chunk of (q,) k, (v,) Tinv, b and beta on its way to LDS, in row-contiguous
+// 16-byte pieces (rows past the end read zeros; b past the end repeats the last value,
+// beta past the end is 0).
+template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_V>
 struct DoStaged {
   using E = Elem<T>;
   using C = DoCfg<T, DK, DVS>;
-  typename E::Vec8 q[LOAD_Q ? C::QU : 1], k[C::QU], w[C::QU], u[LOAD_U ? C::UU : 1];
-  float b;
+  typename E::Vec8 q[LOAD_Q ? C::QU : 1], k[C::QU], v[LOAD_V ? C::VU : 1], ti[C::TU];
+  float b, be;
 
-  // chunk at token t0 of the slice starting at value column col0
-  __device__ __forceinline__ void load(const rsrc_t& rq, const rsrc_t& rk, const rsrc_t& rw, const rsrc_t& ru,
-                                       const rsrc_t& rb, uint32_t Tn, int dv, uint32_t t0, int col0, int tid) {
+  // chunk c (first token t0) of the slice starting at value column col0
+  __device__ __forceinline__ void load(const rsrc_t& rq, const rsrc_t& rk, const rsrc_t& rv, const rsrc_t& rt,
+                                       const rsrc_t& rb, const rsrc_t& rbe, uint32_t Tn, int dv, int c, int col0,
+                                       int tid) {
     const int lane = tid & 63;
-    const uint32_t tb = t0 + lane;
+    const uint32_t t0 = (uint32_t)c * kChunk, tb = t0 + lane;
     b = buf_load4(rb, (tb < Tn ? tb : Tn - 1) * 4u);
+    be = buf_load4(rbe, tb * 4u);  // past the end: out of range, reads 0
 #pragma unroll
     for (int m = 0; m < C::QU; ++m) {
       const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
       const uint32_t off = dl_row(t0 + row, Tn, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T);
       if (LOAD_Q) q[m] = E::load8(rq, off);
       k[m] = E::load8(rk, off);
-      w[m] = E::load8(rw, off);
     }
-    if constexpr (LOAD_U) {
+    if constexpr (LOAD_V) {
 #pragma unroll
-      for (int m = 0; m < C::UU; ++m) {
-        const int v = tid + m * C::NT, row = v / (DVS / 8), c8 = v % (DVS / 8);
-        u[m] = E::load8(ru, dl_row(t0 + row, Tn, (uint32_t)dv * (uint32_t)sizeof(T)) +
+      for (int m = 0; m < C::VU; ++m) {
+        const int u = tid + m * C::NT, row = u / (DVS / 8), c8 = u % (DVS / 8);
+        v[m] = E::load8(rv, dl_row(t0 + row, Tn, (uint32_t)dv * (uint32_t)sizeof(T)) +
                                 (col0 + c8 * 8) * (uint32_t)sizeof(T));
       }
     }
-  }
-
-  // Ut of the chunk into the token-major tile ui
-  __device__ __forceinline__ void store_u(T* ui, int tid) const {
-    if constexpr (LOAD_U) {
 #pragma unroll
-      for (int m = 0; m < C::UU; ++m) {
-        const int v = tid + m * C::NT, row = v / (DVS / 8), c8 = v % (DVS / 8);
-        TokTile<T, DVS>::store8_raw(ui, row, c8 * 8, u[m]);
-      }
+    for (int m = 0; m < C::TU; ++m) {
+      const int u = tid + m * C::NT;  // row u / 8, columns 8 (u % 8)..+7 of chunk c's Tinv
+      ti[m] = E::load8(rt, ((uint32_t)c * 4096u + (uint32_t)u * 8u) * (uint32_t)sizeof(T));
     }
   }
 };
 
-// -W and k e^{gamma - b} of the staged chunk into LDS.
-template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_U>
-__device__ __forceinline__ void stage_w_kp(T* wn, T* kp, const DoStaged<T, DK, DVS, LOAD_Q, LOAD_U>& st,
-                                           const ChunkDecay& cd, int tid) {
-  using E = Elem<T>;
+// The state-side operands of the staged chunk into LDS: k e^{gamma - b} (token-major),
+// beta e^b k (token-major), beta v (token-major, with Ut) and Tinv (row-major).
+template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_V>
+__device__ __forceinline__ void stage_state_side(T* kp, T* kb, T* vb, T* tv,
+                                                 const DoStaged<T, DK, DVS, LOAD_Q, LOAD_V>& st,
+                                                 const ChunkDecay& cd, int tid) {
   using C = DoCfg<T, DK, DVS>;
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
-    E::store8_neg_sw(wn + row * C::QLD + c8 * 8, st.w[m], frag_swap<T>(row));
-    TokTile<T, DK>::store8(kp, row, c8 * 8, st.k[m], exp_e(cd.gam - cd.at(row)));
+    const float br = cd.at(row), ber = __shfl(st.be, row);
+    TokTile<T, DK>::store8(kp, row, c8 * 8, st.k[m], exp_e(cd.gam - br));
+    TokTile<T, DK>::store8(kb, row, c8 * 8, st.k[m], ber * exp_e(br));
+  }
+  if constexpr (LOAD_V) {
+#pragma unroll
+    for (int m = 0; m < C::VU; ++m) {
+      const int u = tid + m * C::NT, row = u / (DVS / 8), c8 = u % (DVS / 8);
+      TokTile<T, DVS>::store8(vb, row, c8 * 8, st.v[m], __shfl(st.be, row));
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < C::TU; ++m) {
+    const int u = tid + m * C::NT, row = u >> 3, c8 = u & 7;
+    T* dst = tv + row * C::TLD + c8 * 8;
+    GLA_CHECK_LDS(dst, 8 * (unsigned)sizeof(T));
+    if constexpr (sizeof(T) == 2) {  // rows are 8-byte aligned at this stride
+      *reinterpret_cast<uint2*>(dst) = make_uint2(st.ti[m].u.x, st.ti[m].u.y);
+      *reinterpret_cast<uint2*>(dst + 4) = make_uint2(st.ti[m].u.z, st.ti[m].u.w);
+    } else {
+      *reinterpret_cast<float4*>(dst) = st.ti[m].a;
+      *reinterpret_cast<float4*>(dst + 4) = st.ti[m].b;
+    }
+  }
+}
+
+// -W = -Tinv (beta e^b K) into the row-major -W tile: wave `wave` < WN forms columns
+// wave * WC .. + WC - 1 (Tinv is zero above its diagonal 16x16 blocks, so token block
+// jb needs K-steps up to jb / 2 only).
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void form_w(T* wn, const T* kb, const T* tv, int wave, int lane) {
+  using E = Elem<T>;
+  using C = DoCfg<T, DK, DVS>;
+  const int r16 = lane & 15, g = lane >> 4;
+  if (wave >= C::WN) return;  // wave-uniform
+#pragma unroll
+  for (int cb = 0; cb < C::WC; cb += 16) {
+    const int col = wave * C::WC + cb;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks <= jb / 2; ++ks)
+        E::mfma(acc, TokTile<T, DK>::load(kb, ks * 32, col, lane), E::load_frag(tv + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
+      // acc[e] = W[16 jb + r16][col + 4 g + e]
+      const int t = jb * 16 + r16;
+      E::store4(wn + t * C::QLD + ((col + 4 * g) ^ frag_swz<T>(t)), -acc[0], -acc[1], -acc[2], -acc[3]);
+    }
+  }
+}
+
+// Ut = Tinv (beta V) for the wave's 16 columns (slice column colr) with tokens as
+// accumulator rows: U[tb][e] = Ut[16 tb + 4 g + e][colr + r16] (zeros without v).
+template <typename T, int DK, int DVS, bool LOAD_V>
+__device__ __forceinline__ void form_ut(floatx4 (&U)[4], const T* vb, const T* tv, int colr, int lane) {
+  using E = Elem<T>;
+  using C = DoCfg<T, DK, DVS>;
+  const int r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int tb = 0; tb < 4; ++tb) {
+    U[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (LOAD_V) {
+#pragma unroll
+      for (int ks = 0; ks <= tb / 2; ++ks)
+        E::mfma(U[tb], E::load_frag(tv + (tb * 16 + r16) * C::TLD, ks * 32 + 4 * g),
+                TokTile<T, DVS>::load(vb, ks * 32, colr, lane));
+    }
   }
 }
 
@@ -421,33 +471,13 @@ __device__ __forceinline__ void stage_w_kp(T* wn, T* kp, const DoStaged<T, DK, D
 // the operand fragments of A.U and the state update.  The accumulators hold tokens as
 // rows -- U[jb][e] = U[16 jb + 4 g + e][colr + r16], from the product with -W as the
 // left operand -- so two stacked 16-token blocks are already a 32-token K-step fragment
-// (the fragment convention of gla_device.h), and Ut enters as their initial value, read
-// from the token-major tile by the transposing read (zeros without Ut).
-template <typename T, int DK, int DVS, bool LOAD_U>
-__device__ __forceinline__ void effective_writes(typename Elem<T>::Frag (&Uf)[2],
-                                                 const typename Elem<T>::Frag (&Sf)[DK / 32], const T* wn,
-                                                 const T* ui, int colr, int lane) {
+// (the fragment convention of gla_device.h); Ut (form_ut) is their initial value.
+template <typename T, int DK, int DVS>
+__device__ __forceinline__ void effective_writes(typename Elem<T>::Frag (&Uf)[2], floatx4 (&U)[4],
+                                                 const typename Elem<T>::Frag (&Sf)[DK / 32], const T* wn, int lane) {
   using E = Elem<T>;
   using C = DoCfg<T, DK, DVS>;
   const int r16 = lane & 15, g = lane >> 4;
-  floatx4 U[4];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    if constexpr (!LOAD_U) {
-      U[2 * ks] = U[2 * ks + 1] = floatx4{0.f, 0.f, 0.f, 0.f};
-    } else if constexpr (sizeof(T) == 2) {
-      const typename E::Frag f = TokTile<T, DVS>::load(ui, ks * 32, colr, lane);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        U[2 * ks][e] = static_cast<float>(f.v[e]);
-        U[2 * ks + 1][e] = static_cast<float>(f.v[4 + e]);
-      }
-    } else {
-      const typename E::Frag f = TokTile<T, DVS>::load(ui, ks * 32, colr, lane);
-      U[2 * ks] = f.lo;
-      U[2 * ks + 1] = f.hi;
-    }
-  }
 #pragma unroll
   for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
@@ -498,9 +528,11 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
   const uint32_t Tn = (uint32_t)p.T;
   const uint32_t es = (uint32_t)sizeof(T);
   const rsrc_t rk = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * es);
-  const rsrc_t rw = make_rsrc(static_cast<const T*>(p.W) + (long long)bh * p.T * DK, Tn * DK * es);
-  const rsrc_t ru = make_rsrc(static_cast<const T*>(p.U) + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * es);
+  const rsrc_t rv = make_rsrc(static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * es);
+  const rsrc_t rt = make_rsrc(static_cast<const T*>(p.Tinv) + (long long)bh * p.nchunks * 4096,
+                              (uint32_t)p.nchunks * 4096u * es);
   const rsrc_t rb = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+  const rsrc_t rbe = make_rsrc(p.beta + (long long)bh * p.T, Tn * 4u);
 
   floatx4 S[C::DB];
 #pragma unroll
@@ -525,18 +557,21 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
   }
 
   DoStaged<T, DK, NCOL, false, !PHI> st;
-  if (c_first < c_end) st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_first * kChunk, col0, tid);
+  if (c_first < c_end) st.load(rk, rk, rv, rt, rb, rbe, Tn, p.dv, c_first, col0, tid);
   for (int c = c_first; c < c_end; ++c) {
     const ChunkDecay cd(st.b);
-    stage_w_kp<T, DK, NCOL, false, !PHI>(sm.wn, sm.kp, st, cd, tid);
-    st.store_u(sm.ui, tid);
-    st.load(rk, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, col0, tid);
+    stage_state_side<T, DK, NCOL, false, !PHI>(sm.kp, sm.kb, sm.vb, sm.tv, st, cd, tid);
+    st.load(rk, rk, rv, rt, rb, rbe, Tn, p.dv, min(c + 1, c_end - 1), col0, tid);
+    __syncthreads();
+    form_w<T, DK, NCOL>(sm.wn, sm.kb, sm.tv, wave, lane);
+    floatx4 U[4];
+    form_ut<T, DK, NCOL, !PHI>(U, sm.vb, sm.tv, wave * 16, lane);
     __syncthreads();
     typename E::Frag Sf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
     typename E::Frag Uf[2];
-    effective_writes<T, DK, NCOL, !PHI>(Uf, Sf, sm.wn, sm.ui, wave * 16, lane);
+    effective_writes<T, DK, NCOL>(Uf, U, Sf, sm.wn, lane);
     delta_state_update<T, DK, NCOL>(S, Uf, sm.kp, exp_e(cd.gam), lane);
     if constexpr (PHI) {
       // Once this workgroup's columns of the running transition product are all
@@ -590,9 +625,11 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
   const uint32_t es = (uint32_t)sizeof(T);
   const rsrc_t rq = make_rsrc(static_cast<const T*>(p.q) + (long long)bh * p.T * DK, Tn * DK * es);
   const rsrc_t rk = make_rsrc(static_cast<const T*>(p.k) + (long long)bh * p.T * DK, Tn * DK * es);
-  const rsrc_t rw = make_rsrc(static_cast<const T*>(p.W) + (long long)bh * p.T * DK, Tn * DK * es);
-  const rsrc_t ru = make_rsrc(static_cast<const T*>(p.U) + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * es);
+  const rsrc_t rv = make_rsrc(static_cast<const T*>(p.v) + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * es);
+  const rsrc_t rt = make_rsrc(static_cast<const T*>(p.Tinv) + (long long)bh * p.nchunks * 4096,
+                              (uint32_t)p.nchunks * 4096u * es);
   const rsrc_t rb = make_rsrc(p.b + (long long)bh * p.T, Tn * 4u);
+  const rsrc_t rbe = make_rsrc(p.beta + (long long)bh * p.T, Tn * 4u);
   const rsrc_t ro = make_rsrc(p.o + (long long)bh * p.T * p.dv, Tn * (uint32_t)p.dv * 4u);
 
   // ---- initial state: S0 (or zero), then S <- Phi_p S + H_p over the earlier
@@ -634,7 +671,7 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
   }
 
   DoStaged<T, DK, DVS, true, true> st;
-  if (c_begin < c_end) st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)c_begin * kChunk, col0, tid);
+  if (c_begin < c_end) st.load(rq, rk, rv, rt, rb, rbe, Tn, p.dv, c_begin, col0, tid);
   for (int c = c_begin; c < c_end; ++c) {
     const uint32_t t0 = (uint32_t)c * kChunk;
     const ChunkDecay cd(st.b);
@@ -648,13 +685,13 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       E::store8_scaled_sw(sm.kh + row * C::QLD + c8 * 8, st.k[m], exp_e(r - br), sw);
     }
     T* const kp = sm.kp[(c - c_begin) & 1];
-    stage_w_kp<T, DK, DVS, true, true>(sm.wn, kp, st, cd, tid);
-    st.store_u(sm.ui, tid);
+    stage_state_side<T, DK, DVS, true, true>(kp, sm.kb, sm.vb, sm.tv, st, cd, tid);
     // ---- (2) prefetch chunk c + 1 (the last iteration re-reads its own chunk)
-    st.load(rq, rk, rw, ru, rb, Tn, p.dv, (uint32_t)min(c + 1, c_end - 1) * kChunk, col0, tid);
+    st.load(rq, rk, rv, rt, rb, rbe, Tn, p.dv, min(c + 1, c_end - 1), col0, tid);
     __syncthreads();
 
-    // ---- (3) A over the 10 causal tiles
+    // ---- (3) A over the 10 causal tiles; -W (every wave its columns); Ut of the wave's
+    //      columns; o_inter = e^{r_u} Qh S_0
 #pragma unroll
     for (int t = 0; t < 10; ++t) {
       if (t % C::NW != wave) continue;  // wave-uniform
@@ -670,28 +707,28 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       for (int e = 0; e < 4; ++e) vals[e] = (jb != ib || 4 * g + e <= r16) ? acc[e] * f : 0.0f;
       E::store4(sm.a + (jb * 16 + r16) * C::TLD + ib * 16 + 4 * g, vals[0], vals[1], vals[2], vals[3]);
     }
-
-    // ---- (4) o_inter = e^{r_u} Qh S_0 and U = Ut - W S_0 for the wave's columns
+    form_w<T, DK, DVS>(sm.wn, sm.kb, sm.tv, wave, lane);
+    floatx4 U[4];
+    form_ut<T, DK, DVS, true>(U, sm.vb, sm.tv, wave * 16, lane);
+    typename E::Frag Sf[C::KS];
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
     floatx4 O[4];
-    typename E::Frag Uf[2];
-    {
-      typename E::Frag Sf[C::KS];
 #pragma unroll
-      for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
+    for (int jb = 0; jb < 4; ++jb) {
+      O[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        O[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-          E::mfma(O[jb], Sf[ks], E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
-        if (jb > 0) O[jb] *= exp_e(cd.r(jb));
-      }
-      effective_writes<T, DK, DVS, true>(Uf, Sf, sm.wn, sm.ui, wave * 16, lane);
+      for (int ks = 0; ks < C::KS; ++ks)
+        E::mfma(O[jb], Sf[ks], E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
+      if (jb > 0) O[jb] *= exp_e(cd.r(jb));
     }
     __syncthreads();
 
-    // ---- (5) o += A U; S_c = e^gamma S_0 + (k e^{gamma - b})^T U
+    // ---- (4) U = Ut - W S_0 (every wave's -W columns are in); o += A U;
+    //      S_c = e^gamma S_0 + (k e^{gamma - b})^T U
     {
+      typename E::Frag Uf[2];
+      effective_writes<T, DK, DVS>(Uf, U, Sf, sm.wn, lane);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
@@ -702,9 +739,9 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       for (int jb = 0; jb < 4; ++jb)
         buf_store16(ro, dl_row(t0 + jb * 16 + r16, Tn, (uint32_t)p.dv * 4u) + (wcol + 4 * g) * 4u, O[jb]);
     }
-    // No barrier here: the next chunk's staging writes Qh, Kh, -W and Ut, last read in
-    // (3) and (4) before this chunk's second barrier, and the other k e^{gamma - b}
-    // buffer; A is rewritten only after its first barrier.
+    // No barrier here: the next chunk's staging writes Qh, Kh, beta e^b k, beta v and
+    // Tinv, last read in (3) before this chunk's second barrier, and the other
+    // k e^{gamma - b} buffer; -W and A are rewritten only after its first barrier.
   }
   if (seg == p.segments - 1) {
 #pragma unroll

@@ -125,8 +125,8 @@ struct DeltaParams {
   const float* S0;        // [BH][dk][dv] or nullptr
   float* o;               // [BH][T][dv]
   float* ST;              // [BH][dk][dv]
-  void* W;                // [BH][T][dk] operand dtype: Tinv diag(beta e^b) K per chunk
-  void* U;                // [BH][T][dv] operand dtype: Tinv diag(beta) V per chunk
+  void* Tinv;             // [BH][nchunks][64][64] operand dtype: (I + diag(beta) L)^-1 of each
+                          //    chunk, zero above its diagonal 16x16 blocks
   float* seg_state;       // [BH][segments-1][dk][dv] local final state of each segment
   float* seg_phi;         // [BH][segments-1][dk][dk] state transition of each segment
   int* reset;             // [BH][nchunks] 1 where the chunk's transition e^gamma I - (k e^{gamma-b})^T W

@@ -275,7 +275,8 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
  *   product of the chunk transitions e^gamma I - (k e^{gamma-b})^T W, dk x dk).
  * Built: bf16 with dk, dv in {64, 128} and slices of 32, 64 or 128 columns; fp32
  * with dk = dv = 64 and slices of 32 or 64.  Others: GLA_ERR_UNSUPPORTED or
- * GLA_ERR_PLAN.  The workspace holds b, the per-chunk W, U (operand dtype), the
+ * GLA_ERR_PLAN.  The workspace holds b, each chunk's Tinv (64 x 64, operand dtype;
+ * the passes after the solve form W and U~ from it and the chunk's k and v), the
  * segment maps and one reset flag per chunk; workspace == NULL returns its size.
  * Errors and validation as gla_chunk_fwd.
  * Segment pre-pass: a chunk whose transition scales any incoming state by less than

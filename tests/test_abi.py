@@ -354,10 +354,11 @@ def test_delta_validation_and_workspace_query(lib):
     assert dl() == OK                       # explicit plan: size query without a device
     es = 2
     align = lambda b: (b + 255) // 256 * 256
-    assert n.value == align(2 * 100 * 4) + align(2 * 100 * 64 * es) + align(2 * 100 * 64 * es)
+    # b per token, and one 64 x 64 Tinv per chunk (2 heads x 2 chunks)
+    assert n.value == align(2 * 100 * 4) + align(2 * 2 * 64 * 64 * es)
     # two segments add one local state and one transition per head, and a reset flag per chunk
     assert dl(plan=(2, 1)) == OK
-    assert n.value == (align(2 * 100 * 4) + 2 * align(2 * 100 * 64 * es) + align(2 * 64 * 64 * 4)
+    assert n.value == (align(2 * 100 * 4) + align(2 * 2 * 64 * 64 * es) + align(2 * 64 * 64 * 4)
                        + align(2 * 64 * 64 * 4) + align(2 * 2 * 4))
     need = n.value
     assert dl(plan=(2, 1), ws=0x10000000, beta=None) == NULL
