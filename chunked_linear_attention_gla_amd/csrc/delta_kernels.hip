@@ -28,15 +28,17 @@
 //   delta_prep_kernel   one workgroup per (head, chunk), all chunks in parallel:
 //                       L, Tinv (fp32, 16x16 blocks: forward substitution on the
 //                       diagonal blocks, matrix-core products for the others),
-//                       W and Ut, written to the workspace in the operand dtype.
+//                       written to the workspace in the operand dtype, and with
+//                       segments each chunk's reset flag (below).
 //   delta_segment_kernel for sequence segments: the affine map S_end = Phi S_start
 //                       + H of every segment but the last (Phi = prod of the chunk
 //                       transitions e^gamma I - (k e^{gamma-b})^T W, run as dk extra
 //                       columns from the identity with no writes).
 //   delta_output_kernel one workgroup per (head, slice of value columns, segment),
-//                       chunks in order from the folded start state: U = Ut - W S_0
-//                       on the matrix cores, then o and the state update as in the
-//                       linear-attention output pass.
+//                       chunks in order from the folded start state: W and Ut from
+//                       Tinv and the staged k and v, U = Ut - W S_0 on the matrix
+//                       cores, then o and the state update as in the linear-attention
+//                       output pass.
 #include "chunk_common.h"
 
 namespace gla {
@@ -86,40 +88,36 @@ struct PrepCfg {
   static constexpr int NT = 256;
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int QLD = DK + PAD;
-  static constexpr int TLD = 64 + 4;   // A row stride: its 8-byte stores and fragment reads are conflict-free
   static constexpr int QU = 8 * DK / NT;
   static constexpr int KS = DK / 32;
-  // fp32 16x16 blocks: M is read as the left operand of the fp32 products (row r,
-  // column 4s + g: conflict-free at a stride of 2 mod 32 words); Tinv is read as both
-  // operands and written by store16, for which 68 is the best single stride
-  static constexpr int MLD = 66;
-  static constexpr int FLD = 68;
-  static constexpr int SLD = 20;  // scratch blocks: written by store16, read as the right operand
+  static constexpr int KL = DK / 8;   // lanes that stage one key row
+  // M and Tinv are held as their 10 lower 16x16 blocks (block (I, J), J <= I, at
+  // index I (I + 1) / 2 + J), 16 rows each at a padded stride: M's 18 puts the left-
+  // operand reads of the fp32 block products (row r, column 4 s + g) on banks 18 r + g,
+  // distinct within each half-wave; Tinv's 20 does the same for store16 (banks 16 g + r).
+  static constexpr int MLD = 18;
+  static constexpr int FLD = 20;
 };
 
-// LDS regions are reused across the phases of the pass: u1 holds the keys for L,
-// then Tinv in fp32 with its scratch blocks, then W's right-hand side (for the reset
-// test); u2 holds M, then Tinv in the operand dtype.  At d = 128 that is 40 KB, four
-// workgroups per compute unit (the pass is a chain of short phases between barriers,
-// so the workgroups in flight set its speed).
+__device__ __forceinline__ constexpr int lblk(int I, int J) { return I * (I + 1) / 2 + J; }
+
+// LDS: the staged keys, then (over them) Tinv in fp32; M; per-row factors.  At d = 128
+// that is 29 KB, five workgroups per compute unit (the pass is a chain of short phases
+// between barriers, so the workgroups in flight set its speed).  M's diagonal block I,
+// read only by the forward substitution, is wave I's scratch block afterwards.
 template <typename T, int DK, int DV>
 struct PrepSmem {
   using C = PrepCfg<T, DK, DV>;
   union {
-    T kr[64 * C::QLD];            // k as loaded
-    struct {
-      float tf[64][C::FLD];       // Tinv (fp32)
-      float scr[4][16][C::SLD];
-    } t;
-    T kb[TokTile<T, DK>::SIZE];   // beta_s e^{b_s} k_s, token-major (W's right-hand side)
+    T kr[64 * C::QLD];               // k as loaded
+    float tf[10][16 * C::FLD];       // Tinv (fp32), lower blocks
   } u1;
-  union alignas(16) {             // 16-byte aligned: Tinv's operand copy is written 4 elements at a time
-    float mf[64][C::MLD];         // M = diag(beta) L (strictly lower)
-    T tb[64 * C::TLD];            // Tinv in the operand dtype
-  } u2;
-  float sb[64];                   // b; at the end, the waves' reset votes
+  float mf[10][16 * C::MLD];         // M = diag(beta) L, lower blocks (zero on and above the diagonal)
+  float sb[64];                      // b
   float sbeta[64];
-  float lk[64];                   // log2 of max_d |k_t[d] e^{gamma - b_t}|, per row
+  float lk[64];                      // log2 of max_d |k_t[d] e^{gamma - b_t}|, per row
+  float fac[64];                     // beta_s e^{b_s} max_d |k_s[d]|, per row
+  int vote[4];
 };
 
 template <typename T, int DK, int DV>
@@ -134,13 +132,14 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   const int c = (int)(blockIdx.x - bh * p.nchunks);
   const uint32_t t0 = (uint32_t)c * kChunk;
   const uint32_t Tn = (uint32_t)p.T;
+  const bool test = p.reset != nullptr;  // uniform: the reset test only runs for plans with segments
   const rsrc_t rk = make_rsrc(static_cast<const T*>(p.k) + bh * p.T * DK, Tn * DK * (uint32_t)sizeof(T));
 
   // ---- operands: loads first, decays after the barrier that publishes b and beta
   typename E::Vec8 kv[C::QU];
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
-    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
+    const int u = tid + m * C::NT, row = u / C::KL, c8 = u % C::KL;
     kv[m] = E::load8(rk, dl_row(t0 + row, Tn, DK * (uint32_t)sizeof(T)) + c8 * 8 * (uint32_t)sizeof(T));
   }
   if (tid < 64) {
@@ -154,17 +153,21 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   const float gam = sm.sb[last];  // the chunk's total log-decay
 #pragma unroll
   for (int m = 0; m < C::QU; ++m) {
-    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
-    const float br = sm.sb[row];
+    const int u = tid + m * C::NT, row = u / C::KL, c8 = u % C::KL;
     E::store8_scaled_sw(sm.u1.kr + row * C::QLD + c8 * 8, kv[m], 1.0f, frag_swap<T>(row));
-    // reset test, key side: log2 max_d |k_row[d]| + (gamma - b_row) log2 e (the threads of a
-    // row are DK / 8 consecutive lanes)
-    float mx = 0.0f;
+    if (test) {
+      // max_d |k_row[d]| over the row's KL consecutive lanes: the key side of the reset
+      // test and the row's factor in the bound on |W| below
+      float mx = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(E::get(kv[m], e)));
-#pragma unroll
-    for (int off = DK / 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-    if (c8 == 0) sm.lk[row] = __builtin_amdgcn_logf(mx) + (gam - br) * kLog2e;
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(E::get(kv[m], e)));
+      mx = group_max<C::KL>(mx);
+      if (c8 == 0) {
+        const float br = sm.sb[row];
+        sm.lk[row] = __builtin_amdgcn_logf(mx) + (gam - br) * kLog2e;
+        sm.fac[row] = sm.sbeta[row] * exp_e(br) * mx;
+      }
+    }
   }
   __syncthreads();
 
@@ -174,7 +177,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
 #pragma unroll
   for (int t = 0; t < 10; ++t) {
     if (t % 4 != wave) continue;  // wave-uniform
-    const int jb = tri_j(t), ib = tri_i(t);
+    const int jb = tri_j(t), ib = tri_i(t);  // block row, block column; t = lblk(jb, ib)
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
@@ -186,113 +189,95 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int sc = ib * 16 + 4 * g + e;
-      sm.u2.mf[tr][sc] = (jb != ib || 4 * g + e < r16) ? acc[e] * (exp_e(bt - sm.sb[sc]) * bet) : 0.0f;
+      sm.mf[t][r16 * C::MLD + 4 * g + e] =
+          (jb != ib || 4 * g + e < r16) ? acc[e] * (exp_e(bt - sm.sb[sc]) * bet) : 0.0f;
     }
   }
   __syncthreads();
 
-  // ---- Tinv = (I + M)^-1, diagonal blocks by forward substitution (lane = column)
+  // ---- diagonal blocks of Tinv = (I + M)^-1 by forward substitution, wave I taking
+  //      block I (lane = column): each x_q, once final, is subtracted from the later
+  //      rows at once, so the dependent chain is 15 steps long
   if (lane < 16) {
-    const int o = 16 * wave, j = lane;
+    const float* mb = &sm.mf[lblk(wave, wave)][0];
     float x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float s = (i == j) ? 1.0f : 0.0f;
+    for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.0f : 0.0f;
 #pragma unroll
-      for (int q = 0; q < i; ++q) s -= sm.u2.mf[o + i][o + q] * x[q];
-      x[i] = s;
-    }
+    for (int q = 0; q < 15; ++q)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.u1.t.tf[o + i][o + j] = x[i];
+      for (int i = q + 1; i < 16; ++i) x[i] = fmaf(-mb[i * C::MLD + q], x[q], x[i]);
+    float* tb = &sm.u1.tf[lblk(wave, wave)][0];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) tb[i * C::FLD + lane] = x[i];
   }
   __syncthreads();
-  // block row I, column J < I:  X_IJ = -D_I sum_{J <= K < I} M_IK X_KJ, by distance I - J
-#pragma unroll
-  for (int dist = 1; dist <= 3; ++dist) {
-    const int I = wave, J = wave - dist;
-    if (J >= 0) {  // wave-uniform
+  // ---- blocks below the diagonal, wave J taking block column J from the top:
+  //      X_IJ = -D_I sum_{J <= K < I} M_IK X_KJ needs only blocks of its own column and
+  //      the diagonal blocks D, so the column needs no barrier until it is complete
+  {
+    const int J = wave;
+    float* scr = &sm.mf[lblk(J, J)][0];
+    for (int I = J + 1; I < 4; ++I) {  // wave-uniform
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int K = J; K < I; ++K)
-        mm16(acc, &sm.u2.mf[16 * I][16 * K], C::MLD, &sm.u1.t.tf[16 * K][16 * J], C::FLD, lane);
-      store16(&sm.u1.t.scr[I][0][0], C::SLD, acc, 1.0f, lane);
+        mm16(acc, &sm.mf[lblk(I, K)][0], C::MLD, &sm.u1.tf[lblk(K, J)][0], C::FLD, lane);
+      store16(scr, C::MLD, acc, 1.0f, lane);
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
-      mm16(x, &sm.u1.t.tf[16 * I][16 * I], C::FLD, &sm.u1.t.scr[I][0][0], C::SLD, lane);
-      store16(&sm.u1.t.tf[16 * I][16 * J], C::FLD, x, -1.0f, lane);
+      mm16(x, &sm.u1.tf[lblk(I, I)][0], C::FLD, scr, C::MLD, lane);
+      store16(&sm.u1.tf[lblk(I, J)][0], C::FLD, x, -1.0f, lane);
     }
-    __syncthreads();
-  }
-  // operand copy of Tinv (over M, no longer read), zero above the diagonal blocks
-  // (8 consecutive elements of a row per thread and step: one 16-column block, so one
-  // select for all 8; two float4 reads and two 4-element stores)
-  for (int e = tid; e < 64 * 8; e += C::NT) {
-    const int t = e >> 3, s = (e & 7) * 8;
-    const bool keep = (s >> 4) <= (t >> 4);
-    const float4 lo = keep ? *reinterpret_cast<const float4*>(&sm.u1.t.tf[t][s]) : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 hi = keep ? *reinterpret_cast<const float4*>(&sm.u1.t.tf[t][s + 4]) : make_float4(0.f, 0.f, 0.f, 0.f);
-    E::store4(sm.u2.tb + t * C::TLD + s, lo.x, lo.y, lo.z, lo.w);
-    E::store4(sm.u2.tb + t * C::TLD + s + 4, hi.x, hi.y, hi.z, hi.w);
   }
   __syncthreads();
 
-  // ---- Tinv (operand dtype) of the chunk to the workspace, row-major [64][64]: the
-  //      later passes form W and Ut from it and the chunk's k and v
+  // ---- Tinv in the operand dtype to the workspace, row-major [64][64] and zero above
+  //      the diagonal blocks (the later passes form W and Ut from it and the chunk's k
+  //      and v); 8 consecutive elements of a row per thread and step.  With the reset
+  //      test, the same values bound each row of W = Tinv diag(beta e^b) K:
+  //      max_d |W[t][d]| <= sum_s |Tinv[t][s]| beta_s e^{b_s} max_d |k_s[d]|.
   T* Tg = static_cast<T*>(p.Tinv) + ((long long)bh * p.nchunks + c) * (64 * 64);
-  for (int e = tid; e < 64 * 8; e += C::NT) {
-    const int t = e >> 3, s = (e & 7) * 8;
+  bool ok = gam * kLog2e < -127.0f;
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int e = tid + m * C::NT, t = e >> 3, s = (e & 7) * 8;
+    const int I = t >> 4, J = s >> 4;
+    const bool keep = J <= I;
+    const float* src = &sm.u1.tf[lblk(I, keep ? J : I)][(t & 15) * C::FLD + (s & 15)];
+    const float4 lo = *reinterpret_cast<const float4*>(src);
+    const float4 hi = *reinterpret_cast<const float4*>(src + 4);
+    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = keep ? v[k] : 0.0f;
     if constexpr (sizeof(T) == 2) {
-      const uint2 lo = *reinterpret_cast<const uint2*>(sm.u2.tb + t * C::TLD + s);
-      const uint2 hi = *reinterpret_cast<const uint2*>(sm.u2.tb + t * C::TLD + s + 4);
-      *reinterpret_cast<uint4*>(Tg + t * 64 + s) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      typename E::Frag o;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o.v[k] = E::cvt(v[k]);
+      *reinterpret_cast<bf16x8*>(Tg + t * 64 + s) = o.v;
     } else {
-      *reinterpret_cast<float4*>(Tg + t * 64 + s) = *reinterpret_cast<const float4*>(sm.u2.tb + t * C::TLD + s);
-      *reinterpret_cast<float4*>(Tg + t * 64 + s + 4) = *reinterpret_cast<const float4*>(sm.u2.tb + t * C::TLD + s + 4);
+      *reinterpret_cast<float4*>(Tg + t * 64 + s) = make_float4(v[0], v[1], v[2], v[3]);
+      *reinterpret_cast<float4*>(Tg + t * 64 + s + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    }
+    if (test) {
+      const float4 f0 = *reinterpret_cast<const float4*>(&sm.fac[s]);
+      const float4 f1 = *reinterpret_cast<const float4*>(&sm.fac[s + 4]);
+      float wb = fabsf(v[0]) * f0.x + fabsf(v[1]) * f0.y + fabsf(v[2]) * f0.z + fabsf(v[3]) * f0.w +
+                 fabsf(v[4]) * f1.x + fabsf(v[5]) * f1.y + fabsf(v[6]) * f1.z + fabsf(v[7]) * f1.w;
+      wb = group_sum<8>(wb);  // the row's 8 threads are consecutive lanes
+      ok = ok && (sm.lk[t] + __builtin_amdgcn_logf(wb) < -128.0f);
     }
   }
-  if (!p.reset) return;  // uniform: without segments there is no reset test
-
-  // ---- W = Tinv (beta e^b K) for its row maxima (reset test below): wave w owns a
-  //      quarter of the columns
-  float wmax[4] = {0.f, 0.f, 0.f, 0.f};  // per jb: this lane's max |W| of row 16 jb + r16
-#pragma unroll
-  for (int m = 0; m < C::QU; ++m) {
-    const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
-    TokTile<T, DK>::store8(sm.u1.kb, row, c8 * 8, kv[m], sm.sbeta[row] * exp_e(sm.sb[row]));
-  }
+  if (!test) return;  // uniform
+  // Reset test of the chunk.  The transition P = e^gamma I - (k e^{gamma-b})^T W has
+  // |P[d][e]| <= e^gamma + sum_t |kt_t|max |w_t|max, so |P H| <= 2^13 2^-127 max|H| once
+  // every term is below 2^-127 (64 rows, 128 columns): the state after this chunk then
+  // does not depend on the state before it, to 2^-114 relative.  The terms are compared
+  // in log2 (no product underflows on the way) against 2^-128, which leaves a factor 2
+  // for the rounding of Tinv, k and the factors in the operand dtype; NaN terms fail
+  // the comparison, so they never mark a reset.
+  const unsigned long long no = __ballot(!ok);
+  if (lane == 0) sm.vote[wave] = no == 0ull;
   __syncthreads();
-  for (int cb = wave * (DK / 4); cb < (wave + 1) * (DK / 4); cb += 16) {
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks <= jb / 2; ++ks)
-        E::mfma(acc, TokTile<T, DK>::load(sm.u1.kb, ks * 32, cb, lane),
-                E::load_frag(sm.u2.tb + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
-      // acc[e] = W[t0 + 16 jb + r16][cb + 4 g + e]
-#pragma unroll
-      for (int e = 0; e < 4; ++e) wmax[jb] = fmaxf(wmax[jb], fabsf(acc[e]));
-    }
-  }
-  // Reset test of the chunk (only when the plan has segments).  The transition
-  // P = e^gamma I - (k e^{gamma-b})^T W has |P[d][e]| <= e^gamma + sum_t |kt_t|max |w_t|max,
-  // so |P H| <= 2^13 2^-127 max|H| once every term is below 2^-127 (64 rows, 128 columns):
-  // the state after this chunk then does not depend on the state before it, to 2^-114
-  // relative.  The terms are compared in log2 (no product underflows on the way);
-  // NaN terms fail the comparison, so they never mark a reset.
-  {
-    bool ok = gam * kLog2e < -127.0f;
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      float mx = wmax[jb];
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      ok = ok && (sm.lk[jb * 16 + r16] + __builtin_amdgcn_logf(mx) < -127.0f);
-    }
-    // sb is not read after the staging above: it takes the waves' votes
-    if (lane == 0) sm.sb[wave] = __ballot(!ok) == 0ull ? 1.0f : 0.0f;
-    __syncthreads();
-    if (tid == 0)
-      p.reset[bh * p.nchunks + c] = (sm.sb[0] != 0.0f && sm.sb[1] != 0.0f && sm.sb[2] != 0.0f && sm.sb[3] != 0.0f);
-  }
+  if (tid == 0) p.reset[bh * p.nchunks + c] = sm.vote[0] & sm.vote[1] & sm.vote[2] & sm.vote[3];
 }
 
 // ============================================================================

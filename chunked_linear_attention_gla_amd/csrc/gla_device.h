@@ -110,6 +110,29 @@ __device__ __forceinline__ float dpp_or_zero(float v) {
                                                                0xF, 0xF, true));
 }
 
+// Maximum and sum over aligned groups of N consecutive lanes (N = 2, 4, 8 or 16), left
+// in every lane of the group: lane swaps within quads (xor 1, xor 2), then the mirror
+// images within 8 and 16 lanes, each of which maps the group's two halves onto each
+// other.  Every lane of the wavefront must be active.
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group of 2, 4, 8 or 16 lanes");
+  v = fmaxf(v, dpp_or_zero<0xB1>(v));                          // quad_perm [1,0,3,2]
+  if constexpr (N >= 4) v = fmaxf(v, dpp_or_zero<0x4E>(v));    // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v = fmaxf(v, dpp_or_zero<0x141>(v));   // row_half_mirror
+  if constexpr (N >= 16) v = fmaxf(v, dpp_or_zero<0x140>(v));  // row_mirror
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(N == 2 || N == 4 || N == 8 || N == 16, "group of 2, 4, 8 or 16 lanes");
+  v += dpp_or_zero<0xB1>(v);
+  if constexpr (N >= 4) v += dpp_or_zero<0x4E>(v);
+  if constexpr (N >= 8) v += dpp_or_zero<0x141>(v);
+  if constexpr (N >= 16) v += dpp_or_zero<0x140>(v);
+  return v;
+}
+
 // Inclusive prefix sum over the 64 lanes of the wavefront: DPP row shifts inside each
 // 16-lane row, then the three row totals read across lanes.  Every kernel that forms
 // the chunk-local cumulative log-decay uses this one routine, so they all get the
