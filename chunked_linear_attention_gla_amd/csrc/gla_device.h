@@ -133,6 +133,40 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// v_permlane16_swap_b32 with both of its results: the odd 16-lane rows of a trade
+// places with the even rows of b, so a = (a0, b0, a2, b2) and b = (a1, b1, a3, b3) by
+// row.  Written out because this compiler's builtin hands back its first result for
+// either index; the s_nop gives the two wait states the instruction needs after a
+// VALU write of its operands.
+__device__ __forceinline__ void permlane16_swap_pair(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Exclusive prefix sum of v over the lanes l - S, l - 2S, ... (S = STRIDE in 1, 2, 4, 8
+// or 16: lanes that hold the same item of earlier groups of S lanes).  Inside each
+// 16-lane row: DPP row shifts for the prefix and rotations for the row total (both
+// keep a lane's position modulo S); across the four rows: the row-pair and half-wave
+// swap permutes of gfx950, which hand every lane the totals of the rows before its
+// own at the same position.
+template <int STRIDE>
+__device__ __forceinline__ float strided_exclusive_scan(float v, int lane) {
+  static_assert(STRIDE == 1 || STRIDE == 2 || STRIDE == 4 || STRIDE == 8 || STRIDE == 16, "stride");
+  float incl = v, rt = v;
+  if constexpr (STRIDE <= 1) { incl += dpp_or_zero<0x111>(incl); rt += dpp_or_zero<0x121>(rt); }  // row_shr / row_ror 1
+  if constexpr (STRIDE <= 2) { incl += dpp_or_zero<0x112>(incl); rt += dpp_or_zero<0x122>(rt); }
+  if constexpr (STRIDE <= 4) { incl += dpp_or_zero<0x114>(incl); rt += dpp_or_zero<0x124>(rt); }
+  if constexpr (STRIDE <= 8) { incl += dpp_or_zero<0x118>(incl); rt += dpp_or_zero<0x128>(rt); }
+  // Across rows (R_r: the row totals at the lane's position): one row-pair swap of rt
+  // with itself gives every lane the totals of both rows of its pair, a half-wave swap
+  // moves the sum of rows 0 and 1 into the high half of a zero register.
+  uint32_t ev = __builtin_bit_cast(uint32_t, rt), od = ev;
+  permlane16_swap_pair(ev, od);
+  const float even = __builtin_bit_cast(float, ev), odd = __builtin_bit_cast(float, od);
+  const float low = __builtin_bit_cast(
+      float, __builtin_amdgcn_permlane32_swap(0u, __builtin_bit_cast(uint32_t, even + odd), false, false)[0]);
+  return (incl - v) + ((lane & 16) ? even : 0.0f) + low;  // rows 0..3: + 0, R0, R0 + R1, R2 + R0 + R1
+}
+
 // Inclusive prefix sum over the 64 lanes of the wavefront: DPP row shifts inside each
 // 16-lane row, then the three row totals read across lanes.  Every kernel that forms
 // the chunk-local cumulative log-decay uses this one routine, so they all get the

@@ -193,16 +193,10 @@ __device__ __forceinline__ void tile_log_decay(PcLam<T, DK, DVS>& lam,
     }
   }
   // exclusive prefix of the lane totals over the row groups of the same columns
+  // (lane = rg * C8W + column group)
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float tot = lam.v[C::R - 1][e];
-    float incl = tot;
-#pragma unroll
-    for (int off = C::C8W; off < 64; off <<= 1) {
-      const float y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    const float ex = incl - tot;
+    const float ex = strided_exclusive_scan<C::C8W>(lam.v[C::R - 1][e], lane);
 #pragma unroll
     for (int m = 0; m < C::R; ++m) lam.v[m][e] += ex;
   }
