@@ -34,7 +34,11 @@ namespace {
 
 template <typename T, int DK, int DV>
 struct DxCfg {
-  static constexpr int NW = DK / 32;            // waves, one per 32 state columns (over dk)
+  // 16-column blocks of state columns per wave: two for bf16 (four waves at d = 128; eight
+  // waves of one block each measured 8 % slower), one for fp32 (whose two-block waves
+  // spill registers)
+  static constexpr int NB = sizeof(T) == 2 ? 2 : 1;
+  static constexpr int NW = DK / (16 * NB);     // waves, one per 16 NB state columns (over dk)
   static constexpr int NT = 64 * NW;
   static constexpr int PAD = Elem<T>::kPad;
   static constexpr int LDK = DK + PAD;          // row stride of q, k in LDS
@@ -168,7 +172,7 @@ __device__ __forceinline__ typename Elem<T>::Frag scale_frag(typename Elem<T>::F
   return f;
 }
 
-// One workgroup per chunk c of one head; wave w owns 32 state columns (over dk).  The
+// One workgroup per chunk c of one head; wave w owns 16 NB state columns (over dk).  The
 // forward pass stored S^T before each even chunk and the reversed pass D^T after each odd
 // chunk (and after the last chunk), one state per pair of chunks (2m, 2m + 1).  The state
 // missing for chunk c is one chunk step from the stored one of its pair:
@@ -251,25 +255,26 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
     svv.load(rv, t0, tid);
     sg.load(rg, t0, tid);
   }
-  const long long sidx = (((bh * ((nchunks + 1) / 2) + (c >> 1)) * (DK / 32) + w) * 2) * (long long)X::DB * 256;
+  // the pair's stored states: 16-column block n of the state at ((n DB + db) 64 + lane) 4
+  const long long sidx = (bh * ((nchunks + 1) / 2) + (c >> 1)) * (DK / 16) * (long long)X::DB * 256;
   using RS = StateRaw<T>;
-  typename RS::V sv[2][X::DB], ev[2][X::DB];
+  typename RS::V sv[X::NB][X::DB], ev[X::NB][X::DB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < X::NB; ++nb)
 #pragma unroll
     for (int db = 0; db < X::DB; ++db) {
-      sv[nb][db] = RS::load(Sfw + sidx + ((nb * X::DB + db) * 64 + lane) * 4);
-      ev[nb][db] = RS::load(Sbw + sidx + ((nb * X::DB + db) * 64 + lane) * 4);
+      sv[nb][db] = RS::load(Sfw + sidx + (((X::NB * w + nb) * X::DB + db) * 64 + lane) * 4);
+      ev[nb][db] = RS::load(Sbw + sidx + (((X::NB * w + nb) * X::DB + db) * 64 + lane) * 4);
     }
   if (tid < 64) sm.b[tid] = bval;
   else if (tid < 128) sm.bn[tid - 64] = bval;
 
   // st <- f0 st + sum over the neighbour's tokens s of fexp(s) ta_s tb_s^T: ta the tile
   // over dv (v or dO), tb the tile over dk (k or q), in fp32 and back to the stored form
-  const auto rebuild = [&](typename RS::V (&st)[2][X::DB], const T* ta, const T* tb, float f0, auto&& fexp) {
-    floatx4 acc[2][X::DB];
+  const auto rebuild = [&](typename RS::V (&st)[X::NB][X::DB], const T* ta, const T* tb, float f0, auto&& fexp) {
+    floatx4 acc[X::NB][X::DB];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < X::NB; ++nb)
 #pragma unroll
       for (int db = 0; db < X::DB; ++db) acc[nb][db] = RS::f32(st[nb][db]) * f0;
 #pragma unroll
@@ -277,18 +282,18 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
       float fac[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) fac[e] = fexp(ks * 32 + 16 * (e >> 2) + 4 * g + (e & 3));
-      typename E::Frag fb[2];
+      typename E::Frag fb[X::NB];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) fb[nb] = tok_frag<T, X::LDK>(tb, ks * 32, 32 * w + 16 * nb, lane);
+      for (int nb = 0; nb < X::NB; ++nb) fb[nb] = tok_frag<T, X::LDK>(tb, ks * 32, 16 * (X::NB * w + nb), lane);
 #pragma unroll
       for (int db = 0; db < X::DB; ++db) {
         const typename E::Frag fa = scale_frag<T>(tok_frag<T, X::LDV>(ta, ks * 32, db * 16, lane), fac);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) E::mfma(acc[nb][db], fa, fb[nb]);
+        for (int nb = 0; nb < X::NB; ++nb) E::mfma(acc[nb][db], fa, fb[nb]);
       }
     }
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < X::NB; ++nb)
 #pragma unroll
       for (int db = 0; db < X::DB; ++db) st[nb][db] = RS::raw(acc[nb][db]);
   };
@@ -344,7 +349,7 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
   }
   float z = 0.0f;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < X::NB; ++nb)
 #pragma unroll
     for (int db = 0; db < X::DB; ++db) {
       const floatx4 a4 = RS::f32(sv[nb][db]), b4 = RS::f32(ev[nb][db]);
@@ -358,9 +363,9 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
 
   // ---- (2) and (3): dO_j^T S^T and v_i^T D^T on the matrix cores, dotted with q_j, k_i
   {
-    typename E::Frag Sf[2][X::KS], Ef[2][X::KS];
+    typename E::Frag Sf[X::NB][X::KS], Ef[X::NB][X::KS];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < X::NB; ++nb)
 #pragma unroll
       for (int ks = 0; ks < X::KS; ++ks) {
         Sf[nb][ks] = RS::frag(sv[nb][2 * ks], sv[nb][2 * ks + 1]);
@@ -368,26 +373,26 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
       }
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
-      floatx4 M[2], N[2];
+      floatx4 M[X::NB], N[X::NB];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) M[nb] = N[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int nb = 0; nb < X::NB; ++nb) M[nb] = N[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < X::KS; ++ks) {
         const typename E::Frag gf = E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + 4 * g);
         const typename E::Frag vf = E::load_frag(sm.v + (jb * 16 + r16) * X::LDV, ks * 32 + 4 * g);
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < X::NB; ++nb) {
           E::mfma(M[nb], Sf[nb][ks], gf);  // M[nb][e] = (dO_j^T S^T)[n], j = 16 jb + r16
           E::mfma(N[nb], Ef[nb][ks], vf);  // N[nb][e] = (v_j^T D^T)[n]
         }
       }
-      // n = 32 w + 16 nb + 4 g + e
+      // n = 16 (NB w + nb) + 4 g + e
       float rp = 0.0f, up = 0.0f;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < X::NB; ++nb)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int n = 32 * w + 16 * nb + 4 * g + e;
+          const int n = 16 * (X::NB * w + nb) + 4 * g + e;
           rp += M[nb][e] * E::to_f32(sm.q[(jb * 16 + r16) * X::LDK + n]);
           up += N[nb][e] * E::to_f32(sm.k[(jb * 16 + r16) * X::LDK + n]);
         }
