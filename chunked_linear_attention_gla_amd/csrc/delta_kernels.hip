@@ -101,18 +101,18 @@ struct PrepCfg {
 
 __device__ __forceinline__ constexpr int lblk(int I, int J) { return I * (I + 1) / 2 + J; }
 
-// LDS: the staged keys, then (over them) Tinv in fp32; M; per-row factors.  At d = 128
-// that is 29 KB, five workgroups per compute unit (the pass is a chain of short phases
-// between barriers, so the workgroups in flight set its speed).  M's diagonal block I,
-// read only by the forward substitution, is wave I's scratch block afterwards.
+// LDS: the staged keys, then (over them) Tinv's blocks below the diagonal in fp32; M,
+// whose diagonal blocks become Tinv's once inverted; per-row factors.  At d = 128 that
+// is 29 KB, five workgroups per compute unit (the pass is a chain of short phases
+// between barriers, so the workgroups in flight set its speed).
 template <typename T, int DK, int DV>
 struct PrepSmem {
   using C = PrepCfg<T, DK, DV>;
   union {
     T kr[64 * C::QLD];               // k as loaded
-    float tf[10][16 * C::FLD];       // Tinv (fp32), lower blocks
+    float tf[10][16 * C::FLD];       // Tinv (fp32), blocks below the diagonal
   } u1;
-  float mf[10][16 * C::MLD];         // M = diag(beta) L, lower blocks (zero on and above the diagonal)
+  float mf[10][16 * C::MLD];         // M = diag(beta) L, lower blocks; diagonal ones then D_I of Tinv
   float sb[64];                      // b
   float sbeta[64];
   float lk[64];                      // log2 of max_d |k_t[d] e^{gamma - b_t}|, per row
@@ -173,11 +173,10 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
 
   // ---- M = diag(beta) L over the 10 causal tiles, strictly below the diagonal:
   //      k_t . k_s on the matrix cores, then the decay e^{b_t - b_s} (<= 1 where kept;
-  //      the masked entries are selected away, never multiplied)
-#pragma unroll
-  for (int t = 0; t < 10; ++t) {
-    if (t % 4 != wave) continue;  // wave-uniform
-    const int jb = tri_j(t), ib = tri_i(t);  // block row, block column; t = lblk(jb, ib)
+  //      the masked entries are selected away, never multiplied).  Wave I forms its
+  //      diagonal tile first and inverts it at once (below); the six tiles below the
+  //      diagonal follow, two for waves 0 and 1, one for waves 2 and 3.
+  const auto m_tile = [&](int jb, int ib) {  // block row, block column
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
@@ -186,20 +185,20 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     // acc[e]: row t = 16 jb + r16, column s = 16 ib + 4 g + e
     const int tr = jb * 16 + r16;
     const float bt = sm.sb[tr], bet = sm.sbeta[tr];
+    float* mb = &sm.mf[lblk(jb, ib)][0];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int sc = ib * 16 + 4 * g + e;
-      sm.mf[t][r16 * C::MLD + 4 * g + e] =
-          (jb != ib || 4 * g + e < r16) ? acc[e] * (exp_e(bt - sm.sb[sc]) * bet) : 0.0f;
+      mb[r16 * C::MLD + 4 * g + e] = (jb != ib || 4 * g + e < r16) ? acc[e] * (exp_e(bt - sm.sb[sc]) * bet) : 0.0f;
     }
-  }
-  __syncthreads();
-
-  // ---- diagonal blocks of Tinv = (I + M)^-1 by forward substitution, wave I taking
-  //      block I (lane = column): each x_q, once final, is subtracted from the later
-  //      rows at once, so the dependent chain is 15 steps long
+  };
+  m_tile(wave, wave);
+  // ---- diagonal block D_I of Tinv = (I + M)^-1 by forward substitution (lane =
+  //      column; right-looking: each x_q, once final, is subtracted from the later rows
+  //      at once, so the dependent chain is 15 steps).  D_I replaces M's diagonal block,
+  //      which nothing reads afterwards; the wave's own LDS writes and reads stay in order.
   if (lane < 16) {
-    const float* mb = &sm.mf[lblk(wave, wave)][0];
+    float* mb = &sm.mf[lblk(wave, wave)][0];
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.0f : 0.0f;
@@ -207,25 +206,32 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     for (int q = 0; q < 15; ++q)
 #pragma unroll
       for (int i = q + 1; i < 16; ++i) x[i] = fmaf(-mb[i * C::MLD + q], x[q], x[i]);
-    float* tb = &sm.u1.tf[lblk(wave, wave)][0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) tb[i * C::FLD + lane] = x[i];
+    for (int i = 0; i < 16; ++i) mb[i * C::MLD + lane] = x[i];
   }
+  if (wave == 0) { m_tile(1, 0); m_tile(3, 0); }
+  else if (wave == 1) { m_tile(2, 0); m_tile(3, 1); }
+  else if (wave == 2) m_tile(2, 1);
+  else m_tile(3, 2);
   __syncthreads();
   // ---- blocks below the diagonal, wave J taking block column J from the top:
   //      X_IJ = -D_I sum_{J <= K < I} M_IK X_KJ needs only blocks of its own column and
-  //      the diagonal blocks D, so the column needs no barrier until it is complete
+  //      the diagonal blocks D, so the column needs no barrier until it is complete.
+  //      X_JJ = D_J sits in M's diagonal block (stride MLD), the others in tf (over the
+  //      keys, no longer read); the block being formed is its own scratch (mm16 reads
+  //      all of it before the store).
   {
     const int J = wave;
-    float* scr = &sm.mf[lblk(J, J)][0];
     for (int I = J + 1; I < 4; ++I) {  // wave-uniform
+      float* dst = &sm.u1.tf[lblk(I, J)][0];
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int K = J; K < I; ++K)
+      mm16(acc, &sm.mf[lblk(I, J)][0], C::MLD, &sm.mf[lblk(J, J)][0], C::MLD, lane);
+      for (int K = J + 1; K < I; ++K)
         mm16(acc, &sm.mf[lblk(I, K)][0], C::MLD, &sm.u1.tf[lblk(K, J)][0], C::FLD, lane);
-      store16(scr, C::MLD, acc, 1.0f, lane);
+      store16(dst, C::FLD, acc, 1.0f, lane);
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
-      mm16(x, &sm.u1.tf[lblk(I, I)][0], C::FLD, scr, C::MLD, lane);
-      store16(&sm.u1.tf[lblk(I, J)][0], C::FLD, x, -1.0f, lane);
+      mm16(x, &sm.mf[lblk(I, I)][0], C::MLD, dst, C::FLD, lane);
+      store16(dst, C::FLD, x, -1.0f, lane);
     }
   }
   __syncthreads();
@@ -242,10 +248,17 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     const int e = tid + m * C::NT, t = e >> 3, s = (e & 7) * 8;
     const int I = t >> 4, J = s >> 4;
     const bool keep = J <= I;
-    const float* src = &sm.u1.tf[lblk(I, keep ? J : I)][(t & 15) * C::FLD + (s & 15)];
-    const float4 lo = *reinterpret_cast<const float4*>(src);
-    const float4 hi = *reinterpret_cast<const float4*>(src + 4);
-    float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    // diagonal blocks in M's place (stride MLD), the others in tf; 8-byte reads (a row
+    // of M's blocks starts at a multiple of 8 bytes only)
+    const float* src = J < I ? &sm.u1.tf[lblk(I, J)][(t & 15) * C::FLD + (s & 15)]
+                             : &sm.mf[lblk(I, I)][(t & 15) * C::MLD + (s & 15)];
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; k += 2) {
+      const float2 pr = *reinterpret_cast<const float2*>(src + k);
+      v[k] = pr.x;
+      v[k + 1] = pr.y;
+    }
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = keep ? v[k] : 0.0f;
     if constexpr (sizeof(T) == 2) {

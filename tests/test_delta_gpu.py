@@ -193,3 +193,38 @@ def test_repeat_calls_are_bitwise_identical():
     o2, S2 = gla.chunk_fwd_delta(*args, plan=gla.Plan(4, 1))
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+@pytest.mark.parametrize("beta_one", [False, True])
+def test_reset_flags_mark_only_negligible_transitions(beta_one):
+    """The per-chunk pass's reset flags, read from the workspace (b, the Tinv of every
+    chunk, the segment maps, then one int32 flag per chunk): every planted strong-decay
+    chunk (x = +8) is flagged and no weakly decaying chunk is; and for each flagged chunk
+    the fp64 oracle's transition over it -- the delta rule run over the chunk alone with
+    v = 0 from S_0 = I, i.e. the state map S_start -> S_end -- has entries below 2^-114."""
+    w, inp = make(64 * 40 + 11, H=2, x_mean=-6.0, seed=23)
+    planted = (7, 18, 19, 33)
+    for ch in planted:
+        inp["x"][:, :, ch * 64:(ch + 1) * 64] = 8.0
+    if beta_one:
+        inp["beta"].fill_(1.0)
+    BH, T, d, P, es = 2, w.T, 128, 4, 2
+    nc = (T + 63) // 64
+    al = lambda n: (n + 255) // 256 * 256
+    off = al(BH * T * 4) + al(BH * nc * 64 * 64 * es) + al(BH * (P - 1) * d * d * 4) * 2
+    ws = torch.zeros(off + al(BH * nc * 4), dtype=torch.uint8, device=device())
+    gla.chunk_fwd_delta(inp["q"], inp["k"], inp["v"], inp["x"], inp["beta"], inp["S0"], plan=gla.Plan(P, 1),
+                        workspace=ws)
+    torch.cuda.synchronize()
+    flags = ws[off:off + BH * nc * 4].view(torch.int32).reshape(BH, nc).cpu().numpy()
+    expect = np.zeros((BH, nc), dtype=np.int32)
+    expect[:, list(planted)] = 1
+    assert (flags == expect).all(), np.argwhere(flags != expect)
+    for h in range(BH):
+        for c in planted:
+            sl = slice(c * 64, (c + 1) * 64)
+            kc = gin.to_numpy_bits(inp["k"][0, h, sl])
+            zero = np.zeros_like(kc)
+            _, trans = oracle.forward_delta(zero, kc, zero, inp["x"][0, h, sl].cpu().numpy(),
+                                            inp["beta"][0, h, sl].cpu().numpy(), np.eye(d))
+            assert np.abs(trans).max() < 2.0 ** -114, (h, c)
