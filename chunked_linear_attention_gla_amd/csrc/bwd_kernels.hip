@@ -79,6 +79,16 @@ __device__ __forceinline__ float gate_slope(float x) {
   return -5.0f * sg * (1.0f - sg);                      // d/dx -5 sigmoid(x)
 }
 
+// The four chunk tiles are read both as MFMA fragments (ds_read2_b64: one 8-byte piece
+// from each of 16 rows, cols c and c + 16) and transposed (ds_read_tr16_b64).  At a row
+// stride of 136 elements rows r and r + 8 of a fragment read share banks; rows with bit
+// 3 set therefore hold each 16-byte group with its 8-byte halves swapped: element
+// column c of row r is at c ^ dx_swz(r) (bf16 only).
+template <typename T>
+__device__ __forceinline__ int dx_swz(int row) {
+  return sizeof(T) == 2 ? (row & 8) >> 1 : 0;
+}
+
 // 64 rows of a per-head [T][ncol] tensor, 8-element units spread over the threads:
 // all loads are issued first (load), the LDS stores come after (store), so a
 // workgroup has its whole chunk in flight at once.  Rows past the end read zeros.
@@ -98,7 +108,13 @@ struct RowStage {
 #pragma unroll
     for (int m = 0; m < U; ++m) {
       const int u = tid + m * NT, row = u / (NCOL / 8), c8 = u % (NCOL / 8);
-      Elem<T>::store8_raw(dst + row * LD + c8 * 8, r[m]);
+      if constexpr (sizeof(T) == 2) {
+        const uint4 u = r[m].u;
+        GLA_CHECK_LDS(dst + row * LD + c8 * 8, 16);
+        *reinterpret_cast<uint4*>(dst + row * LD + c8 * 8) = dx_swz<T>(row) ? make_uint4(u.z, u.w, u.x, u.y) : u;
+      } else {
+        Elem<T>::store8_raw(dst + row * LD + c8 * 8, r[m]);
+      }
     }
   }
 };
@@ -137,11 +153,23 @@ template <> struct StateRaw<float> {
 };
 
 // Operand fragment whose contraction index is the token (kappa order), for column
-// c0 + r16 of a row-major [64][LD] tile.
+// c0 + r16 of a row-major [64][LD] tile (bf16: transposing reads of the swizzled rows).
 template <typename T, int LD>
 __device__ __forceinline__ typename Elem<T>::Frag tok_frag(const T* tile, int k0, int c0, int lane) {
   if constexpr (sizeof(T) == 2) {
-    return TokTile<T, 16, LD>::load(tile, k0, c0, lane);
+    typedef short shortx4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+    const int s = lane & 15, g = lane >> 4;
+    const int row = k0 + 4 * g + (s >> 2);  // rows row and row + 16 share bit 3
+    const T* p0 = tile + row * LD + c0 + ((4 * (s & 3)) ^ dx_swz<T>(row));
+    const T* p1 = p0 + 16 * LD;
+    GLA_CHECK_LDS(p0, 8);
+    GLA_CHECK_LDS(p1, 8);
+    const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p0));
+    const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(p1));
+    typename Elem<T>::Frag f;
+    f.v = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    return f;
   } else {
     const int g = lane >> 4, r = lane & 15;
     GLA_CHECK_LDS(tile + (k0 + 4 * g) * LD + c0 + r, 4);
@@ -378,8 +406,8 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
       for (int nb = 0; nb < X::NB; ++nb) M[nb] = N[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < X::KS; ++ks) {
-        const typename E::Frag gf = E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + 4 * g);
-        const typename E::Frag vf = E::load_frag(sm.v + (jb * 16 + r16) * X::LDV, ks * 32 + 4 * g);
+        const typename E::Frag gf = E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ dx_swz<T>(r16)));
+        const typename E::Frag vf = E::load_frag(sm.v + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ dx_swz<T>(r16)));
 #pragma unroll
         for (int nb = 0; nb < X::NB; ++nb) {
           E::mfma(M[nb], Sf[nb][ks], gf);  // M[nb][e] = (dO_j^T S^T)[n], j = 16 jb + r16
@@ -393,8 +421,8 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int n = 16 * (X::NB * w + nb) + 4 * g + e;
-          rp += M[nb][e] * E::to_f32(sm.q[(jb * 16 + r16) * X::LDK + n]);
-          up += N[nb][e] * E::to_f32(sm.k[(jb * 16 + r16) * X::LDK + n]);
+          rp += M[nb][e] * E::to_f32(sm.q[(jb * 16 + r16) * X::LDK + (n ^ dx_swz<T>(r16))]);
+          up += N[nb][e] * E::to_f32(sm.k[(jb * 16 + r16) * X::LDK + (n ^ dx_swz<T>(r16))]);
         }
       rp += __shfl_xor(rp, 16);
       rp += __shfl_xor(rp, 32);
@@ -416,12 +444,12 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
     floatx4 qk = {0.f, 0.f, 0.f, 0.f}, gv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks)
-      E::mfma(qk, E::load_frag(sm.k + (ib * 16 + r16) * X::LDK, ks * 32 + 4 * g),
-              E::load_frag(sm.q + (jb * 16 + r16) * X::LDK, ks * 32 + 4 * g));
+      E::mfma(qk, E::load_frag(sm.k + (ib * 16 + r16) * X::LDK, ks * 32 + ((4 * g) ^ dx_swz<T>(r16))),
+              E::load_frag(sm.q + (jb * 16 + r16) * X::LDK, ks * 32 + ((4 * g) ^ dx_swz<T>(r16))));
 #pragma unroll
     for (int ks = 0; ks < DV / 32; ++ks)
-      E::mfma(gv, E::load_frag(sm.v + (ib * 16 + r16) * X::LDV, ks * 32 + 4 * g),
-              E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + 4 * g));
+      E::mfma(gv, E::load_frag(sm.v + (ib * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ dx_swz<T>(r16))),
+              E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ dx_swz<T>(r16))));
     // lane (g, r16), element e: j = 16 jb + r16, s = 16 ib + 4 g + e
     const float bj = sm.b[jb * 16 + r16];
     float pe[4], row = 0.0f;
