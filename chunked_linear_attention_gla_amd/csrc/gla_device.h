@@ -286,6 +286,15 @@ template <> struct Elem<bf16> {
     if (swap) o = __builtin_shufflevector(o, o, 4, 5, 6, 7, 0, 1, 2, 3);
     *reinterpret_cast<bf16x8*>(dst) = o;
   }
+  // 8 fp32 values rounded to bf16, as one 16-byte LDS write (halves swapped when `swap`)
+  __device__ static __forceinline__ void store8_f32_sw(bf16* dst, const float (&x)[8], bool swap) {
+    GLA_CHECK_LDS(dst, 16);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = cvt(x[e]);
+    if (swap) o = __builtin_shufflevector(o, o, 4, 5, 6, 7, 0, 1, 2, 3);
+    *reinterpret_cast<bf16x8*>(dst) = o;
+  }
   __device__ static __forceinline__ void store8_neg_sw(bf16* dst, const Vec8& v, bool swap) {
     GLA_CHECK_LDS(dst, 16);
     constexpr uint32_t m = 0x80008000u;
@@ -377,6 +386,11 @@ template <> struct Elem<float> {
   __device__ static __forceinline__ void store8_scaled_sw(float* dst, const Vec8& v, float s, bool) {
     store8_scaled(dst, v, s);
   }
+  __device__ static __forceinline__ void store8_f32_sw(float* dst, const float (&x)[8], bool) {
+    GLA_CHECK_LDS(dst, 32);
+    *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(dst + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
   __device__ static __forceinline__ void store8_neg_sw(float* dst, const Vec8& v, bool) { store8_neg(dst, v); }
   __device__ static __forceinline__ void store8_vscaled_sw(float* dst, const Vec8& v, const float (&s)[8], bool) {
     store8_vscaled(dst, v, s);
@@ -447,6 +461,9 @@ template <int NCOL, int LDX> struct TokTile<bf16, NCOL, LDX> {
   __device__ static __forceinline__ void store8_v(bf16* t, int row, int col, const E::Vec8& v, const float (&s)[8]) {
     E::store8_vscaled(t + row * LD + col, v, s);
   }
+  __device__ static __forceinline__ void store8_f32(bf16* t, int row, int col, const float (&x)[8]) {
+    E::store8_f32_sw(t + row * LD + col, x, false);
+  }
   __device__ static __forceinline__ E::Frag load(const bf16* t, int k0, int c0, int lane) {
     typedef short shortx4 __attribute__((ext_vector_type(4)));
     typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
@@ -484,6 +501,12 @@ template <int NCOL, int LDX> struct TokTile<float, NCOL, LDX> {
     GLA_CHECK_LDS(t + (col + 7) * LD + row, 4);
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = E::get(v, e) * s[e];
+  }
+  __device__ static __forceinline__ void store8_f32(float* t, int row, int col, const float (&x)[8]) {
+    GLA_CHECK_LDS(t + col * LD + row, 4);
+    GLA_CHECK_LDS(t + (col + 7) * LD + row, 4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[(col + e) * LD + row] = x[e];
   }
   __device__ static __forceinline__ E::Frag load(const float* t, int k0, int c0, int lane) {
     return E::load_frag(t + (c0 + (lane & 15)) * LD, k0 + 4 * (lane >> 4));

@@ -220,6 +220,31 @@ __device__ __forceinline__ void read_tau(float (&tv)[4][8], const float (*tau)[D
   }
 }
 
+// The key-side chain of the wave's tile: row i starts at k_i e^{-b_i + r_tile} (lam is
+// b - r_tile) and is multiplied by e^{tau_u} for u = tile, ..., 3 (tile u's total per
+// channel), passing through k_i e^{r_u - b_i} (the key operand of query tile u) and
+// ending at k_i e^{gamma - b_i}, the state-side operand.  The values only shrink, so a
+// step underflows only where the true weight does.  Both kernels run this same
+// sequence of fp32 operations, so their state-side operands are bit-identical.
+template <typename T, int DK, int DVS, bool LOAD_Q, int R>
+__device__ __forceinline__ void key_chain_start(float (&kf)[R][8], const PcStaged<T, DK, DVS, LOAD_Q>& st,
+                                                const PcLam<T, DK, DVS>& lam) {
+#pragma unroll
+  for (int m = 0; m < R; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kf[m][e] = Elem<T>::get(st.k[m], e) * exp2_hw(-lam.v[m][e]);
+}
+template <int R>
+__device__ __forceinline__ void key_chain_step(float (&kf)[R][8], const float (&tau)[8]) {
+  float step[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) step[e] = exp2_hw(tau[e]);
+#pragma unroll
+  for (int m = 0; m < R; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) kf[m][e] *= step[e];
+}
+
 // k_i e^{gamma - b_i} (token-major) for the wave's tile and, from the lanes of tile 0's
 // waves and row group 0 (which together cover every channel once), e^{gamma}.
 template <typename T, int DK, int DVS, bool LOAD_Q>
@@ -238,13 +263,13 @@ __device__ __forceinline__ void stage_state_side(T* kp, float* eg, const PcStage
       if (u >= pl.tile) s += tv[u][e];
     G[e] = s;
   }
+  float kf[C::R][8];
+  key_chain_start<T, DK, DVS, LOAD_Q, C::R>(kf, st, lam);
 #pragma unroll
-  for (int m = 0; m < C::R; ++m) {
-    float f[8];
+  for (int u = 0; u < 4; ++u)
+    if (u >= pl.tile) key_chain_step<C::R>(kf, tv[u]);  // wave-uniform
 #pragma unroll
-    for (int e = 0; e < 8; ++e) f[e] = exp2_hw(G[e] - lam.v[m][e]);
-    TokTile<T, DK>::store8_v(kp, 16 * pl.tile + rg * C::R + m, c8 * 8, st.k[m], f);
-  }
+  for (int m = 0; m < C::R; ++m) TokTile<T, DK>::store8_f32(kp, 16 * pl.tile + rg * C::R + m, c8 * 8, kf[m]);
   if (pl.tile == 0 && rg == 0) {
     float f[8];
 #pragma unroll
@@ -491,13 +516,12 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
     PcLam<T, DK, DVS> lam;
     float (*tau)[DK] = sm.tau[(c - c_begin) & 1];
     tile_log_decay<T, DK, DVS, true>(lam, st, tau, t0, Tn, p.gate, wave, lane);
-    float fq[C::R][8];  // e^{b_j - r_u}
+    float qf[C::R][8];  // q_j e^{b_j - r_u} in fp32 (kept for q e^{b} below)
 #pragma unroll
     for (int m = 0; m < C::R; ++m) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) fq[m][e] = exp2_hw(lam.v[m][e]);
-      E::store8_vscaled_sw(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], fq[m],
-                           pc_swz<T>(rg * C::R + m) != 0);
+      for (int e = 0; e < 8; ++e) qf[m][e] = E::get(st.q[m], e) * exp2_hw(lam.v[m][e]);
+      E::store8_f32_sw(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, qf[m], pc_swz<T>(rg * C::R + m) != 0);
     }
     __syncthreads();
 
@@ -517,40 +541,27 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         }
 #pragma unroll
         for (int m = 0; m < C::R; ++m) {
-          float f[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = fq[m][e] * er[e];
-          E::store8_vscaled_sw(sm.qe + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, st.q[m], f,
-                               pc_swz<T>(rg * C::R + m) != 0);
+          for (int e = 0; e < 8; ++e) qf[m][e] *= er[e];
+          E::store8_f32_sw(sm.qe + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, qf[m], pc_swz<T>(rg * C::R + m) != 0);
         }
       }
-      // Key tile `tile` serves the query tiles u >= tile as K^(u) = k e^{r_u - b}, and the
-      // state update as k e^{gamma - b}.  Along that chain the factor of row i goes
-      // e^{r_tile - b_i} -> e^{r_{tile+1} - b_i} -> ... -> e^{gamma - b_i}, each step a
-      // multiply by e^{tau_u} (tile u's total, one per channel): the factors only shrink,
-      // so a step underflows only where the true weight does.
+      // Key tile `tile` serves the query tiles u >= tile as K^(u) = k e^{r_u - b} and the
+      // state update as k e^{gamma - b}: the key chain (above), with each K^(u) stored on
+      // the way.
       float kf[C::R][8];
-#pragma unroll
-      for (int m = 0; m < C::R; ++m)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kf[m][e] = exp2_hw(-lam.v[m][e]);
+      key_chain_start<T, DK, DVS, true, C::R>(kf, st, lam);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         if (u < tile) continue;  // wave-uniform
         T* kt = sm.kt + (u * (u + 1) / 2 + tile) * 16 * C::QLD;
 #pragma unroll
         for (int m = 0; m < C::R; ++m)
-          E::store8_vscaled_sw(kt + (rg * C::R + m) * C::QLD + c8 * 8, st.k[m], kf[m], pc_swz<T>(rg * C::R + m) != 0);
-        float step[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) step[e] = exp2_hw(tv[u][e]);
-#pragma unroll
-        for (int m = 0; m < C::R; ++m)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) kf[m][e] *= step[e];
+          E::store8_f32_sw(kt + (rg * C::R + m) * C::QLD + c8 * 8, kf[m], pc_swz<T>(rg * C::R + m) != 0);
+        key_chain_step<C::R>(kf, tv[u]);
       }
 #pragma unroll
-      for (int m = 0; m < C::R; ++m) TokTile<T, DK>::store8_v(sm.kp, 16 * tile + rg * C::R + m, c8 * 8, st.k[m], kf[m]);
+      for (int m = 0; m < C::R; ++m) TokTile<T, DK>::store8_f32(sm.kp, 16 * tile + rg * C::R + m, c8 * 8, kf[m]);
       if (tile == 0 && rg == 0) {  // e^{gamma}: these lanes cover every channel once
         float f[8];
 #pragma unroll
