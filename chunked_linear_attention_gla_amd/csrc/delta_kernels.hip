@@ -101,18 +101,21 @@ struct PrepCfg {
 
 __device__ __forceinline__ constexpr int lblk(int I, int J) { return I * (I + 1) / 2 + J; }
 
-// LDS: the staged keys, then (over them) Tinv's blocks below the diagonal in fp32; M,
-// whose diagonal blocks become Tinv's once inverted; per-row factors.  At d = 128 that
-// is 29 KB, five workgroups per compute unit (the pass is a chain of short phases
-// between barriers, so the workgroups in flight set its speed).
+// LDS: the staged keys, then (over them, once M is formed in registers) M and Tinv's
+// blocks below the diagonal in fp32 (M's diagonal blocks become Tinv's once inverted);
+// per-row factors.  At d = 128 that is 25 KB, six workgroups per compute unit where
+// the registers allow (the pass is a chain of short phases between barriers, so the
+// workgroups in flight set its speed).
 template <typename T, int DK, int DV>
 struct PrepSmem {
   using C = PrepCfg<T, DK, DV>;
   union {
     T kr[64 * C::QLD];               // k as loaded
-    float tf[10][16 * C::FLD];       // Tinv (fp32), blocks below the diagonal
+    struct {
+      float tf[10][16 * C::FLD];     // Tinv (fp32), blocks below the diagonal
+      float mf[10][16 * C::MLD];     // M = diag(beta) L, lower blocks; diagonal ones then D_I of Tinv
+    } t;
   } u1;
-  float mf[10][16 * C::MLD];         // M = diag(beta) L, lower blocks; diagonal ones then D_I of Tinv
   float sb[64];                      // b
   float sbeta[64];
   float lk[64];                      // log2 of max_d |k_t[d] e^{gamma - b_t}|, per row
@@ -174,9 +177,9 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   // ---- M = diag(beta) L over the 10 causal tiles, strictly below the diagonal:
   //      k_t . k_s on the matrix cores, then the decay e^{b_t - b_s} (<= 1 where kept;
   //      the masked entries are selected away, never multiplied).  Wave I forms its
-  //      diagonal tile first and inverts it at once (below); the six tiles below the
-  //      diagonal follow, two for waves 0 and 1, one for waves 2 and 3.
-  const auto m_tile = [&](int jb, int ib) {  // block row, block column
+  //      diagonal tile and one or two of the six below the diagonal in registers; they
+  //      go to LDS over the keys once every wave is done with those.
+  const auto m_tile = [&](int jb, int ib, floatx4& out) {  // block row, block column
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks)
@@ -185,20 +188,34 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     // acc[e]: row t = 16 jb + r16, column s = 16 ib + 4 g + e
     const int tr = jb * 16 + r16;
     const float bt = sm.sb[tr], bet = sm.sbeta[tr];
-    float* mb = &sm.mf[lblk(jb, ib)][0];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int sc = ib * 16 + 4 * g + e;
-      mb[r16 * C::MLD + 4 * g + e] = (jb != ib || 4 * g + e < r16) ? acc[e] * (exp_e(bt - sm.sb[sc]) * bet) : 0.0f;
+      out[e] = (jb != ib || 4 * g + e < r16) ? acc[e] * (exp_e(bt - sm.sb[sc]) * bet) : 0.0f;
     }
   };
-  m_tile(wave, wave);
+  const auto m_store = [&](int jb, int ib, const floatx4& v) {
+    float* mb = &sm.u1.t.mf[lblk(jb, ib)][0];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) mb[r16 * C::MLD + 4 * g + e] = v[e];
+  };
+  // wave I: (I, I), then (1, 0) and (3, 0) | (2, 0) and (3, 1) | (2, 1) | (3, 2)
+  const int ja = wave == 2 ? 2 : 3, ia = wave == 0 ? 0 : wave == 1 ? 1 : wave == 2 ? 1 : 2;
+  const int jb2 = wave == 0 ? 1 : 2;  // second tile of waves 0 and 1: (1, 0), (2, 0)
+  floatx4 md, m1, m2;
+  m_tile(wave, wave, md);
+  m_tile(ja, ia, m1);
+  if (wave < 2) m_tile(jb2, 0, m2);  // wave-uniform
+  __syncthreads();  // the keys are read; M goes over them
+  m_store(wave, wave, md);
+  m_store(ja, ia, m1);
+  if (wave < 2) m_store(jb2, 0, m2);
   // ---- diagonal block D_I of Tinv = (I + M)^-1 by forward substitution (lane =
   //      column; right-looking: each x_q, once final, is subtracted from the later rows
   //      at once, so the dependent chain is 15 steps).  D_I replaces M's diagonal block,
   //      which nothing reads afterwards; the wave's own LDS writes and reads stay in order.
   if (lane < 16) {
-    float* mb = &sm.mf[lblk(wave, wave)][0];
+    float* mb = &sm.u1.t.mf[lblk(wave, wave)][0];
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.0f : 0.0f;
@@ -209,28 +226,23 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) mb[i * C::MLD + lane] = x[i];
   }
-  if (wave == 0) { m_tile(1, 0); m_tile(3, 0); }
-  else if (wave == 1) { m_tile(2, 0); m_tile(3, 1); }
-  else if (wave == 2) m_tile(2, 1);
-  else m_tile(3, 2);
   __syncthreads();
   // ---- blocks below the diagonal, wave J taking block column J from the top:
   //      X_IJ = -D_I sum_{J <= K < I} M_IK X_KJ needs only blocks of its own column and
   //      the diagonal blocks D, so the column needs no barrier until it is complete.
-  //      X_JJ = D_J sits in M's diagonal block (stride MLD), the others in tf (over the
-  //      keys, no longer read); the block being formed is its own scratch (mm16 reads
-  //      all of it before the store).
+  //      X_JJ = D_J sits in M's diagonal block (stride MLD), the others in tf; the block
+  //      being formed is its own scratch (mm16 reads all of it before the store).
   {
     const int J = wave;
     for (int I = J + 1; I < 4; ++I) {  // wave-uniform
-      float* dst = &sm.u1.tf[lblk(I, J)][0];
+      float* dst = &sm.u1.t.tf[lblk(I, J)][0];
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-      mm16(acc, &sm.mf[lblk(I, J)][0], C::MLD, &sm.mf[lblk(J, J)][0], C::MLD, lane);
+      mm16(acc, &sm.u1.t.mf[lblk(I, J)][0], C::MLD, &sm.u1.t.mf[lblk(J, J)][0], C::MLD, lane);
       for (int K = J + 1; K < I; ++K)
-        mm16(acc, &sm.mf[lblk(I, K)][0], C::MLD, &sm.u1.tf[lblk(K, J)][0], C::FLD, lane);
+        mm16(acc, &sm.u1.t.mf[lblk(I, K)][0], C::MLD, &sm.u1.t.tf[lblk(K, J)][0], C::FLD, lane);
       store16(dst, C::FLD, acc, 1.0f, lane);
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
-      mm16(x, &sm.mf[lblk(I, I)][0], C::MLD, dst, C::FLD, lane);
+      mm16(x, &sm.u1.t.mf[lblk(I, I)][0], C::MLD, dst, C::FLD, lane);
       store16(dst, C::FLD, x, -1.0f, lane);
     }
   }
@@ -250,8 +262,8 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     const bool keep = J <= I;
     // diagonal blocks in M's place (stride MLD), the others in tf; 8-byte reads (a row
     // of M's blocks starts at a multiple of 8 bytes only)
-    const float* src = J < I ? &sm.u1.tf[lblk(I, J)][(t & 15) * C::FLD + (s & 15)]
-                             : &sm.mf[lblk(I, I)][(t & 15) * C::MLD + (s & 15)];
+    const float* src = J < I ? &sm.u1.t.tf[lblk(I, J)][(t & 15) * C::FLD + (s & 15)]
+                             : &sm.u1.t.mf[lblk(I, I)][(t & 15) * C::MLD + (s & 15)];
     float v[8];
 #pragma unroll
     for (int k = 0; k < 8; k += 2) {
