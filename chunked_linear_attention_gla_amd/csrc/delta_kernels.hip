@@ -35,10 +35,11 @@
 //                       transitions e^gamma I - (k e^{gamma-b})^T W, run as dk extra
 //                       columns from the identity with no writes).
 //   delta_output_kernel one workgroup per (head, slice of value columns, segment),
-//                       chunks in order from the folded start state: W and Ut from
-//                       Tinv and the staged k and v, U = Ut - W S_0 on the matrix
-//                       cores, then o and the state update as in the linear-attention
-//                       output pass.
+//                       chunks in order from the folded start state: the effective
+//                       writes U = Tinv (diag(beta) V - diag(beta e^b) K S_0) (= Ut -
+//                       W S_0) on the matrix cores from Tinv and the staged k and v,
+//                       then o and the state update as in the linear-attention output
+//                       pass.
 #include "chunk_common.h"
 
 namespace gla {
@@ -306,11 +307,10 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
 }
 
 // ============================================================================
-// Pass 2 (and the segment pre-pass): chunks in order.  Each chunk's
-// W = Tinv diag(beta e^b) K and Ut = Tinv diag(beta) V (of the slice) are formed here
-// from the chunk's Tinv (pass 1) and the k and v these passes stage anyway: W by all
-// waves into the -W tile, Ut by each wave for its own columns, straight into the
-// accumulators of U (tokens as rows).
+// Pass 2 (and the segment pre-pass): chunks in order.  Each wave forms the effective
+// writes of its own value columns from the chunk's Tinv (pass 1) and the k and v these
+// passes stage anyway, U = Tinv (diag(beta) V - diag(beta e^b) K S_0): the same U as
+// Ut - W S_0, without forming W.
 // ============================================================================
 template <typename T, int DK, int DVS>
 struct DoCfg {
@@ -322,14 +322,11 @@ struct DoCfg {
   static constexpr int QU = 8 * DK / NT;
   static constexpr int VU = 8 * DVS / NT;      // 8-element v pieces per thread
   static constexpr int TU = 64 * 64 / 8 / NT;  // 8-element Tinv pieces per thread
-  static constexpr int WN = DK / 16 < NW ? DK / 16 : NW;  // waves that form W
-  static constexpr int WC = DK / WN;                      // W columns formed per such wave
   static constexpr int DB = DK / 16;
   static constexpr int KS = DK / 32;
   static_assert(QU >= 1 && QU * NT == 8 * DK, "staging must divide evenly");
   static_assert(VU >= 1 && VU * NT == 8 * DVS, "v staging must divide evenly");
   static_assert(TU >= 1 && TU * NT * 8 == 64 * 64, "Tinv staging must divide evenly");
-  static_assert(WC % 16 == 0, "W columns per wave");
 };
 
 template <typename T, int DK, int DVS>
@@ -337,10 +334,9 @@ struct DoSmem {
   using C = DoCfg<T, DK, DVS>;
   T qh[64 * C::QLD];
   T kh[64 * C::QLD];
-  T wn[64 * C::QLD];              // -W
   T kp[2][TokTile<T, DK>::SIZE];  // k e^{gamma - b}, token-major, by chunk parity
-  T kb[TokTile<T, DK>::SIZE];     // beta e^b k, token-major (W's right-hand side)
-  T vb[TokTile<T, DVS>::SIZE];    // beta v of the slice, token-major (Ut's)
+  T kb[64 * C::QLD];              // beta e^b k, row-major, read as fragments (swizzled as qh)
+  T vb[TokTile<T, DVS>::SIZE];    // beta v of the slice, token-major
   T tv[64 * C::TLD];              // Tinv
   T a[64 * C::TLD];
 };
@@ -348,9 +344,8 @@ struct DoSmem {
 template <typename T, int DK, int DVS>
 struct DsSmem {
   using C = DoCfg<T, DK, DVS>;
-  T wn[64 * C::QLD];
   T kp[TokTile<T, DK>::SIZE];
-  T kb[TokTile<T, DK>::SIZE];
+  T kb[64 * C::QLD];
   T vb[TokTile<T, DVS>::SIZE];
   T tv[64 * C::TLD];
   int nonzero[2][C::NW];  // transition half: per wave, whether its columns are nonzero, by chunk parity
@@ -398,7 +393,8 @@ struct DoStaged {
 };
 
 // The state-side operands of the staged chunk into LDS: k e^{gamma - b} (token-major),
-// beta e^b k (token-major), beta v (token-major, with Ut) and Tinv (row-major).
+// beta e^b k (row-major, swizzled for fragment reads), beta v (token-major, with v) and
+// Tinv (row-major).
 template <typename T, int DK, int DVS, bool LOAD_Q, bool LOAD_V>
 __device__ __forceinline__ void stage_state_side(T* kp, T* kb, T* vb, T* tv,
                                                  const DoStaged<T, DK, DVS, LOAD_Q, LOAD_V>& st,
@@ -409,7 +405,7 @@ __device__ __forceinline__ void stage_state_side(T* kp, T* kb, T* vb, T* tv,
     const int u = tid + m * C::NT, row = u / (DK / 8), c8 = u % (DK / 8);
     const float br = cd.at(row), ber = __shfl(st.be, row);
     TokTile<T, DK>::store8(kp, row, c8 * 8, st.k[m], exp_e(cd.gam - br));
-    TokTile<T, DK>::store8(kb, row, c8 * 8, st.k[m], ber * exp_e(br));
+    Elem<T>::store8_scaled_sw(kb + row * C::QLD + c8 * 8, st.k[m], ber * exp_e(br), frag_swap<T>(row));
   }
   if constexpr (LOAD_V) {
 #pragma unroll
@@ -433,66 +429,56 @@ __device__ __forceinline__ void stage_state_side(T* kp, T* kb, T* vb, T* tv,
   }
 }
 
-// -W = -Tinv (beta e^b K) into the row-major -W tile: wave `wave` < WN forms columns
-// wave * WC .. + WC - 1 (Tinv is zero above its diagonal 16x16 blocks, so token block
-// jb needs K-steps up to jb / 2 only).
-template <typename T, int DK, int DVS>
-__device__ __forceinline__ void form_w(T* wn, const T* kb, const T* tv, int wave, int lane) {
-  using E = Elem<T>;
-  using C = DoCfg<T, DK, DVS>;
-  const int r16 = lane & 15, g = lane >> 4;
-  if (wave >= C::WN) return;  // wave-uniform
-#pragma unroll
-  for (int cb = 0; cb < C::WC; cb += 16) {
-    const int col = wave * C::WC + cb;
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks <= jb / 2; ++ks)
-        E::mfma(acc, TokTile<T, DK>::load(kb, ks * 32, col, lane), E::load_frag(tv + (jb * 16 + r16) * C::TLD, ks * 32 + 4 * g));
-      // acc[e] = W[16 jb + r16][col + 4 g + e]
-      const int t = jb * 16 + r16;
-      E::store4(wn + t * C::QLD + ((col + 4 * g) ^ frag_swz<T>(t)), -acc[0], -acc[1], -acc[2], -acc[3]);
-    }
-  }
-}
-
-// Ut = Tinv (beta V) for the wave's 16 columns (slice column colr) with tokens as
-// accumulator rows: U[tb][e] = Ut[16 tb + 4 g + e][colr + r16] (zeros without v).
+// The effective writes of the wave's 16 value columns (slice column colr), S_0 given
+// as operand fragments Sf: U = Tinv R with R = diag(beta) V - Y, Y = diag(beta e^b) K S_0.
+// Y comes out with tokens as accumulator rows -- Y[jb][e] = Y[16 jb + 4 g + e][colr + r16]
+// -- so two stacked 16-token blocks are already the right-hand operand of the product
+// with Tinv (the fragment convention of gla_device.h), beta v entering through the
+// transposing read of the same tokens and columns; U's accumulators again hold tokens as
+// rows, so Uf are the operand fragments of A.U and the state update.  Tinv is zero
+// above its diagonal 16x16 blocks, so token block tb needs K-steps up to tb / 2 only.
+// Without v (LOAD_V = false: the transition half) R = -Y.
 template <typename T, int DK, int DVS, bool LOAD_V>
-__device__ __forceinline__ void form_ut(floatx4 (&U)[4], const T* vb, const T* tv, int colr, int lane) {
+__device__ __forceinline__ void effective_writes(typename Elem<T>::Frag (&Uf)[2],
+                                                 const typename Elem<T>::Frag (&Sf)[DK / 32], const T* kb,
+                                                 const T* vb, const T* tv, int colr, int lane) {
   using E = Elem<T>;
   using C = DoCfg<T, DK, DVS>;
   const int r16 = lane & 15, g = lane >> 4;
+  floatx4 Y[4];
+#pragma unroll
+  for (int jb = 0; jb < 4; ++jb) {
+    Y[jb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks)
+      E::mfma(Y[jb], E::load_frag(kb + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))), Sf[ks]);
+  }
+  typename E::Frag R[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    floatx4 lo = -Y[2 * ks], hi = -Y[2 * ks + 1];
+    if constexpr (LOAD_V) {
+      const typename E::Frag vf = TokTile<T, DVS>::load(vb, ks * 32, colr, lane);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] += static_cast<float>(vf.v[e]);
+          hi[e] += static_cast<float>(vf.v[4 + e]);
+        }
+      } else {
+        lo += vf.lo;
+        hi += vf.hi;
+      }
+    }
+    R[ks] = E::from_acc(lo, hi);
+  }
+  floatx4 U[4];
 #pragma unroll
   for (int tb = 0; tb < 4; ++tb) {
     U[tb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (LOAD_V) {
 #pragma unroll
-      for (int ks = 0; ks <= tb / 2; ++ks)
-        E::mfma(U[tb], E::load_frag(tv + (tb * 16 + r16) * C::TLD, ks * 32 + 4 * g),
-                TokTile<T, DVS>::load(vb, ks * 32, colr, lane));
-    }
+    for (int ks = 0; ks <= tb / 2; ++ks) E::mfma(U[tb], E::load_frag(tv + (tb * 16 + r16) * C::TLD, ks * 32 + 4 * g), R[ks]);
   }
-}
-
-// U = Ut - W S_0 for the wave's 16 columns (S_0 as operand fragments Sf), straight into
-// the operand fragments of A.U and the state update.  The accumulators hold tokens as
-// rows -- U[jb][e] = U[16 jb + 4 g + e][colr + r16], from the product with -W as the
-// left operand -- so two stacked 16-token blocks are already a 32-token K-step fragment
-// (the fragment convention of gla_device.h); Ut (form_ut) is their initial value.
-template <typename T, int DK, int DVS>
-__device__ __forceinline__ void effective_writes(typename Elem<T>::Frag (&Uf)[2], floatx4 (&U)[4],
-                                                 const typename Elem<T>::Frag (&Sf)[DK / 32], const T* wn, int lane) {
-  using E = Elem<T>;
-  using C = DoCfg<T, DK, DVS>;
-  const int r16 = lane & 15, g = lane >> 4;
-#pragma unroll
-  for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-    for (int ks = 0; ks < C::KS; ++ks)
-      E::mfma(U[jb], E::load_frag(wn + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))), Sf[ks]);
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) Uf[ks] = E::from_acc(U[2 * ks], U[2 * ks + 1]);
 }
@@ -573,15 +559,11 @@ __global__ void __launch_bounds__((DoCfg<T, DK, NCOL>::NT)) delta_segment_kernel
     stage_state_side<T, DK, NCOL, false, !PHI>(sm.kp, sm.kb, sm.vb, sm.tv, st, cd, tid);
     st.load(rk, rk, rv, rt, rb, rbe, Tn, p.dv, min(c + 1, c_end - 1), col0, tid);
     __syncthreads();
-    form_w<T, DK, NCOL>(sm.wn, sm.kb, sm.tv, wave, lane);
-    floatx4 U[4];
-    form_ut<T, DK, NCOL, !PHI>(U, sm.vb, sm.tv, wave * 16, lane);
-    __syncthreads();
     typename E::Frag Sf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
     typename E::Frag Uf[2];
-    effective_writes<T, DK, NCOL>(Uf, U, Sf, sm.wn, lane);
+    effective_writes<T, DK, NCOL, !PHI>(Uf, Sf, sm.kb, sm.vb, sm.tv, wave * 16, lane);
     delta_state_update<T, DK, NCOL>(S, Uf, sm.kp, exp_e(cd.gam), lane);
     if constexpr (PHI) {
       // Once this workgroup's columns of the running transition product are all
@@ -700,8 +682,8 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
     st.load(rq, rk, rv, rt, rb, rbe, Tn, p.dv, min(c + 1, c_end - 1), col0, tid);
     __syncthreads();
 
-    // ---- (3) A over the 10 causal tiles; -W (every wave its columns); Ut of the wave's
-    //      columns; o_inter = e^{r_u} Qh S_0
+    // ---- (3) A over the 10 causal tiles; the effective writes U of the wave's columns;
+    //      o_inter = e^{r_u} Qh S_0
 #pragma unroll
     for (int t = 0; t < 10; ++t) {
       if (t % C::NW != wave) continue;  // wave-uniform
@@ -717,12 +699,11 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
       for (int e = 0; e < 4; ++e) vals[e] = (jb != ib || 4 * g + e <= r16) ? acc[e] * f : 0.0f;
       E::store4(sm.a + (jb * 16 + r16) * C::TLD + ib * 16 + 4 * g, vals[0], vals[1], vals[2], vals[3]);
     }
-    form_w<T, DK, DVS>(sm.wn, sm.kb, sm.tv, wave, lane);
-    floatx4 U[4];
-    form_ut<T, DK, DVS, true>(U, sm.vb, sm.tv, wave * 16, lane);
     typename E::Frag Sf[C::KS];
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) Sf[ks] = E::from_acc(S[2 * ks], S[2 * ks + 1]);
+    typename E::Frag Uf[2];
+    effective_writes<T, DK, DVS, true>(Uf, Sf, sm.kb, sm.vb, sm.tv, wave * 16, lane);
     floatx4 O[4];
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
@@ -734,11 +715,8 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
     }
     __syncthreads();
 
-    // ---- (4) U = Ut - W S_0 (every wave's -W columns are in); o += A U;
-    //      S_c = e^gamma S_0 + (k e^{gamma - b})^T U
+    // ---- (4) o += A U (every wave's A tiles are in); S_c = e^gamma S_0 + (k e^{gamma - b})^T U
     {
-      typename E::Frag Uf[2];
-      effective_writes<T, DK, DVS>(Uf, U, Sf, sm.wn, lane);
 #pragma unroll
       for (int jb = 0; jb < 4; ++jb)
 #pragma unroll
@@ -751,7 +729,7 @@ __global__ void __launch_bounds__((DoCfg<T, DK, DVS>::NT)) delta_output_kernel(D
     }
     // No barrier here: the next chunk's staging writes Qh, Kh, beta e^b k, beta v and
     // Tinv, last read in (3) before this chunk's second barrier, and the other
-    // k e^{gamma - b} buffer; -W and A are rewritten only after its first barrier.
+    // k e^{gamma - b} buffer; A is rewritten only after its first barrier.
   }
   if (seg == p.segments - 1) {
 #pragma unroll
