@@ -384,8 +384,7 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
 #pragma unroll
       for (int e = 0; e < 4; ++e) z += a4[e] * b4[e];
     }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off);
+  z = row_sum4(group_sum<16>(z));  // all 64 lanes
   if (lane == 0) sm.zpart[w] = z;
   __syncthreads();
 
@@ -414,20 +413,42 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
           E::mfma(N[nb], Ef[nb][ks], vf);  // N[nb][e] = (v_j^T D^T)[n]
         }
       }
-      // n = 16 (NB w + nb) + 4 g + e
+      // n = 16 (NB w + nb) + 4 g + e: four consecutive columns (also after the swap,
+      // which moves whole 8-byte halves), read as one 8-byte (bf16) or 16-byte piece
       float rp = 0.0f, up = 0.0f;
 #pragma unroll
-      for (int nb = 0; nb < X::NB; ++nb)
+      for (int nb = 0; nb < X::NB; ++nb) {
+        const int n0 = (16 * (X::NB * w + nb) + 4 * g) ^ dx_swz<T>(r16);
+        const T* qrow = sm.q + (jb * 16 + r16) * X::LDK + n0;
+        const T* krow = sm.k + (jb * 16 + r16) * X::LDK + n0;
+        float qv[4], kv[4];
+        if constexpr (sizeof(T) == 2) {
+          GLA_CHECK_LDS(qrow, 8);
+          GLA_CHECK_LDS(krow, 8);
+          const bf16x4 q4 = *reinterpret_cast<const bf16x4*>(qrow), k4 = *reinterpret_cast<const bf16x4*>(krow);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qv[e] = static_cast<float>(q4[e]);
+            kv[e] = static_cast<float>(k4[e]);
+          }
+        } else {
+          GLA_CHECK_LDS(qrow, 16);
+          GLA_CHECK_LDS(krow, 16);
+          const floatx4 q4 = *reinterpret_cast<const floatx4*>(qrow), k4 = *reinterpret_cast<const floatx4*>(krow);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            qv[e] = q4[e];
+            kv[e] = k4[e];
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int n = 16 * (X::NB * w + nb) + 4 * g + e;
-          rp += M[nb][e] * E::to_f32(sm.q[(jb * 16 + r16) * X::LDK + (n ^ dx_swz<T>(r16))]);
-          up += N[nb][e] * E::to_f32(sm.k[(jb * 16 + r16) * X::LDK + (n ^ dx_swz<T>(r16))]);
+          rp += M[nb][e] * qv[e];
+          up += N[nb][e] * kv[e];
         }
-      rp += __shfl_xor(rp, 16);
-      rp += __shfl_xor(rp, 32);
-      up += __shfl_xor(up, 16);
-      up += __shfl_xor(up, 32);
+      }
+      rp = row_sum4(rp);
+      up = row_sum4(up);
       if (g == 0) {
         sm.rpart[w][jb * 16 + r16] = rp;
         sm.upart[w][jb * 16 + r16] = up;
@@ -459,8 +480,7 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
       pe[e] = keep ? qk[e] * gv[e] * exp_e(bj - sm.b[ib * 16 + 4 * g + e]) : 0.0f;
       row += pe[e];
     }
-    row += __shfl_xor(row, 16);
-    row += __shfl_xor(row, 32);
+    row = row_sum4(row);
     if (g == 0) sm.prow[t][r16] = row;
     // column sums over the 16 lanes of a row group: DPP row shifts, the total lands in
     // the row's last lane

@@ -142,6 +142,24 @@ __device__ __forceinline__ void permlane16_swap_pair(uint32_t& a, uint32_t& b) {
   asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
+// v_permlane32_swap_b32 with both of its results: the high 32 lanes of a trade places
+// with the low 32 lanes of b, so a = (a_lo, b_lo) and b = (a_hi, b_hi) by half-wave.
+// Written out for the reason given above.
+__device__ __forceinline__ void permlane32_swap_pair(uint32_t& a, uint32_t& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Sum over the four 16-lane rows of the lanes at the same position (lanes l, l ^ 16,
+// l ^ 32, l ^ 48), left in all four: a row-pair swap, then a half-wave swap.
+__device__ __forceinline__ float row_sum4(float v) {
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  permlane16_swap_pair(a, b);  // a: the pair's even row, b: its odd row
+  const float pair = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+  uint32_t c = __builtin_bit_cast(uint32_t, pair), d = c;
+  permlane32_swap_pair(c, d);  // c: the low pair's sum, d: the high pair's
+  return __builtin_bit_cast(float, c) + __builtin_bit_cast(float, d);
+}
+
 // Exclusive prefix sum of v over the lanes l - S, l - 2S, ... (S = STRIDE in 1, 2, 4, 8
 // or 16: lanes that hold the same item of earlier groups of S lanes).  Inside each
 // 16-lane row: DPP row shifts for the prefix and rotations for the row total (both
