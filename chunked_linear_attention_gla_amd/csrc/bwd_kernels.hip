@@ -79,15 +79,9 @@ __device__ __forceinline__ float gate_slope(float x) {
   return -5.0f * sg * (1.0f - sg);                      // d/dx -5 sigmoid(x)
 }
 
-// The four chunk tiles are read both as MFMA fragments (ds_read2_b64: one 8-byte piece
-// from each of 16 rows, cols c and c + 16) and transposed (ds_read_tr16_b64).  At a row
-// stride of 136 elements rows r and r + 8 of a fragment read share banks; rows with bit
-// 3 set therefore hold each 16-byte group with its 8-byte halves swapped: element
-// column c of row r is at c ^ dx_swz(r) (bf16 only).
-template <typename T>
-__device__ __forceinline__ int dx_swz(int row) {
-  return sizeof(T) == 2 ? (row & 8) >> 1 : 0;
-}
+// The four chunk tiles are read both as MFMA fragments and transposed
+// (ds_read_tr16_b64); they are swizzled by frag_swz (gla_device.h) and every read
+// applies the same swap.
 
 // 64 rows of a per-head [T][ncol] tensor, 8-element units spread over the threads:
 // all loads are issued first (load), the LDS stores come after (store), so a
@@ -111,7 +105,7 @@ struct RowStage {
       if constexpr (sizeof(T) == 2) {
         const uint4 u = r[m].u;
         GLA_CHECK_LDS(dst + row * LD + c8 * 8, 16);
-        *reinterpret_cast<uint4*>(dst + row * LD + c8 * 8) = dx_swz<T>(row) ? make_uint4(u.z, u.w, u.x, u.y) : u;
+        *reinterpret_cast<uint4*>(dst + row * LD + c8 * 8) = frag_swz<T>(row) ? make_uint4(u.z, u.w, u.x, u.y) : u;
       } else {
         Elem<T>::store8_raw(dst + row * LD + c8 * 8, r[m]);
       }
@@ -161,7 +155,7 @@ __device__ __forceinline__ typename Elem<T>::Frag tok_frag(const T* tile, int k0
     typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
     const int s = lane & 15, g = lane >> 4;
     const int row = k0 + 4 * g + (s >> 2);  // rows row and row + 16 share bit 3
-    const T* p0 = tile + row * LD + c0 + ((4 * (s & 3)) ^ dx_swz<T>(row));
+    const T* p0 = tile + row * LD + c0 + ((4 * (s & 3)) ^ frag_swz<T>(row));
     const T* p1 = p0 + 16 * LD;
     GLA_CHECK_LDS(p0, 8);
     GLA_CHECK_LDS(p1, 8);
@@ -405,8 +399,8 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
       for (int nb = 0; nb < X::NB; ++nb) M[nb] = N[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < X::KS; ++ks) {
-        const typename E::Frag gf = E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ dx_swz<T>(r16)));
-        const typename E::Frag vf = E::load_frag(sm.v + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ dx_swz<T>(r16)));
+        const typename E::Frag gf = E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ frag_swz<T>(r16)));
+        const typename E::Frag vf = E::load_frag(sm.v + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ frag_swz<T>(r16)));
 #pragma unroll
         for (int nb = 0; nb < X::NB; ++nb) {
           E::mfma(M[nb], Sf[nb][ks], gf);  // M[nb][e] = (dO_j^T S^T)[n], j = 16 jb + r16
@@ -418,7 +412,7 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
       float rp = 0.0f, up = 0.0f;
 #pragma unroll
       for (int nb = 0; nb < X::NB; ++nb) {
-        const int n0 = (16 * (X::NB * w + nb) + 4 * g) ^ dx_swz<T>(r16);
+        const int n0 = (16 * (X::NB * w + nb) + 4 * g) ^ frag_swz<T>(r16);
         const T* qrow = sm.q + (jb * 16 + r16) * X::LDK + n0;
         const T* krow = sm.k + (jb * 16 + r16) * X::LDK + n0;
         float qv[4], kv[4];
@@ -465,12 +459,12 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
     floatx4 qk = {0.f, 0.f, 0.f, 0.f}, gv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < DK / 32; ++ks)
-      E::mfma(qk, E::load_frag(sm.k + (ib * 16 + r16) * X::LDK, ks * 32 + ((4 * g) ^ dx_swz<T>(r16))),
-              E::load_frag(sm.q + (jb * 16 + r16) * X::LDK, ks * 32 + ((4 * g) ^ dx_swz<T>(r16))));
+      E::mfma(qk, E::load_frag(sm.k + (ib * 16 + r16) * X::LDK, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))),
+              E::load_frag(sm.q + (jb * 16 + r16) * X::LDK, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
 #pragma unroll
     for (int ks = 0; ks < DV / 32; ++ks)
-      E::mfma(gv, E::load_frag(sm.v + (ib * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ dx_swz<T>(r16))),
-              E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ dx_swz<T>(r16))));
+      E::mfma(gv, E::load_frag(sm.v + (ib * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))),
+              E::load_frag(sm.g + (jb * 16 + r16) * X::LDV, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
     // lane (g, r16), element e: j = 16 jb + r16, s = 16 ib + 4 g + e
     const float bj = sm.b[jb * 16 + r16];
     float pe[4], row = 0.0f;

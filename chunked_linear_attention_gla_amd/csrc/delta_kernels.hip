@@ -50,21 +50,10 @@ __device__ __forceinline__ uint32_t dl_row(uint32_t t, uint32_t Tn, uint32_t row
   return t < Tn ? t * row_bytes : kDroppedOffset;
 }
 
-// Row-major bf16 tiles read as MFMA fragments (Qh, Kh, -W, the key operands of L): a
-// fragment read (ds_read2_b64) takes one 8-byte piece from each of 16 rows, and at a
-// row stride of 136 elements rows r and r + 8 fall on the same bank pair, a 2-way
-// conflict on every read.  Rows with bit 3 set therefore hold each 16-byte group with
-// its 8-byte halves swapped: element column c of row r is at c ^ frag_swz<T>(r).  The
-// staging loops below give each wave whole 8-row groups (the row advances by a
-// multiple of 16 per pass), so a store's swap is wave-uniform.
-template <typename T>
-__device__ __forceinline__ int frag_swz(int row) {
-  return Elem<T>::kSwizzle ? (row & 8) >> 1 : 0;
-}
-template <typename T>
-__device__ __forceinline__ bool frag_swap(int row) {
-  return __builtin_amdgcn_readfirstlane(frag_swz<T>(row)) != 0;
-}
+// Row-major tiles read as MFMA fragments (Qh, Kh, beta e^b k, the key operands of L)
+// use the swizzle frag_swz of gla_device.h; the staging loops below give each wave
+// whole 8-row groups (the row advances by a multiple of 16 per pass), so a store's swap
+// is wave-uniform (frag_swap).
 
 // acc += X Z for 16x16 fp32 blocks in LDS (X row stride ldx, Z row stride ldz):
 // afterwards lane (g, r16) holds (X Z)[4 g + e][r16] in acc[e].

@@ -464,6 +464,22 @@ template <> struct Elem<float> {
 // with SQ_LDS_BANK_CONFLICT).  A tile that is also written with 8-byte stores in the
 // accumulator layout (16 rows of one column piece per store cycle) is better at
 // NCOL + 8: those stores are 2-way there and 4-way at NCOL + 16.
+// Row-major bf16 tiles read as MFMA fragments (ds_read2_b64: one 8-byte piece from each
+// of 16 rows, columns c and c + 16): at a row stride of 136 elements rows r and r + 8
+// fall on the same bank pair, a 2-way conflict on every read.  Rows with bit 3 set
+// therefore hold each 16-byte group with its 8-byte halves swapped: element column c of
+// row r is at c ^ frag_swz<T>(r) (bf16 only; the swap moves whole 8-byte halves, so
+// four consecutive columns starting at a multiple of 4 stay consecutive).  frag_swap is
+// the same test for a store whose rows share bit 3 across the wavefront.
+template <typename T>
+__device__ __forceinline__ int frag_swz(int row) {
+  return Elem<T>::kSwizzle ? (row & 8) >> 1 : 0;
+}
+template <typename T>
+__device__ __forceinline__ bool frag_swap(int row) {
+  return __builtin_amdgcn_readfirstlane(frag_swz<T>(row)) != 0;
+}
+
 template <typename T, int NCOL, int LDX = NCOL + 16> struct TokTile;
 
 template <int NCOL, int LDX> struct TokTile<bf16, NCOL, LDX> {

@@ -143,14 +143,8 @@ struct PcStaged {
   }
 };
 
-// Qh, q e^b and the key tiles are read as MFMA fragments (ds_read2_b64: one 8-byte
-// piece from each of 16 rows); at a row stride of 136 elements rows r and r + 8 share
-// a bank pair.  Rows with bit 3 set hold each 16-byte group with its 8-byte halves
-// swapped, so element column c of row r is at c ^ pc_swz<T>(r) (bf16 only).
-template <typename T>
-__device__ __forceinline__ int pc_swz(int row) {
-  return Elem<T>::kSwizzle ? (row & 8) >> 1 : 0;
-}
+// Qh, q e^b and the key tiles are read as MFMA fragments, swizzled by frag_swz
+// (gla_device.h).
 
 // Log-decay of one channel in base 2: g log2 e.  The bounded gate evaluates
 // sigmoid(x) = 1 / (1 + e^{-x}) directly: a sum of positive terms, so no
@@ -521,7 +515,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
     for (int m = 0; m < C::R; ++m) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) qf[m][e] = E::get(st.q[m], e) * exp2_hw(lam.v[m][e]);
-      E::store8_f32_sw(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, qf[m], pc_swz<T>(rg * C::R + m) != 0);
+      E::store8_f32_sw(sm.qh + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, qf[m], frag_swz<T>(rg * C::R + m) != 0);
     }
     __syncthreads();
 
@@ -543,7 +537,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         for (int m = 0; m < C::R; ++m) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) qf[m][e] *= er[e];
-          E::store8_f32_sw(sm.qe + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, qf[m], pc_swz<T>(rg * C::R + m) != 0);
+          E::store8_f32_sw(sm.qe + (16 * tile + rg * C::R + m) * C::QLD + c8 * 8, qf[m], frag_swz<T>(rg * C::R + m) != 0);
         }
       }
       // Key tile `tile` serves the query tiles u >= tile as K^(u) = k e^{r_u - b} and the
@@ -557,7 +551,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         T* kt = sm.kt + (u * (u + 1) / 2 + tile) * 16 * C::QLD;
 #pragma unroll
         for (int m = 0; m < C::R; ++m)
-          E::store8_f32_sw(kt + (rg * C::R + m) * C::QLD + c8 * 8, kf[m], pc_swz<T>(rg * C::R + m) != 0);
+          E::store8_f32_sw(kt + (rg * C::R + m) * C::QLD + c8 * 8, kf[m], frag_swz<T>(rg * C::R + m) != 0);
         key_chain_step<C::R>(kf, tv[u]);
       }
 #pragma unroll
@@ -584,8 +578,8 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < C::KS; ++ks)
-        E::mfma(acc, E::load_frag(sm.kt + (t * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ pc_swz<T>(r16))),
-                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ pc_swz<T>(r16))));
+        E::mfma(acc, E::load_frag(sm.kt + (t * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))),
+                E::load_frag(sm.qh + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16))));
       // acc[e]: j = 16 jb + r16, i = 16 ib + 4 g + e; causal select on the diagonal tile
       float vals[4];
 #pragma unroll
@@ -611,7 +605,7 @@ __global__ void __launch_bounds__((PcCfg<T, DK, DVS>::NT)) pc_chunk_output_kerne
         for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-          const typename E::Frag qb = E::load_frag(sm.qe + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ pc_swz<T>(r16)));
+          const typename E::Frag qb = E::load_frag(sm.qe + (jb * 16 + r16) * C::QLD, ks * 32 + ((4 * g) ^ frag_swz<T>(r16)));
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], sf[nb][ks], qb);
         }

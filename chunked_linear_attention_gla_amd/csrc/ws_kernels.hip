@@ -133,8 +133,8 @@ __device__ __forceinline__ void attention_tile(bf16* a, const bf16* qh, const bf
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < DK / 32; ++ks) {
-    const E::Frag ka = E::load_frag(kh + (ib * 16 + r16) * LD, ks * 32 + 4 * g);
-    const E::Frag qb = E::load_frag(qh + (jb * 16 + r16) * LD, ks * 32 + 4 * g);
+    const E::Frag ka = E::load_frag(kh + (ib * 16 + r16) * LD, ks * 32 + ((4 * g) ^ frag_swz<bf16>(r16)));
+    const E::Frag qb = E::load_frag(qh + (jb * 16 + r16) * LD, ks * 32 + ((4 * g) ^ frag_swz<bf16>(r16)));
     E::mfma(acc, ka, qb);
   }
   // acc[e] = Qh_j . Kh_i for j = 16 jb + r16, i = 16 ib + 4 g + e
@@ -287,7 +287,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
       for (int ks = 0; ks < C::KS; ++ks) {
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
-          const E::Frag qb = E::load_frag(sm.qh[slot] + (jb * 16 + r16) * W::LD, ks * 32 + 4 * g);
+          const E::Frag qb = E::load_frag(sm.qh[slot] + (jb * 16 + r16) * W::LD, ks * 32 + ((4 * g) ^ frag_swz<bf16>(r16)));
 #pragma unroll
           for (int nb = 0; nb < C::NB; ++nb) E::mfma(O[jb][nb], Sf[nb][ks], qb);
         }
@@ -338,8 +338,9 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         E::Vec8 qv, kv;
         qv.u = stg.q[m];
         kv.u = stg.k[m];
-        E::store8_scaled(sm.qh[ns] + row * W::LD + c8 * 8, qv, exp_e(brow[m] - rj));
-        E::store8_scaled(sm.kh + row * W::LD + c8 * 8, kv, exp_e((DIAG ? cd.end(tile) : rj) - brow[m]));
+        const bool swap = frag_swap<bf16>(row);  // Qh and Kh rows swizzled for the fragment reads
+        E::store8_scaled_sw(sm.qh[ns] + row * W::LD + c8 * 8, qv, exp_e(brow[m] - rj), swap);
+        E::store8_scaled_sw(sm.kh + row * W::LD + c8 * 8, kv, exp_e((DIAG ? cd.end(tile) : rj) - brow[m]), swap);
         E::store8_scaled(sm.kp[ns] + row * W::KLD + c8 * 8, kv, exp_e(cd.gam - brow[m]));
         if (DIAG) {
           GLA_CHECK_LDS(sm.qr + row * DK + raw_piece(c8, row) * 8, 16);
