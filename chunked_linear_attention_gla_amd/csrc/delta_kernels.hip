@@ -73,6 +73,23 @@ __device__ __forceinline__ void store16(float* dst, int ld, const floatx4& acc, 
 // ============================================================================
 // Pass 1: Tinv = (I + diag(beta) L)^-1 of every chunk (and its reset flag).
 // ============================================================================
+// Steps Q..14 of the right-looking forward substitution of a unit lower triangular
+// 16x16 block (strictly lower part in m, row stride LD) on 64 lanes: lane (g, r16)
+// holds rows 4 k + g of column r16 in x[k]; step q broadcasts the final x_q from row
+// group q % 4 and subtracts m[i][q] x_q from every row i > q.
+template <int Q, int LD>
+__device__ __forceinline__ void substitute_rows(float (&x)[4], const float* m, int g) {
+  if constexpr (Q < 15) {
+    const float xq = row_broadcast<Q % 4>(x[Q / 4]);
+#pragma unroll
+    for (int k = Q / 4; k < 4; ++k) {
+      const float u = fmaf(-m[(4 * k + g) * LD + Q], xq, x[k]);
+      x[k] = (k > Q / 4 || g > Q % 4) ? u : x[k];  // rows 4 k + g > Q only
+    }
+    substitute_rows<Q + 1, LD>(x, m, g);
+  }
+}
+
 template <typename T, int DK, int DV>
 struct PrepCfg {
   static constexpr int NT = 256;
@@ -200,23 +217,21 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   m_store(wave, wave, md);
   m_store(ja, ia, m1);
   if (wave < 2) m_store(jb2, 0, m2);
-  // ---- diagonal block D_I of Tinv = (I + M)^-1 by forward substitution (lane =
-  //      column; right-looking: each x_q, once final, is subtracted from the later rows
-  //      at once, so the dependent chain is 15 steps).  D_I replaces M's diagonal block,
-  //      which nothing reads afterwards; the wave's own LDS writes and reads stay in order.
-  if (lane < 16) {
+  // ---- diagonal block D_I of Tinv = (I + M)^-1 by forward substitution, right-looking
+  //      (each x_q, once final, is subtracted from the later rows at once: a 15-step
+  //      chain) on all 64 lanes: lane (g, r16) holds rows 4 k + g (k = 0..3) of column
+  //      r16, and x_q passes from row group q % 4 to the others by a row broadcast.  D_I
+  //      replaces M's diagonal block, which nothing reads afterwards; the wave's own LDS
+  //      writes and reads stay in order.
+  {
     float* mb = &sm.u1.t.mf[lblk(wave, wave)][0];
-    float x[16];
+    float x[4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = (i == lane) ? 1.0f : 0.0f;
+    for (int k = 0; k < 4; ++k) x[k] = (4 * k + g == r16) ? 1.0f : 0.0f;
+    substitute_rows<0, C::MLD>(x, mb, g);
 #pragma unroll
-    for (int q = 0; q < 15; ++q)
-#pragma unroll
-      for (int i = q + 1; i < 16; ++i) x[i] = fmaf(-mb[i * C::MLD + q], x[q], x[i]);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mb[i * C::MLD + lane] = x[i];
+    for (int k = 0; k < 4; ++k) mb[(4 * k + g) * C::MLD + r16] = x[k];
   }
-  __syncthreads();
   // ---- blocks below the diagonal, wave J taking block column J from the top:
   //      X_IJ = -D_I sum_{J <= K < I} M_IK X_KJ needs only blocks of its own column and
   //      the diagonal blocks D, so the column needs no barrier until it is complete.

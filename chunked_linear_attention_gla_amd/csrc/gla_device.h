@@ -149,6 +149,19 @@ __device__ __forceinline__ void permlane32_swap_pair(uint32_t& a, uint32_t& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
 }
 
+// Row R0's value at the lane's position, in every row (a broadcast across the four
+// 16-lane rows): a row-pair swap picks row R0 % 2 of each pair, a half-wave swap the
+// pair R0 / 2.
+template <int R0>
+__device__ __forceinline__ float row_broadcast(float v) {
+  static_assert(R0 >= 0 && R0 < 4, "row of a wavefront");
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = a;
+  permlane16_swap_pair(a, b);  // a: the pair's even row, b: its odd row
+  uint32_t c = (R0 & 1) ? b : a, d = c;
+  permlane32_swap_pair(c, d);  // c: the low pair's, d: the high pair's
+  return __builtin_bit_cast(float, (R0 & 2) ? d : c);
+}
+
 // Sum over the four 16-lane rows of the lanes at the same position (lanes l, l ^ 16,
 // l ^ 32, l ^ 48), left in all four: a row-pair swap, then a half-wave swap.
 __device__ __forceinline__ float row_sum4(float v) {
