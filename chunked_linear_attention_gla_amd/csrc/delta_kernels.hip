@@ -98,28 +98,31 @@ struct PrepCfg {
   static constexpr int QU = 8 * DK / NT;
   static constexpr int KS = DK / 32;
   static constexpr int KL = DK / 8;   // lanes that stage one key row
-  // M and Tinv are held as their 10 lower 16x16 blocks (block (I, J), J <= I, at
-  // index I (I + 1) / 2 + J), 16 rows each at a padded stride: M's 18 puts the left-
-  // operand reads of the fp32 block products (row r, column 4 s + g) on banks 18 r + g,
-  // distinct within each half-wave; Tinv's 20 does the same for store16 (banks 16 g + r).
+  // M is held as its 10 lower 16x16 blocks (block (I, J), J <= I, at index
+  // I (I + 1) / 2 + J; the diagonal ones later hold Tinv's), Tinv's six blocks below the
+  // diagonal apart (J < I, at index I (I - 1) / 2 + J), 16 rows each at a padded
+  // stride: M's 18 puts the left-operand reads of the fp32 block products (row r,
+  // column 4 s + g) on banks 18 r + g, distinct within each half-wave; Tinv's 20 does
+  // the same for store16 (banks 16 g + r).
   static constexpr int MLD = 18;
   static constexpr int FLD = 20;
 };
 
 __device__ __forceinline__ constexpr int lblk(int I, int J) { return I * (I + 1) / 2 + J; }
+__device__ __forceinline__ constexpr int sblk(int I, int J) { return I * (I - 1) / 2 + J; }  // J < I
 
 // LDS: the staged keys, then (over them, once M is formed in registers) M and Tinv's
 // blocks below the diagonal in fp32 (M's diagonal blocks become Tinv's once inverted);
-// per-row factors.  At d = 128 that is 25 KB, six workgroups per compute unit where
-// the registers allow (the pass is a chain of short phases between barriers, so the
-// workgroups in flight set its speed).
+// per-row factors.  At d = 128 that is 20 KB, eight workgroups per compute unit (the
+// pass is a chain of short phases between barriers, so the workgroups in flight set its
+// speed).
 template <typename T, int DK, int DV>
 struct PrepSmem {
   using C = PrepCfg<T, DK, DV>;
   union {
     T kr[64 * C::QLD];               // k as loaded
     struct {
-      float tf[10][16 * C::FLD];     // Tinv (fp32), blocks below the diagonal
+      float tf[6][16 * C::FLD];      // Tinv (fp32), blocks below the diagonal
       float mf[10][16 * C::MLD];     // M = diag(beta) L, lower blocks; diagonal ones then D_I of Tinv
     } t;
   } u1;
@@ -240,11 +243,11 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
   {
     const int J = wave;
     for (int I = J + 1; I < 4; ++I) {  // wave-uniform
-      float* dst = &sm.u1.t.tf[lblk(I, J)][0];
+      float* dst = &sm.u1.t.tf[sblk(I, J)][0];
       floatx4 acc = {0.f, 0.f, 0.f, 0.f};
       mm16(acc, &sm.u1.t.mf[lblk(I, J)][0], C::MLD, &sm.u1.t.mf[lblk(J, J)][0], C::MLD, lane);
       for (int K = J + 1; K < I; ++K)
-        mm16(acc, &sm.u1.t.mf[lblk(I, K)][0], C::MLD, &sm.u1.t.tf[lblk(K, J)][0], C::FLD, lane);
+        mm16(acc, &sm.u1.t.mf[lblk(I, K)][0], C::MLD, &sm.u1.t.tf[sblk(K, J)][0], C::FLD, lane);
       store16(dst, C::FLD, acc, 1.0f, lane);
       floatx4 x = {0.f, 0.f, 0.f, 0.f};
       mm16(x, &sm.u1.t.mf[lblk(I, I)][0], C::MLD, dst, C::FLD, lane);
@@ -267,7 +270,7 @@ __global__ void __launch_bounds__(256) delta_prep_kernel(DeltaParams p) {
     const bool keep = J <= I;
     // diagonal blocks in M's place (stride MLD), the others in tf; 8-byte reads (a row
     // of M's blocks starts at a multiple of 8 bytes only)
-    const float* src = J < I ? &sm.u1.t.tf[lblk(I, J)][(t & 15) * C::FLD + (s & 15)]
+    const float* src = J < I ? &sm.u1.t.tf[sblk(I, J)][(t & 15) * C::FLD + (s & 15)]
                              : &sm.u1.t.mf[lblk(I, I)][(t & 15) * C::MLD + (s & 15)];
     float v[8];
 #pragma unroll
