@@ -304,12 +304,14 @@ __global__ void __launch_bounds__((DxCfg<T, DK, DV>::NT)) __attribute__((amdgpu_
       float fac[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) fac[e] = fexp(ks * 32 + 16 * (e >> 2) + 4 * g + (e & 3));
+      // the per-token factor goes on the NB fragments of tb rather than the DB of ta
       typename E::Frag fb[X::NB];
 #pragma unroll
-      for (int nb = 0; nb < X::NB; ++nb) fb[nb] = tok_frag<T, X::LDK>(tb, ks * 32, 16 * (X::NB * w + nb), lane);
+      for (int nb = 0; nb < X::NB; ++nb)
+        fb[nb] = scale_frag<T>(tok_frag<T, X::LDK>(tb, ks * 32, 16 * (X::NB * w + nb), lane), fac);
 #pragma unroll
       for (int db = 0; db < X::DB; ++db) {
-        const typename E::Frag fa = scale_frag<T>(tok_frag<T, X::LDV>(ta, ks * 32, db * 16, lane), fac);
+        const typename E::Frag fa = tok_frag<T, X::LDV>(ta, ks * 32, db * 16, lane);
 #pragma unroll
         for (int nb = 0; nb < X::NB; ++nb) E::mfma(acc[nb][db], fa, fb[nb]);
       }
