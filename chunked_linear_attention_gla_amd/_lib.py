@@ -81,6 +81,7 @@ _SIGS = {
     "gla_bench_stream": (_i, [_vp, _vp, _vp, _vp, ctypes.c_ulonglong, _i, _vp]),
     "gla_debug_flags": (_i, [ctypes.POINTER(ctypes.c_uint)]),
     "gla_debug_selftest": (_i, [_vp, _vp, _vp]),
+    "gla_lane_selftest": (_i, [_vp, _vp, _vp]),
     "gla_chunk_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i,
                            _i, _i, _i, _vp, _psz, _vp]),
 }
@@ -128,6 +129,16 @@ def debug_flags(lib: Optional[ctypes.CDLL] = None) -> int:
     v = ctypes.c_uint(0)
     _check("gla_debug_flags", (lib or load()).gla_debug_flags(ctypes.byref(v)))
     return int(v.value)
+
+
+def lane_selftest(values: torch.Tensor) -> torch.Tensor:
+    """Run gla_lane_selftest on 64 fp32 values on a GPU; returns the 17 x 64 slots (see
+    include/gla.h) as a tensor on the same device."""
+    _need(values.is_cuda and values.dtype == torch.float32 and values.numel() == 64 and values.is_contiguous(),
+          "values must be 64 contiguous fp32 values on a GPU")
+    out = torch.empty(17, 64, device=values.device, dtype=torch.float32)
+    _check("gla_lane_selftest", load().gla_lane_selftest(_ptr(values), _ptr(out), _stream(values.device)))
+    return out
 
 
 def _check(fn: str, code: int) -> None:

@@ -916,3 +916,8 @@ extern "C" gla_status_t gla_debug_selftest(const float* probe, float* out, void*
   return GLA_ERR_UNSUPPORTED;
 #endif
 }
+
+extern "C" gla_status_t gla_lane_selftest(const float* in, float* out, void* stream) {
+  if (!in || !out) return GLA_ERR_NULL;
+  return gla::launch_lane_selftest(in, out, (hipStream_t)stream) == hipSuccess ? GLA_OK : GLA_ERR_HIP;
+}

@@ -160,6 +160,44 @@ hipError_t launch_debug_selftest(const float* g, float* out, hipStream_t stream)
 }
 #endif
 
+// One wavefront runs each cross-lane helper the kernels rely on over `in` (64
+// values; the swaps pair it with in + 100) and writes slot k of `out` (64 values per
+// slot), so that a test can hold every lane layout against its definition.
+__global__ void __launch_bounds__(64) lane_selftest_kernel(const float* in, float* out) {
+  const int l = threadIdx.x;
+  const float v = in[l];
+  float r[kLaneSelftestSlots];
+  r[0] = group_max<8>(v);
+  r[1] = group_max<16>(v);
+  r[2] = group_sum<8>(v);
+  r[3] = group_sum<16>(v);
+  r[4] = strided_exclusive_scan<4>(v, l);
+  r[5] = strided_exclusive_scan<8>(v, l);
+  r[6] = strided_exclusive_scan<16>(v, l);
+  r[7] = wave_inclusive_scan(v, l);
+  r[8] = row_broadcast<0>(v);
+  r[9] = row_broadcast<1>(v);
+  r[10] = row_broadcast<2>(v);
+  r[11] = row_broadcast<3>(v);
+  r[12] = row_sum4(v);
+  uint32_t a = __builtin_bit_cast(uint32_t, v), b = __builtin_bit_cast(uint32_t, v + 100.0f);
+  permlane16_swap_pair(a, b);
+  r[13] = __builtin_bit_cast(float, a);
+  r[14] = __builtin_bit_cast(float, b);
+  a = __builtin_bit_cast(uint32_t, v);
+  b = __builtin_bit_cast(uint32_t, v + 100.0f);
+  permlane32_swap_pair(a, b);
+  r[15] = __builtin_bit_cast(float, a);
+  r[16] = __builtin_bit_cast(float, b);
+#pragma unroll
+  for (int k = 0; k < kLaneSelftestSlots; ++k) out[k * 64 + l] = r[k];
+}
+
+hipError_t launch_lane_selftest(const float* in, float* out, hipStream_t stream) {
+  hipLaunchKernelGGL(lane_selftest_kernel, dim3(1), dim3(64), 0, stream, in, out);
+  return hipGetLastError();
+}
+
 // debug builds: this unit's LDS-check word (see GLA_CHECK_LDS)
 GLA_DEBUG_ACCESSOR(debug_word_gate_cumsum)
 

@@ -176,5 +176,7 @@ unsigned int debug_word_delta_kernels();
 // the LDS checks' self-test: one workgroup of 64 threads; out: 64 floats it writes
 hipError_t launch_debug_selftest(const float* g, float* out, hipStream_t stream);
 #endif
+constexpr int kLaneSelftestSlots = 17;  // output slots of gla_lane_selftest (64 floats each)
+hipError_t launch_lane_selftest(const float* in, float* out, hipStream_t stream);
 
 }  // namespace gla

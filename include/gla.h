@@ -375,6 +375,18 @@ gla_status_t gla_chunk_fwd_pc(const void* q, const void* k, const void* v, const
 gla_status_t gla_bench_stream(const void* a, const void* b, const void* c, void* out,
                               unsigned long long units, int grid, void* stream);
 
+/* Cross-lane self-test: one wavefront of 64 lanes runs each wavefront helper the
+ * kernels build on -- DPP group maxima and sums over 8 and 16 lanes, the strided
+ * exclusive scans over lane groups of 4, 8 and 16, the 64-lane inclusive scan, the
+ * broadcast of each 16-lane row to the other three, the sum over the four rows, and
+ * the gfx950 row-pair and half-wave swaps -- on in[0..63] (the swaps pair it with
+ * in + 100) and writes 17 slots of 64 floats to out, in that order (slots 13/14: the
+ * row-pair swap's two results, 15/16: the half-wave swap's).  A caller holds them
+ * against the definitions to confirm the lane layouts on its device and compiler.
+ * in, out: device memory (64 and 17 x 64 floats); enqueued on `stream`.  NULL
+ * pointers: GLA_ERR_NULL; a failed launch: GLA_ERR_HIP. */
+gla_status_t gla_lane_selftest(const float* in, float* out, void* stream);
+
 /* ------------------------------------------------------------------------
  * Debug builds (the library compiled with -DGLA_DEBUG, libgla_debug.so next to
  * libgla.so): every LDS access made through the kernels' shared load/store

@@ -62,6 +62,12 @@ def test_debug_entry_points_on_the_release_build(lib):
     assert lib.gla_debug_selftest(dummy, dummy, None) == UNSUP
 
 
+def test_lane_selftest_rejects_null_pointers(lib):
+    dummy = ctypes.c_void_p(16)
+    assert lib.gla_lane_selftest(None, dummy, None) == NULL
+    assert lib.gla_lane_selftest(dummy, None, None) == NULL
+
+
 def test_version_and_status_strings(lib):
     assert lib.gla_abi_version() == 2
     for code in range(11):
