@@ -155,6 +155,12 @@ gla::ChunkParams make_params(const void* q, const void* k, const void* v, const 
   p.cu_seqlens = nullptr;
   p.H = H;
   p.unit_order = nullptr;
+  p.gx_mode = 0;
+  p.gx_op = nullptr;
+  p.gx_b = nullptr;
+  p.gx_x = nullptr;
+  p.gx_out = nullptr;
+  p.gx_states = nullptr;
   return p;
 }
 
@@ -366,11 +372,27 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
   if (!valid_gate(gate) || !valid_path(path)) return GLA_ERR_ARG;
   // plans of the three passes: dq and dk run with state dims (dv, dk), dv with (dk, dv)
   gla_plan_t pa, pc;
+  // bf16 at dk = dv = 128 on the unified path: the gate gradient is formed inside the dq and
+  // dk passes (one full-width slice each) instead of by the dx kernel
+  const bool fused_dx = T > 0 && dtype == GLA_BF16 && dk_ == 128 && dv_ == 128 && path == GLA_PATH_UNIFIED;
   if (T > 0) {
     st = gla_plan_default(B, H, T, dv_, dk_, dtype, path, &pa);
     if (st != GLA_OK) return st;
     st = gla_plan_default(B, H, T, dk_, dv_, dtype, path, &pc);
     if (st != GLA_OK) return st;
+    if (fused_dx && pa.dv_split != 1) {
+      // one slice, segments doubled as the default plan does until the grid covers the CUs
+      int cus = 0;
+      st = device_cus(&cus);
+      if (st != GLA_OK) return st;
+      const long long units = (long long)B * H, nch = n_chunks(T);
+      int segs = 1;
+      while (segs < GLA_MAX_SEGMENTS && units * segs < cus && nch / (2LL * segs) >= 4) segs *= 2;
+      if (segs > std::max(1LL, nch)) segs = (int)std::max(1LL, nch);
+      pa.segments = segs;
+      pa.dv_split = 1;
+      pc = pa;
+    }
   } else {
     pa.segments = pc.segments = 1;
     pa.dv_split = pc.dv_split = 1;
@@ -455,28 +477,49 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
       p.grid = (int)(BH * pl.dv_split * pl.segments);
       return gla::launch_chunk_output(p, dt, diag, s);
     };
-    // dq = forward(dO, v, k) from S0^T; stores S^T before every even chunk
-    const gla::ChunkParams pdq = make(dO, v, k, b, S0, 1, 0, dq, STt, dv_, dk_, pa);
+    // dq = forward(dO, v, k) from S0^T; stores S^T before every even chunk (fused_dx: forms
+    // the pairs inside and entering each chunk into dx, and stores S^T before every chunk
+    // whose crossing factor is not exactly 0)
+    gla::ChunkParams pdq = make(dO, v, k, b, S0, 1, 0, dq, STt, dv_, dk_, pa);
+    if (fused_dx) {
+      pdq.gx_mode = 1;
+      pdq.gx_op = q;
+      pdq.gx_b = b;
+      pdq.gx_out = dx;
+      pdq.gx_states = Sfw;
+    }
     if (e == hipSuccess) e = prepass(pdq, pa);
-    if (e == hipSuccess) e = output(pdq, pa, Sfw);
-    // dk = reversed forward(v, dO, q) from dS_T^T (stores D^T after every odd chunk) and
+    if (e == hipSuccess) e = output(pdq, pa, fused_dx ? nullptr : Sfw);
+    // dk = reversed forward(v, dO, q) from dS_T^T (stores D^T after every odd chunk; fused_dx:
+    // adds the pairs leaving and crossing each chunk and finishes dx) and
     // dv = reversed forward(k, q, dO) from dS_T (final state D_0) carry the same state
     // gradient, transposed, under the same decays: with equal segment counts the dk
     // pass starts its segments from the dv pass's segment states, read transposed
     gla::ChunkParams pdk = make(v, dO, q, br, dS_T, 1, 1, dk, Sdk, dv_, dk_, pa);
+    if (fused_dx) {
+      pdk.gx_mode = 2;
+      pdk.gx_op = k;
+      pdk.gx_b = b;
+      pdk.gx_x = x;
+      pdk.gate = g;
+      pdk.gx_out = dx;
+      pdk.gx_states = Sfw;
+    }
+    void* const dk_states = fused_dx ? nullptr : Sbw;
     const gla::ChunkParams pdv = make(k, q, dO, br, dS_T, 0, 1, dv, D0, dk_, dv_, pc);
     if (pa.segments == pc.segments) {
       pdk.seg_transposed = 1;
       if (e == hipSuccess) e = prepass(pdv, pc);
-      if (e == hipSuccess) e = output(pdk, pa, Sbw);
+      if (e == hipSuccess) e = output(pdk, pa, dk_states);
       if (e == hipSuccess) e = output(pdv, pc, nullptr);
     } else {
       if (e == hipSuccess) e = prepass(pdk, pa);
-      if (e == hipSuccess) e = output(pdk, pa, Sbw);
+      if (e == hipSuccess) e = output(pdk, pa, dk_states);
       if (e == hipSuccess) e = prepass(pdv, pc);
       if (e == hipSuccess) e = output(pdv, pc, nullptr);
     }
-    if (e == hipSuccess) e = gla::launch_grad_dx(q, k, v, dO, b, x, Sfw, Sbw, dx, BH, T, dk_, dv_, dt, g, s);
+    if (!fused_dx && e == hipSuccess)
+      e = gla::launch_grad_dx(q, k, v, dO, b, x, Sfw, Sbw, dx, BH, T, dk_, dv_, dt, g, s);
   }
   if (e == hipSuccess) e = gla::launch_grad_ds0(D0, b, dS_T, dS0, BH, T, dk_, dv_, s);
   return e == hipSuccess ? GLA_OK : GLA_ERR_HIP;

@@ -66,19 +66,6 @@ struct DxSmem {
   float pcol[10][16];
 };
 
-__device__ __forceinline__ float sigmoid_f(float x) {
-  if (x >= 0.0f) return 1.0f / (1.0f + exp_e(-x));
-  const float e = exp_e(x);
-  return e / (1.0f + e);
-}
-
-template <int GATE>
-__device__ __forceinline__ float gate_slope(float x) {
-  if (GATE == kGateNegSoftplus) return sigmoid_f(-x);  // d/dx log sigmoid(x)
-  const float sg = sigmoid_f(x);
-  return -5.0f * sg * (1.0f - sg);                      // d/dx -5 sigmoid(x)
-}
-
 // The four chunk tiles are read both as MFMA fragments and transposed
 // (ds_read_tr16_b64); they are swizzled by frag_swz (gla_device.h) and every read
 // applies the same swap.

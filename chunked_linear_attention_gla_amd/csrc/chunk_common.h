@@ -155,6 +155,20 @@ __device__ __forceinline__ float decay_finish(const HeadBuffers& hb, const Chunk
   return wave_inclusive_scan(g, lane);
 }
 
+__device__ __forceinline__ float sigmoid_f(float x) {
+  if (x >= 0.0f) return 1.0f / (1.0f + exp_e(-x));
+  const float e = exp_e(x);
+  return e / (1.0f + e);
+}
+
+// Slope g'(x) of the gate (backward pass).
+template <int GATE>
+__device__ __forceinline__ float gate_slope(float x) {
+  if (GATE == kGateNegSoftplus) return sigmoid_f(-x);  // d/dx log sigmoid(x)
+  const float sg = sigmoid_f(x);
+  return -5.0f * sg * (1.0f - sg);                      // d/dx -5 sigmoid(x)
+}
+
 // Shared memory for the workgroup-wide search below (x path).
 struct SegScanSmem {
   int last_zero[16];

@@ -253,6 +253,11 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t off) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ uint2 buf_load8(rsrc_t r, uint32_t off) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
 __device__ __forceinline__ float buf_load4(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0));
 }

@@ -65,7 +65,7 @@ struct WsCfg {
 
 };
 
-template <int DK, int DVS, bool DIAG>
+template <int DK, int DVS, bool DIAG, int GX = 0>
 struct WsSmem {
   using W = WsCfg<DK, DVS, DIAG>;
   bf16 qh[2][64 * W::LD];          // Qh[j][d]
@@ -76,6 +76,12 @@ struct WsSmem {
   float sb[64];                    // b of the chunk
   bf16 qr[DIAG ? 64 * DK : 1];     // raw q, 16-byte pieces swizzled by row (ablation)
   bf16 kr[DIAG ? 64 * DK : 1];     // raw k, same layout (ablation)
+  // gate-gradient terms (GX), per chunk parity and compute wave, per token of the chunk:
+  // GX 1: column sums of P, row sums of P, r; GX 2: u, and the crossing term in gx_r[.][.][0]
+  static constexpr int GXP = GX ? 2 : 1, GXW = GX ? W::NCW : 1, GXT = GX ? 64 : 1;
+  float gx_a[GXP][GXW][GXT];
+  float gx_c[GX == 1 ? 2 : 1][GX == 1 ? W::NCW : 1][GX == 1 ? 64 : 1];
+  float gx_r[GXP][GXW][GXT];
 };
 
 // Physical 16-byte piece of logical piece p in row r of the raw q/k tiles: the
@@ -212,12 +218,45 @@ __device__ __forceinline__ void diagonal_pairs(bf16* a, const bf16* qr, const bf
   Elem<bf16>::store4(a + (u * 16 + j) * TLD + u * 16 + iq * 4, vals[0], vals[1], vals[2], vals[3]);
 }
 
-template <int DK, int DVS, bool DIAG>
+// ---------------------------------------------------------------- gate-gradient terms
+// The backward pass's dL/dg_t is the sum over the pairs (key token s, output token j)
+// that span t (s < t <= j); per chunk c they fall into four groups (listed with the dx
+// kernel in bwd_kernels.hip).  With GX != 0 the dq pass (forward time, holding S_{c-1})
+// and the dk pass (reversed time, holding D = dL/dS after the chunk) form them beside
+// their own outputs, so that no further pass re-reads q, k, v and dO:
+//   GX 1, dq pass: (1) the pairs inside the chunk, P_js = A_js (q_j . k_s) for s < j, from
+//     the pass's own score tile A_js = e^{b_j - b_s}(dO_j . v_s) and q, which the compute
+//     waves read themselves, 32 columns each (a wave's share of q_j . k_s is one MFMA per
+//     tile, and the row and column sums of P are linear in it); (2) the pairs entering,
+//     r_j = q_j . (e^{b_j} S_{c-1}^T dO_j), q dotted with the pass's inter-chunk output
+//     term before the intra-chunk term is added.  W_t = (exclusive prefix over the chunk of
+//     column sum - row sum of P) + (inclusive suffix of r) -> gx_out.  It also stores
+//     S_{c-1} (bf16) wherever the crossing factor a e^gamma of chunk c is not exactly 0.
+//   GX 2, dk pass: (3) the pairs leaving, u_s = k_s . (a e^{gamma - b_s} D v_s): the pass's
+//     inter-chunk output term for token s dotted with k (the reversed pass's cumulative
+//     decay at s is exactly log a + gamma - b_s); (4) the pairs crossing the chunk whole,
+//     a e^gamma <D, S_{c-1}>, with S_{c-1} from the dq pass; then
+//     dx_t = g'(x_t) (W_t + exclusive prefix of u + (4)) -> gx_out.
+// a e^gamma (a the decay of the first token after the chunk, 1 after the last chunk) is
+// formed by both passes from the same two entries of the forward b buffer with the same
+// operations, so they agree exactly on the chunks where it is 0: there the dq pass stores
+// no state and the dk pass reads none (the term is exactly 0).
+__device__ __forceinline__ float gx_cross_factor(float b_end, float b_next) { return exp_e(b_end + b_next); }
+
+// Offset (elements) of compute wave cw's 32-column group of the bf16 state stored for chunk
+// pc, in the fragment order of store_chunk_state.
+template <int DK>
+__device__ __forceinline__ long long gx_state_offset(const ChunkParams& p, int bh, int pc, int cw) {
+  return (((long long)bh * p.nchunks + pc) * (p.dv / 32) + cw) * 2LL * (DK / 16) * 256;
+}
+
+template <int DK, int DVS, bool DIAG, int GX = 0>
 __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_kernel(ChunkParams p) {
   using W = WsCfg<DK, DVS, DIAG>;
   using C = typename W::C;
   using E = Elem<bf16>;
-  __shared__ __attribute__((aligned(16))) WsSmem<DK, DVS, DIAG> sm;  // 16-byte aligned: row stores compile to ds_write_b128
+  static_assert(GX == 0 || (!DIAG && DVS == 128), "gate-gradient terms: unified path, one 128-column slice");
+  __shared__ __attribute__((aligned(16))) WsSmem<DK, DVS, DIAG, GX> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool compute = wave < W::NCW;  // wave-uniform role
@@ -248,14 +287,65 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
   // loop, two per chunk), so that the registers of one role are free for the
   // other: the compute waves hold the state and o accumulators, the staging waves
   // two register sets of prefetched chunks.
+  // gate-gradient terms: physical chunk of logical chunk c, and the operands of the
+  // crossing factor of chunk c (last token's b, next chunk's first b) from the forward b
+  const float* gxb = GX ? p.gx_b + span.row0 : nullptr;
+  const long long Tg = (long long)hb.T;
+  const auto gx_phys = [&](int c) { return p.reverse ? p.nchunks - 1 - c : c; };
+  const auto gx_cross_load = [&](int c, float& be, float& bn) {
+    const int pc = gx_phys(c);
+    const long long e = min((long long)pc * kChunk + kChunk - 1, Tg - 1), n = (long long)(pc + 1) * kChunk;
+    be = gxb[e];
+    bn = n < Tg ? gxb[n] : 0.0f;
+  };
   if (compute) {
     StateAcc<bf16, DK, DVS> S;
     load_initial_state<bf16, DK, DVS>(S, p, bh, seg, wcol, g, r16);
+    // GX: the operand this pass lacks (q or k), rows of the unit, p.dv columns
+    const rsrc_t gxop = GX ? make_rsrc(static_cast<const bf16*>(p.gx_op) + span.row0 * p.dv, hb.T * (uint32_t)p.dv * 2u)
+                           : make_rsrc(nullptr, 0u);
+    bf16* gx_st = GX ? static_cast<bf16*>(p.gx_states) : nullptr;
+    float gx_be = 0.0f, gx_bn = 0.0f;  // GX 2: crossing-factor operands, loaded one chunk ahead
+    if constexpr (GX == 2) {
+      if (c_begin < c_end) gx_cross_load(c_begin, gx_be, gx_bn);
+    }
     __syncthreads();
     for (int c = c_begin; c < c_end; ++c) {
       const int slot = (c - c_begin) & 1;
       const uint32_t t0 = (uint32_t)c * kChunk;
       if (p.state_out) store_chunk_state<bf16, DK, DVS>(S, p, bh, c, wcol, lane);
+      // GX: this wave's 32 columns of q (GX 1) or k (GX 2) for the chunk's tokens, four
+      // consecutive columns per lane: [t0 + 16 jb + r16][wcol + 16 nb + 4 g ..]
+      [[maybe_unused]] uint2 gxo[4][2];
+      [[maybe_unused]] float gxf = 0.0f;         // crossing factor a e^gamma of this chunk (wave-uniform)
+      [[maybe_unused]] uint2 gxs[C::NB][C::DB];  // GX 2: S_{c-1} where gxf != 0
+      if constexpr (GX != 0) {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            gxo[jb][nb] = buf_load8(gxop, row_offset(p, hb.T, t0 + jb * 16 + r16, (uint32_t)p.dv * 2u) +
+                                              (uint32_t)(wcol + nb * 16 + 4 * g) * 2u);
+        if constexpr (GX == 1) {
+          float be, bn;
+          gx_cross_load(c, be, bn);
+          gxf = gx_cross_factor(be, bn);
+        } else {
+          gxf = gx_cross_factor(gx_be, gx_bn);
+          if (c + 1 < c_end) gx_cross_load(c + 1, gx_be, gx_bn);
+        }
+        gxf = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, gxf)));
+        if constexpr (GX == 2) {
+          if (gxf != 0.0f) {
+            const bf16* src = gx_st + gx_state_offset<DK>(p, bh, gx_phys(c), cw);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+              for (int db = 0; db < C::DB; ++db)
+                gxs[nb][db] = *reinterpret_cast<const uint2*>(src + ((nb * C::DB + db) * 64 + lane) * 4);
+          }
+        }
+      }
 
       // ---- part 1: off-diagonal tiles of A(c)
       const ChunkDecay cd(sm.sb[lane]);
@@ -266,14 +356,94 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         const float ri = DIAG ? cd.end(ib) : cd.r(ib);
         attention_tile<DK, W::TLD, W::LD>(sm.a, sm.qh[slot], sm.kh, jb, ib, exp_e(cd.r(jb) - ri), g, r16);
       }
+      if constexpr (GX == 2) {
+        // (4), at the end of part 1 so that S_{c-1} is not held further: <D, S_{c-1}> over this wave's slice, times a e^gamma
+        float z = 0.0f;
+        if (gxf != 0.0f) {
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db) {
+              const bf16x4 s4 = __builtin_bit_cast(bf16x4, gxs[nb][db]);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) z += S.s[nb][db][e] * static_cast<float>(s4[e]);
+            }
+          z = row_sum4(group_sum<16>(z));  // all 64 lanes
+        }
+        if (lane == 0) sm.gx_r[slot][cw][0] = gxf * z;
+      }
       __syncthreads();
 
       // ---- part 2: o(c) and S_c
+      if constexpr (GX == 1) {
+        // (1): this wave's share of q_j . k_s (its 32 columns) on the 10 causal tiles, times
+        // A_js, reduced to row sums (over s < j) and column sums (over j > s)
+        typename E::Frag qf[4], kf[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+          qf[jb].v = __builtin_shufflevector(__builtin_bit_cast(bf16x4, gxo[jb][0]), __builtin_bit_cast(bf16x4, gxo[jb][1]),
+                                             0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) kf[ib] = E::load_frag(sm.vv[slot] + (ib * 16 + r16) * W::VLD, cw * C::CPW + 4 * g);
+        floatx4 colP[4];
+        float rowP[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          colP[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+          rowP[u] = 0.0f;
+        }
+#pragma unroll
+        for (int t = 0; t < 10; ++t) {
+          const int jb = tri_j(t), ib = tri_i(t);
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+          E::mfma(acc, kf[ib], qf[jb]);  // acc[e]: k_s . q_j over the wave's columns, j = 16 jb + r16, s = 16 ib + 4 g + e
+          GLA_CHECK_LDS(sm.a + (jb * 16 + r16) * W::TLD + ib * 16 + 4 * g, 8);
+          const bf16x4 a4 = *reinterpret_cast<const bf16x4*>(sm.a + (jb * 16 + r16) * W::TLD + ib * 16 + 4 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float pe = (jb != ib || 4 * g + e < r16) ? acc[e] * static_cast<float>(a4[e]) : 0.0f;
+            colP[ib][e] += pe;
+            rowP[jb] += pe;
+          }
+        }
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const float rs = row_sum4(rowP[jb]);
+          if (g == 0) sm.gx_c[slot][cw][jb * 16 + r16] = rs;
+        }
+        // column sums over the 16 lanes of a row group (DPP row shifts; total in the last lane)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float col = colP[ib][e];
+            col += dpp_or_zero<0x111>(col);  // row_shr:1
+            col += dpp_or_zero<0x112>(col);  // row_shr:2
+            col += dpp_or_zero<0x114>(col);  // row_shr:4
+            col += dpp_or_zero<0x118>(col);  // row_shr:8
+            if (r16 == 15) sm.gx_a[slot][cw][ib * 16 + 4 * g + e] = col;
+          }
+      }
       typename E::Frag Sf[C::NB][C::KS];
 #pragma unroll
       for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) Sf[nb][ks] = E::from_acc(S.s[nb][2 * ks], S.s[nb][2 * ks + 1]);
+      if constexpr (GX == 1) {
+        // S_{c-1} for the dk pass's crossing term, where its factor is not exactly 0
+        if (gxf != 0.0f) {
+          bf16* dst = gx_st + gx_state_offset<DK>(p, bh, c, cw);
+#pragma unroll
+          for (int nb = 0; nb < C::NB; ++nb)
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+              *reinterpret_cast<bf16x4*>(dst + ((nb * C::DB + 2 * ks) * 64 + lane) * 4) =
+                  __builtin_shufflevector(Sf[nb][ks].v, Sf[nb][ks].v, 0, 1, 2, 3);
+              *reinterpret_cast<bf16x4*>(dst + ((nb * C::DB + 2 * ks + 1) * 64 + lane) * 4) =
+                  __builtin_shufflevector(Sf[nb][ks].v, Sf[nb][ks].v, 4, 5, 6, 7);
+            }
+        }
+      }
       VFrags<bf16, DK, DVS> Vf;
       load_v_frags<bf16, DK, DVS, W::VLD>(Vf, sm.vv[slot], cw, lane);
 
@@ -297,6 +467,22 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         const float f = exp_e(cd.r(jb));
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) O[jb][nb] *= f;
+      }
+      if constexpr (GX != 0) {
+        // (2) r_j (GX 1) or (3) u_s (GX 2): the inter-chunk term of the output row dotted
+        // with q or k over this wave's columns
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          float d = 0.0f;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const bf16x4 o4 = __builtin_bit_cast(bf16x4, gxo[jb][nb]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d += static_cast<float>(o4[e]) * O[jb][nb][e];
+          }
+          d = row_sum4(d);
+          if (g == 0) (GX == 1 ? sm.gx_r : sm.gx_a)[slot][cw][jb * 16 + r16] = d;
+        }
       }
       // intra-chunk: O^T[n][j] += sum_i v[n][i] A[j][i], keys up to the end of tile jb
 #pragma unroll
@@ -370,6 +556,56 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         attention_tile<DK, W::TLD, W::LD>(sm.a, sm.qh[(c - c_begin) & 1], sm.kh, sw, sw, 1.0f, g, r16);
       }
     };
+    // GX: the last staging wave combines the compute waves' sums of chunk c during part 1
+    // of chunk c + 1 (the sums alternate between two LDS buffers by chunk parity), the
+    // last chunk's after the loop.  One lane per token of the chunk.
+    const bool gx_wave = GX != 0 && sw == W::NSW - 1;
+    float* gx_out = GX ? p.gx_out + span.row0 : nullptr;
+    const float* gx_x = GX == 2 ? p.gx_x + span.row0 : nullptr;
+    float gx_xv = 0.0f, gx_wv = 0.0f;  // GX 2: x and W of the chunk combined next (loaded one chunk ahead)
+    const auto gx_token = [&](int cc) -> long long {  // physical token of this lane's row of chunk cc
+      const long long tl = (long long)cc * kChunk + lane;
+      return p.reverse ? Tg - 1 + p.pad - tl : tl;
+    };
+    const auto gx_fetch = [&](int cc) {
+      const long long t = gx_token(cc);
+      const bool in = t >= 0 && t < Tg;
+      gx_xv = in ? gx_x[t] : 0.0f;
+      gx_wv = in ? gx_out[t] : 0.0f;
+    };
+    const auto gx_combine = [&](int cc) {
+      const int par = (cc - c_begin) & 1;
+      const long long t = gx_token(cc);
+      if constexpr (GX == 1) {
+        float col = 0.0f, row = 0.0f, r = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W::NCW; ++w) {
+          col += sm.gx_a[par][w][lane];
+          row += sm.gx_c[par][w][lane];
+          r += sm.gx_r[par][w][lane];
+        }
+        // pairs inside: exclusive prefix of (column sum - row sum); entering: inclusive suffix of r
+        const float d = col - row;
+        const float R = wave_inclusive_scan(d, lane) - d;
+        const float rincl = wave_inclusive_scan(r, lane);
+        const float rsuf = lane_value(rincl, 63) - rincl + r;
+        if (t < Tg) gx_out[t] = R + rsuf;
+      } else if constexpr (GX == 2) {
+        float u = 0.0f, z = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W::NCW; ++w) {
+          u += sm.gx_a[par][w][lane];
+          z += sm.gx_r[par][w][0];
+        }
+        // leaving: the sum over the physically earlier tokens of the chunk = later rows here
+        const float uincl = wave_inclusive_scan(u, lane);
+        const float uex = lane_value(uincl, 63) - uincl;
+        const float slope = p.gate == kGateBoundedSigmoid ? gate_slope<kGateBoundedSigmoid>(gx_xv)
+                                                          : gate_slope<kGateNegSoftplus>(gx_xv);
+        if (t >= 0 && t < Tg) gx_out[t] = slope * (gx_wv + uex + z);
+        if (cc + 1 < c_end) gx_fetch(cc + 1);
+      }
+    };
     // Register set s0 holds the chunks at even offsets from c_begin, s1 the odd
     // ones; chunk c+1 is staged during chunk c, and the loads of chunk c+3 are
     // issued right after into the freed set, two chunks ahead of their use.
@@ -379,6 +615,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
       stage(s0, 0);
       s1.load(hb, p, chunk_t0(c_begin + 1), col0, st);
       s0.load(hb, p, chunk_t0(c_begin + 2), col0, st);
+      if (GX == 2 && gx_wave) gx_fetch(c_begin);
     }
     __syncthreads();
     // Chunks are taken in pairs so that each set is named statically; staging and
@@ -388,11 +625,13 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
     int c = c_begin;
     for (; c + 1 < c_end; c += 2) {
       diagonal(c);
+      if (gx_wave && c > c_begin) gx_combine(c - 1);
       __syncthreads();
       stage(s1, 1);
       s1.load(hb, p, chunk_t0(c + 3), col0, st);
       __syncthreads();
       diagonal(c + 1);
+      if (gx_wave) gx_combine(c);
       __syncthreads();
       stage(s0, 0);
       s0.load(hb, p, chunk_t0(c + 4), col0, st);
@@ -400,9 +639,11 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
     }
     if (c < c_end) {  // odd number of chunks: the last one has nothing to stage after it
       diagonal(c);
+      if (gx_wave && c > c_begin) gx_combine(c - 1);
       __syncthreads();
       __syncthreads();
     }
+    if (gx_wave && c_begin < c_end) gx_combine(c_end - 1);
     // no loads left in flight when the wave ends
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -528,6 +769,17 @@ hipError_t ws_seg_launch(const ChunkParams& p, hipStream_t s) {
 
 template <int DK, int DVS, bool DIAG>
 hipError_t ws_launch(const ChunkParams& p, hipStream_t s) {
+  if constexpr (DK == 128 && DVS == 128 && !DIAG) {
+    if (p.gx_mode == 1) {
+      hipLaunchKernelGGL((chunk_output_ws_kernel<DK, DVS, DIAG, 1>), dim3(p.grid), dim3(WsCfg<DK, DVS, DIAG>::NT), 0, s, p);
+      return hipGetLastError();
+    }
+    if (p.gx_mode == 2) {
+      hipLaunchKernelGGL((chunk_output_ws_kernel<DK, DVS, DIAG, 2>), dim3(p.grid), dim3(WsCfg<DK, DVS, DIAG>::NT), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  if (p.gx_mode != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL((chunk_output_ws_kernel<DK, DVS, DIAG>), dim3(p.grid), dim3(WsCfg<DK, DVS, DIAG>::NT), 0, s, p);
   return hipGetLastError();
 }
