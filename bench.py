@@ -557,7 +557,7 @@ def delta_result(gla, gin, torch, steps, warmup, cpu_seconds, settle_s=0.3):
     return res
 
 
-def backward_result(gla, gin, torch, w, path, steps, warmup, settle_s=0.3):
+def backward_result(gla, gin, torch, w, path, steps, warmup, settle_s=0.3, weak=False):
     t = BackwardTimer(gla, gin, torch, w, path)
     ms_host, ms_ev = t.run(steps, warmup, settle_s)
     B, H, T, dk, dv = t.shape
@@ -567,7 +567,7 @@ def backward_result(gla, gin, torch, w, path, steps, warmup, settle_s=0.3):
     nbytes = bh * T * backward_bytes_per_token_head(dk, dv, es) + bh * dk * dv * 4 * 3
     flops = bh * T * backward_flops_per_token_head(dk, dv)
     achieved = nbytes / (ms_ev / 1e3) / 1e9
-    return {
+    res = {
         "what": "gla_chunk_bwd: dq, dk, dv, dx, dS0 from dO and dS_T (all kernels of the call)",
         "steps": steps,
         "ms_per_call": round(ms_host, 4),
@@ -577,6 +577,19 @@ def backward_result(gla, gin, torch, w, path, steps, warmup, settle_s=0.3):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_call": nbytes},
     }
+    if weak:
+        # the same call where no chunk's crossing factor a e^gamma is exactly 0: the dq pass
+        # then stores, and the dk pass reads, the state of every chunk
+        ww = w.with_(x_mean=-6.0, x_std=1.0)
+        tw = BackwardTimer(gla, gin, torch, ww, path)
+        steps_w = max(steps // 2, 5)
+        _, ms_w = tw.run(steps_w, warmup, 0.0)
+        del tw
+        res["weak_decay"] = {
+            "what": "same shapes, x ~ N(-6,1): every chunk's state is stored by the dq pass and read by the dk pass",
+            "x": f"N({ww.x_mean},{ww.x_std})", "steps": steps_w, "ms_per_call_events": round(ms_w, 4),
+            "tokens_per_s": round(B * T / (ms_w / 1e3), 1)}
+    return res
 
 
 def main():
@@ -729,7 +742,7 @@ def main():
             "tokens_per_s": round(ww.B * ww.T / (ms_w / 1e3), 1)}
     if not args.no_backward and not args.plan:
         result["backward"] = backward_result(gla, gin, torch, w, path, min(args.steps, 20), min(args.warmup, 5),
-                                             args.settle_s)
+                                             args.settle_s, weak=True)
         if not args.no_cpu_baseline:
             result["backward"]["cpu_baseline"] = cpu_baseline_backward(w, args.cpu_seconds / 2)
     if not args.no_per_channel and not args.plan and w.name == gin.HEADLINE:

@@ -72,6 +72,23 @@ def test_bf16_backward_decay_regimes(regime, x_mean):
     check(w, inp, dO, dST)
 
 
+def test_bf16_backward_mixed_crossing_factors():
+    """Chunks whose crossing factor a e^gamma is exactly 0 in fp32 (strongly decaying
+    chunks, x = 4) beside chunks where it is not (x = -6, and x = -0.79, a chunk log-decay
+    near -100 whose factor is tiny or flushed), in an irregular pattern across several
+    segments: at d = 128 the dq pass stores, and the dk pass reads, only the states that
+    the crossing term needs."""
+    T = 64 * 40 + 9
+    w, inp, dO, dST = make(T, H=2, x_mean=-6.0)
+    x = inp["x"]
+    for c in (1, 2, 5, 9, 10, 11, 17, 30, 31, 39):
+        x[:, :, 64 * c:64 * c + 64] += 10.0
+    for c in (6, 20, 33):
+        x[:, :, 64 * c:64 * c + 64] = -0.79
+    x[:, 1, 64 * 24:64 * 24 + 40] = 6.0  # one head only: a chunk strong in part
+    check(w, inp, dO, dST)
+
+
 def test_bf16_backward_segmented_plans():
     """Long enough for the default plans of every pass to use several segments."""
     w, inp, dO, dST = make(64 * 64 + 31, H=2)
