@@ -240,11 +240,17 @@ gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, con
  * output token j) pairs whose decay path spans t (s < t <= j, with j = "after the
  * end" for the final state), taken per chunk: pairs inside the chunk from q.k and
  * dO.v on the matrix cores, pairs that enter or leave the chunk from the states
- * before and after it, and pairs that cross it whole; dx = g'(x) dL/dg.  The dq
- * and dk passes store one of those states per pair of chunks (bf16 for bf16
- * operands) and the dx kernel steps the other one across the neighbouring chunk.  Each pass uses the device's default plan; the dq and
- * dk passes need value slices of at least 32 columns (GLA_ERR_UNSUPPORTED
- * otherwise, which the default plans never give).
+ * before and after it, and pairs that cross it whole; dx = g'(x) dL/dg.  bf16
+ * with dk = dv = 128 on the unified path: the dq pass forms the pairs inside and
+ * entering each chunk (it holds the state before the chunk) and the dk pass the
+ * pairs leaving and crossing it (it holds the state gradient after the chunk), the
+ * dq pass handing over the state before each chunk whose crossing factor is not
+ * exactly 0; both passes then run with one full-width slice.  Otherwise the dq and
+ * dk passes store one state per pair of chunks (bf16 for bf16 operands) and a
+ * separate dx kernel steps the other one across the neighbouring chunk.  Each pass
+ * uses the device's default plan; the dq and dk passes need value slices of at
+ * least 32 columns (GLA_ERR_UNSUPPORTED otherwise, which the default plans never
+ * give).
  * workspace == NULL: *workspace_bytes receives the size and nothing is enqueued;
  * otherwise the workspace (256-byte aligned device memory) must be at least that
  * size.  Errors as gla_chunk_fwd; everything is validated before anything is
