@@ -107,6 +107,15 @@ def test_bf16_backward_diag_branch(gate, x_mean):
     check(w, inp, dO, dST, gate=gate, path="diag_branch")
 
 
+@pytest.mark.parametrize("x_mean", [0.0, 3.0])
+def test_bf16_backward_softplus_gate_unified_path(x_mean):
+    """The negative-softplus gate on the unified path at d = 128 (gate gradient inside the
+    dq and dk passes, with that gate's slope sigmoid(-x)); decays mild enough that every
+    16-token tile stays in range (x ~ N(0,1): about -0.7 per token; N(3,1): weak)."""
+    w, inp, dO, dST = make(64 * 12 + 21, H=2, x_mean=x_mean, gate="neg_softplus")
+    check(w, inp, dO, dST, gate="neg_softplus", path="unified")
+
+
 @pytest.mark.parametrize("T,dk,dv", [(64 * 4 + 3, 64, 64), (64 * 5 + 17, 128, 128), (64 * 2, 128, 64), (64 * 3, 64, 128)])
 def test_fp32_backward(T, dk, dv):
     """fp32 operands at every head size: odd chunks rebuild the state before them and
