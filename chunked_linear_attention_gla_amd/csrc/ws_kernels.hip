@@ -283,10 +283,6 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
     sm.a[(blk * 32 + rr) * W::TLD + blk * 32 + 16 + cc] = E::cvt(0.0f);
   }
 
-  // The two roles run separate loops with the same barriers (one before the
-  // loop, two per chunk), so that the registers of one role are free for the
-  // other: the compute waves hold the state and o accumulators, the staging waves
-  // two register sets of prefetched chunks.
   // gate-gradient terms: physical chunk of logical chunk c, and the operands of the
   // crossing factor of chunk c (last token's b, next chunk's first b) from the forward b
   const float* gxb = GX ? p.gx_b + span.row0 : nullptr;
@@ -298,6 +294,11 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
     be = gxb[e];
     bn = n < Tg ? gxb[n] : 0.0f;
   };
+
+  // The two roles run separate loops with the same barriers (one before the
+  // loop, two per chunk), so that the registers of one role are free for the
+  // other: the compute waves hold the state and o accumulators, the staging waves
+  // two register sets of prefetched chunks.
   if (compute) {
     StateAcc<bf16, DK, DVS> S;
     load_initial_state<bf16, DK, DVS>(S, p, bh, seg, wcol, g, r16);
@@ -357,7 +358,8 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
         attention_tile<DK, W::TLD, W::LD>(sm.a, sm.qh[slot], sm.kh, jb, ib, exp_e(cd.r(jb) - ri), g, r16);
       }
       if constexpr (GX == 2) {
-        // (4), at the end of part 1 so that S_{c-1} is not held further: <D, S_{c-1}> over this wave's slice, times a e^gamma
+        // (4): <D, S_{c-1}> over this wave's slice, times a e^gamma; at the end of part 1
+        // so that S_{c-1} is not held into part 2
         float z = 0.0f;
         if (gxf != 0.0f) {
 #pragma unroll
