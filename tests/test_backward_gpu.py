@@ -107,6 +107,13 @@ def test_bf16_backward_diag_branch(gate, x_mean):
     check(w, inp, dO, dST, gate=gate, path="diag_branch")
 
 
+def test_bf16_backward_batched():
+    """B = 2: the (batch, head) units of every pass, the per-chunk states handed from the
+    dq to the dk pass and the per-token dx terms are indexed by b * H + h."""
+    w, inp, dO, dST = make(64 * 7 + 9, H=3, B=2, x_mean=-3.0)
+    check(w, inp, dO, dST)
+
+
 @pytest.mark.parametrize("x_mean", [0.0, 3.0])
 def test_bf16_backward_softplus_gate_unified_path(x_mean):
     """The negative-softplus gate on the unified path at d = 128 (gate gradient inside the
