@@ -372,9 +372,9 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
   if (!valid_gate(gate) || !valid_path(path)) return GLA_ERR_ARG;
   // plans of the three passes: dq and dk run with state dims (dv, dk), dv with (dk, dv)
   gla_plan_t pa, pc;
-  // bf16 at dk = dv = 128 on the unified path: the gate gradient is formed inside the dq and
-  // dk passes (one full-width slice each) instead of by the dx kernel
-  const bool fused_dx = T > 0 && dtype == GLA_BF16 && dk_ == 128 && dv_ == 128 && path == GLA_PATH_UNIFIED;
+  // bf16 on the unified path: the gate gradient is formed inside the dq and dk passes (one
+  // full-width slice each) instead of by the dx kernel
+  const bool fused_dx = T > 0 && dtype == GLA_BF16 && path == GLA_PATH_UNIFIED;
   if (T > 0) {
     st = gla_plan_default(B, H, T, dv_, dk_, dtype, path, &pa);
     if (st != GLA_OK) return st;

@@ -26,8 +26,8 @@
 // rebuilds the other state of each chunk from its pair's neighbour chunk.
 // dH_c = a_{first token of c+1} D (dS_T after the last chunk).
 // dx_t = g'(x_t) dL/dg_t with g' the slope of the gate of §3.2.
-// This kernel serves the configurations other than bf16 at dk = dv = 128 on the unified
-// path; there the same four groups are formed inside the dq and dk passes (the gate-
+// This kernel serves the fp32 operands and the diagonal-branch path; for bf16 on the
+// unified path the same four groups are formed inside the dq and dk passes (the gate-
 // gradient terms of chunk_output_ws_kernel in ws_kernels.hip).
 #include "chunk_common.h"
 

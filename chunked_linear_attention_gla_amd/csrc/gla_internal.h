@@ -51,17 +51,17 @@ struct ChunkParams {
   const int* unit_order;  // packed sequences: sequence indices, longest first (the work
                           //    order); nullptr: dense order
   // Backward pass, gradient of the gate folded into the dq and dk passes (dense bf16
-  // layout, one 128-column slice; see the pair terms in bwd_kernels.hip):
+  // layout, one full-width slice; see the pair terms in bwd_kernels.hip):
   int gx_mode;            // 0: none.  1 (dq pass, forward time): the pairs inside each chunk
                           //    and the pairs entering it, W_t -> gx_out; the state before every
                           //    chunk whose crossing factor is not exactly 0 -> gx_states.
                           //    2 (dk pass, reversed time): the pairs leaving each chunk and
                           //    those crossing it, dx_t = g'(x_t) (W_t + ...) -> gx_out
-  const void* gx_op;      // [BH][T][128]: q (mode 1) or k (mode 2), the operand the pass lacks
+  const void* gx_op;      // [BH][T][dv]: q (mode 1) or k (mode 2), the operand the pass lacks
   const float* gx_b;      // [BH][T] forward chunk-local cumulative log-decay
   const float* gx_x;      // [BH][T] gate pre-activation (mode 2: the slope g'(x))
   float* gx_out;          // [BH][T] W (mode 1 writes it, mode 2 reads it and writes dx)
-  void* gx_states;        // [BH][nchunks][128 x 128] bf16 states in fragment order
+  void* gx_states;        // [BH][nchunks][dk x dv] bf16 states in fragment order
 };
 
 // Byte offset of logical token t's row in a per-unit tensor of T rows with rows of

@@ -255,7 +255,7 @@ __global__ void __launch_bounds__((WsCfg<DK, DVS, DIAG>::NT)) chunk_output_ws_ke
   using W = WsCfg<DK, DVS, DIAG>;
   using C = typename W::C;
   using E = Elem<bf16>;
-  static_assert(GX == 0 || (!DIAG && DVS == 128), "gate-gradient terms: unified path, one 128-column slice");
+  static_assert(GX == 0 || (!DIAG && DVS >= 64), "gate-gradient terms: unified path, one full-width slice");
   __shared__ __attribute__((aligned(16))) WsSmem<DK, DVS, DIAG, GX> sm;  // 16-byte aligned: row stores compile to ds_write_b128
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -771,7 +771,9 @@ hipError_t ws_seg_launch(const ChunkParams& p, hipStream_t s) {
 
 template <int DK, int DVS, bool DIAG>
 hipError_t ws_launch(const ChunkParams& p, hipStream_t s) {
-  if constexpr (DK == 128 && DVS == 128 && !DIAG) {
+  if constexpr (DVS >= 64 && !DIAG) {
+    // the gate-gradient terms need the whole value width in one workgroup
+    if (p.gx_mode != 0 && p.nslices != 1) return hipErrorInvalidValue;
     if (p.gx_mode == 1) {
       hipLaunchKernelGGL((chunk_output_ws_kernel<DK, DVS, DIAG, 1>), dim3(p.grid), dim3(WsCfg<DK, DVS, DIAG>::NT), 0, s, p);
       return hipGetLastError();

@@ -241,7 +241,7 @@ gla_status_t gla_chunk_fwd_plan(const void* q, const void* k, const void* v, con
  * end" for the final state), taken per chunk: pairs inside the chunk from q.k and
  * dO.v on the matrix cores, pairs that enter or leave the chunk from the states
  * before and after it, and pairs that cross it whole; dx = g'(x) dL/dg.  bf16
- * with dk = dv = 128 on the unified path: the dq pass forms the pairs inside and
+ * on the unified path: the dq pass forms the pairs inside and
  * entering each chunk (it holds the state before the chunk) and the dk pass the
  * pairs leaving and crossing it (it holds the state gradient after the chunk), the
  * dq pass handing over the state before each chunk whose crossing factor is not

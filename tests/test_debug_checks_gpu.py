@@ -82,7 +82,7 @@ def test_delta_rule(qkv, d):
                                                     plan=gla.Plan(3, 1)))
 
 
-@pytest.mark.parametrize("qkv,d,T", [("bf16", 128, 64 * 5 + 3), ("f32", 128, 64 * 3 + 1)])
+@pytest.mark.parametrize("qkv,d,T", [("bf16", 128, 64 * 5 + 3), ("bf16", 64, 64 * 4 + 9), ("f32", 128, 64 * 3 + 1)])
 def test_backward(qkv, d, T):
     w, inp = small("bf16_8k", B=1, H=2, T=T, dk=d, dv=d, qkv_dtype=qkv)
     gen = torch.Generator(device=device()).manual_seed(77)
