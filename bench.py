@@ -85,6 +85,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="bf16_64k_strong")
+    ap.add_argument("--x-mean", type=float, default=None,
+                    help="override the workload's gate-input mean (e.g. -6 for the weak-decay regime; profiling)")
     ap.add_argument("--path", default=None, help="unified (default) or diag_branch")
     ap.add_argument("--plan", default=None, help="segments,dv_split (default: the library's plan)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target length of the oracle sample")
@@ -607,6 +609,8 @@ def main():
     from chunked_linear_attention_gla_amd import inputs as gin
 
     w = gin.WORKLOADS[args.workload]
+    if args.x_mean is not None:
+        w = w.with_(x_mean=args.x_mean)
     path = args.path or "unified"
     torch.cuda.set_device(torch.device("cuda:0"))
     plan = gla.Plan(*(int(s) for s in args.plan.split(","))) if args.plan else None
@@ -643,8 +647,9 @@ def main():
                                                             args.settle_s)}), flush=True)
         return
     if args.backward_only:
-        print(json.dumps({"workload": w.name, "backward": backward_result(gla, gin, torch, w, path, args.steps,
-                                                                         args.warmup, args.settle_s)}), flush=True)
+        print(json.dumps({"workload": w.name, "x": f"N({w.x_mean},{w.x_std})",
+                          "backward": backward_result(gla, gin, torch, w, path, args.steps, args.warmup,
+                                                      args.settle_s)}), flush=True)
         return
     timer = StepTimer(gla, gin, torch, w, path, plan)
     plan = timer.plan
