@@ -2,15 +2,22 @@
 counts, head sizes, launch plans, gates, paths, decay regimes and the optional states
 are drawn from fixed seeds, and each call is checked against the fp64 oracles at the
 same bars as the targeted tests (2e-2 with bf16 operands, 1e-4 on the fp32 path).
+Entry points: forward, backward, per-channel forward, delta rule, packed sequences and
+the decode step.
 
 The negative-softplus gate runs on the diagonal-branch path, and on the unified path
 only where its decays stay mild (x >= 0): that gate has no lower bound, so strong decays
 can take a 16-token tile past the range the unified path relies on."""
 import numpy as np
 import pytest
+import torch
 
+import oracle
 import chunked_linear_attention_gla_amd as gla
+from chunked_linear_attention_gla_amd import inputs as gin
+from gpu_util import TOL, rel
 import test_backward_gpu as bw
+import test_decode_varlen_gpu as dv_
 import test_delta_gpu as dl
 import test_parity_gpu as fw
 import test_pc_gpu as pcm
@@ -78,3 +85,45 @@ def test_delta_rule(case):
     w, inp = dl.make(c["T"], H=c["H"], B=c["B"], dk=c["dk"], dv=c["dv"], x_mean=c["x_mean"], x_std=c["x_std"],
                      s0=c["s0"], seed=400 + case)
     dl.check(w, inp, plan=plan(r, c["T"], c["dv"]))
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_packed_sequences(case):
+    r = np.random.default_rng(9400 + case)
+    c = common(r)
+    n = int(r.integers(1, 9))
+    lengths = [int(L) for L in r.choice([0, 1, 17, 63, 64, 65, 200, 700, 1500], size=n)]
+    if sum(lengths) == 0:
+        lengths.append(33)
+    gate, path = gate_path(r, c["x_mean"])
+    w = dv_.VAR.with_(H=c["H"], dk=c["dk"], dv=c["dv"], x_mean=c["x_mean"], x_std=c["x_std"], s0_std=c["s0"],
+                      gate=gate)
+    nc = max(1, -(-max(lengths) // 64))
+    segs = int(r.integers(1, min(4, nc) + 1))
+    dv_.varlen_check(w, lengths, gate=gate, path=path, seed=500 + case,
+                     plan=gla.Plan(segs, 1) if r.random() < 0.5 else None)
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_decode_step(case):
+    r = np.random.default_rng(9500 + case)
+    c = common(r)
+    gate = str(r.choice(["bounded", "neg_softplus"]))
+    per_channel = bool(r.random() < 0.5)
+    qkv = "f32" if (c["dk"] == 64 and c["dv"] == 64 and r.random() < 0.3) else "bf16"
+    B, H, dk, dv = int(r.integers(1, 9)), int(r.integers(1, 9)), c["dk"], c["dv"]
+    w = dv_.DEC.with_(B=B, H=H, dk=dk, dv=dv, qkv_dtype=qkv, per_channel=per_channel, gate=gate,
+                      x_mean=c["x_mean"], x_std=c["x_std"])
+    inp = gin.make_decode_inputs(w, fw.device(), seed=600 + case)
+    S_in = inp["S"].clone()
+    o = gla.decode_step(inp["q"], inp["k"], inp["v"], inp["x"], inp["S"], gate=gate)
+    torch.cuda.synchronize()
+    BH = B * H
+    flat = lambda t: t.reshape(BH, 1, *t.shape[2:])
+    q, k, v = (gin.to_numpy_bits(flat(inp[n])) for n in ("q", "k", "v"))
+    x = gin.to_numpy_bits(inp["x"].reshape(BH, 1, *inp["x"].shape[2:]))
+    fwd = oracle.forward_pc if per_channel else oracle.forward
+    o_ref, S_ref = fwd(q, k, v, x, S_in.reshape(BH, dk, dv).cpu().numpy().astype(np.float64), gate=gate)
+    tol = TOL[qkv]
+    assert rel(o.reshape(BH, 1, dv).cpu().double().numpy(), o_ref) <= tol
+    assert rel(inp["S"].reshape(BH, dk, dv).cpu().double().numpy(), S_ref) <= tol
