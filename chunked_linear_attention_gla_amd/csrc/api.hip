@@ -451,8 +451,7 @@ gla_status_t gla_chunk_bwd(const void* q, const void* k, const void* v, const fl
   const int pad = (int)(nc * GLA_CHUNK - T);
   hipError_t e = hipSuccess;
   if (T > 0) {
-    e = gla::launch_gate_cumsum(x, b, BH, T, g, false, s);
-    if (e == hipSuccess) e = gla::launch_gate_cumsum(x, br, BH, T, g, true, s);
+    e = gla::launch_gate_cumsum_pair(x, b, br, BH, T, g, s);
     // forward-shaped passes: segment pre-pass (when segmented) and output pass.  A
     // reversed pass reads its rows back to front behind `pad` zero rows, so that its
     // chunks are the forward chunks in reverse order.

@@ -20,14 +20,13 @@ namespace gla {
 // loads before the first scan, so one memory round trip covers several chunks.
 constexpr int kGateChunksPerWave = 8;
 
+// The scan of one workgroup's chunks (block = the workgroup's index within its scan).
 template <int GATE, bool REV>
-__global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restrict__ x,
-                                                          float* __restrict__ b, long long T,
-                                                          long long chunks_per_head,
-                                                          long long total_chunks) {
+__device__ __forceinline__ void gate_cumsum_block(const float* __restrict__ x, float* __restrict__ b, long long T,
+                                                  long long chunks_per_head, long long total_chunks, long long block) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const long long first = ((long long)blockIdx.x * 4 + wave) * kGateChunksPerWave;
+  const long long first = (block * 4 + wave) * kGateChunksPerWave;
   if (first >= total_chunks) return;  // uniform across the wavefront
   // REV: the reversed sequence has pad absent tokens first, then original tokens
   // T-1 .. 0; logical token t > pad takes the gate of original token T + pad - t
@@ -61,6 +60,26 @@ __global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restric
     const float s = wave_inclusive_scan(g[i], lane);
     if (valid[i]) b[dst[i]] = s;
   }
+}
+
+template <int GATE, bool REV>
+__global__ void __launch_bounds__(256) gate_cumsum_kernel(const float* __restrict__ x,
+                                                          float* __restrict__ b, long long T,
+                                                          long long chunks_per_head,
+                                                          long long total_chunks) {
+  gate_cumsum_block<GATE, REV>(x, b, T, chunks_per_head, total_chunks, blockIdx.x);
+}
+
+// Both scans of the backward pass in one launch: the first `fwd_blocks` workgroups write
+// b, the others the reversed-padded b' (the two are independent).
+template <int GATE>
+__global__ void __launch_bounds__(256) gate_cumsum_pair_kernel(const float* __restrict__ x, float* __restrict__ b,
+                                                               float* __restrict__ br, long long T,
+                                                               long long chunks_per_head, long long total_chunks,
+                                                               long long fwd_blocks) {
+  const long long blk = blockIdx.x;
+  if (blk < fwd_blocks) gate_cumsum_block<GATE, false>(x, b, T, chunks_per_head, total_chunks, blk);
+  else gate_cumsum_block<GATE, true>(x, br, T, chunks_per_head, total_chunks, blk - fwd_blocks);
 }
 
 constexpr int kOrderThreads = 1024;
@@ -136,6 +155,23 @@ hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long 
     else
       hipLaunchKernelGGL((gate_cumsum_kernel<kGateNegSoftplus, false>), grid, block, 0, stream, x, b, T, cph, total);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gate_cumsum_pair(const float* x, float* b, float* br, long long BH, long long T, int gate,
+                                   hipStream_t stream) {
+  const long long cph = (T + kChunk - 1) / kChunk;  // the reversed-padded sequence has as many chunks
+  const long long total = BH * cph;
+  if (total == 0) return hipSuccess;
+  const long long blocks = (total + 4 * kGateChunksPerWave - 1) / (4 * kGateChunksPerWave);
+  if (2 * blocks > 0x7FFFFFFFLL) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(2 * blocks)), block(256);
+  if (gate == kGateBoundedSigmoid)
+    hipLaunchKernelGGL((gate_cumsum_pair_kernel<kGateBoundedSigmoid>), grid, block, 0, stream, x, b, br, T, cph, total,
+                       blocks);
+  else
+    hipLaunchKernelGGL((gate_cumsum_pair_kernel<kGateNegSoftplus>), grid, block, 0, stream, x, b, br, T, cph, total,
+                       blocks);
   return hipGetLastError();
 }
 

@@ -82,6 +82,9 @@ __host__ __device__ inline unsigned row_offset(const ChunkParams& p, unsigned T,
 // that line up with the forward chunks.
 hipError_t launch_gate_cumsum(const float* x, float* b, long long BH, long long T, int gate,
                               bool reversed_shift, hipStream_t stream);
+// Both of the above (b and the reversed-padded b') in one launch.
+hipError_t launch_gate_cumsum_pair(const float* x, float* b, float* br, long long BH, long long T, int gate,
+                                   hipStream_t stream);
 // Packed sequences: q, k, v, x and o are [H][T][.] (T = total tokens), sequence n of
 // every head covers rows [cu_seqlens[n], cu_seqlens[n+1]) and restarts its chunks
 // there; at most max_chunks chunks per sequence.
