@@ -181,6 +181,32 @@ def stream_ceiling(gla, torch, nbytes: int, reps: int = 10) -> dict:
             "ms": round(ms, 4), "GB_per_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def chunk_stream_ceiling(gla, torch, BH: int, T: int, segments: int, reps: int = 10) -> dict:
+    """The output pass's access pattern without its arithmetic (gla_bench_chunk_stream):
+    BH * segments workgroups, at most one per compute unit, each streaming its run of
+    64-token chunks in order (q, k, v in bf16 and o in fp32 at d = 128) with the next
+    chunk's loads in flight.  The ceiling of that pattern, below the flat stream's."""
+    dev = torch.device("cuda:0")
+    nb = BH * T * 256
+    q = torch.ones(nb, dtype=torch.uint8, device=dev)
+    k, v = torch.ones_like(q), torch.ones_like(q)
+    o = torch.empty(2 * nb, dtype=torch.uint8, device=dev)
+    fn = lambda: gla.bench_chunk_stream(q, k, v, o, BH, T, segments)
+    settle(torch, fn, 0.1)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for _ in range(reps):
+        fn()
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / reps
+    gbs = 5 * nb / (ms / 1e3) / 1e9
+    del q, k, v, o
+    return {"what": f"the output pass's loads and stores without its arithmetic ({BH} heads x {segments} segments, "
+                    f"one workgroup per compute unit, 64-token chunks in order; gla_bench_chunk_stream)",
+            "ms": round(ms, 4), "GB_per_s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(w, target_s: float, per_channel: bool = False):
     """Time the fp64 oracle on a bounded sample of the workload (all heads, a prefix of
     the sequence sized to take about target_s seconds on this host)."""
@@ -716,6 +742,8 @@ def main():
         "context": {"device_copy": device_copy_rate(torch),
                     "stream_ceiling": stream_ceiling(gla, torch, B * H * T * dk * es)},
     }
+    if dk == 128 and dv == 128 and es == 2 and T % (64 * plan.segments) == 0:
+        result["context"]["chunk_stream_ceiling"] = chunk_stream_ceiling(gla, torch, B * H, T, plan.segments)
     if w.name == gin.HEADLINE and path == "unified" and not args.plan and not args.no_ablation:
         # the pages' comparison: conventional gate + diagonal branch against the unified
         # path, both on the ablation's own inputs (same shapes, strong decay)

@@ -79,6 +79,7 @@ _SIGS = {
                                  _psz, _vp]),
     "gla_chunk_fwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _ll, _i, _i, _i, _i, _i, _vp]),
     "gla_bench_stream": (_i, [_vp, _vp, _vp, _vp, ctypes.c_ulonglong, _i, _vp]),
+    "gla_bench_chunk_stream": (_i, [_vp, _vp, _vp, _vp, _i, ctypes.c_longlong, _i, _vp]),
     "gla_debug_flags": (_i, [ctypes.POINTER(ctypes.c_uint)]),
     "gla_debug_selftest": (_i, [_vp, _vp, _vp]),
     "gla_lane_selftest": (_i, [_vp, _vp, _vp]),
@@ -531,3 +532,17 @@ def bench_stream(a: torch.Tensor, b: torch.Tensor, c: torch.Tensor, out: torch.T
         _need(t.is_cuda and t.is_contiguous() and t.device == a.device, "tensors must be contiguous on one GPU")
     _check("gla_bench_stream", load().gla_bench_stream(_ptr(a), _ptr(b), _ptr(c), _ptr(out), nb // 16, grid,
                                                        _stream(a.device)))
+
+
+def bench_chunk_stream(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, BH: int, T: int,
+                       segments: int) -> None:
+    """Measurement helper: the output pass's access pattern without its arithmetic
+    (gla_bench_chunk_stream).  q, k, v: BH * T * 256 bytes each; o: BH * T * 512 bytes;
+    all contiguous on one GPU."""
+    nb = BH * T * 256
+    _need(all(t.numel() * t.element_size() >= nb for t in (q, k, v)), "q, k, v must hold BH * T * 256 bytes")
+    _need(o.numel() * o.element_size() >= 2 * nb, "o must hold BH * T * 512 bytes")
+    for t in (q, k, v, o):
+        _need(t.is_cuda and t.is_contiguous() and t.device == q.device, "tensors must be contiguous on one GPU")
+    _check("gla_bench_chunk_stream", load().gla_bench_chunk_stream(_ptr(q), _ptr(k), _ptr(v), _ptr(o), BH, T,
+                                                                   segments, _stream(q.device)))

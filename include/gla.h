@@ -381,6 +381,21 @@ gla_status_t gla_chunk_fwd_pc(const void* q, const void* k, const void* v, const
 gla_status_t gla_bench_stream(const void* a, const void* b, const void* c, void* out,
                               unsigned long long units, int grid, void* stream);
 
+/* Measurement helper (not part of the method).  The output pass's access pattern
+ * without its arithmetic: BH * segments workgroups of 512 threads, at most one per
+ * compute unit (each reserves 96 KB of LDS), workgroup w taking head w / segments and
+ * the (w % segments)-th run of (T / 64) / segments consecutive 64-token chunks, in
+ * order, with the next chunk's loads in flight while the current chunk's output is
+ * stored.  Per chunk it reads 16 KB from each of q, k, v (64 rows of 128 bf16) and
+ * writes 32 KB of o (64 rows of 128 fp32): 16-byte unit j of a chunk's o is the xor of
+ * unit j mod 1024 of q, k and v.  q, k, v: BH * T * 256 bytes each, o: BH * T * 512
+ * bytes, device memory, 16-byte aligned, o overlapping none of the inputs.  BH or T
+ * = 0: nothing is enqueued.  T not a multiple of 64, (T / 64) not a multiple of
+ * segments, a negative size or segments < 1: GLA_ERR_SHAPE; other errors as
+ * gla_bench_stream. */
+gla_status_t gla_bench_chunk_stream(const void* q, const void* k, const void* v, void* o, int BH, long long T,
+                                    int segments, void* stream);
+
 /* Cross-lane self-test: one wavefront of 64 lanes runs each wavefront helper the
  * kernels build on -- DPP group maxima and sums over 8 and 16 lanes, the strided
  * exclusive scans over lane groups of 4, 8 and 16, the 64-lane inclusive scan, the
